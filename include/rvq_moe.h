@@ -1,0 +1,218 @@
+/*
+ * rvq_moe.h -- C ABI of the routed RVQ-MoE decode layer for MI355X (gfx950).
+ *
+ * One Mixture-of-Experts layer whose expert weights are stored as 3-stage
+ * residual vector quantisation: three 256-entry codebooks over 8-wide weight
+ * vectors, one code byte per stage, 3.00 bits per weight.  The layer routes
+ * every token to its top-k experts and evaluates each expert's SwiGLU FFN
+ * (gate, up, down) straight from the codes through tables of partial dot
+ * products built in LDS, never materialising a dense matrix.
+ *
+ * Sources:
+ *   [FR] "Exécuter Kimi K3 avec 29 Go de RAM à 0,50 tok/s" (fr.news.hada.io,
+ *        topic 32035):
+ *        - "Quantification et exactitude": the RVQ format (3 stages, 256
+ *          entries, 8-dim vectors, 3.00 bits/weight) and its evaluation (a
+ *          table of partial dot products, 3 lookups and 2 additions per row).
+ *        - "Architecture de streaming depuis le disque": gate, up and down of
+ *          one expert are contiguous so one expert is one read; records are
+ *          validated by expert id and offset range.
+ *        - "Lecture anticipée et prédiction du routeur": the router of a layer
+ *          decides 16 expert ids and expert reads are consumed as they land.
+ *        - "Objectif et forme d'implémentation de WASTE": a small public C API
+ *          (open, set a memory limit, run, close) called from Python by ctypes.
+ *        - "Budget RAM et fenêtre de performance étroite": 16 experts per token
+ *          per layer; the engine refuses to start below its minimum budget.
+ *   [RU] "WASTE: запускаем полную Kimi K3 на MacBook Pro с 64 ГБ памяти"
+ *        (feed.hirify.me), "Расчёт строится на устройстве MoE": 16 experts per
+ *        layer, gate/up/down stored back to back, the matrix never unfolded.
+ *
+ * Conventions for every entry point:
+ *   - Pointers are DEVICE pointers (HIP, the device current at rvq_moe_open)
+ *     unless stated otherwise.  Arrays are dense, row-major, little-endian.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Work is enqueued asynchronously on it; nothing in route_topk or
+ *     layer_forward synchronises the host.
+ *   - Return value: RVQ_MOE_OK (0) or a negative rvq_moe_status.  Arguments
+ *     are validated before anything is enqueued; on error nothing is
+ *     enqueued, nothing is allocated and no output is written.
+ *     rvq_moe_last_error() gives a human-readable reason.
+ *   - A handle is not thread-safe (its workspace is shared by its calls);
+ *     distinct handles are independent.  Calls that overlap on one handle
+ *     from different streams race.
+ */
+#ifndef RVQ_MOE_H
+#define RVQ_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define RVQ_MOE_ABI_VERSION 1
+
+typedef enum rvq_moe_status {
+    RVQ_MOE_OK = 0,
+    RVQ_MOE_EINVAL = -1,   /* bad dimension, pointer, token count or id */
+    RVQ_MOE_ENOTSUP = -2,  /* valid but unsupported format (stages != 3, codes != 256, vec != 8, ...) */
+    RVQ_MOE_EBUDGET = -3,  /* slot cache smaller than one token's working set (0 < cache_slots < top_k) */
+    RVQ_MOE_ENOMEM = -4,   /* device or pinned allocation failed */
+    RVQ_MOE_EHIP = -5,     /* a HIP runtime call or launch failed */
+    RVQ_MOE_EDEVICE = -6   /* deferred: a kernel saw an expert id outside [0, n_experts) */
+} rvq_moe_status;
+
+typedef enum rvq_moe_cb_dtype {
+    RVQ_MOE_CB_F32 = 0,    /* IEEE binary32 codebook entries */
+    RVQ_MOE_CB_F16 = 1     /* IEEE binary16 codebook entries */
+} rvq_moe_cb_dtype;
+
+typedef enum rvq_moe_codes_location {
+    RVQ_MOE_CODES_DEVICE = 0,      /* codes are in device memory; copied and repacked at open */
+    RVQ_MOE_CODES_PINNED_HOST = 1  /* codes stay in pinned host memory (borrowed) */
+} rvq_moe_codes_location;
+
+/*
+ * Layer description, read only during rvq_moe_open.
+ *
+ *   d, ffn       hidden size and expert FFN width; both multiples of 8 (the
+ *                vector width), d <= 65536, ffn <= 65536.
+ *   n_experts    E, 1 <= E <= 1024.     top_k   k, 1 <= k <= min(E, 64).
+ *   n_stages, n_codes, vec_dim   must be 3, 256, 8 ([FR] "Quantification et
+ *                exactitude"); anything else is RVQ_MOE_ENOTSUP.
+ *   codebook_dtype  rvq_moe_cb_dtype.
+ *   router_w     fp32 [d][E] router matrix: logits[e] = sum_i x_i W[i][e].
+ *   codebooks    [E][3 matrices: gate, up, down][3 stages][256][8] entries of
+ *                codebook_dtype.  A weight is c1 + c2 + c3, the sum of its
+ *                three stage vectors' entries; no scale, no bias.
+ *   codes        [E][record] with record = gate [ffn][d/8][3] u8, then up
+ *                [ffn][d/8][3] u8, then down [d][ffn/8][3] u8: byte s of
+ *                (row, slice j) indexes stage s's codebook for the 8 weights
+ *                row[8j .. 8j+7].  Record bytes = 9 * d * ffn / 8.
+ *   codes_location  rvq_moe_codes_location.  Only RVQ_MOE_CODES_DEVICE is
+ *                implemented by this version (PINNED_HOST: RVQ_MOE_ENOTSUP).
+ *   cache_slots  0 = all experts resident.  Otherwise the number of HBM expert
+ *                slots; must be >= top_k (RVQ_MOE_EBUDGET), mirroring the
+ *                refusal to start below one token's working set.
+ *   pre_rmsnorm  nonzero: x_hat = x / sqrt(mean(x^2) + eps) feeds both the
+ *                router and the experts (unit norm weight).  eps is double.
+ *   residual     nonzero: layer_forward returns x + MoE(x_hat) instead of
+ *                MoE(x_hat).
+ *   max_tokens   largest n_tokens any later call will pass (sizes the
+ *                per-handle workspace, allocated once at open).
+ *   stream       stream used for the upload and repack inside open.
+ */
+typedef struct rvq_moe_desc {
+    uint32_t struct_size;       /* = sizeof(rvq_moe_desc) */
+    int32_t d;
+    int32_t ffn;
+    int32_t n_experts;
+    int32_t top_k;
+    int32_t n_stages;
+    int32_t n_codes;
+    int32_t vec_dim;
+    int32_t codebook_dtype;
+    int32_t codes_location;
+    int32_t cache_slots;
+    int32_t pre_rmsnorm;
+    int32_t residual;
+    int32_t max_tokens;
+    double eps;
+    const float *router_w;
+    const void *codebooks;
+    const uint8_t *codes;
+    void *stream;
+} rvq_moe_desc;
+
+typedef struct rvq_moe rvq_moe;
+
+/*
+ * rvq_moe_open -- validate `desc`, allocate the handle, copy the router and
+ * codebooks, and repack the codes into the library's tiled internal layout.
+ * Synchronises `desc->stream` before returning; the caller may free every
+ * input buffer afterwards (the library owns its copies and its workspace).
+ * On failure *out is set to NULL and nothing stays allocated.
+ * Errors: EINVAL (null desc/out/pointers, struct_size mismatch, bad dims,
+ * k > E, max_tokens < 1), ENOTSUP (format or codes_location), EBUDGET
+ * (0 < cache_slots < top_k), ENOMEM, EHIP.
+ */
+int rvq_moe_open(const rvq_moe_desc *desc, rvq_moe **out);
+
+/*
+ * rvq_moe_route_topk -- router GEMV (fp64 accumulation of fp32 products),
+ * then the k largest logits per token in descending order (ties to the lower
+ * id) and their softmax gates (sum to 1).  [FR] "Lecture anticipée et
+ * prédiction du routeur": the router decides the token's expert ids.
+ *   x      [n_tokens][d] fp32 (the un-normalised input when pre_rmsnorm).
+ *   ids    [n_tokens][k] int32 out.       gates  [n_tokens][k] fp32 out.
+ * Errors: EINVAL (null handle/pointer, n_tokens < 1 or > max_tokens), EHIP.
+ * Asynchronous; may be called on its own (e.g. to prefetch for a later layer).
+ */
+int rvq_moe_route_topk(rvq_moe *h, const float *x, int32_t n_tokens, int32_t *ids, float *gates,
+                       void *stream);
+
+/*
+ * rvq_moe_layer_forward -- y[t] = sum_j gates[t][j] * FFN_{ids[t][j]}(x_hat[t])
+ * (+ x[t] when residual), FFN(v) = W_d (silu(W_g v) * (W_u v)) evaluated from
+ * the codes by per-token tables of partial dot products ([FR]
+ * "Quantification et exactitude").
+ *   x      [n_tokens][d] fp32.   ids [n_tokens][k] int32.   gates [n_tokens][k] fp32.
+ *   y      [n_tokens][d] fp32 out (must not alias x).
+ * Ids outside [0, E) are detected on the device: the affected outputs are
+ * unspecified and the error is returned by rvq_moe_sync / rvq_moe_close
+ * (RVQ_MOE_EDEVICE).
+ * Errors: EINVAL (null handle/pointer, n_tokens < 1 or > max_tokens, y == x), EHIP.
+ */
+int rvq_moe_layer_forward(rvq_moe *h, const float *x, int32_t n_tokens, const int32_t *ids,
+                          const float *gates, float *y, void *stream);
+
+/*
+ * rvq_moe_sync -- synchronise `stream`, then return and clear any deferred
+ * device-side error (RVQ_MOE_EDEVICE) recorded by earlier calls.
+ */
+int rvq_moe_sync(rvq_moe *h, void *stream);
+
+/*
+ * rvq_moe_close -- synchronise the device, free everything the handle owns,
+ * and return any deferred device-side error.  NULL is accepted (returns OK).
+ */
+int rvq_moe_close(rvq_moe *h);
+
+/* Reason for the last failure on this thread (never NULL; "" if none). */
+const char *rvq_moe_last_error(void);
+
+/* Library ABI version (RVQ_MOE_ABI_VERSION of the built library). */
+int rvq_moe_abi_version(void);
+
+/* Per-handle counters, exact and host-side (no device readback). */
+typedef struct rvq_moe_stats {
+    uint64_t route_calls;
+    uint64_t forward_calls;
+    uint64_t tokens_routed;
+    uint64_t tokens_forwarded;
+    uint64_t expert_evals;          /* token x expert pairs evaluated */
+    uint64_t code_bytes_resident;   /* bytes of the library's code copy */
+    uint64_t record_bytes;          /* canonical bytes per expert record */
+    uint64_t codebook_bytes;        /* bytes of one expert's codebooks */
+} rvq_moe_stats;
+
+int rvq_moe_get_stats(const rvq_moe *h, rvq_moe_stats *out);
+
+/*
+ * Kernel timing.  rvq_moe_set_profiling(h, every) makes every `every`-th
+ * forward call bracket each of its kernels with HIP events on the caller's
+ * stream (0 disables).  rvq_moe_kernel_times synchronises the device and
+ * returns, per kernel kind, the number of timed launches and their summed
+ * duration in milliseconds; names[] are static strings.  Kinds:
+ *   0 router, 1 topk, 2 gate/up gather, 3 down gather, 4 combine.
+ */
+#define RVQ_MOE_N_KERNEL_KINDS 5
+int rvq_moe_set_profiling(rvq_moe *h, int every);
+int rvq_moe_kernel_times(rvq_moe *h, const char **names, uint64_t *launches, double *total_ms,
+                         int max_kinds);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -42,6 +42,8 @@ def lib():
         if not os.path.exists(LIB_PATH) or os.path.getmtime(LIB_PATH) < os.path.getmtime(SRC_PATH):
             build()
         L = ctypes.CDLL(LIB_PATH)
+        L.rvq_oracle_threads.argtypes = []
+        L.rvq_oracle_threads.restype = ctypes.c_int
         L.rvq_oracle_half_to_double.argtypes = [ctypes.c_uint16]
         L.rvq_oracle_half_to_double.restype = ctypes.c_double
         L.rvq_oracle_rmsnorm.argtypes = [ctypes.c_int, _f32p, ctypes.c_double, _f64p]
@@ -76,6 +78,10 @@ def _cb_dtype_code(cb: np.ndarray) -> int:
 def _check(rc: int, what: str):
     if rc != 0:
         raise ValueError(f"oracle {what} rejected its arguments (rc={rc})")
+
+
+def threads() -> int:
+    return lib().rvq_oracle_threads()
 
 
 def half_to_double(bits: int) -> float:

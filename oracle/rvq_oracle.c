@@ -35,6 +35,17 @@
 #include <math.h>
 #include <stdlib.h>
 #include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+int rvq_oracle_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
 
 double rvq_oracle_half_to_double(uint16_t h) {
     int sign = (h >> 15) & 1;
@@ -123,21 +134,26 @@ int rvq_oracle_matvec(int rows, int cols, const void *codebook, int cb_dtype, co
     if (cb_dtype != 0 && cb_dtype != 1) return -1;
     const int n_slices = cols / RVQO_VEC;
     const size_t stage_stride = (size_t)RVQO_CODES * RVQO_VEC;
+    /* decode the three stage codebooks to double once (exact for fp32 and fp16) */
+    double *cb = (double *)malloc(sizeof(double) * RVQO_STAGES * stage_stride);
+    if (!cb) return -1;
+    for (size_t idx = 0; idx < RVQO_STAGES * stage_stride; idx++) cb[idx] = cb_value(codebook, cb_dtype, idx);
 #pragma omp parallel for schedule(static)
     for (int r = 0; r < rows; r++) {
         double acc = 0.0;
         for (int j = 0; j < n_slices; j++) {
             const uint8_t *c = codes + ((size_t)r * n_slices + j) * RVQO_STAGES;
+            const double *c1 = cb + 0 * stage_stride + (size_t)c[0] * RVQO_VEC;
+            const double *c2 = cb + 1 * stage_stride + (size_t)c[1] * RVQO_VEC;
+            const double *c3 = cb + 2 * stage_stride + (size_t)c[2] * RVQO_VEC;
             for (int i = 0; i < RVQO_VEC; i++) {
-                double w1 = cb_value(codebook, cb_dtype, 0 * stage_stride + (size_t)c[0] * RVQO_VEC + i);
-                double w2 = cb_value(codebook, cb_dtype, 1 * stage_stride + (size_t)c[1] * RVQO_VEC + i);
-                double w3 = cb_value(codebook, cb_dtype, 2 * stage_stride + (size_t)c[2] * RVQO_VEC + i);
-                double w = (w1 + w2) + w3; /* the explicit c1 + c2 + c3 reconstruction */
+                double w = (c1[i] + c2[i]) + c3[i]; /* the explicit c1 + c2 + c3 reconstruction */
                 acc += w * v[(size_t)j * RVQO_VEC + i];
             }
         }
         out[r] = acc;
     }
+    free(cb);
     return 0;
 }
 

@@ -38,6 +38,9 @@ extern "C" {
 #define RVQO_CODES 256
 #define RVQO_VEC 8
 
+/* Threads the row loops use (OpenMP max threads; 1 without OpenMP). */
+int rvq_oracle_threads(void);
+
 /* IEEE binary16 bit pattern -> double, by field decoding. */
 double rvq_oracle_half_to_double(uint16_t h);
 

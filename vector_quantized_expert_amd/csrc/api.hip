@@ -1,0 +1,341 @@
+// api.hip -- the C ABI declared in include/rvq_moe.h.
+//
+// [FR] "Objectif et forme d'implémentation de WASTE": the engine exposes a small
+// C API (open, set a memory limit, run, close) that Python calls through
+// ctypes; [FR] "Budget RAM et fenêtre de performance étroite": it refuses to
+// start below the minimum budget instead of degrading.  Here: open validates
+// everything and owns all device memory; route_topk and layer_forward only
+// enqueue kernels on the caller's stream (no host synchronisation, no
+// allocation); close frees everything.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <vector>
+
+#include "../../include/rvq_moe.h"
+#include "internal.hpp"
+
+using namespace rvq;
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+struct EventPair {
+    hipEvent_t a, b;
+    int kind;
+};
+
+}  // namespace
+
+struct rvq_moe {
+    int device;
+    Geometry g;
+    int pre_rmsnorm, residual, max_tokens;
+    double eps;
+    uint8_t *codes;      // [E][rec_int] internal layout
+    void *cbs;           // [E][3][3][256][8]
+    float *router_w;     // [d][E]
+    Workspace ws;
+    rvq_moe_stats stats;
+    int prof_every;
+    uint64_t prof_calls;
+    std::vector<EventPair> prof_events;
+    std::vector<hipEvent_t> prof_pool;
+};
+
+namespace rvq {
+
+Geometry make_geometry(int d, int ffn, int E, int k, int cb_dtype) {
+    Geometry g{};
+    g.d = d;
+    g.ffn = ffn;
+    g.E = E;
+    g.k = k;
+    g.cb_dtype = cb_dtype;
+    const int rows[3] = {ffn, ffn, d};
+    const int slices[3] = {d / kVec, d / kVec, ffn / kVec};
+    int64_t off = 0;
+    for (int m = 0; m < 3; m++) {
+        MatGeom &mg = g.m[m];
+        mg.rows = rows[m];
+        mg.slices = slices[m];
+        mg.n_tiles = (slices[m] + kTileSlices - 1) / kTileSlices;
+        mg.n_chunks = (rows[m] + kChunkRows - 1) / kChunkRows;
+        mg.off = off;
+        mg.bytes = (int64_t)mg.n_tiles * mg.n_chunks * kChunkBytes;
+        off += mg.bytes;
+    }
+    g.rec_int = off;
+    g.rec_canon = (int64_t)9 * d * ffn / 8;
+    g.cb_bytes = (int64_t)3 * kStages * kCodes * kVec * (cb_dtype == 0 ? 4 : 2);
+    g.ffn_pad = g.m[0].n_chunks * kChunkRows;
+    g.d_pad = g.m[2].n_chunks * kChunkRows;
+    // Down rows are split so that a token's k experts x ffn tiles x row blocks
+    // give at least ~4 workgroups per CU of the 256 on MI355X.
+    const int want = 1024;
+    const int per_tok = k * g.m[2].n_tiles;
+    int nrb = (want + per_tok - 1) / per_tok;
+    if (nrb > g.m[2].n_chunks) nrb = g.m[2].n_chunks;
+    if (nrb < 1) nrb = 1;
+    g.down_row_block = (g.m[2].n_chunks + nrb - 1) / nrb;
+    g.n_down_rb = (g.m[2].n_chunks + g.down_row_block - 1) / g.down_row_block;
+    return g;
+}
+
+}  // namespace rvq
+
+static void free_handle(rvq_moe *h) {
+    if (!h) return;
+    (void)hipFree(h->codes);
+    (void)hipFree(h->cbs);
+    (void)hipFree(h->router_w);
+    (void)hipFree(h->ws.tok_r);
+    (void)hipFree(h->ws.route_part);
+    (void)hipFree(h->ws.part_gu);
+    (void)hipFree(h->ws.part_dn);
+    (void)hipFree(h->ws.err);
+    for (hipEvent_t e : h->prof_pool) (void)hipEventDestroy(e);
+    delete h;
+}
+
+#define HIP_TRY(call)                                                                     \
+    do {                                                                                  \
+        hipError_t _e = (call);                                                           \
+        if (_e != hipSuccess) {                                                           \
+            int _code = (_e == hipErrorOutOfMemory) ? RVQ_MOE_ENOMEM : RVQ_MOE_EHIP;      \
+            fail(_code, "%s failed: %s", #call, hipGetErrorString(_e));                   \
+            return _code;                                                                 \
+        }                                                                                 \
+    } while (0)
+
+static int open_impl(const rvq_moe_desc *desc, rvq_moe *h) {
+    const rvq_moe_desc &D = *desc;
+    hipStream_t s = static_cast<hipStream_t>(D.stream);
+    HIP_TRY(hipGetDevice(&h->device));
+    h->g = make_geometry(D.d, D.ffn, D.n_experts, D.top_k, D.codebook_dtype);
+    h->pre_rmsnorm = D.pre_rmsnorm != 0;
+    h->residual = D.residual != 0;
+    h->eps = D.eps;
+    h->max_tokens = D.max_tokens;
+    const Geometry &g = h->g;
+    const int64_t E = D.n_experts;
+    HIP_TRY(hipMalloc(&h->codes, (size_t)(E * g.rec_int)));
+    HIP_TRY(hipMalloc(&h->cbs, (size_t)(E * g.cb_bytes)));
+    HIP_TRY(hipMalloc(&h->router_w, sizeof(float) * (size_t)D.d * E));
+    h->ws.n_rblk = (D.d + kRouterRows - 1) / kRouterRows;
+    const int64_t T = D.max_tokens;
+    HIP_TRY(hipMalloc(&h->ws.tok_r, sizeof(double) * (size_t)T));
+    HIP_TRY(hipMalloc(&h->ws.route_part, sizeof(double) * (size_t)(T * h->ws.n_rblk * E)));
+    HIP_TRY(hipMalloc(&h->ws.part_gu, sizeof(float) * (size_t)(T * D.top_k * 2 * g.m[0].n_tiles * g.ffn_pad)));
+    HIP_TRY(hipMalloc(&h->ws.part_dn, sizeof(float) * (size_t)(T * D.top_k * g.m[2].n_tiles * g.d_pad)));
+    HIP_TRY(hipMalloc(&h->ws.err, sizeof(int)));
+    HIP_TRY(hipMemsetAsync(h->ws.err, 0, sizeof(int), s));
+    HIP_TRY(hipMemcpyAsync(h->cbs, D.codebooks, (size_t)(E * g.cb_bytes), hipMemcpyDeviceToDevice, s));
+    HIP_TRY(hipMemcpyAsync(h->router_w, D.router_w, sizeof(float) * (size_t)D.d * E, hipMemcpyDeviceToDevice, s));
+    HIP_TRY(launch_repack(g, D.codes, h->codes, D.n_experts, s));
+    HIP_TRY(hipStreamSynchronize(s));
+    h->stats.code_bytes_resident = (uint64_t)(E * g.rec_int);
+    h->stats.record_bytes = (uint64_t)g.rec_canon;
+    h->stats.codebook_bytes = (uint64_t)g.cb_bytes;
+    return RVQ_MOE_OK;
+}
+
+extern "C" int rvq_moe_open(const rvq_moe_desc *desc, rvq_moe **out) {
+    g_err[0] = 0;
+    if (!out) return fail(RVQ_MOE_EINVAL, "out is NULL");
+    *out = nullptr;
+    if (!desc) return fail(RVQ_MOE_EINVAL, "desc is NULL");
+    const rvq_moe_desc &D = *desc;
+    if (D.struct_size != sizeof(rvq_moe_desc))
+        return fail(RVQ_MOE_EINVAL, "struct_size %u != %zu", D.struct_size, sizeof(rvq_moe_desc));
+    if (D.n_stages != kStages || D.n_codes != kCodes || D.vec_dim != kVec)
+        return fail(RVQ_MOE_ENOTSUP, "only 3 stages x 256 codes x 8-wide vectors are supported");
+    if (D.d <= 0 || D.ffn <= 0 || D.d % kVec || D.ffn % kVec || D.d > 65536 || D.ffn > 65536)
+        return fail(RVQ_MOE_EINVAL, "d=%d ffn=%d must be positive multiples of 8, <= 65536", D.d, D.ffn);
+    if (D.n_experts < 1 || D.n_experts > kMaxExperts)
+        return fail(RVQ_MOE_EINVAL, "n_experts=%d outside [1, %d]", D.n_experts, kMaxExperts);
+    if (D.top_k < 1 || D.top_k > D.n_experts || D.top_k > kMaxTopK)
+        return fail(RVQ_MOE_EINVAL, "top_k=%d outside [1, min(E, %d)]", D.top_k, kMaxTopK);
+    if (D.codebook_dtype != RVQ_MOE_CB_F32 && D.codebook_dtype != RVQ_MOE_CB_F16)
+        return fail(RVQ_MOE_EINVAL, "codebook_dtype=%d", D.codebook_dtype);
+    if (D.max_tokens < 1) return fail(RVQ_MOE_EINVAL, "max_tokens=%d < 1", D.max_tokens);
+    if (D.cache_slots < 0) return fail(RVQ_MOE_EINVAL, "cache_slots=%d < 0", D.cache_slots);
+    if (D.cache_slots > 0 && D.cache_slots < D.top_k)
+        return fail(RVQ_MOE_EBUDGET, "cache_slots=%d below one token's working set (top_k=%d)", D.cache_slots,
+                    D.top_k);
+    if (D.codes_location != RVQ_MOE_CODES_DEVICE && D.codes_location != RVQ_MOE_CODES_PINNED_HOST)
+        return fail(RVQ_MOE_EINVAL, "codes_location=%d", D.codes_location);
+    if (D.codes_location != RVQ_MOE_CODES_DEVICE || D.cache_slots != 0)
+        return fail(RVQ_MOE_ENOTSUP, "only resident device codes are implemented");
+    if (!D.router_w || !D.codebooks || !D.codes) return fail(RVQ_MOE_EINVAL, "null router_w/codebooks/codes");
+    if (!(D.eps >= 0.0)) return fail(RVQ_MOE_EINVAL, "eps must be >= 0");
+    rvq_moe *h = new (std::nothrow) rvq_moe();
+    if (!h) return fail(RVQ_MOE_ENOMEM, "host allocation failed");
+    const int rc = open_impl(desc, h);
+    if (rc != RVQ_MOE_OK) {
+        free_handle(h);
+        return rc;
+    }
+    *out = h;
+    return RVQ_MOE_OK;
+}
+
+static int check_call(rvq_moe *h, const void *x, int32_t T) {
+    if (!h) return fail(RVQ_MOE_EINVAL, "handle is NULL");
+    if (!x) return fail(RVQ_MOE_EINVAL, "x is NULL");
+    if (T < 1 || T > h->max_tokens) return fail(RVQ_MOE_EINVAL, "n_tokens=%d outside [1, %d]", T, h->max_tokens);
+    return RVQ_MOE_OK;
+}
+
+// Brackets one kernel launch with profiling events when this call is sampled.
+struct ProfScope {
+    rvq_moe *h;
+    hipStream_t s;
+    bool on;
+    int kind;
+    hipEvent_t a = nullptr, b = nullptr;
+    ProfScope(rvq_moe *h_, hipStream_t s_, bool on_, int kind_) : h(h_), s(s_), on(on_), kind(kind_) {
+        if (!on) return;
+        if (h->prof_pool.size() < 2) {
+            on = false;
+            return;
+        }
+        b = h->prof_pool.back();
+        h->prof_pool.pop_back();
+        a = h->prof_pool.back();
+        h->prof_pool.pop_back();
+        (void)hipEventRecord(a, s);
+    }
+    ~ProfScope() {
+        if (!on) return;
+        (void)hipEventRecord(b, s);
+        h->prof_events.push_back({a, b, kind});
+    }
+};
+
+extern "C" int rvq_moe_route_topk(rvq_moe *h, const float *x, int32_t T, int32_t *ids, float *gates,
+                                  void *stream) {
+    int rc = check_call(h, x, T);
+    if (rc) return rc;
+    if (!ids || !gates) return fail(RVQ_MOE_EINVAL, "ids/gates is NULL");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    HIP_TRY(launch_prep(h->g, h->ws, x, T, h->pre_rmsnorm, h->eps, s));
+    HIP_TRY(launch_router(h->g, h->ws, x, h->router_w, T, s));
+    HIP_TRY(launch_topk(h->g, h->ws, T, ids, gates, s));
+    h->stats.route_calls++;
+    h->stats.tokens_routed += (uint64_t)T;
+    return RVQ_MOE_OK;
+}
+
+extern "C" int rvq_moe_layer_forward(rvq_moe *h, const float *x, int32_t T, const int32_t *ids,
+                                     const float *gates, float *y, void *stream) {
+    int rc = check_call(h, x, T);
+    if (rc) return rc;
+    if (!ids || !gates || !y) return fail(RVQ_MOE_EINVAL, "ids/gates/y is NULL");
+    if ((const void *)y == (const void *)x) return fail(RVQ_MOE_EINVAL, "y aliases x");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const bool prof = h->prof_every > 0 && (h->prof_calls++ % (uint64_t)h->prof_every) == 0;
+    HIP_TRY(launch_prep(h->g, h->ws, x, T, h->pre_rmsnorm, h->eps, s));
+    {
+        ProfScope p(h, s, prof, 2);
+        HIP_TRY(launch_gateup(h->g, h->ws, h->codes, h->cbs, x, ids, T, s));
+    }
+    {
+        ProfScope p(h, s, prof, 3);
+        HIP_TRY(launch_down(h->g, h->ws, h->codes, h->cbs, ids, T, s));
+    }
+    {
+        ProfScope p(h, s, prof, 4);
+        HIP_TRY(launch_combine(h->g, h->ws, x, ids, gates, y, T, h->residual, s));
+    }
+    h->stats.forward_calls++;
+    h->stats.tokens_forwarded += (uint64_t)T;
+    h->stats.expert_evals += (uint64_t)T * (uint64_t)h->g.k;
+    return RVQ_MOE_OK;
+}
+
+static int take_device_error(rvq_moe *h) {
+    int flag = 0;
+    HIP_TRY(hipMemcpy(&flag, h->ws.err, sizeof(int), hipMemcpyDeviceToHost));
+    if (flag) {
+        HIP_TRY(hipMemset(h->ws.err, 0, sizeof(int)));
+        return fail(RVQ_MOE_EDEVICE, "a kernel saw an expert id outside [0, %d)", h->g.E);
+    }
+    return RVQ_MOE_OK;
+}
+
+extern "C" int rvq_moe_sync(rvq_moe *h, void *stream) {
+    if (!h) return fail(RVQ_MOE_EINVAL, "handle is NULL");
+    HIP_TRY(hipStreamSynchronize(static_cast<hipStream_t>(stream)));
+    return take_device_error(h);
+}
+
+extern "C" int rvq_moe_close(rvq_moe *h) {
+    if (!h) return RVQ_MOE_OK;
+    int rc = RVQ_MOE_OK;
+    if (hipDeviceSynchronize() != hipSuccess) rc = fail(RVQ_MOE_EHIP, "hipDeviceSynchronize failed at close");
+    if (rc == RVQ_MOE_OK) rc = take_device_error(h);
+    free_handle(h);
+    return rc;
+}
+
+extern "C" const char *rvq_moe_last_error(void) { return g_err; }
+
+extern "C" int rvq_moe_abi_version(void) { return RVQ_MOE_ABI_VERSION; }
+
+extern "C" int rvq_moe_get_stats(const rvq_moe *h, rvq_moe_stats *out) {
+    if (!h || !out) return fail(RVQ_MOE_EINVAL, "null handle or out");
+    *out = h->stats;
+    return RVQ_MOE_OK;
+}
+
+static const char *kKindNames[RVQ_MOE_N_KERNEL_KINDS] = {"router", "topk", "gateup_gather", "down_gather",
+                                                          "combine"};
+
+extern "C" int rvq_moe_set_profiling(rvq_moe *h, int every) {
+    if (!h || every < 0) return fail(RVQ_MOE_EINVAL, "bad handle or every");
+    h->prof_every = every;
+    h->prof_calls = 0;
+    if (every > 0 && h->prof_pool.empty() && h->prof_events.empty()) {
+        for (int i = 0; i < 8192; i++) {
+            hipEvent_t e;
+            HIP_TRY(hipEventCreate(&e));
+            h->prof_pool.push_back(e);
+        }
+    }
+    return RVQ_MOE_OK;
+}
+
+extern "C" int rvq_moe_kernel_times(rvq_moe *h, const char **names, uint64_t *launches, double *total_ms,
+                                    int max_kinds) {
+    if (!h || max_kinds < 0) return fail(RVQ_MOE_EINVAL, "bad handle");
+    HIP_TRY(hipDeviceSynchronize());
+    const int n = max_kinds < RVQ_MOE_N_KERNEL_KINDS ? max_kinds : RVQ_MOE_N_KERNEL_KINDS;
+    for (int i = 0; i < n; i++) {
+        if (names) names[i] = kKindNames[i];
+        if (launches) launches[i] = 0;
+        if (total_ms) total_ms[i] = 0.0;
+    }
+    for (const EventPair &p : h->prof_events) {
+        float ms = 0.f;
+        HIP_TRY(hipEventElapsedTime(&ms, p.a, p.b));
+        if (p.kind < n) {
+            if (launches) launches[p.kind]++;
+            if (total_ms) total_ms[p.kind] += ms;
+        }
+        h->prof_pool.push_back(p.a);
+        h->prof_pool.push_back(p.b);
+    }
+    h->prof_events.clear();
+    return n;
+}
