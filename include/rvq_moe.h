@@ -201,13 +201,16 @@ int rvq_moe_get_stats(const rvq_moe *h, rvq_moe_stats *out);
 
 /*
  * Kernel timing.  rvq_moe_set_profiling(h, every) makes every `every`-th
- * forward call bracket each of its kernels with HIP events on the caller's
- * stream (0 disables).  rvq_moe_kernel_times synchronises the device and
- * returns, per kernel kind, the number of timed launches and their summed
- * duration in milliseconds; names[] are static strings.  Kinds:
- *   0 router, 1 topk, 2 gate/up gather, 3 down gather, 4 combine.
+ * route_topk and every `every`-th layer_forward call bracket its kernel with
+ * HIP events on the caller's stream (0 disables).  rvq_moe_kernel_times
+ * synchronises the device and returns, per kernel kind, the number of timed
+ * launches and their summed duration in milliseconds, then clears the
+ * samples; names[] receives static strings.  Returns the number of kinds
+ * filled (>= 0) or a negative status.  Kinds:
+ *   0 "route_topk"  the router + top-k kernel of rvq_moe_route_topk,
+ *   1 "layer_lut"   the persistent LUT kernel of rvq_moe_layer_forward.
  */
-#define RVQ_MOE_N_KERNEL_KINDS 5
+#define RVQ_MOE_N_KERNEL_KINDS 2
 int rvq_moe_set_profiling(rvq_moe *h, int every);
 int rvq_moe_kernel_times(rvq_moe *h, const char **names, uint64_t *launches, double *total_ms,
                          int max_kinds);

@@ -230,3 +230,24 @@ def test_k3_layer_batch1_sampled_tokens(torch_mod):
     worst = _check(inp, shape, x, ids, gates, y)
     print(f"K3 layer worst rel L2 {worst:.3e}")
     layer.close()
+
+
+def test_router_ties_go_to_the_lower_id_and_k_equals_e(torch_mod):
+    """Experts 3 and 9 (and 5, 11) get identical router columns, so their logits
+    tie exactly on both sides; the lower id must come first, as in the oracle."""
+    from synth import gpu as G
+    shape = S.Shape(256, 64, 12, 12, "f32")
+    inp = G.LayerInputs(shape, seed=4, layer=0, host_codes=True)
+    inp.w_r[:, 9] = inp.w_r[:, 3]
+    inp.w_r[:, 11] = inp.w_r[:, 5]
+    inp.w_r_dev.copy_(G.to_device(inp.w_r))
+    layer = _layer(torch_mod, inp, shape, 4)
+    x = S.tokens(4, 0, 4, shape.d)
+    ids, gates, y = _run(torch_mod, layer, shape, x)
+    for t in range(4):
+        ref = O.layer(x[t], inp.w_r, shape.top_k, inp.codebook, inp.record, shape.d, shape.ffn)
+        assert np.array_equal(ids[t], ref.route.ids)
+        pos = {int(e): j for j, e in enumerate(ids[t])}
+        assert pos[3] + 1 == pos[9] and pos[5] + 1 == pos[11]
+        np.testing.assert_allclose(gates[t], ref.route.gates, rtol=TOL_G)
+    layer.close()

@@ -13,7 +13,7 @@
 
 #include <vector>
 
-#include "../../include/rvq_moe.h"
+#include "rvq_moe.h"
 #include "internal.hpp"
 
 using namespace rvq;
@@ -44,11 +44,12 @@ struct rvq_moe {
     double eps;
     uint8_t *codes;      // [E][rec_int] internal layout
     void *cbs;           // [E][3][3][256][8]
-    float *router_w;     // [d][E]
+    float *router_wt;    // [E][d] (transposed copy)
     Workspace ws;
     rvq_moe_stats stats;
     int prof_every;
     uint64_t prof_calls;
+    uint64_t prof_route_calls;
     std::vector<EventPair> prof_events;
     std::vector<hipEvent_t> prof_pool;
 };
@@ -80,15 +81,6 @@ Geometry make_geometry(int d, int ffn, int E, int k, int cb_dtype) {
     g.cb_bytes = (int64_t)3 * kStages * kCodes * kVec * (cb_dtype == 0 ? 4 : 2);
     g.ffn_pad = g.m[0].n_chunks * kChunkRows;
     g.d_pad = g.m[2].n_chunks * kChunkRows;
-    // Down rows are split so that a token's k experts x ffn tiles x row blocks
-    // give at least ~4 workgroups per CU of the 256 on MI355X.
-    const int want = 1024;
-    const int per_tok = k * g.m[2].n_tiles;
-    int nrb = (want + per_tok - 1) / per_tok;
-    if (nrb > g.m[2].n_chunks) nrb = g.m[2].n_chunks;
-    if (nrb < 1) nrb = 1;
-    g.down_row_block = (g.m[2].n_chunks + nrb - 1) / nrb;
-    g.n_down_rb = (g.m[2].n_chunks + g.down_row_block - 1) / g.down_row_block;
     return g;
 }
 
@@ -98,11 +90,14 @@ static void free_handle(rvq_moe *h) {
     if (!h) return;
     (void)hipFree(h->codes);
     (void)hipFree(h->cbs);
-    (void)hipFree(h->router_w);
-    (void)hipFree(h->ws.tok_r);
-    (void)hipFree(h->ws.route_part);
+    (void)hipFree(h->router_wt);
+    (void)hipFree(h->ws.logits);
+    (void)hipFree(h->ws.sel);
     (void)hipFree(h->ws.part_gu);
     (void)hipFree(h->ws.part_dn);
+    (void)hipFree(h->ws.cntA);
+    (void)hipFree(h->ws.cntB);
+    (void)hipFree(h->ws.done);
     (void)hipFree(h->ws.err);
     for (hipEvent_t e : h->prof_pool) (void)hipEventDestroy(e);
     delete h;
@@ -131,17 +126,28 @@ static int open_impl(const rvq_moe_desc *desc, rvq_moe *h) {
     const int64_t E = D.n_experts;
     HIP_TRY(hipMalloc(&h->codes, (size_t)(E * g.rec_int)));
     HIP_TRY(hipMalloc(&h->cbs, (size_t)(E * g.cb_bytes)));
-    HIP_TRY(hipMalloc(&h->router_w, sizeof(float) * (size_t)D.d * E));
-    h->ws.n_rblk = (D.d + kRouterRows - 1) / kRouterRows;
-    const int64_t T = D.max_tokens;
-    HIP_TRY(hipMalloc(&h->ws.tok_r, sizeof(double) * (size_t)T));
-    HIP_TRY(hipMalloc(&h->ws.route_part, sizeof(double) * (size_t)(T * h->ws.n_rblk * E)));
-    HIP_TRY(hipMalloc(&h->ws.part_gu, sizeof(float) * (size_t)(T * D.top_k * 2 * g.m[0].n_tiles * g.ffn_pad)));
-    HIP_TRY(hipMalloc(&h->ws.part_dn, sizeof(float) * (size_t)(T * D.top_k * g.m[2].n_tiles * g.d_pad)));
+    HIP_TRY(hipMalloc(&h->router_wt, sizeof(float) * (size_t)D.d * E));
+    const int64_t T = D.max_tokens, P = T * D.top_k;
+    HIP_TRY(hipMalloc(&h->ws.logits, sizeof(double) * (size_t)(T * E)));
+    HIP_TRY(hipMalloc(&h->ws.sel, sizeof(double) * (size_t)(T * D.top_k)));
+    HIP_TRY(hipMalloc(&h->ws.part_gu, sizeof(float) * (size_t)(P * 2 * g.m[0].n_tiles * g.ffn_pad)));
+    HIP_TRY(hipMalloc(&h->ws.part_dn, sizeof(float) * (size_t)(P * g.m[2].n_tiles * g.d_pad)));
+    HIP_TRY(hipMalloc(&h->ws.cntA, sizeof(int) * (size_t)P));
+    HIP_TRY(hipMalloc(&h->ws.cntB, sizeof(int) * (size_t)T));
+    HIP_TRY(hipMalloc(&h->ws.done, sizeof(int)));
     HIP_TRY(hipMalloc(&h->ws.err, sizeof(int)));
+    int n_cu = 0;
+    HIP_TRY(hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, h->device));
+    int per_cu = 0;
+    HIP_TRY(layer_blocks_per_cu(D.codebook_dtype, &per_cu));
+    if (n_cu < 1 || per_cu < 1) return fail(RVQ_MOE_EHIP, "occupancy query gave %d CUs x %d blocks", n_cu, per_cu);
+    h->ws.n_wg = n_cu * per_cu;
+    HIP_TRY(hipMemsetAsync(h->ws.cntA, 0, sizeof(int) * (size_t)P, s));
+    HIP_TRY(hipMemsetAsync(h->ws.cntB, 0, sizeof(int) * (size_t)T, s));
+    HIP_TRY(hipMemsetAsync(h->ws.done, 0, sizeof(int), s));
     HIP_TRY(hipMemsetAsync(h->ws.err, 0, sizeof(int), s));
     HIP_TRY(hipMemcpyAsync(h->cbs, D.codebooks, (size_t)(E * g.cb_bytes), hipMemcpyDeviceToDevice, s));
-    HIP_TRY(hipMemcpyAsync(h->router_w, D.router_w, sizeof(float) * (size_t)D.d * E, hipMemcpyDeviceToDevice, s));
+    HIP_TRY(launch_transpose(D.router_w, h->router_wt, D.d, D.n_experts, s));
     HIP_TRY(launch_repack(g, D.codes, h->codes, D.n_experts, s));
     HIP_TRY(hipStreamSynchronize(s));
     h->stats.code_bytes_resident = (uint64_t)(E * g.rec_int);
@@ -229,9 +235,11 @@ extern "C" int rvq_moe_route_topk(rvq_moe *h, const float *x, int32_t T, int32_t
     if (rc) return rc;
     if (!ids || !gates) return fail(RVQ_MOE_EINVAL, "ids/gates is NULL");
     hipStream_t s = static_cast<hipStream_t>(stream);
-    HIP_TRY(launch_prep(h->g, h->ws, x, T, h->pre_rmsnorm, h->eps, s));
-    HIP_TRY(launch_router(h->g, h->ws, x, h->router_w, T, s));
-    HIP_TRY(launch_topk(h->g, h->ws, T, ids, gates, s));
+    const bool prof = h->prof_every > 0 && (h->prof_route_calls++ % (uint64_t)h->prof_every) == 0;
+    {
+        ProfScope p(h, s, prof, 0);
+        HIP_TRY(launch_route(h->g, h->ws, x, h->router_wt, T, h->pre_rmsnorm, h->eps, ids, gates, s));
+    }
     h->stats.route_calls++;
     h->stats.tokens_routed += (uint64_t)T;
     return RVQ_MOE_OK;
@@ -245,18 +253,10 @@ extern "C" int rvq_moe_layer_forward(rvq_moe *h, const float *x, int32_t T, cons
     if ((const void *)y == (const void *)x) return fail(RVQ_MOE_EINVAL, "y aliases x");
     hipStream_t s = static_cast<hipStream_t>(stream);
     const bool prof = h->prof_every > 0 && (h->prof_calls++ % (uint64_t)h->prof_every) == 0;
-    HIP_TRY(launch_prep(h->g, h->ws, x, T, h->pre_rmsnorm, h->eps, s));
     {
-        ProfScope p(h, s, prof, 2);
-        HIP_TRY(launch_gateup(h->g, h->ws, h->codes, h->cbs, x, ids, T, s));
-    }
-    {
-        ProfScope p(h, s, prof, 3);
-        HIP_TRY(launch_down(h->g, h->ws, h->codes, h->cbs, ids, T, s));
-    }
-    {
-        ProfScope p(h, s, prof, 4);
-        HIP_TRY(launch_combine(h->g, h->ws, x, ids, gates, y, T, h->residual, s));
+        ProfScope p(h, s, prof, 1);
+        HIP_TRY(launch_layer(h->g, h->ws, h->codes, h->cbs, x, ids, gates, y, T, h->pre_rmsnorm, h->residual,
+                             h->eps, s));
     }
     h->stats.forward_calls++;
     h->stats.tokens_forwarded += (uint64_t)T;
@@ -269,7 +269,9 @@ static int take_device_error(rvq_moe *h) {
     HIP_TRY(hipMemcpy(&flag, h->ws.err, sizeof(int), hipMemcpyDeviceToHost));
     if (flag) {
         HIP_TRY(hipMemset(h->ws.err, 0, sizeof(int)));
-        return fail(RVQ_MOE_EDEVICE, "a kernel saw an expert id outside [0, %d)", h->g.E);
+        return fail(RVQ_MOE_EDEVICE, "device error flags 0x%x:%s%s", flag,
+                    (flag & 1) ? " an expert id outside [0, E)" : "",
+                    (flag & 2) ? " an inter-workgroup wait timed out" : "");
     }
     return RVQ_MOE_OK;
 }
@@ -299,13 +301,13 @@ extern "C" int rvq_moe_get_stats(const rvq_moe *h, rvq_moe_stats *out) {
     return RVQ_MOE_OK;
 }
 
-static const char *kKindNames[RVQ_MOE_N_KERNEL_KINDS] = {"router", "topk", "gateup_gather", "down_gather",
-                                                          "combine"};
+static const char *kKindNames[RVQ_MOE_N_KERNEL_KINDS] = {"route_topk", "layer_lut"};
 
 extern "C" int rvq_moe_set_profiling(rvq_moe *h, int every) {
     if (!h || every < 0) return fail(RVQ_MOE_EINVAL, "bad handle or every");
     h->prof_every = every;
     h->prof_calls = 0;
+    h->prof_route_calls = 0;
     if (every > 0 && h->prof_pool.empty() && h->prof_events.empty()) {
         for (int i = 0; i < 8192; i++) {
             hipEvent_t e;

@@ -45,41 +45,67 @@ struct Geometry {
     int64_t cb_bytes;      // one expert's codebooks: 3 * 3 * 256 * 8 * elem
     int ffn_pad;           // gate chunks * 32
     int d_pad;             // down chunks * 32
-    int down_row_block;    // chunks per down workgroup
-    int n_down_rb;         // down row blocks
 };
 
 Geometry make_geometry(int d, int ffn, int E, int k, int cb_dtype);
 
+// Data handed between workgroups of one launch (partial sums, logits) is
+// written and read with agent-scope relaxed atomics: on gfx950 these are plain
+// loads/stores with the sc1 bit, coherent across the XCDs' L2 caches per
+// access, so no cache-wide writeback or invalidate (what a fence costs) is
+// needed.  A producer waits for its stores to complete (vmcnt 0) before a
+// counter increment publishes them.
+__device__ inline void store_coherent(float *p, float v) {
+    __hip_atomic_store(reinterpret_cast<uint32_t *>(p), __float_as_uint(v), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline float load_coherent(const float *p) {
+    return __uint_as_float(__hip_atomic_load(reinterpret_cast<const uint32_t *>(p), __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT));
+}
+__device__ inline void store_coherent(double *p, double v) {
+    __hip_atomic_store(reinterpret_cast<uint64_t *>(p), __double_as_longlong(v), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline double load_coherent(const double *p) {
+    return __longlong_as_double(
+        (long long)__hip_atomic_load(reinterpret_cast<const uint64_t *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+}
+__device__ inline int load_counter(const int *p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline void store_counter(int *p, int v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Wait until this wave's vector memory operations (including sc1 stores) completed.
+__device__ inline void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 // Workspace of one handle (device memory, sized for max_tokens at open).
 struct Workspace {
-    double *tok_r;      // [T] RMS divisor (1.0 when no normalisation)
-    double *route_part; // [T][n_rblk][E] fp64 partial logits
+    double *logits;     // [T][E] fp64 router logits
+    double *sel;        // [T][k] fp64 logits of the selected experts, by rank
     float *part_gu;     // [T*k][2][n_tiles_in][ffn_pad] partial gate/up sums
-    float *part_dn;     // [T*k][n_tiles_ffn][d_pad] partial down sums
-    int *err;           // device error flag
-    int n_rblk;         // router row blocks
+    float *part_dn;     // [T*k][n_tiles_ffn][d_pad] partial down sums (gate-weighted)
+    int *cntA;          // [T*k] finished gate/up chunks per pair (self-resetting)
+    int *cntB;          // [T] finished down chunks per token (self-resetting)
+    int *done;          // workgroups finished (self-resetting)
+    int *err;           // device error flag: bit 0 bad id, bit 1 wait timeout
+    int n_wg;           // persistent workgroups (all resident at once: blocks per CU x CUs)
 };
 
-constexpr int kRouterRows = 64;    // rows of W_r per router workgroup
-constexpr int kRouterTok = 4;      // tokens per router workgroup
+constexpr int kRouteTok = 8;       // tokens per router workgroup when T > 1
 constexpr int kMaxExperts = 1024;
 constexpr int kMaxTopK = 64;
 
 // Launchers (all asynchronous on `s`; return hipError_t of the launch).
 hipError_t launch_repack(const Geometry &g, const uint8_t *canon, uint8_t *internal, int n_experts,
                          hipStream_t s);
-hipError_t launch_prep(const Geometry &g, const Workspace &w, const float *x, int T, int pre_rmsnorm,
-                       double eps, hipStream_t s);
-hipError_t launch_router(const Geometry &g, const Workspace &w, const float *x, const float *router_w,
-                         int T, hipStream_t s);
-hipError_t launch_topk(const Geometry &g, const Workspace &w, int T, int32_t *ids, float *gates,
-                       hipStream_t s);
-hipError_t launch_gateup(const Geometry &g, const Workspace &w, const uint8_t *codes, const void *cbs,
-                         const float *x, const int32_t *ids, int T, hipStream_t s);
-hipError_t launch_down(const Geometry &g, const Workspace &w, const uint8_t *codes, const void *cbs,
-                       const int32_t *ids, int T, hipStream_t s);
-hipError_t launch_combine(const Geometry &g, const Workspace &w, const float *x, const int32_t *ids,
-                          const float *gates, float *y, int T, int residual, hipStream_t s);
+hipError_t launch_transpose(const float *W, float *Wt, int d, int E, hipStream_t s);
+hipError_t launch_route(const Geometry &g, const Workspace &w, const float *x, const float *Wt, int T, int pre,
+                        double eps, int32_t *ids, float *gates, hipStream_t s);
+hipError_t layer_blocks_per_cu(int cb_dtype, int *out);
+hipError_t launch_layer(const Geometry &g, const Workspace &w, const uint8_t *codes, const void *cbs,
+                        const float *x, const int32_t *ids, const float *gates, float *y, int T, int pre,
+                        int residual, double eps, hipStream_t s);
 
 }  // namespace rvq

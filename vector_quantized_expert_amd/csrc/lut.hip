@@ -1,5 +1,5 @@
 // lut.hip -- expert evaluation from RVQ codes through tables of partial dot
-// products held in LDS.
+// products held in LDS, as one persistent kernel per layer call.
 //
 // [FR] "Quantification et exactitude": expert weights are 3-stage residual VQ
 // (256-entry codebooks, 8-dim vectors, 3.00 bits per weight); the matrix is not
@@ -12,15 +12,33 @@
 //     T_s[j][c] = sum_{i<8} C_s[c][i] * v[8j + i]      (s = stage, c = code)
 // and row r is  sum_j T_0[j][c0(r,j)] + T_1[j][c1(r,j)] + T_2[j][c2(r,j)].
 //
-// MI355X mapping.  A workgroup owns one tile of 32 slices of one matrix and
-// streams all (or a block of) its rows.  Its 3 x 256 x 32 fp32 table (96 KB)
-// sits in LDS laid out [stage][code][lane]: lane l of a half-wave always
-// serves slice l, so its lookups hit LDS bank l whatever the code value and a
-// half-wave's 32 random lookups are bank-conflict free.  Each lane loads 16
-// code bytes per stage (16 rows of its slice) with one 16-byte load; a wave's
-// load is 1 KB contiguous.  The 16 per-lane row values are then summed across
-// the 32 slice lanes with a transposed butterfly (each step halves the values
-// held per lane), leaving one row total per lane pair.
+// MI355X mapping
+// --------------
+// * One workgroup (16 waves) per CU, as many as can be resident at once (LDS
+//   use allows one per CU).  The call's work is three phases of 32-row chunks:
+//     A  gate and up: (pair, matrix, 32-slice tile) segments x row chunks,
+//     B  down:        (pair, 32-slice tile of h) segments x row chunks,
+//     C  final sum of the down partials (+ residual) per token.
+//   Each phase's chunks are split into equal contiguous ranges, one per
+//   workgroup, so every CU streams the same number of code bytes.  A segment
+//   whose range is cut between two workgroups is built twice (its table) but
+//   read once (its codes).  Per-pair counters order A before B and per-token
+//   counters order B before C; the last workgroup out resets them.
+// * Table layout in LDS (128 KB), byte address for stage s, code c, lane l:
+//     s = 0: c*256 + 4l;   s = 1: c*256 + 128 + 4l;   s = 2: 65536 + c*256 + 4l.
+//   Lane l of each half-wave always serves slice l, so a half-wave's 32 random
+//   lookups hit 32 distinct banks whatever the codes (bank-conflict free), and
+//   one v_perm_b32 turns a packed code byte plus the lane base into the
+//   address.  The other half of each stage-2 row holds the staged codebook.
+// * Codes are read as 16-byte loads: lane (h, l) of a wave loads 16 rows of
+//   slice l for one stage; a wave load is 1 KB contiguous (internal layout
+//   of internal.hpp); the next chunk is prefetched while one is summed.
+// * The 16 per-lane row values are summed over the 32 slice lanes by a
+//   transposed butterfly: permlane16_swap for lane bit 4 (no selects), DPP
+//   row rotations for bits 3 and 2, quad permutes for bits 1 and 0.
+// * The SwiGLU finish h = silu(a) * b (the FFN reading of the layer) and the
+//   routing gate are applied while building the down table:
+//   table(g * h) = g * table(h), so phase C is a plain sum.
 #include <math.h>
 
 #include "internal.hpp"
@@ -29,8 +47,11 @@ namespace rvq {
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kBlock = 1024;  // threads per gather workgroup (16 waves)
-constexpr int kLutFloats = kStages * kCodes * kTileSlices;  // 24576 (96 KB)
+constexpr int kBlock = 1024;              // threads per workgroup (16 waves)
+constexpr int kWaves = kBlock / 64;
+constexpr int kLutWords = 32768;          // 128 KB
+constexpr int kStage2Word = 16384;        // byte 65536
+constexpr int kCbHalfWord = 32;           // codebook staging: words 32..63 of each stage-2 row
 
 // ---------------------------------------------------------------------------
 // Repack: canonical [rows][slices][3] per matrix -> tiled internal layout.
@@ -40,10 +61,10 @@ __global__ __launch_bounds__(256) void k_repack(const uint8_t *__restrict__ cano
     const int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (u >= total_units) return;
     const int64_t e = u / units_per_expert;
-    int64_t lu = u % units_per_expert;  // unit inside the internal record
+    int64_t lu = u % units_per_expert;
     int m = 0;
     int64_t canon_off = 0;
-    for (; m < 3; m++) {
+    for (; m < 2; m++) {
         const int64_t mu = g.m[m].bytes / 16;
         if (lu < mu) break;
         lu -= mu;
@@ -86,233 +107,617 @@ hipError_t launch_repack(const Geometry &g, const uint8_t *canon, uint8_t *inter
 }
 
 // ---------------------------------------------------------------------------
-// Codebook access: entry (stage s, code c) of matrix m of expert e, 8 values.
+// LDS helpers
+__device__ inline float lds_at(const float *lut, uint32_t byte_addr) {
+    return *reinterpret_cast<const float *>(reinterpret_cast<const char *>(lut) + byte_addr);
+}
+
+__device__ inline int lut_word(int s, int c, int l) {
+    return (s == 2 ? kStage2Word : 0) + c * 64 + (s == 1 ? 32 : 0) + l;
+}
+
+// Stage one matrix's codebook ([3][256][8] entries) into the free halves of the
+// stage-2 rows: entry idx (0..767) goes to row idx / R, slot idx % R, where a
+// 128-byte half row holds R = 128 / entry_bytes entries.  Split into a global
+// load into registers (issued one segment ahead) and an LDS store.
 template <int CB>
-__device__ inline void load_entry(const void *cbs, int64_t e, int m, int s, int c, float (&w)[8]) {
-    const int64_t idx = ((((e * 3 + m) * kStages + s) * kCodes) + c) * kVec;
-    if (CB == 0) {
-        const float4 *p = reinterpret_cast<const float4 *>(static_cast<const float *>(cbs) + idx);
-        const float4 a = p[0], b = p[1];
-        w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
-        w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
-    } else {
-        const uint4 q = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(cbs) + idx);
-        const uint32_t u[4] = {q.x, q.y, q.z, q.w};
+struct CbRegs {
+    static constexpr int kEntryBytes = CB == 0 ? 32 : 16;
+    static constexpr int kUnits = kStages * kCodes * kEntryBytes / 16;  // 16-byte units
+    static constexpr int kRegs = (kUnits + kBlock - 1) / kBlock;
+    uint4 r[kRegs];
+};
+
+template <int CB>
+__device__ inline void cb_load(CbRegs<CB> &cr, const void *cbs, int64_t e, int m) {
+    using C = CbRegs<CB>;
+    const uint4 *src = reinterpret_cast<const uint4 *>(static_cast<const char *>(cbs) +
+                                                       (e * 3 + m) * (int64_t)kStages * kCodes * C::kEntryBytes);
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
-            w[2 * i] = (float)__builtin_bit_cast(_Float16, (uint16_t)(u[i] & 0xffff));
-            w[2 * i + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(u[i] >> 16));
+    for (int k = 0; k < C::kRegs; k++) {
+        const int u = threadIdx.x + k * kBlock;
+        if (u < C::kUnits) cr.r[k] = src[u];
+    }
+}
+
+template <int CB>
+__device__ inline void cb_store(float *lut, const CbRegs<CB> &cr) {
+    using C = CbRegs<CB>;
+    constexpr int kPerRow = 128 / C::kEntryBytes;
+#pragma unroll
+    for (int k = 0; k < C::kRegs; k++) {
+        const int u = threadIdx.x + k * kBlock;
+        if (u < C::kUnits) {
+            const int entry = u / (C::kEntryBytes / 16), part = u % (C::kEntryBytes / 16);
+            const int row = entry / kPerRow, slot = entry % kPerRow;
+            uint4 *dst = reinterpret_cast<uint4 *>(lut + kStage2Word + row * 64 + kCbHalfWord) +
+                         slot * (C::kEntryBytes / 16) + part;
+            *dst = cr.r[k];
         }
     }
 }
 
-// Build the [stage][code][lane] table of one 32-slice tile in LDS.
-// vs[l][i] holds the 8 input values of slice (tile*32 + l) (zero past the end).
+// Build the table of one 32-slice tile on the matrix cores.  The table is the
+// product of the staged codebook C [768 codes x 8] with the slice inputs
+// vs [32 slices][8] taken as [8 x 32] -- an exact dense contraction -- done as
+// 24 blocks of 32 codes x 32 slices with v_mfma_f32_32x32x16_f16 (fp32
+// accumulation).  The fp32 inputs are split v = v_hi + v_lo into two fp16
+// parts fed as the two K halves (lanes 0-31 carry v_hi, lanes 32-63 v_lo,
+// against the same codebook entry), so one instruction forms C.v_hi + C.v_lo,
+// within ~2^-22 of C.v; fp16 codebooks are exact, fp32 codebooks get a second
+// pass with their own low part.  The inputs are first scaled by 2^-e2 so the
+// largest is near 2^14 (no fp16 overflow, negligible underflow) and the table
+// is scaled back by 2^e2, both exact.  Operand layout (wave64, verified):
+// element j of lane l pairs A[l % 32] with B column l % 32 within the lane
+// half l / 32; accumulator v of lane l is D[8 (v / 4) + 4 (l / 32) + v % 4][l % 32].
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
 template <int CB>
-__device__ inline void build_lut(float *lut, const float (*vs)[kVec], const void *cbs, int64_t e, int m) {
-    const int l = threadIdx.x & 31;
-    float xv[kVec];
+__device__ inline void build_lut(float *lut, const float (*vs)[kVec], int e2) {
+    constexpr int kEntryBytes = CB == 0 ? 32 : 16;
+    constexpr int kPerRow = 128 / kEntryBytes;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int j = lane & 31, kh = lane >> 5;
+    const float down = ldexpf(1.f, -e2), up = ldexpf(1.f, e2);
+    half8 bop;
 #pragma unroll
-    for (int i = 0; i < kVec; i++) xv[i] = vs[l][i];
-    for (int idx = threadIdx.x >> 5; idx < kStages * kCodes; idx += kBlock / 32) {
-        const int s = idx >> 8, c = idx & 255;
-        float w[8];
-        load_entry<CB>(cbs, e, m, s, c, w);
-        float acc = 0.f;
+    for (int i = 0; i < kVec; i++) {
+        const float v = vs[j][i] * down;
+        const _Float16 hi = (_Float16)v;
+        bop[i] = kh ? (_Float16)(v - (float)hi) : hi;
+    }
+    for (int mb = wave; mb < kStages * kCodes / 32; mb += kWaves) {
+        const int s = mb >> 3, c0 = (mb & 7) * 32;
+        const int idx = s * kCodes + c0 + j;
+        const char *p = reinterpret_cast<const char *>(lut + kStage2Word + (idx / kPerRow) * 64 + kCbHalfWord) +
+                        (idx % kPerRow) * kEntryBytes;
+        f32x16 acc = {};
+        if (CB == 1) {
+            const half8 aop = *reinterpret_cast<const half8 *>(p);
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(aop, bop, acc, 0, 0, 0);
+        } else {
+            const float4 w0 = reinterpret_cast<const float4 *>(p)[0], w1 = reinterpret_cast<const float4 *>(p)[1];
+            const float w[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+            half8 ahi, alo;
 #pragma unroll
-        for (int i = 0; i < kVec; i++) acc = fmaf(w[i], xv[i], acc);
-        lut[idx * kTileSlices + l] = acc;
+            for (int i = 0; i < kVec; i++) {
+                ahi[i] = (_Float16)w[i];
+                alo[i] = (_Float16)(w[i] - (float)ahi[i]);
+            }
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ahi, bop, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(alo, bop, acc, 0, 0, 0);
+        }
+#pragma unroll
+        for (int v = 0; v < 16; v++) {
+            const int c = c0 + 8 * (v >> 2) + 4 * kh + (v & 3);
+            lut[lut_word(s, c, j)] = acc[v] * up;
+        }
     }
 }
 
-__device__ inline uint32_t byte_of(const u32x4 &q, int i) {
-    const uint32_t w = (i < 4) ? q.x : (i < 8) ? q.y : (i < 12) ? q.z : q.w;
-    return (w >> (8 * (i & 3))) & 0xffu;
+// Exponent e2 with max|v| * 2^-e2 in [2^13, 2^14) over the tile's 256 inputs
+// (0 when all are zero or not finite).  The four waves that hold the inputs
+// (threads 0..255) each publish their maximum with tile_max_publish() before
+// the barrier that follows the vs stores; tile_exponent() reads the four
+// maxima after it, so the exponent costs no barrier of its own.
+__device__ __forceinline__ void tile_max_publish(float v, float *red2) {
+    float m = fabsf(v);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+    if ((threadIdx.x & 63) == 0) red2[threadIdx.x >> 6] = m;
 }
 
-// Gather one 32-row chunk: returns the row total held by this lane (valid on
-// even lanes of each half; row = chunk*32 + half*16 + (lane&31)/2).
-__device__ inline float gather_chunk(const float *lut, const uint8_t *blk, int lane) {
-    const u32x4 *p = reinterpret_cast<const u32x4 *>(blk) + lane;
-    const u32x4 q0 = __builtin_nontemporal_load(p);
-    const u32x4 q1 = __builtin_nontemporal_load(p + 64);
-    const u32x4 q2 = __builtin_nontemporal_load(p + 128);
-    const int l = lane & 31;
-    const float *t0 = lut + l;
-    const float *t1 = lut + kCodes * kTileSlices + l;
-    const float *t2 = lut + 2 * kCodes * kTileSlices + l;
+__device__ __forceinline__ int tile_exponent(const float *red2) {
+    const float m = fmaxf(fmaxf(red2[0], red2[1]), fmaxf(red2[2], red2[3]));
+    if (!(m > 0.f) || !isfinite(m)) return 0;
+    int ex;
+    frexpf(m, &ex);  // m = f * 2^ex, f in [0.5, 1)
+    return ex - 14;
+}
+
+// ---------------------------------------------------------------------------
+// Cross-lane helpers (wave64, DPP rows of 16 lanes).
+#define RVQ_DPP(v, ctrl) __uint_as_float(__builtin_amdgcn_update_dpp(0u, __float_as_uint(v), (ctrl), 0xF, 0xF, true))
+constexpr int kRor4 = 0x124, kRor8 = 0x128, kRor12 = 0x12C;
+constexpr int kQuadXor2 = 0x4E;  // quad_perm [2,3,0,1]
+constexpr int kQuadXor1 = 0xB1;  // quad_perm [1,0,3,2]
+
+// Sum 16 row values over the 32 slice lanes of each half-wave.  On return the
+// lane pair (2r, 2r+1) of a half holds the total of that half's row r.
+__device__ __forceinline__ float reduce16(float (&v)[16], int l) {
+    // lane bit 4: swap odd DPP rows of v[i] with even rows of v[i+8]
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+        auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v[i]), __float_as_uint(v[i + 8]), false, false);
+        v[i] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    }
+    // lane bit 3: partner l ^ 8 (row rotate by 8)
+    const bool b3 = l & 8, b2 = l & 4, b1 = l & 2;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        const float lo = v[i] + RVQ_DPP(v[i], kRor8);
+        const float hi = v[i + 4] + RVQ_DPP(v[i + 4], kRor8);
+        v[i] = b3 ? hi : lo;
+    }
+    // lane bit 2: partner l ^ 4 (rotate by 12 for bit2 = 0 lanes, by 4 otherwise)
+#pragma unroll
+    for (int i = 0; i < 2; i++) {
+        const float lo = v[i] + RVQ_DPP(v[i], kRor12);
+        const float hi = v[i + 2] + RVQ_DPP(v[i + 2], kRor4);
+        v[i] = b2 ? hi : lo;
+    }
+    // lane bit 1
+    {
+        const float lo = v[0] + RVQ_DPP(v[0], kQuadXor2);
+        const float hi = v[1] + RVQ_DPP(v[1], kQuadXor2);
+        v[0] = b1 ? hi : lo;
+    }
+    // lane bit 0
+    return v[0] + RVQ_DPP(v[0], kQuadXor1);
+}
+
+// Sum one 32-row chunk whose stage words are q0, q1, q2 (this lane's 16 rows).
+__device__ __forceinline__ float sum_chunk(const float *lut, const u32x4 &q0, const u32x4 &q1, const u32x4 &q2, int l) {
+    const uint32_t lb0 = 4u * l, lb1 = 128u + 4u * l, lb2 = 0x10000u + 4u * l;
     float v[16];
 #pragma unroll
     for (int i = 0; i < 16; i++) {
-        v[i] = t0[byte_of(q0, i) * kTileSlices] + t1[byte_of(q1, i) * kTileSlices] +
-               t2[byte_of(q2, i) * kTileSlices];
+        const uint32_t sel = 0x0C060004u | ((uint32_t)(i & 3) << 8);
+        const int w = i >> 2;
+        const uint32_t a0 = __builtin_amdgcn_perm(lb0, q0[w], sel);
+        const uint32_t a1 = __builtin_amdgcn_perm(lb1, q1[w], sel);
+        const uint32_t a2 = __builtin_amdgcn_perm(lb2, q2[w], sel);
+        v[i] = lds_at(lut, a0) + lds_at(lut, a1) + lds_at(lut, a2);
     }
-    // transposed butterfly over the 32 slice lanes of the half-wave
-#pragma unroll
-    for (int i = 0; i < 8; i++) {
-        const bool hi = l & 16;
-        const float send = hi ? v[i] : v[i + 8];
-        const float keep = hi ? v[i + 8] : v[i];
-        v[i] = keep + __shfl_xor(send, 16);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-        const bool hi = l & 8;
-        const float send = hi ? v[i] : v[i + 4];
-        const float keep = hi ? v[i + 4] : v[i];
-        v[i] = keep + __shfl_xor(send, 8);
-    }
-#pragma unroll
-    for (int i = 0; i < 2; i++) {
-        const bool hi = l & 4;
-        const float send = hi ? v[i] : v[i + 2];
-        const float keep = hi ? v[i + 2] : v[i];
-        v[i] = keep + __shfl_xor(send, 4);
-    }
-    {
-        const bool hi = l & 2;
-        const float send = hi ? v[0] : v[1];
-        const float keep = hi ? v[1] : v[0];
-        v[0] = keep + __shfl_xor(send, 2);
-    }
-    return v[0] + __shfl_xor(v[0], 1);
+    return reduce16(v, l);
 }
 
-// ---------------------------------------------------------------------------
-// Gate and up: grid (tile, matrix, pair).  Writes the tile's partial sums of
-// every row: part_gu[pair][m][tile][row].
-template <int CB>
-__global__ __launch_bounds__(kBlock) void k_gateup(const uint8_t *__restrict__ codes, const void *__restrict__ cbs,
-                                                   const float *__restrict__ x, const double *__restrict__ r,
-                                                   const int32_t *__restrict__ ids, Geometry g,
-                                                   float *__restrict__ part, int *__restrict__ err) {
-    __shared__ float lut[kLutFloats];
-    __shared__ float vs[kTileSlices][kVec];
-    const int tile = blockIdx.x, m = blockIdx.y, pair = blockIdx.z;
-    const int tok = pair / g.k;
-    const int e = ids[pair];
-    if (e < 0 || e >= g.E) {
-        if (threadIdx.x == 0) atomicOr(err, 1);
-        return;
+__device__ __forceinline__ void load_chunk(const uint8_t *blk, int lane, u32x4 &q0, u32x4 &q1, u32x4 &q2) {
+    const u32x4 *p = reinterpret_cast<const u32x4 *>(blk) + lane;
+    q0 = __builtin_nontemporal_load(p);
+    q1 = __builtin_nontemporal_load(p + 64);
+    q2 = __builtin_nontemporal_load(p + 128);
+}
+
+// Row totals of the chunks being gathered are staged in LDS, in the free
+// halves of the stage-2 rows (the codebook staging area, idle once the table is
+// built): chunk i of a sub-range owns piece i, 32 floats.  Keeping global
+// stores out of the gather loop keeps their completion off its critical path;
+// flush_rows() writes a whole sub-range with coalesced coherent stores.
+constexpr int kStagePieces = 256;  // chunks per sub-range (one piece per stage-2 row)
+
+__device__ __forceinline__ float *stage_piece(float *lut, int i) { return lut + kStage2Word + i * 64 + kCbHalfWord; }
+
+// Gather chunks [c0, c1) (c1 - c0 <= kStagePieces) of one tile, waves
+// round-robin.  The first chunk of this wave was already loaded into
+// (p0, p1, p2) by the caller.  Two register sets alternate (no copies between
+// them), and a scheduling barrier keeps each prefetch ahead of any use of the
+// chunk being summed, so the wait before summing one chunk leaves the next
+// chunk's three loads in flight (vmcnt completes in order).
+__device__ __forceinline__ void gather_range(float *lut, const uint8_t *tile_base, int c0, int c1, u32x4 p0,
+                                             u32x4 p1, u32x4 p2) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, l = lane & 31;
+    const int row_in = (lane >> 5) * 16 + (l >> 1);
+    int q = c0 + wave;
+    if (q >= c1) return;
+    u32x4 n0, n1, n2;
+    while (true) {
+        int qn = q + kWaves;
+        if (qn >= c1) {
+            const float sum = sum_chunk(lut, p0, p1, p2, l);
+            if (!(lane & 1)) stage_piece(lut, q - c0)[row_in] = sum;
+            return;
+        }
+        load_chunk(tile_base + (int64_t)qn * kChunkBytes, lane, n0, n1, n2);
+        __builtin_amdgcn_sched_barrier(0);  // issue the prefetch before any use of the current chunk
+        {
+            const float sum = sum_chunk(lut, p0, p1, p2, l);
+            if (!(lane & 1)) stage_piece(lut, q - c0)[row_in] = sum;
+        }
+        q = qn;
+        qn = q + kWaves;
+        if (qn >= c1) {
+            const float sum = sum_chunk(lut, n0, n1, n2, l);
+            if (!(lane & 1)) stage_piece(lut, q - c0)[row_in] = sum;
+            return;
+        }
+        load_chunk(tile_base + (int64_t)qn * kChunkBytes, lane, p0, p1, p2);
+        __builtin_amdgcn_sched_barrier(0);
+        {
+            const float sum = sum_chunk(lut, n0, n1, n2, l);
+            if (!(lane & 1)) stage_piece(lut, q - c0)[row_in] = sum;
+        }
+        q = qn;
     }
-    const MatGeom mg = g.m[m];
-    if (threadIdx.x < kTileSlices * kVec) {
-        const int col = tile * kTileSlices * kVec + threadIdx.x;
-        float v = 0.f;
-        if (col < g.d) v = (float)((double)x[(size_t)tok * g.d + col] / r[tok]);
-        vs[threadIdx.x / kVec][threadIdx.x % kVec] = v;
-    }
-    __syncthreads();
-    build_lut<CB>(lut, vs, cbs, e, m);
-    __syncthreads();
+}
+
+// Write the staged row totals of chunks [c0, c1) to out[c0*32 ..): all threads,
+// after a barrier; coherent stores, completed before the segment is signalled.
+__device__ __forceinline__ void flush_rows(float *lut, float *out, int c0, int c1) {
+    const int n = (c1 - c0) * kChunkRows;
+    for (int i = threadIdx.x; i < n; i += kBlock)
+        store_coherent(out + c0 * kChunkRows + i, stage_piece(lut, i / kChunkRows)[i % kChunkRows]);
+}
+
+// Whole segment: gather [c0, c1) in sub-ranges of at most kStagePieces chunks,
+// flushing each.  (p0, p1, p2) hold this wave's first chunk of the segment.
+__device__ __forceinline__ void gather_segment(float *lut, const uint8_t *tile_base, int c0, int c1, float *out,
+                                               u32x4 p0, u32x4 p1, u32x4 p2) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const uint8_t *base = codes + (int64_t)e * g.rec_int + mg.off + (int64_t)tile * mg.n_chunks * kChunkBytes;
-    float *out = part + (((int64_t)pair * 2 + m) * g.m[0].n_tiles + tile) * g.ffn_pad;
-    for (int q = wave; q < mg.n_chunks; q += kBlock / 64) {
-        const float sum = gather_chunk(lut, base + (int64_t)q * kChunkBytes, lane);
-        if (!(lane & 1)) out[q * kChunkRows + (lane >> 5) * 16 + ((lane & 31) >> 1)] = sum;
+    for (int s0 = c0; s0 < c1; s0 += kStagePieces) {
+        const int s1 = min(c1, s0 + kStagePieces);
+        if (s0 != c0 && s0 + wave < s1) load_chunk(tile_base + (int64_t)(s0 + wave) * kChunkBytes, lane, p0, p1, p2);
+        gather_range(lut, tile_base, s0, s1, p0, p1, p2);
+        __syncthreads();
+        flush_rows(lut, out, s0, s1);
+        __syncthreads();
     }
-}
-
-hipError_t launch_gateup(const Geometry &g, const Workspace &w, const uint8_t *codes, const void *cbs,
-                         const float *x, const int32_t *ids, int T, hipStream_t s) {
-    dim3 grid(g.m[0].n_tiles, 2, T * g.k);
-    if (g.cb_dtype == 0)
-        hipLaunchKernelGGL(k_gateup<0>, grid, dim3(kBlock), 0, s, codes, cbs, x, w.tok_r, ids, g, w.part_gu, w.err);
-    else
-        hipLaunchKernelGGL(k_gateup<1>, grid, dim3(kBlock), 0, s, codes, cbs, x, w.tok_r, ids, g, w.part_gu, w.err);
-    return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
-// Down: grid (ffn tile, row block, pair).  First finishes h for the tile's
-// 256 FFN entries, h = silu(a) * b with a, b the summed gate/up partials (the
-// SwiGLU reading of the expert FFN), then builds the table over h and gathers
-// the row block: part_dn[pair][tile][row].
-template <int CB>
-__global__ __launch_bounds__(kBlock) void k_down(const uint8_t *__restrict__ codes, const void *__restrict__ cbs,
-                                                 const int32_t *__restrict__ ids, Geometry g,
-                                                 const float *__restrict__ part_gu, float *__restrict__ part,
-                                                 int *__restrict__ err) {
-    __shared__ float lut[kLutFloats];
-    __shared__ float vs[kTileSlices][kVec];
-    const int tile = blockIdx.x, rb = blockIdx.y, pair = blockIdx.z;
-    const int e = ids[pair];
-    if (e < 0 || e >= g.E) {
-        if (threadIdx.x == 0) atomicOr(err, 1);
-        return;
+// Inter-workgroup ordering (all workgroups are resident together).
+__device__ inline void signal_add(int *cnt, int n) {
+    wait_stores();  // this wave's coherent partial-sum stores are complete
+    __syncthreads();
+    if (threadIdx.x == 0) atomicAdd(cnt, n);
+}
+
+// Wait until *cnt >= target (bounded: after ~0.5 s the error flag gets bit 2 and
+// the wait gives up, so every wave always reaches the end of the kernel).
+// Consumers read the published data with coherent loads after the barrier.
+__device__ inline void wait_count(const int *cnt, int target, int *err) {
+    if (threadIdx.x == 0) {
+        const uint64_t t0 = wall_clock64();
+        while (load_counter(cnt) < target) {
+            __builtin_amdgcn_s_sleep(2);
+            if (wall_clock64() - t0 > 50000000ull) {
+                atomicOr(err, 2);
+                break;
+            }
+        }
     }
-    const MatGeom mg = g.m[2];
-    const int nti = g.m[0].n_tiles;
-    if (threadIdx.x < kTileSlices * kVec) {
-        const int f = tile * kTileSlices * kVec + threadIdx.x;
+    __syncthreads();
+}
+
+// ---------------------------------------------------------------------------
+struct LayerArgs {
+    const uint8_t *codes;
+    const void *cbs;
+    const float *x;
+    const int32_t *ids;
+    const float *gates;
+    float *y;
+    float *part_gu;  // [P][2][n_ti][ffn_pad]
+    float *part_dn;  // [P][n_tf][d_pad]
+    int *cntA;       // [P]
+    int *cntB;       // [T]
+    int *done;
+    int *err;
+    Geometry g;
+    int T;
+    int pre;
+    int residual;
+    double eps;
+};
+
+// x_hat scale of token t: r = sqrt(mean(x^2) + eps) in fp64 (1 without
+// normalisation); cached per workgroup for the last token asked.
+__device__ inline double token_r(const LayerArgs &a, int t, int &r_tok, double &r_val, double *red) {
+    if (!a.pre) return 1.0;
+    if (r_tok == t) return r_val;
+    const float *xt = a.x + (size_t)t * a.g.d;
+    double ss = 0.0;
+    for (int i = threadIdx.x; i < a.g.d; i += kBlock) ss = fma((double)xt[i], (double)xt[i], ss);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+    __syncthreads();
+    double tot = 0.0;
+#pragma unroll
+    for (int w = 0; w < kWaves; w++) tot += red[w];
+    __syncthreads();
+    r_tok = t;
+    r_val = sqrt(tot / (double)a.g.d + a.eps);
+    return r_val;
+}
+
+// h' = gate * silu(a) * b for the 256 FFN entries of down tile ft of pair p,
+// where a and b are the gate and up row sums (sum over the input tiles' partial
+// sums).  Four threads per entry each add every fourth tile (up to 8 loads
+// per matrix in flight per thread), then the four partials meet in LDS.
+__device__ inline void finish_h(const LayerArgs &a, int p, int ft, float (*vs)[kVec], float (*hred)[256][2],
+                                float *red2) {
+    const Geometry &g = a.g;
+    const int n_ti = g.m[0].n_tiles;
+    const int fi = threadIdx.x & 255, part = threadIdx.x >> 8;
+    const int f = ft * kTileSlices * kVec + fi;
+    float sa = 0.f, sb = 0.f;
+    if (f < g.ffn) {
+        const float *pa = a.part_gu + ((int64_t)p * 2) * n_ti * g.ffn_pad + f;
+        const float *pb = pa + (int64_t)n_ti * g.ffn_pad;
+        for (int t0 = part; t0 < n_ti; t0 += 32) {
+            float va[8], vb[8];
+#pragma unroll
+            for (int j = 0; j < 8; j++) {
+                const int t = t0 + 4 * j;
+                va[j] = t < n_ti ? load_coherent(pa + (int64_t)t * g.ffn_pad) : 0.f;
+                vb[j] = t < n_ti ? load_coherent(pb + (int64_t)t * g.ffn_pad) : 0.f;
+            }
+#pragma unroll
+            for (int j = 0; j < 8; j++) {
+                sa += va[j];
+                sb += vb[j];
+            }
+        }
+    }
+    hred[part][fi][0] = sa;
+    hred[part][fi][1] = sb;
+    __syncthreads();
+    if (threadIdx.x < 256) {
         float hv = 0.f;
         if (f < g.ffn) {
-            const float *pa = part_gu + ((int64_t)pair * 2 + 0) * nti * g.ffn_pad + f;
-            const float *pb = part_gu + ((int64_t)pair * 2 + 1) * nti * g.ffn_pad + f;
-            float a = 0.f, b = 0.f;
-            for (int t = 0; t < nti; t++) {
-                a += pa[(int64_t)t * g.ffn_pad];
-                b += pb[(int64_t)t * g.ffn_pad];
-            }
-            hv = a / (1.f + expf(-a)) * b;
+            const float av = hred[0][fi][0] + hred[1][fi][0] + hred[2][fi][0] + hred[3][fi][0];
+            const float bv = hred[0][fi][1] + hred[1][fi][1] + hred[2][fi][1] + hred[3][fi][1];
+            hv = a.gates[p] * (av / (1.f + expf(-av)) * bv);
         }
-        vs[threadIdx.x / kVec][threadIdx.x % kVec] = hv;
+        vs[fi / kVec][fi % kVec] = hv;
+        tile_max_publish(hv, red2);
     }
-    __syncthreads();
-    build_lut<CB>(lut, vs, cbs, e, 2);
-    __syncthreads();
+}
+
+// A phase-A segment: chunks [c0, c1) of one (pair, matrix, tile); e = expert id.
+struct SegA {
+    int p, m, tile, c0, c1, e;
+};
+// A phase-B segment: chunks [c0, c1) of one (pair, ffn tile).
+struct SegB {
+    int p, ft, c0, c1, e;
+};
+
+// Expert ids of the pairs a workgroup touches, cached in LDS at kernel start so
+// that no segment start waits on a global load: pairs [base, base + n) of
+// phase A and of phase B (n <= kIdCache; beyond that, the global array).
+constexpr int kIdCache = 128;
+struct IdCache {
+    int a_base, a_n, b_base, b_n;
+    const int32_t *ids;
+    const int *lds;  // [2][kIdCache]
+    __device__ int a(int p) const { return (p - a_base) < a_n ? lds[p - a_base] : ids[p]; }
+    __device__ int b(int p) const { return (p - b_base) < b_n ? lds[kIdCache + p - b_base] : ids[p]; }
+};
+
+__device__ inline SegA seg_a(int64_t u, int64_t u1, int n_ti, int n_cf, const IdCache &ic) {
+    SegA s;
+    const int64_t seg = u / n_cf;
+    s.c0 = (int)(u % n_cf);
+    s.c1 = (int)min((int64_t)n_cf, s.c0 + (u1 - u));
+    s.tile = (int)(seg % n_ti);
+    s.m = (int)((seg / n_ti) & 1);
+    s.p = (int)(seg / (2 * n_ti));
+    s.e = ic.a(s.p);
+    return s;
+}
+
+__device__ inline SegB seg_b(int64_t u, int64_t u1, int n_tf, int n_cd, const IdCache &ic) {
+    SegB s;
+    const int64_t seg = u / n_cd;
+    s.c0 = (int)(u % n_cd);
+    s.c1 = (int)min((int64_t)n_cd, s.c0 + (u1 - u));
+    s.ft = (int)(seg % n_tf);
+    s.p = (int)(seg / n_tf);
+    s.e = ic.b(s.p);
+    return s;
+}
+
+template <int CB>
+__global__ __launch_bounds__(kBlock) void k_layer(LayerArgs a) {
+    __shared__ float lut[kLutWords];
+    __shared__ float vs[kTileSlices][kVec];
+    __shared__ double red[kWaves];
+    __shared__ float csum[kWaves][64];
+    __shared__ float hred[4][256][2];
+    __shared__ float red2[kWaves];
+    const Geometry &g = a.g;
+    const int G = gridDim.x, wg = blockIdx.x;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const uint8_t *base = codes + (int64_t)e * g.rec_int + mg.off + (int64_t)tile * mg.n_chunks * kChunkBytes;
-    float *out = part + ((int64_t)pair * mg.n_tiles + tile) * g.d_pad;
-    const int q0 = rb * g.down_row_block;
-    const int q1 = min(mg.n_chunks, q0 + g.down_row_block);
-    for (int q = q0 + wave; q < q1; q += kBlock / 64) {
-        const float sum = gather_chunk(lut, base + (int64_t)q * kChunkBytes, lane);
-        if (!(lane & 1)) out[q * kChunkRows + (lane >> 5) * 16 + ((lane & 31) >> 1)] = sum;
+    const int P = a.T * g.k;
+    const int n_ti = g.m[0].n_tiles, n_cf = g.m[0].n_chunks;
+    const int n_tf = g.m[2].n_tiles, n_cd = g.m[2].n_chunks;
+    int r_tok = -1;
+    double r_val = 1.0;
+    CbRegs<CB> cb;
+    __shared__ int id_lds[2 * kIdCache];
+    IdCache ic;
+    {
+        const int64_t nA = (int64_t)P * 2 * n_ti * n_cf, nB = (int64_t)P * n_tf * n_cd;
+        const int64_t a0 = nA * wg / G, a1 = nA * (wg + 1) / G, b0 = nB * wg / G, b1 = nB * (wg + 1) / G;
+        ic.ids = a.ids;
+        ic.lds = id_lds;
+        ic.a_base = (int)(a0 / n_cf / (2 * n_ti));
+        ic.a_n = a1 > a0 ? min(kIdCache, (int)((a1 - 1) / n_cf / (2 * n_ti)) - ic.a_base + 1) : 0;
+        ic.b_base = (int)(b0 / n_cd / n_tf);
+        ic.b_n = b1 > b0 ? min(kIdCache, (int)((b1 - 1) / n_cd / n_tf) - ic.b_base + 1) : 0;
+        if (threadIdx.x < ic.a_n) id_lds[threadIdx.x] = a.ids[ic.a_base + threadIdx.x];
+        if (threadIdx.x < ic.b_n) id_lds[kIdCache + threadIdx.x] = a.ids[ic.b_base + threadIdx.x];
+        __syncthreads();
+    }
+
+    // ---------------- phase A: gate and up
+    {
+        const int64_t nA = (int64_t)P * 2 * n_ti * n_cf;
+        int64_t u = nA * wg / G;
+        const int64_t u1 = nA * (wg + 1) / G;
+        float xv = 0.f;  // this thread's raw input element of the segment's tile
+        auto prefetch = [&](const SegA &sg) {
+            if (sg.e >= 0 && sg.e < g.E) cb_load<CB>(cb, a.cbs, sg.e, sg.m);
+            const int col = sg.tile * kTileSlices * kVec + threadIdx.x;
+            xv = (threadIdx.x < kTileSlices * kVec && col < g.d) ? a.x[(size_t)(sg.p / g.k) * g.d + col] : 0.f;
+        };
+        SegA cur{};
+        if (u < u1) {
+            cur = seg_a(u, u1, n_ti, n_cf, ic);
+            prefetch(cur);
+        }
+        while (u < u1) {
+            const int64_t un = u + (cur.c1 - cur.c0);
+            SegA nxt{};
+            if (un < u1) nxt = seg_a(un, u1, n_ti, n_cf, ic);
+            if (cur.e >= 0 && cur.e < g.E) {
+                const uint8_t *base = a.codes + (int64_t)cur.e * g.rec_int + g.m[cur.m].off +
+                                      (int64_t)cur.tile * n_cf * kChunkBytes;
+                // consume the prefetched codebook and inputs first, so that waiting
+                // for them does not also wait for the code loads issued below
+                const double r = token_r(a, cur.p / g.k, r_tok, r_val, red);
+                cb_store<CB>(lut, cb);
+                if (threadIdx.x < kTileSlices * kVec) {
+                    const float v = a.pre ? (float)((double)xv / r) : xv;
+                    vs[threadIdx.x / kVec][threadIdx.x % kVec] = v;
+                    tile_max_publish(v, red2);
+                }
+                u32x4 p0, p1, p2;
+                if (cur.c0 + wave < cur.c1)
+                    load_chunk(base + (int64_t)(cur.c0 + wave) * kChunkBytes, lane, p0, p1, p2);
+                __syncthreads();
+                build_lut<CB>(lut, vs, tile_exponent(red2));
+                __syncthreads();
+                if (un < u1) prefetch(nxt);
+                float *out = a.part_gu + (((int64_t)cur.p * 2 + cur.m) * n_ti + cur.tile) * g.ffn_pad;
+                gather_segment(lut, base, cur.c0, cur.c1, out, p0, p1, p2);
+            } else {
+                if (threadIdx.x == 0) atomicOr(a.err, 1);
+                if (un < u1) prefetch(nxt);
+            }
+            signal_add(&a.cntA[cur.p], cur.c1 - cur.c0);
+            cur = nxt;
+            u = un;
+        }
+    }
+
+    // ---------------- phase B: SwiGLU finish, gate, down
+    {
+        const int64_t nB = (int64_t)P * n_tf * n_cd;
+        int64_t u = nB * wg / G;
+        const int64_t u1 = nB * (wg + 1) / G;
+        const int needA = 2 * n_ti * n_cf;
+        SegB cur{};
+        if (u < u1) {
+            cur = seg_b(u, u1, n_tf, n_cd, ic);
+            if (cur.e >= 0 && cur.e < g.E) cb_load<CB>(cb, a.cbs, cur.e, 2);
+        }
+        while (u < u1) {
+            const int64_t un = u + (cur.c1 - cur.c0);
+            SegB nxt{};
+            if (un < u1) nxt = seg_b(un, u1, n_tf, n_cd, ic);
+            if (cur.e >= 0 && cur.e < g.E) {
+                const uint8_t *base = a.codes + (int64_t)cur.e * g.rec_int + g.m[2].off +
+                                      (int64_t)cur.ft * n_cd * kChunkBytes;
+                cb_store<CB>(lut, cb);
+                u32x4 p0, p1, p2;
+                if (cur.c0 + wave < cur.c1)
+                    load_chunk(base + (int64_t)(cur.c0 + wave) * kChunkBytes, lane, p0, p1, p2);
+                wait_count(&a.cntA[cur.p], needA, a.err);
+                finish_h(a, cur.p, cur.ft, vs, hred, red2);
+                __syncthreads();
+                build_lut<CB>(lut, vs, tile_exponent(red2));
+                __syncthreads();
+                if (un < u1 && nxt.e >= 0 && nxt.e < g.E) cb_load<CB>(cb, a.cbs, nxt.e, 2);
+                float *out = a.part_dn + ((int64_t)cur.p * n_tf + cur.ft) * g.d_pad;
+                gather_segment(lut, base, cur.c0, cur.c1, out, p0, p1, p2);
+            } else if (un < u1 && nxt.e >= 0 && nxt.e < g.E) {
+                cb_load<CB>(cb, a.cbs, nxt.e, 2);
+            }
+            signal_add(&a.cntB[cur.p / g.k], cur.c1 - cur.c0);
+            cur = nxt;
+            u = un;
+        }
+    }
+
+    // ---------------- phase C: y[t][q] = sum over the token's pairs and down tiles (+ x)
+    {
+        const int rb_n = (g.d + 63) / 64;
+        const int64_t nC = (int64_t)a.T * rb_n;
+        const int needB = g.k * n_tf * n_cd;
+        for (int64_t u = nC * wg / G; u < nC * (wg + 1) / G; u++) {
+            const int t = (int)(u / rb_n);
+            const int q = (int)(u % rb_n) * 64 + lane;
+            wait_count(&a.cntB[t], needB, a.err);
+            float s = 0.f;
+            bool bad = false;
+            const int n_terms = g.k * n_tf;
+            for (int j = wave; j < n_terms; j += kWaves) {
+                const int p = t * g.k + j / n_tf;
+                const int ft = j % n_tf;
+                if (q < g.d) s += load_coherent(a.part_dn + ((int64_t)p * n_tf + ft) * g.d_pad + q);
+            }
+            csum[wave][lane] = s;
+            __syncthreads();
+            if (wave == 0 && q < g.d) {
+                float tot = 0.f;
+#pragma unroll
+                for (int w = 0; w < kWaves; w++) tot += csum[w][lane];
+                for (int j = 0; j < g.k; j++) {
+                    const int e = a.ids[t * g.k + j];
+                    bad |= (e < 0 || e >= g.E);
+                }
+                if (a.residual) tot += a.x[(size_t)t * g.d + q];
+                a.y[(size_t)t * g.d + q] = bad ? __int_as_float(0x7fc00000) : tot;
+            }
+            __syncthreads();
+        }
+    }
+
+    // ---------------- the last workgroup out resets the counters for the next call
+    __shared__ int last;
+    __syncthreads();
+    if (threadIdx.x == 0) last = (atomicAdd(a.done, 1) == G - 1);
+    __syncthreads();
+    if (last) {
+        for (int i = threadIdx.x; i < P; i += kBlock) store_counter(a.cntA + i, 0);
+        for (int i = threadIdx.x; i < a.T; i += kBlock) store_counter(a.cntB + i, 0);
+        if (threadIdx.x == 0) store_counter(a.done, 0);
     }
 }
 
-hipError_t launch_down(const Geometry &g, const Workspace &w, const uint8_t *codes, const void *cbs,
-                       const int32_t *ids, int T, hipStream_t s) {
-    dim3 grid(g.m[2].n_tiles, g.n_down_rb, T * g.k);
+hipError_t launch_layer(const Geometry &g, const Workspace &w, const uint8_t *codes, const void *cbs,
+                        const float *x, const int32_t *ids, const float *gates, float *y, int T, int pre,
+                        int residual, double eps, hipStream_t s) {
+    LayerArgs a{codes, cbs, x, ids, gates, y, w.part_gu, w.part_dn, w.cntA, w.cntB, w.done, w.err, g, T, pre,
+                residual, eps};
+    // A plain launch of exactly as many workgroups as can be resident at once
+    // (sized at open from the occupancy query); the inter-workgroup waits are
+    // bounded, so a launch that somehow did not get all of them resident ends
+    // with an error flag instead of hanging.
     if (g.cb_dtype == 0)
-        hipLaunchKernelGGL(k_down<0>, grid, dim3(kBlock), 0, s, codes, cbs, ids, g, w.part_gu, w.part_dn, w.err);
+        hipLaunchKernelGGL(k_layer<0>, dim3(w.n_wg), dim3(kBlock), 0, s, a);
     else
-        hipLaunchKernelGGL(k_down<1>, grid, dim3(kBlock), 0, s, codes, cbs, ids, g, w.part_gu, w.part_dn, w.err);
+        hipLaunchKernelGGL(k_layer<1>, dim3(w.n_wg), dim3(kBlock), 0, s, a);
     return hipGetLastError();
 }
 
-// ---------------------------------------------------------------------------
-// Combine: y[t][q] = sum_j gates[t][j] * y_j[q] (+ x[t][q]), y_j the summed
-// down partials of pair (t, j), j ascending.
-__global__ __launch_bounds__(256) void k_combine(const float *__restrict__ part, const float *__restrict__ x,
-                                                 const int32_t *__restrict__ ids, const float *__restrict__ gates,
-                                                 Geometry g, int residual, float *__restrict__ y) {
-    const int q = blockIdx.x * 256 + threadIdx.x;
-    const int t = blockIdx.y;
-    if (q >= g.d) return;
-    const int ntf = g.m[2].n_tiles;
-    float acc = 0.f;
-    bool bad = false;
-    for (int j = 0; j < g.k; j++) {
-        const int pair = t * g.k + j;
-        const int e = ids[pair];
-        bad |= (e < 0 || e >= g.E);
-        const float *p = part + (int64_t)pair * ntf * g.d_pad + q;
-        float yj = 0.f;
-        for (int tt = 0; tt < ntf; tt++) yj += p[(int64_t)tt * g.d_pad];
-        acc = fmaf(gates[pair], yj, acc);
-    }
-    if (residual) acc += x[(size_t)t * g.d + q];
-    y[(size_t)t * g.d + q] = bad ? __int_as_float(0x7fc00000) : acc;
-}
-
-hipError_t launch_combine(const Geometry &g, const Workspace &w, const float *x, const int32_t *ids,
-                          const float *gates, float *y, int T, int residual, hipStream_t s) {
-    dim3 grid((g.d + 255) / 256, T);
-    hipLaunchKernelGGL(k_combine, grid, dim3(256), 0, s, w.part_dn, x, ids, gates, g, residual, y);
-    return hipGetLastError();
+hipError_t layer_blocks_per_cu(int cb_dtype, int *out) {
+    return cb_dtype == 0 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(out, k_layer<0>, kBlock, 0)
+                         : hipOccupancyMaxActiveBlocksPerMultiprocessor(out, k_layer<1>, kBlock, 0);
 }
 
 }  // namespace rvq

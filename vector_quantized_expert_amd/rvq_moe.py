@@ -21,7 +21,7 @@ OK, EINVAL, ENOTSUP, EBUDGET, ENOMEM, EHIP, EDEVICE = 0, -1, -2, -3, -4, -5, -6
 STATUS_NAMES = {0: "OK", -1: "EINVAL", -2: "ENOTSUP", -3: "EBUDGET", -4: "ENOMEM", -5: "EHIP", -6: "EDEVICE"}
 CB_F32, CB_F16 = 0, 1
 CODES_DEVICE, CODES_PINNED_HOST = 0, 1
-KERNEL_KINDS = 5
+KERNEL_KINDS = 2
 
 
 class RvqMoeError(RuntimeError):
