@@ -97,17 +97,20 @@ def test_tiny_layer_64_tokens(torch_mod, tiny):
     layer.close()
 
 
-def test_tiny_per_token_calls_equal_batched_call_bitwise(torch_mod, tiny):
+def test_tiny_per_token_calls_match_batched_call(torch_mod, tiny):
+    """Ids and gates are bitwise identical whether tokens come one per call or
+    all in one call, and across repeated calls.  Outputs are accumulated with
+    fp32 atomics (summation order varies), so they agree to 1e-6 relative."""
     shape = S.TINY
     layer = _layer(torch_mod, tiny, shape, 16)
     x = S.tokens(0, 100, 16, shape.d)
     a = _run(torch_mod, layer, shape, x)
     b = _run(torch_mod, layer, shape, x, per_token=True)
-    for u, v in zip(a, b):
-        assert np.array_equal(u, v)
-    c = _run(torch_mod, layer, shape, x)  # determinism: same input, same bits
-    for u, v in zip(a, c):
-        assert np.array_equal(u, v)
+    c = _run(torch_mod, layer, shape, x)
+    for other in (b, c):
+        assert np.array_equal(a[0], other[0]) and np.array_equal(a[1], other[1])
+        err = np.linalg.norm(a[2] - other[2], axis=1) / np.linalg.norm(a[2], axis=1)
+        assert err.max() <= 1e-6, err.max()
     layer.close()
 
 

@@ -94,9 +94,8 @@ static void free_handle(rvq_moe *h) {
     (void)hipFree(h->ws.logits);
     (void)hipFree(h->ws.sel);
     (void)hipFree(h->ws.part_gu);
-    (void)hipFree(h->ws.part_dn);
     (void)hipFree(h->ws.cntA);
-    (void)hipFree(h->ws.cntB);
+    (void)hipFree(h->ws.yinit);
     (void)hipFree(h->ws.done);
     (void)hipFree(h->ws.err);
     for (hipEvent_t e : h->prof_pool) (void)hipEventDestroy(e);
@@ -131,9 +130,8 @@ static int open_impl(const rvq_moe_desc *desc, rvq_moe *h) {
     HIP_TRY(hipMalloc(&h->ws.logits, sizeof(double) * (size_t)(T * E)));
     HIP_TRY(hipMalloc(&h->ws.sel, sizeof(double) * (size_t)(T * D.top_k)));
     HIP_TRY(hipMalloc(&h->ws.part_gu, sizeof(float) * (size_t)(P * 2 * g.m[0].n_tiles * g.ffn_pad)));
-    HIP_TRY(hipMalloc(&h->ws.part_dn, sizeof(float) * (size_t)(P * g.m[2].n_tiles * g.d_pad)));
     HIP_TRY(hipMalloc(&h->ws.cntA, sizeof(int) * (size_t)P));
-    HIP_TRY(hipMalloc(&h->ws.cntB, sizeof(int) * (size_t)T));
+    HIP_TRY(hipMalloc(&h->ws.yinit, sizeof(int)));
     HIP_TRY(hipMalloc(&h->ws.done, sizeof(int)));
     HIP_TRY(hipMalloc(&h->ws.err, sizeof(int)));
     int n_cu = 0;
@@ -143,7 +141,7 @@ static int open_impl(const rvq_moe_desc *desc, rvq_moe *h) {
     if (n_cu < 1 || per_cu < 1) return fail(RVQ_MOE_EHIP, "occupancy query gave %d CUs x %d blocks", n_cu, per_cu);
     h->ws.n_wg = n_cu * per_cu;
     HIP_TRY(hipMemsetAsync(h->ws.cntA, 0, sizeof(int) * (size_t)P, s));
-    HIP_TRY(hipMemsetAsync(h->ws.cntB, 0, sizeof(int) * (size_t)T, s));
+    HIP_TRY(hipMemsetAsync(h->ws.yinit, 0, sizeof(int), s));
     HIP_TRY(hipMemsetAsync(h->ws.done, 0, sizeof(int), s));
     HIP_TRY(hipMemsetAsync(h->ws.err, 0, sizeof(int), s));
     HIP_TRY(hipMemcpyAsync(h->cbs, D.codebooks, (size_t)(E * g.cb_bytes), hipMemcpyDeviceToDevice, s));

@@ -85,9 +85,8 @@ struct Workspace {
     double *logits;     // [T][E] fp64 router logits
     double *sel;        // [T][k] fp64 logits of the selected experts, by rank
     float *part_gu;     // [T*k][2][n_tiles_in][ffn_pad] partial gate/up sums
-    float *part_dn;     // [T*k][n_tiles_ffn][d_pad] partial down sums (gate-weighted)
     int *cntA;          // [T*k] finished gate/up chunks per pair (self-resetting)
-    int *cntB;          // [T] finished down chunks per token (self-resetting)
+    int *yinit;         // workgroups that initialised their slice of y (self-resetting)
     int *done;          // workgroups finished (self-resetting)
     int *err;           // device error flag: bit 0 bad id, bit 1 wait timeout
     int n_wg;           // persistent workgroups (all resident at once: blocks per CU x CUs)

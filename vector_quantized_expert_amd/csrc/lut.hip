@@ -360,17 +360,32 @@ __device__ __forceinline__ void flush_rows(float *lut, float *out, int c0, int c
         store_coherent(out + c0 * kChunkRows + i, stage_piece(lut, i / kChunkRows)[i % kChunkRows]);
 }
 
+// Add the staged row totals of chunks [c0, c1) into out[row] (rows < n_rows)
+// with device-scope fp32 atomics (the hardware global_atomic_add_f32).
+__device__ __forceinline__ void flush_rows_add(float *lut, float *out, int c0, int c1, int n_rows) {
+    const int n = (c1 - c0) * kChunkRows;
+    for (int i = threadIdx.x; i < n; i += kBlock) {
+        const int row = c0 * kChunkRows + i;
+        if (row < n_rows) unsafeAtomicAdd(out + row, stage_piece(lut, i / kChunkRows)[i % kChunkRows]);
+    }
+}
+
 // Whole segment: gather [c0, c1) in sub-ranges of at most kStagePieces chunks,
 // flushing each.  (p0, p1, p2) hold this wave's first chunk of the segment.
+// (p0, p1, p2) hold this wave's first chunk of the segment.
+template <bool kAdd>
 __device__ __forceinline__ void gather_segment(float *lut, const uint8_t *tile_base, int c0, int c1, float *out,
-                                               u32x4 p0, u32x4 p1, u32x4 p2) {
+                                               int n_rows, u32x4 p0, u32x4 p1, u32x4 p2) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     for (int s0 = c0; s0 < c1; s0 += kStagePieces) {
         const int s1 = min(c1, s0 + kStagePieces);
         if (s0 != c0 && s0 + wave < s1) load_chunk(tile_base + (int64_t)(s0 + wave) * kChunkBytes, lane, p0, p1, p2);
         gather_range(lut, tile_base, s0, s1, p0, p1, p2);
         __syncthreads();
-        flush_rows(lut, out, s0, s1);
+        if (kAdd)
+            flush_rows_add(lut, out, s0, s1, n_rows);
+        else
+            flush_rows(lut, out, s0, s1);
         __syncthreads();
     }
 }
@@ -409,9 +424,8 @@ struct LayerArgs {
     const float *gates;
     float *y;
     float *part_gu;  // [P][2][n_ti][ffn_pad]
-    float *part_dn;  // [P][n_tf][d_pad]
     int *cntA;       // [P]
-    int *cntB;       // [T]
+    int *yinit;      // workgroups that initialised their slice of y
     int *done;
     int *err;
     Geometry g;
@@ -535,7 +549,6 @@ __global__ __launch_bounds__(kBlock) void k_layer(LayerArgs a) {
     __shared__ float lut[kLutWords];
     __shared__ float vs[kTileSlices][kVec];
     __shared__ double red[kWaves];
-    __shared__ float csum[kWaves][64];
     __shared__ float hred[4][256][2];
     __shared__ float red2[kWaves];
     const Geometry &g = a.g;
@@ -562,6 +575,15 @@ __global__ __launch_bounds__(kBlock) void k_layer(LayerArgs a) {
         if (threadIdx.x < ic.b_n) id_lds[kIdCache + threadIdx.x] = a.ids[ic.b_base + threadIdx.x];
         __syncthreads();
     }
+
+    // ---------------- y starts as 0 (or x with the residual); phase B adds into it
+    {
+        const int64_t n = (int64_t)a.T * g.d;
+        for (int64_t i = n * wg / G + threadIdx.x; i < n * (wg + 1) / G; i += kBlock)
+            store_coherent(a.y + i, a.residual ? a.x[i] : 0.f);
+        signal_add(a.yinit, 1);
+    }
+    bool y_ready = false;
 
     // ---------------- phase A: gate and up
     {
@@ -603,7 +625,7 @@ __global__ __launch_bounds__(kBlock) void k_layer(LayerArgs a) {
                 __syncthreads();
                 if (un < u1) prefetch(nxt);
                 float *out = a.part_gu + (((int64_t)cur.p * 2 + cur.m) * n_ti + cur.tile) * g.ffn_pad;
-                gather_segment(lut, base, cur.c0, cur.c1, out, p0, p1, p2);
+                gather_segment<false>(lut, base, cur.c0, cur.c1, out, 0, p0, p1, p2);
             } else {
                 if (threadIdx.x == 0) atomicOr(a.err, 1);
                 if (un < u1) prefetch(nxt);
@@ -642,48 +664,25 @@ __global__ __launch_bounds__(kBlock) void k_layer(LayerArgs a) {
                 build_lut<CB>(lut, vs, tile_exponent(red2));
                 __syncthreads();
                 if (un < u1 && nxt.e >= 0 && nxt.e < g.E) cb_load<CB>(cb, a.cbs, nxt.e, 2);
-                float *out = a.part_dn + ((int64_t)cur.p * n_tf + cur.ft) * g.d_pad;
-                gather_segment(lut, base, cur.c0, cur.c1, out, p0, p1, p2);
-            } else if (un < u1 && nxt.e >= 0 && nxt.e < g.E) {
-                cb_load<CB>(cb, a.cbs, nxt.e, 2);
+                if (!y_ready) {
+                    wait_count(a.yinit, G, a.err);
+                    y_ready = true;
+                }
+                gather_segment<true>(lut, base, cur.c0, cur.c1, a.y + (size_t)(cur.p / g.k) * g.d, g.d, p0, p1, p2);
+            } else {
+                // an invalid id poisons its token's output (the error flag is already set)
+                if (!y_ready) {
+                    wait_count(a.yinit, G, a.err);
+                    y_ready = true;
+                }
+                if (cur.ft == 0)
+                    for (int r = cur.c0 * kChunkRows + threadIdx.x; r < min(g.d, cur.c1 * kChunkRows); r += kBlock)
+                        unsafeAtomicAdd(a.y + (size_t)(cur.p / g.k) * g.d + r, __int_as_float(0x7fc00000));
+                if (un < u1 && nxt.e >= 0 && nxt.e < g.E) cb_load<CB>(cb, a.cbs, nxt.e, 2);
             }
-            signal_add(&a.cntB[cur.p / g.k], cur.c1 - cur.c0);
+            __syncthreads();
             cur = nxt;
             u = un;
-        }
-    }
-
-    // ---------------- phase C: y[t][q] = sum over the token's pairs and down tiles (+ x)
-    {
-        const int rb_n = (g.d + 63) / 64;
-        const int64_t nC = (int64_t)a.T * rb_n;
-        const int needB = g.k * n_tf * n_cd;
-        for (int64_t u = nC * wg / G; u < nC * (wg + 1) / G; u++) {
-            const int t = (int)(u / rb_n);
-            const int q = (int)(u % rb_n) * 64 + lane;
-            wait_count(&a.cntB[t], needB, a.err);
-            float s = 0.f;
-            bool bad = false;
-            const int n_terms = g.k * n_tf;
-            for (int j = wave; j < n_terms; j += kWaves) {
-                const int p = t * g.k + j / n_tf;
-                const int ft = j % n_tf;
-                if (q < g.d) s += load_coherent(a.part_dn + ((int64_t)p * n_tf + ft) * g.d_pad + q);
-            }
-            csum[wave][lane] = s;
-            __syncthreads();
-            if (wave == 0 && q < g.d) {
-                float tot = 0.f;
-#pragma unroll
-                for (int w = 0; w < kWaves; w++) tot += csum[w][lane];
-                for (int j = 0; j < g.k; j++) {
-                    const int e = a.ids[t * g.k + j];
-                    bad |= (e < 0 || e >= g.E);
-                }
-                if (a.residual) tot += a.x[(size_t)t * g.d + q];
-                a.y[(size_t)t * g.d + q] = bad ? __int_as_float(0x7fc00000) : tot;
-            }
-            __syncthreads();
         }
     }
 
@@ -694,15 +693,17 @@ __global__ __launch_bounds__(kBlock) void k_layer(LayerArgs a) {
     __syncthreads();
     if (last) {
         for (int i = threadIdx.x; i < P; i += kBlock) store_counter(a.cntA + i, 0);
-        for (int i = threadIdx.x; i < a.T; i += kBlock) store_counter(a.cntB + i, 0);
-        if (threadIdx.x == 0) store_counter(a.done, 0);
+        if (threadIdx.x == 0) {
+            store_counter(a.yinit, 0);
+            store_counter(a.done, 0);
+        }
     }
 }
 
 hipError_t launch_layer(const Geometry &g, const Workspace &w, const uint8_t *codes, const void *cbs,
                         const float *x, const int32_t *ids, const float *gates, float *y, int T, int pre,
                         int residual, double eps, hipStream_t s) {
-    LayerArgs a{codes, cbs, x, ids, gates, y, w.part_gu, w.part_dn, w.cntA, w.cntB, w.done, w.err, g, T, pre,
+    LayerArgs a{codes, cbs, x, ids, gates, y, w.part_gu, w.cntA, w.yinit, w.done, w.err, g, T, pre,
                 residual, eps};
     // A plain launch of exactly as many workgroups as can be resident at once
     // (sized at open from the occupancy query); the inter-workgroup waits are
