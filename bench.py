@@ -38,6 +38,9 @@ def main():
     ap.add_argument("--cpu-tokens", type=int, default=2, help="tokens the oracle baseline runs (0: skip)")
     ap.add_argument("--profile-every", type=int, default=8, help="time kernels with events every n-th call")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--path", choices=("fused", "two-call"), default="two-call",
+                    help="fused: rvq_moe_route_forward (one launch per token); "
+                         "two-call: rvq_moe_route_topk then rvq_moe_layer_forward")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -71,9 +74,14 @@ def main():
     y = torch.empty((n_tok, shape.d), dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream()
 
-    def step(t):
+    def step_two(t):
         layer.route_topk(x[t], 1, ids[t], gates[t], stream)
         layer.layer_forward(x[t], 1, ids[t], gates[t], y[t], stream)
+
+    def step_fused(t):
+        layer.route_forward(x[t], 1, ids[t], gates[t], y[t], stream)
+
+    step = step_fused if args.path == "fused" else step_two
 
     print(f"[bench] warmup {W} tokens", file=sys.stderr, flush=True)
     for t in range(W):
@@ -103,7 +111,7 @@ def main():
 
     # Dominant kernel: the persistent LUT kernel of layer_forward.  Algorithmic
     # bytes per launch (T = 1) = k experts x (code record + 3 matrices' codebooks).
-    n_l, l_ms = ktimes["layer_lut"]
+    n_l, l_ms = ktimes["route_layer_lut" if args.path == "fused" else "layer_lut"]
     l_avg_us = l_ms / max(n_l, 1) * 1e3
     l_gbps = per_token_bytes / (l_avg_us * 1e-6) / 1e9
     kernels = {k: {"launches": int(n), "avg_us": (v / n * 1e3 if n else None)} for k, (n, v) in ktimes.items()}
@@ -143,12 +151,15 @@ def main():
         "data": "synthetic",
         "config": {"workload": "K3-scale routed RVQ-MoE layer, batch-1 decode: d=7168 ffn=2048 E=384 top-16, "
                                "3-stage x 256 x 8 fp16 codebooks, uniform u8 codes, T=1 per call",
-                   "global_batch": 1, "tokens": K},
+                   "global_batch": 1, "tokens": K,
+                   "path": "rvq_moe_route_forward" if args.path == "fused"
+                   else "rvq_moe_route_topk + rvq_moe_layer_forward"},
         "compressed_GBps": gbps,
         "hbm_frac": gbps / HBM_PEAK_GBPS,
         "compressed_bytes_per_token": per_token_bytes,
         "roofline": {"bound": "hbm", "achieved": l_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": l_gbps / HBM_PEAK_GBPS, "traffic": None, "kernel": "k_layer",
+                     "frac": l_gbps / HBM_PEAK_GBPS, "traffic": None,
+                     "kernel": "k_layer<route>" if args.path == "fused" else "k_layer",
                      "algorithmic_bytes_per_launch": per_token_bytes, "avg_us": l_avg_us, "timed_launches": int(n_l)},
         "kernels": kernels,
         "cpu_baseline": cpu,

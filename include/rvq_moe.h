@@ -168,6 +168,21 @@ int rvq_moe_layer_forward(rvq_moe *h, const float *x, int32_t n_tokens, const in
                           const float *gates, float *y, void *stream);
 
 /*
+ * rvq_moe_route_forward -- rvq_moe_route_topk and rvq_moe_layer_forward in one
+ * launch: writes ids and gates (the same selection: top k of fp64 logits,
+ * descending, ties to the lower id, softmax over the k) and y (the layer output
+ * for them).  The logits' fp64 summation order differs from route_topk's, so
+ * gates may differ from it in the last fp32 bit and near-ties (within ~1e-15
+ * relative) may resolve differently.
+ *   x [n_tokens][d] fp32; ids [n_tokens][k] int32 out; gates [n_tokens][k] fp32
+ *   out; y [n_tokens][d] fp32 out (must not alias x).
+ * Errors: EINVAL (null handle/pointer, n_tokens < 1 or > max_tokens,
+ * n_tokens * top_k > 1024, y == x), EHIP.
+ */
+int rvq_moe_route_forward(rvq_moe *h, const float *x, int32_t n_tokens, int32_t *ids, float *gates, float *y,
+                          void *stream);
+
+/*
  * rvq_moe_sync -- synchronise `stream`, then return and clear any deferred
  * device-side error (RVQ_MOE_EDEVICE) recorded by earlier calls.
  */
@@ -201,16 +216,17 @@ int rvq_moe_get_stats(const rvq_moe *h, rvq_moe_stats *out);
 
 /*
  * Kernel timing.  rvq_moe_set_profiling(h, every) makes every `every`-th
- * route_topk and every `every`-th layer_forward call bracket its kernel with
+ * route_topk and every `every`-th layer_forward / route_forward call bracket its kernels with
  * HIP events on the caller's stream (0 disables).  rvq_moe_kernel_times
  * synchronises the device and returns, per kernel kind, the number of timed
  * launches and their summed duration in milliseconds, then clears the
  * samples; names[] receives static strings.  Returns the number of kinds
  * filled (>= 0) or a negative status.  Kinds:
- *   0 "route_topk"  the router + top-k kernel of rvq_moe_route_topk,
- *   1 "layer_lut"   the persistent LUT kernel of rvq_moe_layer_forward.
+ *   0 "route_topk"       the router and selection kernels of rvq_moe_route_topk,
+ *   1 "layer_lut"        the persistent LUT kernel of rvq_moe_layer_forward,
+ *   2 "route_layer_lut"  the persistent kernel of rvq_moe_route_forward.
  */
-#define RVQ_MOE_N_KERNEL_KINDS 2
+#define RVQ_MOE_N_KERNEL_KINDS 3
 int rvq_moe_set_profiling(rvq_moe *h, int every);
 int rvq_moe_kernel_times(rvq_moe *h, const char **names, uint64_t *launches, double *total_ms,
                          int max_kinds);

@@ -254,3 +254,50 @@ def test_router_ties_go_to_the_lower_id_and_k_equals_e(torch_mod):
         assert pos[3] + 1 == pos[9] and pos[5] + 1 == pos[11]
         np.testing.assert_allclose(gates[t], ref.route.gates, rtol=TOL_G)
     layer.close()
+
+
+@pytest.mark.parametrize("shape_args,T,pre", [
+    ((256, 128, 16, 4, "f32"), 8, False),
+    ((264, 136, 5, 2, "f16"), 3, False),
+    ((512, 256, 32, 8, "f16"), 4, True),
+])
+def test_route_forward_one_launch_matches_two_calls_and_oracle(torch_mod, shape_args, T, pre):
+    from synth import gpu as G
+    shape = S.Shape(*shape_args)
+    inp = G.LayerInputs(shape, seed=13, layer=1, host_codes=True)
+    layer = _layer(torch_mod, inp, shape, T, pre_rmsnorm=pre, residual=pre, eps=1e-6)
+    x = S.tokens(13, 0, T, shape.d)
+    xd = G.to_device(x)
+    ids = torch_mod.empty((T, shape.top_k), dtype=torch_mod.int32, device="cuda")
+    gates = torch_mod.empty((T, shape.top_k), dtype=torch_mod.float32, device="cuda")
+    y = torch_mod.empty((T, shape.d), dtype=torch_mod.float32, device="cuda")
+    for _ in range(2):  # second call checks that the in-launch counters were reset
+        layer.route_forward(xd, T, ids, gates, y)
+        layer.sync()
+    fused = (ids.cpu().numpy(), gates.cpu().numpy(), y.cpu().numpy())
+    two = _run(torch_mod, layer, shape, x)
+    _check(inp, shape, x, *fused, pre_rmsnorm=pre, residual=pre)
+    assert np.array_equal(fused[0], two[0])
+    np.testing.assert_allclose(fused[1], two[1], rtol=1e-6)
+    err = np.linalg.norm(fused[2] - two[2], axis=1) / np.linalg.norm(two[2], axis=1)
+    assert err.max() <= 1e-6
+    layer.close()
+
+
+def test_k3_route_forward_batch1(torch_mod):
+    from synth import gpu as G
+    shape = S.K3
+    inp = G.LayerInputs(shape, seed=0, layer=0)
+    layer = _layer(torch_mod, inp, shape, 1)
+    inp.free_codes()
+    torch_mod.cuda.empty_cache()
+    x = S.tokens(0, 500, 2, shape.d)
+    xd = G.to_device(x)
+    ids = torch_mod.empty((2, shape.top_k), dtype=torch_mod.int32, device="cuda")
+    gates = torch_mod.empty((2, shape.top_k), dtype=torch_mod.float32, device="cuda")
+    y = torch_mod.empty((2, shape.d), dtype=torch_mod.float32, device="cuda")
+    for t in range(2):
+        layer.route_forward(xd[t], 1, ids[t], gates[t], y[t])
+    layer.sync()
+    _check(inp, shape, x, ids.cpu().numpy(), gates.cpu().numpy(), y.cpu().numpy())
+    layer.close()

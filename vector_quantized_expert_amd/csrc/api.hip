@@ -95,8 +95,7 @@ static void free_handle(rvq_moe *h) {
     (void)hipFree(h->ws.sel);
     (void)hipFree(h->ws.part_gu);
     (void)hipFree(h->ws.cntA);
-    (void)hipFree(h->ws.yinit);
-    (void)hipFree(h->ws.done);
+    (void)hipFree(h->ws.gbar);
     (void)hipFree(h->ws.err);
     for (hipEvent_t e : h->prof_pool) (void)hipEventDestroy(e);
     delete h;
@@ -131,8 +130,7 @@ static int open_impl(const rvq_moe_desc *desc, rvq_moe *h) {
     HIP_TRY(hipMalloc(&h->ws.sel, sizeof(double) * (size_t)(T * D.top_k)));
     HIP_TRY(hipMalloc(&h->ws.part_gu, sizeof(float) * (size_t)(P * 2 * g.m[0].n_tiles * g.ffn_pad)));
     HIP_TRY(hipMalloc(&h->ws.cntA, sizeof(int) * (size_t)P));
-    HIP_TRY(hipMalloc(&h->ws.yinit, sizeof(int)));
-    HIP_TRY(hipMalloc(&h->ws.done, sizeof(int)));
+    HIP_TRY(hipMalloc(&h->ws.gbar, sizeof(int) * kGbarInts));
     HIP_TRY(hipMalloc(&h->ws.err, sizeof(int)));
     int n_cu = 0;
     HIP_TRY(hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, h->device));
@@ -140,9 +138,9 @@ static int open_impl(const rvq_moe_desc *desc, rvq_moe *h) {
     HIP_TRY(layer_blocks_per_cu(D.codebook_dtype, &per_cu));
     if (n_cu < 1 || per_cu < 1) return fail(RVQ_MOE_EHIP, "occupancy query gave %d CUs x %d blocks", n_cu, per_cu);
     h->ws.n_wg = n_cu * per_cu;
+    if (h->ws.n_wg > 1024) h->ws.n_wg = 1024;  // grid arrival counters cover up to 1024 workgroups
     HIP_TRY(hipMemsetAsync(h->ws.cntA, 0, sizeof(int) * (size_t)P, s));
-    HIP_TRY(hipMemsetAsync(h->ws.yinit, 0, sizeof(int), s));
-    HIP_TRY(hipMemsetAsync(h->ws.done, 0, sizeof(int), s));
+    HIP_TRY(hipMemsetAsync(h->ws.gbar, 0, sizeof(int) * kGbarInts, s));
     HIP_TRY(hipMemsetAsync(h->ws.err, 0, sizeof(int), s));
     HIP_TRY(hipMemcpyAsync(h->cbs, D.codebooks, (size_t)(E * g.cb_bytes), hipMemcpyDeviceToDevice, s));
     HIP_TRY(launch_transpose(D.router_w, h->router_wt, D.d, D.n_experts, s));
@@ -253,9 +251,32 @@ extern "C" int rvq_moe_layer_forward(rvq_moe *h, const float *x, int32_t T, cons
     const bool prof = h->prof_every > 0 && (h->prof_calls++ % (uint64_t)h->prof_every) == 0;
     {
         ProfScope p(h, s, prof, 1);
-        HIP_TRY(launch_layer(h->g, h->ws, h->codes, h->cbs, x, ids, gates, y, T, h->pre_rmsnorm, h->residual,
-                             h->eps, s));
+        HIP_TRY(launch_layer(h->g, h->ws, h->codes, h->cbs, h->router_wt, x, ids, gates, y, T, h->pre_rmsnorm,
+                             h->residual, h->eps, false, s));
     }
+    h->stats.forward_calls++;
+    h->stats.tokens_forwarded += (uint64_t)T;
+    h->stats.expert_evals += (uint64_t)T * (uint64_t)h->g.k;
+    return RVQ_MOE_OK;
+}
+
+extern "C" int rvq_moe_route_forward(rvq_moe *h, const float *x, int32_t T, int32_t *ids, float *gates, float *y,
+                                     void *stream) {
+    int rc = check_call(h, x, T);
+    if (rc) return rc;
+    if (!ids || !gates || !y) return fail(RVQ_MOE_EINVAL, "ids/gates/y is NULL");
+    if ((const void *)y == (const void *)x) return fail(RVQ_MOE_EINVAL, "y aliases x");
+    if (T * h->g.k > kRouteMaxPairs)
+        return fail(RVQ_MOE_EINVAL, "n_tokens * top_k = %d above %d for one routed call", T * h->g.k, kRouteMaxPairs);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const bool prof = h->prof_every > 0 && (h->prof_calls++ % (uint64_t)h->prof_every) == 0;
+    {
+        ProfScope p(h, s, prof, 2);
+        HIP_TRY(launch_layer(h->g, h->ws, h->codes, h->cbs, h->router_wt, x, ids, gates, y, T, h->pre_rmsnorm,
+                             h->residual, h->eps, true, s));
+    }
+    h->stats.route_calls++;
+    h->stats.tokens_routed += (uint64_t)T;
     h->stats.forward_calls++;
     h->stats.tokens_forwarded += (uint64_t)T;
     h->stats.expert_evals += (uint64_t)T * (uint64_t)h->g.k;
@@ -299,7 +320,7 @@ extern "C" int rvq_moe_get_stats(const rvq_moe *h, rvq_moe_stats *out) {
     return RVQ_MOE_OK;
 }
 
-static const char *kKindNames[RVQ_MOE_N_KERNEL_KINDS] = {"route_topk", "layer_lut"};
+static const char *kKindNames[RVQ_MOE_N_KERNEL_KINDS] = {"route_topk", "layer_lut", "route_layer_lut"};
 
 extern "C" int rvq_moe_set_profiling(rvq_moe *h, int every) {
     if (!h || every < 0) return fail(RVQ_MOE_EINVAL, "bad handle or every");

@@ -86,8 +86,7 @@ struct Workspace {
     double *sel;        // [T][k] fp64 logits of the selected experts, by rank
     float *part_gu;     // [T*k][2][n_tiles_in][ffn_pad] partial gate/up sums
     int *cntA;          // [T*k] finished gate/up chunks per pair (self-resetting)
-    int *yinit;         // workgroups that initialised their slice of y (self-resetting)
-    int *done;          // workgroups finished (self-resetting)
+    int *gbar;          // grid arrival counters of the persistent kernel (self-resetting)
     int *err;           // device error flag: bit 0 bad id, bit 1 wait timeout
     int n_wg;           // persistent workgroups (all resident at once: blocks per CU x CUs)
 };
@@ -95,6 +94,8 @@ struct Workspace {
 constexpr int kRouteTok = 8;       // tokens per router workgroup when T > 1
 constexpr int kMaxExperts = 1024;
 constexpr int kMaxTopK = 64;
+constexpr int kRouteMaxPairs = 1024;
+constexpr int kGbarInts = 4 * 65;  // 4 grid barriers x (64 group counters + top)  // tokens x top_k of one rvq_moe_route_forward call
 
 // Launchers (all asynchronous on `s`; return hipError_t of the launch).
 hipError_t launch_repack(const Geometry &g, const uint8_t *canon, uint8_t *internal, int n_experts,
@@ -104,7 +105,7 @@ hipError_t launch_route(const Geometry &g, const Workspace &w, const float *x, c
                         double eps, int32_t *ids, float *gates, hipStream_t s);
 hipError_t layer_blocks_per_cu(int cb_dtype, int *out);
 hipError_t launch_layer(const Geometry &g, const Workspace &w, const uint8_t *codes, const void *cbs,
-                        const float *x, const int32_t *ids, const float *gates, float *y, int T, int pre,
-                        int residual, double eps, hipStream_t s);
+                        const float *Wt, const float *x, const int32_t *ids, const float *gates, float *y, int T,
+                        int pre, int residual, double eps, bool route, hipStream_t s);
 
 }  // namespace rvq

@@ -159,7 +159,7 @@ __device__ inline void cb_store(float *lut, const CbRegs<CB> &cr) {
 
 // Build the table of one 32-slice tile on the matrix cores.  The table is the
 // product of the staged codebook C [768 codes x 8] with the slice inputs
-// vs [32 slices][8] taken as [8 x 32] -- an exact dense contraction -- done as
+// vs [8][32 slices] (element-major, so each lane's reads are bank-conflict free) -- an exact dense contraction -- done as
 // 24 blocks of 32 codes x 32 slices with v_mfma_f32_32x32x16_f16 (fp32
 // accumulation).  The fp32 inputs are split v = v_hi + v_lo into two fp16
 // parts fed as the two K halves (lanes 0-31 carry v_hi, lanes 32-63 v_lo,
@@ -174,7 +174,7 @@ typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 template <int CB>
-__device__ inline void build_lut(float *lut, const float (*vs)[kVec], int e2) {
+__device__ inline void build_lut(float *lut, const float (*vs)[kTileSlices], int e2) {
     constexpr int kEntryBytes = CB == 0 ? 32 : 16;
     constexpr int kPerRow = 128 / kEntryBytes;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -183,7 +183,7 @@ __device__ inline void build_lut(float *lut, const float (*vs)[kVec], int e2) {
     half8 bop;
 #pragma unroll
     for (int i = 0; i < kVec; i++) {
-        const float v = vs[j][i] * down;
+        const float v = vs[i][j] * down;
         const _Float16 hi = (_Float16)v;
         bop[i] = kh ? (_Float16)(v - (float)hi) : hi;
     }
@@ -415,8 +415,36 @@ __device__ inline void wait_count(const int *cnt, int target, int *err) {
     __syncthreads();
 }
 
+// Grid-wide arrival counts without a hot spot: workgroups arrive in groups of
+// kGridGroup on their own counter; the last of a group resets it and bumps
+// the top counter, which waiters poll.  (256 arrivals on one address
+// serialise at the device-scope atomic unit: several microseconds.)
+constexpr int kGridGroup = 16;
+constexpr int kMaxGridGroups = 64;  // up to 1024 workgroups
+
+// counter block layout: [barrier][kMaxGridGroups + 1]; entry kMaxGridGroups is the top
+__device__ inline void grid_arrive(int *blk) {
+    wait_stores();
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const int G = gridDim.x, grp = blockIdx.x / kGridGroup;
+        const int gsz = min(kGridGroup, G - grp * kGridGroup);
+        if (atomicAdd(blk + grp, 1) == gsz - 1) {
+            store_counter(blk + grp, 0);
+            atomicAdd(blk + kMaxGridGroups, 1);
+        }
+    }
+}
+
+__device__ inline int grid_groups() { return (gridDim.x + kGridGroup - 1) / kGridGroup; }
+
 // ---------------------------------------------------------------------------
 struct LayerArgs {
+    // routing inside the launch (rvq_moe_route_forward); unused otherwise
+    const float *Wt;    // [E][d] transposed router
+    double *logits;     // [T][E]
+    double *sel;        // [T][k] selected logits by rank
+    int *gbar;          // [4][kMaxGridGroups + 1] grid arrival counters: y init, logits, ranks, exit
     const uint8_t *codes;
     const void *cbs;
     const float *x;
@@ -425,8 +453,6 @@ struct LayerArgs {
     float *y;
     float *part_gu;  // [P][2][n_ti][ffn_pad]
     int *cntA;       // [P]
-    int *yinit;      // workgroups that initialised their slice of y
-    int *done;
     int *err;
     Geometry g;
     int T;
@@ -460,8 +486,8 @@ __device__ inline double token_r(const LayerArgs &a, int t, int &r_tok, double &
 // where a and b are the gate and up row sums (sum over the input tiles' partial
 // sums).  Four threads per entry each add every fourth tile (up to 8 loads
 // per matrix in flight per thread), then the four partials meet in LDS.
-__device__ inline void finish_h(const LayerArgs &a, int p, int ft, float (*vs)[kVec], float (*hred)[256][2],
-                                float *red2) {
+__device__ inline void finish_h(const LayerArgs &a, const float *gate_src, int p, int ft, float (*vs)[kTileSlices],
+                                float (*hred)[256][2], float *red2) {
     const Geometry &g = a.g;
     const int n_ti = g.m[0].n_tiles;
     const int fi = threadIdx.x & 255, part = threadIdx.x >> 8;
@@ -493,9 +519,9 @@ __device__ inline void finish_h(const LayerArgs &a, int p, int ft, float (*vs)[k
         if (f < g.ffn) {
             const float av = hred[0][fi][0] + hred[1][fi][0] + hred[2][fi][0] + hred[3][fi][0];
             const float bv = hred[0][fi][1] + hred[1][fi][1] + hred[2][fi][1] + hred[3][fi][1];
-            hv = a.gates[p] * (av / (1.f + expf(-av)) * bv);
+            hv = gate_src[p] * (av / (1.f + expf(-av)) * bv);
         }
-        vs[fi / kVec][fi % kVec] = hv;
+        vs[fi % kVec][fi / kVec] = hv;
         tile_max_publish(hv, red2);
     }
 }
@@ -544,11 +570,112 @@ __device__ inline SegB seg_b(int64_t u, int64_t u1, int n_tf, int n_cd, const Id
     return s;
 }
 
-template <int CB>
+// fp64 sum over the workgroup; every thread gets the total.  dred: >= kWaves doubles.
+__device__ inline double block_sum(double v, double *dred) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) dred[threadIdx.x >> 6] = v;
+    __syncthreads();
+    double s = 0.0;
+#pragma unroll
+    for (int w = 0; w < kWaves; w++) s += dred[w];
+    return s;
+}
+
+// Routing inside the launch ([FR] "Lecture anticipée et prédiction du routeur":
+// the router decides the token's experts; reading as in the separate route
+// kernels: top-k of fp64 logits, ties to the lower id, softmax over the k).
+//  R1  logits of experts e = wg, wg + G, ...: fp64 sums of exact fp32 products,
+//      divided by the fp64 RMS divisor when normalising;
+//  R2  (all logits published) rank of each of those experts among all E,
+//      ids[t][rank] = e and sel[t][rank] = logit for rank < k;
+//  R3  (all ranks published) every workgroup forms the softmax gates it needs
+//      (gate_lds, fp64 in selection order) and workgroup 0 writes them out.
+__device__ void route_phase(const LayerArgs &a, double *dred, double *lg_lds, float *gate_lds, int *cnt_lds) {
+    const Geometry &g = a.g;
+    const int G = gridDim.x, wg = blockIdx.x;
+    const int n4 = g.d / 4;
+    for (int e = wg; e < g.E; e += G) {
+        const float4 *w4 = reinterpret_cast<const float4 *>(a.Wt + (size_t)e * g.d);
+        for (int t = 0; t < a.T; t++) {
+            const float4 *x4 = reinterpret_cast<const float4 *>(a.x + (size_t)t * g.d);
+            double acc = 0.0, ss = 0.0;
+            for (int i = threadIdx.x; i < n4; i += kBlock) {
+                const float4 wv = w4[i], xv = x4[i];
+                acc = fma((double)xv.x, (double)wv.x, acc);
+                acc = fma((double)xv.y, (double)wv.y, acc);
+                acc = fma((double)xv.z, (double)wv.z, acc);
+                acc = fma((double)xv.w, (double)wv.w, acc);
+                if (a.pre) {
+                    ss = fma((double)xv.x, (double)xv.x, ss);
+                    ss = fma((double)xv.y, (double)xv.y, ss);
+                    ss = fma((double)xv.z, (double)xv.z, ss);
+                    ss = fma((double)xv.w, (double)xv.w, ss);
+                }
+            }
+            const double sa = block_sum(acc, dred);
+            const double sq = a.pre ? block_sum(ss, dred) : 0.0;
+            const double r = a.pre ? sqrt(sq / (double)g.d + a.eps) : 1.0;
+            if (threadIdx.x == 0) store_coherent(a.logits + (size_t)t * g.E + e, sa / r);
+        }
+    }
+    grid_arrive(a.gbar + 1 * (kMaxGridGroups + 1));
+    wait_count(a.gbar + 1 * (kMaxGridGroups + 1) + kMaxGridGroups, grid_groups(), a.err);
+    for (int t = 0; t < a.T; t++) {
+        if (wg >= g.E) break;
+        for (int i = threadIdx.x; i < g.E; i += kBlock) {
+            const double v = load_coherent(a.logits + (size_t)t * g.E + i);
+            lg_lds[i] = isnan(v) ? -INFINITY : v;
+        }
+        __syncthreads();
+        for (int e = wg; e < g.E; e += G) {
+            const double me = lg_lds[e];
+            int c = 0;
+            for (int i = threadIdx.x; i < g.E; i += kBlock) {
+                const double v = lg_lds[i];
+                c += (v > me || (v == me && i < e)) ? 1 : 0;
+            }
+#pragma unroll
+            for (int o = 32; o > 0; o >>= 1) c += __shfl_xor(c, o);
+            if ((threadIdx.x & 63) == 0) cnt_lds[threadIdx.x >> 6] = c;
+            __syncthreads();
+            if (threadIdx.x == 0) {
+                int rank = 0;
+                for (int w = 0; w < kWaves; w++) rank += cnt_lds[w];
+                if (rank < g.k) {
+                    store_counter(const_cast<int32_t *>(a.ids) + (size_t)t * g.k + rank, e);
+                    store_coherent(a.sel + (size_t)t * g.k + rank, me);
+                }
+            }
+            __syncthreads();
+        }
+    }
+    grid_arrive(a.gbar + 2 * (kMaxGridGroups + 1));
+    wait_count(a.gbar + 2 * (kMaxGridGroups + 1) + kMaxGridGroups, grid_groups(), a.err);
+    // gates: stage the T * k selected logits in LDS (one coherent load each, all
+    // in flight together), then thread i = (t, j) forms its softmax in fp64
+    const int P = a.T * g.k;
+    for (int i = threadIdx.x; i < P; i += kBlock) lg_lds[i] = load_coherent(a.sel + i);
+    __syncthreads();
+    for (int i = threadIdx.x; i < P; i += kBlock) {
+        const int t = i / g.k;
+        const double top = lg_lds[t * g.k];
+        double sum = 0.0;
+        for (int j = 0; j < g.k; j++) sum += exp(lg_lds[t * g.k + j] - top);
+        const float gt = (float)(exp(lg_lds[i] - top) / sum);
+        gate_lds[i] = gt;
+        if (wg == 0) const_cast<float *>(a.gates)[i] = gt;
+    }
+    __syncthreads();
+}
+
+template <int CB, bool kRoute>
 __global__ __launch_bounds__(kBlock) void k_layer(LayerArgs a) {
     __shared__ float lut[kLutWords];
-    __shared__ float vs[kTileSlices][kVec];
+    __shared__ float vs[kVec][kTileSlices];  // [element][slice]
     __shared__ double red[kWaves];
+    static_assert(kMaxExperts * sizeof(double) <= kLutWords * sizeof(float), "logit staging must fit the table area");
     __shared__ float hred[4][256][2];
     __shared__ float red2[kWaves];
     const Geometry &g = a.g;
@@ -560,6 +687,13 @@ __global__ __launch_bounds__(kBlock) void k_layer(LayerArgs a) {
     int r_tok = -1;
     double r_val = 1.0;
     CbRegs<CB> cb;
+    __shared__ float gate_lds[kRouteMaxPairs];
+    const float *gate_src = a.gates;
+    if (kRoute) {
+        // the logits staging and counts reuse the table area, which is idle until phase A
+        route_phase(a, red, reinterpret_cast<double *>(lut), gate_lds, reinterpret_cast<int *>(hred));
+        gate_src = gate_lds;
+    }
     __shared__ int id_lds[2 * kIdCache];
     IdCache ic;
     {
@@ -571,8 +705,8 @@ __global__ __launch_bounds__(kBlock) void k_layer(LayerArgs a) {
         ic.a_n = a1 > a0 ? min(kIdCache, (int)((a1 - 1) / n_cf / (2 * n_ti)) - ic.a_base + 1) : 0;
         ic.b_base = (int)(b0 / n_cd / n_tf);
         ic.b_n = b1 > b0 ? min(kIdCache, (int)((b1 - 1) / n_cd / n_tf) - ic.b_base + 1) : 0;
-        if (threadIdx.x < ic.a_n) id_lds[threadIdx.x] = a.ids[ic.a_base + threadIdx.x];
-        if (threadIdx.x < ic.b_n) id_lds[kIdCache + threadIdx.x] = a.ids[ic.b_base + threadIdx.x];
+        if (threadIdx.x < ic.a_n) id_lds[threadIdx.x] = load_counter(a.ids + ic.a_base + threadIdx.x);
+        if (threadIdx.x < ic.b_n) id_lds[kIdCache + threadIdx.x] = load_counter(a.ids + ic.b_base + threadIdx.x);
         __syncthreads();
     }
 
@@ -581,7 +715,7 @@ __global__ __launch_bounds__(kBlock) void k_layer(LayerArgs a) {
         const int64_t n = (int64_t)a.T * g.d;
         for (int64_t i = n * wg / G + threadIdx.x; i < n * (wg + 1) / G; i += kBlock)
             store_coherent(a.y + i, a.residual ? a.x[i] : 0.f);
-        signal_add(a.yinit, 1);
+        signal_add(a.gbar + kMaxGridGroups, 1);  // flat, non-returning: nobody waits on it here
     }
     bool y_ready = false;
 
@@ -614,7 +748,7 @@ __global__ __launch_bounds__(kBlock) void k_layer(LayerArgs a) {
                 cb_store<CB>(lut, cb);
                 if (threadIdx.x < kTileSlices * kVec) {
                     const float v = a.pre ? (float)((double)xv / r) : xv;
-                    vs[threadIdx.x / kVec][threadIdx.x % kVec] = v;
+                    vs[threadIdx.x % kVec][threadIdx.x / kVec] = v;
                     tile_max_publish(v, red2);
                 }
                 u32x4 p0, p1, p2;
@@ -659,20 +793,20 @@ __global__ __launch_bounds__(kBlock) void k_layer(LayerArgs a) {
                 if (cur.c0 + wave < cur.c1)
                     load_chunk(base + (int64_t)(cur.c0 + wave) * kChunkBytes, lane, p0, p1, p2);
                 wait_count(&a.cntA[cur.p], needA, a.err);
-                finish_h(a, cur.p, cur.ft, vs, hred, red2);
+                finish_h(a, gate_src, cur.p, cur.ft, vs, hred, red2);
                 __syncthreads();
                 build_lut<CB>(lut, vs, tile_exponent(red2));
                 __syncthreads();
                 if (un < u1 && nxt.e >= 0 && nxt.e < g.E) cb_load<CB>(cb, a.cbs, nxt.e, 2);
                 if (!y_ready) {
-                    wait_count(a.yinit, G, a.err);
+                    wait_count(a.gbar + kMaxGridGroups, G, a.err);
                     y_ready = true;
                 }
                 gather_segment<true>(lut, base, cur.c0, cur.c1, a.y + (size_t)(cur.p / g.k) * g.d, g.d, p0, p1, p2);
             } else {
                 // an invalid id poisons its token's output (the error flag is already set)
                 if (!y_ready) {
-                    wait_count(a.yinit, G, a.err);
+                    wait_count(a.gbar + kMaxGridGroups, G, a.err);
                     y_ready = true;
                 }
                 if (cur.ft == 0)
@@ -687,38 +821,46 @@ __global__ __launch_bounds__(kBlock) void k_layer(LayerArgs a) {
     }
 
     // ---------------- the last workgroup out resets the counters for the next call
+    // (one flat counter: workgroups finish spread out in time, so there is no hot
+    // spot, and the last one learns it is last in one round trip)
     __shared__ int last;
+    int *xb = a.gbar + 3 * (kMaxGridGroups + 1) + kMaxGridGroups;
     __syncthreads();
-    if (threadIdx.x == 0) last = (atomicAdd(a.done, 1) == G - 1);
+    if (threadIdx.x == 0) last = atomicAdd(xb, 1) == G - 1;
     __syncthreads();
     if (last) {
         for (int i = threadIdx.x; i < P; i += kBlock) store_counter(a.cntA + i, 0);
-        if (threadIdx.x == 0) {
-            store_counter(a.yinit, 0);
-            store_counter(a.done, 0);
-        }
+        if (threadIdx.x < 4) store_counter(a.gbar + threadIdx.x * (kMaxGridGroups + 1) + kMaxGridGroups, 0);
     }
 }
 
 hipError_t launch_layer(const Geometry &g, const Workspace &w, const uint8_t *codes, const void *cbs,
-                        const float *x, const int32_t *ids, const float *gates, float *y, int T, int pre,
-                        int residual, double eps, hipStream_t s) {
-    LayerArgs a{codes, cbs, x, ids, gates, y, w.part_gu, w.cntA, w.yinit, w.done, w.err, g, T, pre,
+                        const float *Wt, const float *x, const int32_t *ids, const float *gates, float *y, int T,
+                        int pre, int residual, double eps, bool route, hipStream_t s) {
+    LayerArgs a{Wt, w.logits, w.sel, w.gbar, codes, cbs, x, ids, gates, y, w.part_gu, w.cntA, w.err, g, T, pre,
                 residual, eps};
     // A plain launch of exactly as many workgroups as can be resident at once
     // (sized at open from the occupancy query); the inter-workgroup waits are
     // bounded, so a launch that somehow did not get all of them resident ends
     // with an error flag instead of hanging.
-    if (g.cb_dtype == 0)
-        hipLaunchKernelGGL(k_layer<0>, dim3(w.n_wg), dim3(kBlock), 0, s, a);
-    else
-        hipLaunchKernelGGL(k_layer<1>, dim3(w.n_wg), dim3(kBlock), 0, s, a);
+    if (g.cb_dtype == 0) {
+        if (route)
+            hipLaunchKernelGGL((k_layer<0, true>), dim3(w.n_wg), dim3(kBlock), 0, s, a);
+        else
+            hipLaunchKernelGGL((k_layer<0, false>), dim3(w.n_wg), dim3(kBlock), 0, s, a);
+    } else {
+        if (route)
+            hipLaunchKernelGGL((k_layer<1, true>), dim3(w.n_wg), dim3(kBlock), 0, s, a);
+        else
+            hipLaunchKernelGGL((k_layer<1, false>), dim3(w.n_wg), dim3(kBlock), 0, s, a);
+    }
     return hipGetLastError();
 }
 
 hipError_t layer_blocks_per_cu(int cb_dtype, int *out) {
-    return cb_dtype == 0 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(out, k_layer<0>, kBlock, 0)
-                         : hipOccupancyMaxActiveBlocksPerMultiprocessor(out, k_layer<1>, kBlock, 0);
+    // the routing variant uses the same resources or more: size the grid by it
+    return cb_dtype == 0 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(out, k_layer<0, true>, kBlock, 0)
+                         : hipOccupancyMaxActiveBlocksPerMultiprocessor(out, k_layer<1, true>, kBlock, 0);
 }
 
 }  // namespace rvq

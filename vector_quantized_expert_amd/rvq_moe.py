@@ -21,7 +21,7 @@ OK, EINVAL, ENOTSUP, EBUDGET, ENOMEM, EHIP, EDEVICE = 0, -1, -2, -3, -4, -5, -6
 STATUS_NAMES = {0: "OK", -1: "EINVAL", -2: "ENOTSUP", -3: "EBUDGET", -4: "ENOMEM", -5: "EHIP", -6: "EDEVICE"}
 CB_F32, CB_F16 = 0, 1
 CODES_DEVICE, CODES_PINNED_HOST = 0, 1
-KERNEL_KINDS = 2
+KERNEL_KINDS = 3
 
 
 class RvqMoeError(RuntimeError):
@@ -74,6 +74,7 @@ def lib():
         L.rvq_moe_open.argtypes = [ctypes.POINTER(Desc), ctypes.POINTER(vp)]
         L.rvq_moe_route_topk.argtypes = [vp, vp, i32, vp, vp, vp]
         L.rvq_moe_layer_forward.argtypes = [vp, vp, i32, vp, vp, vp, vp]
+        L.rvq_moe_route_forward.argtypes = [vp, vp, i32, vp, vp, vp, vp]
         L.rvq_moe_sync.argtypes = [vp, vp]
         L.rvq_moe_close.argtypes = [vp]
         L.rvq_moe_last_error.argtypes = []
@@ -83,7 +84,7 @@ def lib():
         L.rvq_moe_set_profiling.argtypes = [vp, ctypes.c_int]
         L.rvq_moe_kernel_times.argtypes = [vp, ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(ctypes.c_uint64),
                                            ctypes.POINTER(ctypes.c_double), ctypes.c_int]
-        for n in ("rvq_moe_open", "rvq_moe_route_topk", "rvq_moe_layer_forward", "rvq_moe_sync",
+        for n in ("rvq_moe_open", "rvq_moe_route_topk", "rvq_moe_layer_forward", "rvq_moe_route_forward", "rvq_moe_sync",
                   "rvq_moe_close", "rvq_moe_abi_version", "rvq_moe_get_stats", "rvq_moe_set_profiling",
                   "rvq_moe_kernel_times"):
             getattr(L, n).restype = ctypes.c_int
@@ -157,6 +158,10 @@ class RvqMoe:
     def layer_forward(self, x, n_tokens, ids, gates, y, stream=None):
         return _check(lib().rvq_moe_layer_forward(self.h, _ptr(x), n_tokens, _ptr(ids), _ptr(gates), _ptr(y),
                                                   _stream(stream)), "rvq_moe_layer_forward")
+
+    def route_forward(self, x, n_tokens, ids, gates, y, stream=None):
+        return _check(lib().rvq_moe_route_forward(self.h, _ptr(x), n_tokens, _ptr(ids), _ptr(gates), _ptr(y),
+                                                  _stream(stream)), "rvq_moe_route_forward")
 
     def sync(self, stream=None):
         return _check(lib().rvq_moe_sync(self.h, _stream(stream)), "rvq_moe_sync")
