@@ -38,6 +38,8 @@ def main():
     ap.add_argument("--cpu-tokens", type=int, default=2, help="tokens the oracle baseline runs (0: skip)")
     ap.add_argument("--profile-every", type=int, default=8, help="time kernels with events every n-th call")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--batch", type=int, default=1,
+                    help="tokens per call; above 1 the pairs of a call are grouped by expert (batched decode)")
     ap.add_argument("--path", choices=("fused", "two-call"), default="two-call",
                     help="fused: rvq_moe_route_forward (one launch per token); "
                          "two-call: rvq_moe_route_topk then rvq_moe_layer_forward")
@@ -57,16 +59,19 @@ def main():
 
     torch.cuda.set_device(0)
     shape = S.K3
-    K, W = args.steps, args.warmup
+    K, W, B = args.steps, args.warmup, args.batch
+    if B < 1 or (args.path == "fused" and B * shape.top_k > 1024):
+        print(f"--batch {B} outside what the chosen path takes", file=sys.stderr)
+        sys.exit(2)
     print(f"[bench] staging inputs d={shape.d} ffn={shape.ffn} E={shape.n_experts} k={shape.top_k}", file=sys.stderr,
           flush=True)
     inp = G.LayerInputs(shape, seed=args.seed, layer=0)
     layer = RvqMoe(d=shape.d, ffn=shape.ffn, n_experts=shape.n_experts, top_k=shape.top_k, codebook_dtype=1,
-                   router_w=inp.w_r_dev, codebooks=inp.cb_dev, codes=inp.codes_dev, max_tokens=1)
+                   router_w=inp.w_r_dev, codebooks=inp.cb_dev, codes=inp.codes_dev, max_tokens=B)
     inp.free_codes()
     torch.cuda.empty_cache()
 
-    n_tok = W + K
+    n_tok = (W + K) * B
     x_host = S.tokens(args.seed, 0, n_tok, shape.d)
     x = G.to_device(x_host)
     ids = torch.empty((n_tok, shape.top_k), dtype=torch.int32, device="cuda")
@@ -75,15 +80,17 @@ def main():
     stream = torch.cuda.current_stream()
 
     def step_two(t):
-        layer.route_topk(x[t], 1, ids[t], gates[t], stream)
-        layer.layer_forward(x[t], 1, ids[t], gates[t], y[t], stream)
+        r = slice(t * B, (t + 1) * B)
+        layer.route_topk(x[r], B, ids[r], gates[r], stream)
+        layer.layer_forward(x[r], B, ids[r], gates[r], y[r], stream)
 
     def step_fused(t):
-        layer.route_forward(x[t], 1, ids[t], gates[t], y[t], stream)
+        r = slice(t * B, (t + 1) * B)
+        layer.route_forward(x[r], B, ids[r], gates[r], y[r], stream)
 
     step = step_fused if args.path == "fused" else step_two
 
-    print(f"[bench] warmup {W} tokens", file=sys.stderr, flush=True)
+    print(f"[bench] warmup {W} calls of {B} token(s)", file=sys.stderr, flush=True)
     for t in range(W):
         step(t)
     layer.sync(stream)
@@ -101,19 +108,23 @@ def main():
     layer.set_profiling(0)
     ktimes = layer.kernel_times()
     layer.sync(stream)
-    print(f"[bench] timed {K} tokens in {ms:.2f} ms", file=sys.stderr, flush=True)
+    print(f"[bench] timed {K} calls in {ms:.2f} ms", file=sys.stderr, flush=True)
 
     rec = shape.record_bytes
     cb_bytes = 3 * 3 * 256 * 8 * 2
-    per_token_bytes = shape.top_k * (rec + cb_bytes)
-    tok_s = K / (ms / 1e3)
-    gbps = per_token_bytes * tok_s / 1e9
+    # Algorithmic bytes of one call: every distinct expert the call routes to,
+    # read once (code record + its 3 matrices' codebooks).  At batch 1 that is
+    # k experts; in a batch, experts shared by several tokens count once.
+    ids_all = ids.cpu().numpy().reshape(W + K, B * shape.top_k)
+    uniq = np.array([len(np.unique(ids_all[t])) for t in range(W, W + K)], dtype=np.float64)
+    per_call_bytes = float(uniq.mean()) * (rec + cb_bytes)
+    tok_s = K * B / (ms / 1e3)
+    gbps = per_call_bytes * (K / (ms / 1e3)) / 1e9
 
-    # Dominant kernel: the persistent LUT kernel of layer_forward.  Algorithmic
-    # bytes per launch (T = 1) = k experts x (code record + 3 matrices' codebooks).
+    # Dominant kernel: the persistent LUT kernel of the layer call.
     n_l, l_ms = ktimes["route_layer_lut" if args.path == "fused" else "layer_lut"]
     l_avg_us = l_ms / max(n_l, 1) * 1e3
-    l_gbps = per_token_bytes / (l_avg_us * 1e-6) / 1e9
+    l_gbps = per_call_bytes / (l_avg_us * 1e-6) / 1e9
     kernels = {k: {"launches": int(n), "avg_us": (v / n * 1e3 if n else None)} for k, (n, v) in ktimes.items()}
 
     # Parity on the timed tokens the oracle re-runs, and the CPU baseline.
@@ -126,7 +137,7 @@ def main():
         errs, ok_ids = [], True
         t0 = time.perf_counter()
         for j in range(args.cpu_tokens):
-            t = W + j
+            t = W * B + j
             ref = O.layer(x_host[t], inp.w_r, shape.top_k, inp.codebook, inp.record, shape.d, shape.ffn)
             ok_ids &= bool(np.array_equal(ids_h[t], ref.route.ids))
             errs.append(float(np.linalg.norm(y_h[t] - ref.delta) / np.linalg.norm(ref.delta)))
@@ -144,23 +155,25 @@ def main():
         "steps": K,
         "warmup": W,
         "ms_per_step": ms / K,
+        "tokens_per_step": B,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": "K3-scale routed RVQ-MoE layer, batch-1 decode: d=7168 ffn=2048 E=384 top-16, "
-                               "3-stage x 256 x 8 fp16 codebooks, uniform u8 codes, T=1 per call",
-                   "global_batch": 1, "tokens": K,
+        "config": {"workload": f"K3-scale routed RVQ-MoE layer, batch-{B} decode: d=7168 ffn=2048 E=384 top-16, "
+                               f"3-stage x 256 x 8 fp16 codebooks, uniform u8 codes, T={B} per call",
+                   "global_batch": B, "tokens": K * B,
                    "path": "rvq_moe_route_forward" if args.path == "fused"
                    else "rvq_moe_route_topk + rvq_moe_layer_forward"},
         "compressed_GBps": gbps,
         "hbm_frac": gbps / HBM_PEAK_GBPS,
-        "compressed_bytes_per_token": per_token_bytes,
+        "compressed_bytes_per_call": per_call_bytes,
+        "distinct_experts_per_call": float(uniq.mean()),
         "roofline": {"bound": "hbm", "achieved": l_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": l_gbps / HBM_PEAK_GBPS, "traffic": None,
                      "kernel": "k_layer<route>" if args.path == "fused" else "k_layer",
-                     "algorithmic_bytes_per_launch": per_token_bytes, "avg_us": l_avg_us, "timed_launches": int(n_l)},
+                     "algorithmic_bytes_per_launch": per_call_bytes, "avg_us": l_avg_us, "timed_launches": int(n_l)},
         "kernels": kernels,
         "cpu_baseline": cpu,
         "parity": parity,

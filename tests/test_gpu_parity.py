@@ -301,3 +301,73 @@ def test_k3_route_forward_batch1(torch_mod):
     layer.sync()
     _check(inp, shape, x, ids.cpu().numpy(), gates.cpu().numpy(), y.cpu().numpy())
     layer.close()
+
+
+# --------------------------------------------------------------------------- batched decode (pair order)
+def test_explicit_ids_with_repeats_follow_the_oracle(torch_mod, tiny):
+    """Caller-supplied ids may repeat within a token and across tokens; the
+    expert-grouped pair order must still give every pair its own gate-weighted
+    contribution."""
+    from synth import gpu as G
+    shape = S.TINY
+    T = 6
+    ids_h = np.array([[2, 2, 2, 2], [2, 5, 7, 2], [0, 15, 8, 1], [15, 15, 3, 3], [5, 6, 7, 8], [9, 9, 9, 0]],
+                     dtype=np.int32)
+    rng = np.random.default_rng(21)
+    gates_h = rng.uniform(-1.0, 1.0, size=(T, 4)).astype(np.float32)
+    layer = _layer(torch_mod, tiny, shape, T)
+    x = S.tokens(0, 300, T, shape.d)
+    ids = torch_mod.tensor(ids_h, device="cuda")
+    gates = torch_mod.tensor(gates_h, device="cuda")
+    y = torch_mod.empty((T, shape.d), device="cuda")
+    layer.layer_forward(G.to_device(x), T, ids, gates, y)
+    layer.sync()
+    yh = y.cpu().numpy()
+    for t in range(T):
+        ref = O.moe(shape.d, shape.ffn, gates_h[t].astype(np.float64), [tiny.codebook(int(e)) for e in ids_h[t]],
+                    [tiny.record(int(e)) for e in ids_h[t]], x[t])
+        err = np.linalg.norm(yh[t] - ref) / np.linalg.norm(ref)
+        assert err <= TOL_Y, (t, err)
+    layer.close()
+
+
+def test_batch_beyond_the_order_table_uses_pair_order(torch_mod, tiny):
+    """160 tokens x top-4 = 640 pairs: above the grouped-order table, so the
+    pairs run in plain pair order; every token still matches the oracle."""
+    shape = S.TINY
+    layer = _layer(torch_mod, tiny, shape, 160)
+    x = S.tokens(0, 1000, 160, shape.d)
+    ids, gates, y = _run(torch_mod, layer, shape, x)
+    _check(tiny, shape, x, ids, gates, y)
+    layer.close()
+
+
+def test_k3_batch32_grouped_matches_per_token_and_oracle(torch_mod):
+    """d=7168, ffn=2048, E=384, top-16, 32 tokens in one call (512 pairs, the
+    expert-grouped order): the whole batch agrees with 32 one-token calls, and
+    sampled tokens with the oracle.  The one-launch routed call is checked too."""
+    from synth import gpu as G
+    shape = S.K3
+    T = 32
+    inp = G.LayerInputs(shape, seed=0, layer=3)
+    layer = _layer(torch_mod, inp, shape, T)
+    inp.free_codes()
+    torch_mod.cuda.empty_cache()
+    x = S.tokens(0, 2000, T, shape.d)
+    batched = _run(torch_mod, layer, shape, x)
+    single = _run(torch_mod, layer, shape, x, per_token=True)
+    assert np.array_equal(batched[0], single[0]) and np.array_equal(batched[1], single[1])
+    err = np.linalg.norm(batched[2] - single[2], axis=1) / np.linalg.norm(single[2], axis=1)
+    assert err.max() <= 1e-6, err.max()
+    xd = G.to_device(x)
+    ids = torch_mod.empty((T, shape.top_k), dtype=torch_mod.int32, device="cuda")
+    gates = torch_mod.empty((T, shape.top_k), dtype=torch_mod.float32, device="cuda")
+    y = torch_mod.empty((T, shape.d), dtype=torch_mod.float32, device="cuda")
+    layer.route_forward(xd, T, ids, gates, y)
+    layer.sync()
+    assert np.array_equal(ids.cpu().numpy(), batched[0])
+    err = np.linalg.norm(y.cpu().numpy() - batched[2], axis=1) / np.linalg.norm(batched[2], axis=1)
+    assert err.max() <= 1e-6, err.max()
+    worst = _check(inp, shape, x, *batched, tokens=[0, 17, 31])
+    print(f"K3 batch-32 worst rel L2 {worst:.3e}")
+    layer.close()

@@ -11,9 +11,11 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
 #include <vector>
 
 #include "rvq_moe.h"
+
 #include "internal.hpp"
 
 using namespace rvq;
@@ -93,6 +95,7 @@ static void free_handle(rvq_moe *h) {
     (void)hipFree(h->router_wt);
     (void)hipFree(h->ws.logits);
     (void)hipFree(h->ws.sel);
+    (void)hipFree(h->ws.route_logits);
     (void)hipFree(h->ws.part_gu);
     (void)hipFree(h->ws.cntA);
     (void)hipFree(h->ws.gbar);
@@ -128,6 +131,7 @@ static int open_impl(const rvq_moe_desc *desc, rvq_moe *h) {
     const int64_t T = D.max_tokens, P = T * D.top_k;
     HIP_TRY(hipMalloc(&h->ws.logits, sizeof(double) * (size_t)(T * E)));
     HIP_TRY(hipMalloc(&h->ws.sel, sizeof(double) * (size_t)(T * D.top_k)));
+    HIP_TRY(hipMalloc(&h->ws.route_logits, sizeof(double) * (size_t)route_logit_slots(T, D.n_experts)));
     HIP_TRY(hipMalloc(&h->ws.part_gu, sizeof(float) * (size_t)(P * 2 * g.m[0].n_tiles * g.ffn_pad)));
     HIP_TRY(hipMalloc(&h->ws.cntA, sizeof(int) * (size_t)P));
     HIP_TRY(hipMalloc(&h->ws.gbar, sizeof(int) * kGbarInts));
@@ -137,6 +141,7 @@ static int open_impl(const rvq_moe_desc *desc, rvq_moe *h) {
     int per_cu = 0;
     HIP_TRY(layer_blocks_per_cu(D.codebook_dtype, &per_cu));
     if (n_cu < 1 || per_cu < 1) return fail(RVQ_MOE_EHIP, "occupancy query gave %d CUs x %d blocks", n_cu, per_cu);
+    HIP_TRY(init_route(h->ws, D.n_experts, T, n_cu, s));
     h->ws.n_wg = n_cu * per_cu;
     if (h->ws.n_wg > 1024) h->ws.n_wg = 1024;  // grid arrival counters cover up to 1024 workgroups
     HIP_TRY(hipMemsetAsync(h->ws.cntA, 0, sizeof(int) * (size_t)P, s));
@@ -171,6 +176,15 @@ extern "C" int rvq_moe_open(const rvq_moe_desc *desc, rvq_moe **out) {
     if (D.codebook_dtype != RVQ_MOE_CB_F32 && D.codebook_dtype != RVQ_MOE_CB_F16)
         return fail(RVQ_MOE_EINVAL, "codebook_dtype=%d", D.codebook_dtype);
     if (D.max_tokens < 1) return fail(RVQ_MOE_EINVAL, "max_tokens=%d < 1", D.max_tokens);
+    {
+        // the layer kernel numbers its work units (one 32-row chunk of one
+        // 32-slice tile of one pair's matrix) in 32 bits
+        const int64_t n_ti = (D.d / kVec + kTileSlices - 1) / kTileSlices, n_cf = (D.ffn + kChunkRows - 1) / kChunkRows;
+        const int64_t n_tf = (D.ffn / kVec + kTileSlices - 1) / kTileSlices, n_cd = (D.d + kChunkRows - 1) / kChunkRows;
+        const int64_t per_pair = std::max(2 * n_ti * n_cf, n_tf * n_cd);
+        if ((int64_t)D.max_tokens * D.top_k * per_pair >= ((int64_t)1 << 31))
+            return fail(RVQ_MOE_EINVAL, "max_tokens=%d: one call would exceed 2^31 work units", D.max_tokens);
+    }
     if (D.cache_slots < 0) return fail(RVQ_MOE_EINVAL, "cache_slots=%d < 0", D.cache_slots);
     if (D.cache_slots > 0 && D.cache_slots < D.top_k)
         return fail(RVQ_MOE_EBUDGET, "cache_slots=%d below one token's working set (top_k=%d)", D.cache_slots,

@@ -84,6 +84,12 @@ __device__ inline void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "me
 struct Workspace {
     double *logits;     // [T][E] fp64 router logits
     double *sel;        // [T][k] fp64 logits of the selected experts, by rank
+    double *route_logits;  // router logit slots (route_logit_slots()); unpublished slots hold a marker NaN:
+                           // [max_tokens][E] for several tokens, then [2][E] logits and [2][kMaxTopK]
+                           // selected logits for one token (alternating buffers)
+    int64_t route_cap;     // max_tokens * E
+    int route_parity;      // buffer of the next one-token call
+    bool route_one;        // the one-token kernel fits (all E workgroups resident)
     float *part_gu;     // [T*k][2][n_tiles_in][ffn_pad] partial gate/up sums
     int *cntA;          // [T*k] finished gate/up chunks per pair (self-resetting)
     int *gbar;          // grid arrival counters of the persistent kernel (self-resetting)
@@ -101,7 +107,9 @@ constexpr int kGbarInts = 4 * 65;  // 4 grid barriers x (64 group counters + top
 hipError_t launch_repack(const Geometry &g, const uint8_t *canon, uint8_t *internal, int n_experts,
                          hipStream_t s);
 hipError_t launch_transpose(const float *W, float *Wt, int d, int E, hipStream_t s);
-hipError_t launch_route(const Geometry &g, const Workspace &w, const float *x, const float *Wt, int T, int pre,
+int64_t route_logit_slots(int64_t max_tokens, int E);
+hipError_t init_route(Workspace &w, int E, int64_t max_tokens, int n_cu, hipStream_t s);
+hipError_t launch_route(const Geometry &g, Workspace &w, const float *x, const float *Wt, int T, int pre,
                         double eps, int32_t *ids, float *gates, hipStream_t s);
 hipError_t layer_blocks_per_cu(int cb_dtype, int *out);
 hipError_t launch_layer(const Geometry &g, const Workspace &w, const uint8_t *codes, const void *cbs,

@@ -293,11 +293,20 @@ __device__ __forceinline__ float sum_chunk(const float *lut, const u32x4 &q0, co
     return reduce16(v, l);
 }
 
-__device__ __forceinline__ void load_chunk(const uint8_t *blk, int lane, u32x4 &q0, u32x4 &q1, u32x4 &q2) {
+// nt: streaming (non-temporal) loads, for codes no later segment of the call
+// re-reads; otherwise ordinary loads, so that the next token of an expert group
+// finds the tile in L2 or the Infinity Cache.
+__device__ __forceinline__ void load_chunk(const uint8_t *blk, int lane, u32x4 &q0, u32x4 &q1, u32x4 &q2, bool nt) {
     const u32x4 *p = reinterpret_cast<const u32x4 *>(blk) + lane;
-    q0 = __builtin_nontemporal_load(p);
-    q1 = __builtin_nontemporal_load(p + 64);
-    q2 = __builtin_nontemporal_load(p + 128);
+    if (nt) {  // uniform branch
+        q0 = __builtin_nontemporal_load(p);
+        q1 = __builtin_nontemporal_load(p + 64);
+        q2 = __builtin_nontemporal_load(p + 128);
+    } else {
+        q0 = p[0];
+        q1 = p[64];
+        q2 = p[128];
+    }
 }
 
 // Row totals of the chunks being gathered are staged in LDS, in the free
@@ -316,7 +325,7 @@ __device__ __forceinline__ float *stage_piece(float *lut, int i) { return lut + 
 // chunk being summed, so the wait before summing one chunk leaves the next
 // chunk's three loads in flight (vmcnt completes in order).
 __device__ __forceinline__ void gather_range(float *lut, const uint8_t *tile_base, int c0, int c1, u32x4 p0,
-                                             u32x4 p1, u32x4 p2) {
+                                             u32x4 p1, u32x4 p2, bool nt) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, l = lane & 31;
     const int row_in = (lane >> 5) * 16 + (l >> 1);
     int q = c0 + wave;
@@ -329,7 +338,7 @@ __device__ __forceinline__ void gather_range(float *lut, const uint8_t *tile_bas
             if (!(lane & 1)) stage_piece(lut, q - c0)[row_in] = sum;
             return;
         }
-        load_chunk(tile_base + (int64_t)qn * kChunkBytes, lane, n0, n1, n2);
+        load_chunk(tile_base + (int64_t)qn * kChunkBytes, lane, n0, n1, n2, nt);
         __builtin_amdgcn_sched_barrier(0);  // issue the prefetch before any use of the current chunk
         {
             const float sum = sum_chunk(lut, p0, p1, p2, l);
@@ -342,7 +351,7 @@ __device__ __forceinline__ void gather_range(float *lut, const uint8_t *tile_bas
             if (!(lane & 1)) stage_piece(lut, q - c0)[row_in] = sum;
             return;
         }
-        load_chunk(tile_base + (int64_t)qn * kChunkBytes, lane, p0, p1, p2);
+        load_chunk(tile_base + (int64_t)qn * kChunkBytes, lane, p0, p1, p2, nt);
         __builtin_amdgcn_sched_barrier(0);
         {
             const float sum = sum_chunk(lut, n0, n1, n2, l);
@@ -372,15 +381,15 @@ __device__ __forceinline__ void flush_rows_add(float *lut, float *out, int c0, i
 
 // Whole segment: gather [c0, c1) in sub-ranges of at most kStagePieces chunks,
 // flushing each.  (p0, p1, p2) hold this wave's first chunk of the segment.
-// (p0, p1, p2) hold this wave's first chunk of the segment.
 template <bool kAdd>
 __device__ __forceinline__ void gather_segment(float *lut, const uint8_t *tile_base, int c0, int c1, float *out,
-                                               int n_rows, u32x4 p0, u32x4 p1, u32x4 p2) {
+                                               int n_rows, u32x4 p0, u32x4 p1, u32x4 p2, bool nt) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     for (int s0 = c0; s0 < c1; s0 += kStagePieces) {
         const int s1 = min(c1, s0 + kStagePieces);
-        if (s0 != c0 && s0 + wave < s1) load_chunk(tile_base + (int64_t)(s0 + wave) * kChunkBytes, lane, p0, p1, p2);
-        gather_range(lut, tile_base, s0, s1, p0, p1, p2);
+        if (s0 != c0 && s0 + wave < s1)
+            load_chunk(tile_base + (int64_t)(s0 + wave) * kChunkBytes, lane, p0, p1, p2, nt);
+        gather_range(lut, tile_base, s0, s1, p0, p1, p2, nt);
         __syncthreads();
         if (kAdd)
             flush_rows_add(lut, out, s0, s1, n_rows);
@@ -535,38 +544,150 @@ struct SegB {
     int p, ft, c0, c1, e;
 };
 
-// Expert ids of the pairs a workgroup touches, cached in LDS at kernel start so
-// that no segment start waits on a global load: pairs [base, base + n) of
-// phase A and of phase B (n <= kIdCache; beyond that, the global array).
+// Order of the (token, expert) pairs inside a call (the token x expert
+// permutation).  The phases walk groups of positions.  With the order table
+// (T > 1 and P <= kOrderMax), positions are pairs sorted by (expert, pair)
+// and a group is every pair routed to one expert, so a group's tokens stream
+// the same code tile one after another (re-reads hit L2 / the Infinity Cache:
+// each expert's codes come from HBM about once per call).  Without it (one
+// token, or large P), every pair is its own group in pair order.  Every
+// workgroup derives the same table, deterministically, in LDS.
+constexpr int kOrderMax = 512;
 constexpr int kIdCache = 128;
-struct IdCache {
+struct Order {
+    bool tab;
+    const int *info;      // [P] position -> group start | group size << 16
+    const short *pair;    // [P] position -> pair
+    const short *expert;  // [P] position -> expert id (may be out of range)
+    // without the table: expert ids of the positions a workgroup touches
     int a_base, a_n, b_base, b_n;
-    const int32_t *ids;
     const int *lds;  // [2][kIdCache]
-    __device__ int a(int p) const { return (p - a_base) < a_n ? lds[p - a_base] : ids[p]; }
-    __device__ int b(int p) const { return (p - b_base) < b_n ? lds[kIdCache + p - b_base] : ids[p]; }
+    const int32_t *ids;
+    // (LDS reads give per-lane registers; the values are uniform, so they are
+    // moved to scalar registers and the segment arithmetic stays scalar)
+    __device__ void group(int q, int &gs, int &gn) const {
+        if (tab) {
+            const int v = __builtin_amdgcn_readfirstlane(info[q]);
+            gs = v & 0xffff;
+            gn = v >> 16;
+        } else {
+            gs = q;
+            gn = 1;
+        }
+    }
+    __device__ int pair_at(int pos) const { return tab ? __builtin_amdgcn_readfirstlane(pair[pos]) : pos; }
+    __device__ int expert_a(int pos) const {
+        return __builtin_amdgcn_readfirstlane(
+            tab ? expert[pos] : ((pos - a_base) < a_n ? lds[pos - a_base] : ids[pos]));
+    }
+    __device__ int expert_b(int pos) const {
+        return __builtin_amdgcn_readfirstlane(
+            tab ? expert[pos] : ((pos - b_base) < b_n ? lds[kIdCache + pos - b_base] : ids[pos]));
+    }
 };
 
-__device__ inline SegA seg_a(int64_t u, int64_t u1, int n_ti, int n_cf, const IdCache &ic) {
+// Build the order table in LDS (all threads).  tmp: scratch of at least
+// (E + 1) * (kOrderMax / 64) * 8 + 2 * (E + 1) * 4 bytes (the table area, idle
+// here).  Ids outside [0, E) form a last group of their own.
+__device__ void build_order(const int32_t *ids, int P, int E, char *tmp, int *info, short *pair, short *expert) {
+    constexpr int kW = kOrderMax / 64;
+    const int NE = E + 1;
+    uint64_t *mask = reinterpret_cast<uint64_t *>(tmp);  // [NE][kW] pair bitmask per expert
+    int *cnt = reinterpret_cast<int *>(mask + (size_t)NE * kW);
+    int *off = cnt + NE;
+    for (int i = threadIdx.x; i < NE * kW; i += kBlock) mask[i] = 0;
+    for (int i = threadIdx.x; i < NE; i += kBlock) cnt[i] = 0;
+    __syncthreads();
+    for (int p = threadIdx.x; p < P; p += kBlock) {
+        int e = load_counter(ids + p);
+        if (e < 0 || e >= E) e = E;
+        atomicOr(reinterpret_cast<unsigned long long *>(mask + (size_t)e * kW + (p >> 6)), 1ull << (p & 63));
+        atomicAdd(cnt + e, 1);
+        expert[p] = (short)e;  // temporarily indexed by pair
+    }
+    __syncthreads();
+    if (threadIdx.x < 64) {  // exclusive scan of cnt[0..NE) by one wave
+        const int lane = threadIdx.x, per = (NE + 63) / 64;
+        int sum = 0;
+        for (int i = lane * per; i < min(NE, (lane + 1) * per); i++) sum += cnt[i];
+        int incl = sum;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int v = __shfl_up(incl, o);
+            if (lane >= o) incl += v;
+        }
+        int run = incl - sum;
+        for (int i = lane * per; i < min(NE, (lane + 1) * per); i++) {
+            off[i] = run;
+            run += cnt[i];
+        }
+    }
+    __syncthreads();
+    int my_e[(kOrderMax + kBlock - 1) / kBlock];
+    int my_pos[(kOrderMax + kBlock - 1) / kBlock];
+#pragma unroll
+    for (int r = 0; r < (kOrderMax + kBlock - 1) / kBlock; r++) {
+        const int p = threadIdx.x + r * kBlock;
+        my_e[r] = my_pos[r] = -1;
+        if (p < P) {
+            const int e = expert[p];
+            const uint64_t *m = mask + (size_t)e * kW;
+            int rank = __popcll(m[p >> 6] & ((1ull << (p & 63)) - 1));
+            for (int w = 0; w < (p >> 6); w++) rank += __popcll(m[w]);
+            my_e[r] = e;
+            my_pos[r] = off[e] + rank;
+        }
+    }
+    __syncthreads();  // all reads of expert[] by pair done before it is rewritten by position
+#pragma unroll
+    for (int r = 0; r < (kOrderMax + kBlock - 1) / kBlock; r++) {
+        const int p = threadIdx.x + r * kBlock;
+        if (p < P) {
+            const int e = my_e[r], pos = my_pos[r];
+            pair[pos] = (short)p;
+            expert[pos] = (short)e;
+            info[pos] = off[e] | (cnt[e] << 16);
+        }
+    }
+    __syncthreads();
+}
+
+// First unit of range r when n units are split over G workgroups.
+__device__ inline int range_lo(int n, int r, int G) { return (int)((int64_t)n * r / G); }
+
+// Work units (one chunk of one pair's matrix tile) are numbered in 32 bits:
+// a call has fewer than 2^31 of them (checked when the handle is opened).
+__device__ inline SegA seg_a(int u, int u1, int n_ti, int n_cf, const Order &o) {
     SegA s;
-    const int64_t seg = u / n_cf;
-    s.c0 = (int)(u % n_cf);
-    s.c1 = (int)min((int64_t)n_cf, s.c0 + (u1 - u));
-    s.tile = (int)(seg % n_ti);
-    s.m = (int)((seg / n_ti) & 1);
-    s.p = (int)(seg / (2 * n_ti));
-    s.e = ic.a(s.p);
+    const int per = 2 * n_ti * n_cf;
+    int gs, gn;
+    o.group(u / per, gs, gn);
+    int w = u - gs * per;
+    s.c0 = w % n_cf;
+    w /= n_cf;
+    const int j = w % gn;
+    w /= gn;
+    s.tile = w % n_ti;
+    s.m = w / n_ti;
+    s.c1 = min(n_cf, s.c0 + (u1 - u));
+    s.p = o.pair_at(gs + j);
+    s.e = o.expert_a(gs + j);
     return s;
 }
 
-__device__ inline SegB seg_b(int64_t u, int64_t u1, int n_tf, int n_cd, const IdCache &ic) {
+__device__ inline SegB seg_b(int u, int u1, int n_tf, int n_cd, const Order &o) {
     SegB s;
-    const int64_t seg = u / n_cd;
-    s.c0 = (int)(u % n_cd);
-    s.c1 = (int)min((int64_t)n_cd, s.c0 + (u1 - u));
-    s.ft = (int)(seg % n_tf);
-    s.p = (int)(seg / n_tf);
-    s.e = ic.b(s.p);
+    const int per = n_tf * n_cd;
+    int gs, gn;
+    o.group(u / per, gs, gn);
+    int w = u - gs * per;
+    s.c0 = w % n_cd;
+    w /= n_cd;
+    const int j = w % gn;
+    s.ft = w / gn;
+    s.c1 = min(n_cd, s.c0 + (u1 - u));
+    s.p = o.pair_at(gs + j);
+    s.e = o.expert_b(gs + j);
     return s;
 }
 
@@ -658,28 +779,41 @@ __device__ void route_phase(const LayerArgs &a, double *dred, double *lg_lds, fl
     const int P = a.T * g.k;
     for (int i = threadIdx.x; i < P; i += kBlock) lg_lds[i] = load_coherent(a.sel + i);
     __syncthreads();
+    // one exp per selected logit, then each gate sums its token's k in slot order
+    double *ex = lg_lds + kRouteMaxPairs;
+    for (int i = threadIdx.x; i < P; i += kBlock) ex[i] = exp(lg_lds[i] - lg_lds[(i / g.k) * g.k]);
+    __syncthreads();
     for (int i = threadIdx.x; i < P; i += kBlock) {
         const int t = i / g.k;
-        const double top = lg_lds[t * g.k];
         double sum = 0.0;
-        for (int j = 0; j < g.k; j++) sum += exp(lg_lds[t * g.k + j] - top);
-        const float gt = (float)(exp(lg_lds[i] - top) / sum);
+        for (int j = 0; j < g.k; j++) sum += ex[t * g.k + j];
+        const float gt = (float)(ex[i] / sum);
         gate_lds[i] = gt;
         if (wg == 0) const_cast<float *>(a.gates)[i] = gt;
     }
     __syncthreads();
 }
 
-template <int CB, bool kRoute>
+// kNT: codes are read with streaming loads.  Off for a batch in expert-grouped
+// order, whose re-reads of a tile by the next token of a group should hit the
+// caches.
+template <int CB, bool kRoute, bool kNT>
 __global__ __launch_bounds__(kBlock) void k_layer(LayerArgs a) {
-    __shared__ float lut[kLutWords];
+    __shared__ __align__(16) float lut[kLutWords];  // also 8-byte staging (logits, order masks)
     __shared__ float vs[kVec][kTileSlices];  // [element][slice]
     __shared__ double red[kWaves];
-    static_assert(kMaxExperts * sizeof(double) <= kLutWords * sizeof(float), "logit staging must fit the table area");
+    static_assert(kMaxExperts * sizeof(double) <= kLutWords * sizeof(float) &&
+                      2 * kRouteMaxPairs * sizeof(double) <= kLutWords * sizeof(float),
+                  "logit staging must fit the table area");
     __shared__ float hred[4][256][2];
     __shared__ float red2[kWaves];
     const Geometry &g = a.g;
     const int G = gridDim.x, wg = blockIdx.x;
+    // range index: consecutive ranges go to workgroups on the same XCD (workgroups
+    // are dealt round-robin over the 8 XCDs), so a code tile split between two
+    // neighbouring ranges, or re-read by the next token of its group, stays in
+    // one XCD's L2
+    const int rw = (G % 8 == 0) ? (wg % 8) * (G / 8) + wg / 8 : wg;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int P = a.T * g.k;
     const int n_ti = g.m[0].n_tiles, n_cf = g.m[0].n_chunks;
@@ -694,19 +828,31 @@ __global__ __launch_bounds__(kBlock) void k_layer(LayerArgs a) {
         route_phase(a, red, reinterpret_cast<double *>(lut), gate_lds, reinterpret_cast<int *>(hred));
         gate_src = gate_lds;
     }
+    // ---------------- pair order (the token x expert permutation)
     __shared__ int id_lds[2 * kIdCache];
-    IdCache ic;
-    {
-        const int64_t nA = (int64_t)P * 2 * n_ti * n_cf, nB = (int64_t)P * n_tf * n_cd;
-        const int64_t a0 = nA * wg / G, a1 = nA * (wg + 1) / G, b0 = nB * wg / G, b1 = nB * (wg + 1) / G;
-        ic.ids = a.ids;
-        ic.lds = id_lds;
-        ic.a_base = (int)(a0 / n_cf / (2 * n_ti));
-        ic.a_n = a1 > a0 ? min(kIdCache, (int)((a1 - 1) / n_cf / (2 * n_ti)) - ic.a_base + 1) : 0;
-        ic.b_base = (int)(b0 / n_cd / n_tf);
-        ic.b_n = b1 > b0 ? min(kIdCache, (int)((b1 - 1) / n_cd / n_tf) - ic.b_base + 1) : 0;
-        if (threadIdx.x < ic.a_n) id_lds[threadIdx.x] = load_counter(a.ids + ic.a_base + threadIdx.x);
-        if (threadIdx.x < ic.b_n) id_lds[kIdCache + threadIdx.x] = load_counter(a.ids + ic.b_base + threadIdx.x);
+    __shared__ int o_info[kOrderMax];
+    __shared__ short o_pair[kOrderMax], o_expert[kOrderMax];
+    Order ord;
+    ord.tab = a.T > 1 && P <= kOrderMax;
+    ord.info = o_info;
+    ord.pair = o_pair;
+    ord.expert = o_expert;
+    ord.ids = a.ids;
+    ord.lds = id_lds;
+    ord.a_n = ord.b_n = 0;
+    ord.a_base = ord.b_base = 0;
+    if (ord.tab) {
+        build_order(a.ids, P, g.E, reinterpret_cast<char *>(lut), o_info, o_pair, o_expert);
+    } else {
+        // pair order: cache the expert ids of the pairs this workgroup's ranges touch
+        const int a0 = range_lo(P * 2 * n_ti * n_cf, rw, G), a1 = range_lo(P * 2 * n_ti * n_cf, rw + 1, G);
+        const int b0 = range_lo(P * n_tf * n_cd, rw, G), b1 = range_lo(P * n_tf * n_cd, rw + 1, G);
+        ord.a_base = a0 / (2 * n_ti * n_cf);
+        ord.a_n = a1 > a0 ? min(kIdCache, (a1 - 1) / (2 * n_ti * n_cf) - ord.a_base + 1) : 0;
+        ord.b_base = b0 / (n_tf * n_cd);
+        ord.b_n = b1 > b0 ? min(kIdCache, (b1 - 1) / (n_tf * n_cd) - ord.b_base + 1) : 0;
+        if (threadIdx.x < ord.a_n) id_lds[threadIdx.x] = load_counter(a.ids + ord.a_base + threadIdx.x);
+        if (threadIdx.x < ord.b_n) id_lds[kIdCache + threadIdx.x] = load_counter(a.ids + ord.b_base + threadIdx.x);
         __syncthreads();
     }
 
@@ -721,9 +867,9 @@ __global__ __launch_bounds__(kBlock) void k_layer(LayerArgs a) {
 
     // ---------------- phase A: gate and up
     {
-        const int64_t nA = (int64_t)P * 2 * n_ti * n_cf;
-        int64_t u = nA * wg / G;
-        const int64_t u1 = nA * (wg + 1) / G;
+        const int nA = P * 2 * n_ti * n_cf;
+        int u = range_lo(nA, rw, G);
+        const int u1 = range_lo(nA, rw + 1, G);
         float xv = 0.f;  // this thread's raw input element of the segment's tile
         auto prefetch = [&](const SegA &sg) {
             if (sg.e >= 0 && sg.e < g.E) cb_load<CB>(cb, a.cbs, sg.e, sg.m);
@@ -732,13 +878,13 @@ __global__ __launch_bounds__(kBlock) void k_layer(LayerArgs a) {
         };
         SegA cur{};
         if (u < u1) {
-            cur = seg_a(u, u1, n_ti, n_cf, ic);
+            cur = seg_a(u, u1, n_ti, n_cf, ord);
             prefetch(cur);
         }
         while (u < u1) {
-            const int64_t un = u + (cur.c1 - cur.c0);
+            const int un = u + (cur.c1 - cur.c0);
             SegA nxt{};
-            if (un < u1) nxt = seg_a(un, u1, n_ti, n_cf, ic);
+            if (un < u1) nxt = seg_a(un, u1, n_ti, n_cf, ord);
             if (cur.e >= 0 && cur.e < g.E) {
                 const uint8_t *base = a.codes + (int64_t)cur.e * g.rec_int + g.m[cur.m].off +
                                       (int64_t)cur.tile * n_cf * kChunkBytes;
@@ -753,13 +899,13 @@ __global__ __launch_bounds__(kBlock) void k_layer(LayerArgs a) {
                 }
                 u32x4 p0, p1, p2;
                 if (cur.c0 + wave < cur.c1)
-                    load_chunk(base + (int64_t)(cur.c0 + wave) * kChunkBytes, lane, p0, p1, p2);
+                    load_chunk(base + (int64_t)(cur.c0 + wave) * kChunkBytes, lane, p0, p1, p2, kNT);
                 __syncthreads();
                 build_lut<CB>(lut, vs, tile_exponent(red2));
                 __syncthreads();
                 if (un < u1) prefetch(nxt);
                 float *out = a.part_gu + (((int64_t)cur.p * 2 + cur.m) * n_ti + cur.tile) * g.ffn_pad;
-                gather_segment<false>(lut, base, cur.c0, cur.c1, out, 0, p0, p1, p2);
+                gather_segment<false>(lut, base, cur.c0, cur.c1, out, 0, p0, p1, p2, kNT);
             } else {
                 if (threadIdx.x == 0) atomicOr(a.err, 1);
                 if (un < u1) prefetch(nxt);
@@ -772,26 +918,26 @@ __global__ __launch_bounds__(kBlock) void k_layer(LayerArgs a) {
 
     // ---------------- phase B: SwiGLU finish, gate, down
     {
-        const int64_t nB = (int64_t)P * n_tf * n_cd;
-        int64_t u = nB * wg / G;
-        const int64_t u1 = nB * (wg + 1) / G;
+        const int nB = P * n_tf * n_cd;
+        int u = range_lo(nB, rw, G);
+        const int u1 = range_lo(nB, rw + 1, G);
         const int needA = 2 * n_ti * n_cf;
         SegB cur{};
         if (u < u1) {
-            cur = seg_b(u, u1, n_tf, n_cd, ic);
+            cur = seg_b(u, u1, n_tf, n_cd, ord);
             if (cur.e >= 0 && cur.e < g.E) cb_load<CB>(cb, a.cbs, cur.e, 2);
         }
         while (u < u1) {
-            const int64_t un = u + (cur.c1 - cur.c0);
+            const int un = u + (cur.c1 - cur.c0);
             SegB nxt{};
-            if (un < u1) nxt = seg_b(un, u1, n_tf, n_cd, ic);
+            if (un < u1) nxt = seg_b(un, u1, n_tf, n_cd, ord);
             if (cur.e >= 0 && cur.e < g.E) {
                 const uint8_t *base = a.codes + (int64_t)cur.e * g.rec_int + g.m[2].off +
                                       (int64_t)cur.ft * n_cd * kChunkBytes;
                 cb_store<CB>(lut, cb);
                 u32x4 p0, p1, p2;
                 if (cur.c0 + wave < cur.c1)
-                    load_chunk(base + (int64_t)(cur.c0 + wave) * kChunkBytes, lane, p0, p1, p2);
+                    load_chunk(base + (int64_t)(cur.c0 + wave) * kChunkBytes, lane, p0, p1, p2, kNT);
                 wait_count(&a.cntA[cur.p], needA, a.err);
                 finish_h(a, gate_src, cur.p, cur.ft, vs, hred, red2);
                 __syncthreads();
@@ -802,7 +948,8 @@ __global__ __launch_bounds__(kBlock) void k_layer(LayerArgs a) {
                     wait_count(a.gbar + kMaxGridGroups, G, a.err);
                     y_ready = true;
                 }
-                gather_segment<true>(lut, base, cur.c0, cur.c1, a.y + (size_t)(cur.p / g.k) * g.d, g.d, p0, p1, p2);
+                float *yt = a.y + (size_t)(cur.p / g.k) * g.d;
+                gather_segment<true>(lut, base, cur.c0, cur.c1, yt, g.d, p0, p1, p2, kNT);
             } else {
                 // an invalid id poisons its token's output (the error flag is already set)
                 if (!y_ready) {
@@ -834,6 +981,15 @@ __global__ __launch_bounds__(kBlock) void k_layer(LayerArgs a) {
     }
 }
 
+typedef void (*LayerKernel)(LayerArgs);
+static LayerKernel layer_kernel(int cb_dtype, bool route, bool nt) {
+    if (cb_dtype == 0)
+        return route ? (nt ? k_layer<0, true, true> : k_layer<0, true, false>)
+                     : (nt ? k_layer<0, false, true> : k_layer<0, false, false>);
+    return route ? (nt ? k_layer<1, true, true> : k_layer<1, true, false>)
+                 : (nt ? k_layer<1, false, true> : k_layer<1, false, false>);
+}
+
 hipError_t launch_layer(const Geometry &g, const Workspace &w, const uint8_t *codes, const void *cbs,
                         const float *Wt, const float *x, const int32_t *ids, const float *gates, float *y, int T,
                         int pre, int residual, double eps, bool route, hipStream_t s) {
@@ -843,24 +999,23 @@ hipError_t launch_layer(const Geometry &g, const Workspace &w, const uint8_t *co
     // (sized at open from the occupancy query); the inter-workgroup waits are
     // bounded, so a launch that somehow did not get all of them resident ends
     // with an error flag instead of hanging.
-    if (g.cb_dtype == 0) {
-        if (route)
-            hipLaunchKernelGGL((k_layer<0, true>), dim3(w.n_wg), dim3(kBlock), 0, s, a);
-        else
-            hipLaunchKernelGGL((k_layer<0, false>), dim3(w.n_wg), dim3(kBlock), 0, s, a);
-    } else {
-        if (route)
-            hipLaunchKernelGGL((k_layer<1, true>), dim3(w.n_wg), dim3(kBlock), 0, s, a);
-        else
-            hipLaunchKernelGGL((k_layer<1, false>), dim3(w.n_wg), dim3(kBlock), 0, s, a);
-    }
+    const bool group = T > 1 && T * g.k <= kOrderMax;  // the kernel takes the same decision
+    hipLaunchKernelGGL(layer_kernel(g.cb_dtype, route, !group), dim3(w.n_wg), dim3(kBlock), 0, s, a);
     return hipGetLastError();
 }
 
 hipError_t layer_blocks_per_cu(int cb_dtype, int *out) {
-    // the routing variant uses the same resources or more: size the grid by it
-    return cb_dtype == 0 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(out, k_layer<0, true>, kBlock, 0)
-                         : hipOccupancyMaxActiveBlocksPerMultiprocessor(out, k_layer<1, true>, kBlock, 0);
+    // the grid must be resident under every variant: take the smallest occupancy
+    int best = 1 << 30;
+    for (int v = 0; v < 4; v++) {
+        int n = 0;
+        const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, layer_kernel(cb_dtype, v & 1, v & 2),
+                                                                          kBlock, 0);
+        if (e != hipSuccess) return e;
+        best = n < best ? n : best;
+    }
+    *out = best;
+    return hipSuccess;
 }
 
 }  // namespace rvq

@@ -13,13 +13,17 @@
 // (sum_i x_i W[i][e]) / r with r = sqrt(mean(x^2) + eps) computed in fp64,
 // equal in exact arithmetic to sum_i (x_i / r) W[i][e].
 //
-// MI355X mapping: the router matrix is stored transposed ([E][d]) so that a
-// workgroup streams one expert's column as contiguous 1 KB wave loads (its 4
-// waves take a quarter each) for up to TT tokens.  Selection avoids a serial
-// chain of k argmax rounds: a second launch ranks every expert in parallel (one
-// wave counts the experts ahead of it) and the k with rank < k write their id
-// and logit to that slot; a third gives each token one wave for the softmax.
-// Wave reductions use DPP row moves and permlane swaps (no LDS round trips).
+// MI355X mapping: one launch.  The router matrix is stored transposed ([E][d])
+// so that a workgroup streams one expert's column as contiguous 1 KB wave
+// loads (its 4 waves take a quarter each) for up to TT tokens.  Each workgroup
+// publishes its logits and then raises its own flag (the call's epoch number:
+// no counter, so no atomics serialised on one address); workgroup 0 of a token
+// block waits for the block's E flags and selects for those tokens while the
+// rest have already exited.
+// Selection avoids a serial chain of k argmax rounds: every expert's rank is
+// counted in parallel (the experts ahead of it in the order), and the k with
+// rank < k write their id to that slot; then the k gates.  Wave reductions use
+// DPP row moves and permlane swaps (no LDS round trips).
 #include <math.h>
 
 #include "internal.hpp"
@@ -94,43 +98,234 @@ __device__ inline double wave_sum(double v) {
 // NaN logits rank below every number (and among themselves by id).
 __device__ inline double rank_value(double v) { return isnan(v) ? -INFINITY : v; }
 
-// grid (E, ceil(T / TT)), 256 threads: the 4 waves of a workgroup each take a
-// quarter of expert e's column (float4 granules) for TT tokens.
+// (va, expert ia) comes before (vb, ib) in the strict order: logit descending, id ascending.
+__device__ inline bool before(double va, int ia, double vb, int ib) { return va > vb || (va == vb && ia < ib); }
+
+// Top-k selection in one 256-thread workgroup by radix select.  Logits become
+// order-preserving 64-bit keys (NaN ranks as -inf, -0 as +0, so equal keys are
+// exactly the ties of the fp64 order).  The leading bits every key shares are
+// fixed first (a block-wide AND / OR).  Then four bits at a time, a 16-bin
+// histogram of the candidates' next digit fixes the digit of the k-th largest
+// key, until the candidates sharing the fixed prefix are exactly the ones still
+// needed (or all 64 bits are fixed: then equal keys go by lower id).  Each wave
+// counts its digits with ballots (no contended LDS atomics), every thread reads
+// the 16 bins and finds the digit itself, and the histograms rotate over three
+// buffers, so a pass costs one barrier.
+constexpr int kSelPer = kMaxExperts / 256;  // experts per thread
+
+__device__ inline uint64_t order_key(double v) {
+    v = rank_value(v);
+    if (v == 0.0) v = 0.0;
+    const uint64_t b = (uint64_t)__double_as_longlong(v);
+    return (b >> 63) ? ~b : (b | 0x8000000000000000ull);
+}
+
+// Sum over each row of 16 lanes (every lane of the row gets it).
+__device__ inline int row16_sum(int v) {
+    v += (int)RVQ_DPP_U((uint32_t)v, kDppXor1);
+    v += (int)RVQ_DPP_U((uint32_t)v, kDppXor2);
+    v += (int)RVQ_DPP_U((uint32_t)v, kDppRor4);
+    v += (int)RVQ_DPP_U((uint32_t)v, kDppRor8);
+    return v;
+}
+
+// Bitwise AND (and OR) over the wave, every lane gets it.
+__device__ inline uint32_t wave_and(uint32_t v) {
+    v &= RVQ_DPP_U(v, kDppXor1);
+    v &= RVQ_DPP_U(v, kDppXor2);
+    v &= RVQ_DPP_U(v, kDppRor4);
+    v &= RVQ_DPP_U(v, kDppRor8);
+    const bool o16 = threadIdx.x & 16, o32 = threadIdx.x & 32;
+    v &= swap_other(v, false, o16);
+    v &= swap_other(v, true, o32);
+    return v;
+}
+
+struct SelectLds {
+    uint64_t key[kMaxExperts];
+    int hist[3][16];
+    uint32_t red[4][4];  // per wave: AND lo, AND hi, ~OR lo, ~OR hi
+    int n_cand;
+    uint64_t cand_key[kMaxTopK];
+    double cand_v[kMaxTopK];
+    int cand_id[kMaxTopK];
+};
+
+// Expert i = threadIdx.x + 256 r (i < E) has value v[r] (its rank value) and
+// key[r].  Writes the k selected ids in the strict order (logit descending, id
+// ascending) to ids_out and their values to v_out (LDS).
+__device__ void select_topk(const uint64_t (&key)[kSelPer], const double (&v)[kSelPer], int E, int k, SelectLds &L,
+                            int32_t *ids_out, double *v_out) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // ---- bits shared by every key
+    uint64_t all_and = ~0ull, all_nor = ~0ull;  // AND of keys, AND of complemented keys
+#pragma unroll
+    for (int r = 0; r < kSelPer; r++) {
+        if (tid + 256 * r < E) {
+            L.key[tid + 256 * r] = key[r];
+            all_and &= key[r];
+            all_nor &= ~key[r];
+        }
+    }
+    {
+        const uint32_t a0 = wave_and((uint32_t)all_and), a1 = wave_and((uint32_t)(all_and >> 32));
+        const uint32_t n0 = wave_and((uint32_t)all_nor), n1 = wave_and((uint32_t)(all_nor >> 32));
+        if (lane == 0) {
+            L.red[wave][0] = a0;
+            L.red[wave][1] = a1;
+            L.red[wave][2] = n0;
+            L.red[wave][3] = n1;
+        }
+    }
+    if (tid < 32) L.hist[tid >> 4][tid & 15] = 0;
+    if (tid == 0) L.n_cand = 0;
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < 4; w++) {
+        all_and &= ((uint64_t)L.red[w][1] << 32) | L.red[w][0];
+        all_nor &= ((uint64_t)L.red[w][3] << 32) | L.red[w][2];
+    }
+    const uint64_t differ = ~(all_and | all_nor);  // bits where two keys differ
+    int used = differ ? (__clzll((long long)differ) & ~3) : 64;
+    uint64_t prefix = used == 0 ? 0 : (used == 64 ? all_and : all_and >> (64 - used));
+    int need = k, buf = 0;
+    bool all_in = false;
+    // ---- four bits per pass
+    while (used < 64) {
+        int *h = L.hist[buf];
+        int cnt = 0;  // lane j < 16: this wave's count of digit j
+#pragma unroll
+        for (int r = 0; r < kSelPer; r++) {
+            const bool live = tid + 256 * r < E && (used == 0 || (key[r] >> (64 - used)) == prefix);
+            if (__ballot(live) == 0) continue;
+            const int dg = (int)((key[r] >> (60 - used)) & 15);
+#pragma unroll
+            for (int j = 0; j < 16; j++) {
+                const int c = __popcll(__ballot(live && dg == j));
+                cnt += lane == j ? c : 0;
+            }
+        }
+        if (lane < 16 && cnt) atomicAdd(&h[lane], cnt);
+        __syncthreads();
+        if (tid < 16) L.hist[buf == 0 ? 2 : buf - 1][tid] = 0;  // the buffer two passes ahead
+        int c[16];
+#pragma unroll
+        for (int j = 0; j < 16; j++) c[j] = h[j];
+        int dgt = 0, gt = 0, eq = 0, above = 0;
+#pragma unroll
+        for (int j = 15; j >= 0; j--) {
+            if (above < need && need <= above + c[j]) {
+                dgt = j;
+                gt = above;
+                eq = c[j];
+            }
+            above += c[j];
+        }
+        prefix = (prefix << 4) | (uint64_t)dgt;
+        used += 4;
+        need -= gt;
+        buf = buf == 2 ? 0 : buf + 1;
+        if (eq == need) {
+            all_in = true;
+            break;
+        }
+    }
+    // ---- the selected experts: prefix above the threshold's, or equal to it
+    // and (all of those are needed, or among the `need` lowest ids of equal keys)
+#pragma unroll
+    for (int r = 0; r < kSelPer; r++) {
+        const int i = tid + 256 * r;
+        if (i >= E) continue;
+        const uint64_t top = used == 64 ? key[r] : key[r] >> (64 - used);
+        bool in = top > prefix;
+        if (top == prefix) {
+            if (all_in) {
+                in = true;
+            } else {
+                int lower = 0;
+                for (int j = 0; j < i; j++) lower += L.key[j] == key[r];
+                in = lower < need;
+            }
+        }
+        if (in) {
+            const int slot = atomicAdd(&L.n_cand, 1);
+            L.cand_key[slot] = key[r];
+            L.cand_v[slot] = v[r];
+            L.cand_id[slot] = i;
+        }
+    }
+    __syncthreads();
+    // ---- order the k: a row of 16 lanes per candidate, each lane comparing a
+    // sixteenth of the others, summed across the row
+    for (int j = tid >> 4; j < k; j += 16) {
+        const uint64_t mk = L.cand_key[j];
+        const int mi = L.cand_id[j];
+        int ahead = 0;
+        for (int q = tid & 15; q < k; q += 16) {
+            const uint64_t ok = L.cand_key[q];
+            ahead += ok > mk || (ok == mk && L.cand_id[q] < mi);
+        }
+        const int rank = row16_sum(ahead);
+        if ((tid & 15) == 0) {
+            ids_out[rank] = mi;
+            v_out[rank] = L.cand_v[j];
+        }
+    }
+    __syncthreads();
+}
+
+// Logit slots hold this NaN until written.  It is a signalling NaN, which no
+// arithmetic result is (results are quiet NaNs at most), so a slot holds it
+// exactly while its logit is not yet published.
+constexpr uint64_t kUnpublished = 0x7FF4DEAD7FF4DEADull;
+constexpr uint32_t kUnpublishedHalf = 0x7FF4DEADu;
+
+// Router dot products of expert e (= blockIdx.x) for tokens [t0, t0 + nt):
+// 256 threads; the 4 waves each take a quarter of the expert's column (float4
+// granules), all of a lane's loads of a pass in flight together.  out[t] (LDS)
+// gets the logit, sum / r, for every thread after the internal barrier.
 template <int TT>
-__global__ __launch_bounds__(256) void k_route(const float *__restrict__ x, const float *__restrict__ Wt, int d, int E,
-                                               int T, int pre, double eps, double *__restrict__ logits) {
+__device__ void router_dot(const float *__restrict__ x, const float *__restrict__ Wt, int d, int t0, int nt, int pre,
+                           double eps, double *out) {
     const int e = blockIdx.x;
-    const int t0 = blockIdx.y * TT;
-    const int nt = min(TT, T - t0);
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int n4 = d / 4;
     const int g0 = n4 * wave / 4, g1 = n4 * (wave + 1) / 4;
     const float4 *w4 = reinterpret_cast<const float4 *>(Wt + (size_t)e * d);
+    constexpr int kU = TT == 1 ? 8 : 2;  // float4 loads per lane per pass
     double acc[TT], ss[TT];
 #pragma unroll
     for (int t = 0; t < TT; t++) acc[t] = ss[t] = 0.0;
-    for (int i = g0 + lane; i < g1; i += 64 * 4) {
-        float4 wv[4];
+    for (int base = g0 + lane; base < g1; base += 64 * kU) {
+        // loads are unconditional (clamped index) so that all of them are in
+        // flight together; granules past the end are dropped where they are used
+        float4 wv[kU];
+        bool ok[kU];
 #pragma unroll
-        for (int u = 0; u < 4; u++) wv[u] = (i + 64 * u < g1) ? w4[i + 64 * u] : make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int u = 0; u < kU; u++) {
+            ok[u] = base + 64 * u < g1;
+            wv[u] = w4[min(base + 64 * u, g1 - 1)];
+        }
 #pragma unroll
         for (int t = 0; t < TT; t++) {
             if (t >= nt) break;
             const float4 *x4 = reinterpret_cast<const float4 *>(x + (size_t)(t0 + t) * d);
+            float4 xv[kU];
 #pragma unroll
-            for (int u = 0; u < 4; u++) {
-                if (i + 64 * u < g1) {
-                    const float4 xv = x4[i + 64 * u];
-                    acc[t] = fma((double)xv.x, (double)wv[u].x, acc[t]);
-                    acc[t] = fma((double)xv.y, (double)wv[u].y, acc[t]);
-                    acc[t] = fma((double)xv.z, (double)wv[u].z, acc[t]);
-                    acc[t] = fma((double)xv.w, (double)wv[u].w, acc[t]);
-                    if (pre) {
-                        ss[t] = fma((double)xv.x, (double)xv.x, ss[t]);
-                        ss[t] = fma((double)xv.y, (double)xv.y, ss[t]);
-                        ss[t] = fma((double)xv.z, (double)xv.z, ss[t]);
-                        ss[t] = fma((double)xv.w, (double)xv.w, ss[t]);
-                    }
+            for (int u = 0; u < kU; u++) xv[u] = x4[min(base + 64 * u, g1 - 1)];
+#pragma unroll
+            for (int u = 0; u < kU; u++) {
+                const double x0 = ok[u] ? (double)xv[u].x : 0.0, x1 = ok[u] ? (double)xv[u].y : 0.0;
+                const double x2 = ok[u] ? (double)xv[u].z : 0.0, x3 = ok[u] ? (double)xv[u].w : 0.0;
+                acc[t] = fma(x0, (double)wv[u].x, acc[t]);
+                acc[t] = fma(x1, (double)wv[u].y, acc[t]);
+                acc[t] = fma(x2, (double)wv[u].z, acc[t]);
+                acc[t] = fma(x3, (double)wv[u].w, acc[t]);
+                if (pre) {
+                    ss[t] = fma(x0, x0, ss[t]);
+                    ss[t] = fma(x1, x1, ss[t]);
+                    ss[t] = fma(x2, x2, ss[t]);
+                    ss[t] = fma(x3, x3, ss[t]);
                 }
             }
         }
@@ -152,60 +347,189 @@ __global__ __launch_bounds__(256) void k_route(const float *__restrict__ x, cons
         const double sa = red[0][t][0] + red[1][t][0] + red[2][t][0] + red[3][t][0];
         const double sq = red[0][t][1] + red[1][t][1] + red[2][t][1] + red[3][t][1];
         const double r = pre ? sqrt(sq / (double)d + eps) : 1.0;
-        logits[(size_t)(t0 + t) * E + e] = sa / r;
+        out[t] = sa / r;
+    }
+    __syncthreads();
+}
+
+// Several tokens: grid (E, ceil(T / TT)), 256 threads.  Workgroup (e, by)
+// stores its logits into slots that hold kUnpublished and exits; workgroup
+// (0, by) polls the block's slots until every logit is in (a bounded wait:
+// ~0.5 s, then err bit 2, so every workgroup always ends), selects, and puts
+// kUnpublished back for the next call.  No counters, so no atomics serialised
+// on one address, and the poll reads the logits themselves.
+template <int TT>
+__global__ __launch_bounds__(256) void k_route(const float *__restrict__ x, const float *__restrict__ Wt, int d, int E,
+                                               int k, int T, int pre, double eps, double *__restrict__ logits,
+                                               int *__restrict__ err, int32_t *__restrict__ ids,
+                                               float *__restrict__ gates) {
+    const int e = blockIdx.x;
+    const int t0 = blockIdx.y * TT;
+    const int nt = min(TT, T - t0);
+    __shared__ double lgt[TT];
+    router_dot<TT>(x, Wt, d, t0, nt, pre, eps, lgt);
+    if (threadIdx.x < nt) store_coherent(logits + (size_t)(t0 + threadIdx.x) * E + e, lgt[threadIdx.x]);
+    if (e != 0) return;
+
+    // ---- workgroup (0, by): wait for the block's logits, select, gates
+    __shared__ SelectLds L;
+    __shared__ double sel[kMaxTopK];
+    __shared__ double ex[kMaxTopK];
+    const uint64_t t_start = wall_clock64();
+    for (int t = t0; t < t0 + nt; t++) {
+        double *lt = logits + (size_t)t * E;
+        double v[kSelPer];
+        while (true) {
+            int ready = 1;
+#pragma unroll
+            for (int r = 0; r < kSelPer; r++) {
+                const int i = threadIdx.x + 256 * r;
+                v[r] = i < E ? load_coherent(lt + i) : -INFINITY;
+                ready &= (uint64_t)__double_as_longlong(v[r]) != kUnpublished;
+            }
+            if (__syncthreads_and(ready)) break;
+            if (wall_clock64() - t_start > 50000000ull) {  // 0.5 s at the 100 MHz constant clock
+                if (threadIdx.x == 0) atomicOr(err, 2);
+                break;
+            }
+            __builtin_amdgcn_s_sleep(1);
+        }
+        uint64_t key[kSelPer];
+#pragma unroll
+        for (int r = 0; r < kSelPer; r++) {
+            const int i = threadIdx.x + 256 * r;
+            if (i < E) store_coherent(lt + i, __longlong_as_double((long long)kUnpublished));  // for the next call
+            v[r] = rank_value(v[r]);
+            key[r] = order_key(v[r]);
+        }
+        select_topk(key, v, E, k, L, ids + (size_t)t * k, sel);
+        // softmax over the k selected logits (slot 0 is the largest), fp64: one
+        // exp per selected logit, summed in slot order
+        if (threadIdx.x < k) ex[threadIdx.x] = exp(sel[threadIdx.x] - sel[0]);
+        __syncthreads();
+        if (threadIdx.x < k) {
+            double sum = 0.0;
+            for (int j = 0; j < k; j++) sum += ex[j];
+            gates[(size_t)t * k + threadIdx.x] = (float)(ex[threadIdx.x] / sum);
+        }
+        __syncthreads();
     }
 }
 
-// Rank of every expert in the strict order (logit descending, id ascending):
-// one wave per (expert, token) counts the experts that precede it (E / 64
-// comparisons per lane, then a wave sum).  Exactly k experts get a rank < k;
-// each writes its id and logit into slot `rank` of the token's selection.
-// grid (ceil(E / 4), T), 256 threads.
-__global__ __launch_bounds__(256) void k_rank(const double *__restrict__ logits, int E, int k,
-                                              int32_t *__restrict__ ids, double *__restrict__ sel) {
-    const int t = blockIdx.y;
-    const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
-    const int lane = threadIdx.x & 63;
-    if (e >= E) return;
-    const double *lg = logits + (size_t)t * E;
-    const double me = rank_value(lg[e]);
-    double cnt = 0.0;
-    for (int o = lane; o < E; o += 64) {
-        const double v = rank_value(lg[o]);
-        cnt += (v > me || (v == me && o < e)) ? 1.0 : 0.0;
+// One token: grid (E), 256 threads, every workgroup resident at once (checked
+// when the handle is opened).  No workgroup selects for the others: each
+// publishes its logit, polls until all E are in, and counts the experts ahead
+// of its own in the strict order (logit descending, id ascending).  The k with
+// rank < k publish their logit into slot `rank`, poll the k slots, and write
+// their id and gate.  Buffers alternate between calls (parity), and each
+// workgroup puts kUnpublished into the other buffer's slots it owns, for the
+// next call: nobody can still be reading those.  Waits are bounded (~0.5 s,
+// then err bit 2).
+__global__ __launch_bounds__(256) void k_route_one(const float *__restrict__ x, const float *__restrict__ Wt, int d,
+                                                   int E, int k, int pre, double eps, double *__restrict__ lg_cur,
+                                                   double *__restrict__ lg_next, double *__restrict__ sel_cur,
+                                                   double *__restrict__ sel_next, int *__restrict__ err,
+                                                   int32_t *__restrict__ ids, float *__restrict__ gates) {
+    const int e = blockIdx.x, tid = threadIdx.x;
+    const double unpub = __longlong_as_double((long long)kUnpublished);
+    __shared__ double lgt[1];
+    router_dot<1>(x, Wt, d, 0, 1, pre, eps, lgt);
+    const double mine = lgt[0];
+    if (tid == 0) {
+        store_coherent(lg_cur + e, mine);
+        store_coherent(lg_next + e, unpub);
     }
-    const int rank = (int)wave_sum(cnt);
-    if (lane == 0 && rank < k) {
-        ids[(size_t)t * k + rank] = e;
-        sel[(size_t)t * k + rank] = me;
+    const uint64_t t_start = wall_clock64();
+    auto timed_out = [&]() {
+        if (wall_clock64() - t_start > 50000000ull) {  // 0.5 s at the 100 MHz constant clock
+            if (tid == 0) atomicOr(err, 2);
+            return true;
+        }
+        __builtin_amdgcn_s_sleep(1);
+        return false;
+    };
+    double v[kSelPer];
+    while (true) {
+        int ready = 1;
+#pragma unroll
+        for (int r = 0; r < kSelPer; r++) {
+            const int i = tid + 256 * r;
+            v[r] = i < E ? load_coherent(lg_cur + i) : 0.0;
+            ready &= (uint64_t)__double_as_longlong(v[r]) != kUnpublished;
+        }
+        if (__syncthreads_and(ready) || timed_out()) break;
+    }
+    // rank of e
+    const double me = rank_value(mine);
+    int ahead = 0;
+#pragma unroll
+    for (int r = 0; r < kSelPer; r++) {
+        const int i = tid + 256 * r;
+        if (i < E) ahead += before(rank_value(v[r]), i, me, e);
+    }
+    __shared__ int part[4];
+    ahead = row16_sum(ahead);
+    ahead += (int)swap_other((uint32_t)ahead, false, tid & 16);
+    ahead += (int)swap_other((uint32_t)ahead, true, tid & 32);
+    if ((tid & 63) == 0) part[tid >> 6] = ahead;
+    __syncthreads();
+    const int rank = part[0] + part[1] + part[2] + part[3];
+    if (rank >= k) return;
+    if (tid == 0) {
+        store_coherent(sel_cur + rank, me);
+        store_coherent(sel_next + rank, unpub);
+        ids[rank] = e;
+    }
+    // gates: softmax over the k selected logits (slot 0 is the largest), one
+    // exp per slot, summed in slot order
+    __shared__ double ex[kMaxTopK];
+    while (true) {
+        double sv = 0.0;
+        if (tid < k) sv = load_coherent(sel_cur + tid);
+        const int ready = tid >= k || (uint64_t)__double_as_longlong(sv) != kUnpublished;
+        if (__syncthreads_and(ready) || timed_out()) {
+            if (tid < k) ex[tid] = sv;
+            break;
+        }
+    }
+    __syncthreads();
+    if (tid < k) ex[tid] = exp(ex[tid] - ex[0]);
+    __syncthreads();
+    if (tid == 0) {
+        double sum = 0.0;
+        for (int j = 0; j < k; j++) sum += ex[j];
+        gates[rank] = (float)(ex[rank] / sum);
     }
 }
 
-// One wave per token: softmax over the k selected logits (slot 0 is the largest).
-__global__ __launch_bounds__(64) void k_gates(const double *__restrict__ sel, int k, float *__restrict__ gates) {
-    const int t = blockIdx.x, lane = threadIdx.x;
-    const double top = sel[(size_t)t * k];
-    double ex = 0.0;
-    for (int j = lane; j < k; j += 64) ex += exp(sel[(size_t)t * k + j] - top);
-    const double sum = wave_sum(ex);
-    for (int j = lane; j < k; j += 64) gates[(size_t)t * k + j] = (float)(exp(sel[(size_t)t * k + j] - top) / sum);
-}
-
-hipError_t launch_route(const Geometry &g, const Workspace &w, const float *x, const float *Wt, int T, int pre,
-                        double eps, int32_t *ids, float *gates, hipStream_t s) {
-    if (T == 1) {
-        hipLaunchKernelGGL(k_route<1>, dim3(g.E, 1), dim3(256), 0, s, x, Wt, g.d, g.E, T, pre, eps, w.logits);
+hipError_t launch_route(const Geometry &g, Workspace &w, const float *x, const float *Wt, int T, int pre, double eps,
+                        int32_t *ids, float *gates, hipStream_t s) {
+    if (T == 1 && w.route_one) {
+        double *lg[2] = {w.route_logits + w.route_cap, w.route_logits + w.route_cap + g.E};
+        double *sl[2] = {w.route_logits + w.route_cap + 2 * g.E, w.route_logits + w.route_cap + 2 * g.E + kMaxTopK};
+        const int p = w.route_parity;
+        w.route_parity ^= 1;
+        hipLaunchKernelGGL(k_route_one, dim3(g.E), dim3(256), 0, s, x, Wt, g.d, g.E, g.k, pre, eps, lg[p], lg[p ^ 1],
+                           sl[p], sl[p ^ 1], w.err, ids, gates);
     } else {
         hipLaunchKernelGGL(k_route<kRouteTok>, dim3(g.E, (T + kRouteTok - 1) / kRouteTok), dim3(256), 0, s, x, Wt,
-                           g.d, g.E, T, pre, eps, w.logits);
+                           g.d, g.E, g.k, T, pre, eps, w.route_logits, w.err, ids, gates);
     }
-    hipError_t err = hipGetLastError();
-    if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(k_rank, dim3((g.E + 3) / 4, T), dim3(256), 0, s, w.logits, g.E, g.k, ids, w.sel);
-    err = hipGetLastError();
-    if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(k_gates, dim3(T), dim3(64), 0, s, w.sel, g.k, gates);
     return hipGetLastError();
+}
+
+int64_t route_logit_slots(int64_t max_tokens, int E) { return max_tokens * E + 2 * E + 2 * kMaxTopK; }
+
+hipError_t init_route(Workspace &w, int E, int64_t max_tokens, int n_cu, hipStream_t s) {
+    w.route_cap = max_tokens * E;
+    w.route_parity = 0;
+    // the one-token kernel needs all E workgroups resident together
+    int per_cu = 0;
+    const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_route_one, 256, 0);
+    if (e != hipSuccess) return e;
+    w.route_one = (int64_t)per_cu * n_cu >= E;
+    return hipMemsetD32Async(reinterpret_cast<hipDeviceptr_t>(w.route_logits), kUnpublishedHalf,
+                             (size_t)(2 * route_logit_slots(max_tokens, E)), s);
 }
 
 }  // namespace rvq
