@@ -1,18 +1,23 @@
 #!/usr/bin/env python3
-"""Benchmark: routed RVQ-MoE layer, batch-1 decode at K3 scale, one MI355X.
+"""Benchmark: routed RVQ-MoE layer on one MI355X.
 
-Workload: one MoE layer with d=7168, ffn=2048, E=384 experts, top-16, expert
-weights as 3-stage RVQ (256-entry fp16 codebooks over 8-wide vectors, uniform
-u8 codes, 16,515,072 B per expert record), router N(0, 0.02), tokens x ~ N(0,1)
-with one seed per token.  A step is one token through the whole hot path:
-rvq_moe_route_topk (RMS-free router GEMV + top-16 + softmax gates) then
-rvq_moe_layer_forward (LUT build, gate/up gather + SiLU, down gather,
-gate-weighted combine), T = 1 per call, every token distinct, all inputs
-resident in HBM before the timed region.
+Default workload (the headline): one K3-scale MoE layer, batch-1 decode.
+d=7168, ffn=2048, E=384 experts, top-16, expert weights as 3-stage RVQ
+(256-entry fp16 codebooks over 8-wide vectors, uniform u8 codes, 16,515,072 B
+per expert record), router N(0, 0.02), tokens x ~ N(0,1) with one seed per
+token.  A step is one call of the whole hot path: rvq_moe_route_topk (router
+GEMV + top-16 + softmax gates) then rvq_moe_layer_forward (LUT build, gate/up
+gather + SiLU, down gather, gate-weighted combine), every token distinct, all
+inputs resident in HBM before the timed region.
+
+Other workloads of the same layer shape:
+  --batch B    B tokens per call (batched decode, pairs grouped by expert);
+  --layers L   a depth chain: L layers, each with RMS normalisation before
+               routing and a residual add, one token through all L per step.
 
 Prints one JSON line: tokens/s (value), effective compressed-weight GB/s and
 its fraction of the 8 TB/s HBM peak, the roofline record of the dominant
-kernel (gate/up gather, timed with HIP events on the launch stream), and the
+kernel (the layer kernel, timed with HIP events on its launch stream), and the
 oracle timed on the host cores on a bounded sample (cpu_baseline).
 """
 from __future__ import annotations
@@ -28,20 +33,27 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
 METRIC = "routed MoE-layer tokens/s + effective compressed-weight GB/s vs HBM peak"
+CB_BYTES = 3 * 3 * 256 * 8 * 2  # one expert's fp16 codebooks (3 matrices x 3 stages)
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=2000, help="timed tokens (one layer call each)")
+    ap.add_argument("--steps", type=int, default=2000, help="timed steps (one call, or one token through the chain)")
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--cpu-tokens", type=int, default=2, help="tokens the oracle baseline runs (0: skip)")
     ap.add_argument("--profile-every", type=int, default=8, help="time kernels with events every n-th call")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--batch", type=int, default=1,
                     help="tokens per call; above 1 the pairs of a call are grouped by expert (batched decode)")
+    ap.add_argument("--layers", type=int, default=1,
+                    help="depth chain of this many layers (RMS normalisation before routing, residual add)")
     ap.add_argument("--path", choices=("fused", "two-call"), default="two-call",
-                    help="fused: rvq_moe_route_forward (one launch per token); "
+                    help="fused: rvq_moe_route_forward (one launch per call); "
                          "two-call: rvq_moe_route_topk then rvq_moe_layer_forward")
     args = ap.parse_args()
 
@@ -59,43 +71,48 @@ def main():
 
     torch.cuda.set_device(0)
     shape = S.K3
-    K, W, B = args.steps, args.warmup, args.batch
-    if B < 1 or (args.path == "fused" and B * shape.top_k > 1024):
-        print(f"--batch {B} outside what the chosen path takes", file=sys.stderr)
+    K, W, B, L = args.steps, args.warmup, args.batch, args.layers
+    chain = L > 1
+    if B < 1 or L < 1 or (chain and B != 1) or (args.path == "fused" and B * shape.top_k > 1024):
+        print(f"--batch {B} / --layers {L} outside what the chosen path takes", file=sys.stderr)
         sys.exit(2)
-    print(f"[bench] staging inputs d={shape.d} ffn={shape.ffn} E={shape.n_experts} k={shape.top_k}", file=sys.stderr,
-          flush=True)
-    inp = G.LayerInputs(shape, seed=args.seed, layer=0)
-    layer = RvqMoe(d=shape.d, ffn=shape.ffn, n_experts=shape.n_experts, top_k=shape.top_k, codebook_dtype=1,
-                   router_w=inp.w_r_dev, codebooks=inp.cb_dev, codes=inp.codes_dev, max_tokens=B)
-    inp.free_codes()
-    torch.cuda.empty_cache()
+
+    layers, inputs = [], []
+    for li in range(L):
+        log(f"staging layer {li}: d={shape.d} ffn={shape.ffn} E={shape.n_experts} k={shape.top_k}")
+        inp = G.LayerInputs(shape, seed=args.seed, layer=li)
+        layers.append(RvqMoe(d=shape.d, ffn=shape.ffn, n_experts=shape.n_experts, top_k=shape.top_k,
+                             codebook_dtype=1, router_w=inp.w_r_dev, codebooks=inp.cb_dev, codes=inp.codes_dev,
+                             max_tokens=B, pre_rmsnorm=chain, residual=chain, eps=1e-6))
+        inp.free_codes()
+        inputs.append(inp)
+        torch.cuda.empty_cache()
 
     n_tok = (W + K) * B
     x_host = S.tokens(args.seed, 0, n_tok, shape.d)
-    x = G.to_device(x_host)
-    ids = torch.empty((n_tok, shape.top_k), dtype=torch.int32, device="cuda")
-    gates = torch.empty((n_tok, shape.top_k), dtype=torch.float32, device="cuda")
-    y = torch.empty((n_tok, shape.d), dtype=torch.float32, device="cuda")
+    # h[l] is the input of layer l (h[0] = the tokens); h[L] the chain's output
+    h = torch.empty((L + 1, n_tok, shape.d), dtype=torch.float32, device="cuda")
+    h[0].copy_(G.to_device(x_host))
+    ids = torch.empty((L, n_tok, shape.top_k), dtype=torch.int32, device="cuda")
+    gates = torch.empty((L, n_tok, shape.top_k), dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream()
 
-    def step_two(t):
+    def step(t):
         r = slice(t * B, (t + 1) * B)
-        layer.route_topk(x[r], B, ids[r], gates[r], stream)
-        layer.layer_forward(x[r], B, ids[r], gates[r], y[r], stream)
+        for li, layer in enumerate(layers):
+            if args.path == "fused":
+                layer.route_forward(h[li, r], B, ids[li, r], gates[li, r], h[li + 1, r], stream)
+            else:
+                layer.route_topk(h[li, r], B, ids[li, r], gates[li, r], stream)
+                layer.layer_forward(h[li, r], B, ids[li, r], gates[li, r], h[li + 1, r], stream)
 
-    def step_fused(t):
-        r = slice(t * B, (t + 1) * B)
-        layer.route_forward(x[r], B, ids[r], gates[r], y[r], stream)
-
-    step = step_fused if args.path == "fused" else step_two
-
-    print(f"[bench] warmup {W} calls of {B} token(s)", file=sys.stderr, flush=True)
+    log(f"warmup {W} steps of {B} token(s) x {L} layer(s)")
     for t in range(W):
         step(t)
-    layer.sync(stream)
-    layer.kernel_times()  # drop warmup samples
-    layer.set_profiling(args.profile_every)
+    for layer in layers:
+        layer.sync(stream)
+        layer.kernel_times()  # drop warmup samples
+        layer.set_profiling(args.profile_every)
 
     torch.cuda.synchronize()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -105,48 +122,66 @@ def main():
     ev1.record(stream)
     torch.cuda.synchronize()
     ms = ev0.elapsed_time(ev1)
-    layer.set_profiling(0)
-    ktimes = layer.kernel_times()
-    layer.sync(stream)
-    print(f"[bench] timed {K} calls in {ms:.2f} ms", file=sys.stderr, flush=True)
+    n_l, l_ms = 0, 0.0
+    kernels = {}
+    lut_kind = "route_layer_lut" if args.path == "fused" else "layer_lut"
+    for layer in layers:
+        layer.set_profiling(0)
+        for kind, (n, v) in layer.kernel_times().items():
+            a = kernels.setdefault(kind, [0, 0.0])
+            a[0] += n
+            a[1] += v
+        layer.sync(stream)
+    n_l, l_ms = kernels[lut_kind]
+    log(f"timed {K} steps in {ms:.2f} ms")
 
     rec = shape.record_bytes
-    cb_bytes = 3 * 3 * 256 * 8 * 2
-    # Algorithmic bytes of one call: every distinct expert the call routes to,
-    # read once (code record + its 3 matrices' codebooks).  At batch 1 that is
-    # k experts; in a batch, experts shared by several tokens count once.
-    ids_all = ids.cpu().numpy().reshape(W + K, B * shape.top_k)
-    uniq = np.array([len(np.unique(ids_all[t])) for t in range(W, W + K)], dtype=np.float64)
-    per_call_bytes = float(uniq.mean()) * (rec + cb_bytes)
+    # Algorithmic bytes of one layer call: every distinct expert the call routes
+    # to, read once (code record + its 3 matrices' codebooks).  At batch 1 that
+    # is k experts; in a batch, experts shared by several tokens count once.
+    ids_h = ids.cpu().numpy()
+    uniq = np.array([[len(np.unique(ids_h[li, t * B:(t + 1) * B])) for t in range(W, W + K)] for li in range(L)],
+                    dtype=np.float64)
+    per_call_bytes = float(uniq.mean()) * (rec + CB_BYTES)
+    calls_s = K * L / (ms / 1e3)
     tok_s = K * B / (ms / 1e3)
-    gbps = per_call_bytes * (K / (ms / 1e3)) / 1e9
-
-    # Dominant kernel: the persistent LUT kernel of the layer call.
-    n_l, l_ms = ktimes["route_layer_lut" if args.path == "fused" else "layer_lut"]
+    gbps = per_call_bytes * calls_s / 1e9
     l_avg_us = l_ms / max(n_l, 1) * 1e3
     l_gbps = per_call_bytes / (l_avg_us * 1e-6) / 1e9
-    kernels = {k: {"launches": int(n), "avg_us": (v / n * 1e3 if n else None)} for k, (n, v) in ktimes.items()}
+    kernels = {k: {"launches": int(n), "avg_us": (v / n * 1e3 if n else None)} for k, (n, v) in kernels.items()}
 
-    # Parity on the timed tokens the oracle re-runs, and the CPU baseline.
+    # Parity on timed tokens (teacher-forced through the chain: the oracle runs
+    # layer l on the GPU's own input of layer l) and the CPU baseline.
     cpu = None
     parity = None
     if args.cpu_tokens > 0:
         from oracle import oracle as O
-        ids_h = ids.cpu().numpy()
-        y_h = y.cpu().numpy()
+        hs = h.cpu().numpy()
         errs, ok_ids = [], True
         t0 = time.perf_counter()
         for j in range(args.cpu_tokens):
             t = W * B + j
-            ref = O.layer(x_host[t], inp.w_r, shape.top_k, inp.codebook, inp.record, shape.d, shape.ffn)
-            ok_ids &= bool(np.array_equal(ids_h[t], ref.route.ids))
-            errs.append(float(np.linalg.norm(y_h[t] - ref.delta) / np.linalg.norm(ref.delta)))
+            for li in range(L):
+                inp = inputs[li]
+                ref = O.layer(hs[li, t], inp.w_r, shape.top_k, inp.codebook, inp.record, shape.d, shape.ffn,
+                              pre_rmsnorm=chain, eps=1e-6, residual=chain)
+                ok_ids &= bool(np.array_equal(ids_h[li, t], ref.route.ids))
+                delta = hs[li + 1, t].astype(np.float64) - (hs[li, t].astype(np.float64) if chain else 0.0)
+                errs.append(float(np.linalg.norm(delta - ref.delta) / np.linalg.norm(ref.delta)))
         cpu_s = time.perf_counter() - t0
+        what = f"{L}-layer chain, teacher-forced" if chain else "one layer"
         cpu = {"value": args.cpu_tokens / cpu_s, "unit": "tokens/s", "cores": O.threads(), "kind": "oracle",
-               "sample": f"{args.cpu_tokens} timed tokens of the same workload, full layer each (route + 16 experts "
-                         f"rebuilt as c1+c2+c3 in fp64); includes regenerating their code records on the host"}
-        parity = {"tokens": args.cpu_tokens, "ids_bit_exact": ok_ids, "max_rel_l2": max(errs)}
+               "sample": f"{args.cpu_tokens} timed token(s) of the same workload ({what}; route + 16 experts per "
+                         f"layer rebuilt as c1+c2+c3 in fp64); includes regenerating their code records on the host"}
+        parity = {"tokens": args.cpu_tokens, "layers_checked": L, "ids_bit_exact": ok_ids, "max_rel_l2": max(errs)}
 
+    if chain:
+        workload = (f"K3-scale depth chain, batch-1 decode: {L} layers of d=7168 ffn=2048 E=384 top-16 "
+                    f"(3-stage x 256 x 8 fp16 codebooks, uniform u8 codes), RMSNorm (w=1, eps=1e-6) before "
+                    f"routing and a residual add per layer, all resident")
+    else:
+        workload = (f"K3-scale routed RVQ-MoE layer, batch-{B} decode: d=7168 ffn=2048 E=384 top-16, "
+                    f"3-stage x 256 x 8 fp16 codebooks, uniform u8 codes, T={B} per call")
     out = {
         "metric": METRIC,
         "value": tok_s,
@@ -161,11 +196,10 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": f"K3-scale routed RVQ-MoE layer, batch-{B} decode: d=7168 ffn=2048 E=384 top-16, "
-                               f"3-stage x 256 x 8 fp16 codebooks, uniform u8 codes, T={B} per call",
-                   "global_batch": B, "tokens": K * B,
+        "config": {"workload": workload, "global_batch": B, "layers": L, "tokens": K * B,
                    "path": "rvq_moe_route_forward" if args.path == "fused"
                    else "rvq_moe_route_topk + rvq_moe_layer_forward"},
+        "layer_calls_per_s": calls_s,
         "compressed_GBps": gbps,
         "hbm_frac": gbps / HBM_PEAK_GBPS,
         "compressed_bytes_per_call": per_call_bytes,
@@ -178,7 +212,8 @@ def main():
         "cpu_baseline": cpu,
         "parity": parity,
     }
-    layer.close()
+    for layer in layers:
+        layer.close()
     print(json.dumps(out), flush=True)
 
 
