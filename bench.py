@@ -12,6 +12,8 @@ inputs resident in HBM before the timed region.
 
 Other workloads of the same layer shape:
   --batch B    B tokens per call (batched decode, pairs grouped by expert);
+  --chunk      with --batch: every call takes the chunk path (prefill chunk:
+               weights rebuilt as bf16 tiles feeding the matrix cores);
   --layers L   a depth chain: L layers, each with RMS normalisation before
                routing and a residual add, one token through all L per step.
 
@@ -52,6 +54,8 @@ def main():
                     help="tokens per call; above 1 the pairs of a call are grouped by expert (batched decode)")
     ap.add_argument("--layers", type=int, default=1,
                     help="depth chain of this many layers (RMS normalisation before routing, residual add)")
+    ap.add_argument("--chunk", action="store_true",
+                    help="every layer_forward call takes the chunk path (bf16 matrix cores)")
     ap.add_argument("--path", choices=("fused", "two-call"), default="two-call",
                     help="fused: rvq_moe_route_forward (one launch per call); "
                          "two-call: rvq_moe_route_topk then rvq_moe_layer_forward")
@@ -73,7 +77,7 @@ def main():
     shape = S.K3
     K, W, B, L = args.steps, args.warmup, args.batch, args.layers
     chain = L > 1
-    if B < 1 or L < 1 or (chain and B != 1) or (args.path == "fused" and B * shape.top_k > 1024):
+    if (B < 1 or L < 1 or (chain and B != 1) or (args.path == "fused" and (B * shape.top_k > 1024 or args.chunk))):
         print(f"--batch {B} / --layers {L} outside what the chosen path takes", file=sys.stderr)
         sys.exit(2)
 
@@ -83,7 +87,8 @@ def main():
         inp = G.LayerInputs(shape, seed=args.seed, layer=li)
         layers.append(RvqMoe(d=shape.d, ffn=shape.ffn, n_experts=shape.n_experts, top_k=shape.top_k,
                              codebook_dtype=1, router_w=inp.w_r_dev, codebooks=inp.cb_dev, codes=inp.codes_dev,
-                             max_tokens=B, pre_rmsnorm=chain, residual=chain, eps=1e-6))
+                             max_tokens=B, pre_rmsnorm=chain, residual=chain, eps=1e-6,
+                             chunk_min_tokens=1 if args.chunk else B + 1))
         inp.free_codes()
         inputs.append(inp)
         torch.cuda.empty_cache()
@@ -124,7 +129,7 @@ def main():
     ms = ev0.elapsed_time(ev1)
     n_l, l_ms = 0, 0.0
     kernels = {}
-    lut_kind = "route_layer_lut" if args.path == "fused" else "layer_lut"
+    lut_kind = "route_layer_lut" if args.path == "fused" else ("chunk" if args.chunk else "layer_lut")
     for layer in layers:
         layer.set_profiling(0)
         for kind, (n, v) in layer.kernel_times().items():
@@ -175,7 +180,11 @@ def main():
                          f"layer rebuilt as c1+c2+c3 in fp64); includes regenerating their code records on the host"}
         parity = {"tokens": args.cpu_tokens, "layers_checked": L, "ids_bit_exact": ok_ids, "max_rel_l2": max(errs)}
 
-    if chain:
+    if args.chunk:
+        workload = (f"K3-scale prefill chunk, resident codes: {B} tokens per call through d=7168 ffn=2048 E=384 "
+                    f"top-16, tokens grouped by expert, RVQ tiles rebuilt as bf16 for the matrix cores "
+                    f"(fp32 accumulation)")
+    elif chain:
         workload = (f"K3-scale depth chain, batch-1 decode: {L} layers of d=7168 ffn=2048 E=384 top-16 "
                     f"(3-stage x 256 x 8 fp16 codebooks, uniform u8 codes), RMSNorm (w=1, eps=1e-6) before "
                     f"routing and a residual add per layer, all resident")
@@ -194,7 +203,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "bf16" if args.chunk else "f32",
         "data": "synthetic",
         "config": {"workload": workload, "global_batch": B, "layers": L, "tokens": K * B,
                    "path": "rvq_moe_route_forward" if args.path == "fused"
@@ -206,9 +215,14 @@ def main():
         "distinct_experts_per_call": float(uniq.mean()),
         "roofline": {"bound": "hbm", "achieved": l_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": l_gbps / HBM_PEAK_GBPS, "traffic": None,
-                     "kernel": "k_layer<route>" if args.path == "fused" else "k_layer",
+                     "kernel": "k_layer<route>" if args.path == "fused" else
+                     ("k_chunk_prep + k_chunk_stage + k_chunk_gu + k_chunk_down" if args.chunk else "k_layer"),
                      "algorithmic_bytes_per_launch": per_call_bytes, "avg_us": l_avg_us, "timed_launches": int(n_l)},
         "kernels": kernels,
+        "mfma": ({"flops_per_call": 6.0 * B * shape.top_k * shape.d * shape.ffn,
+                  "tflops": 6.0 * B * shape.top_k * shape.d * shape.ffn / (l_avg_us * 1e-6) / 1e12,
+                  "frac_of_bf16_dense_peak": 6.0 * B * shape.top_k * shape.d * shape.ffn / (l_avg_us * 1e-6) / 2.5e15}
+                 if args.chunk else None),
         "cpu_baseline": cpu,
         "parity": parity,
     }

@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define RVQ_MOE_ABI_VERSION 1
+#define RVQ_MOE_ABI_VERSION 2
 
 typedef enum rvq_moe_status {
     RVQ_MOE_OK = 0,
@@ -62,6 +62,9 @@ typedef enum rvq_moe_status {
     RVQ_MOE_EHIP = -5,     /* a HIP runtime call or launch failed */
     RVQ_MOE_EDEVICE = -6   /* deferred: a kernel saw an expert id outside [0, n_experts) */
 } rvq_moe_status;
+
+/* Default chunk-path threshold (tokens per layer_forward call). */
+#define RVQ_MOE_CHUNK_MIN_TOKENS 256
 
 typedef enum rvq_moe_cb_dtype {
     RVQ_MOE_CB_F32 = 0,    /* IEEE binary32 codebook entries */
@@ -101,6 +104,13 @@ typedef enum rvq_moe_codes_location {
  *                MoE(x_hat).
  *   max_tokens   largest n_tokens any later call will pass (sizes the
  *                per-handle workspace, allocated once at open).
+ *   chunk_min_tokens  layer_forward calls with n_tokens >= this take the chunk
+ *                path (tokens grouped by expert, weights rebuilt as bf16 and
+ *                contracted on the matrix cores, see rvq_moe_layer_forward);
+ *                0 = the library default (RVQ_MOE_CHUNK_MIN_TOKENS); a value
+ *                above max_tokens never takes it (and allocates nothing for
+ *                it).  Must be >= 0.
+ *   reserved     must be 0.
  *   stream       stream used for the upload and repack inside open.
  */
 typedef struct rvq_moe_desc {
@@ -118,6 +128,8 @@ typedef struct rvq_moe_desc {
     int32_t pre_rmsnorm;
     int32_t residual;
     int32_t max_tokens;
+    int32_t chunk_min_tokens;
+    int32_t reserved;           /* must be 0 */
     double eps;
     const float *router_w;
     const void *codebooks;
@@ -154,9 +166,14 @@ int rvq_moe_route_topk(rvq_moe *h, const float *x, int32_t n_tokens, int32_t *id
 
 /*
  * rvq_moe_layer_forward -- y[t] = sum_j gates[t][j] * FFN_{ids[t][j]}(x_hat[t])
- * (+ x[t] when residual), FFN(v) = W_d (silu(W_g v) * (W_u v)) evaluated from
- * the codes by per-token tables of partial dot products ([FR]
- * "Quantification et exactitude").
+ * (+ x[t] when residual), FFN(v) = W_d (silu(W_g v) * (W_u v)).  Below the
+ * chunk threshold it is evaluated from the codes by per-token tables of
+ * partial dot products ([FR] "Quantification et exactitude"), fp32 throughout
+ * (a batch is grouped by expert, so an expert's codes are read once per call).
+ * At or above it (the chunk path, for prefill-sized calls) the tokens are
+ * grouped by expert, the weights are rebuilt as bf16(c1 + c2 + c3) tile by
+ * tile in registers, and x_hat and h are rounded to bf16 for bf16 x bf16 ->
+ * fp32 matrix-core products: expect ~1e-3 relative error instead of ~1e-6.
  *   x      [n_tokens][d] fp32.   ids [n_tokens][k] int32.   gates [n_tokens][k] fp32.
  *   y      [n_tokens][d] fp32 out (must not alias x).
  * Ids outside [0, E) are detected on the device: the affected outputs are
@@ -225,8 +242,9 @@ int rvq_moe_get_stats(const rvq_moe *h, rvq_moe_stats *out);
  *   0 "route_topk"       the router and selection kernels of rvq_moe_route_topk,
  *   1 "layer_lut"        the persistent LUT kernel of rvq_moe_layer_forward,
  *   2 "route_layer_lut"  the persistent kernel of rvq_moe_route_forward.
+ *   3 "chunk"            the chunk-path kernels of rvq_moe_layer_forward.
  */
-#define RVQ_MOE_N_KERNEL_KINDS 3
+#define RVQ_MOE_N_KERNEL_KINDS 4
 int rvq_moe_set_profiling(rvq_moe *h, int every);
 int rvq_moe_kernel_times(rvq_moe *h, const char **names, uint64_t *launches, double *total_ms,
                          int max_kinds);

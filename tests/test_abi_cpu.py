@@ -14,7 +14,7 @@ def test_library_exports_every_header_symbol():
     L = R.lib()
     for n in names:
         assert hasattr(L, n), n
-    assert L.rvq_moe_abi_version() == 1
+    assert L.rvq_moe_abi_version() == 2
 
 
 def _desc(**over):

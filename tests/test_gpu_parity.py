@@ -371,3 +371,98 @@ def test_k3_batch32_grouped_matches_per_token_and_oracle(torch_mod):
     worst = _check(inp, shape, x, *batched, tokens=[0, 17, 31])
     print(f"K3 batch-32 worst rel L2 {worst:.3e}")
     layer.close()
+
+
+# --------------------------------------------------------------------------- chunk path (bf16 matrix cores)
+TOL_Y_BF16 = 2e-2  # bf16 operands (weights, tokens, h) with fp32 accumulation
+
+
+def _check_chunk(inp, shape, x, ids, gates, y, pre_rmsnorm=False, residual=False, tokens=None):
+    worst = 0.0
+    for t in (range(x.shape[0]) if tokens is None else tokens):
+        ref = O.layer(x[t], inp.w_r, shape.top_k, inp.codebook, inp.record, shape.d, shape.ffn,
+                      pre_rmsnorm=pre_rmsnorm, eps=1e-6)
+        assert np.array_equal(ids[t], ref.route.ids), t
+        delta = y[t].astype(np.float64) - (x[t].astype(np.float64) if residual else 0.0)
+        err = np.linalg.norm(delta - ref.delta) / np.linalg.norm(ref.delta)
+        assert err <= TOL_Y_BF16, (t, err)
+        worst = max(worst, err)
+    return worst
+
+
+@pytest.mark.parametrize("d,ffn,E,k,cb,T", [
+    (256, 128, 16, 4, "f32", 64),     # the small layer; 64 tokens, 16 pairs per expert on average
+    (264, 136, 5, 2, "f16", 200),     # ragged tiles and chunks; 80 tokens per expert: two 64-token passes
+    (520, 72, 7, 7, "f32", 9),        # k == E: every expert gets every token
+    (1024, 520, 9, 3, "f16", 33),     # several tiles both ways, ragged row chunks
+    (8, 8, 1, 1, "f32", 1),           # smallest
+])
+def test_chunk_path_follows_the_oracle(torch_mod, d, ffn, E, k, cb, T):
+    from synth import gpu as G
+    shape = S.Shape(d, ffn, E, k, cb)
+    inp = G.LayerInputs(shape, seed=17, layer=1, host_codes=True)
+    layer = _layer(torch_mod, inp, shape, T, chunk_min_tokens=1)
+    x = S.tokens(17, 0, T, d)
+    ids, gates, y = _run(torch_mod, layer, shape, x)
+    worst = _check_chunk(inp, shape, x, ids, gates, y)
+    print(f"chunk path {shape} T={T}: worst rel L2 {worst:.3e}")
+    layer.close()
+
+
+def test_chunk_path_rmsnorm_residual_and_threshold(torch_mod):
+    """RMS normalisation and the residual on the chunk path; a call below the
+    threshold of the same handle takes the table path (1e-4 bar)."""
+    from synth import gpu as G
+    shape = S.Shape(512, 256, 32, 8, "f16")
+    inp = G.LayerInputs(shape, seed=9, layer=4, host_codes=True)
+    layer = _layer(torch_mod, inp, shape, 40, pre_rmsnorm=True, residual=True, eps=1e-6, chunk_min_tokens=16)
+    x = S.tokens(9, 50, 40, shape.d)
+    ids, gates, y = _run(torch_mod, layer, shape, x)            # 40 >= 16: chunk path
+    _check_chunk(inp, shape, x, ids, gates, y, pre_rmsnorm=True, residual=True)
+    ids2, gates2, y2 = _run(torch_mod, layer, shape, x[:15])   # 15 < 16: table path
+    _check(inp, shape, x[:15], ids2, gates2, y2, pre_rmsnorm=True, residual=True)
+    layer.close()
+
+
+def test_chunk_path_invalid_ids_poison_only_their_token(torch_mod, tiny):
+    from synth import gpu as G
+    from vector_quantized_expert_amd import RvqMoeError
+    from vector_quantized_expert_amd import rvq_moe as R
+    shape = S.TINY
+    layer = _layer(torch_mod, tiny, shape, 3, chunk_min_tokens=1)
+    x = G.to_device(S.tokens(0, 0, 3, shape.d))
+    ids = torch_mod.tensor([[0, 1, 2, 3], [0, 1, -4, 3], [5, 6, 7, 8]], dtype=torch_mod.int32, device="cuda")
+    gates = torch_mod.full((3, 4), 0.25, device="cuda")
+    y = torch_mod.zeros((3, shape.d), device="cuda")
+    layer.layer_forward(x, 3, ids, gates, y)
+    with pytest.raises(RvqMoeError) as ei:
+        layer.sync()
+    assert ei.value.status == R.EDEVICE
+    yh = y.cpu().numpy()
+    assert np.all(np.isfinite(yh[0])) and np.all(np.isnan(yh[1])) and np.all(np.isfinite(yh[2]))
+    layer.close()
+
+
+def test_k3_chunk_512_tokens_against_table_path_and_oracle(torch_mod):
+    """The prefill chunk: 512 tokens through the d=7168, ffn=2048, E=384, top-16
+    layer in one call on the chunk path; every token against the table path of a
+    second handle on the same weights, sampled tokens against the oracle."""
+    from synth import gpu as G
+    shape = S.K3
+    T = 512
+    inp = G.LayerInputs(shape, seed=0, layer=5)
+    chunk = _layer(torch_mod, inp, shape, T, chunk_min_tokens=64)
+    table = _layer(torch_mod, inp, shape, T, chunk_min_tokens=T + 1)
+    inp.free_codes()
+    torch_mod.cuda.empty_cache()
+    x = S.tokens(0, 3000, T, shape.d)
+    a = _run(torch_mod, chunk, shape, x)
+    b = _run(torch_mod, table, shape, x)
+    assert np.array_equal(a[0], b[0])
+    err = np.linalg.norm(a[2] - b[2], axis=1) / np.linalg.norm(b[2], axis=1)
+    print(f"K3 chunk vs table: max rel L2 {err.max():.3e}, mean {err.mean():.3e}")
+    assert err.max() <= TOL_Y_BF16
+    worst = _check_chunk(inp, shape, x, *a, tokens=[0, 255, 511])
+    print(f"K3 chunk vs oracle: worst rel L2 {worst:.3e}")
+    chunk.close()
+    table.close()

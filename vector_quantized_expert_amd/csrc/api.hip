@@ -43,6 +43,8 @@ struct rvq_moe {
     int device;
     Geometry g;
     int pre_rmsnorm, residual, max_tokens;
+    int chunk_min;       // layer_forward calls with T >= chunk_min take the chunk path
+    ChunkWork cw;        // its workspace (all null when max_tokens < chunk_min)
     double eps;
     uint8_t *codes;      // [E][rec_int] internal layout
     void *cbs;           // [E][3][3][256][8]
@@ -100,6 +102,12 @@ static void free_handle(rvq_moe *h) {
     (void)hipFree(h->ws.cntA);
     (void)hipFree(h->ws.gbar);
     (void)hipFree(h->ws.err);
+    (void)hipFree(h->cw.X);
+    (void)hipFree(h->cw.H);
+    (void)hipFree(h->cw.perm);
+    (void)hipFree(h->cw.pos_of);
+    (void)hipFree(h->cw.grp_off);
+    (void)hipFree(h->cw.act);
     for (hipEvent_t e : h->prof_pool) (void)hipEventDestroy(e);
     delete h;
 }
@@ -123,6 +131,7 @@ static int open_impl(const rvq_moe_desc *desc, rvq_moe *h) {
     h->residual = D.residual != 0;
     h->eps = D.eps;
     h->max_tokens = D.max_tokens;
+    h->chunk_min = D.chunk_min_tokens > 0 ? D.chunk_min_tokens : RVQ_MOE_CHUNK_MIN_TOKENS;
     const Geometry &g = h->g;
     const int64_t E = D.n_experts;
     HIP_TRY(hipMalloc(&h->codes, (size_t)(E * g.rec_int)));
@@ -136,6 +145,14 @@ static int open_impl(const rvq_moe_desc *desc, rvq_moe *h) {
     HIP_TRY(hipMalloc(&h->ws.cntA, sizeof(int) * (size_t)P));
     HIP_TRY(hipMalloc(&h->ws.gbar, sizeof(int) * kGbarInts));
     HIP_TRY(hipMalloc(&h->ws.err, sizeof(int)));
+    if (h->max_tokens >= h->chunk_min) {
+        HIP_TRY(hipMalloc(&h->cw.X, 2 * (size_t)(P * D.d)));
+        HIP_TRY(hipMalloc(&h->cw.H, 2 * (size_t)(P * D.ffn)));
+        HIP_TRY(hipMalloc(&h->cw.perm, sizeof(int) * (size_t)P));
+        HIP_TRY(hipMalloc(&h->cw.pos_of, sizeof(int) * (size_t)P));
+        HIP_TRY(hipMalloc(&h->cw.grp_off, sizeof(int) * (size_t)(E + 2)));
+        HIP_TRY(hipMalloc(&h->cw.act, sizeof(int) * (size_t)(E + 1)));
+    }
     int n_cu = 0;
     HIP_TRY(hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, h->device));
     int per_cu = 0;
@@ -186,6 +203,8 @@ extern "C" int rvq_moe_open(const rvq_moe_desc *desc, rvq_moe **out) {
             return fail(RVQ_MOE_EINVAL, "max_tokens=%d: one call would exceed 2^31 work units", D.max_tokens);
     }
     if (D.cache_slots < 0) return fail(RVQ_MOE_EINVAL, "cache_slots=%d < 0", D.cache_slots);
+    if (D.chunk_min_tokens < 0) return fail(RVQ_MOE_EINVAL, "chunk_min_tokens=%d < 0", D.chunk_min_tokens);
+    if (D.reserved != 0) return fail(RVQ_MOE_EINVAL, "reserved=%d must be 0", D.reserved);
     if (D.cache_slots > 0 && D.cache_slots < D.top_k)
         return fail(RVQ_MOE_EBUDGET, "cache_slots=%d below one token's working set (top_k=%d)", D.cache_slots,
                     D.top_k);
@@ -263,7 +282,11 @@ extern "C" int rvq_moe_layer_forward(rvq_moe *h, const float *x, int32_t T, cons
     if ((const void *)y == (const void *)x) return fail(RVQ_MOE_EINVAL, "y aliases x");
     hipStream_t s = static_cast<hipStream_t>(stream);
     const bool prof = h->prof_every > 0 && (h->prof_calls++ % (uint64_t)h->prof_every) == 0;
-    {
+    if (T >= h->chunk_min) {
+        ProfScope p(h, s, prof, 3);
+        HIP_TRY(launch_chunk(h->g, h->cw, h->codes, h->cbs, x, ids, gates, y, T, h->pre_rmsnorm, h->residual,
+                             h->eps, h->ws.err, s));
+    } else {
         ProfScope p(h, s, prof, 1);
         HIP_TRY(launch_layer(h->g, h->ws, h->codes, h->cbs, h->router_wt, x, ids, gates, y, T, h->pre_rmsnorm,
                              h->residual, h->eps, false, s));
@@ -334,7 +357,7 @@ extern "C" int rvq_moe_get_stats(const rvq_moe *h, rvq_moe_stats *out) {
     return RVQ_MOE_OK;
 }
 
-static const char *kKindNames[RVQ_MOE_N_KERNEL_KINDS] = {"route_topk", "layer_lut", "route_layer_lut"};
+static const char *kKindNames[RVQ_MOE_N_KERNEL_KINDS] = {"route_topk", "layer_lut", "route_layer_lut", "chunk"};
 
 extern "C" int rvq_moe_set_profiling(rvq_moe *h, int every) {
     if (!h || every < 0) return fail(RVQ_MOE_EINVAL, "bad handle or every");

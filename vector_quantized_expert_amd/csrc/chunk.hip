@@ -1,0 +1,398 @@
+// chunk.hip -- the multi-token (prefill chunk) path: tokens grouped by expert,
+// RVQ code tiles dequantised on the fly into bf16 operands of the matrix cores.
+//
+// [FR] "Quantification et exactitude": each weight is the sum of one entry of
+// each of the 3 stage codebooks, w = c1 + c2 + c3 over an 8-wide vector.  With
+// T_e tokens per expert the layer is a small dense contraction per expert
+// (T_e x d times d x F, then T_e x F times F x d), so here the weights are
+// rebuilt (fp32 sum of the three entries, rounded to bf16) and fed to
+// v_mfma_f32_32x32x16_bf16 with fp32 accumulation; tokens are rounded to bf16
+// (RNE) once, and so is the SwiGLU output h.  Pages "Lecture anticipée"
+// (a chunk of tokens touches most experts): the tokens are permuted so that
+// each expert's tokens are contiguous and every code tile is read once per
+// group of up to 64 tokens.
+//
+// Steps (one launch each, all asynchronous on the caller's stream):
+//   prep   ids -> per-expert counts, offsets, the permutation and the list of
+//          experts with tokens (one workgroup);
+//   stage  x -> bf16 rows in permuted order (RMS-normalised first when asked);
+//          y <- x (residual) or 0, NaN for a token with an invalid id;
+//   gu     per (expert, 64 output rows): gate and up tiles -> h = silu(a) b in bf16;
+//   down   per (expert, 128 output rows): h W_d^T scaled by the gate, added into y.
+//
+// MI355X mapping.  A workgroup is 4 waves; each wave owns one 32-row chunk of a
+// matrix and one or two 32-token tiles (accumulators in registers).  Per
+// 256-wide input tile the token tile is staged in LDS (shared by the 4 waves)
+// and each wave stages its 3 KB code block in LDS; a lane then forms exactly
+// the B operand it needs (row l % 32, 8 consecutive inputs of one slice): three
+// code bytes, three codebook entries from LDS, fp32 sum, RNE to bf16.  The
+// dense weight tile never exists in LDS or HBM.
+#include <math.h>
+
+#include "internal.hpp"
+
+namespace rvq {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16c __attribute__((ext_vector_type(16)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+
+constexpr int kCkThreads = 256;
+constexpr int kCkMt = 2;                      // 32-token tiles per pass
+constexpr int kXRow = kTileSlices * kVec + 8;  // bf16 per staged token row (padded: 264)
+
+// ---------------------------------------------------------------------------
+// prep: one workgroup of 1024 threads.
+__global__ __launch_bounds__(1024) void k_chunk_prep(const int32_t *__restrict__ ids, int P, int E,
+                                                     int *__restrict__ grp_off, int *__restrict__ perm,
+                                                     int *__restrict__ pos_of, int *__restrict__ act,
+                                                     int *__restrict__ err) {
+    __shared__ int cnt[kMaxExperts + 1];
+    __shared__ int off[kMaxExperts + 2];
+    __shared__ int aoff[kMaxExperts + 1];
+    const int NE = E + 1;  // bin E: ids outside [0, E)
+    for (int i = threadIdx.x; i < NE; i += 1024) cnt[i] = 0;
+    __syncthreads();
+    for (int p = threadIdx.x; p < P; p += 1024) {
+        int e = ids[p];
+        if (e < 0 || e >= E) {
+            e = E;
+            atomicOr(err, 1);
+        }
+        atomicAdd(&cnt[e], 1);
+    }
+    __syncthreads();
+    if (threadIdx.x < 64) {
+        // exclusive scans of the counts and of the non-empty flags, one wave
+        const int lane = threadIdx.x, per = (NE + 63) / 64;
+        int s = 0, a = 0;
+        for (int i = lane * per; i < min(NE, (lane + 1) * per); i++) {
+            s += cnt[i];
+            a += (i < E && cnt[i] > 0);
+        }
+        int is = s, ia = a;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int vs = __shfl_up(is, o), va = __shfl_up(ia, o);
+            if (lane >= o) {
+                is += vs;
+                ia += va;
+            }
+        }
+        int rs = is - s, ra = ia - a;
+        for (int i = lane * per; i < min(NE, (lane + 1) * per); i++) {
+            off[i] = rs;
+            aoff[i] = ra;
+            rs += cnt[i];
+            ra += (i < E && cnt[i] > 0);
+        }
+        if (lane == 63) {
+            off[NE] = rs;
+            act[E] = ra;  // number of experts with tokens
+        }
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i <= NE; i += 1024) grp_off[i] = off[i];
+    for (int i = threadIdx.x; i < E; i += 1024)
+        if (cnt[i] > 0) act[aoff[i]] = i;
+    __syncthreads();
+    // placement: order within a group is the order the atomics hand out (the
+    // result does not depend on it beyond fp32 summation order)
+    for (int p = threadIdx.x; p < P; p += 1024) {
+        int e = ids[p];
+        if (e < 0 || e >= E) e = E;
+        const int pos = atomicAdd(&off[e], 1);
+        perm[pos] = p;
+        pos_of[p] = pos;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// stage: grid (T), 256 threads.  X[pos][i] = bf16(x_hat[t][i]) for the k
+// positions of token t; y[t] = x[t] (residual) or 0, or NaN if one of the
+// token's ids is invalid.
+__global__ __launch_bounds__(kCkThreads) void k_chunk_stage(const float *__restrict__ x, int d, int k, int pre,
+                                                            double eps, int residual, int E,
+                                                            const int32_t *__restrict__ ids,
+                                                            const int *__restrict__ pos_of, __bf16 *__restrict__ X,
+                                                            float *__restrict__ y) {
+    const int t = blockIdx.x;
+    const float *xt = x + (size_t)t * d;
+    __shared__ double red[kCkThreads / 64];
+    __shared__ int bad;
+    double r = 1.0;
+    if (threadIdx.x == 0) bad = 0;
+    __syncthreads();
+    if (threadIdx.x < k) {
+        const int e = ids[(size_t)t * k + threadIdx.x];
+        if (e < 0 || e >= E) bad = 1;
+    }
+    if (pre) {
+        double ss = 0.0;
+        for (int i = threadIdx.x; i < d; i += kCkThreads) ss = fma((double)xt[i], (double)xt[i], ss);
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
+        if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+    }
+    __syncthreads();
+    if (pre) r = sqrt((red[0] + red[1] + red[2] + red[3]) / (double)d + eps);
+    const float poison = bad ? __int_as_float(0x7fc00000) : 0.f;
+    for (int i = threadIdx.x; i < d; i += kCkThreads) y[(size_t)t * d + i] = (residual ? xt[i] : 0.f) + poison;
+    for (int j = 0; j < k; j++) {
+        __bf16 *dst = X + (size_t)pos_of[(size_t)t * k + j] * d;
+        for (int i = threadIdx.x; i < d; i += kCkThreads) {
+            const float v = pre ? (float)((double)xt[i] / r) : xt[i];
+            dst[i] = (__bf16)v;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Shared pieces of the two contraction kernels.
+
+// Codebooks of one matrix in LDS: [3][256] entries of 8 values, as stored
+// (fp32 or fp16).
+template <int CB>
+struct CkCb {
+    static constexpr int kEntryBytes = CB == 0 ? 32 : 16;
+    static constexpr int kBytes = kStages * kCodes * kEntryBytes;
+};
+
+template <int CB>
+__device__ inline void ck_stage_cb(char *dst, const void *cbs, int e, int m) {
+    const uint4 *src = reinterpret_cast<const uint4 *>(static_cast<const char *>(cbs) +
+                                                       ((int64_t)e * 3 + m) * CkCb<CB>::kBytes);
+    uint4 *d4 = reinterpret_cast<uint4 *>(dst);
+    for (int u = threadIdx.x; u < CkCb<CB>::kBytes / 16; u += kCkThreads) d4[u] = src[u];
+}
+
+template <int CB>
+__device__ inline f32x8 ck_entry(const char *cb, int s, int c) {
+    const char *p = cb + (s * kCodes + c) * CkCb<CB>::kEntryBytes;
+    if (CB == 0) {
+        return *reinterpret_cast<const f32x8 *>(p);
+    } else {
+        const f16x8 h = *reinterpret_cast<const f16x8 *>(p);
+        f32x8 f;
+#pragma unroll
+        for (int i = 0; i < 8; i++) f[i] = (float)h[i];
+        return f;
+    }
+}
+
+// B operand of K-step kk (slices 2kk, 2kk+1 of the tile) for lane l: row
+// l % 32 of the chunk, slice 2kk + l / 32, 8 weights = bf16(c1 + c2 + c3).
+// blk: the chunk's 3 KB code block in LDS ([stage][half][slice][16 rows]).
+template <int CB>
+__device__ inline bf16x8 ck_weights(const uint8_t *blk, const char *cb, int kk, int lane) {
+    const int n = lane & 31, j = 2 * kk + (lane >> 5);
+    const int o = (n >> 4) * 512 + j * 16 + (n & 15);
+    const f32x8 a = ck_entry<CB>(cb, 0, blk[o]);
+    const f32x8 b = ck_entry<CB>(cb, 1, blk[1024 + o]);
+    const f32x8 c = ck_entry<CB>(cb, 2, blk[2048 + o]);
+    bf16x8 w;
+#pragma unroll
+    for (int i = 0; i < 8; i++) w[i] = (__bf16)((a[i] + b[i]) + c[i]);
+    return w;
+}
+
+// Stage a token tile: rows [p0, p0 + 32 * kCkMt) of the permuted bf16 matrix
+// src [P][ld], columns [c0, c0 + 256), into LDS rows of kXRow; rows at or past
+// p_end and columns at or past n_cols are zero.
+__device__ inline void ck_stage_rows(__bf16 *dst, const __bf16 *src, int ld, int p0, int p_end, int c0, int n_cols) {
+    // 16-byte pieces: 32 per row
+    for (int u = threadIdx.x; u < 32 * kCkMt * 32; u += kCkThreads) {
+        const int row = u >> 5, piece = u & 31;
+        const int p = p0 + row, col = c0 + piece * 8;
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (p < p_end) {
+            const __bf16 *s = src + (size_t)p * ld + col;
+            if (col + 8 <= n_cols) {
+                v = *reinterpret_cast<const uint4 *>(s);
+            } else if (col < n_cols) {
+                __bf16 tmp[8];
+#pragma unroll
+                for (int i = 0; i < 8; i++) tmp[i] = col + i < n_cols ? s[i] : (__bf16)0.f;
+                v = *reinterpret_cast<const uint4 *>(tmp);
+            }
+        }
+        *reinterpret_cast<uint4 *>(dst + row * kXRow + piece * 8) = v;
+    }
+}
+
+// A operand of K-step kk for lane l: token row l % 32 of tile mt, inputs
+// kk * 16 + 8 (l / 32) .. + 8.
+__device__ inline bf16x8 ck_tokens(const __bf16 *xs, int mt, int kk, int lane) {
+    return *reinterpret_cast<const bf16x8 *>(xs + (mt * 32 + (lane & 31)) * kXRow + kk * 16 + (lane >> 5) * 8);
+}
+
+// Stage this wave's 3 KB code block in LDS (lane l: 3 x 16 bytes), or zeros.
+__device__ inline void ck_stage_codes(uint8_t *dst, const uint8_t *blk, bool valid, int lane) {
+    uint4 *d4 = reinterpret_cast<uint4 *>(dst);
+    const uint4 *s4 = reinterpret_cast<const uint4 *>(blk);
+#pragma unroll
+    for (int s = 0; s < 3; s++) d4[s * 64 + lane] = valid ? s4[s * 64 + lane] : make_uint4(0, 0, 0, 0);
+}
+
+struct ChunkArgs {
+    const uint8_t *codes;
+    const void *cbs;
+    const int *grp_off, *act, *perm;
+    const __bf16 *X;  // [P][d] permuted bf16 tokens
+    __bf16 *H;        // [P][ffn] permuted bf16 SwiGLU outputs
+    const float *gates;
+    float *y;
+    Geometry g;
+};
+
+// ---------------------------------------------------------------------------
+// gate/up: grid (ceil(ffn / 64), E), 256 threads.  Workgroup (nb, a) takes
+// active expert act[a] and output rows nb * 64 .. + 64 of gate and of up:
+// wave w = (matrix w / 2, chunk 2 nb + w % 2).
+template <int CB>
+__global__ __launch_bounds__(kCkThreads) void k_chunk_gu(ChunkArgs A) {
+    const Geometry &g = A.g;
+    const int a = blockIdx.y;
+    if (a >= A.act[g.E]) return;
+    const int e = A.act[a];
+    const int g0 = A.grp_off[e], g1 = A.grp_off[e + 1];
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int m = wave >> 1, chunk = 2 * blockIdx.x + (wave & 1);
+    const MatGeom &mg = g.m[m];
+    const bool chunk_ok = chunk < mg.n_chunks;
+    __shared__ __align__(16) char cb_lds[2][CkCb<CB>::kBytes];
+    __shared__ __align__(16) uint8_t code_lds[4][kChunkBytes];
+    __shared__ __align__(16) __bf16 xs[32 * kCkMt * kXRow];
+    ck_stage_cb<CB>(cb_lds[0], A.cbs, e, 0);
+    ck_stage_cb<CB>(cb_lds[1], A.cbs, e, 1);
+    const uint8_t *mat = A.codes + (int64_t)e * g.rec_int + mg.off;
+    for (int p0 = g0; p0 < g1; p0 += 32 * kCkMt) {
+        f32x16c acc[kCkMt];
+#pragma unroll
+        for (int mt = 0; mt < kCkMt; mt++)
+#pragma unroll
+            for (int v = 0; v < 16; v++) acc[mt][v] = 0.f;
+        for (int kt = 0; kt < mg.n_tiles; kt++) {
+            __syncthreads();  // previous tile's LDS reads are done
+            ck_stage_rows(xs, A.X, g.d, p0, g1, kt * kTileSlices * kVec, g.d);
+            ck_stage_codes(code_lds[wave], mat + ((int64_t)kt * mg.n_chunks + chunk) * kChunkBytes, chunk_ok, lane);
+            __syncthreads();
+#pragma unroll 2
+            for (int kk = 0; kk < kTileSlices / 2; kk++) {
+                const bf16x8 w = ck_weights<CB>(code_lds[wave], cb_lds[m], kk, lane);
+#pragma unroll
+                for (int mt = 0; mt < kCkMt; mt++)
+                    acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ck_tokens(xs, mt, kk, lane), w, acc[mt], 0, 0,
+                                                                      0);
+            }
+        }
+        // h = silu(gate) * up: the up waves hand their tiles to the gate waves
+        __syncthreads();
+        float *ex = reinterpret_cast<float *>(xs);  // [2 chunks][kCkMt][16][64]
+        if (m == 1)
+#pragma unroll
+            for (int mt = 0; mt < kCkMt; mt++)
+#pragma unroll
+                for (int v = 0; v < 16; v++) ex[(((wave & 1) * kCkMt + mt) * 16 + v) * 64 + lane] = acc[mt][v];
+        __syncthreads();
+        if (m == 0 && chunk_ok) {
+            const int row = chunk * kChunkRows + (lane & 31);
+#pragma unroll
+            for (int mt = 0; mt < kCkMt; mt++) {
+#pragma unroll
+                for (int v = 0; v < 16; v++) {
+                    const int p = p0 + mt * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+                    const float ga = acc[mt][v], up = ex[(((wave & 1) * kCkMt + mt) * 16 + v) * 64 + lane];
+                    const float h = ga / (1.f + expf(-ga)) * up;
+                    if (p < g1 && row < g.ffn) A.H[(size_t)p * g.ffn + row] = (__bf16)h;
+                }
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// down: grid (ceil(d / 128), E), 256 threads.  Workgroup (nb, a) takes active
+// expert act[a] and output rows nb * 128 .. + 128 (wave w: chunk 4 nb + w);
+// y[t][row] += gate * (h W_d^T)[pos][row] with fp32 atomics.
+template <int CB>
+__global__ __launch_bounds__(kCkThreads) void k_chunk_down(ChunkArgs A) {
+    const Geometry &g = A.g;
+    const int a = blockIdx.y;
+    if (a >= A.act[g.E]) return;
+    const int e = A.act[a];
+    const int g0 = A.grp_off[e], g1 = A.grp_off[e + 1];
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const MatGeom &mg = g.m[2];
+    const int chunk = 4 * blockIdx.x + wave;
+    const bool chunk_ok = chunk < mg.n_chunks;
+    __shared__ __align__(16) char cb_lds[CkCb<CB>::kBytes];
+    __shared__ __align__(16) uint8_t code_lds[4][kChunkBytes];
+    __shared__ __align__(16) __bf16 hs[32 * kCkMt * kXRow];
+    ck_stage_cb<CB>(cb_lds, A.cbs, e, 2);
+    const uint8_t *mat = A.codes + (int64_t)e * g.rec_int + mg.off;
+    const int k = g.k;
+    for (int p0 = g0; p0 < g1; p0 += 32 * kCkMt) {
+        f32x16c acc[kCkMt];
+#pragma unroll
+        for (int mt = 0; mt < kCkMt; mt++)
+#pragma unroll
+            for (int v = 0; v < 16; v++) acc[mt][v] = 0.f;
+        for (int kt = 0; kt < mg.n_tiles; kt++) {
+            __syncthreads();
+            ck_stage_rows(hs, A.H, g.ffn, p0, g1, kt * kTileSlices * kVec, g.ffn);
+            ck_stage_codes(code_lds[wave], mat + ((int64_t)kt * mg.n_chunks + chunk) * kChunkBytes, chunk_ok, lane);
+            __syncthreads();
+#pragma unroll 2
+            for (int kk = 0; kk < kTileSlices / 2; kk++) {
+                const bf16x8 w = ck_weights<CB>(code_lds[wave], cb_lds, kk, lane);
+#pragma unroll
+                for (int mt = 0; mt < kCkMt; mt++)
+                    acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ck_tokens(hs, mt, kk, lane), w, acc[mt], 0, 0,
+                                                                      0);
+            }
+        }
+        if (chunk_ok) {
+            const int row = chunk * kChunkRows + (lane & 31);
+#pragma unroll
+            for (int mt = 0; mt < kCkMt; mt++) {
+#pragma unroll
+                for (int v = 0; v < 16; v++) {
+                    const int p = p0 + mt * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+                    if (p < g1 && row < g.d) {
+                        const int pair = A.perm[p];
+                        unsafeAtomicAdd(A.y + (size_t)(pair / k) * g.d + row, A.gates[pair] * acc[mt][v]);
+                    }
+                }
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+hipError_t launch_chunk(const Geometry &g, const ChunkWork &cw, const uint8_t *codes, const void *cbs, const float *x,
+                        const int32_t *ids, const float *gates, float *y, int T, int pre, int residual, double eps,
+                        int *err, hipStream_t s) {
+    const int P = T * g.k;
+    hipLaunchKernelGGL(k_chunk_prep, dim3(1), dim3(1024), 0, s, ids, P, g.E, cw.grp_off, cw.perm, cw.pos_of, cw.act,
+                       err);
+    hipError_t rc = hipGetLastError();
+    if (rc != hipSuccess) return rc;
+    hipLaunchKernelGGL(k_chunk_stage, dim3(T), dim3(kCkThreads), 0, s, x, g.d, g.k, pre, eps, residual, g.E, ids,
+                       cw.pos_of, cw.X, y);
+    rc = hipGetLastError();
+    if (rc != hipSuccess) return rc;
+    ChunkArgs A{codes, cbs, cw.grp_off, cw.act, cw.perm, cw.X, cw.H, gates, y, g};
+    const dim3 ggu((g.m[0].n_chunks + 1) / 2, g.E), gdn((g.m[2].n_chunks + 3) / 4, g.E);
+    if (g.cb_dtype == 0) {
+        hipLaunchKernelGGL(k_chunk_gu<0>, ggu, dim3(kCkThreads), 0, s, A);
+        hipLaunchKernelGGL(k_chunk_down<0>, gdn, dim3(kCkThreads), 0, s, A);
+    } else {
+        hipLaunchKernelGGL(k_chunk_gu<1>, ggu, dim3(kCkThreads), 0, s, A);
+        hipLaunchKernelGGL(k_chunk_down<1>, gdn, dim3(kCkThreads), 0, s, A);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace rvq

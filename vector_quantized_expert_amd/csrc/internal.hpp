@@ -97,6 +97,16 @@ struct Workspace {
     int n_wg;           // persistent workgroups (all resident at once: blocks per CU x CUs)
 };
 
+// Chunk-path workspace (device), sized for max_tokens * k pairs.
+struct ChunkWork {
+    __bf16 *X;     // [P][d] tokens in expert-grouped order, bf16
+    __bf16 *H;     // [P][ffn] SwiGLU outputs in the same order, bf16
+    int *perm;     // [P] position -> pair
+    int *pos_of;   // [P] pair -> position
+    int *grp_off;  // [E + 2] group offsets (group E: invalid ids)
+    int *act;      // [E + 1] experts with tokens, then their count at [E]
+};
+
 constexpr int kRouteTok = 8;       // tokens per router workgroup when T > 1
 constexpr int kMaxExperts = 1024;
 constexpr int kMaxTopK = 64;
@@ -112,6 +122,9 @@ hipError_t init_route(Workspace &w, int E, int64_t max_tokens, int n_cu, hipStre
 hipError_t launch_route(const Geometry &g, Workspace &w, const float *x, const float *Wt, int T, int pre,
                         double eps, int32_t *ids, float *gates, hipStream_t s);
 hipError_t layer_blocks_per_cu(int cb_dtype, int *out);
+hipError_t launch_chunk(const Geometry &g, const ChunkWork &cw, const uint8_t *codes, const void *cbs, const float *x,
+                        const int32_t *ids, const float *gates, float *y, int T, int pre, int residual, double eps,
+                        int *err, hipStream_t s);
 hipError_t launch_layer(const Geometry &g, const Workspace &w, const uint8_t *codes, const void *cbs,
                         const float *Wt, const float *x, const int32_t *ids, const float *gates, float *y, int T,
                         int pre, int residual, double eps, bool route, hipStream_t s);

@@ -21,7 +21,7 @@ OK, EINVAL, ENOTSUP, EBUDGET, ENOMEM, EHIP, EDEVICE = 0, -1, -2, -3, -4, -5, -6
 STATUS_NAMES = {0: "OK", -1: "EINVAL", -2: "ENOTSUP", -3: "EBUDGET", -4: "ENOMEM", -5: "EHIP", -6: "EDEVICE"}
 CB_F32, CB_F16 = 0, 1
 CODES_DEVICE, CODES_PINNED_HOST = 0, 1
-KERNEL_KINDS = 3
+KERNEL_KINDS = 4
 
 
 class RvqMoeError(RuntimeError):
@@ -46,6 +46,8 @@ class Desc(ctypes.Structure):
         ("pre_rmsnorm", ctypes.c_int32),
         ("residual", ctypes.c_int32),
         ("max_tokens", ctypes.c_int32),
+        ("chunk_min_tokens", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
         ("eps", ctypes.c_double),
         ("router_w", ctypes.c_void_p),
         ("codebooks", ctypes.c_void_p),
@@ -127,10 +129,11 @@ def _stream(stream) -> int:
 
 def make_desc(*, d, ffn, n_experts, top_k, codebook_dtype, router_w, codebooks, codes,
               codes_location=CODES_DEVICE, cache_slots=0, pre_rmsnorm=False, eps=1e-6, residual=False,
-              max_tokens=1, stream=None, n_stages=3, n_codes=256, vec_dim=8) -> Desc:
+              max_tokens=1, chunk_min_tokens=0, stream=None, n_stages=3, n_codes=256, vec_dim=8) -> Desc:
     return Desc(ctypes.sizeof(Desc), d, ffn, n_experts, top_k, n_stages, n_codes, vec_dim, codebook_dtype,
-                codes_location, cache_slots, int(bool(pre_rmsnorm)), int(bool(residual)), max_tokens, eps,
-                _ptr(router_w), _ptr(codebooks), _ptr(codes), _stream(stream) if stream != 0 else 0)
+                codes_location, cache_slots, int(bool(pre_rmsnorm)), int(bool(residual)), max_tokens,
+                chunk_min_tokens, 0, eps, _ptr(router_w), _ptr(codebooks), _ptr(codes),
+                _stream(stream) if stream != 0 else 0)
 
 
 def open_raw(desc: Desc) -> tuple[int, int]:
