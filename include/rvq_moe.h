@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define RVQ_MOE_ABI_VERSION 2
+#define RVQ_MOE_ABI_VERSION 3
 
 typedef enum rvq_moe_status {
     RVQ_MOE_OK = 0,
@@ -227,6 +227,10 @@ typedef struct rvq_moe_stats {
     uint64_t code_bytes_resident;   /* bytes of the library's code copy */
     uint64_t record_bytes;          /* canonical bytes per expert record */
     uint64_t codebook_bytes;        /* bytes of one expert's codebooks */
+    uint64_t h2d_bytes;             /* slot cache: bytes copied host -> HBM slots */
+    uint64_t slot_hits;             /* slot cache: experts a call found resident */
+    uint64_t slot_misses;           /* slot cache: experts copied in */
+    uint64_t host_syncs;            /* slot cache: calls that read their ids back */
 } rvq_moe_stats;
 
 int rvq_moe_get_stats(const rvq_moe *h, rvq_moe_stats *out);

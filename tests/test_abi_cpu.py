@@ -14,7 +14,7 @@ def test_library_exports_every_header_symbol():
     L = R.lib()
     for n in names:
         assert hasattr(L, n), n
-    assert L.rvq_moe_abi_version() == 2
+    assert L.rvq_moe_abi_version() == 3
 
 
 def _desc(**over):
@@ -40,6 +40,10 @@ def _desc(**over):
     (dict(vec_dim=4), R.ENOTSUP),
     (dict(cache_slots=3), R.EBUDGET),  # below one token's working set (k = 4)
     (dict(cache_slots=-1), R.EINVAL),
+    (dict(cache_slots=8), R.EINVAL),   # slots stream pinned host codes only
+    (dict(codes_location=1), R.EINVAL),  # pinned host codes need slots
+    (dict(codes_location=5), R.EINVAL),
+    (dict(chunk_min_tokens=-1), R.EINVAL),
     (dict(eps=-1.0), R.EINVAL),
 ])
 def test_open_rejects_bad_descriptions_before_any_device_call(over, status):

@@ -28,7 +28,7 @@ def _layer(torch, inp, shape, max_tokens, **kw):
     from vector_quantized_expert_amd import RvqMoe
     return RvqMoe(d=shape.d, ffn=shape.ffn, n_experts=shape.n_experts, top_k=shape.top_k,
                   codebook_dtype=0 if shape.cb_dtype == "f32" else 1, router_w=inp.w_r_dev,
-                  codebooks=inp.cb_dev, codes=inp.codes_dev, max_tokens=max_tokens, **kw)
+                  codebooks=inp.cb_dev, codes=kw.pop("codes", inp.codes_dev), max_tokens=max_tokens, **kw)
 
 
 def _run(torch, layer, shape, x, per_token=False):
@@ -466,3 +466,152 @@ def test_k3_chunk_512_tokens_against_table_path_and_oracle(torch_mod):
     print(f"K3 chunk vs oracle: worst rel L2 {worst:.3e}")
     chunk.close()
     table.close()
+
+
+# --------------------------------------------------------------------------- HBM slot cache (pinned host bank)
+def _pinned_bank(torch, inp):
+    """The canonical code bank copied into pinned host memory (hipHostMalloc)."""
+    dev = inp.codes_dev
+    bank = torch.empty(dev.shape, dtype=torch.uint8, pin_memory=True)
+    bank.copy_(dev)
+    return bank
+
+
+def _lru_model(S, runs):
+    """Hits and misses of the cache policy: per acquire, hits keep their slots;
+    each miss takes the least recently used slot not used by this acquire
+    (the lowest index among equals)."""
+    slot_of, expert_in, last = {}, [-1] * S, [0] * S
+    hits = misses = 0
+    for clock, experts in enumerate(runs, start=1):
+        for e in experts:
+            if e in slot_of:
+                last[slot_of[e]] = clock
+                hits += 1
+        for e in experts:
+            if e in slot_of:
+                continue
+            v = min((sl for sl in range(S) if last[sl] != clock), key=lambda sl: (last[sl], sl))
+            if expert_in[v] >= 0:
+                del slot_of[expert_in[v]]
+            expert_in[v], slot_of[e], last[v] = e, v, clock
+            misses += 1
+    return hits, misses
+
+
+def _table_runs(ids, S):
+    """Token runs of one table-path call whose distinct experts fit S slots."""
+    runs, cur = [], []
+    for row in ids:
+        fresh = [e for e in dict.fromkeys(row.tolist()) if e not in cur]
+        if len(cur) + len(fresh) > S:
+            runs.append(cur)
+            cur = []
+            fresh = list(dict.fromkeys(row.tolist()))
+        cur += fresh
+    runs.append(cur)
+    return runs
+
+
+def test_streaming_table_path_matches_resident_and_counts_lru(torch_mod, tiny):
+    """Codes in pinned host memory through 5 HBM slots (k = 4): one-token calls
+    that evict, and a 12-token call whose experts exceed the slots (run
+    splitting), against a resident handle; hits/misses/bytes against the
+    policy's model."""
+    from synth import gpu as G
+    shape = S.TINY
+    bank = _pinned_bank(torch_mod, tiny)
+    slots = 5
+    st = _layer(torch_mod, tiny, shape, 12, codes=bank, codes_location=1, cache_slots=slots)
+    rs = _layer(torch_mod, tiny, shape, 12)
+    x = S.tokens(0, 700, 20, shape.d)
+    a = _run(torch_mod, st, shape, x, per_token=True)
+    b = _run(torch_mod, rs, shape, x, per_token=True)
+    assert np.array_equal(a[0], b[0])
+    err = np.linalg.norm(a[2] - b[2], axis=1) / np.linalg.norm(b[2], axis=1)
+    assert err.max() <= 1e-6, err.max()
+    runs = [list(dict.fromkeys(row.tolist())) for row in a[0]]
+    x2 = S.tokens(0, 800, 12, shape.d)
+    a2 = _run(torch_mod, st, shape, x2)
+    b2 = _run(torch_mod, rs, shape, x2)
+    err = np.linalg.norm(a2[2] - b2[2], axis=1) / np.linalg.norm(b2[2], axis=1)
+    assert err.max() <= 1e-6, err.max()
+    runs += _table_runs(a2[0], slots)
+    hits, misses = _lru_model(slots, runs)
+    stats = st.stats()
+    assert (stats["slot_hits"], stats["slot_misses"]) == (hits, misses)
+    assert stats["h2d_bytes"] == misses * (stats["code_bytes_resident"] // slots)
+    assert stats["host_syncs"] == 21
+    _check(tiny, shape, x, *a, tokens=range(4))
+    st.close()
+    rs.close()
+
+
+def test_streaming_chunk_path_matches_resident(torch_mod):
+    """The chunk path with 4 slots: experts in rounds of 2, copies overlapping
+    the previous round's kernels; same outputs as with resident codes."""
+    from synth import gpu as G
+    shape = S.Shape(264, 136, 12, 3, "f16")
+    inp = G.LayerInputs(shape, seed=23, layer=0, host_codes=True)
+    bank = _pinned_bank(torch_mod, inp)
+    st = _layer(torch_mod, inp, shape, 48, codes=bank, codes_location=1, cache_slots=4, chunk_min_tokens=8)
+    rs = _layer(torch_mod, inp, shape, 48, chunk_min_tokens=8)
+    x = S.tokens(23, 0, 48, shape.d)
+    for _ in range(2):
+        a = _run(torch_mod, st, shape, x)
+        b = _run(torch_mod, rs, shape, x)
+        assert np.array_equal(a[0], b[0])
+        err = np.linalg.norm(a[2] - b[2], axis=1) / np.linalg.norm(b[2], axis=1)
+        assert err.max() <= 1e-6, err.max()
+    _check_chunk(inp, shape, x, *a, tokens=[0, 47])
+    n_exp = len(np.unique(a[0]))
+    assert st.stats()["slot_misses"] + st.stats()["slot_hits"] == 2 * n_exp
+    st.close()
+    rs.close()
+
+
+def test_streaming_validation(torch_mod, tiny):
+    from vector_quantized_expert_amd import RvqMoeError
+    from vector_quantized_expert_amd import rvq_moe as R
+    shape = S.TINY
+    bank = _pinned_bank(torch_mod, tiny)
+    with pytest.raises(RvqMoeError) as ei:
+        _layer(torch_mod, tiny, shape, 1, codes=bank, codes_location=1, cache_slots=3)   # < top_k
+    assert ei.value.status == R.EBUDGET
+    pageable = tiny.codes_dev.cpu()
+    with pytest.raises(RvqMoeError) as ei:
+        _layer(torch_mod, tiny, shape, 1, codes=pageable, codes_location=1, cache_slots=4)
+    assert ei.value.status == R.EINVAL
+    st = _layer(torch_mod, tiny, shape, 2, codes=bank, codes_location=1, cache_slots=4)
+    x = torch_mod.zeros((2, shape.d), device="cuda")
+    ids = torch_mod.zeros((2, 4), dtype=torch_mod.int32, device="cuda")
+    g = torch_mod.zeros((2, 4), device="cuda")
+    y = torch_mod.zeros((2, shape.d), device="cuda")
+    with pytest.raises(RvqMoeError) as ei:
+        st.route_forward(x, 1, ids, g, y)
+    assert ei.value.status == R.ENOTSUP
+    st.close()
+
+
+def test_k3_streaming_batch1_matches_resident(torch_mod):
+    """d=7168, ffn=2048, E=384, top-16 from a pinned host bank through 32 slots,
+    one token per call; against a resident handle and the oracle."""
+    from synth import gpu as G
+    shape = S.K3
+    inp = G.LayerInputs(shape, seed=0, layer=6)
+    bank = _pinned_bank(torch_mod, inp)
+    st = _layer(torch_mod, inp, shape, 1, codes=bank, codes_location=1, cache_slots=32)
+    rs = _layer(torch_mod, inp, shape, 1)
+    inp.free_codes()
+    torch_mod.cuda.empty_cache()
+    x = S.tokens(0, 4000, 4, shape.d)
+    a = _run(torch_mod, st, shape, x, per_token=True)
+    b = _run(torch_mod, rs, shape, x, per_token=True)
+    assert np.array_equal(a[0], b[0])
+    err = np.linalg.norm(a[2] - b[2], axis=1) / np.linalg.norm(b[2], axis=1)
+    assert err.max() <= 1e-6, err.max()
+    _check(inp, shape, x, *a, tokens=[0])
+    assert st.stats()["slot_misses"] >= 16
+    st.close()
+    rs.close()
+    del bank

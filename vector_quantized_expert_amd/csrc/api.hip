@@ -17,6 +17,7 @@
 #include "rvq_moe.h"
 
 #include "internal.hpp"
+#include "slots.hpp"
 
 using namespace rvq;
 
@@ -46,7 +47,11 @@ struct rvq_moe {
     int chunk_min;       // layer_forward calls with T >= chunk_min take the chunk path
     ChunkWork cw;        // its workspace (all null when max_tokens < chunk_min)
     double eps;
-    uint8_t *codes;      // [E][rec_int] internal layout
+    uint8_t *codes;      // [E][rec_int] internal layout (resident codes), or null when streaming
+    bool streaming;      // codes in pinned host memory, cached in HBM slots
+    SlotCache cache;     // the slot cache (streaming only)
+    std::vector<int> call_experts;  // scratch: a call's distinct experts
+    std::vector<int> call_used;     // scratch: slots a launch reads
     void *cbs;           // [E][3][3][256][8]
     float *router_wt;    // [E][d] (transposed copy)
     Workspace ws;
@@ -109,6 +114,7 @@ static void free_handle(rvq_moe *h) {
     (void)hipFree(h->cw.grp_off);
     (void)hipFree(h->cw.act);
     for (hipEvent_t e : h->prof_pool) (void)hipEventDestroy(e);
+    slots_close(h->cache);
     delete h;
 }
 
@@ -134,7 +140,8 @@ static int open_impl(const rvq_moe_desc *desc, rvq_moe *h) {
     h->chunk_min = D.chunk_min_tokens > 0 ? D.chunk_min_tokens : RVQ_MOE_CHUNK_MIN_TOKENS;
     const Geometry &g = h->g;
     const int64_t E = D.n_experts;
-    HIP_TRY(hipMalloc(&h->codes, (size_t)(E * g.rec_int)));
+    h->streaming = D.codes_location == RVQ_MOE_CODES_PINNED_HOST;
+    if (!h->streaming) HIP_TRY(hipMalloc(&h->codes, (size_t)(E * g.rec_int)));
     HIP_TRY(hipMalloc(&h->cbs, (size_t)(E * g.cb_bytes)));
     HIP_TRY(hipMalloc(&h->router_wt, sizeof(float) * (size_t)D.d * E));
     const int64_t T = D.max_tokens, P = T * D.top_k;
@@ -166,9 +173,14 @@ static int open_impl(const rvq_moe_desc *desc, rvq_moe *h) {
     HIP_TRY(hipMemsetAsync(h->ws.err, 0, sizeof(int), s));
     HIP_TRY(hipMemcpyAsync(h->cbs, D.codebooks, (size_t)(E * g.cb_bytes), hipMemcpyDeviceToDevice, s));
     HIP_TRY(launch_transpose(D.router_w, h->router_wt, D.d, D.n_experts, s));
-    HIP_TRY(launch_repack(g, D.codes, h->codes, D.n_experts, s));
+    if (h->streaming) {
+        const int S = D.cache_slots < D.n_experts ? D.cache_slots : D.n_experts;
+        HIP_TRY(slots_open(h->cache, g, S, (int)P, D.codes, s));
+    } else {
+        HIP_TRY(launch_repack(g, D.codes, h->codes, D.n_experts, s));
+    }
     HIP_TRY(hipStreamSynchronize(s));
-    h->stats.code_bytes_resident = (uint64_t)(E * g.rec_int);
+    h->stats.code_bytes_resident = h->streaming ? (uint64_t)(h->cache.S * g.rec_int) : (uint64_t)(E * g.rec_int);
     h->stats.record_bytes = (uint64_t)g.rec_canon;
     h->stats.codebook_bytes = (uint64_t)g.cb_bytes;
     return RVQ_MOE_OK;
@@ -210,8 +222,18 @@ extern "C" int rvq_moe_open(const rvq_moe_desc *desc, rvq_moe **out) {
                     D.top_k);
     if (D.codes_location != RVQ_MOE_CODES_DEVICE && D.codes_location != RVQ_MOE_CODES_PINNED_HOST)
         return fail(RVQ_MOE_EINVAL, "codes_location=%d", D.codes_location);
-    if (D.codes_location != RVQ_MOE_CODES_DEVICE || D.cache_slots != 0)
-        return fail(RVQ_MOE_ENOTSUP, "only resident device codes are implemented");
+    if (D.codes_location == RVQ_MOE_CODES_DEVICE && D.cache_slots != 0)
+        return fail(RVQ_MOE_EINVAL, "cache_slots=%d: the slot cache streams PINNED_HOST codes only", D.cache_slots);
+    if (D.codes_location == RVQ_MOE_CODES_PINNED_HOST) {
+        if (D.cache_slots == 0) return fail(RVQ_MOE_EINVAL, "PINNED_HOST codes need cache_slots >= top_k");
+        if (D.codes) {
+            hipPointerAttribute_t attr;
+            const hipError_t pe = hipPointerGetAttributes(&attr, D.codes);
+            (void)hipGetLastError();  // clear the error a plain host pointer leaves
+            if (pe != hipSuccess || attr.type != hipMemoryTypeHost)
+                return fail(RVQ_MOE_EINVAL, "PINNED_HOST codes must be pinned host memory (hipHostMalloc)");
+        }
+    }
     if (!D.router_w || !D.codebooks || !D.codes) return fail(RVQ_MOE_EINVAL, "null router_w/codebooks/codes");
     if (!(D.eps >= 0.0)) return fail(RVQ_MOE_EINVAL, "eps must be >= 0");
     rvq_moe *h = new (std::nothrow) rvq_moe();
@@ -274,6 +296,78 @@ extern "C" int rvq_moe_route_topk(rvq_moe *h, const float *x, int32_t T, int32_t
     return RVQ_MOE_OK;
 }
 
+// layer_forward with the codes streaming through the slot cache.  Reads the
+// call's ids back (the one host synchronisation), then enqueues everything:
+//  - table path: tokens in runs whose distinct experts fit the slots; per run,
+//    the copies of its missing experts, then one layer launch on the run;
+//  - chunk path: grouping and staging once, then the active experts in rounds
+//    of S / 2, so that the copies of one round overlap the kernels of the
+//    previous one (least-recently-used slots are the round before's).
+static int stream_forward(rvq_moe *h, const float *x, int T, const int32_t *ids, const float *gates, float *y,
+                          hipStream_t s) {
+    SlotCache &c = h->cache;
+    const Geometry &g = h->g;
+    const int k = g.k;
+    HIP_TRY(hipMemcpyAsync(c.ids_host, ids, sizeof(int32_t) * (size_t)T * k, hipMemcpyDeviceToHost, s));
+    HIP_TRY(hipStreamSynchronize(s));
+    c.syncs++;
+    std::vector<int> &U = h->call_experts;
+    U.clear();
+    if (T >= h->chunk_min) {
+        for (int p = 0; p < T * k; p++) {
+            const int e = c.ids_host[p];
+            if (e >= 0 && e < g.E && c.mark[e] != c.clock + 1) {
+                c.mark[e] = (uint32_t)(c.clock + 1);
+                U.push_back(e);
+            }
+        }
+        std::sort(U.begin(), U.end());  // the device's order of active experts
+        HIP_TRY(launch_chunk_prep(g, h->cw, x, ids, y, T, h->pre_rmsnorm, h->residual, h->eps, h->ws.err, s));
+        const int R = c.S >= 2 ? c.S / 2 : 1;
+        for (int a0 = 0; a0 < (int)U.size(); a0 += R) {
+            const int a1 = a0 + R < (int)U.size() ? a0 + R : (int)U.size();
+            HIP_TRY(slots_acquire(c, U.data() + a0, a1 - a0, s, h->call_used));
+            HIP_TRY(launch_chunk_experts(g, h->cw, nullptr, c.tab_dev, h->cbs, gates, y, a0, a1, s));
+            HIP_TRY(slots_release(c, h->call_used, s));
+        }
+        return RVQ_MOE_OK;
+    }
+    int t0 = 0;
+    uint32_t stamp = (uint32_t)(c.clock + 1);
+    auto flush = [&](int t1) -> int {
+        HIP_TRY(slots_acquire(c, U.data(), (int)U.size(), s, h->call_used));
+        HIP_TRY(launch_layer(g, h->ws, nullptr, c.tab_dev, h->cbs, h->router_wt, x + (size_t)t0 * g.d,
+                             ids + (size_t)t0 * k, gates + (size_t)t0 * k, y + (size_t)t0 * g.d, t1 - t0,
+                             h->pre_rmsnorm, h->residual, h->eps, false, s));
+        HIP_TRY(slots_release(c, h->call_used, s));
+        return RVQ_MOE_OK;
+    };
+    for (int t = 0; t < T; t++) {
+        int fresh = 0;  // this token's experts not yet in the run's set
+        for (int j = 0; j < k; j++) {
+            const int e = c.ids_host[t * k + j];
+            if (e < 0 || e >= g.E || c.mark[e] == stamp) continue;
+            bool dup = false;
+            for (int i = 0; i < j; i++) dup |= c.ids_host[t * k + i] == e;
+            fresh += !dup;
+        }
+        if ((int)U.size() + fresh > c.S) {
+            const int rc = flush(t);
+            if (rc) return rc;
+            t0 = t;
+            U.clear();
+            stamp = (uint32_t)(c.clock + 1);  // flush advanced the clock: a fresh stamp
+        }
+        for (int j = 0; j < k; j++) {
+            const int e = c.ids_host[t * k + j];
+            if (e < 0 || e >= g.E || c.mark[e] == stamp) continue;
+            c.mark[e] = stamp;
+            U.push_back(e);
+        }
+    }
+    return flush(T);
+}
+
 extern "C" int rvq_moe_layer_forward(rvq_moe *h, const float *x, int32_t T, const int32_t *ids,
                                      const float *gates, float *y, void *stream) {
     int rc = check_call(h, x, T);
@@ -282,14 +376,18 @@ extern "C" int rvq_moe_layer_forward(rvq_moe *h, const float *x, int32_t T, cons
     if ((const void *)y == (const void *)x) return fail(RVQ_MOE_EINVAL, "y aliases x");
     hipStream_t s = static_cast<hipStream_t>(stream);
     const bool prof = h->prof_every > 0 && (h->prof_calls++ % (uint64_t)h->prof_every) == 0;
-    if (T >= h->chunk_min) {
+    if (h->streaming) {
+        ProfScope p(h, s, prof, T >= h->chunk_min ? 3 : 1);
+        rc = stream_forward(h, x, T, ids, gates, y, s);
+        if (rc) return rc;
+    } else if (T >= h->chunk_min) {
         ProfScope p(h, s, prof, 3);
         HIP_TRY(launch_chunk(h->g, h->cw, h->codes, h->cbs, x, ids, gates, y, T, h->pre_rmsnorm, h->residual,
                              h->eps, h->ws.err, s));
     } else {
         ProfScope p(h, s, prof, 1);
-        HIP_TRY(launch_layer(h->g, h->ws, h->codes, h->cbs, h->router_wt, x, ids, gates, y, T, h->pre_rmsnorm,
-                             h->residual, h->eps, false, s));
+        HIP_TRY(launch_layer(h->g, h->ws, h->codes, nullptr, h->cbs, h->router_wt, x, ids, gates, y, T,
+                             h->pre_rmsnorm, h->residual, h->eps, false, s));
     }
     h->stats.forward_calls++;
     h->stats.tokens_forwarded += (uint64_t)T;
@@ -305,12 +403,14 @@ extern "C" int rvq_moe_route_forward(rvq_moe *h, const float *x, int32_t T, int3
     if ((const void *)y == (const void *)x) return fail(RVQ_MOE_EINVAL, "y aliases x");
     if (T * h->g.k > kRouteMaxPairs)
         return fail(RVQ_MOE_EINVAL, "n_tokens * top_k = %d above %d for one routed call", T * h->g.k, kRouteMaxPairs);
+    if (h->streaming)
+        return fail(RVQ_MOE_ENOTSUP, "route_forward needs resident codes (streaming reads the ids on the host)");
     hipStream_t s = static_cast<hipStream_t>(stream);
     const bool prof = h->prof_every > 0 && (h->prof_calls++ % (uint64_t)h->prof_every) == 0;
     {
         ProfScope p(h, s, prof, 2);
-        HIP_TRY(launch_layer(h->g, h->ws, h->codes, h->cbs, h->router_wt, x, ids, gates, y, T, h->pre_rmsnorm,
-                             h->residual, h->eps, true, s));
+        HIP_TRY(launch_layer(h->g, h->ws, h->codes, nullptr, h->cbs, h->router_wt, x, ids, gates, y, T,
+                             h->pre_rmsnorm, h->residual, h->eps, true, s));
     }
     h->stats.route_calls++;
     h->stats.tokens_routed += (uint64_t)T;
@@ -354,6 +454,10 @@ extern "C" int rvq_moe_abi_version(void) { return RVQ_MOE_ABI_VERSION; }
 extern "C" int rvq_moe_get_stats(const rvq_moe *h, rvq_moe_stats *out) {
     if (!h || !out) return fail(RVQ_MOE_EINVAL, "null handle or out");
     *out = h->stats;
+    out->h2d_bytes = h->cache.h2d_bytes;
+    out->slot_hits = h->cache.hits;
+    out->slot_misses = h->cache.misses;
+    out->host_syncs = h->cache.syncs;
     return RVQ_MOE_OK;
 }
 

@@ -237,6 +237,8 @@ __device__ inline void ck_stage_codes(uint8_t *dst, const uint8_t *blk, bool val
 
 struct ChunkArgs {
     const uint8_t *codes;
+    const uint8_t *const *slot_tab;  // [E] record pointers (slot cache) or null
+    int a0, a1;                      // active experts act[a0 .. a1)
     const void *cbs;
     const int *grp_off, *act, *perm;
     const __bf16 *X;  // [P][d] permuted bf16 tokens
@@ -253,8 +255,8 @@ struct ChunkArgs {
 template <int CB>
 __global__ __launch_bounds__(kCkThreads) void k_chunk_gu(ChunkArgs A) {
     const Geometry &g = A.g;
-    const int a = blockIdx.y;
-    if (a >= A.act[g.E]) return;
+    const int a = A.a0 + blockIdx.y;
+    if (a >= A.a1 || a >= A.act[g.E]) return;
     const int e = A.act[a];
     const int g0 = A.grp_off[e], g1 = A.grp_off[e + 1];
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -266,7 +268,7 @@ __global__ __launch_bounds__(kCkThreads) void k_chunk_gu(ChunkArgs A) {
     __shared__ __align__(16) __bf16 xs[32 * kCkMt * kXRow];
     ck_stage_cb<CB>(cb_lds[0], A.cbs, e, 0);
     ck_stage_cb<CB>(cb_lds[1], A.cbs, e, 1);
-    const uint8_t *mat = A.codes + (int64_t)e * g.rec_int + mg.off;
+    const uint8_t *mat = (A.slot_tab ? A.slot_tab[e] : A.codes + (int64_t)e * g.rec_int) + mg.off;
     for (int p0 = g0; p0 < g1; p0 += 32 * kCkMt) {
         f32x16c acc[kCkMt];
 #pragma unroll
@@ -319,8 +321,8 @@ __global__ __launch_bounds__(kCkThreads) void k_chunk_gu(ChunkArgs A) {
 template <int CB>
 __global__ __launch_bounds__(kCkThreads) void k_chunk_down(ChunkArgs A) {
     const Geometry &g = A.g;
-    const int a = blockIdx.y;
-    if (a >= A.act[g.E]) return;
+    const int a = A.a0 + blockIdx.y;
+    if (a >= A.a1 || a >= A.act[g.E]) return;
     const int e = A.act[a];
     const int g0 = A.grp_off[e], g1 = A.grp_off[e + 1];
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -331,7 +333,7 @@ __global__ __launch_bounds__(kCkThreads) void k_chunk_down(ChunkArgs A) {
     __shared__ __align__(16) uint8_t code_lds[4][kChunkBytes];
     __shared__ __align__(16) __bf16 hs[32 * kCkMt * kXRow];
     ck_stage_cb<CB>(cb_lds, A.cbs, e, 2);
-    const uint8_t *mat = A.codes + (int64_t)e * g.rec_int + mg.off;
+    const uint8_t *mat = (A.slot_tab ? A.slot_tab[e] : A.codes + (int64_t)e * g.rec_int) + mg.off;
     const int k = g.k;
     for (int p0 = g0; p0 < g1; p0 += 32 * kCkMt) {
         f32x16c acc[kCkMt];
@@ -371,9 +373,8 @@ __global__ __launch_bounds__(kCkThreads) void k_chunk_down(ChunkArgs A) {
 }
 
 // ---------------------------------------------------------------------------
-hipError_t launch_chunk(const Geometry &g, const ChunkWork &cw, const uint8_t *codes, const void *cbs, const float *x,
-                        const int32_t *ids, const float *gates, float *y, int T, int pre, int residual, double eps,
-                        int *err, hipStream_t s) {
+hipError_t launch_chunk_prep(const Geometry &g, const ChunkWork &cw, const float *x, const int32_t *ids, float *y,
+                             int T, int pre, int residual, double eps, int *err, hipStream_t s) {
     const int P = T * g.k;
     hipLaunchKernelGGL(k_chunk_prep, dim3(1), dim3(1024), 0, s, ids, P, g.E, cw.grp_off, cw.perm, cw.pos_of, cw.act,
                        err);
@@ -381,10 +382,15 @@ hipError_t launch_chunk(const Geometry &g, const ChunkWork &cw, const uint8_t *c
     if (rc != hipSuccess) return rc;
     hipLaunchKernelGGL(k_chunk_stage, dim3(T), dim3(kCkThreads), 0, s, x, g.d, g.k, pre, eps, residual, g.E, ids,
                        cw.pos_of, cw.X, y);
-    rc = hipGetLastError();
-    if (rc != hipSuccess) return rc;
-    ChunkArgs A{codes, cbs, cw.grp_off, cw.act, cw.perm, cw.X, cw.H, gates, y, g};
-    const dim3 ggu((g.m[0].n_chunks + 1) / 2, g.E), gdn((g.m[2].n_chunks + 3) / 4, g.E);
+    return hipGetLastError();
+}
+
+hipError_t launch_chunk_experts(const Geometry &g, const ChunkWork &cw, const uint8_t *codes,
+                                const uint8_t *const *slot_tab, const void *cbs, const float *gates, float *y, int a0,
+                                int a1, hipStream_t s) {
+    if (a1 <= a0) return hipSuccess;
+    ChunkArgs A{codes, slot_tab, a0, a1, cbs, cw.grp_off, cw.act, cw.perm, cw.X, cw.H, gates, y, g};
+    const dim3 ggu((g.m[0].n_chunks + 1) / 2, a1 - a0), gdn((g.m[2].n_chunks + 3) / 4, a1 - a0);
     if (g.cb_dtype == 0) {
         hipLaunchKernelGGL(k_chunk_gu<0>, ggu, dim3(kCkThreads), 0, s, A);
         hipLaunchKernelGGL(k_chunk_down<0>, gdn, dim3(kCkThreads), 0, s, A);
@@ -393,6 +399,14 @@ hipError_t launch_chunk(const Geometry &g, const ChunkWork &cw, const uint8_t *c
         hipLaunchKernelGGL(k_chunk_down<1>, gdn, dim3(kCkThreads), 0, s, A);
     }
     return hipGetLastError();
+}
+
+hipError_t launch_chunk(const Geometry &g, const ChunkWork &cw, const uint8_t *codes, const void *cbs, const float *x,
+                        const int32_t *ids, const float *gates, float *y, int T, int pre, int residual, double eps,
+                        int *err, hipStream_t s) {
+    const hipError_t rc = launch_chunk_prep(g, cw, x, ids, y, T, pre, residual, eps, err, s);
+    if (rc != hipSuccess) return rc;
+    return launch_chunk_experts(g, cw, codes, nullptr, cbs, gates, y, 0, g.E, s);
 }
 
 }  // namespace rvq

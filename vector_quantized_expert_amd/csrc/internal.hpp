@@ -122,11 +122,21 @@ hipError_t init_route(Workspace &w, int E, int64_t max_tokens, int n_cu, hipStre
 hipError_t launch_route(const Geometry &g, Workspace &w, const float *x, const float *Wt, int T, int pre,
                         double eps, int32_t *ids, float *gates, hipStream_t s);
 hipError_t layer_blocks_per_cu(int cb_dtype, int *out);
+// Chunk path: prep + stage (grouping, bf16 tokens, y init), then the
+// contractions for the active experts act[a0 .. a1) (a1 clipped to the number
+// of active experts on the device); launch_chunk does both for all experts.
+hipError_t launch_chunk_prep(const Geometry &g, const ChunkWork &cw, const float *x, const int32_t *ids, float *y,
+                             int T, int pre, int residual, double eps, int *err, hipStream_t s);
+hipError_t launch_chunk_experts(const Geometry &g, const ChunkWork &cw, const uint8_t *codes,
+                                const uint8_t *const *slot_tab, const void *cbs, const float *gates, float *y, int a0,
+                                int a1, hipStream_t s);
 hipError_t launch_chunk(const Geometry &g, const ChunkWork &cw, const uint8_t *codes, const void *cbs, const float *x,
                         const int32_t *ids, const float *gates, float *y, int T, int pre, int residual, double eps,
                         int *err, hipStream_t s);
-hipError_t launch_layer(const Geometry &g, const Workspace &w, const uint8_t *codes, const void *cbs,
-                        const float *Wt, const float *x, const int32_t *ids, const float *gates, float *y, int T,
-                        int pre, int residual, double eps, bool route, hipStream_t s);
+// slot_tab: null (resident codes: expert e's record at codes + e * rec_int) or
+// a device table [E] of record pointers (the HBM slot cache).
+hipError_t launch_layer(const Geometry &g, const Workspace &w, const uint8_t *codes, const uint8_t *const *slot_tab,
+                        const void *cbs, const float *Wt, const float *x, const int32_t *ids, const float *gates,
+                        float *y, int T, int pre, int residual, double eps, bool route, hipStream_t s);
 
 }  // namespace rvq

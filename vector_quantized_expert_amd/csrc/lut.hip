@@ -455,6 +455,7 @@ struct LayerArgs {
     double *sel;        // [T][k] selected logits by rank
     int *gbar;          // [4][kMaxGridGroups + 1] grid arrival counters: y init, logits, ranks, exit
     const uint8_t *codes;
+    const uint8_t *const *slot_tab;  // [E] record of each expert (HBM slot cache), or null: codes + e * rec
     const void *cbs;
     const float *x;
     const int32_t *ids;
@@ -469,6 +470,12 @@ struct LayerArgs {
     int residual;
     double eps;
 };
+
+// Internal code record of expert e (its slot when the codes stream through
+// the HBM slot cache).
+__device__ inline const uint8_t *expert_record(const LayerArgs &a, int e) {
+    return a.slot_tab ? a.slot_tab[e] : a.codes + (int64_t)e * a.g.rec_int;
+}
 
 // x_hat scale of token t: r = sqrt(mean(x^2) + eps) in fp64 (1 without
 // normalisation); cached per workgroup for the last token asked.
@@ -886,7 +893,7 @@ __global__ __launch_bounds__(kBlock) void k_layer(LayerArgs a) {
             SegA nxt{};
             if (un < u1) nxt = seg_a(un, u1, n_ti, n_cf, ord);
             if (cur.e >= 0 && cur.e < g.E) {
-                const uint8_t *base = a.codes + (int64_t)cur.e * g.rec_int + g.m[cur.m].off +
+                const uint8_t *base = expert_record(a, cur.e) + g.m[cur.m].off +
                                       (int64_t)cur.tile * n_cf * kChunkBytes;
                 // consume the prefetched codebook and inputs first, so that waiting
                 // for them does not also wait for the code loads issued below
@@ -932,7 +939,7 @@ __global__ __launch_bounds__(kBlock) void k_layer(LayerArgs a) {
             SegB nxt{};
             if (un < u1) nxt = seg_b(un, u1, n_tf, n_cd, ord);
             if (cur.e >= 0 && cur.e < g.E) {
-                const uint8_t *base = a.codes + (int64_t)cur.e * g.rec_int + g.m[2].off +
+                const uint8_t *base = expert_record(a, cur.e) + g.m[2].off +
                                       (int64_t)cur.ft * n_cd * kChunkBytes;
                 cb_store<CB>(lut, cb);
                 u32x4 p0, p1, p2;
@@ -990,10 +997,10 @@ static LayerKernel layer_kernel(int cb_dtype, bool route, bool nt) {
                  : (nt ? k_layer<1, false, true> : k_layer<1, false, false>);
 }
 
-hipError_t launch_layer(const Geometry &g, const Workspace &w, const uint8_t *codes, const void *cbs,
-                        const float *Wt, const float *x, const int32_t *ids, const float *gates, float *y, int T,
-                        int pre, int residual, double eps, bool route, hipStream_t s) {
-    LayerArgs a{Wt, w.logits, w.sel, w.gbar, codes, cbs, x, ids, gates, y, w.part_gu, w.cntA, w.err, g, T, pre,
+hipError_t launch_layer(const Geometry &g, const Workspace &w, const uint8_t *codes, const uint8_t *const *slot_tab,
+                        const void *cbs, const float *Wt, const float *x, const int32_t *ids, const float *gates,
+                        float *y, int T, int pre, int residual, double eps, bool route, hipStream_t s) {
+    LayerArgs a{Wt, w.logits, w.sel, w.gbar, codes, slot_tab, cbs, x, ids, gates, y, w.part_gu, w.cntA, w.err, g, T, pre,
                 residual, eps};
     // A plain launch of exactly as many workgroups as can be resident at once
     // (sized at open from the occupancy query); the inter-workgroup waits are

@@ -1,0 +1,43 @@
+// slots.hpp -- HBM expert-slot cache state (host side); see slots.hip.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <vector>
+
+#include "internal.hpp"
+
+namespace rvq {
+
+struct SlotCache {
+    int S = 0;                         // slots
+    int E = 0;
+    int64_t rec = 0;                   // internal record bytes (one slot)
+    uint8_t *slots = nullptr;          // device [S][rec]
+    uint8_t *bank = nullptr;           // pinned host [E][rec], internal layout
+    const uint8_t **tab_dev = nullptr; // device [E]: record pointer of each resident expert
+    int32_t *ids_host = nullptr;       // pinned [max_tokens * k]: the call's ids, read back once per call
+    hipStream_t copy = nullptr;        // the library's copy stream (default priority)
+    std::vector<hipEvent_t> filled;    // [S] copy into the slot done
+    std::vector<hipEvent_t> released;  // [S] last kernel reading the slot done
+    std::vector<int> slot_of;          // [E] slot of a resident expert, or -1
+    std::vector<int> expert_in;        // [S] expert in a slot, or -1
+    std::vector<uint64_t> last_use;    // [S] acquire clock of the last use
+    std::vector<uint32_t> mark;        // [E] scratch for set building
+    uint64_t clock = 0;
+    uint64_t hits = 0, misses = 0, h2d_bytes = 0, syncs = 0;
+};
+
+// Allocate the slots and the pinned bank, and fill the bank from the caller's
+// pinned canonical bank (synchronises `s`).
+hipError_t slots_open(SlotCache &c, const Geometry &g, int S, int max_pairs, const uint8_t *canon_host,
+                      hipStream_t s);
+void slots_close(SlotCache &c);
+// Make experts[0 .. n) (distinct, n <= S) resident for kernels enqueued next on
+// `compute`, and point their table entries at their slots; `used` gets the
+// slots to release after those kernels.
+hipError_t slots_acquire(SlotCache &c, const int *experts, int n, hipStream_t compute, std::vector<int> &used);
+hipError_t slots_release(SlotCache &c, const std::vector<int> &used, hipStream_t compute);
+
+}  // namespace rvq

@@ -59,7 +59,8 @@ class Desc(ctypes.Structure):
 class Stats(ctypes.Structure):
     _fields_ = [(n, ctypes.c_uint64) for n in (
         "route_calls", "forward_calls", "tokens_routed", "tokens_forwarded", "expert_evals",
-        "code_bytes_resident", "record_bytes", "codebook_bytes")]
+        "code_bytes_resident", "record_bytes", "codebook_bytes", "h2d_bytes", "slot_hits", "slot_misses",
+        "host_syncs")]
 
 
 _lib = None
