@@ -15,7 +15,9 @@ Other workloads of the same layer shape:
   --chunk      with --batch: every call takes the chunk path (prefill chunk:
                weights rebuilt as bf16 tiles feeding the matrix cores);
   --layers L   a depth chain: L layers, each with RMS normalisation before
-               routing and a residual add, one token through all L per step.
+               routing and a residual add, one token through all L per step;
+  --stream-slots S   codes kept in pinned host memory and streamed through S
+               HBM expert slots (copies on a side stream, overlapped).
 
 Prints one JSON line: tokens/s (value), effective compressed-weight GB/s and
 its fraction of the 8 TB/s HBM peak, the roofline record of the dominant
@@ -56,6 +58,8 @@ def main():
                     help="depth chain of this many layers (RMS normalisation before routing, residual add)")
     ap.add_argument("--chunk", action="store_true",
                     help="every layer_forward call takes the chunk path (bf16 matrix cores)")
+    ap.add_argument("--stream-slots", type=int, default=0,
+                    help="stream the codes from a pinned host bank through this many HBM slots")
     ap.add_argument("--path", choices=("fused", "two-call"), default="two-call",
                     help="fused: rvq_moe_route_forward (one launch per call); "
                          "two-call: rvq_moe_route_topk then rvq_moe_layer_forward")
@@ -77,7 +81,9 @@ def main():
     shape = S.K3
     K, W, B, L = args.steps, args.warmup, args.batch, args.layers
     chain = L > 1
-    if (B < 1 or L < 1 or (chain and B != 1) or (args.path == "fused" and (B * shape.top_k > 1024 or args.chunk))):
+    streaming = args.stream_slots > 0
+    if (B < 1 or L < 1 or (chain and B != 1) or
+            (args.path == "fused" and (B * shape.top_k > 1024 or args.chunk or streaming))):
         print(f"--batch {B} / --layers {L} outside what the chosen path takes", file=sys.stderr)
         sys.exit(2)
 
@@ -85,10 +91,16 @@ def main():
     for li in range(L):
         log(f"staging layer {li}: d={shape.d} ffn={shape.ffn} E={shape.n_experts} k={shape.top_k}")
         inp = G.LayerInputs(shape, seed=args.seed, layer=li)
+        codes, extra = inp.codes_dev, {}
+        if streaming:
+            codes = torch.empty(inp.codes_dev.shape, dtype=torch.uint8, pin_memory=True)
+            codes.copy_(inp.codes_dev)
+            extra = dict(codes_location=1, cache_slots=args.stream_slots)
         layers.append(RvqMoe(d=shape.d, ffn=shape.ffn, n_experts=shape.n_experts, top_k=shape.top_k,
-                             codebook_dtype=1, router_w=inp.w_r_dev, codebooks=inp.cb_dev, codes=inp.codes_dev,
+                             codebook_dtype=1, router_w=inp.w_r_dev, codebooks=inp.cb_dev, codes=codes,
                              max_tokens=B, pre_rmsnorm=chain, residual=chain, eps=1e-6,
-                             chunk_min_tokens=1 if args.chunk else B + 1))
+                             chunk_min_tokens=1 if args.chunk else B + 1, **extra))
+        del codes
         inp.free_codes()
         inputs.append(inp)
         torch.cuda.empty_cache()
@@ -111,6 +123,23 @@ def main():
                 layer.route_topk(h[li, r], B, ids[li, r], gates[li, r], stream)
                 layer.layer_forward(h[li, r], B, ids[li, r], gates[li, r], h[li + 1, r], stream)
 
+    h2d = None
+    if streaming:
+        # the host -> device ceiling this box measures for one large pinned copy
+        src = torch.empty(1 << 30, dtype=torch.uint8, pin_memory=True)
+        dst = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        dst.copy_(src, non_blocking=True)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(3):
+            dst.copy_(src, non_blocking=True)
+        e1.record()
+        torch.cuda.synchronize()
+        h2d = {"ceiling_GBps": 3 * (1 << 30) / (e0.elapsed_time(e1) * 1e-3) / 1e9}
+        del src, dst
+        torch.cuda.empty_cache()
+
     log(f"warmup {W} steps of {B} token(s) x {L} layer(s)")
     for t in range(W):
         step(t)
@@ -121,6 +150,7 @@ def main():
 
     torch.cuda.synchronize()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    stats0 = [layer.stats() for layer in layers]
     ev0.record(stream)
     for t in range(W, W + K):
         step(t)
@@ -139,6 +169,14 @@ def main():
         layer.sync(stream)
     n_l, l_ms = kernels[lut_kind]
     log(f"timed {K} steps in {ms:.2f} ms")
+    if streaming:
+        st = [layer.stats() for layer in layers]
+        moved = sum(a["h2d_bytes"] - b["h2d_bytes"] for a, b in zip(st, stats0))
+        hits = sum(a["slot_hits"] - b["slot_hits"] for a, b in zip(st, stats0))
+        misses = sum(a["slot_misses"] - b["slot_misses"] for a, b in zip(st, stats0))
+        h2d.update({"slots": args.stream_slots, "h2d_bytes": moved, "GBps": moved / (ms * 1e-3) / 1e9,
+                    "frac_of_ceiling": moved / (ms * 1e-3) / 1e9 / h2d["ceiling_GBps"],
+                    "hit_rate": hits / max(hits + misses, 1)})
 
     rec = shape.record_bytes
     # Algorithmic bytes of one layer call: every distinct expert the call routes
@@ -180,8 +218,10 @@ def main():
                          f"layer rebuilt as c1+c2+c3 in fp64); includes regenerating their code records on the host"}
         parity = {"tokens": args.cpu_tokens, "layers_checked": L, "ids_bit_exact": ok_ids, "max_rel_l2": max(errs)}
 
+    where = (f"codes streamed from pinned host memory through {args.stream_slots} HBM slots" if streaming
+             else "resident codes")
     if args.chunk:
-        workload = (f"K3-scale prefill chunk, resident codes: {B} tokens per call through d=7168 ffn=2048 E=384 "
+        workload = (f"K3-scale prefill chunk, {where}: {B} tokens per call through d=7168 ffn=2048 E=384 "
                     f"top-16, tokens grouped by expert, RVQ tiles rebuilt as bf16 for the matrix cores "
                     f"(fp32 accumulation)")
     elif chain:
@@ -189,7 +229,7 @@ def main():
                     f"(3-stage x 256 x 8 fp16 codebooks, uniform u8 codes), RMSNorm (w=1, eps=1e-6) before "
                     f"routing and a residual add per layer, all resident")
     else:
-        workload = (f"K3-scale routed RVQ-MoE layer, batch-{B} decode: d=7168 ffn=2048 E=384 top-16, "
+        workload = (f"K3-scale routed RVQ-MoE layer, batch-{B} decode, {where}: d=7168 ffn=2048 E=384 top-16, "
                     f"3-stage x 256 x 8 fp16 codebooks, uniform u8 codes, T={B} per call")
     out = {
         "metric": METRIC,
@@ -219,6 +259,7 @@ def main():
                      ("k_chunk_prep + k_chunk_stage + k_chunk_gu + k_chunk_down" if args.chunk else "k_layer"),
                      "algorithmic_bytes_per_launch": per_call_bytes, "avg_us": l_avg_us, "timed_launches": int(n_l)},
         "kernels": kernels,
+        "h2d": h2d,
         "mfma": ({"flops_per_call": 6.0 * B * shape.top_k * shape.d * shape.ffn,
                   "tflops": 6.0 * B * shape.top_k * shape.d * shape.ffn / (l_avg_us * 1e-6) / 1e12,
                   "frac_of_bf16_dense_peak": 6.0 * B * shape.top_k * shape.d * shape.ffn / (l_avg_us * 1e-6) / 2.5e15}
