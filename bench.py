@@ -27,6 +27,8 @@ oracle timed on the host cores on a bounded sample (cpu_baseline).
 from __future__ import annotations
 
 import argparse
+import glob
+import hashlib
 import json
 import os
 import sys
@@ -42,6 +44,36 @@ CB_BYTES = 3 * 3 * 256 * 8 * 2  # one expert's fp16 codebooks (3 matrices x 3 st
 
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def source_sha256() -> str:
+    """Hash of the library's sources (kernels, launchers, ABI header)."""
+    h = hashlib.sha256()
+    files = glob.glob(os.path.join(ROOT, "vector_quantized_expert_amd", "csrc", "*.hip"))
+    files += glob.glob(os.path.join(ROOT, "vector_quantized_expert_amd", "csrc", "*.hpp"))
+    for f in sorted(files + [os.path.join(ROOT, "include", "rvq_moe.h")]):
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def recorded_traffic():
+    """HBM bytes per k_layer launch from the committed counter runs (FETCH_SIZE
+    and WRITE_SIZE scaled by a reference copy), or None when the sources have
+    changed since those counters were taken."""
+    path = os.path.join(ROOT, "profiles", "k_layer_k3_batch1_decode_traffic.md")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as fh:
+        for line in fh:
+            key, sep, val = line.partition(":")
+            if sep and key.strip() in ("traffic_bytes_per_launch", "source_sha256"):
+                fields[key.strip()] = val.strip()
+    if fields.get("source_sha256") != source_sha256():
+        return None
+    return int(fields["traffic_bytes_per_launch"])
 
 
 def main():
@@ -60,6 +92,9 @@ def main():
                     help="every layer_forward call takes the chunk path (bf16 matrix cores)")
     ap.add_argument("--stream-slots", type=int, default=0,
                     help="stream the codes from a pinned host bank through this many HBM slots")
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="after the run, one plain device-to-device copy of this many bytes (a reference kernel "
+                         "of known traffic for scaling hardware byte counters)")
     ap.add_argument("--path", choices=("fused", "two-call"), default="two-call",
                     help="fused: rvq_moe_route_forward (one launch per call); "
                          "two-call: rvq_moe_route_topk then rvq_moe_layer_forward")
@@ -189,7 +224,7 @@ def main():
     calls_s = K * L / (ms / 1e3)
     tok_s = K * B / (ms / 1e3)
     gbps = per_call_bytes * calls_s / 1e9
-    l_avg_us = l_ms / max(n_l, 1) * 1e3
+    l_avg_us = l_ms / n_l * 1e3 if n_l else float("nan")  # nan: kernel timing switched off
     l_gbps = per_call_bytes / (l_avg_us * 1e-6) / 1e9
     kernels = {k: {"launches": int(n), "avg_us": (v / n * 1e3 if n else None)} for k, (n, v) in kernels.items()}
 
@@ -254,7 +289,9 @@ def main():
         "compressed_bytes_per_call": per_call_bytes,
         "distinct_experts_per_call": float(uniq.mean()),
         "roofline": {"bound": "hbm", "achieved": l_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": l_gbps / HBM_PEAK_GBPS, "traffic": None,
+                     "frac": l_gbps / HBM_PEAK_GBPS,
+                     "traffic": (recorded_traffic() if (B == 1 and L == 1 and not args.chunk and not streaming and
+                                                        args.path == "two-call") else None),
                      "kernel": "k_layer<route>" if args.path == "fused" else
                      ("k_chunk_prep + k_chunk_stage + k_chunk_gu + k_chunk_down" if args.chunk else "k_layer"),
                      "algorithmic_bytes_per_launch": per_call_bytes, "avg_us": l_avg_us, "timed_launches": int(n_l)},
@@ -269,6 +306,15 @@ def main():
     }
     for layer in layers:
         layer.close()
+    if args.copy_bytes > 0:
+        torch.cuda.empty_cache()
+        src = torch.ones(args.copy_bytes, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        out["copy_reference_bytes"] = args.copy_bytes
+        del src, dst
     print(json.dumps(out), flush=True)
 
 
