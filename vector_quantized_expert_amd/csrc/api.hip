@@ -103,6 +103,7 @@ static void free_handle(rvq_moe *h) {
     (void)hipFree(h->ws.logits);
     (void)hipFree(h->ws.sel);
     (void)hipFree(h->ws.route_logits);
+    (void)hipFree(h->ws.fused_logits);
     (void)hipFree(h->ws.part_gu);
     (void)hipFree(h->ws.cntA);
     (void)hipFree(h->ws.gbar);
@@ -148,6 +149,7 @@ static int open_impl(const rvq_moe_desc *desc, rvq_moe *h) {
     HIP_TRY(hipMalloc(&h->ws.logits, sizeof(double) * (size_t)(T * E)));
     HIP_TRY(hipMalloc(&h->ws.sel, sizeof(double) * (size_t)(T * D.top_k)));
     HIP_TRY(hipMalloc(&h->ws.route_logits, sizeof(double) * (size_t)route_logit_slots(T, D.n_experts)));
+    HIP_TRY(hipMalloc(&h->ws.fused_logits, sizeof(double) * 2 * (size_t)(T * E)));
     HIP_TRY(hipMalloc(&h->ws.part_gu, sizeof(float) * (size_t)(P * 2 * g.m[0].n_tiles * g.ffn_pad)));
     HIP_TRY(hipMalloc(&h->ws.cntA, sizeof(int) * (size_t)P));
     HIP_TRY(hipMalloc(&h->ws.gbar, sizeof(int) * kGbarInts));

@@ -80,6 +80,12 @@ __device__ inline void store_counter(int *p, int v) {
 // Wait until this wave's vector memory operations (including sc1 stores) completed.
 __device__ inline void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// Logit slots hold this NaN until written.  It is a signalling NaN, which no
+// arithmetic result is (results are quiet NaNs at most), so a slot holds it
+// exactly while its logit is not yet published.
+constexpr uint64_t kUnpublished = 0x7FF4DEAD7FF4DEADull;
+constexpr uint32_t kUnpublishedHalf = 0x7FF4DEADu;
+
 // Workspace of one handle (device memory, sized for max_tokens at open).
 struct Workspace {
     double *logits;     // [T][E] fp64 router logits
@@ -89,6 +95,8 @@ struct Workspace {
                            // selected logits for one token (alternating buffers)
     int64_t route_cap;     // max_tokens * E
     int route_parity;      // buffer of the next one-token call
+    double *fused_logits;  // [2][max_tokens][E] logit slots of the in-launch routing (marker NaN when unpublished)
+    int fused_parity;      // buffer of the next in-launch routing
     bool route_one;        // the one-token kernel fits (all E workgroups resident)
     float *part_gu;     // [T*k][2][n_tiles_in][ffn_pad] partial gate/up sums
     int *cntA;          // [T*k] finished gate/up chunks per pair (self-resetting)
@@ -135,7 +143,7 @@ hipError_t launch_chunk(const Geometry &g, const ChunkWork &cw, const uint8_t *c
                         int *err, hipStream_t s);
 // slot_tab: null (resident codes: expert e's record at codes + e * rec_int) or
 // a device table [E] of record pointers (the HBM slot cache).
-hipError_t launch_layer(const Geometry &g, const Workspace &w, const uint8_t *codes, const uint8_t *const *slot_tab,
+hipError_t launch_layer(const Geometry &g, Workspace &w, const uint8_t *codes, const uint8_t *const *slot_tab,
                         const void *cbs, const float *Wt, const float *x, const int32_t *ids, const float *gates,
                         float *y, int T, int pre, int residual, double eps, bool route, hipStream_t s);
 

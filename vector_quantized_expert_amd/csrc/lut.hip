@@ -454,6 +454,7 @@ struct LayerArgs {
     double *logits;     // [T][E]
     double *sel;        // [T][k] selected logits by rank
     int *gbar;          // [4][kMaxGridGroups + 1] grid arrival counters: y init, logits, ranks, exit
+    double *rl_cur, *rl_next;  // [T][E] logit slots of this launch and of the next (in-launch routing)
     const uint8_t *codes;
     const uint8_t *const *slot_tab;  // [E] record of each expert (HBM slot cache), or null: codes + e * rec
     const void *cbs;
@@ -569,6 +570,7 @@ struct Order {
     // without the table: expert ids of the positions a workgroup touches
     int a_base, a_n, b_base, b_n;
     const int *lds;  // [2][kIdCache]
+    const int *all;  // [P] ids of every pair in LDS (routed in this launch), or null
     const int32_t *ids;
     // (LDS reads give per-lane registers; the values are uniform, so they are
     // moved to scalar registers and the segment arithmetic stays scalar)
@@ -585,18 +587,20 @@ struct Order {
     __device__ int pair_at(int pos) const { return tab ? __builtin_amdgcn_readfirstlane(pair[pos]) : pos; }
     __device__ int expert_a(int pos) const {
         return __builtin_amdgcn_readfirstlane(
-            tab ? expert[pos] : ((pos - a_base) < a_n ? lds[pos - a_base] : ids[pos]));
+            tab ? expert[pos] : (all ? all[pos] : ((pos - a_base) < a_n ? lds[pos - a_base] : ids[pos])));
     }
     __device__ int expert_b(int pos) const {
         return __builtin_amdgcn_readfirstlane(
-            tab ? expert[pos] : ((pos - b_base) < b_n ? lds[kIdCache + pos - b_base] : ids[pos]));
+            tab ? expert[pos]
+                : (all ? all[pos] : ((pos - b_base) < b_n ? lds[kIdCache + pos - b_base] : ids[pos])));
     }
 };
 
 // Build the order table in LDS (all threads).  tmp: scratch of at least
 // (E + 1) * (kOrderMax / 64) * 8 + 2 * (E + 1) * 4 bytes (the table area, idle
 // here).  Ids outside [0, E) form a last group of their own.
-__device__ void build_order(const int32_t *ids, int P, int E, char *tmp, int *info, short *pair, short *expert) {
+__device__ void build_order(const int32_t *ids, const int *lds_ids, int P, int E, char *tmp, int *info, short *pair,
+                            short *expert) {
     constexpr int kW = kOrderMax / 64;
     const int NE = E + 1;
     uint64_t *mask = reinterpret_cast<uint64_t *>(tmp);  // [NE][kW] pair bitmask per expert
@@ -606,7 +610,7 @@ __device__ void build_order(const int32_t *ids, int P, int E, char *tmp, int *in
     for (int i = threadIdx.x; i < NE; i += kBlock) cnt[i] = 0;
     __syncthreads();
     for (int p = threadIdx.x; p < P; p += kBlock) {
-        int e = load_counter(ids + p);
+        int e = lds_ids ? lds_ids[p] : load_counter(ids + p);
         if (e < 0 || e >= E) e = E;
         atomicOr(reinterpret_cast<unsigned long long *>(mask + (size_t)e * kW + (p >> 6)), 1ull << (p & 63));
         atomicAdd(cnt + e, 1);
@@ -698,97 +702,132 @@ __device__ inline SegB seg_b(int u, int u1, int n_tf, int n_cd, const Order &o) 
     return s;
 }
 
-// fp64 sum over the workgroup; every thread gets the total.  dred: >= kWaves doubles.
-__device__ inline double block_sum(double v, double *dred) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-    __syncthreads();
-    if ((threadIdx.x & 63) == 0) dred[threadIdx.x >> 6] = v;
-    __syncthreads();
-    double s = 0.0;
-#pragma unroll
-    for (int w = 0; w < kWaves; w++) s += dred[w];
-    return s;
-}
-
-// Routing inside the launch ([FR] "Lecture anticipée et prédiction du routeur":
-// the router decides the token's experts; reading as in the separate route
-// kernels: top-k of fp64 logits, ties to the lower id, softmax over the k).
-//  R1  logits of experts e = wg, wg + G, ...: fp64 sums of exact fp32 products,
-//      divided by the fp64 RMS divisor when normalising;
-//  R2  (all logits published) rank of each of those experts among all E,
-//      ids[t][rank] = e and sel[t][rank] = logit for rank < k;
-//  R3  (all ranks published) every workgroup forms the softmax gates it needs
-//      (gate_lds, fp64 in selection order) and workgroup 0 writes them out.
-__device__ void route_phase(const LayerArgs &a, double *dred, double *lg_lds, float *gate_lds, int *cnt_lds) {
+// Routing inside the launch (rvq_moe_route_forward).  [FR] "Lecture anticipée
+// et prédiction du routeur": the router decides the token's experts; reading
+// as in the separate route kernels: top-k of fp64 logits, ties to the lower
+// id, softmax over the k.  No grid barrier and no counter:
+//  R1  logits of experts e = wg, wg + G, ... (all of them in one pass) for every
+//      token: fp64 sums of exact fp32 products, divided by the fp64 RMS
+//      divisor when normalising; each is stored into its slot of buffer `cur`,
+//      which holds the marker NaN until then, and the workgroup's slots of the
+//      other buffer get the marker back for the next call;
+//  R2  every workgroup polls a token's E slots until none holds the marker
+//      (the poll reads the logits themselves), ranks every expert in LDS
+//      (thread i counts the experts ahead of expert i), keeps the first k as
+//      pair ids and selected logits, and forms the gates (one exp each, summed
+//      in slot order).  Workgroup 0 writes ids and gates out.
+// Every workgroup thus holds the ids in LDS: no global read-back of them.
+constexpr int kRouteExp = 4;   // experts per workgroup in one pass (E <= 4 G)
+constexpr int kRankParts = 8;  // slices of the rank count per expert
+__device__ void route_phase(const LayerArgs &a, double *scratch, float *gate_lds, int *pair_ids) {
     const Geometry &g = a.g;
     const int G = gridDim.x, wg = blockIdx.x;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int n4 = g.d / 4;
-    for (int e = wg; e < g.E; e += G) {
-        const float4 *w4 = reinterpret_cast<const float4 *>(a.Wt + (size_t)e * g.d);
-        for (int t = 0; t < a.T; t++) {
-            const float4 *x4 = reinterpret_cast<const float4 *>(a.x + (size_t)t * g.d);
-            double acc = 0.0, ss = 0.0;
+    const double unpub = __longlong_as_double((long long)kUnpublished);
+    double *lg = scratch;                 // [E] logits of the token being ranked
+    double *sel = scratch + kMaxExperts;  // [P] selected logits by rank
+    double *ex = sel + kRouteMaxPairs;    // [P] exps
+    double *red = ex + kRouteMaxPairs;    // [kWaves][kRouteExp + 1]
+    int *rank_cnt = reinterpret_cast<int *>(red + kWaves * (kRouteExp + 1));  // [E]
+    for (int t = 0; t < a.T; t++) {
+        const float4 *x4 = reinterpret_cast<const float4 *>(a.x + (size_t)t * g.d);
+        for (int e0 = wg; e0 < g.E; e0 += G * kRouteExp) {
+            double acc[kRouteExp], ss = 0.0;
+#pragma unroll
+            for (int j = 0; j < kRouteExp; j++) acc[j] = 0.0;
             for (int i = threadIdx.x; i < n4; i += kBlock) {
-                const float4 wv = w4[i], xv = x4[i];
-                acc = fma((double)xv.x, (double)wv.x, acc);
-                acc = fma((double)xv.y, (double)wv.y, acc);
-                acc = fma((double)xv.z, (double)wv.z, acc);
-                acc = fma((double)xv.w, (double)wv.w, acc);
+                // loads for all experts are unconditional (a clamped expert index,
+                // dropped at use), so they are in flight together
+                const float4 xv = x4[i];
+                float4 wv[kRouteExp];
+#pragma unroll
+                for (int j = 0; j < kRouteExp; j++)
+                    wv[j] = reinterpret_cast<const float4 *>(a.Wt + (size_t)min(e0 + j * G, g.E - 1) * g.d)[i];
                 if (a.pre) {
                     ss = fma((double)xv.x, (double)xv.x, ss);
                     ss = fma((double)xv.y, (double)xv.y, ss);
                     ss = fma((double)xv.z, (double)xv.z, ss);
                     ss = fma((double)xv.w, (double)xv.w, ss);
                 }
-            }
-            const double sa = block_sum(acc, dred);
-            const double sq = a.pre ? block_sum(ss, dred) : 0.0;
-            const double r = a.pre ? sqrt(sq / (double)g.d + a.eps) : 1.0;
-            if (threadIdx.x == 0) store_coherent(a.logits + (size_t)t * g.E + e, sa / r);
-        }
-    }
-    grid_arrive(a.gbar + 1 * (kMaxGridGroups + 1));
-    wait_count(a.gbar + 1 * (kMaxGridGroups + 1) + kMaxGridGroups, grid_groups(), a.err);
-    for (int t = 0; t < a.T; t++) {
-        if (wg >= g.E) break;
-        for (int i = threadIdx.x; i < g.E; i += kBlock) {
-            const double v = load_coherent(a.logits + (size_t)t * g.E + i);
-            lg_lds[i] = isnan(v) ? -INFINITY : v;
-        }
-        __syncthreads();
-        for (int e = wg; e < g.E; e += G) {
-            const double me = lg_lds[e];
-            int c = 0;
-            for (int i = threadIdx.x; i < g.E; i += kBlock) {
-                const double v = lg_lds[i];
-                c += (v > me || (v == me && i < e)) ? 1 : 0;
+#pragma unroll
+                for (int j = 0; j < kRouteExp; j++) {
+                    acc[j] = fma((double)xv.x, (double)wv[j].x, acc[j]);
+                    acc[j] = fma((double)xv.y, (double)wv[j].y, acc[j]);
+                    acc[j] = fma((double)xv.z, (double)wv[j].z, acc[j]);
+                    acc[j] = fma((double)xv.w, (double)wv[j].w, acc[j]);
+                }
             }
 #pragma unroll
-            for (int o = 32; o > 0; o >>= 1) c += __shfl_xor(c, o);
-            if ((threadIdx.x & 63) == 0) cnt_lds[threadIdx.x >> 6] = c;
+            for (int o = 32; o > 0; o >>= 1) {
+                ss += __shfl_xor(ss, o);
+#pragma unroll
+                for (int j = 0; j < kRouteExp; j++) acc[j] += __shfl_xor(acc[j], o);
+            }
+            if (lane == 0) {
+#pragma unroll
+                for (int j = 0; j < kRouteExp; j++) red[wave * (kRouteExp + 1) + j] = acc[j];
+                red[wave * (kRouteExp + 1) + kRouteExp] = ss;
+            }
             __syncthreads();
-            if (threadIdx.x == 0) {
-                int rank = 0;
-                for (int w = 0; w < kWaves; w++) rank += cnt_lds[w];
-                if (rank < g.k) {
-                    store_counter(const_cast<int32_t *>(a.ids) + (size_t)t * g.k + rank, e);
-                    store_coherent(a.sel + (size_t)t * g.k + rank, me);
+            if (threadIdx.x < kRouteExp) {
+                const int j = threadIdx.x, e = e0 + j * G;
+                double sa = 0.0, sq = 0.0;
+                for (int w = 0; w < kWaves; w++) {
+                    sa += red[w * (kRouteExp + 1) + j];
+                    sq += red[w * (kRouteExp + 1) + kRouteExp];
+                }
+                const double r = a.pre ? sqrt(sq / (double)g.d + a.eps) : 1.0;
+                if (e < g.E) {
+                    store_coherent(a.rl_cur + (size_t)t * g.E + e, sa / r);
+                    store_coherent(a.rl_next + (size_t)t * g.E + e, unpub);
                 }
             }
             __syncthreads();
         }
     }
-    grid_arrive(a.gbar + 2 * (kMaxGridGroups + 1));
-    wait_count(a.gbar + 2 * (kMaxGridGroups + 1) + kMaxGridGroups, grid_groups(), a.err);
-    // gates: stage the T * k selected logits in LDS (one coherent load each, all
-    // in flight together), then thread i = (t, j) forms its softmax in fp64
+    const uint64_t t_start = wall_clock64();
+    for (int t = 0; t < a.T; t++) {
+        while (true) {
+            int ready = 1;
+            for (int i = threadIdx.x; i < g.E; i += kBlock) {
+                const double v = load_coherent(a.rl_cur + (size_t)t * g.E + i);
+                ready &= (uint64_t)__double_as_longlong(v) != kUnpublished;
+                lg[i] = isnan(v) ? -INFINITY : v;
+            }
+            if (__syncthreads_and(ready)) break;
+            if (wall_clock64() - t_start > 50000000ull) {  // 0.5 s at the 100 MHz constant clock
+                if (threadIdx.x == 0) atomicOr(a.err, 2);
+                break;
+            }
+            __builtin_amdgcn_s_sleep(1);
+        }
+        // rank of expert i = the experts ahead of it, counted in kRankParts
+        // slices by different threads and summed with LDS atomics
+        for (int i = threadIdx.x; i < g.E; i += kBlock) rank_cnt[i] = 0;
+        __syncthreads();
+        for (int w = threadIdx.x; w < g.E * kRankParts; w += kBlock) {
+            const int i = w / kRankParts, part = w % kRankParts;
+            const double me = lg[i];
+            int c = 0;
+            for (int j = g.E * part / kRankParts; j < g.E * (part + 1) / kRankParts; j++) {
+                const double o = lg[j];
+                c += (o > me || (o == me && j < i)) ? 1 : 0;
+            }
+            if (c) atomicAdd(&rank_cnt[i], c);
+        }
+        __syncthreads();
+        for (int i = threadIdx.x; i < g.E; i += kBlock) {
+            const int rank = rank_cnt[i];
+            if (rank < g.k) {
+                pair_ids[t * g.k + rank] = i;
+                sel[t * g.k + rank] = lg[i];
+            }
+        }
+        __syncthreads();
+    }
     const int P = a.T * g.k;
-    for (int i = threadIdx.x; i < P; i += kBlock) lg_lds[i] = load_coherent(a.sel + i);
-    __syncthreads();
-    // one exp per selected logit, then each gate sums its token's k in slot order
-    double *ex = lg_lds + kRouteMaxPairs;
-    for (int i = threadIdx.x; i < P; i += kBlock) ex[i] = exp(lg_lds[i] - lg_lds[(i / g.k) * g.k]);
+    for (int i = threadIdx.x; i < P; i += kBlock) ex[i] = exp(sel[i] - sel[(i / g.k) * g.k]);
     __syncthreads();
     for (int i = threadIdx.x; i < P; i += kBlock) {
         const int t = i / g.k;
@@ -796,22 +835,23 @@ __device__ void route_phase(const LayerArgs &a, double *dred, double *lg_lds, fl
         for (int j = 0; j < g.k; j++) sum += ex[t * g.k + j];
         const float gt = (float)(ex[i] / sum);
         gate_lds[i] = gt;
-        if (wg == 0) const_cast<float *>(a.gates)[i] = gt;
+        if (wg == 0) {
+            const_cast<float *>(a.gates)[i] = gt;
+            const_cast<int32_t *>(a.ids)[i] = pair_ids[i];
+        }
     }
     __syncthreads();
 }
 
-// kNT: codes are read with streaming loads.  Off for a batch in expert-grouped
-// order, whose re-reads of a tile by the next token of a group should hit the
-// caches.
 template <int CB, bool kRoute, bool kNT>
 __global__ __launch_bounds__(kBlock) void k_layer(LayerArgs a) {
     __shared__ __align__(16) float lut[kLutWords];  // also 8-byte staging (logits, order masks)
     __shared__ float vs[kVec][kTileSlices];  // [element][slice]
     __shared__ double red[kWaves];
-    static_assert(kMaxExperts * sizeof(double) <= kLutWords * sizeof(float) &&
-                      2 * kRouteMaxPairs * sizeof(double) <= kLutWords * sizeof(float),
-                  "logit staging must fit the table area");
+    static_assert((kMaxExperts + 2 * kRouteMaxPairs + kWaves * (kRouteExp + 1)) * sizeof(double) +
+                          kMaxExperts * sizeof(int) <=
+                      kLutWords * sizeof(float),
+                  "routing scratch must fit the table area");
     __shared__ float hred[4][256][2];
     __shared__ float red2[kWaves];
     const Geometry &g = a.g;
@@ -829,10 +869,11 @@ __global__ __launch_bounds__(kBlock) void k_layer(LayerArgs a) {
     double r_val = 1.0;
     CbRegs<CB> cb;
     __shared__ float gate_lds[kRouteMaxPairs];
+    __shared__ int pair_ids[kRouteMaxPairs];
     const float *gate_src = a.gates;
     if (kRoute) {
-        // the logits staging and counts reuse the table area, which is idle until phase A
-        route_phase(a, red, reinterpret_cast<double *>(lut), gate_lds, reinterpret_cast<int *>(hred));
+        // the routing scratch reuses the table area, which is idle until phase A
+        route_phase(a, reinterpret_cast<double *>(lut), gate_lds, pair_ids);
         gate_src = gate_lds;
     }
     // ---------------- pair order (the token x expert permutation)
@@ -846,11 +887,13 @@ __global__ __launch_bounds__(kBlock) void k_layer(LayerArgs a) {
     ord.expert = o_expert;
     ord.ids = a.ids;
     ord.lds = id_lds;
+    ord.all = kRoute ? pair_ids : nullptr;
     ord.a_n = ord.b_n = 0;
     ord.a_base = ord.b_base = 0;
     if (ord.tab) {
-        build_order(a.ids, P, g.E, reinterpret_cast<char *>(lut), o_info, o_pair, o_expert);
-    } else {
+        build_order(a.ids, kRoute ? pair_ids : nullptr, P, g.E, reinterpret_cast<char *>(lut), o_info, o_pair,
+                    o_expert);
+    } else if (!kRoute) {
         // pair order: cache the expert ids of the pairs this workgroup's ranges touch
         const int a0 = range_lo(P * 2 * n_ti * n_cf, rw, G), a1 = range_lo(P * 2 * n_ti * n_cf, rw + 1, G);
         const int b0 = range_lo(P * n_tf * n_cd, rw, G), b1 = range_lo(P * n_tf * n_cd, rw + 1, G);
@@ -997,10 +1040,16 @@ static LayerKernel layer_kernel(int cb_dtype, bool route, bool nt) {
                  : (nt ? k_layer<1, false, true> : k_layer<1, false, false>);
 }
 
-hipError_t launch_layer(const Geometry &g, const Workspace &w, const uint8_t *codes, const uint8_t *const *slot_tab,
+hipError_t launch_layer(const Geometry &g, Workspace &w, const uint8_t *codes, const uint8_t *const *slot_tab,
                         const void *cbs, const float *Wt, const float *x, const int32_t *ids, const float *gates,
                         float *y, int T, int pre, int residual, double eps, bool route, hipStream_t s) {
-    LayerArgs a{Wt, w.logits, w.sel, w.gbar, codes, slot_tab, cbs, x, ids, gates, y, w.part_gu, w.cntA, w.err, g, T, pre,
+    double *rl_cur = nullptr, *rl_next = nullptr;
+    if (route) {  // the two slot buffers, [2][max_tokens][E], alternate between calls
+        rl_cur = w.fused_logits + (w.fused_parity ? w.route_cap : 0);
+        rl_next = w.fused_logits + (w.fused_parity ? 0 : w.route_cap);
+        w.fused_parity ^= 1;
+    }
+    LayerArgs a{Wt, w.logits, w.sel, w.gbar, rl_cur, rl_next, codes, slot_tab, cbs, x, ids, gates, y, w.part_gu, w.cntA, w.err, g, T, pre,
                 residual, eps};
     // A plain launch of exactly as many workgroups as can be resident at once
     // (sized at open from the occupancy query); the inter-workgroup waits are

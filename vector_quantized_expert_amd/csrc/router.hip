@@ -274,11 +274,6 @@ __device__ void select_topk(const uint64_t (&key)[kSelPer], const double (&v)[kS
     __syncthreads();
 }
 
-// Logit slots hold this NaN until written.  It is a signalling NaN, which no
-// arithmetic result is (results are quiet NaNs at most), so a slot holds it
-// exactly while its logit is not yet published.
-constexpr uint64_t kUnpublished = 0x7FF4DEAD7FF4DEADull;
-constexpr uint32_t kUnpublishedHalf = 0x7FF4DEADu;
 
 // Router dot products of expert e (= blockIdx.x) for tokens [t0, t0 + nt):
 // 256 threads; the 4 waves each take a quarter of the expert's column (float4
@@ -528,6 +523,10 @@ hipError_t init_route(Workspace &w, int E, int64_t max_tokens, int n_cu, hipStre
     const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_route_one, 256, 0);
     if (e != hipSuccess) return e;
     w.route_one = (int64_t)per_cu * n_cu >= E;
+    w.fused_parity = 0;
+    const hipError_t e2 = hipMemsetD32Async(reinterpret_cast<hipDeviceptr_t>(w.fused_logits), kUnpublishedHalf,
+                                            (size_t)(2 * 2 * max_tokens * E), s);
+    if (e2 != hipSuccess) return e2;
     return hipMemsetD32Async(reinterpret_cast<hipDeviceptr_t>(w.route_logits), kUnpublishedHalf,
                              (size_t)(2 * route_logit_slots(max_tokens, E)), s);
 }
