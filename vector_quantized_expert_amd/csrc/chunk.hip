@@ -229,10 +229,11 @@ __device__ inline bf16x8 ck_tokens(const __bf16 *xs, int mt, int kk, int lane) {
 
 // Stage this wave's 3 KB code block in LDS (lane l: 3 x 16 bytes), or zeros.
 __device__ inline void ck_stage_codes(uint8_t *dst, const uint8_t *blk, bool valid, int lane) {
-    uint4 *d4 = reinterpret_cast<uint4 *>(dst);
-    const uint4 *s4 = reinterpret_cast<const uint4 *>(blk);
+    typedef unsigned int w4 __attribute__((ext_vector_type(4)));
+    w4 *d4 = reinterpret_cast<w4 *>(dst);
+    const auto *s4 = global_view(reinterpret_cast<const w4 *>(blk));
 #pragma unroll
-    for (int s = 0; s < 3; s++) d4[s * 64 + lane] = valid ? s4[s * 64 + lane] : make_uint4(0, 0, 0, 0);
+    for (int s = 0; s < 3; s++) d4[s * 64 + lane] = valid ? s4[s * 64 + lane] : w4{0u, 0u, 0u, 0u};
 }
 
 struct ChunkArgs {

@@ -80,6 +80,17 @@ __device__ inline void store_counter(int *p, int v) {
 // Wait until this wave's vector memory operations (including sc1 stores) completed.
 __device__ inline void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// Global-memory (address space 1) view of a device pointer.  Loads through a
+// generic pointer that the compiler cannot place (one read from a table, such
+// as a slot-cache record pointer) become flat loads, which count against the
+// LDS wait counter too: every wait for an LDS result would then also wait for
+// the code loads in flight.  Through this view they are global loads, waited
+// for by the vector-memory counter only.
+template <typename T>
+__device__ __forceinline__ const __attribute__((address_space(1))) T *global_view(const T *p) {
+    return (const __attribute__((address_space(1))) T *)p;
+}
+
 // Logit slots hold this NaN until written.  It is a signalling NaN, which no
 // arithmetic result is (results are quiet NaNs at most), so a slot holds it
 // exactly while its logit is not yet published.

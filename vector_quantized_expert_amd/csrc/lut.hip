@@ -297,7 +297,7 @@ __device__ __forceinline__ float sum_chunk(const float *lut, const u32x4 &q0, co
 // re-reads; otherwise ordinary loads, so that the next token of an expert group
 // finds the tile in L2 or the Infinity Cache.
 __device__ __forceinline__ void load_chunk(const uint8_t *blk, int lane, u32x4 &q0, u32x4 &q1, u32x4 &q2, bool nt) {
-    const u32x4 *p = reinterpret_cast<const u32x4 *>(blk) + lane;
+    const auto *p = global_view(reinterpret_cast<const u32x4 *>(blk)) + lane;
     if (nt) {  // uniform branch
         q0 = __builtin_nontemporal_load(p);
         q1 = __builtin_nontemporal_load(p + 64);
