@@ -106,6 +106,10 @@ hipError_t launch_repack(const Geometry &g, const uint8_t *canon, uint8_t *inter
     return hipGetLastError();
 }
 
+// The wave's index in the workgroup as a wave-uniform value (scalar register),
+// so that loops and branches on it are scalar.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+
 // ---------------------------------------------------------------------------
 // LDS helpers
 __device__ inline float lds_at(const float *lut, uint32_t byte_addr) {
@@ -177,7 +181,7 @@ template <int CB>
 __device__ inline void build_lut(float *lut, const float (*vs)[kTileSlices], int e2) {
     constexpr int kEntryBytes = CB == 0 ? 32 : 16;
     constexpr int kPerRow = 128 / kEntryBytes;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, wave = wave_id();
     const int j = lane & 31, kh = lane >> 5;
     const float down = ldexpf(1.f, -e2), up = ldexpf(1.f, e2);
     half8 bop;
@@ -221,12 +225,7 @@ __device__ inline void build_lut(float *lut, const float (*vs)[kTileSlices], int
 // (threads 0..255) each publish their maximum with tile_max_publish() before
 // the barrier that follows the vs stores; tile_exponent() reads the four
 // maxima after it, so the exponent costs no barrier of its own.
-__device__ __forceinline__ void tile_max_publish(float v, float *red2) {
-    float m = fabsf(v);
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
-    if ((threadIdx.x & 63) == 0) red2[threadIdx.x >> 6] = m;
-}
+__device__ __forceinline__ void tile_max_publish(float v, float *red2);
 
 __device__ __forceinline__ int tile_exponent(const float *red2) {
     const float m = fmaxf(fmaxf(red2[0], red2[1]), fmaxf(red2[2], red2[3]));
@@ -242,6 +241,22 @@ __device__ __forceinline__ int tile_exponent(const float *red2) {
 constexpr int kRor4 = 0x124, kRor8 = 0x128, kRor12 = 0x12C;
 constexpr int kQuadXor2 = 0x4E;  // quad_perm [2,3,0,1]
 constexpr int kQuadXor1 = 0xB1;  // quad_perm [1,0,3,2]
+
+// Maximum of |v| over the wave: quad and row rotations give every lane its
+// 16-lane row's maximum, then the four rows are read as scalars.
+__device__ __forceinline__ void tile_max_publish(float v, float *red2) {
+    float m = fabsf(v);
+    m = fmaxf(m, RVQ_DPP(m, kQuadXor1));
+    m = fmaxf(m, RVQ_DPP(m, kQuadXor2));
+    m = fmaxf(m, RVQ_DPP(m, kRor4));
+    m = fmaxf(m, RVQ_DPP(m, kRor8));
+    const int mi = __float_as_int(m);
+    const float r = fmaxf(fmaxf(__int_as_float(__builtin_amdgcn_readlane(mi, 0)),
+                                __int_as_float(__builtin_amdgcn_readlane(mi, 16))),
+                          fmaxf(__int_as_float(__builtin_amdgcn_readlane(mi, 32)),
+                                __int_as_float(__builtin_amdgcn_readlane(mi, 48))));
+    if ((threadIdx.x & 63) == 0) red2[threadIdx.x >> 6] = r;
+}
 
 // Sum 16 row values over the 32 slice lanes of each half-wave.  On return the
 // lane pair (2r, 2r+1) of a half holds the total of that half's row r.
@@ -278,18 +293,35 @@ __device__ __forceinline__ float reduce16(float (&v)[16], int l) {
 }
 
 // Sum one 32-row chunk whose stage words are q0, q1, q2 (this lane's 16 rows).
+// The 48 table reads go out in batches of 12 (4 rows), each batch issued
+// before the previous one is summed, so a wave waits for LDS a few times per
+// chunk instead of once or twice per row (scheduling groups: mask 2 = VALU,
+// 0x100 = LDS read).
 __device__ __forceinline__ float sum_chunk(const float *lut, const u32x4 &q0, const u32x4 &q1, const u32x4 &q2, int l) {
     const uint32_t lb0 = 4u * l, lb1 = 128u + 4u * l, lb2 = 0x10000u + 4u * l;
-    float v[16];
+    float t[48];
 #pragma unroll
     for (int i = 0; i < 16; i++) {
         const uint32_t sel = 0x0C060004u | ((uint32_t)(i & 3) << 8);
         const int w = i >> 2;
-        const uint32_t a0 = __builtin_amdgcn_perm(lb0, q0[w], sel);
-        const uint32_t a1 = __builtin_amdgcn_perm(lb1, q1[w], sel);
-        const uint32_t a2 = __builtin_amdgcn_perm(lb2, q2[w], sel);
-        v[i] = lds_at(lut, a0) + lds_at(lut, a1) + lds_at(lut, a2);
+        t[3 * i] = lds_at(lut, __builtin_amdgcn_perm(lb0, q0[w], sel));
+        t[3 * i + 1] = lds_at(lut, __builtin_amdgcn_perm(lb1, q1[w], sel));
+        t[3 * i + 2] = lds_at(lut, __builtin_amdgcn_perm(lb2, q2[w], sel));
     }
+    float v[16];
+#pragma unroll
+    for (int i = 0; i < 16; i++) v[i] = t[3 * i] + t[3 * i + 1] + t[3 * i + 2];
+    __builtin_amdgcn_sched_group_barrier(0x002, 12, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, 12, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, 12, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, 12, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);
     return reduce16(v, l);
 }
 
@@ -319,45 +351,34 @@ constexpr int kStagePieces = 256;  // chunks per sub-range (one piece per stage-
 __device__ __forceinline__ float *stage_piece(float *lut, int i) { return lut + kStage2Word + i * 64 + kCbHalfWord; }
 
 // Gather chunks [c0, c1) (c1 - c0 <= kStagePieces) of one tile, waves
-// round-robin.  The first chunk of this wave was already loaded into
-// (p0, p1, p2) by the caller.  Two register sets alternate (no copies between
-// them), and a scheduling barrier keeps each prefetch ahead of any use of the
-// chunk being summed, so the wait before summing one chunk leaves the next
-// chunk's three loads in flight (vmcnt completes in order).
-__device__ __forceinline__ void gather_range(float *lut, const uint8_t *tile_base, int c0, int c1, u32x4 p0,
-                                             u32x4 p1, u32x4 p2, bool nt) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, l = lane & 31;
+// round-robin.  The first chunk of this wave was already loaded into s0 by the
+// caller.  Two register sets alternate (no copies between them): the next
+// chunk's loads are issued before the current chunk is summed.  The loads are
+// unconditional -- past this wave's last chunk they re-read that chunk (a cache
+// hit) -- so every wait is a fixed count of the in-order vector-memory counter.
+// A scheduling barrier keeps each load ahead of the sum that follows it.
+__device__ __forceinline__ void gather_range(float *lut, const uint8_t *tile_base, int c0, int c1, const u32x4 (&s0)[3],
+                                             bool nt) {
+    const int lane = threadIdx.x & 63, wave = wave_id(), l = lane & 31;
     const int row_in = (lane >> 5) * 16 + (l >> 1);
     int q = c0 + wave;
     if (q >= c1) return;
-    u32x4 n0, n1, n2;
+    const int last = c1 - 1 - (c1 - 1 - q) % kWaves;  // this wave's last chunk
+    auto at = [&](int qq) { return tile_base + (int64_t)min(qq, last) * kChunkBytes; };
+    auto emit = [&](int qq, const u32x4 (&r)[3]) {
+        const float sum = sum_chunk(lut, r[0], r[1], r[2], l);
+        if (!(lane & 1)) stage_piece(lut, qq - c0)[row_in] = sum;
+    };
+    u32x4 a[3] = {s0[0], s0[1], s0[2]}, b[3];
     while (true) {
-        int qn = q + kWaves;
-        if (qn >= c1) {
-            const float sum = sum_chunk(lut, p0, p1, p2, l);
-            if (!(lane & 1)) stage_piece(lut, q - c0)[row_in] = sum;
-            return;
-        }
-        load_chunk(tile_base + (int64_t)qn * kChunkBytes, lane, n0, n1, n2, nt);
-        __builtin_amdgcn_sched_barrier(0);  // issue the prefetch before any use of the current chunk
-        {
-            const float sum = sum_chunk(lut, p0, p1, p2, l);
-            if (!(lane & 1)) stage_piece(lut, q - c0)[row_in] = sum;
-        }
-        q = qn;
-        qn = q + kWaves;
-        if (qn >= c1) {
-            const float sum = sum_chunk(lut, n0, n1, n2, l);
-            if (!(lane & 1)) stage_piece(lut, q - c0)[row_in] = sum;
-            return;
-        }
-        load_chunk(tile_base + (int64_t)qn * kChunkBytes, lane, p0, p1, p2, nt);
+        load_chunk(at(q + kWaves), lane, b[0], b[1], b[2], nt);
         __builtin_amdgcn_sched_barrier(0);
-        {
-            const float sum = sum_chunk(lut, n0, n1, n2, l);
-            if (!(lane & 1)) stage_piece(lut, q - c0)[row_in] = sum;
-        }
-        q = qn;
+        emit(q, a);
+        if ((q += kWaves) > last) return;
+        load_chunk(at(q + kWaves), lane, a[0], a[1], a[2], nt);
+        __builtin_amdgcn_sched_barrier(0);
+        emit(q, b);
+        if ((q += kWaves) > last) return;
     }
 }
 
@@ -380,16 +401,16 @@ __device__ __forceinline__ void flush_rows_add(float *lut, float *out, int c0, i
 }
 
 // Whole segment: gather [c0, c1) in sub-ranges of at most kStagePieces chunks,
-// flushing each.  (p0, p1, p2) hold this wave's first chunk of the segment.
+// flushing each.  p holds this wave's first chunk of the segment.
 template <bool kAdd>
 __device__ __forceinline__ void gather_segment(float *lut, const uint8_t *tile_base, int c0, int c1, float *out,
-                                               int n_rows, u32x4 p0, u32x4 p1, u32x4 p2, bool nt) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+                                               int n_rows, u32x4 (&p)[3], bool nt) {
+    const int lane = threadIdx.x & 63, wave = wave_id();
     for (int s0 = c0; s0 < c1; s0 += kStagePieces) {
         const int s1 = min(c1, s0 + kStagePieces);
         if (s0 != c0 && s0 + wave < s1)
-            load_chunk(tile_base + (int64_t)(s0 + wave) * kChunkBytes, lane, p0, p1, p2, nt);
-        gather_range(lut, tile_base, s0, s1, p0, p1, p2, nt);
+            load_chunk(tile_base + (int64_t)(s0 + wave) * kChunkBytes, lane, p[0], p[1], p[2], nt);
+        gather_range(lut, tile_base, s0, s1, p, nt);
         __syncthreads();
         if (kAdd)
             flush_rows_add(lut, out, s0, s1, n_rows);
@@ -400,13 +421,10 @@ __device__ __forceinline__ void gather_segment(float *lut, const uint8_t *tile_b
 }
 
 // ---------------------------------------------------------------------------
-// Inter-workgroup ordering (all workgroups are resident together).
-__device__ inline void signal_add(int *cnt, int n) {
-    wait_stores();  // this wave's coherent partial-sum stores are complete
-    __syncthreads();
-    if (threadIdx.x == 0) atomicAdd(cnt, n);
-}
-
+// Inter-workgroup ordering (all workgroups are resident together).  A producer
+// waits for its stores to complete (vmcnt 0), then a barrier, then one thread
+// adds to a counter; consumers wait on the counter.
+//
 // Wait until *cnt >= target (bounded: after ~0.5 s the error flag gets bit 2 and
 // the wait gives up, so every wave always reaches the end of the kernel).
 // Consumers read the published data with coherent loads after the barrier.
@@ -543,13 +561,14 @@ __device__ inline void finish_h(const LayerArgs &a, const float *gate_src, int p
     }
 }
 
-// A phase-A segment: chunks [c0, c1) of one (pair, matrix, tile); e = expert id.
+// A phase-A segment: chunks [c0, c1) of one (pair, matrix, tile); e = expert id;
+// (gs, gn, j): its group's first position and size, and its position in it.
 struct SegA {
-    int p, m, tile, c0, c1, e;
+    int p, m, tile, c0, c1, e, gs, gn, j;
 };
 // A phase-B segment: chunks [c0, c1) of one (pair, ffn tile).
 struct SegB {
-    int p, ft, c0, c1, e;
+    int p, ft, c0, c1, e, gs, gn, j;
 };
 
 // Order of the (token, expert) pairs inside a call (the token x expert
@@ -681,8 +700,33 @@ __device__ inline SegA seg_a(int u, int u1, int n_ti, int n_cf, const Order &o) 
     s.tile = w % n_ti;
     s.m = w / n_ti;
     s.c1 = min(n_cf, s.c0 + (u1 - u));
+    s.gs = gs;
+    s.gn = gn;
+    s.j = j;
     s.p = o.pair_at(gs + j);
     s.e = o.expert_a(gs + j);
+    return s;
+}
+
+// The segment after c, which ended at its tile's last chunk, starting at unit un
+// (< u1): the same decomposition as seg_a, stepped (chunk, then position in
+// the group, then tile, then matrix, then group) without divisions.
+__device__ inline SegA next_a(const SegA &c, int un, int u1, int n_ti, int n_cf, const Order &o) {
+    SegA s = c;
+    s.c0 = 0;
+    s.c1 = min(n_cf, u1 - un);
+    if (++s.j == s.gn) {
+        s.j = 0;
+        if (++s.tile == n_ti) {
+            s.tile = 0;
+            if (++s.m == 2) {
+                s.m = 0;
+                o.group(c.gs + c.gn, s.gs, s.gn);
+            }
+        }
+    }
+    s.p = o.pair_at(s.gs + s.j);
+    s.e = o.expert_a(s.gs + s.j);
     return s;
 }
 
@@ -697,8 +741,29 @@ __device__ inline SegB seg_b(int u, int u1, int n_tf, int n_cd, const Order &o) 
     const int j = w % gn;
     s.ft = w / gn;
     s.c1 = min(n_cd, s.c0 + (u1 - u));
+    s.gs = gs;
+    s.gn = gn;
+    s.j = j;
     s.p = o.pair_at(gs + j);
     s.e = o.expert_b(gs + j);
+    return s;
+}
+
+// The phase-B segment after c (which ended at its tile's last chunk): chunk,
+// then position in the group, then ffn tile, then group.
+__device__ inline SegB next_b(const SegB &c, int un, int u1, int n_tf, int n_cd, const Order &o) {
+    SegB s = c;
+    s.c0 = 0;
+    s.c1 = min(n_cd, u1 - un);
+    if (++s.j == s.gn) {
+        s.j = 0;
+        if (++s.ft == n_tf) {
+            s.ft = 0;
+            o.group(c.gs + c.gn, s.gs, s.gn);
+        }
+    }
+    s.p = o.pair_at(s.gs + s.j);
+    s.e = o.expert_b(s.gs + s.j);
     return s;
 }
 
@@ -722,7 +787,7 @@ constexpr int kRankParts = 8;  // slices of the rank count per expert
 __device__ void route_phase(const LayerArgs &a, double *scratch, float *gate_lds, int *pair_ids) {
     const Geometry &g = a.g;
     const int G = gridDim.x, wg = blockIdx.x;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, wave = wave_id();
     const int n4 = g.d / 4;
     const double unpub = __longlong_as_double((long long)kUnpublished);
     double *lg = scratch;                 // [E] logits of the token being ranked
@@ -861,7 +926,7 @@ __global__ __launch_bounds__(kBlock) void k_layer(LayerArgs a) {
     // neighbouring ranges, or re-read by the next token of its group, stays in
     // one XCD's L2
     const int rw = (G % 8 == 0) ? (wg % 8) * (G / 8) + wg / 8 : wg;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, wave = wave_id();
     const int P = a.T * g.k;
     const int n_ti = g.m[0].n_tiles, n_cf = g.m[0].n_chunks;
     const int n_tf = g.m[2].n_tiles, n_cd = g.m[2].n_chunks;
@@ -911,9 +976,18 @@ __global__ __launch_bounds__(kBlock) void k_layer(LayerArgs a) {
         const int64_t n = (int64_t)a.T * g.d;
         for (int64_t i = n * wg / G + threadIdx.x; i < n * (wg + 1) / G; i += kBlock)
             store_coherent(a.y + i, a.residual ? a.x[i] : 0.f);
-        signal_add(a.gbar + kMaxGridGroups, 1);  // flat, non-returning: nobody waits on it here
     }
     bool y_ready = false;
+    bool y_signalled = false;  // this workgroup's y stores are published with its first phase-A count
+    auto signal = [&](int *cnt, int n) {  // publish this workgroup's completed stores
+        wait_stores();
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            atomicAdd(cnt, n);
+            if (!y_signalled) atomicAdd(a.gbar + kMaxGridGroups, 1);
+        }
+        y_signalled = true;
+    };
 
     // ---------------- phase A: gate and up
     {
@@ -934,7 +1008,7 @@ __global__ __launch_bounds__(kBlock) void k_layer(LayerArgs a) {
         while (u < u1) {
             const int un = u + (cur.c1 - cur.c0);
             SegA nxt{};
-            if (un < u1) nxt = seg_a(un, u1, n_ti, n_cf, ord);
+            if (un < u1) nxt = next_a(cur, un, u1, n_ti, n_cf, ord);
             if (cur.e >= 0 && cur.e < g.E) {
                 const uint8_t *base = expert_record(a, cur.e) + g.m[cur.m].off +
                                       (int64_t)cur.tile * n_cf * kChunkBytes;
@@ -947,24 +1021,25 @@ __global__ __launch_bounds__(kBlock) void k_layer(LayerArgs a) {
                     vs[threadIdx.x % kVec][threadIdx.x / kVec] = v;
                     tile_max_publish(v, red2);
                 }
-                u32x4 p0, p1, p2;
+                u32x4 p[3];
                 if (cur.c0 + wave < cur.c1)
-                    load_chunk(base + (int64_t)(cur.c0 + wave) * kChunkBytes, lane, p0, p1, p2, kNT);
+                    load_chunk(base + (int64_t)(cur.c0 + wave) * kChunkBytes, lane, p[0], p[1], p[2], kNT);
                 __syncthreads();
                 build_lut<CB>(lut, vs, tile_exponent(red2));
                 __syncthreads();
                 if (un < u1) prefetch(nxt);
                 float *out = a.part_gu + (((int64_t)cur.p * 2 + cur.m) * n_ti + cur.tile) * g.ffn_pad;
-                gather_segment<false>(lut, base, cur.c0, cur.c1, out, 0, p0, p1, p2, kNT);
+                gather_segment<false>(lut, base, cur.c0, cur.c1, out, 0, p, kNT);
             } else {
                 if (threadIdx.x == 0) atomicOr(a.err, 1);
                 if (un < u1) prefetch(nxt);
             }
-            signal_add(&a.cntA[cur.p], cur.c1 - cur.c0);
+            signal(&a.cntA[cur.p], cur.c1 - cur.c0);
             cur = nxt;
             u = un;
         }
     }
+    if (!y_signalled) signal(a.gbar + kMaxGridGroups, 0);  // no phase-A work: a zero count, then the y count
 
     // ---------------- phase B: SwiGLU finish, gate, down
     {
@@ -980,14 +1055,14 @@ __global__ __launch_bounds__(kBlock) void k_layer(LayerArgs a) {
         while (u < u1) {
             const int un = u + (cur.c1 - cur.c0);
             SegB nxt{};
-            if (un < u1) nxt = seg_b(un, u1, n_tf, n_cd, ord);
+            if (un < u1) nxt = next_b(cur, un, u1, n_tf, n_cd, ord);
             if (cur.e >= 0 && cur.e < g.E) {
                 const uint8_t *base = expert_record(a, cur.e) + g.m[2].off +
                                       (int64_t)cur.ft * n_cd * kChunkBytes;
                 cb_store<CB>(lut, cb);
-                u32x4 p0, p1, p2;
+                u32x4 p[3];
                 if (cur.c0 + wave < cur.c1)
-                    load_chunk(base + (int64_t)(cur.c0 + wave) * kChunkBytes, lane, p0, p1, p2, kNT);
+                    load_chunk(base + (int64_t)(cur.c0 + wave) * kChunkBytes, lane, p[0], p[1], p[2], kNT);
                 wait_count(&a.cntA[cur.p], needA, a.err);
                 finish_h(a, gate_src, cur.p, cur.ft, vs, hred, red2);
                 __syncthreads();
@@ -999,7 +1074,7 @@ __global__ __launch_bounds__(kBlock) void k_layer(LayerArgs a) {
                     y_ready = true;
                 }
                 float *yt = a.y + (size_t)(cur.p / g.k) * g.d;
-                gather_segment<true>(lut, base, cur.c0, cur.c1, yt, g.d, p0, p1, p2, kNT);
+                gather_segment<true>(lut, base, cur.c0, cur.c1, yt, g.d, p, kNT);
             } else {
                 // an invalid id poisons its token's output (the error flag is already set)
                 if (!y_ready) {
@@ -1022,6 +1097,7 @@ __global__ __launch_bounds__(kBlock) void k_layer(LayerArgs a) {
     // spot, and the last one learns it is last in one round trip)
     __shared__ int last;
     int *xb = a.gbar + 3 * (kMaxGridGroups + 1) + kMaxGridGroups;
+    wait_stores();  // this workgroup's counter increments have landed before it counts out
     __syncthreads();
     if (threadIdx.x == 0) last = atomicAdd(xb, 1) == G - 1;
     __syncthreads();
