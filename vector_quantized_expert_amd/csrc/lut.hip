@@ -341,24 +341,31 @@ __device__ __forceinline__ void load_chunk(const uint8_t *blk, int lane, u32x4 &
     }
 }
 
-// Row totals of the chunks being gathered are staged in LDS, in the free
-// halves of the stage-2 rows (the codebook staging area, idle once the table is
-// built): chunk i of a sub-range owns piece i, 32 floats.  Keeping global
+// Row totals of the chunks being gathered are staged in LDS: chunk i of a
+// sub-range owns piece i, 32 floats, at base + i * stride.  Keeping global
 // stores out of the gather loop keeps their completion off its critical path;
-// flush_rows() writes a whole sub-range with coalesced coherent stores.
-constexpr int kStagePieces = 256;  // chunks per sub-range (one piece per stage-2 row)
+// flush_rows() writes a whole sub-range with coalesced coherent stores.  Two
+// areas serve: the free halves of the stage-2 rows (the codebook staging area,
+// idle once the table is built; 256 pieces), and a separate 64-piece area,
+// which lets a segment's flush wait until the next segment's table build
+// (the codebook of that segment is staged meanwhile).
+struct Stage {
+    float *base;
+    int stride, cap;  // floats from one piece to the next; pieces held
+    __device__ float *piece(int i) const { return base + i * stride; }
+};
+constexpr int kStagePieces = 256;
+__device__ __forceinline__ Stage cb_area_stage(float *lut) { return {lut + kStage2Word + kCbHalfWord, 64, kStagePieces}; }
 
-__device__ __forceinline__ float *stage_piece(float *lut, int i) { return lut + kStage2Word + i * 64 + kCbHalfWord; }
-
-// Gather chunks [c0, c1) (c1 - c0 <= kStagePieces) of one tile, waves
+// Gather chunks [c0, c1) (c1 - c0 <= st.cap) of one tile, waves
 // round-robin.  The first chunk of this wave was already loaded into s0 by the
 // caller.  Two register sets alternate (no copies between them): the next
 // chunk's loads are issued before the current chunk is summed.  The loads are
 // unconditional -- past this wave's last chunk they re-read that chunk (a cache
 // hit) -- so every wait is a fixed count of the in-order vector-memory counter.
 // A scheduling barrier keeps each load ahead of the sum that follows it.
-__device__ __forceinline__ void gather_range(float *lut, const uint8_t *tile_base, int c0, int c1, const u32x4 (&s0)[3],
-                                             bool nt) {
+__device__ __forceinline__ void gather_range(float *lut, const Stage &st, const uint8_t *tile_base, int c0, int c1,
+                                             const u32x4 (&s0)[3], bool nt) {
     const int lane = threadIdx.x & 63, wave = wave_id(), l = lane & 31;
     const int row_in = (lane >> 5) * 16 + (l >> 1);
     int q = c0 + wave;
@@ -367,7 +374,7 @@ __device__ __forceinline__ void gather_range(float *lut, const uint8_t *tile_bas
     auto at = [&](int qq) { return tile_base + (int64_t)min(qq, last) * kChunkBytes; };
     auto emit = [&](int qq, const u32x4 (&r)[3]) {
         const float sum = sum_chunk(lut, r[0], r[1], r[2], l);
-        if (!(lane & 1)) stage_piece(lut, qq - c0)[row_in] = sum;
+        if (!(lane & 1)) st.piece(qq - c0)[row_in] = sum;
     };
     u32x4 a[3] = {s0[0], s0[1], s0[2]}, b[3];
     while (true) {
@@ -384,39 +391,43 @@ __device__ __forceinline__ void gather_range(float *lut, const uint8_t *tile_bas
 
 // Write the staged row totals of chunks [c0, c1) to out[c0*32 ..): all threads,
 // after a barrier; coherent stores, completed before the segment is signalled.
-__device__ __forceinline__ void flush_rows(float *lut, float *out, int c0, int c1) {
+__device__ __forceinline__ void flush_rows(const Stage &st, float *out, int c0, int c1) {
     const int n = (c1 - c0) * kChunkRows;
     for (int i = threadIdx.x; i < n; i += kBlock)
-        store_coherent(out + c0 * kChunkRows + i, stage_piece(lut, i / kChunkRows)[i % kChunkRows]);
+        store_coherent(out + c0 * kChunkRows + i, st.piece(i / kChunkRows)[i % kChunkRows]);
 }
 
 // Add the staged row totals of chunks [c0, c1) into out[row] (rows < n_rows)
 // with device-scope fp32 atomics (the hardware global_atomic_add_f32).
-__device__ __forceinline__ void flush_rows_add(float *lut, float *out, int c0, int c1, int n_rows) {
+__device__ __forceinline__ void flush_rows_add(const Stage &st, float *out, int c0, int c1, int n_rows) {
     const int n = (c1 - c0) * kChunkRows;
     for (int i = threadIdx.x; i < n; i += kBlock) {
         const int row = c0 * kChunkRows + i;
-        if (row < n_rows) unsafeAtomicAdd(out + row, stage_piece(lut, i / kChunkRows)[i % kChunkRows]);
+        if (row < n_rows) unsafeAtomicAdd(out + row, st.piece(i / kChunkRows)[i % kChunkRows]);
     }
 }
 
-// Whole segment: gather [c0, c1) in sub-ranges of at most kStagePieces chunks,
-// flushing each.  p holds this wave's first chunk of the segment.
-template <bool kAdd>
-__device__ __forceinline__ void gather_segment(float *lut, const uint8_t *tile_base, int c0, int c1, float *out,
-                                               int n_rows, u32x4 (&p)[3], bool nt) {
+// Whole segment: gather [c0, c1) in sub-ranges of at most st.cap chunks,
+// flushing each -- except, with kDeferLast, the last one, whose first chunk is
+// returned: its totals stay staged for the caller to flush after a barrier.
+// p holds this wave's first chunk of the segment.
+template <bool kAdd, bool kDeferLast>
+__device__ __forceinline__ int gather_segment(float *lut, const Stage &st, const uint8_t *tile_base, int c0, int c1,
+                                              float *out, int n_rows, u32x4 (&p)[3], bool nt) {
     const int lane = threadIdx.x & 63, wave = wave_id();
-    for (int s0 = c0; s0 < c1; s0 += kStagePieces) {
-        const int s1 = min(c1, s0 + kStagePieces);
+    for (int s0 = c0;; s0 += st.cap) {
+        const int s1 = min(c1, s0 + st.cap);
         if (s0 != c0 && s0 + wave < s1)
             load_chunk(tile_base + (int64_t)(s0 + wave) * kChunkBytes, lane, p[0], p[1], p[2], nt);
-        gather_range(lut, tile_base, s0, s1, p, nt);
+        gather_range(lut, st, tile_base, s0, s1, p, nt);
+        if (kDeferLast && s1 == c1) return s0;
         __syncthreads();
         if (kAdd)
-            flush_rows_add(lut, out, s0, s1, n_rows);
+            flush_rows_add(st, out, s0, s1, n_rows);
         else
-            flush_rows(lut, out, s0, s1);
+            flush_rows(st, out, s0, s1);
         __syncthreads();
+        if (s1 == c1) return c1;
     }
 }
 
@@ -1000,6 +1011,12 @@ __global__ __launch_bounds__(kBlock) void k_layer(LayerArgs a) {
             const int col = sg.tile * kTileSlices * kVec + threadIdx.x;
             xv = (threadIdx.x < kTileSlices * kVec && col < g.d) ? a.x[(size_t)(sg.p / g.k) * g.d + col] : 0.f;
         };
+        // row totals of phase A go to their own staging area (the finish area of
+        // phase B, idle here); the last sub-range of a segment is flushed, and the
+        // segment counted, during the next segment's table build
+        const Stage ast{&hred[0][0][0], kChunkRows, (int)(sizeof(hred) / sizeof(float)) / kChunkRows};
+        float *pend_out = nullptr;  // pending flush: out, chunks [pend_c0, pend_c1), count pend_n for pair pend_p
+        int pend_c0 = 0, pend_c1 = 0, pend_p = 0, pend_n = 0;
         SegA cur{};
         if (u < u1) {
             cur = seg_a(u, u1, n_ti, n_cf, ord);
@@ -1025,18 +1042,37 @@ __global__ __launch_bounds__(kBlock) void k_layer(LayerArgs a) {
                 if (cur.c0 + wave < cur.c1)
                     load_chunk(base + (int64_t)(cur.c0 + wave) * kChunkBytes, lane, p[0], p[1], p[2], kNT);
                 __syncthreads();
+                if (pend_out) flush_rows(ast, pend_out, pend_c0, pend_c1);
                 build_lut<CB>(lut, vs, tile_exponent(red2));
-                __syncthreads();
+                if (pend_out)
+                    signal(&a.cntA[pend_p], pend_n);  // its barrier also ends the build
+                else
+                    __syncthreads();
                 if (un < u1) prefetch(nxt);
                 float *out = a.part_gu + (((int64_t)cur.p * 2 + cur.m) * n_ti + cur.tile) * g.ffn_pad;
-                gather_segment<false>(lut, base, cur.c0, cur.c1, out, 0, p, kNT);
+                pend_c0 = gather_segment<false, true>(lut, ast, base, cur.c0, cur.c1, out, 0, p, kNT);
+                pend_c1 = cur.c1;
+                pend_out = out;
+                pend_p = cur.p;
+                pend_n = cur.c1 - cur.c0;
             } else {
                 if (threadIdx.x == 0) atomicOr(a.err, 1);
+                if (pend_out) {
+                    __syncthreads();
+                    flush_rows(ast, pend_out, pend_c0, pend_c1);
+                    signal(&a.cntA[pend_p], pend_n);
+                    pend_out = nullptr;
+                }
+                signal(&a.cntA[cur.p], cur.c1 - cur.c0);
                 if (un < u1) prefetch(nxt);
             }
-            signal(&a.cntA[cur.p], cur.c1 - cur.c0);
             cur = nxt;
             u = un;
+        }
+        if (pend_out) {
+            __syncthreads();
+            flush_rows(ast, pend_out, pend_c0, pend_c1);
+            signal(&a.cntA[pend_p], pend_n);
         }
     }
     if (!y_signalled) signal(a.gbar + kMaxGridGroups, 0);  // no phase-A work: a zero count, then the y count
@@ -1074,7 +1110,7 @@ __global__ __launch_bounds__(kBlock) void k_layer(LayerArgs a) {
                     y_ready = true;
                 }
                 float *yt = a.y + (size_t)(cur.p / g.k) * g.d;
-                gather_segment<true>(lut, base, cur.c0, cur.c1, yt, g.d, p, kNT);
+                gather_segment<true, false>(lut, cb_area_stage(lut), base, cur.c0, cur.c1, yt, g.d, p, kNT);
             } else {
                 // an invalid id poisons its token's output (the error flag is already set)
                 if (!y_ready) {
