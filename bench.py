@@ -18,6 +18,10 @@ Other workloads of the same layer shape:
                routing and a residual add, one token through all L per step;
   --stream-slots S   codes kept in pinned host memory and streamed through S
                HBM expert slots (copies on a side stream, overlapped).
+  --lookahead N  with --layers and --stream-slots: after each layer's call,
+               the next layer's router runs on this layer's input and the
+               first N of its predicted experts are prefetched into the next
+               layer's slots (router lookahead).
 
 Prints one JSON line: tokens/s (value), effective compressed-weight GB/s and
 its fraction of the 8 TB/s HBM peak, the roofline record of the dominant
@@ -92,6 +96,9 @@ def main():
                     help="every layer_forward call takes the chunk path (bf16 matrix cores)")
     ap.add_argument("--stream-slots", type=int, default=0,
                     help="stream the codes from a pinned host bank through this many HBM slots")
+    ap.add_argument("--lookahead", type=int, default=0,
+                    help="with --layers and --stream-slots: after layer l's call, run layer l+1's router on layer "
+                         "l's input and prefetch the first N of its predicted experts (rvq_moe_prefetch)")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="after the run, one plain device-to-device copy of this many bytes (a reference kernel "
                          "of known traffic for scaling hardware byte counters)")
@@ -118,7 +125,9 @@ def main():
     chain = L > 1
     streaming = args.stream_slots > 0
     if (B < 1 or L < 1 or (chain and B != 1) or
-            (args.path == "fused" and (B * shape.top_k > 1024 or args.chunk or streaming))):
+            (args.path == "fused" and (B * shape.top_k > 1024 or args.chunk or streaming)) or
+            (args.lookahead and (not chain or not streaming or args.path == "fused" or
+                                 not 1 <= args.lookahead <= shape.top_k))):
         print(f"--batch {B} / --layers {L} outside what the chosen path takes", file=sys.stderr)
         sys.exit(2)
 
@@ -148,6 +157,11 @@ def main():
     ids = torch.empty((L, n_tok, shape.top_k), dtype=torch.int32, device="cuda")
     gates = torch.empty((L, n_tok, shape.top_k), dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream()
+    if args.lookahead:  # predicted ids of layer l (its router on layer l-1's input), routed on a side stream
+        pred = torch.full((L, n_tok, shape.top_k), -1, dtype=torch.int32, device="cuda")
+        pred_g = torch.empty((n_tok, shape.top_k), dtype=torch.float32, device="cuda")
+        side = torch.cuda.Stream()
+        routed = torch.cuda.Event()
 
     def step(t):
         r = slice(t * B, (t + 1) * B)
@@ -156,7 +170,13 @@ def main():
                 layer.route_forward(h[li, r], B, ids[li, r], gates[li, r], h[li + 1, r], stream)
             else:
                 layer.route_topk(h[li, r], B, ids[li, r], gates[li, r], stream)
+                if args.lookahead and li + 1 < L:
+                    routed.record(stream)  # h[li] is complete
                 layer.layer_forward(h[li, r], B, ids[li, r], gates[li, r], h[li + 1, r], stream)
+                if args.lookahead and li + 1 < L:
+                    side.wait_event(routed)
+                    layers[li + 1].route_topk(h[li, r], B, pred[li + 1, r], pred_g[r], side)
+                    layers[li + 1].prefetch(pred[li + 1, r], B, args.lookahead, side)
 
     h2d = None
     if streaming:
@@ -212,6 +232,15 @@ def main():
         h2d.update({"slots": args.stream_slots, "h2d_bytes": moved, "GBps": moved / (ms * 1e-3) / 1e9,
                     "frac_of_ceiling": moved / (ms * 1e-3) / 1e9 / h2d["ceiling_GBps"],
                     "hit_rate": hits / max(hits + misses, 1)})
+        if args.lookahead:
+            fills = sum(a["prefetch_fills"] - b["prefetch_fills"] for a, b in zip(st, stats0))
+            phits = sum(a["prefetch_hits"] - b["prefetch_hits"] for a, b in zip(st, stats0))
+            ph, ih = pred.cpu().numpy(), ids.cpu().numpy()
+            right = [len(set(ph[l, t, :args.lookahead].tolist()) & set(ih[l, t].tolist()))
+                     for l in range(1, L) for t in range(W, W + K)]
+            h2d.update({"lookahead": args.lookahead, "prefetch_fills": fills, "prefetch_hits": phits,
+                        "prefetch_used_frac": phits / max(fills, 1),
+                        "prediction_precision": float(np.mean(right)) / args.lookahead})
 
     rec = shape.record_bytes
     # Algorithmic bytes of one layer call: every distinct expert the call routes
@@ -262,7 +291,9 @@ def main():
     elif chain:
         workload = (f"K3-scale depth chain, batch-1 decode: {L} layers of d=7168 ffn=2048 E=384 top-16 "
                     f"(3-stage x 256 x 8 fp16 codebooks, uniform u8 codes), RMSNorm (w=1, eps=1e-6) before "
-                    f"routing and a residual add per layer, all resident")
+                    f"routing and a residual add per layer, {where}" +
+                    (f", router lookahead prefetching {args.lookahead} experts of the next layer"
+                     if args.lookahead else ""))
     else:
         workload = (f"K3-scale routed RVQ-MoE layer, batch-{B} decode, {where}: d=7168 ffn=2048 E=384 top-16, "
                     f"3-stage x 256 x 8 fp16 codebooks, uniform u8 codes, T={B} per call")

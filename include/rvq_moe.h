@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define RVQ_MOE_ABI_VERSION 3
+#define RVQ_MOE_ABI_VERSION 4
 
 typedef enum rvq_moe_status {
     RVQ_MOE_OK = 0,
@@ -200,6 +200,28 @@ int rvq_moe_route_forward(rvq_moe *h, const float *x, int32_t n_tokens, int32_t 
                           void *stream);
 
 /*
+ * rvq_moe_prefetch -- start making experts resident in the HBM slot cache of
+ * a streaming handle (codes_location PINNED_HOST) ahead of a later
+ * layer_forward.  [FR] "Lecture anticipée et prédiction du routeur": the
+ * router of the next layer, run on the current layer's hidden state, predicts
+ * that layer's experts; the first 6 of its 16 are read early and consumed as
+ * they land.  Typically `ids` come from rvq_moe_route_topk of THIS handle on
+ * an earlier hidden state (any ids are accepted).
+ *   ids        [n_tokens][k] int32, as route_topk writes them.
+ *   per_token  how many leading ids of each token to prefetch, 1..k.
+ * Synchronises `stream` once to read the ids on the host (as a streaming
+ * layer_forward does), then enqueues the copies of the experts not resident
+ * on the handle's copy stream, into least-recently-used slots (a slot still
+ * read by an enqueued kernel is refilled only after that kernel); nothing
+ * waits for them until a layer_forward uses their slots.  At most
+ * cache_slots distinct experts are taken, in token-major order; ids outside
+ * [0, E) are skipped.  Outputs of later calls do not depend on prefetching.
+ * Errors: EINVAL (null handle/pointer, n_tokens < 1 or > max_tokens,
+ * per_token outside 1..k), ENOTSUP (codes resident on the device), EHIP.
+ */
+int rvq_moe_prefetch(rvq_moe *h, const int32_t *ids, int32_t n_tokens, int32_t per_token, void *stream);
+
+/*
  * rvq_moe_sync -- synchronise `stream`, then return and clear any deferred
  * device-side error (RVQ_MOE_EDEVICE) recorded by earlier calls.
  */
@@ -231,6 +253,8 @@ typedef struct rvq_moe_stats {
     uint64_t slot_hits;             /* slot cache: experts a call found resident */
     uint64_t slot_misses;           /* slot cache: experts copied in */
     uint64_t host_syncs;            /* slot cache: calls that read their ids back */
+    uint64_t prefetch_fills;        /* slot cache: experts copied in by rvq_moe_prefetch */
+    uint64_t prefetch_hits;         /* slot cache: of those, found resident by a later call */
 } rvq_moe_stats;
 
 int rvq_moe_get_stats(const rvq_moe *h, rvq_moe_stats *out);

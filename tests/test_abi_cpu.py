@@ -14,7 +14,7 @@ def test_library_exports_every_header_symbol():
     L = R.lib()
     for n in names:
         assert hasattr(L, n), n
-    assert L.rvq_moe_abi_version() == 3
+    assert L.rvq_moe_abi_version() == 4
 
 
 def _desc(**over):
@@ -68,6 +68,7 @@ def test_calls_reject_null_handle():
     assert L.rvq_moe_route_topk(None, 0x1000, 1, 0x2000, 0x3000, None) == R.EINVAL
     assert L.rvq_moe_layer_forward(None, 0x1000, 1, 0x2000, 0x3000, 0x4000, None) == R.EINVAL
     assert L.rvq_moe_sync(None, None) == R.EINVAL
+    assert L.rvq_moe_prefetch(None, 0x1000, 1, 1, None) == R.EINVAL
     assert L.rvq_moe_close(None) == R.OK
     s = R.Stats()
     assert L.rvq_moe_get_stats(None, ctypes.byref(s)) == R.EINVAL

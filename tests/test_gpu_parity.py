@@ -593,6 +593,135 @@ def test_streaming_validation(torch_mod, tiny):
     st.close()
 
 
+def _lru_prefetch_model(S, events):
+    """The cache policy with prefetches: events are ("acquire", experts) or
+    ("prefetch", experts), each one clock tick.  A prefetch refreshes the
+    resident experts, then fills least-recently-used slots not touched by it
+    (the lowest index among equals) until none is left.  Returns (hits,
+    misses, prefetch fills, prefetch hits)."""
+    slot_of, expert_in, last, pref = {}, [-1] * S, [0] * S, [False] * S
+    hits = misses = fills = phits = 0
+
+    def take(e, clock):
+        free = [sl for sl in range(S) if last[sl] != clock]
+        if not free:
+            return None
+        v = min(free, key=lambda sl: (last[sl], sl))
+        if expert_in[v] >= 0:
+            del slot_of[expert_in[v]]
+        expert_in[v], slot_of[e], last[v] = e, v, clock
+        return v
+
+    for clock, (kind, experts) in enumerate(events, start=1):
+        for e in experts:
+            if e in slot_of:
+                sl = slot_of[e]
+                last[sl] = clock
+                if kind == "acquire":
+                    hits += 1
+                    if pref[sl]:
+                        pref[sl] = False
+                        phits += 1
+        for e in experts:
+            if e in slot_of:
+                continue
+            v = take(e, clock)
+            if kind == "acquire":
+                pref[v] = False
+                misses += 1
+            elif v is None:
+                break
+            else:
+                pref[v] = True
+                fills += 1
+    return hits, misses, fills, phits
+
+
+def test_router_lookahead_prefetch_chain(torch_mod):
+    """[FR] "Lecture anticipée et prédiction du routeur": a 3-layer streaming
+    chain (RMS normalisation, residual), run with and without prefetching
+    layer l+1's first 3 predicted experts (its router on layer l's input).
+    Ids are identical, outputs equal within the fp32 atomic-order bound, and
+    the slot counters match the cache policy's model, prefetches included."""
+    from synth import gpu as G
+    shape = S.Shape(512, 256, 32, 8, "f16")
+    L, T, slots, ahead = 3, 6, 12, 3
+    inps = [G.LayerInputs(shape, seed=31, layer=l, host_codes=True) for l in range(L)]
+    banks = [_pinned_bank(torch_mod, inp) for inp in inps]
+    kw = dict(codes_location=1, cache_slots=slots, pre_rmsnorm=True, residual=True, eps=1e-6)
+    runs = {}
+    for mode in ("plain", "ahead"):
+        layers = [_layer(torch_mod, inps[l], shape, 1, codes=banks[l], **kw) for l in range(L)]
+        h = torch_mod.empty((L + 1, T, shape.d), device="cuda")
+        h[0].copy_(G.to_device(S.tokens(31, 0, T, shape.d)))
+        ids = torch_mod.empty((L, T, shape.top_k), dtype=torch_mod.int32, device="cuda")
+        pred = torch_mod.full((L, T, shape.top_k), -1, dtype=torch_mod.int32, device="cuda")
+        g = torch_mod.empty((L, T, shape.top_k), device="cuda")
+        gp = torch_mod.empty((T, shape.top_k), device="cuda")
+        for t in range(T):
+            for l in range(L):
+                layers[l].route_topk(h[l, t:t + 1], 1, ids[l, t:t + 1], g[l, t:t + 1])
+                layers[l].layer_forward(h[l, t:t + 1], 1, ids[l, t:t + 1], g[l, t:t + 1], h[l + 1, t:t + 1])
+                if mode == "ahead" and l + 1 < L:
+                    layers[l + 1].route_topk(h[l, t:t + 1], 1, pred[l + 1, t:t + 1], gp[t:t + 1])
+                    layers[l + 1].prefetch(pred[l + 1, t:t + 1], 1, ahead)
+        for layer in layers:
+            layer.sync()
+        runs[mode] = (ids.cpu().numpy(), pred.cpu().numpy(), h.cpu().numpy(), [x.stats() for x in layers])
+        for layer in layers:
+            layer.close()
+    (ia, _, ha, sa), (ib, pb, hb, sb) = runs["plain"], runs["ahead"]
+    assert np.array_equal(ia, ib)
+    for l in range(1, L + 1):
+        err = np.linalg.norm(ha[l] - hb[l], axis=1) / np.linalg.norm(ha[l], axis=1)
+        assert err.max() <= 1e-6, (l, err.max())
+    assert sum(st["prefetch_fills"] for st in sb) > 0
+    assert all(st["prefetch_fills"] == 0 for st in sa)
+    for l in range(L):
+        events = []
+        for t in range(T):
+            if l > 0:  # layer l's prefetch was issued right after layer l-1's call of token t
+                events.append(("prefetch", list(dict.fromkeys(pb[l, t, :ahead].tolist()))))
+            events.append(("acquire", list(dict.fromkeys(ib[l, t].tolist()))))
+        # the prefetch of token t comes after layer l-1's call of token t, which
+        # precedes layer l's call of token t: the order above
+        hits, misses, fills, phits = _lru_prefetch_model(slots, events)
+        st = sb[l]
+        assert (st["slot_hits"], st["slot_misses"], st["prefetch_fills"], st["prefetch_hits"]) == \
+            (hits, misses, fills, phits), (l, st)
+        assert st["h2d_bytes"] == (misses + fills) * (st["code_bytes_resident"] // slots)
+    # the chain's outputs against the oracle, teacher-forced, on the first token
+    for l in range(L):
+        ref = O.layer(ha[l][0], inps[l].w_r, shape.top_k, inps[l].codebook, inps[l].record, shape.d, shape.ffn,
+                      pre_rmsnorm=True, eps=1e-6)
+        assert np.array_equal(ib[l][0], ref.route.ids)
+        delta = hb[l + 1][0].astype(np.float64) - ha[l][0].astype(np.float64)
+        assert np.linalg.norm(delta - ref.delta) / np.linalg.norm(ref.delta) <= TOL_Y
+
+
+def test_prefetch_validation(torch_mod, tiny):
+    from vector_quantized_expert_amd import RvqMoeError
+    from vector_quantized_expert_amd import rvq_moe as R
+    shape = S.TINY
+    ids = torch_mod.zeros((2, 4), dtype=torch_mod.int32, device="cuda")
+    rs = _layer(torch_mod, tiny, shape, 2)
+    with pytest.raises(RvqMoeError) as ei:
+        rs.prefetch(ids, 1, 2)
+    assert ei.value.status == R.ENOTSUP
+    rs.close()
+    bank = _pinned_bank(torch_mod, tiny)
+    st = _layer(torch_mod, tiny, shape, 2, codes=bank, codes_location=1, cache_slots=4)
+    for n, per in ((0, 1), (3, 1), (1, 0), (1, 5)):
+        with pytest.raises(RvqMoeError) as ei:
+            st.prefetch(ids, n, per)
+        assert ei.value.status == R.EINVAL
+    bad = torch_mod.tensor([[-1, shape.n_experts, 2, 2], [2, 3, 1, 0]], dtype=torch_mod.int32, device="cuda")
+    st.prefetch(bad, 2, 4)  # out-of-range ids skipped, duplicates once, at most 4 slots
+    s = st.stats()
+    assert s["prefetch_fills"] == 4 and s["h2d_bytes"] == 4 * (s["code_bytes_resident"] // 4)
+    st.close()
+
+
 def test_k3_streaming_batch1_matches_resident(torch_mod):
     """d=7168, ffn=2048, E=384, top-16 from a pinned host bank through 32 slots,
     one token per call; against a resident handle and the oracle."""

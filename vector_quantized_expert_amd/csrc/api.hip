@@ -434,6 +434,34 @@ static int take_device_error(rvq_moe *h) {
     return RVQ_MOE_OK;
 }
 
+extern "C" int rvq_moe_prefetch(rvq_moe *h, const int32_t *ids, int32_t T, int32_t per_token, void *stream) {
+    if (!h) return fail(RVQ_MOE_EINVAL, "handle is NULL");
+    if (!ids) return fail(RVQ_MOE_EINVAL, "ids is NULL");
+    if (T < 1 || T > h->max_tokens) return fail(RVQ_MOE_EINVAL, "n_tokens=%d outside [1, %d]", T, h->max_tokens);
+    if (per_token < 1 || per_token > h->g.k)
+        return fail(RVQ_MOE_EINVAL, "per_token=%d outside [1, %d]", per_token, h->g.k);
+    if (!h->streaming) return fail(RVQ_MOE_ENOTSUP, "prefetch needs codes streaming from pinned host memory");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    SlotCache &c = h->cache;
+    const int k = h->g.k;
+    HIP_TRY(hipMemcpyAsync(c.ids_host, ids, sizeof(int32_t) * (size_t)T * k, hipMemcpyDeviceToHost, s));
+    HIP_TRY(hipStreamSynchronize(s));
+    c.syncs++;
+    // distinct experts in token-major order, at most one per slot
+    std::vector<int> &U = h->call_experts;
+    U.clear();
+    const uint32_t stamp = (uint32_t)(c.clock + 1);
+    for (int t = 0; t < T && (int)U.size() < c.S; t++)
+        for (int j = 0; j < per_token && (int)U.size() < c.S; j++) {
+            const int e = c.ids_host[t * k + j];
+            if (e < 0 || e >= h->g.E || c.mark[e] == stamp) continue;
+            c.mark[e] = stamp;
+            U.push_back(e);
+        }
+    HIP_TRY(slots_prefetch(c, U.data(), (int)U.size()));
+    return RVQ_MOE_OK;
+}
+
 extern "C" int rvq_moe_sync(rvq_moe *h, void *stream) {
     if (!h) return fail(RVQ_MOE_EINVAL, "handle is NULL");
     HIP_TRY(hipStreamSynchronize(static_cast<hipStream_t>(stream)));
@@ -460,6 +488,8 @@ extern "C" int rvq_moe_get_stats(const rvq_moe *h, rvq_moe_stats *out) {
     out->slot_hits = h->cache.hits;
     out->slot_misses = h->cache.misses;
     out->host_syncs = h->cache.syncs;
+    out->prefetch_fills = h->cache.prefetch_fills;
+    out->prefetch_hits = h->cache.prefetch_hits;
     return RVQ_MOE_OK;
 }
 

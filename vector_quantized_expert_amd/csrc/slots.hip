@@ -20,6 +20,11 @@
 //     arguments are captured at enqueue time, so the host may run ahead.
 // All bookkeeping is on the host: the caller's call synchronises once to read
 // the expert ids, then everything else is enqueued.
+//
+// Prefetch ([FR] "Lecture anticipée et prédiction du routeur": the next
+// layer's router, run early, predicts its experts and their reads start
+// before they are needed) fills slots the same way without a kernel waiting;
+// a later acquire that finds such a slot waits on its `filled` event.
 #include <string.h>
 
 #include "internal.hpp"
@@ -65,6 +70,7 @@ hipError_t slots_open(SlotCache &c, const Geometry &g, int S, int max_pairs, con
     c.slot_of.assign(g.E, -1);
     c.expert_in.assign(S, -1);
     c.last_use.assign(S, 0);
+    c.prefetched.assign(S, 0);
     c.mark.assign(g.E, 0);
     c.clock = 0;
     // the bank in the internal layout: canonical records go through the GPU
@@ -116,6 +122,12 @@ hipError_t slots_acquire(SlotCache &c, const int *experts, int n, hipStream_t co
             c.last_use[sl] = now;
             used.push_back(sl);
             c.hits++;
+            if (c.prefetched[sl]) {  // its copy may still be in flight
+                c.prefetched[sl] = 0;
+                c.prefetch_hits++;
+            }
+            const hipError_t err = hipStreamWaitEvent(compute, c.filled[sl], 0);
+            if (err != hipSuccess) return err;
         }
     }
     for (int i = 0; i < n; i++) {
@@ -129,6 +141,7 @@ hipError_t slots_acquire(SlotCache &c, const int *experts, int n, hipStream_t co
         c.expert_in[victim] = e;
         c.slot_of[e] = victim;
         c.last_use[victim] = now;
+        c.prefetched[victim] = 0;
         used.push_back(victim);
         c.misses++;
         c.h2d_bytes += (uint64_t)c.rec;
@@ -151,6 +164,36 @@ hipError_t slots_acquire(SlotCache &c, const int *experts, int n, hipStream_t co
         }
         hipLaunchKernelGGL(k_set_slots, dim3(1), dim3(kSetPairs), 0, compute, c.tab_dev, p);
         const hipError_t err = hipGetLastError();
+        if (err != hipSuccess) return err;
+    }
+    return hipSuccess;
+}
+
+hipError_t slots_prefetch(SlotCache &c, const int *experts, int n) {
+    const uint64_t now = ++c.clock;
+    for (int i = 0; i < n; i++) {
+        const int sl = c.slot_of[experts[i]];
+        if (sl >= 0) c.last_use[sl] = now;
+    }
+    for (int i = 0; i < n; i++) {
+        const int e = experts[i];
+        if (c.slot_of[e] >= 0) continue;
+        int victim = -1;
+        for (int sl = 0; sl < c.S; sl++)
+            if (c.last_use[sl] != now && (victim < 0 || c.last_use[sl] < c.last_use[victim])) victim = sl;
+        if (victim < 0) break;  // every slot already holds one of this prefetch's experts
+        if (c.expert_in[victim] >= 0) c.slot_of[c.expert_in[victim]] = -1;
+        c.expert_in[victim] = e;
+        c.slot_of[e] = victim;
+        c.last_use[victim] = now;
+        c.prefetched[victim] = 1;
+        c.prefetch_fills++;
+        c.h2d_bytes += (uint64_t)c.rec;
+        hipError_t err = hipStreamWaitEvent(c.copy, c.released[victim], 0);
+        if (err == hipSuccess)
+            err = hipMemcpyAsync(c.slots + (int64_t)victim * c.rec, c.bank + (int64_t)e * c.rec, (size_t)c.rec,
+                                 hipMemcpyHostToDevice, c.copy);
+        if (err == hipSuccess) err = hipEventRecord(c.filled[victim], c.copy);
         if (err != hipSuccess) return err;
     }
     return hipSuccess;

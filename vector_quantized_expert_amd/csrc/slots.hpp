@@ -24,9 +24,11 @@ struct SlotCache {
     std::vector<int> slot_of;          // [E] slot of a resident expert, or -1
     std::vector<int> expert_in;        // [S] expert in a slot, or -1
     std::vector<uint64_t> last_use;    // [S] acquire clock of the last use
+    std::vector<uint8_t> prefetched;   // [S] filled by a prefetch and not yet used by a call
     std::vector<uint32_t> mark;        // [E] scratch for set building
     uint64_t clock = 0;
     uint64_t hits = 0, misses = 0, h2d_bytes = 0, syncs = 0;
+    uint64_t prefetch_fills = 0, prefetch_hits = 0;
 };
 
 // Allocate the slots and the pinned bank, and fill the bank from the caller's
@@ -39,5 +41,10 @@ void slots_close(SlotCache &c);
 // slots to release after those kernels.
 hipError_t slots_acquire(SlotCache &c, const int *experts, int n, hipStream_t compute, std::vector<int> &used);
 hipError_t slots_release(SlotCache &c, const std::vector<int> &used, hipStream_t compute);
+// Start copies that make experts[0 .. n) (distinct) resident ahead of a later
+// acquire: resident ones are refreshed, the others take least-recently-used
+// slots (at most S experts in all).  Nothing waits for the copies until an
+// acquire uses their slots.
+hipError_t slots_prefetch(SlotCache &c, const int *experts, int n);
 
 }  // namespace rvq

@@ -60,7 +60,7 @@ class Stats(ctypes.Structure):
     _fields_ = [(n, ctypes.c_uint64) for n in (
         "route_calls", "forward_calls", "tokens_routed", "tokens_forwarded", "expert_evals",
         "code_bytes_resident", "record_bytes", "codebook_bytes", "h2d_bytes", "slot_hits", "slot_misses",
-        "host_syncs")]
+        "host_syncs", "prefetch_fills", "prefetch_hits")]
 
 
 _lib = None
@@ -78,6 +78,7 @@ def lib():
         L.rvq_moe_route_topk.argtypes = [vp, vp, i32, vp, vp, vp]
         L.rvq_moe_layer_forward.argtypes = [vp, vp, i32, vp, vp, vp, vp]
         L.rvq_moe_route_forward.argtypes = [vp, vp, i32, vp, vp, vp, vp]
+        L.rvq_moe_prefetch.argtypes = [vp, vp, i32, i32, vp]
         L.rvq_moe_sync.argtypes = [vp, vp]
         L.rvq_moe_close.argtypes = [vp]
         L.rvq_moe_last_error.argtypes = []
@@ -87,7 +88,8 @@ def lib():
         L.rvq_moe_set_profiling.argtypes = [vp, ctypes.c_int]
         L.rvq_moe_kernel_times.argtypes = [vp, ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(ctypes.c_uint64),
                                            ctypes.POINTER(ctypes.c_double), ctypes.c_int]
-        for n in ("rvq_moe_open", "rvq_moe_route_topk", "rvq_moe_layer_forward", "rvq_moe_route_forward", "rvq_moe_sync",
+        for n in ("rvq_moe_open", "rvq_moe_route_topk", "rvq_moe_layer_forward", "rvq_moe_route_forward",
+                  "rvq_moe_prefetch", "rvq_moe_sync",
                   "rvq_moe_close", "rvq_moe_abi_version", "rvq_moe_get_stats", "rvq_moe_set_profiling",
                   "rvq_moe_kernel_times"):
             getattr(L, n).restype = ctypes.c_int
@@ -166,6 +168,10 @@ class RvqMoe:
     def route_forward(self, x, n_tokens, ids, gates, y, stream=None):
         return _check(lib().rvq_moe_route_forward(self.h, _ptr(x), n_tokens, _ptr(ids), _ptr(gates), _ptr(y),
                                                   _stream(stream)), "rvq_moe_route_forward")
+
+    def prefetch(self, ids, n_tokens, per_token, stream=None):
+        return _check(lib().rvq_moe_prefetch(self.h, _ptr(ids), n_tokens, per_token, _stream(stream)),
+                      "rvq_moe_prefetch")
 
     def sync(self, stream=None):
         return _check(lib().rvq_moe_sync(self.h, _stream(stream)), "rvq_moe_sync")
