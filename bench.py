@@ -96,6 +96,9 @@ def main():
                     help="every layer_forward call takes the chunk path (bf16 matrix cores)")
     ap.add_argument("--stream-slots", type=int, default=0,
                     help="stream the codes from a pinned host bank through this many HBM slots")
+    ap.add_argument("--lut-expert-tokens", type=int, default=0,
+                    help="with --chunk: experts routed fewer tokens than this take the table path (0: the "
+                         "library default, 1: every expert on the matrix cores)")
     ap.add_argument("--lookahead", type=int, default=0,
                     help="with --layers and --stream-slots: after layer l's call, run layer l+1's router on layer "
                          "l's input and prefetch the first N of its predicted experts (rvq_moe_prefetch)")
@@ -143,7 +146,8 @@ def main():
         layers.append(RvqMoe(d=shape.d, ffn=shape.ffn, n_experts=shape.n_experts, top_k=shape.top_k,
                              codebook_dtype=1, router_w=inp.w_r_dev, codebooks=inp.cb_dev, codes=codes,
                              max_tokens=B, pre_rmsnorm=chain, residual=chain, eps=1e-6,
-                             chunk_min_tokens=1 if args.chunk else B + 1, **extra))
+                             chunk_min_tokens=1 if args.chunk else B + 1,
+                             lut_expert_tokens=args.lut_expert_tokens, **extra))
         del codes
         inp.free_codes()
         inputs.append(inp)
@@ -180,18 +184,22 @@ def main():
 
     h2d = None
     if streaming:
-        # the host -> device ceiling this box measures for one large pinned copy
-        src = torch.empty(1 << 30, dtype=torch.uint8, pin_memory=True)
-        dst = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        # the host -> device ceiling this box measures for pinned copies of one
+        # expert record each (as the slot fills), 1 GiB in all, three rounds
+        rec_b = shape.record_bytes
+        n_rec = (1 << 30) // rec_b
+        src = torch.empty(n_rec * rec_b, dtype=torch.uint8, pin_memory=True)
+        dst = torch.empty(n_rec * rec_b, dtype=torch.uint8, device="cuda")
         dst.copy_(src, non_blocking=True)
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         for _ in range(3):
-            dst.copy_(src, non_blocking=True)
+            for i in range(n_rec):
+                dst[i * rec_b:(i + 1) * rec_b].copy_(src[i * rec_b:(i + 1) * rec_b], non_blocking=True)
         e1.record()
         torch.cuda.synchronize()
-        h2d = {"ceiling_GBps": 3 * (1 << 30) / (e0.elapsed_time(e1) * 1e-3) / 1e9}
+        h2d = {"ceiling_GBps": 3 * n_rec * rec_b / (e0.elapsed_time(e1) * 1e-3) / 1e9}
         del src, dst
         torch.cuda.empty_cache()
 

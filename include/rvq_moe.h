@@ -63,8 +63,17 @@ typedef enum rvq_moe_status {
     RVQ_MOE_EDEVICE = -6   /* deferred: a kernel saw an expert id outside [0, n_experts) */
 } rvq_moe_status;
 
-/* Default chunk-path threshold (tokens per layer_forward call). */
-#define RVQ_MOE_CHUNK_MIN_TOKENS 256
+/* Default chunk-path threshold (tokens per layer_forward call): where the
+ * chunk path (with the default adaptive dispatch below) overtakes the table
+ * path for d=7168, ffn=2048, E=384, top-16 on one MI355X (64 tokens: table
+ * 3.08 ms, chunk 3.03 ms; 80 tokens: table 3.86 ms, chunk 3.67 ms; 48 tokens:
+ * table 2.35 ms, chunk 2.46 ms).  Other shapes may set their own. */
+#define RVQ_MOE_CHUNK_MIN_TOKENS 72
+
+/* Default of lut_expert_tokens (see rvq_moe_desc): the best of 3..6 measured
+ * at that shape (96 tokens per call: 4.05 ms against 4.97 ms with every expert
+ * on the matrix cores). */
+#define RVQ_MOE_LUT_EXPERT_TOKENS 4
 
 typedef enum rvq_moe_cb_dtype {
     RVQ_MOE_CB_F32 = 0,    /* IEEE binary32 codebook entries */
@@ -110,7 +119,13 @@ typedef enum rvq_moe_codes_location {
  *                0 = the library default (RVQ_MOE_CHUNK_MIN_TOKENS); a value
  *                above max_tokens never takes it (and allocates nothing for
  *                it).  Must be >= 0.
- *   reserved     must be 0.
+ *   lut_expert_tokens  adaptive dispatch inside a chunk-path call: an expert
+ *                routed fewer tokens than this is evaluated by the table path
+ *                (fp32, per-token tables) instead of the matrix cores, as long
+ *                as the pairs so handed over fit the table path's order table
+ *                (512 pairs; experts in id order).  0 = the library default
+ *                (RVQ_MOE_LUT_EXPERT_TOKENS); 1 = every expert on the matrix
+ *                cores.  Streaming handles always use 1.  Must be >= 0.
  *   stream       stream used for the upload and repack inside open.
  */
 typedef struct rvq_moe_desc {
@@ -129,7 +144,7 @@ typedef struct rvq_moe_desc {
     int32_t residual;
     int32_t max_tokens;
     int32_t chunk_min_tokens;
-    int32_t reserved;           /* must be 0 */
+    int32_t lut_expert_tokens;
     double eps;
     const float *router_w;
     const void *codebooks;

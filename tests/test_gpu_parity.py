@@ -335,7 +335,7 @@ def test_batch_beyond_the_order_table_uses_pair_order(torch_mod, tiny):
     """160 tokens x top-4 = 640 pairs: above the grouped-order table, so the
     pairs run in plain pair order; every token still matches the oracle."""
     shape = S.TINY
-    layer = _layer(torch_mod, tiny, shape, 160)
+    layer = _layer(torch_mod, tiny, shape, 160, chunk_min_tokens=161)  # the table path
     x = S.tokens(0, 1000, 160, shape.d)
     ids, gates, y = _run(torch_mod, layer, shape, x)
     _check(tiny, shape, x, ids, gates, y)
@@ -422,6 +422,62 @@ def test_chunk_path_rmsnorm_residual_and_threshold(torch_mod):
     ids2, gates2, y2 = _run(torch_mod, layer, shape, x[:15])   # 15 < 16: table path
     _check(inp, shape, x[:15], ids2, gates2, y2, pre_rmsnorm=True, residual=True)
     layer.close()
+
+
+def _listed_experts(ids, E, lut_tokens, cap=512):
+    """Experts a chunk-path call hands to the table path: those with fewer than
+    lut_tokens tokens (and at least one), in id order while their pairs fit
+    the order table."""
+    cnt = np.bincount(ids.ravel(), minlength=E)
+    listed, total = set(), 0
+    for e in range(E):
+        if 0 < cnt[e] < lut_tokens:
+            total += cnt[e]
+            if total > cap:
+                break
+            listed.add(e)
+    return listed
+
+
+def test_adaptive_dispatch_by_tokens_per_expert(torch_mod):
+    """A chunk-path call with lut_expert_tokens = 12: experts routed fewer than
+    12 of the 48 tokens go to the table path (fp32), the others to the matrix
+    cores.  Tokens whose experts are all on one side match that side's path
+    alone (table-only and matrix-core-only handles on the same weights); every
+    token follows the oracle at the bf16 bar; with a threshold above every
+    count all pairs take the table path and match it at 1e-6."""
+    from synth import gpu as G
+    shape = S.Shape(264, 136, 12, 3, "f16")
+    T, tau = 48, 12
+    inp = G.LayerInputs(shape, seed=23, layer=2, host_codes=True)
+    mix = _layer(torch_mod, inp, shape, T, chunk_min_tokens=8, lut_expert_tokens=tau)
+    mma = _layer(torch_mod, inp, shape, T, chunk_min_tokens=8, lut_expert_tokens=1)
+    tab = _layer(torch_mod, inp, shape, T, chunk_min_tokens=T + 1)
+    alll = _layer(torch_mod, inp, shape, T, chunk_min_tokens=8, lut_expert_tokens=T + 1)
+    x = S.tokens(23, 0, T, shape.d)
+    a, b, c, d_ = (_run(torch_mod, h, shape, x) for h in (mix, mma, tab, alll))
+    for r in (b, c, d_):
+        assert np.array_equal(a[0], r[0])
+    listed = _listed_experts(a[0], shape.n_experts, tau)
+    side = [sum(e in listed for e in row) for row in a[0]]
+    assert 0 < len(listed) < len(set(a[0].ravel().tolist()))
+    n_tab = n_mma = 0
+    for t in range(T):
+        if side[t] == shape.top_k:
+            ref, n_tab = c, n_tab + 1
+        elif side[t] == 0:
+            ref, n_mma = b, n_mma + 1
+        else:
+            continue
+        err = np.linalg.norm(a[2][t] - ref[2][t]) / np.linalg.norm(ref[2][t])
+        assert err <= 1e-6, (t, side[t], err)
+    assert n_tab > 0 and n_mma > 0, (n_tab, n_mma)
+    _check_chunk(inp, shape, x, *a)
+    err = np.linalg.norm(d_[2] - c[2], axis=1) / np.linalg.norm(c[2], axis=1)
+    assert err.max() <= 1e-6, err.max()
+    _check(inp, shape, x, *d_, tokens=range(4))
+    for h in (mix, mma, tab, alll):
+        h.close()
 
 
 def test_chunk_path_invalid_ids_poison_only_their_token(torch_mod, tiny):

@@ -45,6 +45,7 @@ struct rvq_moe {
     Geometry g;
     int pre_rmsnorm, residual, max_tokens;
     int chunk_min;       // layer_forward calls with T >= chunk_min take the chunk path
+    int lut_tokens;      // in such a call, experts with fewer tokens take the table path
     ChunkWork cw;        // its workspace (all null when max_tokens < chunk_min)
     double eps;
     uint8_t *codes;      // [E][rec_int] internal layout (resident codes), or null when streaming
@@ -114,6 +115,7 @@ static void free_handle(rvq_moe *h) {
     (void)hipFree(h->cw.pos_of);
     (void)hipFree(h->cw.grp_off);
     (void)hipFree(h->cw.act);
+    (void)hipFree(h->cw.list);
     for (hipEvent_t e : h->prof_pool) (void)hipEventDestroy(e);
     slots_close(h->cache);
     delete h;
@@ -139,6 +141,8 @@ static int open_impl(const rvq_moe_desc *desc, rvq_moe *h) {
     h->eps = D.eps;
     h->max_tokens = D.max_tokens;
     h->chunk_min = D.chunk_min_tokens > 0 ? D.chunk_min_tokens : RVQ_MOE_CHUNK_MIN_TOKENS;
+    h->lut_tokens = D.lut_expert_tokens > 0 ? D.lut_expert_tokens : RVQ_MOE_LUT_EXPERT_TOKENS;
+    if (D.codes_location == RVQ_MOE_CODES_PINNED_HOST) h->lut_tokens = 1;
     const Geometry &g = h->g;
     const int64_t E = D.n_experts;
     h->streaming = D.codes_location == RVQ_MOE_CODES_PINNED_HOST;
@@ -161,6 +165,7 @@ static int open_impl(const rvq_moe_desc *desc, rvq_moe *h) {
         HIP_TRY(hipMalloc(&h->cw.pos_of, sizeof(int) * (size_t)P));
         HIP_TRY(hipMalloc(&h->cw.grp_off, sizeof(int) * (size_t)(E + 2)));
         HIP_TRY(hipMalloc(&h->cw.act, sizeof(int) * (size_t)(E + 1)));
+        HIP_TRY(hipMalloc(&h->cw.list, sizeof(int) * (size_t)kPairListInts));
     }
     int n_cu = 0;
     HIP_TRY(hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, h->device));
@@ -218,7 +223,7 @@ extern "C" int rvq_moe_open(const rvq_moe_desc *desc, rvq_moe **out) {
     }
     if (D.cache_slots < 0) return fail(RVQ_MOE_EINVAL, "cache_slots=%d < 0", D.cache_slots);
     if (D.chunk_min_tokens < 0) return fail(RVQ_MOE_EINVAL, "chunk_min_tokens=%d < 0", D.chunk_min_tokens);
-    if (D.reserved != 0) return fail(RVQ_MOE_EINVAL, "reserved=%d must be 0", D.reserved);
+    if (D.lut_expert_tokens < 0) return fail(RVQ_MOE_EINVAL, "lut_expert_tokens=%d < 0", D.lut_expert_tokens);
     if (D.cache_slots > 0 && D.cache_slots < D.top_k)
         return fail(RVQ_MOE_EBUDGET, "cache_slots=%d below one token's working set (top_k=%d)", D.cache_slots,
                     D.top_k);
@@ -324,7 +329,7 @@ static int stream_forward(rvq_moe *h, const float *x, int T, const int32_t *ids,
             }
         }
         std::sort(U.begin(), U.end());  // the device's order of active experts
-        HIP_TRY(launch_chunk_prep(g, h->cw, x, ids, y, T, h->pre_rmsnorm, h->residual, h->eps, h->ws.err, s));
+        HIP_TRY(launch_chunk_prep(g, h->cw, x, ids, y, T, h->pre_rmsnorm, h->residual, h->eps, 1, h->ws.err, s));
         const int R = c.S >= 2 ? c.S / 2 : 1;
         for (int a0 = 0; a0 < (int)U.size(); a0 += R) {
             const int a1 = a0 + R < (int)U.size() ? a0 + R : (int)U.size();
@@ -385,7 +390,10 @@ extern "C" int rvq_moe_layer_forward(rvq_moe *h, const float *x, int32_t T, cons
     } else if (T >= h->chunk_min) {
         ProfScope p(h, s, prof, 3);
         HIP_TRY(launch_chunk(h->g, h->cw, h->codes, h->cbs, x, ids, gates, y, T, h->pre_rmsnorm, h->residual,
-                             h->eps, h->ws.err, s));
+                             h->eps, h->lut_tokens, h->ws.err, s));
+        if (h->lut_tokens > 1)  // the experts with few tokens, listed by the chunk prep, on the table path
+            HIP_TRY(launch_layer(h->g, h->ws, h->codes, nullptr, h->cbs, h->router_wt, x, ids, gates, y, T,
+                                 h->pre_rmsnorm, h->residual, h->eps, false, s, h->cw.list));
     } else {
         ProfScope p(h, s, prof, 1);
         HIP_TRY(launch_layer(h->g, h->ws, h->codes, nullptr, h->cbs, h->router_wt, x, ids, gates, y, T,

@@ -14,7 +14,8 @@
 //
 // Steps (one launch each, all asynchronous on the caller's stream):
 //   prep   ids -> per-expert counts, offsets, the permutation and the list of
-//          experts with tokens (one workgroup);
+//          experts for the matrix cores (one workgroup); experts with few
+//          tokens are listed for the table path instead (adaptive dispatch);
 //   stage  x -> bf16 rows in permuted order (RMS-normalised first when asked);
 //          y <- x (residual) or 0, NaN for a token with an invalid id;
 //   gu     per (expert, 64 output rows): gate and up tiles -> h = silu(a) b in bf16;
@@ -44,13 +45,22 @@ constexpr int kXRow = kTileSlices * kVec + 8;  // bf16 per staged token row (pad
 
 // ---------------------------------------------------------------------------
 // prep: one workgroup of 1024 threads.
-__global__ __launch_bounds__(1024) void k_chunk_prep(const int32_t *__restrict__ ids, int P, int E,
+// Adaptive dispatch by tokens per expert: an expert with 0 < count <
+// lut_tokens is evaluated by the table path (its per-token cost is a table
+// build and a gather, against a fixed cost per expert on the matrix cores:
+// rebuilding its weights) as long as the pairs so listed fit the table path's
+// order table; experts are taken in id order, so the listed ones are a prefix
+// of the candidates.  list: n, then per listed position: group start | size
+// << 16, pair, expert.
+__global__ __launch_bounds__(1024) void k_chunk_prep(const int32_t *__restrict__ ids, int P, int E, int lut_tokens,
                                                      int *__restrict__ grp_off, int *__restrict__ perm,
                                                      int *__restrict__ pos_of, int *__restrict__ act,
-                                                     int *__restrict__ err) {
+                                                     int *__restrict__ list, int *__restrict__ err) {
     __shared__ int cnt[kMaxExperts + 1];
     __shared__ int off[kMaxExperts + 2];
     __shared__ int aoff[kMaxExperts + 1];
+    __shared__ int gstart[kMaxExperts + 1];
+    __shared__ int lpos[kMaxExperts];  // list position of an expert's first pair, or -1
     const int NE = E + 1;  // bin E: ids outside [0, E)
     for (int i = threadIdx.x; i < NE; i += 1024) cnt[i] = 0;
     __syncthreads();
@@ -64,12 +74,34 @@ __global__ __launch_bounds__(1024) void k_chunk_prep(const int32_t *__restrict__
     }
     __syncthreads();
     if (threadIdx.x < 64) {
-        // exclusive scans of the counts and of the non-empty flags, one wave
         const int lane = threadIdx.x, per = (NE + 63) / 64;
+        // the table path's experts: exclusive scan of the candidates' counts,
+        // kept while the running total fits the order table
+        auto cand = [&](int i) { return (i < E && cnt[i] > 0 && cnt[i] < lut_tokens) ? cnt[i] : 0; };
+        int c = 0;
+        for (int i = lane * per; i < min(NE, (lane + 1) * per); i++) c += cand(i);
+        int ic = c;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int v = __shfl_up(ic, o);
+            if (lane >= o) ic += v;
+        }
+        int rc = ic - c, listed = 0;
+        for (int i = lane * per; i < min(NE, (lane + 1) * per); i++) {
+            const int n = cand(i);
+            const bool take = n > 0 && rc + n <= kOrderMax;
+            if (i < E) lpos[i] = take ? rc : -1;
+            listed += take ? n : 0;
+            rc += n;
+        }
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) listed += __shfl_xor(listed, o);
+        if (lane == 0) list[0] = listed;
+        // exclusive scans of the counts and of the matrix-core experts
         int s = 0, a = 0;
         for (int i = lane * per; i < min(NE, (lane + 1) * per); i++) {
             s += cnt[i];
-            a += (i < E && cnt[i] > 0);
+            a += (i < E && cnt[i] > 0 && lpos[i] < 0);
         }
         int is = s, ia = a;
 #pragma unroll
@@ -83,9 +115,10 @@ __global__ __launch_bounds__(1024) void k_chunk_prep(const int32_t *__restrict__
         int rs = is - s, ra = ia - a;
         for (int i = lane * per; i < min(NE, (lane + 1) * per); i++) {
             off[i] = rs;
+            gstart[i] = rs;
             aoff[i] = ra;
             rs += cnt[i];
-            ra += (i < E && cnt[i] > 0);
+            ra += (i < E && cnt[i] > 0 && lpos[i] < 0);
         }
         if (lane == 63) {
             off[NE] = rs;
@@ -95,7 +128,7 @@ __global__ __launch_bounds__(1024) void k_chunk_prep(const int32_t *__restrict__
     __syncthreads();
     for (int i = threadIdx.x; i <= NE; i += 1024) grp_off[i] = off[i];
     for (int i = threadIdx.x; i < E; i += 1024)
-        if (cnt[i] > 0) act[aoff[i]] = i;
+        if (cnt[i] > 0 && lpos[i] < 0) act[aoff[i]] = i;
     __syncthreads();
     // placement: order within a group is the order the atomics hand out (the
     // result does not depend on it beyond fp32 summation order)
@@ -105,6 +138,12 @@ __global__ __launch_bounds__(1024) void k_chunk_prep(const int32_t *__restrict__
         const int pos = atomicAdd(&off[e], 1);
         perm[pos] = p;
         pos_of[p] = pos;
+        if (e < E && lpos[e] >= 0) {
+            const int lp = lpos[e] + (pos - gstart[e]);
+            list[1 + lp] = lpos[e] | (cnt[e] << 16);
+            list[1 + kOrderMax + lp] = p;
+            list[1 + 2 * kOrderMax + lp] = e;
+        }
     }
 }
 
@@ -375,10 +414,10 @@ __global__ __launch_bounds__(kCkThreads) void k_chunk_down(ChunkArgs A) {
 
 // ---------------------------------------------------------------------------
 hipError_t launch_chunk_prep(const Geometry &g, const ChunkWork &cw, const float *x, const int32_t *ids, float *y,
-                             int T, int pre, int residual, double eps, int *err, hipStream_t s) {
+                             int T, int pre, int residual, double eps, int lut_tokens, int *err, hipStream_t s) {
     const int P = T * g.k;
-    hipLaunchKernelGGL(k_chunk_prep, dim3(1), dim3(1024), 0, s, ids, P, g.E, cw.grp_off, cw.perm, cw.pos_of, cw.act,
-                       err);
+    hipLaunchKernelGGL(k_chunk_prep, dim3(1), dim3(1024), 0, s, ids, P, g.E, lut_tokens, cw.grp_off, cw.perm,
+                       cw.pos_of, cw.act, cw.list, err);
     hipError_t rc = hipGetLastError();
     if (rc != hipSuccess) return rc;
     hipLaunchKernelGGL(k_chunk_stage, dim3(T), dim3(kCkThreads), 0, s, x, g.d, g.k, pre, eps, residual, g.E, ids,
@@ -404,8 +443,8 @@ hipError_t launch_chunk_experts(const Geometry &g, const ChunkWork &cw, const ui
 
 hipError_t launch_chunk(const Geometry &g, const ChunkWork &cw, const uint8_t *codes, const void *cbs, const float *x,
                         const int32_t *ids, const float *gates, float *y, int T, int pre, int residual, double eps,
-                        int *err, hipStream_t s) {
-    const hipError_t rc = launch_chunk_prep(g, cw, x, ids, y, T, pre, residual, eps, err, s);
+                        int lut_tokens, int *err, hipStream_t s) {
+    const hipError_t rc = launch_chunk_prep(g, cw, x, ids, y, T, pre, residual, eps, lut_tokens, err, s);
     if (rc != hipSuccess) return rc;
     return launch_chunk_experts(g, cw, codes, nullptr, cbs, gates, y, 0, g.E, s);
 }

@@ -123,8 +123,16 @@ struct ChunkWork {
     int *perm;     // [P] position -> pair
     int *pos_of;   // [P] pair -> position
     int *grp_off;  // [E + 2] group offsets (group E: invalid ids)
-    int *act;      // [E + 1] experts with tokens, then their count at [E]
+    int *act;      // [E + 1] experts on the matrix cores, then their count at [E]
+    int *list;     // [kPairListInts] pairs handed to the table path (see below)
 };
+
+// The table path's order table holds up to kOrderMax (token, expert) pairs.
+// A pair list handed from the chunk path to it is [1 + 3 * kOrderMax] ints:
+// n, then per position (pairs grouped by expert): group start | group size
+// << 16, pair index, expert id.
+constexpr int kOrderMax = 512;
+constexpr int kPairListInts = 1 + 3 * kOrderMax;
 
 constexpr int kRouteTok = 8;       // tokens per router workgroup when T > 1
 constexpr int kMaxExperts = 1024;
@@ -144,18 +152,23 @@ hipError_t layer_blocks_per_cu(int cb_dtype, int *out);
 // Chunk path: prep + stage (grouping, bf16 tokens, y init), then the
 // contractions for the active experts act[a0 .. a1) (a1 clipped to the number
 // of active experts on the device); launch_chunk does both for all experts.
+// lut_tokens: experts with fewer tokens (while their pairs fit cw.list) are
+// left out of the matrix-core kernels and listed for the table path (1: none).
 hipError_t launch_chunk_prep(const Geometry &g, const ChunkWork &cw, const float *x, const int32_t *ids, float *y,
-                             int T, int pre, int residual, double eps, int *err, hipStream_t s);
+                             int T, int pre, int residual, double eps, int lut_tokens, int *err, hipStream_t s);
 hipError_t launch_chunk_experts(const Geometry &g, const ChunkWork &cw, const uint8_t *codes,
                                 const uint8_t *const *slot_tab, const void *cbs, const float *gates, float *y, int a0,
                                 int a1, hipStream_t s);
 hipError_t launch_chunk(const Geometry &g, const ChunkWork &cw, const uint8_t *codes, const void *cbs, const float *x,
                         const int32_t *ids, const float *gates, float *y, int T, int pre, int residual, double eps,
-                        int *err, hipStream_t s);
+                        int lut_tokens, int *err, hipStream_t s);
 // slot_tab: null (resident codes: expert e's record at codes + e * rec_int) or
 // a device table [E] of record pointers (the HBM slot cache).
+// list: null, or a pair list written by the chunk path's prep (the layer then
+// evaluates exactly those pairs and leaves y's initial value to that prep).
 hipError_t launch_layer(const Geometry &g, Workspace &w, const uint8_t *codes, const uint8_t *const *slot_tab,
                         const void *cbs, const float *Wt, const float *x, const int32_t *ids, const float *gates,
-                        float *y, int T, int pre, int residual, double eps, bool route, hipStream_t s);
+                        float *y, int T, int pre, int residual, double eps, bool route, hipStream_t s,
+                        const int *list = nullptr);
 
 }  // namespace rvq

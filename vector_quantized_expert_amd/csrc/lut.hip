@@ -484,6 +484,7 @@ struct LayerArgs {
     double *sel;        // [T][k] selected logits by rank
     int *gbar;          // [4][kMaxGridGroups + 1] grid arrival counters: y init, logits, ranks, exit
     double *rl_cur, *rl_next;  // [T][E] logit slots of this launch and of the next (in-launch routing)
+    const int *list;    // pairs handed over by the chunk path (n, then the order table), or null
     const uint8_t *codes;
     const uint8_t *const *slot_tab;  // [E] record of each expert (HBM slot cache), or null: codes + e * rec
     const void *cbs;
@@ -590,12 +591,11 @@ struct SegB {
 // each expert's codes come from HBM about once per call).  Without it (one
 // token, or large P), every pair is its own group in pair order.  Every
 // workgroup derives the same table, deterministically, in LDS.
-constexpr int kOrderMax = 512;
 constexpr int kIdCache = 128;
 struct Order {
     bool tab;
     const int *info;      // [P] position -> group start | group size << 16
-    const short *pair;    // [P] position -> pair
+    const int *pair;      // [P] position -> pair
     const short *expert;  // [P] position -> expert id (may be out of range)
     // without the table: expert ids of the positions a workgroup touches
     int a_base, a_n, b_base, b_n;
@@ -629,7 +629,7 @@ struct Order {
 // Build the order table in LDS (all threads).  tmp: scratch of at least
 // (E + 1) * (kOrderMax / 64) * 8 + 2 * (E + 1) * 4 bytes (the table area, idle
 // here).  Ids outside [0, E) form a last group of their own.
-__device__ void build_order(const int32_t *ids, const int *lds_ids, int P, int E, char *tmp, int *info, short *pair,
+__device__ void build_order(const int32_t *ids, const int *lds_ids, int P, int E, char *tmp, int *info, int *pair,
                             short *expert) {
     constexpr int kW = kOrderMax / 64;
     const int NE = E + 1;
@@ -685,7 +685,7 @@ __device__ void build_order(const int32_t *ids, const int *lds_ids, int P, int E
         const int p = threadIdx.x + r * kBlock;
         if (p < P) {
             const int e = my_e[r], pos = my_pos[r];
-            pair[pos] = (short)p;
+            pair[pos] = p;
             expert[pos] = (short)e;
             info[pos] = off[e] | (cnt[e] << 16);
         }
@@ -919,8 +919,13 @@ __device__ void route_phase(const LayerArgs &a, double *scratch, float *gate_lds
     __syncthreads();
 }
 
-template <int CB, bool kRoute, bool kNT>
+// Where a launch's pairs come from: the caller's ids, the launch's own routing
+// (rvq_moe_route_forward), or a pair list handed over by the chunk path.
+enum LayerMode { kFromIds = 0, kRouted = 1, kListed = 2 };
+
+template <int CB, int kMode, bool kNT>
 __global__ __launch_bounds__(kBlock) void k_layer(LayerArgs a) {
+    constexpr bool kRoute = kMode == kRouted, kList = kMode == kListed;
     __shared__ __align__(16) float lut[kLutWords];  // also 8-byte staging (logits, order masks)
     __shared__ float vs[kVec][kTileSlices];  // [element][slice]
     __shared__ double red[kWaves];
@@ -938,7 +943,8 @@ __global__ __launch_bounds__(kBlock) void k_layer(LayerArgs a) {
     // one XCD's L2
     const int rw = (G % 8 == 0) ? (wg % 8) * (G / 8) + wg / 8 : wg;
     const int lane = threadIdx.x & 63, wave = wave_id();
-    const int P = a.T * g.k;
+    // with a handed-over pair list: exactly its pairs (its count read here)
+    const int P = kList ? __builtin_amdgcn_readfirstlane(load_counter(a.list)) : a.T * g.k;
     const int n_ti = g.m[0].n_tiles, n_cf = g.m[0].n_chunks;
     const int n_tf = g.m[2].n_tiles, n_cd = g.m[2].n_chunks;
     int r_tok = -1;
@@ -955,9 +961,10 @@ __global__ __launch_bounds__(kBlock) void k_layer(LayerArgs a) {
     // ---------------- pair order (the token x expert permutation)
     __shared__ int id_lds[2 * kIdCache];
     __shared__ int o_info[kOrderMax];
-    __shared__ short o_pair[kOrderMax], o_expert[kOrderMax];
+    __shared__ int o_pair[kOrderMax];
+    __shared__ short o_expert[kOrderMax];
     Order ord;
-    ord.tab = a.T > 1 && P <= kOrderMax;
+    ord.tab = kList || (a.T > 1 && P <= kOrderMax);
     ord.info = o_info;
     ord.pair = o_pair;
     ord.expert = o_expert;
@@ -966,7 +973,14 @@ __global__ __launch_bounds__(kBlock) void k_layer(LayerArgs a) {
     ord.all = kRoute ? pair_ids : nullptr;
     ord.a_n = ord.b_n = 0;
     ord.a_base = ord.b_base = 0;
-    if (ord.tab) {
+    if (kList) {
+        for (int i = threadIdx.x; i < P; i += kBlock) {
+            o_info[i] = a.list[1 + i];
+            o_pair[i] = a.list[1 + kOrderMax + i];
+            o_expert[i] = (short)a.list[1 + 2 * kOrderMax + i];
+        }
+        __syncthreads();
+    } else if (ord.tab) {
         build_order(a.ids, kRoute ? pair_ids : nullptr, P, g.E, reinterpret_cast<char *>(lut), o_info, o_pair,
                     o_expert);
     } else if (!kRoute) {
@@ -983,7 +997,8 @@ __global__ __launch_bounds__(kBlock) void k_layer(LayerArgs a) {
     }
 
     // ---------------- y starts as 0 (or x with the residual); phase B adds into it
-    {
+    // (with a handed-over pair list the chunk path has set it already)
+    if (!kList) {
         const int64_t n = (int64_t)a.T * g.d;
         for (int64_t i = n * wg / G + threadIdx.x; i < n * (wg + 1) / G; i += kBlock)
             store_coherent(a.y + i, a.residual ? a.x[i] : 0.f);
@@ -1138,46 +1153,51 @@ __global__ __launch_bounds__(kBlock) void k_layer(LayerArgs a) {
     if (threadIdx.x == 0) last = atomicAdd(xb, 1) == G - 1;
     __syncthreads();
     if (last) {
-        for (int i = threadIdx.x; i < P; i += kBlock) store_counter(a.cntA + i, 0);
+        for (int i = threadIdx.x; i < P; i += kBlock) store_counter(a.cntA + (kList ? o_pair[i] : i), 0);
         if (threadIdx.x < 4) store_counter(a.gbar + threadIdx.x * (kMaxGridGroups + 1) + kMaxGridGroups, 0);
     }
 }
 
 typedef void (*LayerKernel)(LayerArgs);
-static LayerKernel layer_kernel(int cb_dtype, bool route, bool nt) {
-    if (cb_dtype == 0)
-        return route ? (nt ? k_layer<0, true, true> : k_layer<0, true, false>)
-                     : (nt ? k_layer<0, false, true> : k_layer<0, false, false>);
-    return route ? (nt ? k_layer<1, true, true> : k_layer<1, true, false>)
-                 : (nt ? k_layer<1, false, true> : k_layer<1, false, false>);
+static LayerKernel layer_kernel(int cb_dtype, int mode, bool nt) {
+    if (cb_dtype == 0) {
+        if (mode == kListed) return k_layer<0, kListed, false>;
+        if (mode == kRouted) return nt ? k_layer<0, kRouted, true> : k_layer<0, kRouted, false>;
+        return nt ? k_layer<0, kFromIds, true> : k_layer<0, kFromIds, false>;
+    }
+    if (mode == kListed) return k_layer<1, kListed, false>;
+    if (mode == kRouted) return nt ? k_layer<1, kRouted, true> : k_layer<1, kRouted, false>;
+    return nt ? k_layer<1, kFromIds, true> : k_layer<1, kFromIds, false>;
 }
 
 hipError_t launch_layer(const Geometry &g, Workspace &w, const uint8_t *codes, const uint8_t *const *slot_tab,
                         const void *cbs, const float *Wt, const float *x, const int32_t *ids, const float *gates,
-                        float *y, int T, int pre, int residual, double eps, bool route, hipStream_t s) {
+                        float *y, int T, int pre, int residual, double eps, bool route, hipStream_t s,
+                        const int *list) {
     double *rl_cur = nullptr, *rl_next = nullptr;
     if (route) {  // the two slot buffers, [2][max_tokens][E], alternate between calls
         rl_cur = w.fused_logits + (w.fused_parity ? w.route_cap : 0);
         rl_next = w.fused_logits + (w.fused_parity ? 0 : w.route_cap);
         w.fused_parity ^= 1;
     }
-    LayerArgs a{Wt, w.logits, w.sel, w.gbar, rl_cur, rl_next, codes, slot_tab, cbs, x, ids, gates, y, w.part_gu, w.cntA, w.err, g, T, pre,
-                residual, eps};
+    LayerArgs a{Wt, w.logits, w.sel, w.gbar, rl_cur, rl_next, list, codes, slot_tab, cbs, x, ids, gates, y, w.part_gu,
+                w.cntA, w.err, g, T, pre, residual, eps};
     // A plain launch of exactly as many workgroups as can be resident at once
     // (sized at open from the occupancy query); the inter-workgroup waits are
     // bounded, so a launch that somehow did not get all of them resident ends
     // with an error flag instead of hanging.
-    const bool group = T > 1 && T * g.k <= kOrderMax;  // the kernel takes the same decision
-    hipLaunchKernelGGL(layer_kernel(g.cb_dtype, route, !group), dim3(w.n_wg), dim3(kBlock), 0, s, a);
+    const bool group = list || (T > 1 && T * g.k <= kOrderMax);  // the kernel takes the same decision
+    hipLaunchKernelGGL(layer_kernel(g.cb_dtype, list ? kListed : route ? kRouted : kFromIds, !group), dim3(w.n_wg),
+                       dim3(kBlock), 0, s, a);
     return hipGetLastError();
 }
 
 hipError_t layer_blocks_per_cu(int cb_dtype, int *out) {
     // the grid must be resident under every variant: take the smallest occupancy
     int best = 1 << 30;
-    for (int v = 0; v < 4; v++) {
+    for (int v = 0; v < 6; v++) {
         int n = 0;
-        const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, layer_kernel(cb_dtype, v & 1, v & 2),
+        const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, layer_kernel(cb_dtype, v >> 1, v & 1),
                                                                           kBlock, 0);
         if (e != hipSuccess) return e;
         best = n < best ? n : best;
