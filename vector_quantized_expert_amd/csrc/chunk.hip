@@ -227,12 +227,32 @@ template <int CB>
 __device__ inline bf16x8 ck_weights(const uint8_t *blk, const char *cb, int kk, int lane) {
     const int n = lane & 31, j = 2 * kk + (lane >> 5);
     const int o = (n >> 4) * 512 + j * 16 + (n & 15);
-    const f32x8 a = ck_entry<CB>(cb, 0, blk[o]);
-    const f32x8 b = ck_entry<CB>(cb, 1, blk[1024 + o]);
-    const f32x8 c = ck_entry<CB>(cb, 2, blk[2048 + o]);
     bf16x8 w;
+    if (CB == 1) {
+        // fp16 entries, summed in fp32 by mixed-precision fmas (an fp16 source
+        // times 1 plus an fp32 or fp16 addend: one instruction per add, no
+        // separate conversions), the same values as converting and adding
+        typedef unsigned int u32x4c __attribute__((ext_vector_type(4)));
+        const u32x4c a = *reinterpret_cast<const u32x4c *>(cb + blk[o] * CkCb<CB>::kEntryBytes);
+        const u32x4c b = *reinterpret_cast<const u32x4c *>(cb + (kCodes + blk[1024 + o]) * CkCb<CB>::kEntryBytes);
+        const u32x4c c = *reinterpret_cast<const u32x4c *>(cb + (2 * kCodes + blk[2048 + o]) * CkCb<CB>::kEntryBytes);
 #pragma unroll
-    for (int i = 0; i < 8; i++) w[i] = (__bf16)((a[i] + b[i]) + c[i]);
+        for (int q = 0; q < 4; q++) {
+            float lo, hi;
+            asm("v_fma_mix_f32 %0, %1, 1.0, %2 op_sel_hi:[1,0,1]" : "=v"(lo) : "v"(a[q]), "v"(b[q]));
+            asm("v_fma_mix_f32 %0, %1, 1.0, %2 op_sel:[1,0,1] op_sel_hi:[1,0,1]" : "=v"(hi) : "v"(a[q]), "v"(b[q]));
+            asm("v_fma_mix_f32 %0, %1, 1.0, %2 op_sel_hi:[1,0,0]" : "=v"(lo) : "v"(c[q]), "v"(lo));
+            asm("v_fma_mix_f32 %0, %1, 1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(hi) : "v"(c[q]), "v"(hi));
+            w[2 * q] = (__bf16)lo;
+            w[2 * q + 1] = (__bf16)hi;
+        }
+    } else {
+        const f32x8 a = ck_entry<CB>(cb, 0, blk[o]);
+        const f32x8 b = ck_entry<CB>(cb, 1, blk[1024 + o]);
+        const f32x8 c = ck_entry<CB>(cb, 2, blk[2048 + o]);
+#pragma unroll
+        for (int i = 0; i < 8; i++) w[i] = (__bf16)((a[i] + b[i]) + c[i]);
+    }
     return w;
 }
 
