@@ -30,6 +30,8 @@
 // dense weight tile never exists in LDS or HBM.
 #include <math.h>
 
+#include <type_traits>
+
 #include "internal.hpp"
 
 namespace rvq {
@@ -256,27 +258,42 @@ __device__ inline bf16x8 ck_weights(const uint8_t *blk, const char *cb, int kk, 
     return w;
 }
 
-// Stage a token tile: rows [p0, p0 + 32 * kCkMt) of the permuted bf16 matrix
-// src [P][ld], columns [c0, c0 + 256), into LDS rows of kXRow; rows at or past
-// p_end and columns at or past n_cols are zero.
-__device__ inline void ck_stage_rows(__bf16 *dst, const __bf16 *src, int ld, int p0, int p_end, int c0, int n_cols) {
-    // 16-byte pieces: 32 per row
-    for (int u = threadIdx.x; u < 32 * kCkMt * 32; u += kCkThreads) {
-        const int row = u >> 5, piece = u & 31;
-        const int p = p0 + row, col = c0 + piece * 8;
-        uint4 v = make_uint4(0, 0, 0, 0);
-        if (p < p_end) {
-            const __bf16 *s = src + (size_t)p * ld + col;
-            if (col + 8 <= n_cols) {
-                v = *reinterpret_cast<const uint4 *>(s);
-            } else if (col < n_cols) {
-                __bf16 tmp[8];
+// Stage the token tiles of a pass: rows [p0, p0 + 32 * nmt) of the permuted
+// bf16 matrix src [P][ld], columns [c0, c0 + 256), into LDS rows of kXRow;
+// rows at or past p_end and columns at or past n_cols are zero.  Every
+// thread issues all its 16-byte loads before storing any, so the tile costs
+// one round trip.
+__device__ inline void ck_stage_rows(__bf16 *dst, const __bf16 *src, int ld, int p0, int p_end, int c0, int n_cols,
+                              int nmt) {
+    constexpr int kPer = 32 * kCkMt * 32 / kCkThreads;  // 16-byte pieces per thread (32 per row)
+    typedef unsigned int w4 __attribute__((ext_vector_type(4)));
+    w4 v[kPer];
 #pragma unroll
-                for (int i = 0; i < 8; i++) tmp[i] = col + i < n_cols ? s[i] : (__bf16)0.f;
-                v = *reinterpret_cast<const uint4 *>(tmp);
+    for (int i = 0; i < kPer; i++) {
+        const int u = threadIdx.x + i * kCkThreads, row = u >> 5, piece = u & 31;
+        const int p = p0 + row, col = c0 + piece * 8;
+        v[i] = w4{0u, 0u, 0u, 0u};
+        if (row < 32 * nmt && p < p_end && col + 8 <= n_cols)
+            v[i] = *global_view(reinterpret_cast<const w4 *>(src + (size_t)p * ld + col));
+    }
+    if (c0 + kTileSlices * kVec > n_cols) {  // ragged last tile: the piece that straddles n_cols
+#pragma unroll
+        for (int i = 0; i < kPer; i++) {
+            const int u = threadIdx.x + i * kCkThreads, row = u >> 5, piece = u & 31;
+            const int p = p0 + row, col = c0 + piece * 8;
+            if (row < 32 * nmt && p < p_end && col < n_cols && col + 8 > n_cols) {
+                __bf16 tmp[8];
+                const __bf16 *s = src + (size_t)p * ld + col;
+#pragma unroll
+                for (int e = 0; e < 8; e++) tmp[e] = col + e < n_cols ? s[e] : (__bf16)0.f;
+                v[i] = *reinterpret_cast<const w4 *>(tmp);
             }
         }
-        *reinterpret_cast<uint4 *>(dst + row * kXRow + piece * 8) = v;
+    }
+#pragma unroll
+    for (int i = 0; i < kPer; i++) {
+        const int u = threadIdx.x + i * kCkThreads, row = u >> 5, piece = u & 31;
+        if (row < 32 * nmt) *reinterpret_cast<w4 *>(dst + row * kXRow + piece * 8) = v[i];
     }
 }
 
@@ -286,13 +303,19 @@ __device__ inline bf16x8 ck_tokens(const __bf16 *xs, int mt, int kk, int lane) {
     return *reinterpret_cast<const bf16x8 *>(xs + (mt * 32 + (lane & 31)) * kXRow + kk * 16 + (lane >> 5) * 8);
 }
 
-// Stage this wave's 3 KB code block in LDS (lane l: 3 x 16 bytes), or zeros.
-__device__ inline void ck_stage_codes(uint8_t *dst, const uint8_t *blk, bool valid, int lane) {
-    typedef unsigned int w4 __attribute__((ext_vector_type(4)));
-    w4 *d4 = reinterpret_cast<w4 *>(dst);
-    const auto *s4 = global_view(reinterpret_cast<const w4 *>(blk));
+// This wave's 3 KB code block (lane l: 3 x 16 bytes) into registers (zeros
+// when not valid), then into the wave's LDS staging block.  The load of the
+// next tile's block is issued before the current tile is contracted.
+typedef unsigned int ck_w4 __attribute__((ext_vector_type(4)));
+__device__ inline void ck_load_codes(ck_w4 (&r)[3], const uint8_t *blk, bool valid, int lane) {
+    const auto *s4 = global_view(reinterpret_cast<const ck_w4 *>(blk));
 #pragma unroll
-    for (int s = 0; s < 3; s++) d4[s * 64 + lane] = valid ? s4[s * 64 + lane] : w4{0u, 0u, 0u, 0u};
+    for (int s = 0; s < 3; s++) r[s] = valid ? s4[s * 64 + lane] : ck_w4{0u, 0u, 0u, 0u};
+}
+__device__ inline void ck_store_codes(uint8_t *dst, const ck_w4 (&r)[3], int lane) {
+    ck_w4 *d4 = reinterpret_cast<ck_w4 *>(dst);
+#pragma unroll
+    for (int s = 0; s < 3; s++) d4[s * 64 + lane] = r[s];
 }
 
 struct ChunkArgs {
@@ -329,22 +352,29 @@ __global__ __launch_bounds__(kCkThreads) void k_chunk_gu(ChunkArgs A) {
     ck_stage_cb<CB>(cb_lds[0], A.cbs, e, 0);
     ck_stage_cb<CB>(cb_lds[1], A.cbs, e, 1);
     const uint8_t *mat = (A.slot_tab ? A.slot_tab[e] : A.codes + (int64_t)e * g.rec_int) + mg.off;
-    for (int p0 = g0; p0 < g1; p0 += 32 * kCkMt) {
-        f32x16c acc[kCkMt];
+    // one pass per 32 * kCkMt tokens of the group; a pass with at most 32 left
+    // runs the single-tile instance (no contraction of empty token rows)
+    auto pass = [&](int p0, auto nmt_c) {
+        constexpr int nmt = decltype(nmt_c)::value;
+        f32x16c acc[nmt];
 #pragma unroll
-        for (int mt = 0; mt < kCkMt; mt++)
+        for (int mt = 0; mt < nmt; mt++)
 #pragma unroll
             for (int v = 0; v < 16; v++) acc[mt][v] = 0.f;
+        ck_w4 cr[3];
+        ck_load_codes(cr, mat + (int64_t)chunk * kChunkBytes, chunk_ok, lane);
         for (int kt = 0; kt < mg.n_tiles; kt++) {
             __syncthreads();  // previous tile's LDS reads are done
-            ck_stage_rows(xs, A.X, g.d, p0, g1, kt * kTileSlices * kVec, g.d);
-            ck_stage_codes(code_lds[wave], mat + ((int64_t)kt * mg.n_chunks + chunk) * kChunkBytes, chunk_ok, lane);
+            ck_stage_rows(xs, A.X, g.d, p0, g1, kt * kTileSlices * kVec, g.d, nmt);
+            ck_store_codes(code_lds[wave], cr, lane);
+            if (kt + 1 < mg.n_tiles)
+                ck_load_codes(cr, mat + ((int64_t)(kt + 1) * mg.n_chunks + chunk) * kChunkBytes, chunk_ok, lane);
             __syncthreads();
 #pragma unroll 2
             for (int kk = 0; kk < kTileSlices / 2; kk++) {
                 const bf16x8 w = ck_weights<CB>(code_lds[wave], cb_lds[m], kk, lane);
 #pragma unroll
-                for (int mt = 0; mt < kCkMt; mt++)
+                for (int mt = 0; mt < nmt; mt++)
                     acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ck_tokens(xs, mt, kk, lane), w, acc[mt], 0, 0,
                                                                       0);
             }
@@ -354,14 +384,14 @@ __global__ __launch_bounds__(kCkThreads) void k_chunk_gu(ChunkArgs A) {
         float *ex = reinterpret_cast<float *>(xs);  // [2 chunks][kCkMt][16][64]
         if (m == 1)
 #pragma unroll
-            for (int mt = 0; mt < kCkMt; mt++)
+            for (int mt = 0; mt < nmt; mt++)
 #pragma unroll
                 for (int v = 0; v < 16; v++) ex[(((wave & 1) * kCkMt + mt) * 16 + v) * 64 + lane] = acc[mt][v];
         __syncthreads();
         if (m == 0 && chunk_ok) {
             const int row = chunk * kChunkRows + (lane & 31);
 #pragma unroll
-            for (int mt = 0; mt < kCkMt; mt++) {
+            for (int mt = 0; mt < nmt; mt++) {
 #pragma unroll
                 for (int v = 0; v < 16; v++) {
                     const int p = p0 + mt * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
@@ -371,6 +401,12 @@ __global__ __launch_bounds__(kCkThreads) void k_chunk_gu(ChunkArgs A) {
                 }
             }
         }
+    };
+    for (int p0 = g0; p0 < g1; p0 += 32 * kCkMt) {
+        if (g1 - p0 <= 32)
+            pass(p0, std::integral_constant<int, 1>{});
+        else
+            pass(p0, std::integral_constant<int, kCkMt>{});
     }
 }
 
@@ -395,22 +431,27 @@ __global__ __launch_bounds__(kCkThreads) void k_chunk_down(ChunkArgs A) {
     ck_stage_cb<CB>(cb_lds, A.cbs, e, 2);
     const uint8_t *mat = (A.slot_tab ? A.slot_tab[e] : A.codes + (int64_t)e * g.rec_int) + mg.off;
     const int k = g.k;
-    for (int p0 = g0; p0 < g1; p0 += 32 * kCkMt) {
-        f32x16c acc[kCkMt];
+    auto pass = [&](int p0, auto nmt_c) {
+        constexpr int nmt = decltype(nmt_c)::value;
+        f32x16c acc[nmt];
 #pragma unroll
-        for (int mt = 0; mt < kCkMt; mt++)
+        for (int mt = 0; mt < nmt; mt++)
 #pragma unroll
             for (int v = 0; v < 16; v++) acc[mt][v] = 0.f;
+        ck_w4 cr[3];
+        ck_load_codes(cr, mat + (int64_t)chunk * kChunkBytes, chunk_ok, lane);
         for (int kt = 0; kt < mg.n_tiles; kt++) {
             __syncthreads();
-            ck_stage_rows(hs, A.H, g.ffn, p0, g1, kt * kTileSlices * kVec, g.ffn);
-            ck_stage_codes(code_lds[wave], mat + ((int64_t)kt * mg.n_chunks + chunk) * kChunkBytes, chunk_ok, lane);
+            ck_stage_rows(hs, A.H, g.ffn, p0, g1, kt * kTileSlices * kVec, g.ffn, nmt);
+            ck_store_codes(code_lds[wave], cr, lane);
+            if (kt + 1 < mg.n_tiles)
+                ck_load_codes(cr, mat + ((int64_t)(kt + 1) * mg.n_chunks + chunk) * kChunkBytes, chunk_ok, lane);
             __syncthreads();
 #pragma unroll 2
             for (int kk = 0; kk < kTileSlices / 2; kk++) {
                 const bf16x8 w = ck_weights<CB>(code_lds[wave], cb_lds, kk, lane);
 #pragma unroll
-                for (int mt = 0; mt < kCkMt; mt++)
+                for (int mt = 0; mt < nmt; mt++)
                     acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ck_tokens(hs, mt, kk, lane), w, acc[mt], 0, 0,
                                                                       0);
             }
@@ -418,7 +459,7 @@ __global__ __launch_bounds__(kCkThreads) void k_chunk_down(ChunkArgs A) {
         if (chunk_ok) {
             const int row = chunk * kChunkRows + (lane & 31);
 #pragma unroll
-            for (int mt = 0; mt < kCkMt; mt++) {
+            for (int mt = 0; mt < nmt; mt++) {
 #pragma unroll
                 for (int v = 0; v < 16; v++) {
                     const int p = p0 + mt * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
@@ -429,6 +470,12 @@ __global__ __launch_bounds__(kCkThreads) void k_chunk_down(ChunkArgs A) {
                 }
             }
         }
+    };
+    for (int p0 = g0; p0 < g1; p0 += 32 * kCkMt) {
+        if (g1 - p0 <= 32)
+            pass(p0, std::integral_constant<int, 1>{});
+        else
+            pass(p0, std::integral_constant<int, kCkMt>{});
     }
 }
 
