@@ -65,10 +65,10 @@ typedef enum rvq_moe_status {
 
 /* Default chunk-path threshold (tokens per layer_forward call): where the
  * chunk path (with the default adaptive dispatch below) overtakes the table
- * path for d=7168, ffn=2048, E=384, top-16 on one MI355X (64 tokens: table
- * 3.08 ms, chunk 3.03 ms; 80 tokens: table 3.86 ms, chunk 3.67 ms; 48 tokens:
- * table 2.35 ms, chunk 2.46 ms).  Other shapes may set their own. */
-#define RVQ_MOE_CHUNK_MIN_TOKENS 72
+ * path for d=7168, ffn=2048, E=384, top-16 on one MI355X (32 tokens: table
+ * 1.53 ms, chunk 1.61 ms; 48 tokens: table 2.35 ms, chunk 2.23 ms; 64 tokens:
+ * table 3.08 ms, chunk 2.73 ms).  Other shapes may set their own. */
+#define RVQ_MOE_CHUNK_MIN_TOKENS 40
 
 /* Default of lut_expert_tokens (see rvq_moe_desc): the best of 3..6 measured
  * at that shape (96 tokens per call: 4.05 ms against 4.97 ms with every expert

@@ -89,7 +89,7 @@ def tiny(torch_mod):
 
 def test_tiny_layer_64_tokens(torch_mod, tiny):
     shape = S.TINY
-    layer = _layer(torch_mod, tiny, shape, 64)
+    layer = _layer(torch_mod, tiny, shape, 64, chunk_min_tokens=65)  # the table path
     x = S.tokens(0, 0, 64, shape.d)
     ids, gates, y = _run(torch_mod, layer, shape, x)
     worst = _check(tiny, shape, x, ids, gates, y)
