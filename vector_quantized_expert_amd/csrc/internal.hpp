@@ -134,7 +134,6 @@ struct ChunkWork {
 constexpr int kOrderMax = 512;
 constexpr int kPairListInts = 1 + 3 * kOrderMax;
 
-constexpr int kRouteTok = 8;       // tokens per router workgroup when T > 1
 constexpr int kMaxExperts = 1024;
 constexpr int kMaxTopK = 64;
 constexpr int kRouteMaxPairs = 1024;

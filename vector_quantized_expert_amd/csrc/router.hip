@@ -1,4 +1,4 @@
-// router.hip -- router GEMV and top-k gates in one launch.
+// router.hip -- router logits, top-k and softmax gates.
 //
 // [FR] "Lecture anticipée et prédiction du routeur": a layer's router decides
 // the token's expert ids (16 for K3) and the expert reads start from them.  The
@@ -13,17 +13,17 @@
 // (sum_i x_i W[i][e]) / r with r = sqrt(mean(x^2) + eps) computed in fp64,
 // equal in exact arithmetic to sum_i (x_i / r) W[i][e].
 //
-// MI355X mapping: one launch.  The router matrix is stored transposed ([E][d])
-// so that a workgroup streams one expert's column as contiguous 1 KB wave
-// loads (its 4 waves take a quarter each) for up to TT tokens.  Each workgroup
-// publishes its logits and then raises its own flag (the call's epoch number:
-// no counter, so no atomics serialised on one address); workgroup 0 of a token
-// block waits for the block's E flags and selects for those tokens while the
-// rest have already exited.
-// Selection avoids a serial chain of k argmax rounds: every expert's rank is
-// counted in parallel (the experts ahead of it in the order), and the k with
-// rank < k write their id to that slot; then the k gates.  Wave reductions use
-// DPP row moves and permlane swaps (no LDS round trips).
+// MI355X mapping.  The router matrix is stored transposed ([E][d]).
+//   One token (decode): one launch of E workgroups, each streaming one
+//   expert's row as contiguous wave loads; every workgroup publishes its
+//   logit into a slot that holds a marker value, polls the E slots, and ranks
+//   its own expert (the experts ahead of it in the order); the k with rank < k
+//   publish their logit by rank, poll those k, and write id and gate.
+//   Several tokens: the logits are a dense [T][d] x [d][E] contraction, done
+//   in fp64 on the matrix cores (16 x 16 tiles); then one workgroup per token
+//   selects its k (radix select over order-preserving 64-bit keys) and forms
+//   the gates.
+// Wave reductions use DPP row moves and permlane swaps (no LDS round trips).
 #include <math.h>
 
 #include "internal.hpp"
@@ -347,67 +347,91 @@ __device__ void router_dot(const float *__restrict__ x, const float *__restrict_
     __syncthreads();
 }
 
-// Several tokens: grid (E, ceil(T / TT)), 256 threads.  Workgroup (e, by)
-// stores its logits into slots that hold kUnpublished and exits; workgroup
-// (0, by) polls the block's slots until every logit is in (a bounded wait:
-// ~0.5 s, then err bit 2, so every workgroup always ends), selects, and puts
-// kUnpublished back for the next call.  No counters, so no atomics serialised
-// on one address, and the poll reads the logits themselves.
-template <int TT>
-__global__ __launch_bounds__(256) void k_route(const float *__restrict__ x, const float *__restrict__ Wt, int d, int E,
-                                               int k, int T, int pre, double eps, double *__restrict__ logits,
-                                               int *__restrict__ err, int32_t *__restrict__ ids,
-                                               float *__restrict__ gates) {
-    const int e = blockIdx.x;
-    const int t0 = blockIdx.y * TT;
-    const int nt = min(TT, T - t0);
-    __shared__ double lgt[TT];
-    router_dot<TT>(x, Wt, d, t0, nt, pre, eps, lgt);
-    if (threadIdx.x < nt) store_coherent(logits + (size_t)(t0 + threadIdx.x) * E + e, lgt[threadIdx.x]);
-    if (e != 0) return;
+// Several tokens, step 1: the logits as a dense fp64 contraction on the
+// matrix cores, L[t][e] = sum_i x[t][i] Wt[e][i] with v_mfma_f64_16x16x4_f64
+// (fp32 inputs widened exactly, so every product is exact; fp64 sums).  Grid
+// (ceil(E / 16), ceil(T / 16)), 256 threads: wave w takes a quarter of the
+// 16-wide input blocks of one 16 token x 16 expert tile and the four partial
+// tiles are summed in wave order.  Operands: lane l = 16 q + r loads 4
+// consecutive inputs 16 b + 4 q .. + 3 of token row r and of expert row r;
+// MFMA step j pairs the j-th of them (A[r][q] = x, B[q][r] = w), so the four
+// steps of a block cover its 16 inputs once.  The accumulator v of lane l is
+// D[q + 4 v][r] (token q + 4 v, expert r; measured on gfx950).  Rows past T or
+// E are clamped on load and dropped on store.
+typedef double f64x4 __attribute__((ext_vector_type(4)));
+__global__ __launch_bounds__(256) void k_route_mm(const float *__restrict__ x, const float *__restrict__ Wt, int d,
+                                                  int E, int T, double *__restrict__ logits) {
+    const int e0 = blockIdx.x * 16, t0 = blockIdx.y * 16;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, r = lane & 15, q = lane >> 4;
+    const float *xr = x + (size_t)min(t0 + r, T - 1) * d;
+    const float *wr = Wt + (size_t)min(e0 + r, E - 1) * d;
+    const int nb = (d + 15) / 16, b0 = nb * wave / 4, b1 = nb * (wave + 1) / 4;
+    f64x4 acc = {0.0, 0.0, 0.0, 0.0};
+    constexpr int kU = 4;  // blocks per pass, loads in flight together
+    for (int b = b0; b < b1; b += kU) {
+        float4 xv[kU], wv[kU];
+#pragma unroll
+        for (int u = 0; u < kU; u++) {
+            const int i = (b + u) * 16 + 4 * q;
+            const bool ok = b + u < b1 && i < d;  // d % 8 == 0: a 4-aligned start below d has all 4 below d
+            xv[u] = ok ? *reinterpret_cast<const float4 *>(xr + i) : make_float4(0.f, 0.f, 0.f, 0.f);
+            wv[u] = ok ? *reinterpret_cast<const float4 *>(wr + i) : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+#pragma unroll
+        for (int u = 0; u < kU; u++) {
+            acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)xv[u].x, (double)wv[u].x, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)xv[u].y, (double)wv[u].y, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)xv[u].z, (double)wv[u].z, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)xv[u].w, (double)wv[u].w, acc, 0, 0, 0);
+        }
+    }
+    __shared__ double part[4][16][17];  // [wave][token][expert], padded
+#pragma unroll
+    for (int v = 0; v < 4; v++) part[wave][q + 4 * v][r] = acc[v];
+    __syncthreads();
+    const int tt = threadIdx.x >> 4, ee = threadIdx.x & 15;  // 256 threads = the 16 x 16 tile
+    if (t0 + tt < T && e0 + ee < E)
+        logits[(size_t)(t0 + tt) * E + e0 + ee] = ((part[0][tt][ee] + part[1][tt][ee]) + part[2][tt][ee]) +
+                                                  part[3][tt][ee];
+}
 
-    // ---- workgroup (0, by): wait for the block's logits, select, gates
+// Several tokens, step 2: grid (T), 256 threads, one token each.  Divides the
+// token's logits by its RMS divisor (fp64, when normalising), selects the k
+// largest (ties to the lower id) and forms the softmax gates over them (one exp
+// per selected logit, summed in slot order).
+__global__ __launch_bounds__(256) void k_route_sel(const float *__restrict__ x, int d, int E, int k, int pre,
+                                                   double eps, const double *__restrict__ logits,
+                                                   int32_t *__restrict__ ids, float *__restrict__ gates) {
+    const int t = blockIdx.x;
     __shared__ SelectLds L;
     __shared__ double sel[kMaxTopK];
     __shared__ double ex[kMaxTopK];
-    const uint64_t t_start = wall_clock64();
-    for (int t = t0; t < t0 + nt; t++) {
-        double *lt = logits + (size_t)t * E;
-        double v[kSelPer];
-        while (true) {
-            int ready = 1;
-#pragma unroll
-            for (int r = 0; r < kSelPer; r++) {
-                const int i = threadIdx.x + 256 * r;
-                v[r] = i < E ? load_coherent(lt + i) : -INFINITY;
-                ready &= (uint64_t)__double_as_longlong(v[r]) != kUnpublished;
-            }
-            if (__syncthreads_and(ready)) break;
-            if (wall_clock64() - t_start > 50000000ull) {  // 0.5 s at the 100 MHz constant clock
-                if (threadIdx.x == 0) atomicOr(err, 2);
-                break;
-            }
-            __builtin_amdgcn_s_sleep(1);
-        }
-        uint64_t key[kSelPer];
-#pragma unroll
-        for (int r = 0; r < kSelPer; r++) {
-            const int i = threadIdx.x + 256 * r;
-            if (i < E) store_coherent(lt + i, __longlong_as_double((long long)kUnpublished));  // for the next call
-            v[r] = rank_value(v[r]);
-            key[r] = order_key(v[r]);
-        }
-        select_topk(key, v, E, k, L, ids + (size_t)t * k, sel);
-        // softmax over the k selected logits (slot 0 is the largest), fp64: one
-        // exp per selected logit, summed in slot order
-        if (threadIdx.x < k) ex[threadIdx.x] = exp(sel[threadIdx.x] - sel[0]);
+    __shared__ double red[4];
+    double rdiv = 1.0;
+    if (pre) {
+        const float *xt = x + (size_t)t * d;
+        double ss = 0.0;
+        for (int i = threadIdx.x; i < d; i += 256) ss = fma((double)xt[i], (double)xt[i], ss);
+        ss = wave_sum(ss);
+        if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
         __syncthreads();
-        if (threadIdx.x < k) {
-            double sum = 0.0;
-            for (int j = 0; j < k; j++) sum += ex[j];
-            gates[(size_t)t * k + threadIdx.x] = (float)(ex[threadIdx.x] / sum);
-        }
-        __syncthreads();
+        rdiv = sqrt((red[0] + red[1] + red[2] + red[3]) / (double)d + eps);
+    }
+    double v[kSelPer];
+    uint64_t key[kSelPer];
+#pragma unroll
+    for (int r = 0; r < kSelPer; r++) {
+        const int i = threadIdx.x + 256 * r;
+        v[r] = rank_value(i < E ? logits[(size_t)t * E + i] / rdiv : -INFINITY);
+        key[r] = order_key(v[r]);
+    }
+    select_topk(key, v, E, k, L, ids + (size_t)t * k, sel);
+    if (threadIdx.x < k) ex[threadIdx.x] = exp(sel[threadIdx.x] - sel[0]);
+    __syncthreads();
+    if (threadIdx.x < k) {
+        double sum = 0.0;
+        for (int j = 0; j < k; j++) sum += ex[j];
+        gates[(size_t)t * k + threadIdx.x] = (float)(ex[threadIdx.x] / sum);
     }
 }
 
@@ -507,8 +531,13 @@ hipError_t launch_route(const Geometry &g, Workspace &w, const float *x, const f
         hipLaunchKernelGGL(k_route_one, dim3(g.E), dim3(256), 0, s, x, Wt, g.d, g.E, g.k, pre, eps, lg[p], lg[p ^ 1],
                            sl[p], sl[p ^ 1], w.err, ids, gates);
     } else {
-        hipLaunchKernelGGL(k_route<kRouteTok>, dim3(g.E, (T + kRouteTok - 1) / kRouteTok), dim3(256), 0, s, x, Wt,
-                           g.d, g.E, g.k, T, pre, eps, w.route_logits, w.err, ids, gates);
+        // the logits area of the several-token path: plain values, handed from
+        // the contraction to the selection across the launch boundary
+        double *lg = w.route_logits;  // [T][E]
+        hipLaunchKernelGGL(k_route_mm, dim3((g.E + 15) / 16, (T + 15) / 16), dim3(256), 0, s, x, Wt, g.d, g.E, T, lg);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(k_route_sel, dim3(T), dim3(256), 0, s, x, g.d, g.E, g.k, pre, eps, lg, ids, gates);
     }
     return hipGetLastError();
 }
