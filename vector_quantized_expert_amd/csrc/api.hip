@@ -153,7 +153,7 @@ static int open_impl(const rvq_moe_desc *desc, rvq_moe *h) {
     HIP_TRY(hipMalloc(&h->ws.logits, sizeof(double) * (size_t)(T * E)));
     HIP_TRY(hipMalloc(&h->ws.sel, sizeof(double) * (size_t)(T * D.top_k)));
     HIP_TRY(hipMalloc(&h->ws.route_logits, sizeof(double) * (size_t)route_logit_slots(T, D.n_experts)));
-    HIP_TRY(hipMalloc(&h->ws.fused_logits, sizeof(double) * 2 * (size_t)(T * E)));
+    HIP_TRY(hipMalloc(&h->ws.fused_logits, sizeof(double) * (size_t)fused_route_slots(T, D.n_experts, D.top_k)));
     HIP_TRY(hipMalloc(&h->ws.part_gu, sizeof(float) * (size_t)(P * 2 * g.m[0].n_tiles * g.ffn_pad)));
     HIP_TRY(hipMalloc(&h->ws.cntA, sizeof(int) * (size_t)P));
     HIP_TRY(hipMalloc(&h->ws.gbar, sizeof(int) * kGbarInts));
@@ -172,7 +172,7 @@ static int open_impl(const rvq_moe_desc *desc, rvq_moe *h) {
     int per_cu = 0;
     HIP_TRY(layer_blocks_per_cu(D.codebook_dtype, &per_cu));
     if (n_cu < 1 || per_cu < 1) return fail(RVQ_MOE_EHIP, "occupancy query gave %d CUs x %d blocks", n_cu, per_cu);
-    HIP_TRY(init_route(h->ws, D.n_experts, T, n_cu, s));
+    HIP_TRY(init_route(h->ws, D.n_experts, D.top_k, T, n_cu, s));
     h->ws.n_wg = n_cu * per_cu;
     if (h->ws.n_wg > 1024) h->ws.n_wg = 1024;  // grid arrival counters cover up to 1024 workgroups
     HIP_TRY(hipMemsetAsync(h->ws.cntA, 0, sizeof(int) * (size_t)P, s));

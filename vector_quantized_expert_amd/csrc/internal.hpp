@@ -91,6 +91,48 @@ __device__ __forceinline__ const __attribute__((address_space(1))) T *global_vie
     return (const __attribute__((address_space(1))) T *)p;
 }
 
+// Wave-wide sums without LDS round trips: DPP quad and row moves inside each
+// 16-lane row, then 16- and 32-lane permlane swaps.
+#define RVQ_DPP_U(v, ctrl) __builtin_amdgcn_update_dpp(0u, (v), (ctrl), 0xF, 0xF, true)
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppRor4 = 0x124, kDppRor8 = 0x128;
+
+__device__ inline double dpp_d(double v, int step) {
+    const uint64_t b = __double_as_longlong(v);
+    uint32_t lo = (uint32_t)b, hi = (uint32_t)(b >> 32);
+    switch (step) {
+        case 0: lo = RVQ_DPP_U(lo, kDppXor1); hi = RVQ_DPP_U(hi, kDppXor1); break;
+        case 1: lo = RVQ_DPP_U(lo, kDppXor2); hi = RVQ_DPP_U(hi, kDppXor2); break;
+        case 2: lo = RVQ_DPP_U(lo, kDppRor4); hi = RVQ_DPP_U(hi, kDppRor4); break;
+        default: lo = RVQ_DPP_U(lo, kDppRor8); hi = RVQ_DPP_U(hi, kDppRor8); break;
+    }
+    return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
+// The other row's value after a 16-lane (rows 0<->1, 2<->3) or 32-lane swap.
+__device__ inline uint32_t swap_other(uint32_t v, bool wide, bool odd) {
+    if (wide) {
+        auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+        return odd ? r[0] : r[1];
+    }
+    auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    return odd ? r[0] : r[1];
+}
+
+__device__ inline double wave_sum(double v) {
+#pragma unroll
+    for (int st = 0; st < 4; st++) v += dpp_d(v, st);  // every lane: sum of its row of 16
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int w = 0; w < 2; w++) {
+        const bool odd = w ? (lane & 32) : (lane & 16);
+        const uint64_t b = __double_as_longlong(v);
+        const uint32_t lo = swap_other((uint32_t)b, w, odd), hi = swap_other((uint32_t)(b >> 32), w, odd);
+        v += __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+    }
+    return v;  // identical in every lane
+}
+
+
 // Logit slots hold this NaN until written.  It is a signalling NaN, which no
 // arithmetic result is (results are quiet NaNs at most), so a slot holds it
 // exactly while its logit is not yet published.
@@ -106,7 +148,7 @@ struct Workspace {
                            // selected logits for one token (alternating buffers)
     int64_t route_cap;     // max_tokens * E
     int route_parity;      // buffer of the next one-token call
-    double *fused_logits;  // [2][max_tokens][E] logit slots of the in-launch routing (marker NaN when unpublished)
+    double *fused_logits;  // in-launch routing slots, fused_route_slots() doubles (marker NaN when unpublished)
     int fused_parity;      // buffer of the next in-launch routing
     bool route_one;        // the one-token kernel fits (all E workgroups resident)
     float *part_gu;     // [T*k][2][n_tiles_in][ffn_pad] partial gate/up sums
@@ -144,7 +186,11 @@ hipError_t launch_repack(const Geometry &g, const uint8_t *canon, uint8_t *inter
                          hipStream_t s);
 hipError_t launch_transpose(const float *W, float *Wt, int d, int E, hipStream_t s);
 int64_t route_logit_slots(int64_t max_tokens, int E);
-hipError_t init_route(Workspace &w, int E, int64_t max_tokens, int n_cu, hipStream_t s);
+// In-launch routing slots (rvq_moe_route_forward), all doubles: logits
+// [2][max_tokens][E], then selected logits [2][max_tokens * k], then the
+// selected ids [2][max_tokens * k]; the first two hold the marker until written.
+inline int64_t fused_route_slots(int64_t max_tokens, int E, int k) { return 2 * max_tokens * E + 4 * max_tokens * k; }
+hipError_t init_route(Workspace &w, int E, int k, int64_t max_tokens, int n_cu, hipStream_t s);
 hipError_t launch_route(const Geometry &g, Workspace &w, const float *x, const float *Wt, int T, int pre,
                         double eps, int32_t *ids, float *gates, hipStream_t s);
 hipError_t layer_blocks_per_cu(int cb_dtype, int *out);

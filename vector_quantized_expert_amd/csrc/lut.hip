@@ -484,6 +484,8 @@ struct LayerArgs {
     double *sel;        // [T][k] selected logits by rank
     int *gbar;          // [4][kMaxGridGroups + 1] grid arrival counters: y init, logits, ranks, exit
     double *rl_cur, *rl_next;  // [T][E] logit slots of this launch and of the next (in-launch routing)
+    double *sl_cur, *sl_next;  // [T * k] selected-logit slots of this launch and of the next
+    double *si_cur;            // [T * k] selected ids of this launch (announced by the logit slot)
     const int *list;    // pairs handed over by the chunk path (n, then the order table), or null
     const uint8_t *codes;
     const uint8_t *const *slot_tab;  // [E] record of each expert (HBM slot cache), or null: codes + e * rec
@@ -781,20 +783,22 @@ __device__ inline SegB next_b(const SegB &c, int un, int u1, int n_tf, int n_cd,
 // Routing inside the launch (rvq_moe_route_forward).  [FR] "Lecture anticipée
 // et prédiction du routeur": the router decides the token's experts; reading
 // as in the separate route kernels: top-k of fp64 logits, ties to the lower
-// id, softmax over the k.  No grid barrier and no counter:
-//  R1  logits of experts e = wg, wg + G, ... (all of them in one pass) for every
-//      token: fp64 sums of exact fp32 products, divided by the fp64 RMS
-//      divisor when normalising; each is stored into its slot of buffer `cur`,
-//      which holds the marker NaN until then, and the workgroup's slots of the
-//      other buffer get the marker back for the next call;
-//  R2  every workgroup polls a token's E slots until none holds the marker
-//      (the poll reads the logits themselves), ranks every expert in LDS
-//      (thread i counts the experts ahead of expert i), keeps the first k as
-//      pair ids and selected logits, and forms the gates (one exp each, summed
-//      in slot order).  Workgroup 0 writes ids and gates out.
-// Every workgroup thus holds the ids in LDS: no global read-back of them.
-constexpr int kRouteExp = 4;   // experts per workgroup in one pass (E <= 4 G)
-constexpr int kRankParts = 8;  // slices of the rank count per expert
+// id, softmax over the k.  No grid barrier and no counter; workgroup wg owns
+// experts wg, wg + G, ... (at most kRouteExp):
+//  R1  the logits of its experts for every token (fp64 sums of exact fp32
+//      products, wave sums by DPP, divided by the fp64 RMS divisor when
+//      normalising), each stored into its slot of buffer `cur`, which holds the
+//      marker NaN until then; its slots of the other buffer get the marker back
+//      for the next call;
+//  R2  per token, it polls the E logit slots until none holds the marker (the
+//      poll reads the logits themselves) and ranks each of its own experts (one
+//      comparison per thread, counted by the barrier); an expert of rank < k
+//      publishes its id, then (after its store completed) its logit, into
+//      selection slot [token][rank];
+//  R3  every workgroup polls the k selection slots of every token, takes ids
+//      and selected logits in rank order into LDS, and forms the gates (one exp
+//      each, summed in slot order).  Workgroup 0 writes ids and gates out.
+constexpr int kRouteExp = 4;  // experts per workgroup (E <= 4 G)
 __device__ void route_phase(const LayerArgs &a, double *scratch, float *gate_lds, int *pair_ids) {
     const Geometry &g = a.g;
     const int G = gridDim.x, wg = blockIdx.x;
@@ -805,64 +809,69 @@ __device__ void route_phase(const LayerArgs &a, double *scratch, float *gate_lds
     double *sel = scratch + kMaxExperts;  // [P] selected logits by rank
     double *ex = sel + kRouteMaxPairs;    // [P] exps
     double *red = ex + kRouteMaxPairs;    // [kWaves][kRouteExp + 1]
-    int *rank_cnt = reinterpret_cast<int *>(red + kWaves * (kRouteExp + 1));  // [E]
+    const int P = a.T * g.k;
+    // ---- R1
     for (int t = 0; t < a.T; t++) {
         const float4 *x4 = reinterpret_cast<const float4 *>(a.x + (size_t)t * g.d);
-        for (int e0 = wg; e0 < g.E; e0 += G * kRouteExp) {
-            double acc[kRouteExp], ss = 0.0;
+        double acc[kRouteExp], ss = 0.0;
 #pragma unroll
-            for (int j = 0; j < kRouteExp; j++) acc[j] = 0.0;
-            for (int i = threadIdx.x; i < n4; i += kBlock) {
-                // loads for all experts are unconditional (a clamped expert index,
-                // dropped at use), so they are in flight together
-                const float4 xv = x4[i];
-                float4 wv[kRouteExp];
+        for (int j = 0; j < kRouteExp; j++) acc[j] = 0.0;
+        for (int i = threadIdx.x; i < n4; i += kBlock) {
+            // loads for all experts are unconditional (a clamped expert index,
+            // dropped at use), so they are in flight together
+            const float4 xv = x4[i];
+            float4 wv[kRouteExp];
 #pragma unroll
-                for (int j = 0; j < kRouteExp; j++)
-                    wv[j] = reinterpret_cast<const float4 *>(a.Wt + (size_t)min(e0 + j * G, g.E - 1) * g.d)[i];
-                if (a.pre) {
-                    ss = fma((double)xv.x, (double)xv.x, ss);
-                    ss = fma((double)xv.y, (double)xv.y, ss);
-                    ss = fma((double)xv.z, (double)xv.z, ss);
-                    ss = fma((double)xv.w, (double)xv.w, ss);
-                }
-#pragma unroll
-                for (int j = 0; j < kRouteExp; j++) {
-                    acc[j] = fma((double)xv.x, (double)wv[j].x, acc[j]);
-                    acc[j] = fma((double)xv.y, (double)wv[j].y, acc[j]);
-                    acc[j] = fma((double)xv.z, (double)wv[j].z, acc[j]);
-                    acc[j] = fma((double)xv.w, (double)wv[j].w, acc[j]);
-                }
+            for (int j = 0; j < kRouteExp; j++)
+                wv[j] = reinterpret_cast<const float4 *>(a.Wt + (size_t)min(wg + j * G, g.E - 1) * g.d)[i];
+            if (a.pre) {
+                ss = fma((double)xv.x, (double)xv.x, ss);
+                ss = fma((double)xv.y, (double)xv.y, ss);
+                ss = fma((double)xv.z, (double)xv.z, ss);
+                ss = fma((double)xv.w, (double)xv.w, ss);
             }
 #pragma unroll
-            for (int o = 32; o > 0; o >>= 1) {
-                ss += __shfl_xor(ss, o);
-#pragma unroll
-                for (int j = 0; j < kRouteExp; j++) acc[j] += __shfl_xor(acc[j], o);
+            for (int j = 0; j < kRouteExp; j++) {
+                acc[j] = fma((double)xv.x, (double)wv[j].x, acc[j]);
+                acc[j] = fma((double)xv.y, (double)wv[j].y, acc[j]);
+                acc[j] = fma((double)xv.z, (double)wv[j].z, acc[j]);
+                acc[j] = fma((double)xv.w, (double)wv[j].w, acc[j]);
             }
-            if (lane == 0) {
-#pragma unroll
-                for (int j = 0; j < kRouteExp; j++) red[wave * (kRouteExp + 1) + j] = acc[j];
-                red[wave * (kRouteExp + 1) + kRouteExp] = ss;
-            }
-            __syncthreads();
-            if (threadIdx.x < kRouteExp) {
-                const int j = threadIdx.x, e = e0 + j * G;
-                double sa = 0.0, sq = 0.0;
-                for (int w = 0; w < kWaves; w++) {
-                    sa += red[w * (kRouteExp + 1) + j];
-                    sq += red[w * (kRouteExp + 1) + kRouteExp];
-                }
-                const double r = a.pre ? sqrt(sq / (double)g.d + a.eps) : 1.0;
-                if (e < g.E) {
-                    store_coherent(a.rl_cur + (size_t)t * g.E + e, sa / r);
-                    store_coherent(a.rl_next + (size_t)t * g.E + e, unpub);
-                }
-            }
-            __syncthreads();
         }
+#pragma unroll
+        for (int j = 0; j < kRouteExp; j++) acc[j] = wave_sum(acc[j]);
+        if (a.pre) ss = wave_sum(ss);
+        if (lane == 0) {
+#pragma unroll
+            for (int j = 0; j < kRouteExp; j++) red[wave * (kRouteExp + 1) + j] = acc[j];
+            red[wave * (kRouteExp + 1) + kRouteExp] = ss;
+        }
+        __syncthreads();
+        if (threadIdx.x < kRouteExp) {
+            const int j = threadIdx.x, e = wg + j * G;
+            double sa = 0.0, sq = 0.0;
+            for (int w = 0; w < kWaves; w++) {
+                sa += red[w * (kRouteExp + 1) + j];
+                sq += red[w * (kRouteExp + 1) + kRouteExp];
+            }
+            const double r = a.pre ? sqrt(sq / (double)g.d + a.eps) : 1.0;
+            if (e < g.E) {
+                store_coherent(a.rl_cur + (size_t)t * g.E + e, sa / r);
+                store_coherent(a.rl_next + (size_t)t * g.E + e, unpub);
+            }
+        }
+        __syncthreads();
     }
+    // ---- R2
     const uint64_t t_start = wall_clock64();
+    auto timed_out = [&]() {
+        if (wall_clock64() - t_start > 50000000ull) {  // 0.5 s at the 100 MHz constant clock
+            if (threadIdx.x == 0) atomicOr(a.err, 2);
+            return true;
+        }
+        __builtin_amdgcn_s_sleep(1);
+        return false;
+    };
     for (int t = 0; t < a.T; t++) {
         while (true) {
             int ready = 1;
@@ -871,38 +880,34 @@ __device__ void route_phase(const LayerArgs &a, double *scratch, float *gate_lds
                 ready &= (uint64_t)__double_as_longlong(v) != kUnpublished;
                 lg[i] = isnan(v) ? -INFINITY : v;
             }
-            if (__syncthreads_and(ready)) break;
-            if (wall_clock64() - t_start > 50000000ull) {  // 0.5 s at the 100 MHz constant clock
-                if (threadIdx.x == 0) atomicOr(a.err, 2);
-                break;
-            }
-            __builtin_amdgcn_s_sleep(1);
+            if (__syncthreads_and(ready) || timed_out()) break;
         }
-        // rank of expert i = the experts ahead of it, counted in kRankParts
-        // slices by different threads and summed with LDS atomics
-        for (int i = threadIdx.x; i < g.E; i += kBlock) rank_cnt[i] = 0;
-        __syncthreads();
-        for (int w = threadIdx.x; w < g.E * kRankParts; w += kBlock) {
-            const int i = w / kRankParts, part = w % kRankParts;
-            const double me = lg[i];
-            int c = 0;
-            for (int j = g.E * part / kRankParts; j < g.E * (part + 1) / kRankParts; j++) {
-                const double o = lg[j];
-                c += (o > me || (o == me && j < i)) ? 1 : 0;
-            }
-            if (c) atomicAdd(&rank_cnt[i], c);
-        }
-        __syncthreads();
-        for (int i = threadIdx.x; i < g.E; i += kBlock) {
-            const int rank = rank_cnt[i];
-            if (rank < g.k) {
-                pair_ids[t * g.k + rank] = i;
-                sel[t * g.k + rank] = lg[i];
+        for (int j = 0; j < kRouteExp; j++) {  // uniform: the same own experts in every thread
+            const int e = wg + j * G;
+            if (e >= g.E) break;
+            const double me = lg[e];
+            const int i = threadIdx.x;  // E <= kMaxExperts = kBlock: one comparison per thread
+            const int rank = __syncthreads_count(i < g.E && (lg[i] > me || (lg[i] == me && i < e)));
+            if (rank < g.k && threadIdx.x == 0) {
+                const int slot = t * g.k + rank;
+                store_coherent(a.si_cur + slot, (double)e);
+                wait_stores();  // the id lands before the logit that announces it
+                store_coherent(a.sl_cur + slot, me);
+                store_coherent(a.sl_next + slot, unpub);
             }
         }
-        __syncthreads();
     }
-    const int P = a.T * g.k;
+    // ---- R3
+    while (true) {
+        int ready = 1;
+        for (int i = threadIdx.x; i < P; i += kBlock) {
+            const double v = load_coherent(a.sl_cur + i);
+            ready &= (uint64_t)__double_as_longlong(v) != kUnpublished;
+            sel[i] = v;
+        }
+        if (__syncthreads_and(ready) || timed_out()) break;
+    }
+    for (int i = threadIdx.x; i < P; i += kBlock) pair_ids[i] = (int)load_coherent(a.si_cur + i);
     for (int i = threadIdx.x; i < P; i += kBlock) ex[i] = exp(sel[i] - sel[(i / g.k) * g.k]);
     __syncthreads();
     for (int i = threadIdx.x; i < P; i += kBlock) {
@@ -929,10 +934,10 @@ __global__ __launch_bounds__(kBlock) void k_layer(LayerArgs a) {
     __shared__ __align__(16) float lut[kLutWords];  // also 8-byte staging (logits, order masks)
     __shared__ float vs[kVec][kTileSlices];  // [element][slice]
     __shared__ double red[kWaves];
-    static_assert((kMaxExperts + 2 * kRouteMaxPairs + kWaves * (kRouteExp + 1)) * sizeof(double) +
-                          kMaxExperts * sizeof(int) <=
+    static_assert((kMaxExperts + 2 * kRouteMaxPairs + kWaves * (kRouteExp + 1)) * sizeof(double) <=
                       kLutWords * sizeof(float),
                   "routing scratch must fit the table area");
+    static_assert(kMaxExperts <= kBlock, "one rank comparison per thread");
     __shared__ float hred[4][256][2];
     __shared__ float red2[kWaves];
     const Geometry &g = a.g;
@@ -1174,14 +1179,19 @@ hipError_t launch_layer(const Geometry &g, Workspace &w, const uint8_t *codes, c
                         const void *cbs, const float *Wt, const float *x, const int32_t *ids, const float *gates,
                         float *y, int T, int pre, int residual, double eps, bool route, hipStream_t s,
                         const int *list) {
-    double *rl_cur = nullptr, *rl_next = nullptr;
-    if (route) {  // the two slot buffers, [2][max_tokens][E], alternate between calls
-        rl_cur = w.fused_logits + (w.fused_parity ? w.route_cap : 0);
-        rl_next = w.fused_logits + (w.fused_parity ? 0 : w.route_cap);
+    double *rl_cur = nullptr, *rl_next = nullptr, *sl_cur = nullptr, *sl_next = nullptr, *si_cur = nullptr;
+    if (route) {  // the slot buffers (see fused_route_slots) alternate between calls
+        const int64_t cap = w.route_cap, P = cap / g.E * g.k;
+        const int par = w.fused_parity;
+        rl_cur = w.fused_logits + (par ? cap : 0);
+        rl_next = w.fused_logits + (par ? 0 : cap);
+        sl_cur = w.fused_logits + 2 * cap + (par ? P : 0);
+        sl_next = w.fused_logits + 2 * cap + (par ? 0 : P);
+        si_cur = w.fused_logits + 2 * cap + 2 * P + (par ? P : 0);
         w.fused_parity ^= 1;
     }
-    LayerArgs a{Wt, w.logits, w.sel, w.gbar, rl_cur, rl_next, list, codes, slot_tab, cbs, x, ids, gates, y, w.part_gu,
-                w.cntA, w.err, g, T, pre, residual, eps};
+    LayerArgs a{Wt, w.logits, w.sel, w.gbar, rl_cur, rl_next, sl_cur, sl_next, si_cur, list, codes, slot_tab, cbs, x,
+                ids, gates, y, w.part_gu, w.cntA, w.err, g, T, pre, residual, eps};
     // A plain launch of exactly as many workgroups as can be resident at once
     // (sized at open from the occupancy query); the inter-workgroup waits are
     // bounded, so a launch that somehow did not get all of them resident ends

@@ -56,45 +56,6 @@ hipError_t launch_transpose(const float *W, float *Wt, int d, int E, hipStream_t
 // ---------------------------------------------------------------------------
 // Wave64 cross-lane moves without LDS: DPP within rows of 16 lanes,
 // permlane16/32 swaps across rows.
-#define RVQ_DPP_U(v, ctrl) __builtin_amdgcn_update_dpp(0u, (v), (ctrl), 0xF, 0xF, true)
-constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppRor4 = 0x124, kDppRor8 = 0x128;
-
-__device__ inline double dpp_d(double v, int step) {
-    const uint64_t b = __double_as_longlong(v);
-    uint32_t lo = (uint32_t)b, hi = (uint32_t)(b >> 32);
-    switch (step) {
-        case 0: lo = RVQ_DPP_U(lo, kDppXor1); hi = RVQ_DPP_U(hi, kDppXor1); break;
-        case 1: lo = RVQ_DPP_U(lo, kDppXor2); hi = RVQ_DPP_U(hi, kDppXor2); break;
-        case 2: lo = RVQ_DPP_U(lo, kDppRor4); hi = RVQ_DPP_U(hi, kDppRor4); break;
-        default: lo = RVQ_DPP_U(lo, kDppRor8); hi = RVQ_DPP_U(hi, kDppRor8); break;
-    }
-    return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
-}
-
-// The other row's value after a 16-lane (rows 0<->1, 2<->3) or 32-lane swap.
-__device__ inline uint32_t swap_other(uint32_t v, bool wide, bool odd) {
-    if (wide) {
-        auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
-        return odd ? r[0] : r[1];
-    }
-    auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
-    return odd ? r[0] : r[1];
-}
-
-__device__ inline double wave_sum(double v) {
-#pragma unroll
-    for (int st = 0; st < 4; st++) v += dpp_d(v, st);  // every lane: sum of its row of 16
-    const int lane = threadIdx.x & 63;
-#pragma unroll
-    for (int w = 0; w < 2; w++) {
-        const bool odd = w ? (lane & 32) : (lane & 16);
-        const uint64_t b = __double_as_longlong(v);
-        const uint32_t lo = swap_other((uint32_t)b, w, odd), hi = swap_other((uint32_t)(b >> 32), w, odd);
-        v += __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
-    }
-    return v;  // identical in every lane
-}
-
 // NaN logits rank below every number (and among themselves by id).
 __device__ inline double rank_value(double v) { return isnan(v) ? -INFINITY : v; }
 
@@ -544,7 +505,7 @@ hipError_t launch_route(const Geometry &g, Workspace &w, const float *x, const f
 
 int64_t route_logit_slots(int64_t max_tokens, int E) { return max_tokens * E + 2 * E + 2 * kMaxTopK; }
 
-hipError_t init_route(Workspace &w, int E, int64_t max_tokens, int n_cu, hipStream_t s) {
+hipError_t init_route(Workspace &w, int E, int k, int64_t max_tokens, int n_cu, hipStream_t s) {
     w.route_cap = max_tokens * E;
     w.route_parity = 0;
     // the one-token kernel needs all E workgroups resident together
@@ -554,7 +515,7 @@ hipError_t init_route(Workspace &w, int E, int64_t max_tokens, int n_cu, hipStre
     w.route_one = (int64_t)per_cu * n_cu >= E;
     w.fused_parity = 0;
     const hipError_t e2 = hipMemsetD32Async(reinterpret_cast<hipDeviceptr_t>(w.fused_logits), kUnpublishedHalf,
-                                            (size_t)(2 * 2 * max_tokens * E), s);
+                                            (size_t)(2 * fused_route_slots(max_tokens, E, k)), s);
     if (e2 != hipSuccess) return e2;
     return hipMemsetD32Async(reinterpret_cast<hipDeviceptr_t>(w.route_logits), kUnpublishedHalf,
                              (size_t)(2 * route_logit_slots(max_tokens, E)), s);
