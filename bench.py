@@ -5,10 +5,11 @@ Default workload (the headline): one K3-scale MoE layer, batch-1 decode.
 d=7168, ffn=2048, E=384 experts, top-16, expert weights as 3-stage RVQ
 (256-entry fp16 codebooks over 8-wide vectors, uniform u8 codes, 16,515,072 B
 per expert record), router N(0, 0.02), tokens x ~ N(0,1) with one seed per
-token.  A step is one call of the whole hot path: rvq_moe_route_topk (router
-GEMV + top-16 + softmax gates) then rvq_moe_layer_forward (LUT build, gate/up
-gather + SiLU, down gather, gate-weighted combine), every token distinct, all
-inputs resident in HBM before the timed region.
+token.  A step is one call of the whole hot path -- router GEMV, top-16,
+softmax gates, LUT build, gate/up gather + SiLU, down gather, gate-weighted
+combine -- by default as one rvq_moe_route_forward call (the fastest way at
+batch 1; --path two-call times rvq_moe_route_topk then rvq_moe_layer_forward),
+every token distinct, all inputs resident in HBM before the timed region.
 
 Other workloads of the same layer shape:
   --batch B    B tokens per call (batched decode, pairs grouped by expert);
@@ -62,11 +63,12 @@ def source_sha256() -> str:
     return h.hexdigest()
 
 
-def recorded_traffic():
-    """HBM bytes per k_layer launch from the committed counter runs (FETCH_SIZE
-    and WRITE_SIZE scaled by a reference copy), or None when the sources have
-    changed since those counters were taken."""
-    path = os.path.join(ROOT, "profiles", "k_layer_k3_batch1_decode_traffic.md")
+def recorded_traffic(fused: bool):
+    """HBM bytes per layer-kernel launch from the committed counter runs
+    (FETCH_SIZE and WRITE_SIZE scaled by a reference copy), or None when the
+    sources have changed since those counters were taken."""
+    name = "k_layer_routed_k3_batch1_decode_traffic.md" if fused else "k_layer_k3_batch1_decode_traffic.md"
+    path = os.path.join(ROOT, "profiles", name)
     if not os.path.exists(path):
         return None
     fields = {}
@@ -105,10 +107,14 @@ def main():
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="after the run, one plain device-to-device copy of this many bytes (a reference kernel "
                          "of known traffic for scaling hardware byte counters)")
-    ap.add_argument("--path", choices=("fused", "two-call"), default="two-call",
-                    help="fused: rvq_moe_route_forward (one launch per call); "
-                         "two-call: rvq_moe_route_topk then rvq_moe_layer_forward")
+    ap.add_argument("--path", choices=("fused", "two-call"), default=None,
+                    help="fused: rvq_moe_route_forward (one launch per call; the default for batch-1 decode with "
+                         "resident codes); two-call: rvq_moe_route_topk then rvq_moe_layer_forward (the default "
+                         "elsewhere)")
     args = ap.parse_args()
+    if args.path is None:
+        args.path = ("fused" if args.batch == 1 and not args.chunk and args.stream_slots == 0 and not args.lookahead
+                     else "two-call")
 
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the layer is not sharded across GPUs.",
@@ -329,9 +335,9 @@ def main():
         "distinct_experts_per_call": float(uniq.mean()),
         "roofline": {"bound": "hbm", "achieved": l_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": l_gbps / HBM_PEAK_GBPS,
-                     "traffic": (recorded_traffic() if (B == 1 and L == 1 and not args.chunk and not streaming and
-                                                        args.path == "two-call") else None),
-                     "kernel": "k_layer<route>" if args.path == "fused" else
+                     "traffic": (recorded_traffic(args.path == "fused")
+                                 if (B == 1 and L == 1 and not args.chunk and not streaming) else None),
+                     "kernel": "k_layer<routed> (routing and experts in one launch)" if args.path == "fused" else
                      ("k_chunk_prep + k_chunk_stage + k_chunk_gu + k_chunk_down" if args.chunk else "k_layer"),
                      "algorithmic_bytes_per_launch": per_call_bytes, "avg_us": l_avg_us, "timed_launches": int(n_l)},
         "kernels": kernels,
