@@ -56,6 +56,8 @@ def lib():
         L.rvq_oracle_moe.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, _f64p,
                                      ctypes.POINTER(ctypes.c_void_p), ctypes.c_int,
                                      ctypes.POINTER(ctypes.c_void_p), _f64p, _f32p, _f64p]
+        L.rvq_oracle_crc32.argtypes = [_u8p, ctypes.c_int64]
+        L.rvq_oracle_crc32.restype = ctypes.c_uint32
         for name in ("rvq_oracle_rmsnorm", "rvq_oracle_router", "rvq_oracle_topk", "rvq_oracle_matvec",
                      "rvq_oracle_expert", "rvq_oracle_moe"):
             getattr(L, name).restype = ctypes.c_int
@@ -206,3 +208,52 @@ def layer(x_in: np.ndarray, w_r: np.ndarray, k: int, get_codebook, get_record, d
     delta = moe(d, ffn, r.gates, cbs, recs, x)
     out = delta + x_in.astype(np.float64) if residual else delta
     return LayerOut(r, x, delta, out)
+
+
+# --------------------------------------------------------------------------- expert-record integrity
+# [FR] "Architecture de streaming depuis le disque": every record read from
+# an expert bank is checked for its magic, its expert id and its offset range
+# (a truncated or wrongly assembled bank must not hand out another expert's
+# weights); the crc32 of the payload is checked on request only.  The record
+# layout checked here is the library's documented bank format, restated:
+# record e spans [e * stride, (e + 1) * stride); the payload comes first, the
+# trailer starts at the first 4096-byte boundary at or after its end, as
+# little-endian fields magic u32, version u32, expert u32, n_experts u32,
+# offset u64, payload_bytes u64, d i32, ffn i32, crc32 u32, reserved u32.
+
+RECORD_MAGIC = int.from_bytes(b"RVQR", "little")
+RECORD_VERSION = 1
+BAD_MAGIC, BAD_ID, BAD_RANGE, BAD_CRC = 1, 2, 4, 8
+_TRAILER = "<IIIIQQiiII"
+
+
+def crc32(buf) -> int:
+    """CRC-32 of a byte buffer (bitwise C loop; see rvq_oracle_crc32)."""
+    a = np.ascontiguousarray(np.frombuffer(bytes(buf), np.uint8) if not isinstance(buf, np.ndarray) else buf,
+                             dtype=np.uint8)
+    if a.size == 0:
+        return lib().rvq_oracle_crc32(None, 0)
+    return int(lib().rvq_oracle_crc32(_p(a, _u8p), a.size))
+
+
+def trailer_offset(payload: int) -> int:
+    return (payload + 4095) // 4096 * 4096
+
+
+def record_check_flags(record: np.ndarray, e: int, n_experts: int, stride: int, payload: int, d: int, ffn: int,
+                       verify: bool) -> int:
+    """Flags of the checks one record (its `stride` bytes) fails, 0 if none."""
+    import struct
+    t0 = trailer_offset(payload)
+    magic, version, expert, n_exp, offset, pay, td, tffn, crc, _ = struct.unpack_from(
+        _TRAILER, bytes(record[t0:t0 + struct.calcsize(_TRAILER)]))
+    flags = 0
+    if magic != RECORD_MAGIC or version != RECORD_VERSION:
+        flags |= BAD_MAGIC
+    if expert != e or n_exp != n_experts:
+        flags |= BAD_ID
+    if offset != e * stride or pay != payload or td != d or tffn != ffn:
+        flags |= BAD_RANGE
+    if verify and crc32(record[:payload]) != crc:
+        flags |= BAD_CRC
+    return flags

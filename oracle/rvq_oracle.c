@@ -203,3 +203,14 @@ int rvq_oracle_moe(int d, int ffn, int k, const double *gates, const void *const
     free(y);
     return rc;
 }
+
+uint32_t rvq_oracle_crc32(const uint8_t *p, int64_t n) {
+    /* the generator's coefficients x^0 .. x^31 as bits 31 .. 0 (x^32 implied) */
+    const uint32_t gen = 0xEDB88320u;
+    uint32_t r = 0xFFFFFFFFu;
+    for (int64_t i = 0; i < n; i++) {
+        r ^= (uint32_t)p[i];
+        for (int b = 0; b < 8; b++) r = (r & 1u) ? (r >> 1) ^ gen : r >> 1;
+    }
+    return r ^ 0xFFFFFFFFu;
+}

@@ -75,6 +75,14 @@ int rvq_oracle_moe(int d, int ffn, int k, const double *gates, const void *const
                    int cb_dtype, const uint8_t *const *records, const double *x, const float *resid,
                    double *out);
 
+/* CRC-32 of n bytes, one bit at a time: the remainder of the polynomial
+ * division that defines the checksum (generator x^32 + x^26 + x^23 + x^22 +
+ * x^16 + x^12 + x^11 + x^10 + x^8 + x^7 + x^5 + x^4 + x^2 + x + 1, bits
+ * taken least significant first, register preset to all ones and inverted
+ * at the end).  [FR] "Architecture de streaming depuis le disque": an expert
+ * record's payload may be checked by its crc32. */
+uint32_t rvq_oracle_crc32(const uint8_t *p, int64_t n);
+
 #ifdef __cplusplus
 }
 #endif

@@ -367,3 +367,83 @@ def test_layer_combine_is_gate_weighted_sum():
     np.testing.assert_allclose(out.delta, ref, rtol=1e-14, atol=1e-15)
     # routing uses the normalised input
     np.testing.assert_allclose(out.x_hat, x / np.sqrt(np.mean(x.astype(np.float64) ** 2) + 1e-6), rtol=1e-14)
+
+
+# --------------------------------------------------------------------------- record integrity (crc32, trailer)
+def test_crc32_standard_check_value():
+    # The CRC-32 of IEEE 802.3 / ITU-T V.42 (zlib's) has the published check
+    # value 0xCBF43926 for the nine ASCII digits "123456789".
+    assert O.crc32(b"123456789") == 0xCBF43926
+    assert O.crc32(b"") == 0
+
+
+@pytest.mark.parametrize("n", [1, 3, 15, 16, 17, 4095, 4096, 4097, 100003])
+def test_crc32_equals_the_library_routine(n):
+    import zlib
+    buf = np.random.default_rng(n).integers(0, 256, n, dtype=np.uint8)
+    assert O.crc32(buf) == zlib.crc32(buf.tobytes())
+
+
+def test_crc32_residue_and_affinity():
+    rng = np.random.default_rng(7)
+    for n in (1, 8, 77, 4096):
+        m = rng.integers(0, 256, n, dtype=np.uint8)
+        c = O.crc32(m)
+        # appending the checksum (least significant byte first) leaves the
+        # generator's fixed residue, 0x2144DF1C after the final inversion
+        assert O.crc32(np.concatenate([m, np.frombuffer(c.to_bytes(4, "little"), np.uint8)])) == 0x2144DF1C
+        # the checksum is affine over GF(2): an odd number of equal-length
+        # messages xor-ed together has the xor of their checksums
+        a, b = rng.integers(0, 256, (2, n), dtype=np.uint8)
+        assert O.crc32(m ^ a ^ b) == c ^ O.crc32(a) ^ O.crc32(b)
+        # any single flipped bit changes it
+        for bit in (0, 7, 8 * n - 1):
+            f = m.copy()
+            f[bit // 8] ^= np.uint8(1 << (bit % 8))
+            assert O.crc32(f) != c
+
+
+def _record(e, n_experts, payload_bytes, d, ffn, seed=0, **over):
+    import struct
+    stride = O.trailer_offset(payload_bytes) + 4096
+    rec = np.zeros(stride, np.uint8)
+    rec[:payload_bytes] = np.random.default_rng(seed).integers(0, 256, payload_bytes, dtype=np.uint8)
+    f = dict(magic=int.from_bytes(b"RVQR", "little"), version=1, expert=e, n_exp=n_experts,
+             offset=e * stride, payload=payload_bytes, t_d=d, t_ffn=ffn, crc=O.crc32(rec[:payload_bytes]))
+    f.update(over)
+    t = struct.pack("<IIIIQQiiII", f["magic"], f["version"], f["expert"], f["n_exp"], f["offset"],
+                    f["payload"], f["t_d"], f["t_ffn"], f["crc"], 0)
+    t0 = O.trailer_offset(payload_bytes)
+    rec[t0:t0 + len(t)] = np.frombuffer(t, np.uint8)
+    return rec, stride
+
+
+@pytest.mark.parametrize("over,flags", [
+    ({}, 0),
+    (dict(magic=0), O.BAD_MAGIC),
+    (dict(version=2), O.BAD_MAGIC),
+    (dict(expert=4), O.BAD_ID),
+    (dict(n_exp=9), O.BAD_ID),
+    (dict(offset=0), O.BAD_RANGE),
+    (dict(payload=3072), O.BAD_RANGE),
+    (dict(t_d=72), O.BAD_RANGE),
+    (dict(t_ffn=48), O.BAD_RANGE),
+    (dict(crc=1), O.BAD_CRC),
+])
+def test_record_check_flags_each_field(over, flags):
+    d, ffn, E, e, payload = 64, 40, 8, 3, 6144
+    rec, stride = _record(e, E, payload, d, ffn, **over)
+    assert O.record_check_flags(rec, e, E, stride, payload, d, ffn, verify=True) == flags
+    # without verify only the crc goes unchecked
+    assert O.record_check_flags(rec, e, E, stride, payload, d, ffn, verify=False) == flags & ~O.BAD_CRC
+
+
+def test_record_check_catches_a_payload_flip_only_with_crc():
+    d, ffn, E, e, payload = 64, 40, 8, 5, 6144
+    rec, stride = _record(e, E, payload, d, ffn)
+    rec[1234] ^= 0x10
+    assert O.record_check_flags(rec, e, E, stride, payload, d, ffn, verify=False) == 0
+    assert O.record_check_flags(rec, e, E, stride, payload, d, ffn, verify=True) == O.BAD_CRC
+    # a record read for another expert (a mis-assembled bank)
+    rec2, _ = _record(e, E, payload, d, ffn)
+    assert O.record_check_flags(rec2, e + 1, E, stride, payload, d, ffn, verify=False) == O.BAD_ID | O.BAD_RANGE
