@@ -18,7 +18,9 @@ Other workloads of the same layer shape:
   --layers L   a depth chain: L layers, each with RMS normalisation before
                routing and a residual add, one token through all L per step;
   --stream-slots S   codes kept in pinned host memory and streamed through S
-               HBM expert slots (copies on a side stream, overlapped).
+               HBM expert slots (copies on a side stream, overlapped); every
+               record copied in has its trailer checked on the device;
+  --verify     with --stream-slots: also the CRC-32 of every record's payload.
   --lookahead N  with --layers and --stream-slots: after each layer's call,
                the next layer's router runs on this layer's input and the
                first N of its predicted experts are prefetched into the next
@@ -98,6 +100,8 @@ def main():
                     help="every layer_forward call takes the chunk path (bf16 matrix cores)")
     ap.add_argument("--stream-slots", type=int, default=0,
                     help="stream the codes from a pinned host bank through this many HBM slots")
+    ap.add_argument("--verify", action="store_true",
+                    help="with --stream-slots: check the CRC-32 of every expert record copied into a slot")
     ap.add_argument("--lut-expert-tokens", type=int, default=0,
                     help="with --chunk: experts routed fewer tokens than this take the table path (0: the "
                          "library default, 1: every expert on the matrix cores)")
@@ -135,6 +139,7 @@ def main():
     streaming = args.stream_slots > 0
     if (B < 1 or L < 1 or (chain and B != 1) or
             (args.path == "fused" and (B * shape.top_k > 1024 or args.chunk or streaming)) or
+            (args.verify and not streaming) or
             (args.lookahead and (not chain or not streaming or args.path == "fused" or
                                  not 1 <= args.lookahead <= shape.top_k))):
         print(f"--batch {B} / --layers {L} outside what the chosen path takes", file=sys.stderr)
@@ -148,7 +153,7 @@ def main():
         if streaming:
             codes = torch.empty(inp.codes_dev.shape, dtype=torch.uint8, pin_memory=True)
             codes.copy_(inp.codes_dev)
-            extra = dict(codes_location=1, cache_slots=args.stream_slots)
+            extra = dict(codes_location=1, cache_slots=args.stream_slots, verify_records=args.verify)
         layers.append(RvqMoe(d=shape.d, ffn=shape.ffn, n_experts=shape.n_experts, top_k=shape.top_k,
                              codebook_dtype=1, router_w=inp.w_r_dev, codebooks=inp.cb_dev, codes=codes,
                              max_tokens=B, pre_rmsnorm=chain, residual=chain, eps=1e-6,
@@ -243,9 +248,12 @@ def main():
         moved = sum(a["h2d_bytes"] - b["h2d_bytes"] for a, b in zip(st, stats0))
         hits = sum(a["slot_hits"] - b["slot_hits"] for a, b in zip(st, stats0))
         misses = sum(a["slot_misses"] - b["slot_misses"] for a, b in zip(st, stats0))
+        checked = sum(a["records_checked"] - b["records_checked"] for a, b in zip(st, stats0))
+        verified = sum(a["records_verified"] - b["records_verified"] for a, b in zip(st, stats0))
         h2d.update({"slots": args.stream_slots, "h2d_bytes": moved, "GBps": moved / (ms * 1e-3) / 1e9,
                     "frac_of_ceiling": moved / (ms * 1e-3) / 1e9 / h2d["ceiling_GBps"],
-                    "hit_rate": hits / max(hits + misses, 1)})
+                    "hit_rate": hits / max(hits + misses, 1), "records_checked": checked,
+                    "records_crc_verified": verified})
         if args.lookahead:
             fills = sum(a["prefetch_fills"] - b["prefetch_fills"] for a, b in zip(st, stats0))
             phits = sum(a["prefetch_hits"] - b["prefetch_hits"] for a, b in zip(st, stats0))
@@ -296,7 +304,8 @@ def main():
                          f"layer rebuilt as c1+c2+c3 in fp64); includes regenerating their code records on the host"}
         parity = {"tokens": args.cpu_tokens, "layers_checked": L, "ids_bit_exact": ok_ids, "max_rel_l2": max(errs)}
 
-    where = (f"codes streamed from pinned host memory through {args.stream_slots} HBM slots" if streaming
+    where = (f"codes streamed from pinned host memory through {args.stream_slots} HBM slots"
+             + (" (each record's CRC-32 checked)" if args.verify else "") if streaming
              else "resident codes")
     if args.chunk:
         workload = (f"K3-scale prefill chunk, {where}: {B} tokens per call through d=7168 ffn=2048 E=384 "

@@ -15,8 +15,9 @@
  *          entries, 8-dim vectors, 3.00 bits/weight) and its evaluation (a
  *          table of partial dot products, 3 lookups and 2 additions per row).
  *        - "Architecture de streaming depuis le disque": gate, up and down of
- *          one expert are contiguous so one expert is one read; records are
- *          validated by expert id and offset range.
+ *          one expert are contiguous so one expert is one read; every record
+ *          read is checked (magic, expert id, offset range) and, on request,
+ *          its payload's crc32.
  *        - "Lecture anticipée et prédiction du routeur": the router of a layer
  *          decides 16 expert ids and expert reads are consumed as they land.
  *        - "Objectif et forme d'implémentation de WASTE": a small public C API
@@ -51,7 +52,7 @@
 extern "C" {
 #endif
 
-#define RVQ_MOE_ABI_VERSION 4
+#define RVQ_MOE_ABI_VERSION 5
 
 typedef enum rvq_moe_status {
     RVQ_MOE_OK = 0,
@@ -60,7 +61,8 @@ typedef enum rvq_moe_status {
     RVQ_MOE_EBUDGET = -3,  /* slot cache smaller than one token's working set (0 < cache_slots < top_k) */
     RVQ_MOE_ENOMEM = -4,   /* device or pinned allocation failed */
     RVQ_MOE_EHIP = -5,     /* a HIP runtime call or launch failed */
-    RVQ_MOE_EDEVICE = -6   /* deferred: a kernel saw an expert id outside [0, n_experts) */
+    RVQ_MOE_EDEVICE = -6,  /* deferred: a kernel saw an expert id outside [0, n_experts) */
+    RVQ_MOE_ECORRUPT = -7  /* an expert record failed its integrity check (see rvq_moe_record_trailer) */
 } rvq_moe_status;
 
 /* Default chunk-path threshold (tokens per layer_forward call): where the
@@ -81,9 +83,54 @@ typedef enum rvq_moe_cb_dtype {
 } rvq_moe_cb_dtype;
 
 typedef enum rvq_moe_codes_location {
-    RVQ_MOE_CODES_DEVICE = 0,      /* codes are in device memory; copied and repacked at open */
-    RVQ_MOE_CODES_PINNED_HOST = 1  /* codes stay in pinned host memory (borrowed) */
+    RVQ_MOE_CODES_DEVICE = 0,       /* canonical codes in device memory; copied and repacked at open */
+    RVQ_MOE_CODES_PINNED_HOST = 1,  /* canonical codes in pinned host memory; open writes the handle's own
+                                       pinned bank from them (see rvq_moe_write_bank) */
+    RVQ_MOE_CODES_PINNED_BANK = 2   /* `codes` is a bank written by rvq_moe_write_bank, in pinned host
+                                       memory; borrowed (it must outlive the handle) */
 } rvq_moe_codes_location;
+
+/*
+ * Expert-record bank of a streaming handle.  [FR] "Architecture de streaming
+ * depuis le disque": an expert's gate, up and down form one record read in
+ * one piece; each record read is checked for its magic, its expert id and its
+ * offset range, so that a truncated or wrongly assembled bank cannot hand out
+ * another expert's weights; a crc32 of the payload is checked only on request
+ * (about 1 % of the time on K3 there); codebooks carry no checksum.
+ *
+ * Record e of a bank occupies bytes [e * stride, (e + 1) * stride)
+ * (rvq_moe_bank_layout gives stride and payload_bytes; stride is a multiple of
+ * 4096): the payload (the expert's codes in the library's internal layout),
+ * zeros up to the next 4096-byte boundary, then a 4096-byte trailer page
+ * holding an rvq_moe_record_trailer followed by zeros.  Every copy of a record
+ * into an HBM slot is followed, on the device and before any kernel reads the
+ * slot, by the trailer checks (magic and version; expert == e and n_experts;
+ * offset == e * stride, payload_bytes, d and ffn) and, with verify_records,
+ * by the CRC-32 of the payload as it landed in HBM.  A failure is reported
+ * as RVQ_MOE_ECORRUPT by every later rvq_moe_sync and by rvq_moe_close (it is
+ * not cleared: the bank is damaged); outputs of calls that read the record
+ * are unspecified.  Open checks every trailer of a PINNED_BANK on the host.
+ * CRC-32 here is the one of zlib and IEEE 802.3 (reflected polynomial
+ * 0xEDB88320, initial value and final xor 0xFFFFFFFF; "123456789" -> 0xCBF43926).
+ */
+#define RVQ_MOE_RECORD_MAGIC 0x52515652u /* the bytes "RVQR" */
+#define RVQ_MOE_RECORD_VERSION 1u
+typedef struct rvq_moe_record_trailer {
+    uint32_t magic;          /* RVQ_MOE_RECORD_MAGIC */
+    uint32_t version;        /* RVQ_MOE_RECORD_VERSION */
+    uint32_t expert;         /* the expert whose codes the payload holds */
+    uint32_t n_experts;      /* E of the bank */
+    uint64_t offset;         /* byte offset of this record in the bank (expert * stride) */
+    uint64_t payload_bytes;  /* payload size */
+    int32_t d, ffn;          /* layer shape the payload is laid out for */
+    uint32_t crc32;          /* CRC-32 of the payload_bytes payload bytes */
+    uint32_t reserved;       /* 0 */
+} rvq_moe_record_trailer;
+/* Flags of a failed record check (rvq_moe_last_error names them and the expert). */
+#define RVQ_MOE_RECORD_BAD_MAGIC 1 /* magic or version */
+#define RVQ_MOE_RECORD_BAD_ID 2    /* expert or n_experts */
+#define RVQ_MOE_RECORD_BAD_RANGE 4 /* offset, payload_bytes, d or ffn */
+#define RVQ_MOE_RECORD_BAD_CRC 8   /* payload CRC-32 (checked only with verify_records) */
 
 /*
  * Layer description, read only during rvq_moe_open.
@@ -102,8 +149,12 @@ typedef enum rvq_moe_codes_location {
  *                [ffn][d/8][3] u8, then down [d][ffn/8][3] u8: byte s of
  *                (row, slice j) indexes stage s's codebook for the 8 weights
  *                row[8j .. 8j+7].  Record bytes = 9 * d * ffn / 8.
- *   codes_location  rvq_moe_codes_location.  Only RVQ_MOE_CODES_DEVICE is
- *                implemented by this version (PINNED_HOST: RVQ_MOE_ENOTSUP).
+ *                With codes_location PINNED_BANK, `codes` is instead a bank
+ *                written by rvq_moe_write_bank for the same d, ffn, E.
+ *   codes_location  rvq_moe_codes_location.  PINNED_HOST and PINNED_BANK
+ *                stream the codes through cache_slots HBM slots (both need
+ *                cache_slots >= top_k); DEVICE keeps them all resident
+ *                (cache_slots must be 0).
  *   cache_slots  0 = all experts resident.  Otherwise the number of HBM expert
  *                slots; must be >= top_k (RVQ_MOE_EBUDGET), mirroring the
  *                refusal to start below one token's working set.
@@ -126,6 +177,10 @@ typedef enum rvq_moe_codes_location {
  *                (512 pairs; experts in id order).  0 = the library default
  *                (RVQ_MOE_LUT_EXPERT_TOKENS); 1 = every expert on the matrix
  *                cores.  Streaming handles always use 1.  Must be >= 0.
+ *   verify_records  streaming handles: nonzero = also check the CRC-32 of
+ *                every record copied into a slot (see rvq_moe_record_trailer);
+ *                the trailer checks always run.  Ignored for DEVICE codes.
+ *   reserved     must be 0.
  *   stream       stream used for the upload and repack inside open.
  */
 typedef struct rvq_moe_desc {
@@ -145,6 +200,8 @@ typedef struct rvq_moe_desc {
     int32_t max_tokens;
     int32_t chunk_min_tokens;
     int32_t lut_expert_tokens;
+    int32_t verify_records;
+    int32_t reserved;
     double eps;
     const float *router_w;
     const void *codebooks;
@@ -161,10 +218,34 @@ typedef struct rvq_moe rvq_moe;
  * input buffer afterwards (the library owns its copies and its workspace).
  * On failure *out is set to NULL and nothing stays allocated.
  * Errors: EINVAL (null desc/out/pointers, struct_size mismatch, bad dims,
- * k > E, max_tokens < 1), ENOTSUP (format or codes_location), EBUDGET
- * (0 < cache_slots < top_k), ENOMEM, EHIP.
+ * k > E, max_tokens < 1, PINNED_* codes not in pinned host memory), ENOTSUP
+ * (format), EBUDGET (0 < cache_slots < top_k), ECORRUPT (a PINNED_BANK trailer
+ * fails its check: last_error names the expert), ENOMEM, EHIP.
  */
 int rvq_moe_open(const rvq_moe_desc *desc, rvq_moe **out);
+
+/*
+ * rvq_moe_bank_layout -- record stride and payload size (bytes) of the bank
+ * of the layer `desc` describes; the bank is n_experts * stride bytes.  Only
+ * d, ffn, n_experts, top_k and the format fields of desc are read; host only.
+ * Errors: EINVAL (null pointers, struct_size, bad dims), ENOTSUP (format).
+ */
+int rvq_moe_bank_layout(const rvq_moe_desc *desc, int64_t *record_stride, int64_t *payload_bytes);
+
+/*
+ * rvq_moe_write_bank -- write the expert-record bank of the layer `desc`
+ * describes into `bank` (pinned host memory, n_experts * stride bytes, owned
+ * by the caller): each record's payload (desc->codes repacked into the
+ * internal layout on the device), zero fill, and its trailer with the
+ * payload's CRC-32 computed on the device.  desc->codes holds canonical
+ * records (as for open) in device memory (codes_location DEVICE) or pinned
+ * host memory (PINNED_HOST); router_w and codebooks are not read.  Uses
+ * desc->stream and synchronises it; allocates only temporary device buffers.
+ * The bank can then be stored, copied, and opened as PINNED_BANK.
+ * Errors: EINVAL (null pointers, bad dims, bank not pinned host memory,
+ * codes_location PINNED_BANK), ENOTSUP (format), ENOMEM, EHIP.
+ */
+int rvq_moe_write_bank(const rvq_moe_desc *desc, uint8_t *bank);
 
 /*
  * rvq_moe_route_topk -- router GEMV (fp64 accumulation of fp32 products),
@@ -216,7 +297,7 @@ int rvq_moe_route_forward(rvq_moe *h, const float *x, int32_t n_tokens, int32_t 
 
 /*
  * rvq_moe_prefetch -- start making experts resident in the HBM slot cache of
- * a streaming handle (codes_location PINNED_HOST) ahead of a later
+ * a streaming handle (codes_location PINNED_HOST or PINNED_BANK) ahead of a later
  * layer_forward.  [FR] "Lecture anticipée et prédiction du routeur": the
  * router of the next layer, run on the current layer's hidden state, predicts
  * that layer's experts; the first 6 of its 16 are read early and consumed as
@@ -237,8 +318,10 @@ int rvq_moe_route_forward(rvq_moe *h, const float *x, int32_t n_tokens, int32_t 
 int rvq_moe_prefetch(rvq_moe *h, const int32_t *ids, int32_t n_tokens, int32_t per_token, void *stream);
 
 /*
- * rvq_moe_sync -- synchronise `stream`, then return and clear any deferred
- * device-side error (RVQ_MOE_EDEVICE) recorded by earlier calls.
+ * rvq_moe_sync -- synchronise `stream`, then return any deferred device-side
+ * error recorded by earlier calls: RVQ_MOE_ECORRUPT (a record check failed;
+ * returned again by every later sync and by close) before RVQ_MOE_EDEVICE
+ * (cleared once returned).
  */
 int rvq_moe_sync(rvq_moe *h, void *stream);
 
@@ -261,7 +344,7 @@ typedef struct rvq_moe_stats {
     uint64_t tokens_routed;
     uint64_t tokens_forwarded;
     uint64_t expert_evals;          /* token x expert pairs evaluated */
-    uint64_t code_bytes_resident;   /* bytes of the library's code copy */
+    uint64_t code_bytes_resident;   /* bytes of the library's code copy (streaming: its HBM slots) */
     uint64_t record_bytes;          /* canonical bytes per expert record */
     uint64_t codebook_bytes;        /* bytes of one expert's codebooks */
     uint64_t h2d_bytes;             /* slot cache: bytes copied host -> HBM slots */
@@ -270,6 +353,8 @@ typedef struct rvq_moe_stats {
     uint64_t host_syncs;            /* slot cache: calls that read their ids back */
     uint64_t prefetch_fills;        /* slot cache: experts copied in by rvq_moe_prefetch */
     uint64_t prefetch_hits;         /* slot cache: of those, found resident by a later call */
+    uint64_t records_checked;       /* slot cache: record copies followed by the trailer checks */
+    uint64_t records_verified;      /* slot cache: of those, with the payload CRC-32 checked too */
 } rvq_moe_stats;
 
 int rvq_moe_get_stats(const rvq_moe *h, rvq_moe_stats *out);

@@ -14,7 +14,7 @@ def test_library_exports_every_header_symbol():
     L = R.lib()
     for n in names:
         assert hasattr(L, n), n
-    assert L.rvq_moe_abi_version() == 4
+    assert L.rvq_moe_abi_version() == 5
 
 
 def _desc(**over):
@@ -43,6 +43,9 @@ def _desc(**over):
     (dict(cache_slots=8), R.EINVAL),   # slots stream pinned host codes only
     (dict(codes_location=1), R.EINVAL),  # pinned host codes need slots
     (dict(codes_location=5), R.EINVAL),
+    (dict(codes_location=2), R.EINVAL),  # a bank needs slots too
+    (dict(codes_location=2, cache_slots=4), R.EINVAL),  # not pinned host memory
+    (dict(reserved=1), R.EINVAL),
     (dict(chunk_min_tokens=-1), R.EINVAL),
     (dict(eps=-1.0), R.EINVAL),
 ])
@@ -72,3 +75,32 @@ def test_calls_reject_null_handle():
     assert L.rvq_moe_close(None) == R.OK
     s = R.Stats()
     assert L.rvq_moe_get_stats(None, ctypes.byref(s)) == R.EINVAL
+
+
+def test_bank_layout_k3_shape():
+    # d=7168, ffn=2048: every matrix fills whole 32-slice x 32-row blocks, so
+    # the payload is the canonical 9 d ffn / 8 bytes (4032 pages) and the
+    # trailer takes one more page
+    stride, payload = R.bank_layout(d=7168, ffn=2048, n_experts=384, top_k=16, codebook_dtype=R.CB_F16)
+    assert payload == 16_515_072 == 9 * 7168 * 2048 // 8
+    assert stride == payload + 4096
+
+
+@pytest.mark.parametrize("d,ffn", [(256, 128), (264, 136), (64, 40), (8, 8)])
+def test_bank_layout_pages(d, ffn):
+    stride, payload = R.bank_layout(d=d, ffn=ffn, n_experts=4, top_k=2, codebook_dtype=R.CB_F32)
+    assert payload >= 9 * d * ffn // 8 and payload % 16 == 0
+    assert stride % 4096 == 0 and stride - 4096 >= payload > stride - 8192
+
+
+def test_bank_calls_reject_bad_arguments_before_any_device_call():
+    L = R.lib()
+    s, p = ctypes.c_int64(), ctypes.c_int64()
+    assert L.rvq_moe_bank_layout(None, ctypes.byref(s), ctypes.byref(p)) == R.EINVAL
+    assert L.rvq_moe_bank_layout(ctypes.byref(_desc()), None, ctypes.byref(p)) == R.EINVAL
+    assert L.rvq_moe_bank_layout(ctypes.byref(_desc(d=12)), ctypes.byref(s), ctypes.byref(p)) == R.EINVAL
+    assert L.rvq_moe_bank_layout(ctypes.byref(_desc(n_stages=2)), ctypes.byref(s), ctypes.byref(p)) == R.ENOTSUP
+    assert L.rvq_moe_write_bank(ctypes.byref(_desc()), None) == R.EINVAL
+    assert L.rvq_moe_write_bank(ctypes.byref(_desc(codes=0)), 0x5000) == R.EINVAL
+    assert L.rvq_moe_write_bank(ctypes.byref(_desc(codes_location=2)), 0x5000) == R.EINVAL
+    assert L.rvq_moe_write_bank(ctypes.byref(_desc()), 0x5000) == R.EINVAL  # bank not pinned host memory

@@ -779,13 +779,14 @@ def test_prefetch_validation(torch_mod, tiny):
 
 
 def test_k3_streaming_batch1_matches_resident(torch_mod):
-    """d=7168, ffn=2048, E=384, top-16 from a pinned host bank through 32 slots,
-    one token per call; against a resident handle and the oracle."""
+    """d=7168, ffn=2048, E=384, top-16 from a pinned host bank through 32 slots
+    (every record's CRC-32 checked), one token per call; against a resident
+    handle and the oracle."""
     from synth import gpu as G
     shape = S.K3
     inp = G.LayerInputs(shape, seed=0, layer=6)
     bank = _pinned_bank(torch_mod, inp)
-    st = _layer(torch_mod, inp, shape, 1, codes=bank, codes_location=1, cache_slots=32)
+    st = _layer(torch_mod, inp, shape, 1, codes=bank, codes_location=1, cache_slots=32, verify_records=True)
     rs = _layer(torch_mod, inp, shape, 1)
     inp.free_codes()
     torch_mod.cuda.empty_cache()
@@ -797,6 +798,9 @@ def test_k3_streaming_batch1_matches_resident(torch_mod):
     assert err.max() <= 1e-6, err.max()
     _check(inp, shape, x, *a, tokens=[0])
     assert st.stats()["slot_misses"] >= 16
+    # every record copied in had its trailer and its 16.5 MB payload's CRC-32 checked
+    assert st.stats()["records_verified"] == st.stats()["slot_misses"]
+    st.sync()
     st.close()
     rs.close()
     del bank

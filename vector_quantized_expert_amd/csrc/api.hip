@@ -16,6 +16,7 @@
 
 #include "rvq_moe.h"
 
+#include "integrity.hpp"
 #include "internal.hpp"
 #include "slots.hpp"
 
@@ -142,10 +143,10 @@ static int open_impl(const rvq_moe_desc *desc, rvq_moe *h) {
     h->max_tokens = D.max_tokens;
     h->chunk_min = D.chunk_min_tokens > 0 ? D.chunk_min_tokens : RVQ_MOE_CHUNK_MIN_TOKENS;
     h->lut_tokens = D.lut_expert_tokens > 0 ? D.lut_expert_tokens : RVQ_MOE_LUT_EXPERT_TOKENS;
-    if (D.codes_location == RVQ_MOE_CODES_PINNED_HOST) h->lut_tokens = 1;
+    if (D.codes_location != RVQ_MOE_CODES_DEVICE) h->lut_tokens = 1;
     const Geometry &g = h->g;
     const int64_t E = D.n_experts;
-    h->streaming = D.codes_location == RVQ_MOE_CODES_PINNED_HOST;
+    h->streaming = D.codes_location != RVQ_MOE_CODES_DEVICE;
     if (!h->streaming) HIP_TRY(hipMalloc(&h->codes, (size_t)(E * g.rec_int)));
     HIP_TRY(hipMalloc(&h->cbs, (size_t)(E * g.cb_bytes)));
     HIP_TRY(hipMalloc(&h->router_wt, sizeof(float) * (size_t)D.d * E));
@@ -182,21 +183,21 @@ static int open_impl(const rvq_moe_desc *desc, rvq_moe *h) {
     HIP_TRY(launch_transpose(D.router_w, h->router_wt, D.d, D.n_experts, s));
     if (h->streaming) {
         const int S = D.cache_slots < D.n_experts ? D.cache_slots : D.n_experts;
-        HIP_TRY(slots_open(h->cache, g, S, (int)P, D.codes, s));
+        const bool borrowed = D.codes_location == RVQ_MOE_CODES_PINNED_BANK;
+        HIP_TRY(slots_open(h->cache, g, S, (int)P, borrowed ? nullptr : D.codes, borrowed ? D.codes : nullptr,
+                           D.verify_records != 0, s));
     } else {
         HIP_TRY(launch_repack(g, D.codes, h->codes, D.n_experts, s));
     }
     HIP_TRY(hipStreamSynchronize(s));
-    h->stats.code_bytes_resident = h->streaming ? (uint64_t)(h->cache.S * g.rec_int) : (uint64_t)(E * g.rec_int);
+    h->stats.code_bytes_resident = h->streaming ? (uint64_t)(h->cache.S * h->cache.rec) : (uint64_t)(E * g.rec_int);
     h->stats.record_bytes = (uint64_t)g.rec_canon;
     h->stats.codebook_bytes = (uint64_t)g.cb_bytes;
     return RVQ_MOE_OK;
 }
 
-extern "C" int rvq_moe_open(const rvq_moe_desc *desc, rvq_moe **out) {
-    g_err[0] = 0;
-    if (!out) return fail(RVQ_MOE_EINVAL, "out is NULL");
-    *out = nullptr;
+// The layer shape and format fields shared by open, bank_layout and write_bank.
+static int check_shape(const rvq_moe_desc *desc) {
     if (!desc) return fail(RVQ_MOE_EINVAL, "desc is NULL");
     const rvq_moe_desc &D = *desc;
     if (D.struct_size != sizeof(rvq_moe_desc))
@@ -211,6 +212,22 @@ extern "C" int rvq_moe_open(const rvq_moe_desc *desc, rvq_moe **out) {
         return fail(RVQ_MOE_EINVAL, "top_k=%d outside [1, min(E, %d)]", D.top_k, kMaxTopK);
     if (D.codebook_dtype != RVQ_MOE_CB_F32 && D.codebook_dtype != RVQ_MOE_CB_F16)
         return fail(RVQ_MOE_EINVAL, "codebook_dtype=%d", D.codebook_dtype);
+    return RVQ_MOE_OK;
+}
+
+static bool is_pinned_host(const void *p) {
+    hipPointerAttribute_t attr;
+    const hipError_t pe = hipPointerGetAttributes(&attr, p);
+    (void)hipGetLastError();  // clear the error a plain host pointer leaves
+    return pe == hipSuccess && attr.type == hipMemoryTypeHost;
+}
+
+extern "C" int rvq_moe_open(const rvq_moe_desc *desc, rvq_moe **out) {
+    g_err[0] = 0;
+    if (!out) return fail(RVQ_MOE_EINVAL, "out is NULL");
+    *out = nullptr;
+    if (const int rc = check_shape(desc)) return rc;
+    const rvq_moe_desc &D = *desc;
     if (D.max_tokens < 1) return fail(RVQ_MOE_EINVAL, "max_tokens=%d < 1", D.max_tokens);
     {
         // the layer kernel numbers its work units (one 32-row chunk of one
@@ -227,21 +244,33 @@ extern "C" int rvq_moe_open(const rvq_moe_desc *desc, rvq_moe **out) {
     if (D.cache_slots > 0 && D.cache_slots < D.top_k)
         return fail(RVQ_MOE_EBUDGET, "cache_slots=%d below one token's working set (top_k=%d)", D.cache_slots,
                     D.top_k);
-    if (D.codes_location != RVQ_MOE_CODES_DEVICE && D.codes_location != RVQ_MOE_CODES_PINNED_HOST)
+    if (D.codes_location != RVQ_MOE_CODES_DEVICE && D.codes_location != RVQ_MOE_CODES_PINNED_HOST &&
+        D.codes_location != RVQ_MOE_CODES_PINNED_BANK)
         return fail(RVQ_MOE_EINVAL, "codes_location=%d", D.codes_location);
     if (D.codes_location == RVQ_MOE_CODES_DEVICE && D.cache_slots != 0)
-        return fail(RVQ_MOE_EINVAL, "cache_slots=%d: the slot cache streams PINNED_HOST codes only", D.cache_slots);
-    if (D.codes_location == RVQ_MOE_CODES_PINNED_HOST) {
-        if (D.cache_slots == 0) return fail(RVQ_MOE_EINVAL, "PINNED_HOST codes need cache_slots >= top_k");
-        if (D.codes) {
-            hipPointerAttribute_t attr;
-            const hipError_t pe = hipPointerGetAttributes(&attr, D.codes);
-            (void)hipGetLastError();  // clear the error a plain host pointer leaves
-            if (pe != hipSuccess || attr.type != hipMemoryTypeHost)
-                return fail(RVQ_MOE_EINVAL, "PINNED_HOST codes must be pinned host memory (hipHostMalloc)");
+        return fail(RVQ_MOE_EINVAL, "cache_slots=%d: the slot cache streams PINNED_HOST or PINNED_BANK codes only",
+                    D.cache_slots);
+    if (D.reserved != 0) return fail(RVQ_MOE_EINVAL, "reserved=%d must be 0", D.reserved);
+    if (!D.router_w || !D.codebooks || !D.codes) return fail(RVQ_MOE_EINVAL, "null router_w/codebooks/codes");
+    if (D.codes_location != RVQ_MOE_CODES_DEVICE) {
+        if (D.cache_slots == 0) return fail(RVQ_MOE_EINVAL, "streamed codes need cache_slots >= top_k");
+        if (!is_pinned_host(D.codes))
+            return fail(RVQ_MOE_EINVAL, "PINNED_HOST / PINNED_BANK codes must be pinned host memory (hipHostMalloc)");
+    }
+    if (D.codes_location == RVQ_MOE_CODES_PINNED_BANK) {
+        // every trailer, on the host, before anything is allocated
+        const Geometry g = make_geometry(D.d, D.ffn, D.n_experts, D.top_k, D.codebook_dtype);
+        const RecordExpect ex = record_expect(g);
+        for (int e = 0; e < D.n_experts; e++) {
+            const auto *t = reinterpret_cast<const rvq_moe_record_trailer *>(D.codes + (int64_t)e * ex.stride +
+                                                                              ex.trailer_off);
+            if (const int flags = check_trailer(t, ex, e))
+                return fail(RVQ_MOE_ECORRUPT, "bank record %d fails its trailer check (flags 0x%x:%s%s%s)", e, flags,
+                            (flags & RVQ_MOE_RECORD_BAD_MAGIC) ? " magic/version" : "",
+                            (flags & RVQ_MOE_RECORD_BAD_ID) ? " expert id" : "",
+                            (flags & RVQ_MOE_RECORD_BAD_RANGE) ? " offset/size/shape" : "");
         }
     }
-    if (!D.router_w || !D.codebooks || !D.codes) return fail(RVQ_MOE_EINVAL, "null router_w/codebooks/codes");
     if (!(D.eps >= 0.0)) return fail(RVQ_MOE_EINVAL, "eps must be >= 0");
     rvq_moe *h = new (std::nothrow) rvq_moe();
     if (!h) return fail(RVQ_MOE_ENOMEM, "host allocation failed");
@@ -431,6 +460,17 @@ extern "C" int rvq_moe_route_forward(rvq_moe *h, const float *x, int32_t T, int3
 }
 
 static int take_device_error(rvq_moe *h) {
+    if (h->streaming) {
+        int rec[2] = {0, 0};  // never cleared: the bank is damaged
+        HIP_TRY(hipMemcpy(rec, h->cache.rec_err, sizeof rec, hipMemcpyDeviceToHost));
+        if (rec[0])
+            return fail(RVQ_MOE_ECORRUPT, "expert record check failed (flags 0x%x:%s%s%s%s; expert %d%s)", rec[0],
+                        (rec[0] & RVQ_MOE_RECORD_BAD_MAGIC) ? " magic/version" : "",
+                        (rec[0] & RVQ_MOE_RECORD_BAD_ID) ? " expert id" : "",
+                        (rec[0] & RVQ_MOE_RECORD_BAD_RANGE) ? " offset/size/shape" : "",
+                        (rec[0] & RVQ_MOE_RECORD_BAD_CRC) ? " payload crc32" : "", rec[1] - 1,
+                        "; the highest failing one");
+    }
     int flag = 0;
     HIP_TRY(hipMemcpy(&flag, h->ws.err, sizeof(int), hipMemcpyDeviceToHost));
     if (flag) {
@@ -485,6 +525,34 @@ extern "C" int rvq_moe_close(rvq_moe *h) {
     return rc;
 }
 
+extern "C" int rvq_moe_bank_layout(const rvq_moe_desc *desc, int64_t *record_stride, int64_t *payload_bytes) {
+    g_err[0] = 0;
+    if (!record_stride || !payload_bytes) return fail(RVQ_MOE_EINVAL, "null output pointer");
+    if (const int rc = check_shape(desc)) return rc;
+    const Geometry g = make_geometry(desc->d, desc->ffn, desc->n_experts, desc->top_k, desc->codebook_dtype);
+    *record_stride = bank_stride(g);
+    *payload_bytes = g.rec_int;
+    return RVQ_MOE_OK;
+}
+
+extern "C" int rvq_moe_write_bank(const rvq_moe_desc *desc, uint8_t *bank) {
+    g_err[0] = 0;
+    if (const int rc = check_shape(desc)) return rc;
+    const rvq_moe_desc &D = *desc;
+    if (!D.codes || !bank) return fail(RVQ_MOE_EINVAL, "null codes or bank");
+    if (D.codes_location != RVQ_MOE_CODES_DEVICE && D.codes_location != RVQ_MOE_CODES_PINNED_HOST)
+        return fail(RVQ_MOE_EINVAL, "codes_location=%d: canonical codes are DEVICE or PINNED_HOST", D.codes_location);
+    if (D.codes_location == RVQ_MOE_CODES_PINNED_HOST && !is_pinned_host(D.codes))
+        return fail(RVQ_MOE_EINVAL, "PINNED_HOST codes must be pinned host memory (hipHostMalloc)");
+    if (!is_pinned_host(bank)) return fail(RVQ_MOE_EINVAL, "bank must be pinned host memory (hipHostMalloc)");
+    const Geometry g = make_geometry(D.d, D.ffn, D.n_experts, D.top_k, D.codebook_dtype);
+    const hipError_t e = write_bank(g, D.codes, D.codes_location == RVQ_MOE_CODES_PINNED_HOST, bank,
+                                    static_cast<hipStream_t>(D.stream));
+    if (e != hipSuccess)
+        return fail(e == hipErrorOutOfMemory ? RVQ_MOE_ENOMEM : RVQ_MOE_EHIP, "write_bank: %s", hipGetErrorString(e));
+    return RVQ_MOE_OK;
+}
+
 extern "C" const char *rvq_moe_last_error(void) { return g_err; }
 
 extern "C" int rvq_moe_abi_version(void) { return RVQ_MOE_ABI_VERSION; }
@@ -498,6 +566,8 @@ extern "C" int rvq_moe_get_stats(const rvq_moe *h, rvq_moe_stats *out) {
     out->host_syncs = h->cache.syncs;
     out->prefetch_fills = h->cache.prefetch_fills;
     out->prefetch_hits = h->cache.prefetch_hits;
+    out->records_checked = h->cache.records_checked;
+    out->records_verified = h->cache.records_verified;
     return RVQ_MOE_OK;
 }
 

@@ -7,13 +7,20 @@
 // the router has decided, and consumed as they land; overlapping them does not
 // change any result.  [FR] "Budget RAM et fenêtre de performance étroite":
 // a bounded cache of experts, refusing a budget below one token's working set.
-// Here the "disk" is a pinned host bank (in the library's internal layout,
-// written once at open) and the cache is `S` HBM slots of one record each:
+// Here the "disk" is a pinned host record bank (payloads in the library's
+// internal layout, each followed by its trailer: written at open from
+// canonical codes, or written earlier by rvq_moe_write_bank and borrowed) and
+// the cache is `S` HBM slots of one record each:
 //   - a call's experts are made resident by hipMemcpyAsync on the library's
 //     copy stream, one record per copy, into least-recently-used slots;
-//   - per slot, `filled` (copy done; the compute stream waits on it) and
-//     `released` (the last kernel reading the slot is done; the next copy
-//     into the slot waits on it) events order the two streams;
+//   - [FR] "Architecture de streaming depuis le disque": every record read is
+//     checked.  After its copy (`copied` event) the check stream verifies the
+//     slot's trailer (magic, expert id, offset range) and, on request, the
+//     payload's CRC-32 as it landed in HBM, then records `filled`; a failure
+//     is flagged on the device and reported by the next sync;
+//   - per slot, `filled` (copy and checks done; the compute stream waits on
+//     it) and `released` (the last kernel reading the slot is done; the next
+//     copy into the slot waits on it) events order the streams;
 //   - a device table [E] of record pointers tells the kernels where each
 //     expert's codes are.  It is written on the compute stream by a small
 //     kernel whose arguments carry the call's (expert, slot) pairs: launch
@@ -46,24 +53,32 @@ __global__ __launch_bounds__(kSetPairs) void k_set_slots(const uint8_t **tab, Sl
 }
 
 hipError_t slots_open(SlotCache &c, const Geometry &g, int S, int max_pairs, const uint8_t *canon_host,
-                      hipStream_t s) {
+                      const uint8_t *bank, bool verify, hipStream_t s) {
     c.S = S;
     c.E = g.E;
-    c.rec = g.rec_int;
+    c.ex = record_expect(g);
+    c.rec = c.ex.stride;
+    c.verify = verify;
     hipError_t e;
     if ((e = hipMalloc(&c.slots, (size_t)(S * c.rec))) != hipSuccess) return e;
-    if ((e = hipHostMalloc(reinterpret_cast<void **>(&c.bank), (size_t)(g.E * c.rec), hipHostMallocDefault)) !=
-        hipSuccess)
-        return e;
+    if ((e = hipMalloc(&c.rec_err, 2 * sizeof(int))) != hipSuccess) return e;
+    if ((e = hipMemsetAsync(c.rec_err, 0, 2 * sizeof(int), s)) != hipSuccess) return e;
+    if (verify) {
+        if ((e = crc_plan_init(c.plan, c.ex.payload)) != hipSuccess) return e;
+        if ((e = hipMalloc(&c.part, sizeof(uint32_t) * kCrcMaxSpans)) != hipSuccess) return e;
+    }
     if ((e = hipHostMalloc(reinterpret_cast<void **>(&c.ids_host), sizeof(int32_t) * (size_t)max_pairs,
                            hipHostMallocDefault)) != hipSuccess)
         return e;
     if ((e = hipMalloc(&c.tab_dev, sizeof(uint8_t *) * (size_t)g.E)) != hipSuccess) return e;
     if ((e = hipMemsetAsync(c.tab_dev, 0, sizeof(uint8_t *) * (size_t)g.E, s)) != hipSuccess) return e;
     if ((e = hipStreamCreateWithFlags(&c.copy, hipStreamNonBlocking)) != hipSuccess) return e;
+    if ((e = hipStreamCreateWithFlags(&c.check, hipStreamNonBlocking)) != hipSuccess) return e;
+    c.copied.assign(S, nullptr);
     c.filled.assign(S, nullptr);
     c.released.assign(S, nullptr);
     for (int i = 0; i < S; i++) {
+        if ((e = hipEventCreateWithFlags(&c.copied[i], hipEventDisableTiming)) != hipSuccess) return e;
         if ((e = hipEventCreateWithFlags(&c.filled[i], hipEventDisableTiming)) != hipSuccess) return e;
         if ((e = hipEventCreateWithFlags(&c.released[i], hipEventDisableTiming)) != hipSuccess) return e;
     }
@@ -73,41 +88,61 @@ hipError_t slots_open(SlotCache &c, const Geometry &g, int S, int max_pairs, con
     c.prefetched.assign(S, 0);
     c.mark.assign(g.E, 0);
     c.clock = 0;
-    // the bank in the internal layout: canonical records go through the GPU
-    // (upload, repack, download) a few experts at a time
-    const int B = g.E < 8 ? g.E : 8;
-    uint8_t *canon = nullptr, *internal = nullptr;
-    if ((e = hipMalloc(&canon, (size_t)(B * g.rec_canon))) != hipSuccess) return e;
-    if ((e = hipMalloc(&internal, (size_t)(B * c.rec))) != hipSuccess) {
-        (void)hipFree(canon);
+    if (bank) {
+        c.bank = bank;
+        return hipStreamSynchronize(s);
+    }
+    if ((e = hipHostMalloc(reinterpret_cast<void **>(&c.own_bank), (size_t)(g.E * c.rec), hipHostMallocDefault)) !=
+        hipSuccess) {
+        c.own_bank = nullptr;
         return e;
     }
-    for (int e0 = 0; e0 < g.E && e == hipSuccess; e0 += B) {
-        const int n = g.E - e0 < B ? g.E - e0 : B;
-        e = hipMemcpyAsync(canon, canon_host + (int64_t)e0 * g.rec_canon, (size_t)(n * g.rec_canon),
-                           hipMemcpyHostToDevice, s);
-        if (e == hipSuccess) e = launch_repack(g, canon, internal, n, s);
-        if (e == hipSuccess)
-            e = hipMemcpyAsync(c.bank + (int64_t)e0 * c.rec, internal, (size_t)(n * c.rec), hipMemcpyDeviceToHost, s);
-        if (e == hipSuccess) e = hipStreamSynchronize(s);  // the staging buffers are reused
-    }
-    (void)hipFree(canon);
-    (void)hipFree(internal);
-    return e;
+    c.bank = c.own_bank;
+    return write_bank(g, canon_host, true, c.own_bank, s);
 }
 
 void slots_close(SlotCache &c) {
     if (c.copy) (void)hipStreamSynchronize(c.copy);
+    if (c.check) (void)hipStreamSynchronize(c.check);
+    for (hipEvent_t ev : c.copied)
+        if (ev) (void)hipEventDestroy(ev);
     for (hipEvent_t ev : c.filled)
         if (ev) (void)hipEventDestroy(ev);
     for (hipEvent_t ev : c.released)
         if (ev) (void)hipEventDestroy(ev);
     if (c.copy) (void)hipStreamDestroy(c.copy);
+    if (c.check) (void)hipStreamDestroy(c.check);
     (void)hipFree(c.slots);
     (void)hipFree(c.tab_dev);
-    if (c.bank) (void)hipHostFree(c.bank);
+    (void)hipFree(c.rec_err);
+    (void)hipFree(c.part);
+    crc_plan_free(c.plan);
+    if (c.own_bank) (void)hipHostFree(c.own_bank);
     if (c.ids_host) (void)hipHostFree(c.ids_host);
     c = SlotCache{};
+}
+
+// Copy expert e's record into `slot` and check it there; `filled[slot]` is
+// recorded once the checks are done.
+static hipError_t fill_slot(SlotCache &c, int slot, int e) {
+    uint8_t *dst = c.slots + (int64_t)slot * c.rec;
+    c.h2d_bytes += (uint64_t)c.rec;
+    hipError_t err = hipStreamWaitEvent(c.copy, c.released[slot], 0);
+    if (err == hipSuccess) err = hipStreamWaitEvent(c.copy, c.filled[slot], 0);  // the last checks stopped reading
+    if (err == hipSuccess)
+        err = hipMemcpyAsync(dst, c.bank + (int64_t)e * c.rec, (size_t)c.rec, hipMemcpyHostToDevice, c.copy);
+    if (err == hipSuccess) err = hipEventRecord(c.copied[slot], c.copy);
+    if (err == hipSuccess) err = hipStreamWaitEvent(c.check, c.copied[slot], 0);
+    if (err == hipSuccess && c.verify) err = launch_crc_spans(c.plan, dst, c.part, c.check);
+    if (err == hipSuccess)
+        err = launch_check_record(c.verify ? &c.plan : nullptr, dst, c.ex, e, c.verify ? c.part : nullptr, c.rec_err,
+                                  c.check);
+    if (err == hipSuccess) err = hipEventRecord(c.filled[slot], c.check);
+    if (err == hipSuccess) {
+        c.records_checked++;
+        if (c.verify) c.records_verified++;
+    }
+    return err;
 }
 
 hipError_t slots_acquire(SlotCache &c, const int *experts, int n, hipStream_t compute, std::vector<int> &used) {
@@ -144,12 +179,7 @@ hipError_t slots_acquire(SlotCache &c, const int *experts, int n, hipStream_t co
         c.prefetched[victim] = 0;
         used.push_back(victim);
         c.misses++;
-        c.h2d_bytes += (uint64_t)c.rec;
-        hipError_t err = hipStreamWaitEvent(c.copy, c.released[victim], 0);
-        if (err == hipSuccess)
-            err = hipMemcpyAsync(c.slots + (int64_t)victim * c.rec, c.bank + (int64_t)e * c.rec, (size_t)c.rec,
-                                 hipMemcpyHostToDevice, c.copy);
-        if (err == hipSuccess) err = hipEventRecord(c.filled[victim], c.copy);
+        hipError_t err = fill_slot(c, victim, e);
         if (err == hipSuccess) err = hipStreamWaitEvent(compute, c.filled[victim], 0);
         if (err != hipSuccess) return err;
     }
@@ -188,12 +218,7 @@ hipError_t slots_prefetch(SlotCache &c, const int *experts, int n) {
         c.last_use[victim] = now;
         c.prefetched[victim] = 1;
         c.prefetch_fills++;
-        c.h2d_bytes += (uint64_t)c.rec;
-        hipError_t err = hipStreamWaitEvent(c.copy, c.released[victim], 0);
-        if (err == hipSuccess)
-            err = hipMemcpyAsync(c.slots + (int64_t)victim * c.rec, c.bank + (int64_t)e * c.rec, (size_t)c.rec,
-                                 hipMemcpyHostToDevice, c.copy);
-        if (err == hipSuccess) err = hipEventRecord(c.filled[victim], c.copy);
+        const hipError_t err = fill_slot(c, victim, e);
         if (err != hipSuccess) return err;
     }
     return hipSuccess;

@@ -17,10 +17,13 @@ ROOT = os.path.dirname(PKG)
 LIB_PATH = os.path.join(PKG, "librvq_moe.so")
 HEADER = os.path.join(ROOT, "include", "rvq_moe.h")
 
-OK, EINVAL, ENOTSUP, EBUDGET, ENOMEM, EHIP, EDEVICE = 0, -1, -2, -3, -4, -5, -6
-STATUS_NAMES = {0: "OK", -1: "EINVAL", -2: "ENOTSUP", -3: "EBUDGET", -4: "ENOMEM", -5: "EHIP", -6: "EDEVICE"}
+OK, EINVAL, ENOTSUP, EBUDGET, ENOMEM, EHIP, EDEVICE, ECORRUPT = 0, -1, -2, -3, -4, -5, -6, -7
+STATUS_NAMES = {0: "OK", -1: "EINVAL", -2: "ENOTSUP", -3: "EBUDGET", -4: "ENOMEM", -5: "EHIP", -6: "EDEVICE",
+                -7: "ECORRUPT"}
 CB_F32, CB_F16 = 0, 1
-CODES_DEVICE, CODES_PINNED_HOST = 0, 1
+CODES_DEVICE, CODES_PINNED_HOST, CODES_PINNED_BANK = 0, 1, 2
+RECORD_MAGIC, RECORD_VERSION = 0x52515652, 1
+RECORD_BAD_MAGIC, RECORD_BAD_ID, RECORD_BAD_RANGE, RECORD_BAD_CRC = 1, 2, 4, 8
 KERNEL_KINDS = 4
 
 
@@ -48,6 +51,8 @@ class Desc(ctypes.Structure):
         ("max_tokens", ctypes.c_int32),
         ("chunk_min_tokens", ctypes.c_int32),
         ("lut_expert_tokens", ctypes.c_int32),
+        ("verify_records", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
         ("eps", ctypes.c_double),
         ("router_w", ctypes.c_void_p),
         ("codebooks", ctypes.c_void_p),
@@ -60,7 +65,23 @@ class Stats(ctypes.Structure):
     _fields_ = [(n, ctypes.c_uint64) for n in (
         "route_calls", "forward_calls", "tokens_routed", "tokens_forwarded", "expert_evals",
         "code_bytes_resident", "record_bytes", "codebook_bytes", "h2d_bytes", "slot_hits", "slot_misses",
-        "host_syncs", "prefetch_fills", "prefetch_hits")]
+        "host_syncs", "prefetch_fills", "prefetch_hits", "records_checked", "records_verified")]
+
+
+class RecordTrailer(ctypes.Structure):
+    """rvq_moe_record_trailer: the start of each record's 4 KiB trailer page."""
+    _fields_ = [
+        ("magic", ctypes.c_uint32),
+        ("version", ctypes.c_uint32),
+        ("expert", ctypes.c_uint32),
+        ("n_experts", ctypes.c_uint32),
+        ("offset", ctypes.c_uint64),
+        ("payload_bytes", ctypes.c_uint64),
+        ("d", ctypes.c_int32),
+        ("ffn", ctypes.c_int32),
+        ("crc32", ctypes.c_uint32),
+        ("reserved", ctypes.c_uint32),
+    ]
 
 
 _lib = None
@@ -79,6 +100,9 @@ def lib():
         L.rvq_moe_layer_forward.argtypes = [vp, vp, i32, vp, vp, vp, vp]
         L.rvq_moe_route_forward.argtypes = [vp, vp, i32, vp, vp, vp, vp]
         L.rvq_moe_prefetch.argtypes = [vp, vp, i32, i32, vp]
+        L.rvq_moe_bank_layout.argtypes = [ctypes.POINTER(Desc), ctypes.POINTER(ctypes.c_int64),
+                                          ctypes.POINTER(ctypes.c_int64)]
+        L.rvq_moe_write_bank.argtypes = [ctypes.POINTER(Desc), vp]
         L.rvq_moe_sync.argtypes = [vp, vp]
         L.rvq_moe_close.argtypes = [vp]
         L.rvq_moe_last_error.argtypes = []
@@ -89,7 +113,7 @@ def lib():
         L.rvq_moe_kernel_times.argtypes = [vp, ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(ctypes.c_uint64),
                                            ctypes.POINTER(ctypes.c_double), ctypes.c_int]
         for n in ("rvq_moe_open", "rvq_moe_route_topk", "rvq_moe_layer_forward", "rvq_moe_route_forward",
-                  "rvq_moe_prefetch", "rvq_moe_sync",
+                  "rvq_moe_prefetch", "rvq_moe_sync", "rvq_moe_bank_layout", "rvq_moe_write_bank",
                   "rvq_moe_close", "rvq_moe_abi_version", "rvq_moe_get_stats", "rvq_moe_set_profiling",
                   "rvq_moe_kernel_times"):
             getattr(L, n).restype = ctypes.c_int
@@ -132,12 +156,40 @@ def _stream(stream) -> int:
 
 def make_desc(*, d, ffn, n_experts, top_k, codebook_dtype, router_w, codebooks, codes,
               codes_location=CODES_DEVICE, cache_slots=0, pre_rmsnorm=False, eps=1e-6, residual=False,
-              max_tokens=1, chunk_min_tokens=0, lut_expert_tokens=0, stream=None, n_stages=3, n_codes=256,
-              vec_dim=8) -> Desc:
+              max_tokens=1, chunk_min_tokens=0, lut_expert_tokens=0, verify_records=False, stream=None,
+              n_stages=3, n_codes=256, vec_dim=8, reserved=0) -> Desc:
     return Desc(ctypes.sizeof(Desc), d, ffn, n_experts, top_k, n_stages, n_codes, vec_dim, codebook_dtype,
                 codes_location, cache_slots, int(bool(pre_rmsnorm)), int(bool(residual)), max_tokens,
-                chunk_min_tokens, lut_expert_tokens, eps, _ptr(router_w), _ptr(codebooks), _ptr(codes),
-                _stream(stream) if stream != 0 else 0)
+                chunk_min_tokens, lut_expert_tokens, int(bool(verify_records)), reserved, eps, _ptr(router_w),
+                _ptr(codebooks), _ptr(codes), _stream(stream) if stream != 0 else 0)
+
+
+def bank_layout(**kw) -> tuple[int, int]:
+    """rvq_moe_bank_layout: (record stride, payload bytes) of the layer's record bank."""
+    kw.setdefault("router_w", None)
+    kw.setdefault("codebooks", None)
+    kw.setdefault("codes", None)
+    kw.setdefault("stream", 0)
+    desc = make_desc(**kw)
+    stride, payload = ctypes.c_int64(), ctypes.c_int64()
+    _check(lib().rvq_moe_bank_layout(ctypes.byref(desc), ctypes.byref(stride), ctypes.byref(payload)),
+           "rvq_moe_bank_layout")
+    return stride.value, payload.value
+
+
+def write_bank(bank, **kw) -> None:
+    """rvq_moe_write_bank into `bank` (a pinned host tensor of n_experts * stride bytes)."""
+    kw.setdefault("router_w", None)
+    kw.setdefault("codebooks", None)
+    desc = make_desc(**kw)
+    _check(lib().rvq_moe_write_bank(ctypes.byref(desc), _ptr(bank)), "rvq_moe_write_bank")
+
+
+def read_trailer(bank_bytes, expert: int, stride: int, payload: int) -> RecordTrailer:
+    """The trailer of record `expert` from a host byte buffer (numpy uint8 / bytes) of the bank."""
+    off = expert * stride + (payload + 4095) // 4096 * 4096
+    raw = bytes(bank_bytes[off:off + ctypes.sizeof(RecordTrailer)])
+    return RecordTrailer.from_buffer_copy(raw)
 
 
 def open_raw(desc: Desc) -> tuple[int, int]:
