@@ -484,8 +484,7 @@ struct LayerArgs {
     double *sel;        // [T][k] selected logits by rank
     int *gbar;          // [4][kMaxGridGroups + 1] grid arrival counters: y init, logits, ranks, exit
     double *rl_cur, *rl_next;  // [T][E] logit slots of this launch and of the next (in-launch routing)
-    double *sl_cur, *sl_next;  // [T * k] selected-logit slots of this launch and of the next
-    double *si_cur;            // [T * k] selected ids of this launch (announced by the logit slot)
+    double *sl_cur, *sl_next;  // [T * k] selected-id slots of this launch and of the next
     const int *list;    // pairs handed over by the chunk path (n, then the order table), or null
     const uint8_t *codes;
     const uint8_t *const *slot_tab;  // [E] record of each expert (HBM slot cache), or null: codes + e * rec
@@ -793,11 +792,12 @@ __device__ inline SegB next_b(const SegB &c, int un, int u1, int n_tf, int n_cd,
 //  R2  per token, it polls the E logit slots until none holds the marker (the
 //      poll reads the logits themselves) and ranks each of its own experts (one
 //      comparison per thread, counted by the barrier); an expert of rank < k
-//      publishes its id, then (after its store completed) its logit, into
-//      selection slot [token][rank];
-//  R3  every workgroup polls the k selection slots of every token, takes ids
-//      and selected logits in rank order into LDS, and forms the gates (one exp
-//      each, summed in slot order).  Workgroup 0 writes ids and gates out.
+//      publishes its id into selection slot [token][rank] (marker NaN until
+//      then);
+//  R3  every workgroup polls the k selection slots of every token, takes the
+//      ids in rank order and their logits (already in hand from R2) into LDS,
+//      and forms the gates (one exp each, summed in slot order).  Workgroup 0
+//      writes ids and gates out.
 constexpr int kRouteExp = 4;  // experts per workgroup (E <= 4 G)
 __device__ void route_phase(const LayerArgs &a, double *scratch, float *gate_lds, int *pair_ids) {
     const Geometry &g = a.g;
@@ -811,31 +811,43 @@ __device__ void route_phase(const LayerArgs &a, double *scratch, float *gate_lds
     double *red = ex + kRouteMaxPairs;    // [kWaves][kRouteExp + 1]
     const int P = a.T * g.k;
     // ---- R1
+    // own experts of this workgroup (wave-uniform): loads only for those
+    const int n_own = min(kRouteExp, (g.E - wg + G - 1) / G);
     for (int t = 0; t < a.T; t++) {
         const float4 *x4 = reinterpret_cast<const float4 *>(a.x + (size_t)t * g.d);
         double acc[kRouteExp], ss = 0.0;
 #pragma unroll
         for (int j = 0; j < kRouteExp; j++) acc[j] = 0.0;
-        for (int i = threadIdx.x; i < n4; i += kBlock) {
-            // loads for all experts are unconditional (a clamped expert index,
-            // dropped at use), so they are in flight together
-            const float4 xv = x4[i];
-            float4 wv[kRouteExp];
+        // two input blocks per step, every load of both issued before any sum
+        // (clamped indices, masked at use), so one round trip serves 2 kBlock
+        // float4 columns
+        for (int i0 = threadIdx.x; i0 < n4; i0 += 2 * kBlock) {
+            float4 xv[2], wv[2][kRouteExp];
 #pragma unroll
-            for (int j = 0; j < kRouteExp; j++)
-                wv[j] = reinterpret_cast<const float4 *>(a.Wt + (size_t)min(wg + j * G, g.E - 1) * g.d)[i];
-            if (a.pre) {
-                ss = fma((double)xv.x, (double)xv.x, ss);
-                ss = fma((double)xv.y, (double)xv.y, ss);
-                ss = fma((double)xv.z, (double)xv.z, ss);
-                ss = fma((double)xv.w, (double)xv.w, ss);
+            for (int h = 0; h < 2; h++) {
+                const int i = min(i0 + h * kBlock, n4 - 1);
+                xv[h] = x4[i];
+#pragma unroll
+                for (int j = 0; j < kRouteExp; j++)
+                    if (j < n_own) wv[h][j] = reinterpret_cast<const float4 *>(a.Wt + (size_t)(wg + j * G) * g.d)[i];
             }
 #pragma unroll
-            for (int j = 0; j < kRouteExp; j++) {
-                acc[j] = fma((double)xv.x, (double)wv[j].x, acc[j]);
-                acc[j] = fma((double)xv.y, (double)wv[j].y, acc[j]);
-                acc[j] = fma((double)xv.z, (double)wv[j].z, acc[j]);
-                acc[j] = fma((double)xv.w, (double)wv[j].w, acc[j]);
+            for (int h = 0; h < 2; h++) {
+                if (i0 + h * kBlock >= n4) break;
+                if (a.pre) {
+                    ss = fma((double)xv[h].x, (double)xv[h].x, ss);
+                    ss = fma((double)xv[h].y, (double)xv[h].y, ss);
+                    ss = fma((double)xv[h].z, (double)xv[h].z, ss);
+                    ss = fma((double)xv[h].w, (double)xv[h].w, ss);
+                }
+#pragma unroll
+                for (int j = 0; j < kRouteExp; j++) {
+                    if (j >= n_own) break;
+                    acc[j] = fma((double)xv[h].x, (double)wv[h][j].x, acc[j]);
+                    acc[j] = fma((double)xv[h].y, (double)wv[h][j].y, acc[j]);
+                    acc[j] = fma((double)xv[h].z, (double)wv[h][j].z, acc[j]);
+                    acc[j] = fma((double)xv[h].w, (double)wv[h][j].w, acc[j]);
+                }
             }
         }
 #pragma unroll
@@ -847,7 +859,7 @@ __device__ void route_phase(const LayerArgs &a, double *scratch, float *gate_lds
             red[wave * (kRouteExp + 1) + kRouteExp] = ss;
         }
         __syncthreads();
-        if (threadIdx.x < kRouteExp) {
+        if (threadIdx.x < n_own) {
             const int j = threadIdx.x, e = wg + j * G;
             double sa = 0.0, sq = 0.0;
             for (int w = 0; w < kWaves; w++) {
@@ -855,10 +867,8 @@ __device__ void route_phase(const LayerArgs &a, double *scratch, float *gate_lds
                 sq += red[w * (kRouteExp + 1) + kRouteExp];
             }
             const double r = a.pre ? sqrt(sq / (double)g.d + a.eps) : 1.0;
-            if (e < g.E) {
-                store_coherent(a.rl_cur + (size_t)t * g.E + e, sa / r);
-                store_coherent(a.rl_next + (size_t)t * g.E + e, unpub);
-            }
+            store_coherent(a.rl_cur + (size_t)t * g.E + e, sa / r);
+            store_coherent(a.rl_next + (size_t)t * g.E + e, unpub);
         }
         __syncthreads();
     }
@@ -890,9 +900,7 @@ __device__ void route_phase(const LayerArgs &a, double *scratch, float *gate_lds
             const int rank = __syncthreads_count(i < g.E && (lg[i] > me || (lg[i] == me && i < e)));
             if (rank < g.k && threadIdx.x == 0) {
                 const int slot = t * g.k + rank;
-                store_coherent(a.si_cur + slot, (double)e);
-                wait_stores();  // the id lands before the logit that announces it
-                store_coherent(a.sl_cur + slot, me);
+                store_coherent(a.sl_cur + slot, (double)e);
                 store_coherent(a.sl_next + slot, unpub);
             }
         }
@@ -907,7 +915,25 @@ __device__ void route_phase(const LayerArgs &a, double *scratch, float *gate_lds
         }
         if (__syncthreads_and(ready) || timed_out()) break;
     }
-    for (int i = threadIdx.x; i < P; i += kBlock) pair_ids[i] = (int)load_coherent(a.si_cur + i);
+    // the selected logits: every workgroup holds the last token's E logits in
+    // LDS (read in R2); an earlier token's are read back from its slots, which
+    // R2 saw published
+    for (int i = threadIdx.x; i < P; i += kBlock) {
+        const double v = sel[i];  // the marker only after a timed-out wait: an invalid id
+        const int e = (v >= 0.0 && v < (double)g.E) ? (int)v : -1, t = i / g.k;
+        pair_ids[i] = e;
+        double l;
+        if (e < 0) {
+            l = -INFINITY;
+        } else if (t == a.T - 1) {
+            l = lg[e];
+        } else {
+            l = load_coherent(a.rl_cur + (size_t)t * g.E + e);
+            l = isnan(l) ? -INFINITY : l;
+        }
+        sel[i] = l;
+    }
+    __syncthreads();
     for (int i = threadIdx.x; i < P; i += kBlock) ex[i] = exp(sel[i] - sel[(i / g.k) * g.k]);
     __syncthreads();
     for (int i = threadIdx.x; i < P; i += kBlock) {
@@ -1179,7 +1205,7 @@ hipError_t launch_layer(const Geometry &g, Workspace &w, const uint8_t *codes, c
                         const void *cbs, const float *Wt, const float *x, const int32_t *ids, const float *gates,
                         float *y, int T, int pre, int residual, double eps, bool route, hipStream_t s,
                         const int *list) {
-    double *rl_cur = nullptr, *rl_next = nullptr, *sl_cur = nullptr, *sl_next = nullptr, *si_cur = nullptr;
+    double *rl_cur = nullptr, *rl_next = nullptr, *sl_cur = nullptr, *sl_next = nullptr;
     if (route) {  // the slot buffers (see fused_route_slots) alternate between calls
         const int64_t cap = w.route_cap, P = cap / g.E * g.k;
         const int par = w.fused_parity;
@@ -1187,10 +1213,9 @@ hipError_t launch_layer(const Geometry &g, Workspace &w, const uint8_t *codes, c
         rl_next = w.fused_logits + (par ? 0 : cap);
         sl_cur = w.fused_logits + 2 * cap + (par ? P : 0);
         sl_next = w.fused_logits + 2 * cap + (par ? 0 : P);
-        si_cur = w.fused_logits + 2 * cap + 2 * P + (par ? P : 0);
         w.fused_parity ^= 1;
     }
-    LayerArgs a{Wt, w.logits, w.sel, w.gbar, rl_cur, rl_next, sl_cur, sl_next, si_cur, list, codes, slot_tab, cbs, x,
+    LayerArgs a{Wt, w.logits, w.sel, w.gbar, rl_cur, rl_next, sl_cur, sl_next, list, codes, slot_tab, cbs, x,
                 ids, gates, y, w.part_gu, w.cntA, w.err, g, T, pre, residual, eps};
     // A plain launch of exactly as many workgroups as can be resident at once
     // (sized at open from the occupancy query); the inter-workgroup waits are
