@@ -156,7 +156,7 @@ static int open_impl(const rvq_moe_desc *desc, rvq_moe *h) {
     HIP_TRY(hipMalloc(&h->ws.route_logits, sizeof(double) * (size_t)route_logit_slots(T, D.n_experts)));
     HIP_TRY(hipMalloc(&h->ws.fused_logits, sizeof(double) * (size_t)fused_route_slots(T, D.n_experts, D.top_k)));
     HIP_TRY(hipMalloc(&h->ws.part_gu, sizeof(float) * (size_t)(P * 2 * g.m[0].n_tiles * g.ffn_pad)));
-    HIP_TRY(hipMalloc(&h->ws.cntA, sizeof(int) * (size_t)P));
+    HIP_TRY(hipMalloc(&h->ws.cntA, sizeof(int) * (size_t)P * kCntStride));
     HIP_TRY(hipMalloc(&h->ws.gbar, sizeof(int) * kGbarInts));
     HIP_TRY(hipMalloc(&h->ws.err, sizeof(int)));
     if (h->max_tokens >= h->chunk_min) {
@@ -176,7 +176,7 @@ static int open_impl(const rvq_moe_desc *desc, rvq_moe *h) {
     HIP_TRY(init_route(h->ws, D.n_experts, D.top_k, T, n_cu, s));
     h->ws.n_wg = n_cu * per_cu;
     if (h->ws.n_wg > 1024) h->ws.n_wg = 1024;  // grid arrival counters cover up to 1024 workgroups
-    HIP_TRY(hipMemsetAsync(h->ws.cntA, 0, sizeof(int) * (size_t)P, s));
+    HIP_TRY(hipMemsetAsync(h->ws.cntA, 0, sizeof(int) * (size_t)P * kCntStride, s));
     HIP_TRY(hipMemsetAsync(h->ws.gbar, 0, sizeof(int) * kGbarInts, s));
     HIP_TRY(hipMemsetAsync(h->ws.err, 0, sizeof(int), s));
     HIP_TRY(hipMemcpyAsync(h->cbs, D.codebooks, (size_t)(E * g.cb_bytes), hipMemcpyDeviceToDevice, s));

@@ -152,7 +152,7 @@ struct Workspace {
     int fused_parity;      // buffer of the next in-launch routing
     bool route_one;        // the one-token kernel fits (all E workgroups resident)
     float *part_gu;     // [T*k][2][n_tiles_in][ffn_pad] partial gate/up sums
-    int *cntA;          // [T*k] finished gate/up chunks per pair (self-resetting)
+    int *cntA;          // [T*k][kCntStride] finished gate/up chunks per pair (self-resetting)
     int *gbar;          // grid arrival counters of the persistent kernel (self-resetting)
     int *err;           // device error flag: bit 0 bad id, bit 1 wait timeout
     int n_wg;           // persistent workgroups (all resident at once: blocks per CU x CUs)
@@ -175,6 +175,10 @@ struct ChunkWork {
 // << 16, pair index, expert id.
 constexpr int kOrderMax = 512;
 constexpr int kPairListInts = 1 + 3 * kOrderMax;
+
+// Per-pair completion counters sit kCntStride ints (256 B) apart: counters
+// that share a cache line slow each other's atomics and polls down.
+constexpr int kCntStride = 64;
 
 constexpr int kMaxExperts = 1024;
 constexpr int kMaxTopK = 64;

@@ -436,18 +436,60 @@ __device__ __forceinline__ int gather_segment(float *lut, const Stage &st, const
 // waits for its stores to complete (vmcnt 0), then a barrier, then one thread
 // adds to a counter; consumers wait on the counter.
 //
-// Wait until *cnt >= target (bounded: after ~0.5 s the error flag gets bit 2 and
-// the wait gives up, so every wave always reaches the end of the kernel).
-// Consumers read the published data with coherent loads after the barrier.
+// Poll until *cnt >= target (one lane), one load at a time with a short sleep
+// (more polls in flight slow the counter's own atomics down).  Bounded: after
+// ~0.5 s the error flag gets bit 2 and the poll gives up, so every wave
+// reaches the end of the kernel.
+__device__ inline void poll_count(const int *cnt, int target, int *err) {
+    const uint64_t t0 = wall_clock64();
+    while (load_counter(cnt) < target) {
+        __builtin_amdgcn_s_sleep(2);
+        if (wall_clock64() - t0 > 50000000ull) {
+            atomicOr(err, 2);
+            return;
+        }
+    }
+}
+
+// Wait until *cnt >= target.  Consumers read the published data with coherent
+// loads after the barrier.
 __device__ inline void wait_count(const int *cnt, int target, int *err) {
-    if (threadIdx.x == 0) {
-        const uint64_t t0 = wall_clock64();
-        while (load_counter(cnt) < target) {
-            __builtin_amdgcn_s_sleep(2);
-            if (wall_clock64() - t0 > 50000000ull) {
-                atomicOr(err, 2);
-                break;
-            }
+    if (threadIdx.x == 0) poll_count(cnt, target, err);
+    __syncthreads();
+}
+
+// wait_count for a phase-B segment whose pair may still be in phase A
+// elsewhere: while wave 0 polls, waves 1.. read ahead the segment's code
+// blocks [q0, q1) this workgroup gathers later (round-robin over those waves,
+// at most two blocks in flight per wave), so the wait moves code bytes from
+// HBM into the caches instead of leaving the link idle.  The blocks land in
+// LDS through LDS-DMA loads (no registers) into `sink`, 4 KB per wave of
+// table area that is idle until the next table build; their values are never
+// read.  The waves stop reading ahead once the count is seen (or their blocks
+// run out).  The caller waits for this wave's memory operations (vmcnt 0)
+// before the sink area is written again.
+__device__ inline void wait_count_fill(const int *cnt, int target, int *err, const uint8_t *tile_base, int q0,
+                                       int q1, float *sink) {
+    __shared__ int seen;
+    const int wave = wave_id(), lane = threadIdx.x & 63;
+    if (threadIdx.x == 0) seen = 0;
+    __syncthreads();
+    if (wave == 0) {
+        if (lane == 0) {
+            poll_count(cnt, target, err);
+            __hip_atomic_store(&seen, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        }
+    } else {
+        auto *dst = (__attribute__((address_space(3))) char *)(reinterpret_cast<char *>(sink) + wave * 4096);
+        for (int q = q0 + wave - 1; q < q1; q += kWaves - 1) {
+            if (__hip_atomic_load(&seen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)) break;
+            const auto *src = global_view(tile_base + (int64_t)q * kChunkBytes + lane * 16);
+#pragma unroll
+            for (int st = 0; st < kStages; st++)
+                __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)(src + st * 1024),
+                                                 (__attribute__((address_space(3))) void *)(dst + st * 1024), 16, 0,
+                                                 0);
+            asm volatile("s_waitcnt vmcnt(3)" ::: "memory");  // at most two blocks in flight
         }
     }
     __syncthreads();
@@ -494,7 +536,7 @@ struct LayerArgs {
     const float *gates;
     float *y;
     float *part_gu;  // [P][2][n_ti][ffn_pad]
-    int *cntA;       // [P]
+    int *cntA;       // [P][kCntStride]: finished gate/up chunks of pair p at p * kCntStride
     int *err;
     Geometry g;
     int T;
@@ -1091,7 +1133,7 @@ __global__ __launch_bounds__(kBlock) void k_layer(LayerArgs a) {
                 if (pend_out) flush_rows(ast, pend_out, pend_c0, pend_c1);
                 build_lut<CB>(lut, vs, tile_exponent(red2));
                 if (pend_out)
-                    signal(&a.cntA[pend_p], pend_n);  // its barrier also ends the build
+                    signal(a.cntA + pend_p * kCntStride, pend_n);  // its barrier also ends the build
                 else
                     __syncthreads();
                 if (un < u1) prefetch(nxt);
@@ -1106,10 +1148,10 @@ __global__ __launch_bounds__(kBlock) void k_layer(LayerArgs a) {
                 if (pend_out) {
                     __syncthreads();
                     flush_rows(ast, pend_out, pend_c0, pend_c1);
-                    signal(&a.cntA[pend_p], pend_n);
+                    signal(a.cntA + pend_p * kCntStride, pend_n);
                     pend_out = nullptr;
                 }
-                signal(&a.cntA[cur.p], cur.c1 - cur.c0);
+                signal(a.cntA + cur.p * kCntStride, cur.c1 - cur.c0);
                 if (un < u1) prefetch(nxt);
             }
             cur = nxt;
@@ -1118,7 +1160,7 @@ __global__ __launch_bounds__(kBlock) void k_layer(LayerArgs a) {
         if (pend_out) {
             __syncthreads();
             flush_rows(ast, pend_out, pend_c0, pend_c1);
-            signal(&a.cntA[pend_p], pend_n);
+            signal(a.cntA + pend_p * kCntStride, pend_n);
         }
     }
     if (!y_signalled) signal(a.gbar + kMaxGridGroups, 0);  // no phase-A work: a zero count, then the y count
@@ -1145,8 +1187,9 @@ __global__ __launch_bounds__(kBlock) void k_layer(LayerArgs a) {
                 u32x4 p[3];
                 if (cur.c0 + wave < cur.c1)
                     load_chunk(base + (int64_t)(cur.c0 + wave) * kChunkBytes, lane, p[0], p[1], p[2], kNT);
-                wait_count(&a.cntA[cur.p], needA, a.err);
+                wait_count_fill(a.cntA + cur.p * kCntStride, needA, a.err, base, cur.c0 + kWaves, cur.c1, lut);
                 finish_h(a, gate_src, cur.p, cur.ft, vs, hred, red2);
+                wait_stores();  // read-ahead blocks landed in the table area before it is rebuilt
                 __syncthreads();
                 build_lut<CB>(lut, vs, tile_exponent(red2));
                 __syncthreads();
@@ -1184,7 +1227,7 @@ __global__ __launch_bounds__(kBlock) void k_layer(LayerArgs a) {
     if (threadIdx.x == 0) last = atomicAdd(xb, 1) == G - 1;
     __syncthreads();
     if (last) {
-        for (int i = threadIdx.x; i < P; i += kBlock) store_counter(a.cntA + (kList ? o_pair[i] : i), 0);
+        for (int i = threadIdx.x; i < P; i += kBlock) store_counter(a.cntA + (kList ? o_pair[i] : i) * kCntStride, 0);
         if (threadIdx.x < 4) store_counter(a.gbar + threadIdx.x * (kMaxGridGroups + 1) + kMaxGridGroups, 0);
     }
 }
