@@ -1077,15 +1077,28 @@ __global__ __launch_bounds__(kBlock) void k_layer(LayerArgs a) {
             store_coherent(a.y + i, a.residual ? a.x[i] : 0.f);
     }
     bool y_ready = false;
-    bool y_signalled = false;  // this workgroup's y stores are published with its first phase-A count
-    auto signal = [&](int *cnt, int n) {  // publish this workgroup's completed stores
+    // Phase-A chunk counts are published per pair, once the workgroup moves on
+    // to another pair or ends phase A (phase B waits for a pair's total), so
+    // only those transitions wait for the stores to complete.  The y stores
+    // are published with the first publication, at the latest at the second
+    // segment's transition.
+    bool y_signalled = false;
+    int acc_p = -1, acc_n = 0;  // flushed chunks of pair acc_p not yet published
+    auto publish = [&]() {      // all threads
         wait_stores();
         __syncthreads();
         if (threadIdx.x == 0) {
-            atomicAdd(cnt, n);
+            if (acc_p >= 0) atomicAdd(a.cntA + acc_p * kCntStride, acc_n);
             if (!y_signalled) atomicAdd(a.gbar + kMaxGridGroups, 1);
         }
         y_signalled = true;
+        acc_p = -1;
+        acc_n = 0;
+    };
+    auto count = [&](int pp, int n) {  // n chunks of pair pp flushed (stores issued); all threads
+        if (acc_p >= 0 && acc_p != pp) publish();
+        acc_p = pp;
+        acc_n += n;
     };
 
     // ---------------- phase A: gate and up
@@ -1132,10 +1145,11 @@ __global__ __launch_bounds__(kBlock) void k_layer(LayerArgs a) {
                 __syncthreads();
                 if (pend_out) flush_rows(ast, pend_out, pend_c0, pend_c1);
                 build_lut<CB>(lut, vs, tile_exponent(red2));
-                if (pend_out)
-                    signal(a.cntA + pend_p * kCntStride, pend_n);  // its barrier also ends the build
-                else
-                    __syncthreads();
+                if (pend_out) {
+                    count(pend_p, pend_n);
+                    if (!y_signalled) publish();
+                }
+                __syncthreads();
                 if (un < u1) prefetch(nxt);
                 float *out = a.part_gu + (((int64_t)cur.p * 2 + cur.m) * n_ti + cur.tile) * g.ffn_pad;
                 pend_c0 = gather_segment<false, true>(lut, ast, base, cur.c0, cur.c1, out, 0, p, kNT);
@@ -1148,10 +1162,10 @@ __global__ __launch_bounds__(kBlock) void k_layer(LayerArgs a) {
                 if (pend_out) {
                     __syncthreads();
                     flush_rows(ast, pend_out, pend_c0, pend_c1);
-                    signal(a.cntA + pend_p * kCntStride, pend_n);
+                    count(pend_p, pend_n);
                     pend_out = nullptr;
                 }
-                signal(a.cntA + cur.p * kCntStride, cur.c1 - cur.c0);
+                count(cur.p, cur.c1 - cur.c0);
                 if (un < u1) prefetch(nxt);
             }
             cur = nxt;
@@ -1160,10 +1174,10 @@ __global__ __launch_bounds__(kBlock) void k_layer(LayerArgs a) {
         if (pend_out) {
             __syncthreads();
             flush_rows(ast, pend_out, pend_c0, pend_c1);
-            signal(a.cntA + pend_p * kCntStride, pend_n);
+            count(pend_p, pend_n);
         }
     }
-    if (!y_signalled) signal(a.gbar + kMaxGridGroups, 0);  // no phase-A work: a zero count, then the y count
+    if (acc_p >= 0 || !y_signalled) publish();  // the last pair's count (and y, if not yet)
 
     // ---------------- phase B: SwiGLU finish, gate, down
     {
