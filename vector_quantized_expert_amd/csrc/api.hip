@@ -107,8 +107,7 @@ static void free_handle(rvq_moe *h) {
     (void)hipFree(h->ws.route_logits);
     (void)hipFree(h->ws.fused_logits);
     (void)hipFree(h->ws.part_gu);
-    (void)hipFree(h->ws.cntA);
-    (void)hipFree(h->ws.gbar);
+    (void)hipFree(h->ws.cnt);
     (void)hipFree(h->ws.err);
     (void)hipFree(h->cw.X);
     (void)hipFree(h->cw.H);
@@ -156,8 +155,9 @@ static int open_impl(const rvq_moe_desc *desc, rvq_moe *h) {
     HIP_TRY(hipMalloc(&h->ws.route_logits, sizeof(double) * (size_t)route_logit_slots(T, D.n_experts)));
     HIP_TRY(hipMalloc(&h->ws.fused_logits, sizeof(double) * (size_t)fused_route_slots(T, D.n_experts, D.top_k)));
     HIP_TRY(hipMalloc(&h->ws.part_gu, sizeof(float) * (size_t)(P * 2 * g.m[0].n_tiles * g.ffn_pad)));
-    HIP_TRY(hipMalloc(&h->ws.cntA, sizeof(int) * (size_t)P * kCntStride));
-    HIP_TRY(hipMalloc(&h->ws.gbar, sizeof(int) * kGbarInts));
+    h->ws.cnt_per_set = (int)(P + 1);
+    h->ws.cnt_phase = 0;
+    HIP_TRY(hipMalloc(&h->ws.cnt, sizeof(int) * (size_t)kCntSets * (P + 1) * kCntStride));
     HIP_TRY(hipMalloc(&h->ws.err, sizeof(int)));
     if (h->max_tokens >= h->chunk_min) {
         HIP_TRY(hipMalloc(&h->cw.X, 2 * (size_t)(P * D.d)));
@@ -175,9 +175,8 @@ static int open_impl(const rvq_moe_desc *desc, rvq_moe *h) {
     if (n_cu < 1 || per_cu < 1) return fail(RVQ_MOE_EHIP, "occupancy query gave %d CUs x %d blocks", n_cu, per_cu);
     HIP_TRY(init_route(h->ws, D.n_experts, D.top_k, T, n_cu, s));
     h->ws.n_wg = n_cu * per_cu;
-    if (h->ws.n_wg > 1024) h->ws.n_wg = 1024;  // grid arrival counters cover up to 1024 workgroups
-    HIP_TRY(hipMemsetAsync(h->ws.cntA, 0, sizeof(int) * (size_t)P * kCntStride, s));
-    HIP_TRY(hipMemsetAsync(h->ws.gbar, 0, sizeof(int) * kGbarInts, s));
+    if (h->ws.n_wg > 1024) h->ws.n_wg = 1024;  // a bound on the persistent grid
+    HIP_TRY(hipMemsetAsync(h->ws.cnt, 0, sizeof(int) * (size_t)kCntSets * (P + 1) * kCntStride, s));
     HIP_TRY(hipMemsetAsync(h->ws.err, 0, sizeof(int), s));
     HIP_TRY(hipMemcpyAsync(h->cbs, D.codebooks, (size_t)(E * g.cb_bytes), hipMemcpyDeviceToDevice, s));
     HIP_TRY(launch_transpose(D.router_w, h->router_wt, D.d, D.n_experts, s));

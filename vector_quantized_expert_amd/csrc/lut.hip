@@ -15,15 +15,15 @@
 // MI355X mapping
 // --------------
 // * One workgroup (16 waves) per CU, as many as can be resident at once (LDS
-//   use allows one per CU).  The call's work is three phases of 32-row chunks:
+//   use allows one per CU).  The call's work is two phases of 32-row chunks:
 //     A  gate and up: (pair, matrix, 32-slice tile) segments x row chunks,
-//     B  down:        (pair, 32-slice tile of h) segments x row chunks,
-//     C  final sum of the down partials (+ residual) per token.
+//     B  down:        (pair, 32-slice tile of h) segments x row chunks, each
+//        row total times the routing gate added into y with fp32 atomics.
 //   Each phase's chunks are split into equal contiguous ranges, one per
 //   workgroup, so every CU streams the same number of code bytes.  A segment
 //   whose range is cut between two workgroups is built twice (its table) but
-//   read once (its codes).  Per-pair counters order A before B and per-token
-//   counters order B before C; the last workgroup out resets them.
+//   read once (its codes).  Per-pair counters order A before B; launches
+//   alternate between two counter sets, each zeroing the other one as it ends.
 // * Table layout in LDS (128 KB), byte address for stage s, code c, lane l:
 //     s = 0: c*256 + 4l;   s = 1: c*256 + 128 + 4l;   s = 2: 65536 + c*256 + 4l.
 //   Lane l of each half-wave always serves slice l, so a half-wave's 32 random
@@ -495,28 +495,6 @@ __device__ inline void wait_count_fill(const int *cnt, int target, int *err, con
     __syncthreads();
 }
 
-// Grid-wide arrival counts without a hot spot: workgroups arrive in groups of
-// kGridGroup on their own counter; the last of a group resets it and bumps
-// the top counter, which waiters poll.  (256 arrivals on one address
-// serialise at the device-scope atomic unit: several microseconds.)
-constexpr int kGridGroup = 16;
-constexpr int kMaxGridGroups = 64;  // up to 1024 workgroups
-
-// counter block layout: [barrier][kMaxGridGroups + 1]; entry kMaxGridGroups is the top
-__device__ inline void grid_arrive(int *blk) {
-    wait_stores();
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        const int G = gridDim.x, grp = blockIdx.x / kGridGroup;
-        const int gsz = min(kGridGroup, G - grp * kGridGroup);
-        if (atomicAdd(blk + grp, 1) == gsz - 1) {
-            store_counter(blk + grp, 0);
-            atomicAdd(blk + kMaxGridGroups, 1);
-        }
-    }
-}
-
-__device__ inline int grid_groups() { return (gridDim.x + kGridGroup - 1) / kGridGroup; }
 
 // ---------------------------------------------------------------------------
 struct LayerArgs {
@@ -524,7 +502,9 @@ struct LayerArgs {
     const float *Wt;    // [E][d] transposed router
     double *logits;     // [T][E]
     double *sel;        // [T][k] selected logits by rank
-    int *gbar;          // [4][kMaxGridGroups + 1] grid arrival counters: y init, logits, ranks, exit
+    int *ycnt;          // workgroups whose initial y stores are out (this launch's counter set)
+    int *cnt_clear;     // the other counter set, zeroed as this launch ends: n_clear counters kCntStride apart
+    int n_clear;
     double *rl_cur, *rl_next;  // [T][E] logit slots of this launch and of the next (in-launch routing)
     double *sl_cur, *sl_next;  // [T * k] selected-id slots of this launch and of the next
     const int *list;    // pairs handed over by the chunk path (n, then the order table), or null
@@ -536,7 +516,7 @@ struct LayerArgs {
     const float *gates;
     float *y;
     float *part_gu;  // [P][2][n_ti][ffn_pad]
-    int *cntA;       // [P][kCntStride]: finished gate/up chunks of pair p at p * kCntStride
+    int *cntA;       // this launch's set: finished gate/up chunks of pair p at p * kCntStride
     int *err;
     Geometry g;
     int T;
@@ -1089,7 +1069,7 @@ __global__ __launch_bounds__(kBlock) void k_layer(LayerArgs a) {
         __syncthreads();
         if (threadIdx.x == 0) {
             if (acc_p >= 0) atomicAdd(a.cntA + acc_p * kCntStride, acc_n);
-            if (!y_signalled) atomicAdd(a.gbar + kMaxGridGroups, 1);
+            if (!y_signalled) atomicAdd(a.ycnt, 1);
         }
         y_signalled = true;
         acc_p = -1;
@@ -1209,7 +1189,7 @@ __global__ __launch_bounds__(kBlock) void k_layer(LayerArgs a) {
                 __syncthreads();
                 if (un < u1 && nxt.e >= 0 && nxt.e < g.E) cb_load<CB>(cb, a.cbs, nxt.e, 2);
                 if (!y_ready) {
-                    wait_count(a.gbar + kMaxGridGroups, G, a.err);
+                    wait_count(a.ycnt, G, a.err);
                     y_ready = true;
                 }
                 float *yt = a.y + (size_t)(cur.p / g.k) * g.d;
@@ -1217,7 +1197,7 @@ __global__ __launch_bounds__(kBlock) void k_layer(LayerArgs a) {
             } else {
                 // an invalid id poisons its token's output (the error flag is already set)
                 if (!y_ready) {
-                    wait_count(a.gbar + kMaxGridGroups, G, a.err);
+                    wait_count(a.ycnt, G, a.err);
                     y_ready = true;
                 }
                 if (cur.ft == 0)
@@ -1230,20 +1210,9 @@ __global__ __launch_bounds__(kBlock) void k_layer(LayerArgs a) {
             u = un;
         }
     }
-
-    // ---------------- the last workgroup out resets the counters for the next call
-    // (one flat counter: workgroups finish spread out in time, so there is no hot
-    // spot, and the last one learns it is last in one round trip)
-    __shared__ int last;
-    int *xb = a.gbar + 3 * (kMaxGridGroups + 1) + kMaxGridGroups;
-    wait_stores();  // this workgroup's counter increments have landed before it counts out
-    __syncthreads();
-    if (threadIdx.x == 0) last = atomicAdd(xb, 1) == G - 1;
-    __syncthreads();
-    if (last) {
-        for (int i = threadIdx.x; i < P; i += kBlock) store_counter(a.cntA + (kList ? o_pair[i] : i) * kCntStride, 0);
-        if (threadIdx.x < 4) store_counter(a.gbar + threadIdx.x * (kMaxGridGroups + 1) + kMaxGridGroups, 0);
-    }
+    // the other counter set starts the next launch at zero (see kCntSets)
+    for (int i = range_lo(a.n_clear, wg, G) + threadIdx.x; i < range_lo(a.n_clear, wg + 1, G); i += kBlock)
+        store_counter(a.cnt_clear + (size_t)i * kCntStride, 0);
 }
 
 typedef void (*LayerKernel)(LayerArgs);
@@ -1272,8 +1241,14 @@ hipError_t launch_layer(const Geometry &g, Workspace &w, const uint8_t *codes, c
         sl_next = w.fused_logits + 2 * cap + (par ? 0 : P);
         w.fused_parity ^= 1;
     }
-    LayerArgs a{Wt, w.logits, w.sel, w.gbar, rl_cur, rl_next, sl_cur, sl_next, list, codes, slot_tab, cbs, x,
-                ids, gates, y, w.part_gu, w.cntA, w.err, g, T, pre, residual, eps};
+    // counter sets rotate over launches (see kCntSets)
+    const size_t set_ints = (size_t)w.cnt_per_set * kCntStride;
+    int *cnt_cur = w.cnt + w.cnt_phase * set_ints;
+    int *cnt_clear = w.cnt + ((w.cnt_phase + 1) % kCntSets) * set_ints;
+    w.cnt_phase = (w.cnt_phase + 1) % kCntSets;
+    LayerArgs a{Wt, w.logits, w.sel, cnt_cur + (size_t)(w.cnt_per_set - 1) * kCntStride, cnt_clear, w.cnt_per_set,
+                rl_cur, rl_next, sl_cur, sl_next, list, codes, slot_tab, cbs, x, ids, gates, y, w.part_gu, cnt_cur,
+                w.err, g, T, pre, residual, eps};
     // A plain launch of exactly as many workgroups as can be resident at once
     // (sized at open from the occupancy query); the inter-workgroup waits are
     // bounded, so a launch that somehow did not get all of them resident ends
