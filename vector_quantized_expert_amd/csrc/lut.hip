@@ -801,6 +801,15 @@ __device__ inline SegB next_b(const SegB &c, int un, int u1, int n_tf, int n_cd,
     return s;
 }
 
+// y starts as 0 (or x with the residual); phase B adds into it.  Each
+// workgroup writes its share; the stores are published with its first count.
+__device__ inline void init_y(const LayerArgs &a) {
+    const int G = gridDim.x, wg = blockIdx.x;
+    const int64_t n = (int64_t)a.T * a.g.d;
+    for (int64_t i = n * wg / G + threadIdx.x; i < n * (wg + 1) / G; i += kBlock)
+        store_coherent(a.y + i, a.residual ? a.x[i] : 0.f);
+}
+
 // Routing inside the launch (rvq_moe_route_forward).  [FR] "Lecture anticipée
 // et prédiction du routeur": the router decides the token's experts; reading
 // as in the separate route kernels: top-k of fp64 logits, ties to the lower
@@ -894,6 +903,7 @@ __device__ void route_phase(const LayerArgs &a, double *scratch, float *gate_lds
         }
         __syncthreads();
     }
+    init_y(a);  // independent of the routing: done while the logits land
     // ---- R2
     const uint64_t t_start = wall_clock64();
     auto timed_out = [&]() {
@@ -956,6 +966,18 @@ __device__ void route_phase(const LayerArgs &a, double *scratch, float *gate_lds
         sel[i] = l;
     }
     __syncthreads();
+}
+
+// The gates of the routed pairs from the selected logits route_phase left in
+// the scratch (softmax over each token's k, summed in rank order); workgroup
+// 0 also writes ids and gates out.  Separate from route_phase so that the
+// first codebook and input loads of phase A go out before it.
+__device__ void route_gates(const LayerArgs &a, double *scratch, float *gate_lds, const int *pair_ids) {
+    const Geometry &g = a.g;
+    const int wg = blockIdx.x;
+    const double *sel = scratch + kMaxExperts;
+    double *ex = scratch + kMaxExperts + kRouteMaxPairs;
+    const int P = a.T * g.k;
     for (int i = threadIdx.x; i < P; i += kBlock) ex[i] = exp(sel[i] - sel[(i / g.k) * g.k]);
     __syncthreads();
     for (int i = threadIdx.x; i < P; i += kBlock) {
@@ -1011,6 +1033,7 @@ __global__ __launch_bounds__(kBlock) void k_layer(LayerArgs a) {
         route_phase(a, reinterpret_cast<double *>(lut), gate_lds, pair_ids);
         gate_src = gate_lds;
     }
+    bool gates_due = kRoute;  // route_gates not run yet
     // ---------------- pair order (the token x expert permutation)
     __shared__ int id_lds[2 * kIdCache];
     __shared__ int o_info[kOrderMax];
@@ -1034,6 +1057,10 @@ __global__ __launch_bounds__(kBlock) void k_layer(LayerArgs a) {
         }
         __syncthreads();
     } else if (ord.tab) {
+        if (gates_due) {  // the order table reuses the scratch that holds the selected logits
+            route_gates(a, reinterpret_cast<double *>(lut), gate_lds, pair_ids);
+            gates_due = false;
+        }
         build_order(a.ids, kRoute ? pair_ids : nullptr, P, g.E, reinterpret_cast<char *>(lut), o_info, o_pair,
                     o_expert);
     } else if (!kRoute) {
@@ -1049,13 +1076,10 @@ __global__ __launch_bounds__(kBlock) void k_layer(LayerArgs a) {
         __syncthreads();
     }
 
-    // ---------------- y starts as 0 (or x with the residual); phase B adds into it
-    // (with a handed-over pair list the chunk path has set it already)
-    if (!kList) {
-        const int64_t n = (int64_t)a.T * g.d;
-        for (int64_t i = n * wg / G + threadIdx.x; i < n * (wg + 1) / G; i += kBlock)
-            store_coherent(a.y + i, a.residual ? a.x[i] : 0.f);
-    }
+    // ---------------- y starts as 0 (or x with the residual); the routed kernel
+    // did this while routing, and with a handed-over pair list the chunk path
+    // has set it already
+    if (!kList && !kRoute) init_y(a);
     bool y_ready = false;
     // Phase-A chunk counts are published per pair, once the workgroup moves on
     // to another pair or ends phase A (phase B waits for a pair's total), so
@@ -1102,6 +1126,10 @@ __global__ __launch_bounds__(kBlock) void k_layer(LayerArgs a) {
         if (u < u1) {
             cur = seg_a(u, u1, n_ti, n_cf, ord);
             prefetch(cur);
+        }
+        if (gates_due) {  // while the first codebook and inputs are in flight
+            route_gates(a, reinterpret_cast<double *>(lut), gate_lds, pair_ids);
+            gates_due = false;
         }
         while (u < u1) {
             const int un = u + (cur.c1 - cur.c0);
