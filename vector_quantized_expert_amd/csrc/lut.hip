@@ -184,14 +184,23 @@ __device__ inline void build_lut(float *lut, const float (*vs)[kTileSlices], int
     const int lane = threadIdx.x & 63, wave = wave_id();
     const int j = lane & 31, kh = lane >> 5;
     const float down = ldexpf(1.f, -e2), up = ldexpf(1.f, e2);
+    // all eight reads go out before any conversion (one LDS wait, not four)
+    float vin[kVec];
+#pragma unroll
+    for (int i = 0; i < kVec; i++) vin[i] = vs[i][j];
+    __builtin_amdgcn_sched_barrier(0);
     half8 bop;
 #pragma unroll
     for (int i = 0; i < kVec; i++) {
-        const float v = vs[i][j] * down;
+        const float v = vin[i] * down;
         const _Float16 hi = (_Float16)v;
         bop[i] = kh ? (_Float16)(v - (float)hi) : hi;
     }
-    for (int mb = wave; mb < kStages * kCodes / 32; mb += kWaves) {
+    // 24 blocks over 16 waves: waves 0-7 take two, whose operand reads and
+    // products are issued before either block's table writes
+    constexpr int kBlocks = kStages * kCodes / 32;
+    static_assert(kBlocks <= 2 * kWaves, "at most two blocks per wave");
+    auto block = [&](int mb) {
         const int s = mb >> 3, c0 = (mb & 7) * 32;
         const int idx = s * kCodes + c0 + j;
         const char *p = reinterpret_cast<const char *>(lut + kStage2Word + (idx / kPerRow) * 64 + kCbHalfWord) +
@@ -212,10 +221,25 @@ __device__ inline void build_lut(float *lut, const float (*vs)[kTileSlices], int
             acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ahi, bop, acc, 0, 0, 0);
             acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(alo, bop, acc, 0, 0, 0);
         }
+        return acc;
+    };
+    auto store = [&](int mb, const f32x16 &acc) {
+        const int s = mb >> 3, c0 = (mb & 7) * 32;
 #pragma unroll
         for (int v = 0; v < 16; v++) {
             const int c = c0 + 8 * (v >> 2) + 4 * kh + (v & 3);
             lut[lut_word(s, c, j)] = acc[v] * up;
+        }
+    };
+    const int mb0 = wave, mb1 = wave + kWaves;  // wave-uniform
+    if (mb0 < kBlocks) {
+        const f32x16 acc0 = block(mb0);
+        if (mb1 < kBlocks) {
+            const f32x16 acc1 = block(mb1);
+            store(mb0, acc0);
+            store(mb1, acc1);
+        } else {
+            store(mb0, acc0);
         }
     }
 }
