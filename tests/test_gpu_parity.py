@@ -804,3 +804,50 @@ def test_k3_streaming_batch1_matches_resident(torch_mod):
     st.close()
     rs.close()
     del bank
+
+
+def test_mixed_calls_on_one_handle_match_fresh_handles(torch_mod):
+    """One handle through a long mix of calls, enqueued back to back with no
+    host synchronisation between them: one-token table path, one-launch routed
+    calls (one and several tokens), grouped batches, and chunk-path calls that
+    hand few-token experts to the table path.  The layer kernel's completion
+    counters alternate between two sets across its launches, each launch
+    zeroing the other set as it ends; every call must give what the same call
+    gives on a freshly opened handle (ids bit-exact, outputs within 1e-6
+    relative L2: only the order of the fp32 output additions may differ)."""
+    from synth import gpu as G
+    torch = torch_mod
+    shape = S.Shape(264, 136, 12, 3, "f16")
+    T_max = 48
+    inp = G.LayerInputs(shape, seed=31, layer=1, host_codes=True)
+    kw = dict(chunk_min_tokens=8, lut_expert_tokens=12)
+    x = G.to_device(S.tokens(31, 0, T_max, shape.d))
+    plan = [("fused", 1), ("two", 1), ("two", 5), ("two", 48), ("fused", 3), ("two", 1), ("two", 9)] * 3
+
+    def call(layer, kind, T, off):
+        xs = x[off:off + T]
+        ids = torch.empty((T, shape.top_k), dtype=torch.int32, device="cuda")
+        gates = torch.empty((T, shape.top_k), dtype=torch.float32, device="cuda")
+        y = torch.empty((T, shape.d), dtype=torch.float32, device="cuda")
+        if kind == "fused":
+            layer.route_forward(xs, T, ids, gates, y)
+        else:
+            layer.route_topk(xs, T, ids, gates)
+            layer.layer_forward(xs, T, ids, gates, y)
+        return ids, gates, y
+
+    h = _layer(torch, inp, shape, T_max, **kw)
+    outs = [call(h, kind, T, i % (T_max - T + 1)) for i, (kind, T) in enumerate(plan)]
+    h.sync()
+    for i, (kind, T) in enumerate(plan):
+        fresh = _layer(torch, inp, shape, T_max, **kw)
+        ref = call(fresh, kind, T, i % (T_max - T + 1))
+        fresh.sync()
+        a = [t.cpu().numpy() for t in outs[i]]
+        r = [t.cpu().numpy() for t in ref]
+        assert np.array_equal(a[0], r[0]), (i, kind, T)
+        np.testing.assert_allclose(a[1], r[1], rtol=1e-6, atol=0)
+        err = np.linalg.norm(a[2] - r[2], axis=1) / np.linalg.norm(r[2], axis=1)
+        assert err.max() <= 1e-6, (i, kind, T, err.max())
+        fresh.close()
+    h.close()

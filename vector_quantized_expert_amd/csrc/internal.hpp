@@ -150,6 +150,7 @@ struct Workspace {
     int route_parity;      // buffer of the next one-token call
     double *fused_logits;  // in-launch routing slots, fused_route_slots() doubles (marker NaN when unpublished)
     int fused_parity;      // buffer of the next in-launch routing
+    int fused_prev_T;      // tokens of the last in-launch routing (its slots to reset)
     bool route_one;        // the one-token kernel fits (all E workgroups resident)
     float *part_gu;     // [T*k][2][n_tiles_in][ffn_pad] partial gate/up sums
     int *cnt;           // kCntSets sets of cnt_per_set counters kCntStride apart: per pair the

@@ -531,6 +531,7 @@ struct LayerArgs {
     int n_clear;
     double *rl_cur, *rl_next;  // [T][E] logit slots of this launch and of the next (in-launch routing)
     double *sl_cur, *sl_next;  // [T * k] selected-id slots of this launch and of the next
+    int T_reset;               // tokens of the previous routed launch (its slots in the `next` buffers)
     const int *list;    // pairs handed over by the chunk path (n, then the order table), or null
     const uint8_t *codes;
     const uint8_t *const *slot_tab;  // [E] record of each expert (HBM slot cache), or null: codes + e * rec
@@ -923,10 +924,17 @@ __device__ void route_phase(const LayerArgs &a, double *scratch, float *gate_lds
             }
             const double r = a.pre ? sqrt(sq / (double)g.d + a.eps) : 1.0;
             store_coherent(a.rl_cur + (size_t)t * g.E + e, sa / r);
-            store_coherent(a.rl_next + (size_t)t * g.E + e, unpub);
         }
         __syncthreads();
     }
+    // The other buffer goes back to the marker for the next routed call: the
+    // slots the previous routed call wrote there (its T_reset tokens; it has
+    // completed, and the next call starts after this one), the logit slots of
+    // this workgroup's experts and a strided share of the selection slots.
+    if (threadIdx.x < n_own)
+        for (int t = 0; t < a.T_reset; t++)
+            store_coherent(a.rl_next + (size_t)t * g.E + wg + threadIdx.x * G, unpub);
+    for (int i = wg + G * threadIdx.x; i < a.T_reset * g.k; i += G * kBlock) store_coherent(a.sl_next + i, unpub);
     init_y(a);  // independent of the routing: done while the logits land
     // ---- R2
     const uint64_t t_start = wall_clock64();
@@ -957,7 +965,6 @@ __device__ void route_phase(const LayerArgs &a, double *scratch, float *gate_lds
             if (rank < g.k && threadIdx.x == 0) {
                 const int slot = t * g.k + rank;
                 store_coherent(a.sl_cur + slot, (double)e);
-                store_coherent(a.sl_next + slot, unpub);
             }
         }
     }
@@ -1284,6 +1291,7 @@ hipError_t launch_layer(const Geometry &g, Workspace &w, const uint8_t *codes, c
                         float *y, int T, int pre, int residual, double eps, bool route, hipStream_t s,
                         const int *list) {
     double *rl_cur = nullptr, *rl_next = nullptr, *sl_cur = nullptr, *sl_next = nullptr;
+    int T_reset = 0;
     if (route) {  // the slot buffers (see fused_route_slots) alternate between calls
         const int64_t cap = w.route_cap, P = cap / g.E * g.k;
         const int par = w.fused_parity;
@@ -1292,6 +1300,8 @@ hipError_t launch_layer(const Geometry &g, Workspace &w, const uint8_t *codes, c
         sl_cur = w.fused_logits + 2 * cap + (par ? P : 0);
         sl_next = w.fused_logits + 2 * cap + (par ? 0 : P);
         w.fused_parity ^= 1;
+        T_reset = w.fused_prev_T;
+        w.fused_prev_T = T;
     }
     // counter sets rotate over launches (see kCntSets)
     const size_t set_ints = (size_t)w.cnt_per_set * kCntStride;
@@ -1299,7 +1309,7 @@ hipError_t launch_layer(const Geometry &g, Workspace &w, const uint8_t *codes, c
     int *cnt_clear = w.cnt + ((w.cnt_phase + 1) % kCntSets) * set_ints;
     w.cnt_phase = (w.cnt_phase + 1) % kCntSets;
     LayerArgs a{Wt, w.logits, w.sel, cnt_cur + (size_t)(w.cnt_per_set - 1) * kCntStride, cnt_clear, w.cnt_per_set,
-                rl_cur, rl_next, sl_cur, sl_next, list, codes, slot_tab, cbs, x, ids, gates, y, w.part_gu, cnt_cur,
+                rl_cur, rl_next, sl_cur, sl_next, T_reset, list, codes, slot_tab, cbs, x, ids, gates, y, w.part_gu, cnt_cur,
                 w.err, g, T, pre, residual, eps};
     // A plain launch of exactly as many workgroups as can be resident at once
     // (sized at open from the occupancy query); the inter-workgroup waits are
