@@ -851,3 +851,55 @@ def test_mixed_calls_on_one_handle_match_fresh_handles(torch_mod):
         assert err.max() <= 1e-6, (i, kind, T, err.max())
         fresh.close()
     h.close()
+
+
+def test_mixed_calls_on_one_streaming_handle_match_resident(torch_mod):
+    """A streaming handle (codes in pinned host memory through 5 HBM slots,
+    k = 3) through a mix of one-token calls, grouped batches, chunk-path calls
+    (run in rounds of slots) and prefetches of a call's experts just ahead of it, enqueued without host synchronisation between them (beyond
+    the slot cache's own read of each call's ids): every call matches the same
+    sequence on a resident handle (ids bit-exact, outputs within 1e-6 relative
+    L2), and every call and prefetch is counted once by the slot cache."""
+    from synth import gpu as G
+    torch = torch_mod
+    shape = S.Shape(264, 136, 12, 3, "f16")
+    T_max = 48
+    inp = G.LayerInputs(shape, seed=37, layer=3, host_codes=True)
+    bank = _pinned_bank(torch, inp)
+    # a streaming handle puts every expert of a chunk-path call on the matrix
+    # cores (lut_expert_tokens acts as 1), so the resident reference does too
+    st = _layer(torch, inp, shape, T_max, codes=bank, codes_location=1, cache_slots=5, chunk_min_tokens=8,
+                lut_expert_tokens=12)
+    rs = _layer(torch, inp, shape, T_max, chunk_min_tokens=8, lut_expert_tokens=1)
+    x = G.to_device(S.tokens(37, 0, T_max, shape.d))
+    plan = [1, 5, 48, 1, 9, 1, 48, 2] * 2
+
+    def run(layer, stream_pf):
+        outs = []
+        for i, T in enumerate(plan):
+            off = (7 * i) % (T_max - T + 1)
+            xs = x[off:off + T]
+            ids = torch.empty((T, shape.top_k), dtype=torch.int32, device="cuda")
+            gates = torch.empty((T, shape.top_k), dtype=torch.float32, device="cuda")
+            y = torch.empty((T, shape.d), dtype=torch.float32, device="cuda")
+            layer.route_topk(xs, T, ids, gates)
+            if stream_pf and i % 3 == 0:
+                layer.prefetch(ids, T, 2)  # this call's first two experts per token, just ahead of it
+            layer.layer_forward(xs, T, ids, gates, y)
+            outs.append((ids, gates, y))
+        layer.sync()
+        return [[t.cpu().numpy() for t in o] for o in outs]
+
+    a = run(st, True)
+    b = run(rs, False)
+    for i, T in enumerate(plan):
+        assert np.array_equal(a[i][0], b[i][0]), (i, T)
+        np.testing.assert_allclose(a[i][1], b[i][1], rtol=1e-6, atol=0)
+        err = np.linalg.norm(a[i][2] - b[i][2], axis=1) / np.linalg.norm(b[i][2], axis=1)
+        assert err.max() <= 1e-6, (i, T, err.max())
+    stats = st.stats()
+    assert stats["forward_calls"] == len(plan)
+    assert stats["slot_hits"] + stats["slot_misses"] > 0
+    _check(inp, shape, S.tokens(37, 0, T_max, shape.d)[:1], a[0][0], a[0][1], a[0][2])
+    st.close()
+    rs.close()
