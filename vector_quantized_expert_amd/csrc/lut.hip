@@ -376,6 +376,7 @@ __device__ __forceinline__ void load_chunk(const uint8_t *blk, int lane, u32x4 &
 struct Stage {
     float *base;
     int stride, cap;  // floats from one piece to the next; pieces held
+    bool acc = false;  // add into the staged totals instead of replacing them
     __device__ float *piece(int i) const { return base + i * stride; }
 };
 constexpr int kStagePieces = 256;
@@ -398,7 +399,10 @@ __device__ __forceinline__ void gather_range(float *lut, const Stage &st, const 
     auto at = [&](int qq) { return tile_base + (int64_t)min(qq, last) * kChunkBytes; };
     auto emit = [&](int qq, const u32x4 (&r)[3]) {
         const float sum = sum_chunk(lut, r[0], r[1], r[2], l);
-        if (!(lane & 1)) st.piece(qq - c0)[row_in] = sum;
+        if (!(lane & 1)) {
+            float *q = st.piece(qq - c0) + row_in;
+            *q = st.acc ? *q + sum : sum;  // wave-uniform choice
+        }
     };
     u32x4 a[3] = {s0[0], s0[1], s0[2]}, b[3];
     while (true) {
@@ -419,6 +423,17 @@ __device__ __forceinline__ void flush_rows(const Stage &st, float *out, int c0, 
     const int n = (c1 - c0) * kChunkRows;
     for (int i = threadIdx.x; i < n; i += kBlock)
         store_coherent(out + c0 * kChunkRows + i, st.piece(i / kChunkRows)[i % kChunkRows]);
+}
+
+// flush_rows for accumulated totals staged at absolute chunk positions
+// (base + chunk * 32): writes chunks [c0, c1) to out and puts zeros back in
+// their place (each element is read and cleared by the same thread).
+__device__ __forceinline__ void flush_rows_clear(float *base, float *out, int c0, int c1) {
+    for (int i = c0 * kChunkRows + threadIdx.x; i < c1 * kChunkRows; i += kBlock) {
+        const float v = base[i];
+        base[i] = 0.f;
+        store_coherent(out + i, v);
+    }
 }
 
 // Add the staged row totals of chunks [c0, c1) into out[row] (rows < n_rows)
@@ -577,12 +592,26 @@ __device__ inline double token_r(const LayerArgs &a, int t, int &r_tok, double &
     return r_val;
 }
 
+// Merged gate/up partial sums.  In the one-token (pair) order, a workgroup
+// whose range holds consecutive whole tiles of one (pair, matrix) adds their
+// row totals up in LDS and writes the sum once, into the slot of the run's
+// last tile; a tile cut by a range boundary keeps its own slot, each side
+// writing its rows.  Tile t's slot is then empty exactly when t and t + 1 lie
+// whole in one workgroup's range: with u0 the first unit of tile t, that is
+// when the range holding u0 (the largest r with floor(nA r / G) <= u0) ends
+// at or after u0 + 2 n_cf.  Both phases decide this the same way.
+__device__ inline bool merged_away(int64_t nA, int G, int64_t u0, int n_cf, bool last_tile) {
+    if (last_tile) return false;
+    const int64_t r0 = ((u0 + 1) * G + nA - 1) / nA - 1;
+    return nA * (r0 + 1) / G >= u0 + 2 * (int64_t)n_cf;
+}
+
 // h' = gate * silu(a) * b for the 256 FFN entries of down tile ft of pair p,
 // where a and b are the gate and up row sums (sum over the input tiles' partial
-// sums).  Four threads per entry each add every fourth tile (up to 8 loads
+// sums; only the slots vmask marks hold one, see merged_away).  Four threads per entry each add every fourth tile (up to 8 loads
 // per matrix in flight per thread), then the four partials meet in LDS.
 __device__ inline void finish_h(const LayerArgs &a, const float *gate_src, int p, int ft, float (*vs)[kTileSlices],
-                                float (*hred)[256][2], float *red2) {
+                                float (*hred)[256][2], float *red2, const uint64_t *vmask) {
     const Geometry &g = a.g;
     const int n_ti = g.m[0].n_tiles;
     const int fi = threadIdx.x & 255, part = threadIdx.x >> 8;
@@ -596,8 +625,10 @@ __device__ inline void finish_h(const LayerArgs &a, const float *gate_src, int p
 #pragma unroll
             for (int j = 0; j < 8; j++) {
                 const int t = t0 + 4 * j;
-                va[j] = t < n_ti ? load_coherent(pa + (int64_t)t * g.ffn_pad) : 0.f;
-                vb[j] = t < n_ti ? load_coherent(pb + (int64_t)t * g.ffn_pad) : 0.f;
+                // vmask[m] bit t: tile t's partial slot holds a sum (not merged
+                // into a later tile's slot by the workgroup that covered both)
+                va[j] = t < n_ti && (vmask[0] >> (t & 63) & 1) ? load_coherent(pa + (int64_t)t * g.ffn_pad) : 0.f;
+                vb[j] = t < n_ti && (vmask[1] >> (t & 63) & 1) ? load_coherent(pb + (int64_t)t * g.ffn_pad) : 0.f;
             }
 #pragma unroll
             for (int j = 0; j < 8; j++) {
@@ -1136,11 +1167,14 @@ __global__ __launch_bounds__(kBlock) void k_layer(LayerArgs a) {
         acc_n += n;
     };
 
+    // merged gate/up partial sums in the pair order (see merged_away)
+    const bool merge = !ord.tab && n_cf <= 64 && n_ti <= 64;
+    const int64_t nA = (int64_t)P * 2 * n_ti * n_cf;
+    __shared__ uint64_t vmask[2];
     // ---------------- phase A: gate and up
     {
-        const int nA = P * 2 * n_ti * n_cf;
-        int u = range_lo(nA, rw, G);
-        const int u1 = range_lo(nA, rw + 1, G);
+        int u = range_lo((int)nA, rw, G);
+        const int u1 = range_lo((int)nA, rw + 1, G);
         float xv = 0.f;  // this thread's raw input element of the segment's tile
         auto prefetch = [&](const SegA &sg) {
             if (sg.e >= 0 && sg.e < g.E) cb_load<CB>(cb, a.cbs, sg.e, sg.m);
@@ -1151,8 +1185,20 @@ __global__ __launch_bounds__(kBlock) void k_layer(LayerArgs a) {
         // phase B, idle here); the last sub-range of a segment is flushed, and the
         // segment counted, during the next segment's table build
         const Stage ast{&hred[0][0][0], kChunkRows, (int)(sizeof(hred) / sizeof(float)) / kChunkRows};
+        // merged partial sums (see merged_away): totals staged at their chunk
+        // position and accumulated over a run of whole tiles
+        float *const hst = &hred[0][0][0];
+        if (merge)
+            for (int i = threadIdx.x; i < ast.cap * kChunkRows; i += kBlock) hst[i] = 0.f;  // before the first barrier
         float *pend_out = nullptr;  // pending flush: out, chunks [pend_c0, pend_c1), count pend_n for pair pend_p
-        int pend_c0 = 0, pend_c1 = 0, pend_p = 0, pend_n = 0;
+        int pend_c0 = 0, pend_c1 = 0, pend_p = 0, pend_n = 0, pend_m = 0, pend_tile = 0;
+        bool pend_full = false;
+        auto flush_pend = [&]() {  // all threads, after a barrier
+            if (merge)
+                flush_rows_clear(hst, pend_out, pend_c0, pend_c1);
+            else
+                flush_rows(ast, pend_out, pend_c0, pend_c1);
+        };
         SegA cur{};
         if (u < u1) {
             cur = seg_a(u, u1, n_ti, n_cf, ord);
@@ -1181,26 +1227,42 @@ __global__ __launch_bounds__(kBlock) void k_layer(LayerArgs a) {
                 u32x4 p[3];
                 if (cur.c0 + wave < cur.c1)
                     load_chunk(base + (int64_t)(cur.c0 + wave) * kChunkBytes, lane, p[0], p[1], p[2], kNT);
+                // a whole tile right after a whole tile of the same (pair, matrix):
+                // its totals add to the staged ones, nothing is flushed here
+                const bool full = cur.c0 == 0 && cur.c1 == n_cf;
+                const bool extend = merge && pend_out && pend_full && full && cur.p == pend_p && cur.m == pend_m &&
+                                    cur.tile == pend_tile + 1;
+                const bool flush = pend_out && !extend;
                 __syncthreads();
-                if (pend_out) flush_rows(ast, pend_out, pend_c0, pend_c1);
+                if (flush) flush_pend();
                 build_lut<CB>(lut, vs, tile_exponent(red2));
-                if (pend_out) {
-                    count(pend_p, pend_n);
-                    if (!y_signalled) publish();
-                }
+                if (flush) count(pend_p, pend_n);
+                if (pend_out && !y_signalled) publish();
                 __syncthreads();
                 if (un < u1) prefetch(nxt);
                 float *out = a.part_gu + (((int64_t)cur.p * 2 + cur.m) * n_ti + cur.tile) * g.ffn_pad;
-                pend_c0 = gather_segment<false, true>(lut, ast, base, cur.c0, cur.c1, out, 0, p, kNT);
-                pend_c1 = cur.c1;
-                pend_out = out;
-                pend_p = cur.p;
-                pend_n = cur.c1 - cur.c0;
+                Stage st = ast;
+                if (merge) st = Stage{hst + cur.c0 * kChunkRows, kChunkRows, ast.cap - cur.c0, true};
+                const int c0s = gather_segment<false, true>(lut, st, base, cur.c0, cur.c1, out, 0, p, kNT);
+                if (extend) {  // the run now ends at this tile: its slot takes the sum
+                    pend_out = out;
+                    pend_tile = cur.tile;
+                    pend_n += cur.c1 - cur.c0;
+                } else {
+                    pend_c0 = c0s;
+                    pend_c1 = cur.c1;
+                    pend_out = out;
+                    pend_p = cur.p;
+                    pend_m = cur.m;
+                    pend_tile = cur.tile;
+                    pend_n = cur.c1 - cur.c0;
+                    pend_full = full;
+                }
             } else {
                 if (threadIdx.x == 0) atomicOr(a.err, 1);
                 if (pend_out) {
                     __syncthreads();
-                    flush_rows(ast, pend_out, pend_c0, pend_c1);
+                    flush_pend();
                     count(pend_p, pend_n);
                     pend_out = nullptr;
                 }
@@ -1212,7 +1274,7 @@ __global__ __launch_bounds__(kBlock) void k_layer(LayerArgs a) {
         }
         if (pend_out) {
             __syncthreads();
-            flush_rows(ast, pend_out, pend_c0, pend_c1);
+            flush_pend();
             count(pend_p, pend_n);
         }
     }
@@ -1240,8 +1302,17 @@ __global__ __launch_bounds__(kBlock) void k_layer(LayerArgs a) {
                 u32x4 p[3];
                 if (cur.c0 + wave < cur.c1)
                     load_chunk(base + (int64_t)(cur.c0 + wave) * kChunkBytes, lane, p[0], p[1], p[2], kNT);
+                // which gate/up partial slots of this pair hold sums (before the
+                // wait, whose barriers publish it)
+                if (threadIdx.x < 128) {
+                    const int m = threadIdx.x >> 6, t = threadIdx.x & 63;
+                    const int64_t u0 = (((int64_t)cur.p * 2 + m) * n_ti + t) * n_cf;
+                    const bool has = t < n_ti && !(merge && merged_away(nA, G, u0, n_cf, t + 1 == n_ti));
+                    const uint64_t bits = __ballot(has);
+                    if ((threadIdx.x & 63) == 0) vmask[m] = bits;
+                }
                 wait_count_fill(a.cntA + cur.p * kCntStride, needA, a.err, base, cur.c0 + kWaves, cur.c1, lut);
-                finish_h(a, gate_src, cur.p, cur.ft, vs, hred, red2);
+                finish_h(a, gate_src, cur.p, cur.ft, vs, hred, red2, vmask);
                 wait_stores();  // read-ahead blocks landed in the table area before it is rebuilt
                 __syncthreads();
                 build_lut<CB>(lut, vs, tile_exponent(red2));
