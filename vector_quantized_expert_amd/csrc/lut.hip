@@ -497,44 +497,6 @@ __device__ inline void wait_count(const int *cnt, int target, int *err) {
     __syncthreads();
 }
 
-// wait_count for a phase-B segment whose pair may still be in phase A
-// elsewhere: while wave 0 polls, waves 1.. read ahead the segment's code
-// blocks [q0, q1) this workgroup gathers later (round-robin over those waves,
-// at most two blocks in flight per wave), so the wait moves code bytes from
-// HBM into the caches instead of leaving the link idle.  The blocks land in
-// LDS through LDS-DMA loads (no registers) into `sink`, 4 KB per wave of
-// table area that is idle until the next table build; their values are never
-// read.  The waves stop reading ahead once the count is seen (or their blocks
-// run out).  The caller waits for this wave's memory operations (vmcnt 0)
-// before the sink area is written again.
-__device__ inline void wait_count_fill(const int *cnt, int target, int *err, const uint8_t *tile_base, int q0,
-                                       int q1, float *sink) {
-    __shared__ int seen;
-    const int wave = wave_id(), lane = threadIdx.x & 63;
-    if (threadIdx.x == 0) seen = 0;
-    __syncthreads();
-    if (wave == 0) {
-        if (lane == 0) {
-            poll_count(cnt, target, err);
-            __hip_atomic_store(&seen, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-        }
-    } else {
-        auto *dst = (__attribute__((address_space(3))) char *)(reinterpret_cast<char *>(sink) + wave * 4096);
-        for (int q = q0 + wave - 1; q < q1; q += kWaves - 1) {
-            if (__hip_atomic_load(&seen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)) break;
-            const auto *src = global_view(tile_base + (int64_t)q * kChunkBytes + lane * 16);
-#pragma unroll
-            for (int st = 0; st < kStages; st++)
-                __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)(src + st * 1024),
-                                                 (__attribute__((address_space(3))) void *)(dst + st * 1024), 16, 0,
-                                                 0);
-            asm volatile("s_waitcnt vmcnt(3)" ::: "memory");  // at most two blocks in flight
-        }
-    }
-    __syncthreads();
-}
-
-
 // ---------------------------------------------------------------------------
 struct LayerArgs {
     // routing inside the launch (rvq_moe_route_forward); unused otherwise
@@ -1303,7 +1265,7 @@ __global__ __launch_bounds__(kBlock) void k_layer(LayerArgs a) {
                 if (cur.c0 + wave < cur.c1)
                     load_chunk(base + (int64_t)(cur.c0 + wave) * kChunkBytes, lane, p[0], p[1], p[2], kNT);
                 // which gate/up partial slots of this pair hold sums (before the
-                // wait, whose barriers publish it)
+                // wait, whose barrier publishes it)
                 if (threadIdx.x < 128) {
                     const int m = threadIdx.x >> 6, t = threadIdx.x & 63;
                     const int64_t u0 = (((int64_t)cur.p * 2 + m) * n_ti + t) * n_cf;
@@ -1311,9 +1273,8 @@ __global__ __launch_bounds__(kBlock) void k_layer(LayerArgs a) {
                     const uint64_t bits = __ballot(has);
                     if ((threadIdx.x & 63) == 0) vmask[m] = bits;
                 }
-                wait_count_fill(a.cntA + cur.p * kCntStride, needA, a.err, base, cur.c0 + kWaves, cur.c1, lut);
+                wait_count(a.cntA + cur.p * kCntStride, needA, a.err);
                 finish_h(a, gate_src, cur.p, cur.ft, vs, hred, red2, vmask);
-                wait_stores();  // read-ahead blocks landed in the table area before it is rebuilt
                 __syncthreads();
                 build_lut<CB>(lut, vs, tile_exponent(red2));
                 __syncthreads();
