@@ -570,48 +570,44 @@ __device__ inline bool merged_away(int64_t nA, int G, int64_t u0, int n_cf, bool
 
 // h' = gate * silu(a) * b for the 256 FFN entries of down tile ft of pair p,
 // where a and b are the gate and up row sums (sum over the input tiles' partial
-// sums; only the slots vmask marks hold one, see merged_away).  Four threads per entry each add every fourth tile (up to 8 loads
-// per matrix in flight per thread), then the four partials meet in LDS.
+// sums; only the slots vmask marks hold one, see merged_away).
 __device__ inline void finish_h(const LayerArgs &a, const float *gate_src, int p, int ft, float (*vs)[kTileSlices],
-                                float (*hred)[256][2], float *red2, const uint64_t *vmask) {
+                                float *red2, const uint64_t *vmask) {
+    // threads 0..255, one entry each: the valid slots in batches of 16 per
+    // matrix, every load of a batch in flight together
     const Geometry &g = a.g;
     const int n_ti = g.m[0].n_tiles;
-    const int fi = threadIdx.x & 255, part = threadIdx.x >> 8;
+    if (threadIdx.x >= 256) return;
+    const int fi = threadIdx.x;
     const int f = ft * kTileSlices * kVec + fi;
     float sa = 0.f, sb = 0.f;
     if (f < g.ffn) {
         const float *pa = a.part_gu + ((int64_t)p * 2) * n_ti * g.ffn_pad + f;
         const float *pb = pa + (int64_t)n_ti * g.ffn_pad;
-        for (int t0 = part; t0 < n_ti; t0 += 32) {
-            float va[8], vb[8];
+        // vmask[m] bit t: tile t's partial slot holds a sum (not merged into a
+        // later tile's slot by the workgroup that covered both)
+        uint64_t ma = vmask[0], mb = vmask[1];
+        while (ma | mb) {  // uniform
+            float va[16], vb[16];
 #pragma unroll
-            for (int j = 0; j < 8; j++) {
-                const int t = t0 + 4 * j;
-                // vmask[m] bit t: tile t's partial slot holds a sum (not merged
-                // into a later tile's slot by the workgroup that covered both)
-                va[j] = t < n_ti && (vmask[0] >> (t & 63) & 1) ? load_coherent(pa + (int64_t)t * g.ffn_pad) : 0.f;
-                vb[j] = t < n_ti && (vmask[1] >> (t & 63) & 1) ? load_coherent(pb + (int64_t)t * g.ffn_pad) : 0.f;
+            for (int j = 0; j < 16; j++) {
+                const int ta = ma ? __builtin_ctzll(ma) : -1, tb = mb ? __builtin_ctzll(mb) : -1;
+                ma &= ma - 1;
+                mb &= mb - 1;
+                va[j] = ta >= 0 ? load_coherent(pa + (int64_t)ta * g.ffn_pad) : 0.f;
+                vb[j] = tb >= 0 ? load_coherent(pb + (int64_t)tb * g.ffn_pad) : 0.f;
             }
 #pragma unroll
-            for (int j = 0; j < 8; j++) {
+            for (int j = 0; j < 16; j++) {
                 sa += va[j];
                 sb += vb[j];
             }
         }
     }
-    hred[part][fi][0] = sa;
-    hred[part][fi][1] = sb;
-    __syncthreads();
-    if (threadIdx.x < 256) {
-        float hv = 0.f;
-        if (f < g.ffn) {
-            const float av = hred[0][fi][0] + hred[1][fi][0] + hred[2][fi][0] + hred[3][fi][0];
-            const float bv = hred[0][fi][1] + hred[1][fi][1] + hred[2][fi][1] + hred[3][fi][1];
-            hv = gate_src[p] * (av / (1.f + expf(-av)) * bv);
-        }
-        vs[fi % kVec][fi / kVec] = hv;
-        tile_max_publish(hv, red2);
-    }
+    float hv = 0.f;
+    if (f < g.ffn) hv = gate_src[p] * (sa / (1.f + expf(-sa)) * sb);
+    vs[fi % kVec][fi / kVec] = hv;
+    tile_max_publish(hv, red2);
 }
 
 // A phase-A segment: chunks [c0, c1) of one (pair, matrix, tile); e = expert id;
@@ -1274,7 +1270,7 @@ __global__ __launch_bounds__(kBlock) void k_layer(LayerArgs a) {
                     if ((threadIdx.x & 63) == 0) vmask[m] = bits;
                 }
                 wait_count(a.cntA + cur.p * kCntStride, needA, a.err);
-                finish_h(a, gate_src, cur.p, cur.ft, vs, hred, red2, vmask);
+                finish_h(a, gate_src, cur.p, cur.ft, vs, red2, vmask);
                 __syncthreads();
                 build_lut<CB>(lut, vs, tile_exponent(red2));
                 __syncthreads();
