@@ -284,6 +284,46 @@ def test_route_forward_one_launch_matches_two_calls_and_oracle(torch_mod, shape_
     layer.close()
 
 
+@pytest.mark.parametrize("case", ["tied_groups", "many_zero_logits"])
+def test_route_forward_exact_selection_with_ties(torch_mod, case):
+    """The one-launch routing selects each token's top k from candidates at or
+    above the k-th largest maximum of the 16-expert groups.  tied_groups: every
+    group holds the same 16 router columns, so all group maxima tie and the top
+    k are equal logits from different groups (lower ids first).  many_zero_logits:
+    all but 6 router columns are zero, so the k-th place is usually among 122
+    exact zeros (more than 64 candidates).  Ids must equal the oracle's."""
+    from synth import gpu as G
+    shape = S.Shape(256, 64, 128, 4, "f32")
+    inp = G.LayerInputs(shape, seed=21, layer=0, host_codes=True)
+    if case == "tied_groups":
+        for e in range(16, shape.n_experts):
+            inp.w_r[:, e] = inp.w_r[:, e % 16]
+    else:
+        keep = [7, 19, 40, 77, 100, 127]
+        for e in range(shape.n_experts):
+            if e not in keep:
+                inp.w_r[:, e] = 0.0
+    inp.w_r_dev.copy_(G.to_device(inp.w_r))
+    T = 6
+    layer = _layer(torch_mod, inp, shape, T)
+    x = S.tokens(21, 0, T, shape.d)
+    ids = torch_mod.empty((T, shape.top_k), dtype=torch_mod.int32, device="cuda")
+    gates = torch_mod.empty((T, shape.top_k), dtype=torch_mod.float32, device="cuda")
+    y = torch_mod.empty((T, shape.d), dtype=torch_mod.float32, device="cuda")
+    layer.route_forward(G.to_device(x), T, ids, gates, y)
+    layer.sync()
+    ih, gh = ids.cpu().numpy(), gates.cpu().numpy()
+    n_zero_in_top = 0
+    for t in range(T):
+        ref = O.route(x[t], inp.w_r, shape.top_k)
+        assert np.array_equal(ih[t], ref.ids), (t, ih[t], ref.ids)
+        np.testing.assert_allclose(gh[t], ref.gates, rtol=TOL_G, atol=0)
+        n_zero_in_top += int(np.sum(ref.logits[ih[t]] == 0.0))
+    if case == "many_zero_logits":
+        assert n_zero_in_top > 0  # the boundary did fall among the zeros
+    layer.close()
+
+
 def test_k3_route_forward_batch1(torch_mod):
     from synth import gpu as G
     shape = S.K3

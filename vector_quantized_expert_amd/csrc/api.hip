@@ -153,7 +153,7 @@ static int open_impl(const rvq_moe_desc *desc, rvq_moe *h) {
     HIP_TRY(hipMalloc(&h->ws.logits, sizeof(double) * (size_t)(T * E)));
     HIP_TRY(hipMalloc(&h->ws.sel, sizeof(double) * (size_t)(T * D.top_k)));
     HIP_TRY(hipMalloc(&h->ws.route_logits, sizeof(double) * (size_t)route_logit_slots(T, D.n_experts)));
-    HIP_TRY(hipMalloc(&h->ws.fused_logits, sizeof(double) * (size_t)fused_route_slots(T, D.n_experts, D.top_k)));
+    HIP_TRY(hipMalloc(&h->ws.fused_logits, sizeof(double) * (size_t)fused_route_slots(T, D.n_experts)));
     HIP_TRY(hipMalloc(&h->ws.part_gu, sizeof(float) * (size_t)(P * 2 * g.m[0].n_tiles * g.ffn_pad)));
     h->ws.cnt_per_set = (int)(P + 1);
     h->ws.cnt_phase = 0;

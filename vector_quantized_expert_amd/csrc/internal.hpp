@@ -201,9 +201,8 @@ hipError_t launch_repack(const Geometry &g, const uint8_t *canon, uint8_t *inter
 hipError_t launch_transpose(const float *W, float *Wt, int d, int E, hipStream_t s);
 int64_t route_logit_slots(int64_t max_tokens, int E);
 // In-launch routing slots (rvq_moe_route_forward), all doubles: logits
-// [2][max_tokens][E], then selected ids [2][max_tokens * k]; both hold the
-// marker until written.
-inline int64_t fused_route_slots(int64_t max_tokens, int E, int k) { return 2 * max_tokens * E + 2 * max_tokens * k; }
+// [2][max_tokens][E], holding the marker until written.
+inline int64_t fused_route_slots(int64_t max_tokens, int E) { return 2 * max_tokens * E; }
 hipError_t init_route(Workspace &w, int E, int k, int64_t max_tokens, int n_cu, hipStream_t s);
 hipError_t launch_route(const Geometry &g, Workspace &w, const float *x, const float *Wt, int T, int pre,
                         double eps, int32_t *ids, float *gates, hipStream_t s);

@@ -507,8 +507,7 @@ struct LayerArgs {
     int *cnt_clear;     // the other counter set, zeroed as this launch ends: n_clear counters kCntStride apart
     int n_clear;
     double *rl_cur, *rl_next;  // [T][E] logit slots of this launch and of the next (in-launch routing)
-    double *sl_cur, *sl_next;  // [T * k] selected-id slots of this launch and of the next
-    int T_reset;               // tokens of the previous routed launch (its slots in the `next` buffers)
+    int T_reset;               // tokens of the previous routed launch (its slots in the `next` buffer)
     const int *list;    // pairs handed over by the chunk path (n, then the order table), or null
     const uint8_t *codes;
     const uint8_t *const *slot_tab;  // [E] record of each expert (HBM slot cache), or null: codes + e * rec
@@ -824,6 +823,83 @@ __device__ inline void init_y(const LayerArgs &a) {
         store_coherent(a.y + i, a.residual ? a.x[i] : 0.f);
 }
 
+// Exact top k of one token's E logits (in LDS, NaN already mapped to -inf),
+// ties to the lower id, by the whole workgroup without comparing every pair.
+// The maxima of the groups of 16 consecutive experts are distinct logits, so
+// theta, the k-th largest of them, is at most the k-th largest logit: the top k
+// all lie at or above theta and are ranked against those candidates only
+// (about k to 2k of them for spread logits; all E when fewer than k groups or
+// many equal logits, still exact).  Writes the k logits and ids by rank.
+constexpr int kSelGroup = 16;
+__device__ inline int row_sum_u(int v) {  // every lane: the sum over its DPP row of 16 lanes
+    uint32_t u = (uint32_t)v;
+    u += RVQ_DPP_U(u, kDppXor1);
+    u += RVQ_DPP_U(u, kDppXor2);
+    u += RVQ_DPP_U(u, kDppRor4);
+    u += RVQ_DPP_U(u, kDppRor8);
+    return (int)u;
+}
+__device__ void select_top_local(const double *lg, int E, int k, double *sel_out, int *id_out, double *scr) {
+    double *gm = scr;                                         // [E / 16] group maxima
+    double *theta = gm + kMaxExperts / kSelGroup;             // [1]
+    double *cv = theta + 1;                                   // [E] candidate logits
+    int *ci = reinterpret_cast<int *>(cv + kMaxExperts);      // [E] candidate ids
+    int *wc = ci + 2 * kMaxExperts;                           // [kWaves] candidates per wave
+    const int i = threadIdx.x, lane = i & 63, wave = wave_id();
+    const int n_grp = (E + kSelGroup - 1) / kSelGroup;
+    const double v = i < E ? lg[i] : -INFINITY;
+    static_assert(kSelGroup == 16, "a group is one DPP row");
+    double m = v;  // max over the group's DPP row (lanes beyond E add -inf)
+#pragma unroll
+    for (int st = 0; st < 4; st++) m = fmax(m, dpp_d(m, st));
+    if (i % kSelGroup == 0 && i / kSelGroup < n_grp) gm[i / kSelGroup] = m;
+    if (i == 0) *theta = -INFINITY;
+    __syncthreads();
+    if (n_grp >= k) {  // 16 threads per group maximum count those above it and those at or above it
+        const int gi = i / 16, sub = i % 16;
+        int cnt = 0;  // (count greater) + (count greater or equal) << 16
+        if (gi < n_grp) {
+            const double me = gm[gi];
+            for (int h = sub; h < n_grp; h += 16) cnt += (gm[h] > me) + ((gm[h] >= me) << 16);
+        }
+        cnt = row_sum_u(cnt);
+        if (sub == 0 && gi < n_grp && (cnt & 0xffff) < k && (cnt >> 16) >= k) *theta = gm[gi];  // all the same value
+        __syncthreads();
+    }
+    const bool cand = i < E && v >= *theta;
+    const uint64_t bal = __ballot(cand);
+    if (lane == 0) wc[wave] = __popcll(bal);
+    __syncthreads();
+    int pos = __popcll(bal & ((1ull << lane) - 1)), n_c = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; w++) {
+        const int c = wc[w];
+        pos += w < wave ? c : 0;
+        n_c += c;
+    }
+    if (cand) {
+        cv[pos] = v;
+        ci[pos] = i;
+    }
+    __syncthreads();
+    // rank of each candidate among the candidates: 16 threads per candidate
+    // when there are at most 64 of them, else one thread per candidate
+    const int q = n_c <= kBlock / 16 ? 16 : 1;
+    const int c = i / q, sub = i % q;
+    int r = 0;
+    if (c < n_c) {
+        const double me = cv[c];
+        const int id = ci[c];
+        for (int j = sub; j < n_c; j += q) r += cv[j] > me || (cv[j] == me && ci[j] < id);
+    }
+    if (q == 16) r = row_sum_u(r);
+    if (c < n_c && sub == 0 && r < k) {
+        sel_out[r] = cv[c];
+        id_out[r] = ci[c];
+    }
+    __syncthreads();
+}
+
 // Routing inside the launch (rvq_moe_route_forward).  [FR] "Lecture anticipée
 // et prédiction du routeur": the router decides the token's experts; reading
 // as in the separate route kernels: top-k of fp64 logits, ties to the lower
@@ -835,14 +911,10 @@ __device__ inline void init_y(const LayerArgs &a) {
 //      marker NaN until then; its slots of the other buffer get the marker back
 //      for the next call;
 //  R2  per token, it polls the E logit slots until none holds the marker (the
-//      poll reads the logits themselves) and ranks each of its own experts (one
-//      comparison per thread, counted by the barrier); an expert of rank < k
-//      publishes its id into selection slot [token][rank] (marker NaN until
-//      then);
-//  R3  every workgroup polls the k selection slots of every token, takes the
-//      ids in rank order and their logits (already in hand from R2) into LDS,
-//      and forms the gates (one exp each, summed in slot order).  Workgroup 0
-//      writes ids and gates out.
+//      poll reads the logits themselves) and selects the token's top k from
+//      them itself (select_top_local): every workgroup reaches the same ids,
+//      with no further exchange.  The gates follow in route_gates (one exp
+//      each, summed in rank order); workgroup 0 writes ids and gates out.
 constexpr int kRouteExp = 4;  // experts per workgroup (E <= 4 G)
 __device__ void route_phase(const LayerArgs &a, double *scratch, float *gate_lds, int *pair_ids) {
     const Geometry &g = a.g;
@@ -853,7 +925,7 @@ __device__ void route_phase(const LayerArgs &a, double *scratch, float *gate_lds
     double *lg = scratch;                 // [E] logits of the token being ranked
     double *sel = scratch + kMaxExperts;  // [P] selected logits by rank
     double *ex = sel + kRouteMaxPairs;    // [P] exps
-    double *red = ex + kRouteMaxPairs;    // [kWaves][kRouteExp + 1]
+    double *red = ex + kRouteMaxPairs;    // [kWaves][kRouteExp + 1], then the selection scratch
     const int P = a.T * g.k;
     // ---- R1
     // own experts of this workgroup (wave-uniform): loads only for those
@@ -917,13 +989,12 @@ __device__ void route_phase(const LayerArgs &a, double *scratch, float *gate_lds
         __syncthreads();
     }
     // The other buffer goes back to the marker for the next routed call: the
-    // slots the previous routed call wrote there (its T_reset tokens; it has
-    // completed, and the next call starts after this one), the logit slots of
-    // this workgroup's experts and a strided share of the selection slots.
+    // logit slots of this workgroup's experts that the previous routed call
+    // wrote there (its T_reset tokens; it has completed, and the next call
+    // starts after this one).
     if (threadIdx.x < n_own)
         for (int t = 0; t < a.T_reset; t++)
             store_coherent(a.rl_next + (size_t)t * g.E + wg + threadIdx.x * G, unpub);
-    for (int i = wg + G * threadIdx.x; i < a.T_reset * g.k; i += G * kBlock) store_coherent(a.sl_next + i, unpub);
     init_y(a);  // independent of the routing: done while the logits land
     // ---- R2
     const uint64_t t_start = wall_clock64();
@@ -945,47 +1016,8 @@ __device__ void route_phase(const LayerArgs &a, double *scratch, float *gate_lds
             }
             if (__syncthreads_and(ready) || timed_out()) break;
         }
-        for (int j = 0; j < kRouteExp; j++) {  // uniform: the same own experts in every thread
-            const int e = wg + j * G;
-            if (e >= g.E) break;
-            const double me = lg[e];
-            const int i = threadIdx.x;  // E <= kMaxExperts = kBlock: one comparison per thread
-            const int rank = __syncthreads_count(i < g.E && (lg[i] > me || (lg[i] == me && i < e)));
-            if (rank < g.k && threadIdx.x == 0) {
-                const int slot = t * g.k + rank;
-                store_coherent(a.sl_cur + slot, (double)e);
-            }
-        }
+        select_top_local(lg, g.E, g.k, sel + t * g.k, pair_ids + t * g.k, red + kWaves * (kRouteExp + 1));
     }
-    // ---- R3
-    while (true) {
-        int ready = 1;
-        for (int i = threadIdx.x; i < P; i += kBlock) {
-            const double v = load_coherent(a.sl_cur + i);
-            ready &= (uint64_t)__double_as_longlong(v) != kUnpublished;
-            sel[i] = v;
-        }
-        if (__syncthreads_and(ready) || timed_out()) break;
-    }
-    // the selected logits: every workgroup holds the last token's E logits in
-    // LDS (read in R2); an earlier token's are read back from its slots, which
-    // R2 saw published
-    for (int i = threadIdx.x; i < P; i += kBlock) {
-        const double v = sel[i];  // the marker only after a timed-out wait: an invalid id
-        const int e = (v >= 0.0 && v < (double)g.E) ? (int)v : -1, t = i / g.k;
-        pair_ids[i] = e;
-        double l;
-        if (e < 0) {
-            l = -INFINITY;
-        } else if (t == a.T - 1) {
-            l = lg[e];
-        } else {
-            l = load_coherent(a.rl_cur + (size_t)t * g.E + e);
-            l = isnan(l) ? -INFINITY : l;
-        }
-        sel[i] = l;
-    }
-    __syncthreads();
 }
 
 // The gates of the routed pairs from the selected logits route_phase left in
@@ -1024,8 +1056,8 @@ __global__ __launch_bounds__(kBlock) void k_layer(LayerArgs a) {
     __shared__ __align__(16) float lut[kLutWords];  // also 8-byte staging (logits, order masks)
     __shared__ float vs[kVec][kTileSlices];  // [element][slice]
     __shared__ double red[kWaves];
-    static_assert((kMaxExperts + 2 * kRouteMaxPairs + kWaves * (kRouteExp + 1)) * sizeof(double) <=
-                      kLutWords * sizeof(float),
+    static_assert((kMaxExperts + 2 * kRouteMaxPairs + kWaves * (kRouteExp + 1) + kMaxExperts / kSelGroup + 1 +
+                   2 * kMaxExperts + kWaves) * sizeof(double) <= kLutWords * sizeof(float),
                   "routing scratch must fit the table area");
     static_assert(kMaxExperts <= kBlock, "one rank comparison per thread");
     __shared__ float hred[4][256][2];
@@ -1318,15 +1350,13 @@ hipError_t launch_layer(const Geometry &g, Workspace &w, const uint8_t *codes, c
                         const void *cbs, const float *Wt, const float *x, const int32_t *ids, const float *gates,
                         float *y, int T, int pre, int residual, double eps, bool route, hipStream_t s,
                         const int *list) {
-    double *rl_cur = nullptr, *rl_next = nullptr, *sl_cur = nullptr, *sl_next = nullptr;
+    double *rl_cur = nullptr, *rl_next = nullptr;
     int T_reset = 0;
     if (route) {  // the slot buffers (see fused_route_slots) alternate between calls
-        const int64_t cap = w.route_cap, P = cap / g.E * g.k;
+        const int64_t cap = w.route_cap;
         const int par = w.fused_parity;
         rl_cur = w.fused_logits + (par ? cap : 0);
         rl_next = w.fused_logits + (par ? 0 : cap);
-        sl_cur = w.fused_logits + 2 * cap + (par ? P : 0);
-        sl_next = w.fused_logits + 2 * cap + (par ? 0 : P);
         w.fused_parity ^= 1;
         T_reset = w.fused_prev_T;
         w.fused_prev_T = T;
@@ -1337,7 +1367,7 @@ hipError_t launch_layer(const Geometry &g, Workspace &w, const uint8_t *codes, c
     int *cnt_clear = w.cnt + ((w.cnt_phase + 1) % kCntSets) * set_ints;
     w.cnt_phase = (w.cnt_phase + 1) % kCntSets;
     LayerArgs a{Wt, w.logits, w.sel, cnt_cur + (size_t)(w.cnt_per_set - 1) * kCntStride, cnt_clear, w.cnt_per_set,
-                rl_cur, rl_next, sl_cur, sl_next, T_reset, list, codes, slot_tab, cbs, x, ids, gates, y, w.part_gu, cnt_cur,
+                rl_cur, rl_next, T_reset, list, codes, slot_tab, cbs, x, ids, gates, y, w.part_gu, cnt_cur,
                 w.err, g, T, pre, residual, eps};
     // A plain launch of exactly as many workgroups as can be resident at once
     // (sized at open from the occupancy query); the inter-workgroup waits are

@@ -516,7 +516,7 @@ hipError_t init_route(Workspace &w, int E, int k, int64_t max_tokens, int n_cu, 
     w.fused_parity = 0;
     w.fused_prev_T = 0;
     const hipError_t e2 = hipMemsetD32Async(reinterpret_cast<hipDeviceptr_t>(w.fused_logits), kUnpublishedHalf,
-                                            (size_t)(2 * fused_route_slots(max_tokens, E, k)), s);
+                                            (size_t)(2 * fused_route_slots(max_tokens, E)), s);
     if (e2 != hipSuccess) return e2;
     return hipMemsetD32Async(reinterpret_cast<hipDeviceptr_t>(w.route_logits), kUnpublishedHalf,
                              (size_t)(2 * route_logit_slots(max_tokens, E)), s);
