@@ -916,7 +916,9 @@ __device__ void select_top_local(const double *lg, int E, int k, double *sel_out
 //      with no further exchange.  The gates follow in route_gates (one exp
 //      each, summed in rank order); workgroup 0 writes ids and gates out.
 constexpr int kRouteExp = 4;  // experts per workgroup (E <= 4 G)
-__device__ void route_phase(const LayerArgs &a, double *scratch, float *gate_lds, int *pair_ids) {
+// `idle` runs once R1 is published, before the wait for the other logits.
+template <class Idle>
+__device__ void route_phase(const LayerArgs &a, double *scratch, float *gate_lds, int *pair_ids, Idle &&idle) {
     const Geometry &g = a.g;
     const int G = gridDim.x, wg = blockIdx.x;
     const int lane = threadIdx.x & 63, wave = wave_id();
@@ -996,6 +998,7 @@ __device__ void route_phase(const LayerArgs &a, double *scratch, float *gate_lds
         for (int t = 0; t < a.T_reset; t++)
             store_coherent(a.rl_next + (size_t)t * g.E + wg + threadIdx.x * G, unpub);
     init_y(a);  // independent of the routing: done while the logits land
+    idle();
     // ---- R2
     const uint64_t t_start = wall_clock64();
     auto timed_out = [&]() {
@@ -1080,10 +1083,32 @@ __global__ __launch_bounds__(kBlock) void k_layer(LayerArgs a) {
     __shared__ float gate_lds[kRouteMaxPairs];
     __shared__ int pair_ids[kRouteMaxPairs];
     const float *gate_src = a.gates;
+    // Phase A's unit range and, when the pairs keep their order (no order
+    // table), its first segment's position: integer divisions that the routed
+    // launch does while it waits for the logits.  The segment's expert is read
+    // once the ids are known.
+    const bool tab_order = kList || (a.T > 1 && P <= kOrderMax);
+    const int nA_units = (int)((int64_t)P * 2 * n_ti * n_cf);
+    int uA = 0, uA1 = 0;
+    SegA firstA{};
+    bool firstA_placed = false;
+    auto place_a = [&]() {
+        uA = range_lo(nA_units, rw, G);
+        uA1 = range_lo(nA_units, rw + 1, G);
+        if (kRoute && !tab_order && uA < uA1) {
+            Order pos_only{};  // no table; its expert lookups read the (not yet routed) LDS ids
+            pos_only.tab = false;
+            pos_only.all = pair_ids;
+            firstA = seg_a(uA, uA1, n_ti, n_cf, pos_only);
+            firstA_placed = true;
+        }
+    };
     if (kRoute) {
         // the routing scratch reuses the table area, which is idle until phase A
-        route_phase(a, reinterpret_cast<double *>(lut), gate_lds, pair_ids);
+        route_phase(a, reinterpret_cast<double *>(lut), gate_lds, pair_ids, place_a);
         gate_src = gate_lds;
+    } else {
+        place_a();
     }
     bool gates_due = kRoute;  // route_gates not run yet
     // ---------------- pair order (the token x expert permutation)
@@ -1092,7 +1117,7 @@ __global__ __launch_bounds__(kBlock) void k_layer(LayerArgs a) {
     __shared__ int o_pair[kOrderMax];
     __shared__ short o_expert[kOrderMax];
     Order ord;
-    ord.tab = kList || (a.T > 1 && P <= kOrderMax);
+    ord.tab = tab_order;
     ord.info = o_info;
     ord.pair = o_pair;
     ord.expert = o_expert;
@@ -1163,8 +1188,8 @@ __global__ __launch_bounds__(kBlock) void k_layer(LayerArgs a) {
     __shared__ uint64_t vmask[2];
     // ---------------- phase A: gate and up
     {
-        int u = range_lo((int)nA, rw, G);
-        const int u1 = range_lo((int)nA, rw + 1, G);
+        int u = uA;
+        const int u1 = uA1;
         float xv = 0.f;  // this thread's raw input element of the segment's tile
         auto prefetch = [&](const SegA &sg) {
             if (sg.e >= 0 && sg.e < g.E) cb_load<CB>(cb, a.cbs, sg.e, sg.m);
@@ -1191,7 +1216,13 @@ __global__ __launch_bounds__(kBlock) void k_layer(LayerArgs a) {
         };
         SegA cur{};
         if (u < u1) {
-            cur = seg_a(u, u1, n_ti, n_cf, ord);
+            if (firstA_placed) {
+                cur = firstA;
+                cur.p = ord.pair_at(cur.gs + cur.j);
+                cur.e = ord.expert_a(cur.gs + cur.j);
+            } else {
+                cur = seg_a(u, u1, n_ti, n_cf, ord);
+            }
             prefetch(cur);
         }
         if (gates_due) {  // while the first codebook and inputs are in flight
