@@ -844,8 +844,8 @@ __device__ void select_top_local(const double *lg, int E, int k, double *sel_out
     double *theta = gm + kMaxExperts / kSelGroup;             // [1]
     double *cv = theta + 1;                                   // [E] candidate logits
     int *ci = reinterpret_cast<int *>(cv + kMaxExperts);      // [E] candidate ids
-    int *wc = ci + 2 * kMaxExperts;                           // [kWaves] candidates per wave
-    const int i = threadIdx.x, lane = i & 63, wave = wave_id();
+    int *n_cand = ci + 2 * kMaxExperts;                       // [1] candidate count
+    const int i = threadIdx.x;
     const int n_grp = (E + kSelGroup - 1) / kSelGroup;
     const double v = i < E ? lg[i] : -INFINITY;
     static_assert(kSelGroup == 16, "a group is one DPP row");
@@ -853,7 +853,10 @@ __device__ void select_top_local(const double *lg, int E, int k, double *sel_out
 #pragma unroll
     for (int st = 0; st < 4; st++) m = fmax(m, dpp_d(m, st));
     if (i % kSelGroup == 0 && i / kSelGroup < n_grp) gm[i / kSelGroup] = m;
-    if (i == 0) *theta = -INFINITY;
+    if (i == 0) {
+        *theta = -INFINITY;
+        *n_cand = 0;
+    }
     __syncthreads();
     if (n_grp >= k) {  // 16 threads per group maximum count those above it and those at or above it
         const int gi = i / 16, sub = i % 16;
@@ -866,22 +869,13 @@ __device__ void select_top_local(const double *lg, int E, int k, double *sel_out
         if (sub == 0 && gi < n_grp && (cnt & 0xffff) < k && (cnt >> 16) >= k) *theta = gm[gi];  // all the same value
         __syncthreads();
     }
-    const bool cand = i < E && v >= *theta;
-    const uint64_t bal = __ballot(cand);
-    if (lane == 0) wc[wave] = __popcll(bal);
-    __syncthreads();
-    int pos = __popcll(bal & ((1ull << lane) - 1)), n_c = 0;
-#pragma unroll
-    for (int w = 0; w < kWaves; w++) {
-        const int c = wc[w];
-        pos += w < wave ? c : 0;
-        n_c += c;
-    }
-    if (cand) {
+    if (i < E && v >= *theta) {  // candidates in any order (ranked by value, then id)
+        const int pos = atomicAdd(n_cand, 1);
         cv[pos] = v;
         ci[pos] = i;
     }
     __syncthreads();
+    const int n_c = *n_cand;
     // rank of each candidate among the candidates: 16 threads per candidate
     // when there are at most 64 of them, else one thread per candidate
     const int q = n_c <= kBlock / 16 ? 16 : 1;
@@ -970,7 +964,8 @@ __device__ void route_phase(const LayerArgs &a, double *scratch, float *gate_lds
             }
         }
 #pragma unroll
-        for (int j = 0; j < kRouteExp; j++) acc[j] = wave_sum(acc[j]);
+        for (int j = 0; j < kRouteExp; j++)
+            if (j < n_own) acc[j] = wave_sum(acc[j]);  // uniform: only the owned experts' sums
         if (a.pre) ss = wave_sum(ss);
         if (lane == 0) {
 #pragma unroll
