@@ -39,8 +39,20 @@
  *     enqueued, nothing is allocated and no output is written.
  *     rvq_moe_last_error() gives a human-readable reason.
  *   - A handle is not thread-safe (its workspace is shared by its calls);
- *     distinct handles are independent.  Calls that overlap on one handle
+ *     distinct handles hold no shared state.  Calls that overlap on one handle
  *     from different streams race.
+ *   - Residency: the kernels of rvq_moe_layer_forward (table path),
+ *     rvq_moe_route_forward and rvq_moe_route_topk with one token are
+ *     persistent grids whose workgroups wait for one another, so each assumes
+ *     the whole GPU is free for its grid.  Such calls, of any handles, must not
+ *     run concurrently on different streams: order them (same stream, or
+ *     events).  Otherwise two partly resident grids can wait on each other
+ *     until the bounded inter-workgroup wait (~0.5 s) gives up, and the calls
+ *     fail with RVQ_MOE_EDEVICE (timeout flag) at the next sync; the device
+ *     never hangs.  Copies (the slot cache) and the router of a streaming
+ *     handle (codes_location PINNED_*, which always takes the router kernels
+ *     that need no co-resident grid) may overlap them freely, e.g. router
+ *     lookahead on a side stream (rvq_moe_prefetch).
  */
 #ifndef RVQ_MOE_H
 #define RVQ_MOE_H
@@ -144,7 +156,11 @@ typedef struct rvq_moe_record_trailer {
  *   router_w     fp32 [d][E] router matrix: logits[e] = sum_i x_i W[i][e].
  *   codebooks    [E][3 matrices: gate, up, down][3 stages][256][8] entries of
  *                codebook_dtype.  A weight is c1 + c2 + c3, the sum of its
- *                three stage vectors' entries; no scale, no bias.
+ *                three stage vectors' entries; no scale, no bias.  Any finite
+ *                values: fp32 codebooks are scaled per (expert, matrix) by an
+ *                exact power of two inside the table build, so the ~1e-6
+ *                relative accuracy of the table path holds at every scale
+ *                (fp32 range); non-finite entries propagate to the outputs.
  *   codes        [E][record] with record = gate [ffn][d/8][3] u8, then up
  *                [ffn][d/8][3] u8, then down [d][ffn/8][3] u8: byte s of
  *                (row, slice j) indexes stage s's codebook for the 8 weights
@@ -214,6 +230,10 @@ typedef struct rvq_moe rvq_moe;
 /*
  * rvq_moe_open -- validate `desc`, allocate the handle, copy the router and
  * codebooks, and repack the codes into the library's tiled internal layout.
+ * [FR] "Objectif et forme d'implémentation de WASTE": the engine's C API opens
+ * a model once and then runs it; [FR] "Budget RAM et fenêtre de performance
+ * étroite": it refuses to start below its minimum memory budget (here
+ * EBUDGET: fewer HBM slots than one token's top_k experts).
  * Synchronises `desc->stream` before returning; the caller may free every
  * input buffer afterwards (the library owns its copies and its workspace).
  * On failure *out is set to NULL and nothing stays allocated.
@@ -290,7 +310,9 @@ int rvq_moe_layer_forward(rvq_moe *h, const float *x, int32_t n_tokens, const in
  *   x [n_tokens][d] fp32; ids [n_tokens][k] int32 out; gates [n_tokens][k] fp32
  *   out; y [n_tokens][d] fp32 out (must not alias x).
  * Errors: EINVAL (null handle/pointer, n_tokens < 1 or > max_tokens,
- * n_tokens * top_k > 1024, y == x), EHIP.
+ * n_tokens * top_k > 1024, y == x), ENOTSUP (streaming codes; or more than 4
+ * experts per workgroup of the persistent grid, i.e. n_experts above 4 x the
+ * device's resident workgroups -- 1024 on an MI355X), EHIP.
  */
 int rvq_moe_route_forward(rvq_moe *h, const float *x, int32_t n_tokens, int32_t *ids, float *gates, float *y,
                           void *stream);
@@ -328,6 +350,7 @@ int rvq_moe_sync(rvq_moe *h, void *stream);
 /*
  * rvq_moe_close -- synchronise the device, free everything the handle owns,
  * and return any deferred device-side error.  NULL is accepted (returns OK).
+ * [FR] "Objectif et forme d'implémentation de WASTE": the C API's exit call.
  */
 int rvq_moe_close(rvq_moe *h);
 

@@ -131,6 +131,63 @@ def test_ragged_shapes(torch_mod, d, ffn, E, k, cb):
     layer.close()
 
 
+@pytest.mark.parametrize("d,ffn,E,k,cb", [
+    (16392, 16, 3, 2, "f32"),     # 2049 slices: 65 input tiles, just past one 64-bit slot mask
+    (40968, 24, 2, 1, "f16"),     # 5121 slices: 161 input tiles (three mask words)
+])
+def test_wide_hidden_size_past_64_input_tiles(torch_mod, d, ffn, E, k, cb):
+    """Hidden sizes whose gate/up matrices have more than 64 input tiles: the
+    SwiGLU finish must sum the partial slots of every tile, in the batch-1
+    pair order (merged slots), the grouped order, and the routed launch."""
+    from synth import gpu as G
+    shape = S.Shape(d, ffn, E, k, cb)
+    inp = G.LayerInputs(shape, seed=41, layer=0, host_codes=True)
+    layer = _layer(torch_mod, inp, shape, 3)
+    x = S.tokens(41, 0, 3, d)
+    ids, gates, y = _run(torch_mod, layer, shape, x, per_token=True)
+    _check(inp, shape, x, ids, gates, y)
+    ids, gates, y = _run(torch_mod, layer, shape, x)
+    _check(inp, shape, x, ids, gates, y)
+    xd = G.to_device(x[:1])
+    ids_d = torch_mod.empty((1, k), dtype=torch_mod.int32, device="cuda")
+    g_d = torch_mod.empty((1, k), device="cuda")
+    y_d = torch_mod.empty((1, d), device="cuda")
+    layer.route_forward(xd, 1, ids_d, g_d, y_d)
+    layer.sync()
+    _check(inp, shape, x[:1], ids_d.cpu().numpy(), g_d.cpu().numpy(), y_d.cpu().numpy())
+    layer.close()
+
+
+@pytest.mark.parametrize("scale_exp", [-24, -8, 0, 12, 20])
+def test_fp32_codebooks_at_any_scale(torch_mod, scale_exp):
+    """fp32 codebooks scaled by 2^s (s = -24 .. 20: entries from ~1e-10 to
+    beyond the fp16 range) follow the oracle at the 1e-4 bar on the table
+    path, and scaling the up and down codebooks by powers of two scales the
+    output exactly (bitwise; one expert per token and one down tile, so every
+    output element is a single addition onto zero)."""
+    from synth import gpu as G
+    shape = S.Shape(264, 136, 5, 1, "f32")
+    base = G.LayerInputs(shape, seed=43, layer=0, host_codes=True)
+    cb0 = base.cb.copy()
+    base.cb = np.ldexp(cb0, scale_exp).astype(np.float32)
+    base.cb_dev.copy_(G.to_device(base.cb))
+    layer = _layer(torch_mod, base, shape, 4)
+    x = S.tokens(43, 0, 4, shape.d)
+    ids, gates, y = _run(torch_mod, layer, shape, x)
+    _check(base, shape, x, ids, gates, y)
+    layer.close()
+    # up scaled by 2^3, down by 2^-5 (gate unchanged): y scales by 2^-2 exactly
+    scaled = np.array(base.cb)
+    scaled[:, 1] = np.ldexp(scaled[:, 1], 3)
+    scaled[:, 2] = np.ldexp(scaled[:, 2], -5)
+    base.cb_dev.copy_(G.to_device(scaled))
+    layer = _layer(torch_mod, base, shape, 4)
+    ids2, gates2, y2 = _run(torch_mod, layer, shape, x)
+    assert np.array_equal(ids, ids2)
+    assert np.array_equal(y2, np.ldexp(y, -2).astype(np.float32))
+    layer.close()
+
+
 def test_zero_codebooks_give_exact_zero(torch_mod, tiny):
     from synth import gpu as G
     shape = S.TINY
@@ -233,6 +290,74 @@ def test_k3_layer_batch1_sampled_tokens(torch_mod):
     worst = _check(inp, shape, x, ids, gates, y)
     print(f"K3 layer worst rel L2 {worst:.3e}")
     layer.close()
+
+
+def test_k3_every_expert_record_against_the_oracle(torch_mod):
+    """Explicit ids 0..383 in 24 tokens of 16: every expert record of the
+    K3-scale layer (offsets up to 6.3 GB) is read and checked against the
+    oracle, through one grouped 24-token call and through 24 one-token calls
+    (the batch-1 launch configuration)."""
+    from synth import gpu as G
+    shape = S.K3
+    T = shape.n_experts // shape.top_k
+    inp = G.LayerInputs(shape, seed=0, layer=7)
+    layer = _layer(torch_mod, inp, shape, T)
+    inp.free_codes()
+    torch_mod.cuda.empty_cache()
+    x = S.tokens(0, 7000, T, shape.d)
+    ids = np.arange(shape.n_experts, dtype=np.int32).reshape(T, shape.top_k)
+    rng = np.random.default_rng(7)
+    gates = rng.random((T, shape.top_k)).astype(np.float32) + 0.5
+    gates /= gates.sum(axis=1, keepdims=True)
+    xd, ids_d, g_d = G.to_device(x), G.to_device(ids), G.to_device(gates)
+    y_grp = torch_mod.empty((T, shape.d), device="cuda")
+    y_one = torch_mod.empty((T, shape.d), device="cuda")
+    layer.layer_forward(xd, T, ids_d, g_d, y_grp)
+    for t in range(T):
+        layer.layer_forward(xd[t:t + 1], 1, ids_d[t:t + 1], g_d[t:t + 1], y_one[t:t + 1])
+    layer.sync()
+    yg, yo = y_grp.cpu().numpy(), y_one.cpu().numpy()
+    worst = 0.0
+    for t in range(T):
+        recs = [inp.record(int(e)) for e in ids[t]]
+        ref = O.moe(shape.d, shape.ffn, gates[t].astype(np.float64), [inp.codebook(int(e)) for e in ids[t]], recs,
+                    x[t].astype(np.float64))
+        for yy in (yg, yo):
+            err = np.linalg.norm(yy[t] - ref) / np.linalg.norm(ref)
+            assert err <= TOL_Y, (t, err)
+            worst = max(worst, err)
+    print(f"K3 all 384 experts: worst rel L2 {worst:.3e}")
+    layer.close()
+
+
+def test_k3_depth_chain_teacher_forced(torch_mod):
+    """Four K3-scale layers (d=7168, ffn=2048, E=384, top-16) with RMS
+    normalisation before routing and a residual add, each call one token
+    through rvq_moe_route_forward (the batch-1 launch configuration): every
+    layer against the oracle fed the GPU's own input of that layer."""
+    from synth import gpu as G
+    shape = S.K3
+    L, T = 4, 2
+    h = S.tokens(0, 9000, T, shape.d)
+    for li in range(L):
+        inp = G.LayerInputs(shape, seed=0, layer=20 + li)
+        layer = _layer(torch_mod, inp, shape, 1, pre_rmsnorm=True, residual=True, eps=1e-6)
+        inp.free_codes()
+        torch_mod.cuda.empty_cache()
+        hd = G.to_device(h)
+        ids = torch_mod.empty((T, shape.top_k), dtype=torch_mod.int32, device="cuda")
+        gates = torch_mod.empty((T, shape.top_k), device="cuda")
+        y = torch_mod.empty((T, shape.d), device="cuda")
+        for t in range(T):
+            layer.route_forward(hd[t:t + 1], 1, ids[t:t + 1], gates[t:t + 1], y[t:t + 1])
+        layer.sync()
+        yh = y.cpu().numpy()
+        worst = _check(inp, shape, h, ids.cpu().numpy(), gates.cpu().numpy(), yh, pre_rmsnorm=True, residual=True)
+        print(f"K3 chain layer {li}: worst rel L2 {worst:.3e}")
+        layer.close()
+        del inp
+        torch_mod.cuda.empty_cache()
+        h = yh
 
 
 def test_router_ties_go_to_the_lower_id_and_k_equals_e(torch_mod):
@@ -418,6 +543,12 @@ TOL_Y_BF16 = 2e-2  # bf16 operands (weights, tokens, h) with fp32 accumulation
 
 
 def _check_chunk(inp, shape, x, ids, gates, y, pre_rmsnorm=False, residual=False, tokens=None):
+    """Per token: ids bit-exact against the oracle, the MoE output within 2e-2
+    relative L2 of the fp64 oracle, and every output element within
+    chunk_model.element_tolerance of the chunk path's precision model (the
+    documented bf16 roundings around exact products), so that one wrong
+    element or row fails even where the L2 norm would hide it."""
+    import chunk_model as M
     worst = 0.0
     for t in (range(x.shape[0]) if tokens is None else tokens):
         ref = O.layer(x[t], inp.w_r, shape.top_k, inp.codebook, inp.record, shape.d, shape.ffn,
@@ -427,6 +558,12 @@ def _check_chunk(inp, shape, x, ids, gates, y, pre_rmsnorm=False, residual=False
         err = np.linalg.norm(delta - ref.delta) / np.linalg.norm(ref.delta)
         assert err <= TOL_Y_BF16, (t, err)
         worst = max(worst, err)
+        ym, peak, mass = M.layer(x[t], ids[t], gates[t], inp.codebook, inp.record, shape.d, shape.ffn,
+                                 pre_rmsnorm=pre_rmsnorm, eps=1e-6)
+        # the residual add is one more fp32 rounding of x + delta
+        tol = M.element_tolerance(peak, mass) + (np.abs(y[t]) * 2.0 ** -23 if residual else 0.0)
+        bad = np.nonzero(np.abs(delta - ym) > tol)[0]
+        assert bad.size == 0, (t, bad[:8], delta[bad[:8]], ym[bad[:8]], tol[bad[:8]])
     return worst
 
 
@@ -446,6 +583,56 @@ def test_chunk_path_follows_the_oracle(torch_mod, d, ffn, E, k, cb, T):
     ids, gates, y = _run(torch_mod, layer, shape, x)
     worst = _check_chunk(inp, shape, x, ids, gates, y)
     print(f"chunk path {shape} T={T}: worst rel L2 {worst:.3e}")
+    layer.close()
+
+
+@pytest.mark.parametrize("cb", ["f32", "f16"])
+def test_chunk_path_closed_form_element_by_element(torch_mod, cb):
+    """Stage codebooks that are one-hot vectors scaled by 1, 2, 4 (signs per
+    matrix): weight (r, 8j + i) is sum_s sign_s 2^s [code_s(r, j) % 8 == i], an
+    integer in [-7, 7].  With small-integer tokens every weight, token and the
+    pre-activations a, b are exact in bf16 and fp32, so a and b are exact index
+    sums computed here by plain indexing; h is rounded to bf16 as the chunk path
+    does, and the down projection is again an index sum of those h values.
+    Every output element must match (a wrong code byte, stage, slice or lane
+    picks a different h)."""
+    import chunk_model as M
+    from synth import gpu as G
+    d, ffn, E, k, T = 264, 136, 5, 2, 24
+    shape = S.Shape(d, ffn, E, k, cb)
+    inp = G.LayerInputs(shape, seed=23, layer=0, host_codes=True)
+    signs = [(1, 2, 4), (1, -2, 4), (-1, 2, 4)]
+    cbv = np.zeros((E, 3, 3, 256, 8), np.float32)
+    for m in range(3):
+        for s_ in range(3):
+            cbv[:, m, s_, np.arange(256), np.arange(256) % 8] = signs[m][s_]
+    inp.cb = cbv.astype(shape.np_cb_dtype)
+    inp.cb_dev.copy_(G.to_device(inp.cb))
+    layer = _layer(torch_mod, inp, shape, T, chunk_min_tokens=1)
+    rng = np.random.default_rng(5)
+    x = rng.integers(-16, 17, (T, d)).astype(np.float32)
+    ids, gates, y = _run(torch_mod, layer, shape, x)
+
+    def index_sum(codes, v, sg):  # sum_j sum_s sg_s 2^s v[8j + code_s(r, j) % 8]
+        rows, ns, _ = codes.shape
+        base = (np.arange(ns) * 8)[None, :]
+        return sum(sg[s_] * v[base + codes[:, :, s_] % 8].sum(axis=1) for s_ in range(3))
+
+    for t in range(T):
+        ref = np.zeros(d)
+        peak = np.zeros(d)
+        for j in range(k):
+            e, g = int(ids[t, j]), float(gates[t, j])
+            gc, uc, dc = M.matrices(inp.record(e), d, ffn)
+            a = index_sum(gc, x[t].astype(np.float64), signs[0])
+            b = index_sum(uc, x[t].astype(np.float64), signs[1])
+            H = M.bf16((a / (1 + np.exp(-a)) * b).astype(np.float32))
+            ref += g * index_sum(dc, H, signs[2])
+            peak += g * 7 * np.abs(H).max()
+        # two one-ulp flips of a rounded h, plus fp32 accumulation and atomics
+        tol = 2.0 ** -6 * peak + 2.0 ** -20 * np.abs(ref).max()
+        bad = np.nonzero(np.abs(y[t] - ref) > tol)[0]
+        assert bad.size == 0, (t, bad[:8], y[t][bad[:8]], ref[bad[:8]])
     layer.close()
 
 

@@ -146,6 +146,31 @@ def test_topk_equals_best_subset_by_brute_force():
             assert r.margin == srt[k - 1] - srt[k]
 
 
+def test_topk_min_gap_is_the_smallest_pairwise_distance_in_the_top_k():
+    """min_gap decides how strictly ids are compared (ordered list vs set), so
+    it is pinned on its own: brute force over every pair of the selected
+    logits (the smallest |l_i - l_j| among the top k, no sorting involved),
+    exact ties give 0, k = 1 gives +inf, and dyadic logits give exact gaps."""
+    rng = np.random.default_rng(11)
+    for trial in range(200):
+        E = int(rng.integers(2, 40))
+        k = int(rng.integers(2, E + 1))
+        logits = rng.standard_normal(E) * (10.0 ** rng.integers(-3, 3))
+        r = O.topk(logits, k)
+        sel = logits[r.ids]
+        brute = min(abs(sel[i] - sel[j]) for i in range(k) for j in range(k) if i != j)
+        assert r.min_gap == brute, (trial, r.min_gap, brute)
+        # the k selected logits are the k largest: every pairwise distance is
+        # taken among them, never across the boundary
+        assert r.min_gap >= 0.0
+    assert O.topk(np.array([0.25, 3.0, -1.0, 3.0, 2.5]), 3).min_gap == 0.0      # exact tie inside the top k
+    assert O.topk(np.array([0.25, 3.0, -1.0, 3.0, 2.5]), 2).min_gap == 0.0
+    assert O.topk(np.array([4.0, 3.0, 3.0]), 2).min_gap == 1.0                   # the tie sits on the boundary
+    assert O.topk(np.array([4.0, 3.0, 3.0]), 2).margin == 0.0
+    assert math.isinf(O.topk(np.array([0.5, 2.0, 1.0]), 1).min_gap)              # no pair in a top 1
+    assert O.topk(np.array([1.0, 0.125, 0.75, -2.0, 0.5]), 4).min_gap == 0.25   # 1, .75, .5, .125 -> min 0.25
+
+
 def test_topk_ties_go_to_lower_id():
     r = O.topk(np.array([1.0, 2.0, 2.0, 2.0, 0.0]), 2)
     assert r.ids.tolist() == [1, 2]

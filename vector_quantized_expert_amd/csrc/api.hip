@@ -109,6 +109,7 @@ static void free_handle(rvq_moe *h) {
     (void)hipFree(h->ws.part_gu);
     (void)hipFree(h->ws.cnt);
     (void)hipFree(h->ws.err);
+    (void)hipFree(h->ws.cb_exp);
     (void)hipFree(h->cw.X);
     (void)hipFree(h->cw.H);
     (void)hipFree(h->cw.perm);
@@ -159,6 +160,7 @@ static int open_impl(const rvq_moe_desc *desc, rvq_moe *h) {
     h->ws.cnt_phase = 0;
     HIP_TRY(hipMalloc(&h->ws.cnt, sizeof(int) * (size_t)kCntSets * (P + 1) * kCntStride));
     HIP_TRY(hipMalloc(&h->ws.err, sizeof(int)));
+    HIP_TRY(hipMalloc(&h->ws.cb_exp, sizeof(int) * 3 * (size_t)E));
     if (h->max_tokens >= h->chunk_min) {
         HIP_TRY(hipMalloc(&h->cw.X, 2 * (size_t)(P * D.d)));
         HIP_TRY(hipMalloc(&h->cw.H, 2 * (size_t)(P * D.ffn)));
@@ -174,11 +176,15 @@ static int open_impl(const rvq_moe_desc *desc, rvq_moe *h) {
     HIP_TRY(layer_blocks_per_cu(D.codebook_dtype, &per_cu));
     if (n_cu < 1 || per_cu < 1) return fail(RVQ_MOE_EHIP, "occupancy query gave %d CUs x %d blocks", n_cu, per_cu);
     HIP_TRY(init_route(h->ws, D.n_experts, D.top_k, T, n_cu, s));
+    // a streaming handle's router may run on a side stream next to layer
+    // kernels (router lookahead): it takes the kernels that need no co-resident grid
+    if (h->streaming) h->ws.route_one = false;
     h->ws.n_wg = n_cu * per_cu;
     if (h->ws.n_wg > 1024) h->ws.n_wg = 1024;  // a bound on the persistent grid
     HIP_TRY(hipMemsetAsync(h->ws.cnt, 0, sizeof(int) * (size_t)kCntSets * (P + 1) * kCntStride, s));
     HIP_TRY(hipMemsetAsync(h->ws.err, 0, sizeof(int), s));
     HIP_TRY(hipMemcpyAsync(h->cbs, D.codebooks, (size_t)(E * g.cb_bytes), hipMemcpyDeviceToDevice, s));
+    HIP_TRY(launch_cb_exponents(h->cbs, D.codebook_dtype, D.n_experts, h->ws.cb_exp, s));
     HIP_TRY(launch_transpose(D.router_w, h->router_wt, D.d, D.n_experts, s));
     if (h->streaming) {
         const int S = D.cache_slots < D.n_experts ? D.cache_slots : D.n_experts;
@@ -443,6 +449,9 @@ extern "C" int rvq_moe_route_forward(rvq_moe *h, const float *x, int32_t T, int3
         return fail(RVQ_MOE_EINVAL, "n_tokens * top_k = %d above %d for one routed call", T * h->g.k, kRouteMaxPairs);
     if (h->streaming)
         return fail(RVQ_MOE_ENOTSUP, "route_forward needs resident codes (streaming reads the ids on the host)");
+    if (h->g.E > kRouteExperts * h->ws.n_wg)
+        return fail(RVQ_MOE_ENOTSUP, "route_forward: %d experts above %d per workgroup of the %d-workgroup grid",
+                    h->g.E, kRouteExperts, h->ws.n_wg);
     hipStream_t s = static_cast<hipStream_t>(stream);
     const bool prof = h->prof_every > 0 && (h->prof_calls++ % (uint64_t)h->prof_every) == 0;
     {

@@ -159,6 +159,7 @@ struct Workspace {
     int cnt_phase;      // set of the next layer launch (each launch zeroes the other one)
     int *err;           // device error flag: bit 0 bad id, bit 1 wait timeout
     int n_wg;           // persistent workgroups (all resident at once: blocks per CU x CUs)
+    int *cb_exp;        // [E][3] scale exponents of fp32 codebook matrices (0 for fp16), set at open
 };
 
 // Chunk-path workspace (device), sized for max_tokens * k pairs.
@@ -186,6 +187,9 @@ constexpr int kCntStride = 64;
 constexpr int kMaxExperts = 1024;
 constexpr int kMaxTopK = 64;
 constexpr int kRouteMaxPairs = 1024;
+// Routing inside the layer launch: each persistent workgroup computes the
+// logits of at most this many experts (so it needs E <= kRouteExperts * grid).
+constexpr int kRouteExperts = 4;
 // Layer launches alternate between kCntSets counter sets.  Launch n counts in
 // set n % 2 and, as each of its workgroups ends, zeroes its share of the other
 // set: the set launch n - 1 used (it has completed, since launches of one
@@ -207,6 +211,8 @@ hipError_t init_route(Workspace &w, int E, int k, int64_t max_tokens, int n_cu, 
 hipError_t launch_route(const Geometry &g, Workspace &w, const float *x, const float *Wt, int T, int pre,
                         double eps, int32_t *ids, float *gates, hipStream_t s);
 hipError_t layer_blocks_per_cu(int cb_dtype, int *out);
+// The table build's per-matrix scale exponents of fp32 codebooks (zeros for fp16).
+hipError_t launch_cb_exponents(const void *cbs, int cb_dtype, int n_experts, int *out, hipStream_t s);
 // Chunk path: prep + stage (grouping, bf16 tokens, y init), then the
 // contractions for the active experts act[a0 .. a1) (a1 clipped to the number
 // of active experts on the device); launch_chunk does both for all experts.

@@ -130,11 +130,13 @@ struct CbRegs {
     static constexpr int kUnits = kStages * kCodes * kEntryBytes / 16;  // 16-byte units
     static constexpr int kRegs = (kUnits + kBlock - 1) / kBlock;
     uint4 r[kRegs];
+    int ec;  // fp32 codebooks: the matrix's scale exponent (see build_lut)
 };
 
 template <int CB>
-__device__ inline void cb_load(CbRegs<CB> &cr, const void *cbs, int64_t e, int m) {
+__device__ inline void cb_load(CbRegs<CB> &cr, const void *cbs, const int *cb_exp, int64_t e, int m) {
     using C = CbRegs<CB>;
+    cr.ec = CB == 0 ? cb_exp[e * 3 + m] : 0;
     const uint4 *src = reinterpret_cast<const uint4 *>(static_cast<const char *>(cbs) +
                                                        (e * 3 + m) * (int64_t)kStages * kCodes * C::kEntryBytes);
 #pragma unroll
@@ -177,13 +179,20 @@ __device__ inline void cb_store(float *lut, const CbRegs<CB> &cr) {
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
+//
+// fp32 codebooks are first scaled by 2^-ec, ec being the exponent of their
+// matrix's largest finite entry (cb_exponent(), computed once at open), so that
+// entry lies in [2^13, 2^14) as well: the hi + lo split then keeps ~22 bits of
+// every entry whatever the codebook's scale (no fp16 overflow above 65504, no
+// loss to fp16 subnormals for small codebooks); the table is scaled back by
+// 2^(e2 + ec).  All scalings are v_ldexp (exact, no overflow of a scale factor).
 template <int CB>
-__device__ inline void build_lut(float *lut, const float (*vs)[kTileSlices], int e2) {
+__device__ inline void build_lut(float *lut, const float (*vs)[kTileSlices], int e2, int ec) {
     constexpr int kEntryBytes = CB == 0 ? 32 : 16;
     constexpr int kPerRow = 128 / kEntryBytes;
     const int lane = threadIdx.x & 63, wave = wave_id();
     const int j = lane & 31, kh = lane >> 5;
-    const float down = ldexpf(1.f, -e2), up = ldexpf(1.f, e2);
+    const int back = e2 + (CB == 0 ? ec : 0);
     // all eight reads go out before any conversion (one LDS wait, not four)
     float vin[kVec];
 #pragma unroll
@@ -192,7 +201,7 @@ __device__ inline void build_lut(float *lut, const float (*vs)[kTileSlices], int
     half8 bop;
 #pragma unroll
     for (int i = 0; i < kVec; i++) {
-        const float v = vin[i] * down;
+        const float v = __builtin_amdgcn_ldexpf(vin[i], -e2);
         const _Float16 hi = (_Float16)v;
         bop[i] = kh ? (_Float16)(v - (float)hi) : hi;
     }
@@ -215,8 +224,9 @@ __device__ inline void build_lut(float *lut, const float (*vs)[kTileSlices], int
             half8 ahi, alo;
 #pragma unroll
             for (int i = 0; i < kVec; i++) {
-                ahi[i] = (_Float16)w[i];
-                alo[i] = (_Float16)(w[i] - (float)ahi[i]);
+                const float ws = __builtin_amdgcn_ldexpf(w[i], -ec);
+                ahi[i] = (_Float16)ws;
+                alo[i] = (_Float16)(ws - (float)ahi[i]);
             }
             acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ahi, bop, acc, 0, 0, 0);
             acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(alo, bop, acc, 0, 0, 0);
@@ -228,7 +238,7 @@ __device__ inline void build_lut(float *lut, const float (*vs)[kTileSlices], int
 #pragma unroll
         for (int v = 0; v < 16; v++) {
             const int c = c0 + 8 * (v >> 2) + 4 * kh + (v & 3);
-            lut[lut_word(s, c, j)] = acc[v] * up;
+            lut[lut_word(s, c, j)] = __builtin_amdgcn_ldexpf(acc[v], back);
         }
     };
     const int mb0 = wave, mb1 = wave + kWaves;  // wave-uniform
@@ -257,6 +267,41 @@ __device__ __forceinline__ int tile_exponent(const float *red2) {
     int ex;
     frexpf(m, &ex);  // m = f * 2^ex, f in [0.5, 1)
     return ex - 14;
+}
+
+// Exponent ec of each fp32 codebook matrix (all three stages of one expert's
+// gate, up or down): max|entry| * 2^-ec in [2^13, 2^14) over its finite
+// entries (0 when all are zero or not finite).  One workgroup per matrix.
+__global__ __launch_bounds__(256) void k_cb_exponent(const float *__restrict__ cbs, int n_mats,
+                                                     int *__restrict__ out) {
+    const float *c = cbs + (size_t)blockIdx.x * kStages * kCodes * kVec;
+    float m = 0.f;
+    for (int i = threadIdx.x; i < kStages * kCodes * kVec; i += 256) {
+        const float v = fabsf(c[i]);
+        if (isfinite(v)) m = fmaxf(m, v);
+    }
+    __shared__ float red[256];
+    red[threadIdx.x] = m;
+    __syncthreads();
+    for (int w = 128; w > 0; w >>= 1) {
+        if (threadIdx.x < w) red[threadIdx.x] = fmaxf(red[threadIdx.x], red[threadIdx.x + w]);
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) {
+        int ex = 0;
+        if (red[0] > 0.f) {
+            frexpf(red[0], &ex);
+            ex -= 14;
+        }
+        out[blockIdx.x] = ex;
+    }
+}
+
+hipError_t launch_cb_exponents(const void *cbs, int cb_dtype, int n_experts, int *out, hipStream_t s) {
+    if (cb_dtype != 0) return hipMemsetAsync(out, 0, sizeof(int) * 3 * (size_t)n_experts, s);
+    hipLaunchKernelGGL(k_cb_exponent, dim3(3 * n_experts), dim3(256), 0, s, static_cast<const float *>(cbs),
+                       3 * n_experts, out);
+    return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
@@ -512,6 +557,7 @@ struct LayerArgs {
     const uint8_t *codes;
     const uint8_t *const *slot_tab;  // [E] record of each expert (HBM slot cache), or null: codes + e * rec
     const void *cbs;
+    const int *cb_exp;  // [E][3] scale exponents of fp32 codebooks (see build_lut)
     const float *x;
     const int32_t *ids;
     const float *gates;
@@ -567,11 +613,15 @@ __device__ inline bool merged_away(int64_t nA, int G, int64_t u0, int n_cf, bool
     return nA * (r0 + 1) / G >= u0 + 2 * (int64_t)n_cf;
 }
 
+// Input tiles of a gate/up matrix are at most 65536 / 8 / 32 = 256 (d <=
+// 65536): the valid-slot masks take kMaskWords 64-bit words per matrix.
+constexpr int kMaskWords = 4;
+
 // h' = gate * silu(a) * b for the 256 FFN entries of down tile ft of pair p,
 // where a and b are the gate and up row sums (sum over the input tiles' partial
 // sums; only the slots vmask marks hold one, see merged_away).
 __device__ inline void finish_h(const LayerArgs &a, const float *gate_src, int p, int ft, float (*vs)[kTileSlices],
-                                float *red2, const uint64_t *vmask) {
+                                float *red2, const uint64_t (*vmask)[kMaskWords]) {
     // threads 0..255, one entry each: the valid slots in batches of 16 per
     // matrix, every load of a batch in flight together
     const Geometry &g = a.g;
@@ -583,23 +633,26 @@ __device__ inline void finish_h(const LayerArgs &a, const float *gate_src, int p
     if (f < g.ffn) {
         const float *pa = a.part_gu + ((int64_t)p * 2) * n_ti * g.ffn_pad + f;
         const float *pb = pa + (int64_t)n_ti * g.ffn_pad;
-        // vmask[m] bit t: tile t's partial slot holds a sum (not merged into a
-        // later tile's slot by the workgroup that covered both)
-        uint64_t ma = vmask[0], mb = vmask[1];
-        while (ma | mb) {  // uniform
-            float va[16], vb[16];
+        // vmask[m][w] bit t: tile 64 w + t's partial slot holds a sum (not
+        // merged into a later tile's slot by the workgroup that covered both)
+        const int n_words = (n_ti + 63) / 64;
+        for (int w = 0; w < n_words; w++) {  // uniform
+            uint64_t ma = vmask[0][w], mb = vmask[1][w];
+            while (ma | mb) {  // uniform
+                float va[16], vb[16];
 #pragma unroll
-            for (int j = 0; j < 16; j++) {
-                const int ta = ma ? __builtin_ctzll(ma) : -1, tb = mb ? __builtin_ctzll(mb) : -1;
-                ma &= ma - 1;
-                mb &= mb - 1;
-                va[j] = ta >= 0 ? load_coherent(pa + (int64_t)ta * g.ffn_pad) : 0.f;
-                vb[j] = tb >= 0 ? load_coherent(pb + (int64_t)tb * g.ffn_pad) : 0.f;
-            }
+                for (int j = 0; j < 16; j++) {
+                    const int ta = ma ? 64 * w + __builtin_ctzll(ma) : -1, tb = mb ? 64 * w + __builtin_ctzll(mb) : -1;
+                    ma &= ma - 1;
+                    mb &= mb - 1;
+                    va[j] = ta >= 0 ? load_coherent(pa + (int64_t)ta * g.ffn_pad) : 0.f;
+                    vb[j] = tb >= 0 ? load_coherent(pb + (int64_t)tb * g.ffn_pad) : 0.f;
+                }
 #pragma unroll
-            for (int j = 0; j < 16; j++) {
-                sa += va[j];
-                sb += vb[j];
+                for (int j = 0; j < 16; j++) {
+                    sa += va[j];
+                    sb += vb[j];
+                }
             }
         }
     }
@@ -909,7 +962,7 @@ __device__ void select_top_local(const double *lg, int E, int k, double *sel_out
 //      them itself (select_top_local): every workgroup reaches the same ids,
 //      with no further exchange.  The gates follow in route_gates (one exp
 //      each, summed in rank order); workgroup 0 writes ids and gates out.
-constexpr int kRouteExp = 4;  // experts per workgroup (E <= 4 G)
+constexpr int kRouteExp = kRouteExperts;  // experts per workgroup (E <= 4 G)
 // `idle` runs once R1 is published, before the wait for the other logits.
 template <class Idle>
 __device__ void route_phase(const LayerArgs &a, double *scratch, float *gate_lds, int *pair_ids, Idle &&idle) {
@@ -1178,16 +1231,16 @@ __global__ __launch_bounds__(kBlock) void k_layer(LayerArgs a) {
     };
 
     // merged gate/up partial sums in the pair order (see merged_away)
-    const bool merge = !ord.tab && n_cf <= 64 && n_ti <= 64;
+    const bool merge = !ord.tab && n_cf <= 64;
     const int64_t nA = (int64_t)P * 2 * n_ti * n_cf;
-    __shared__ uint64_t vmask[2];
+    __shared__ uint64_t vmask[2][kMaskWords];
     // ---------------- phase A: gate and up
     {
         int u = uA;
         const int u1 = uA1;
         float xv = 0.f;  // this thread's raw input element of the segment's tile
         auto prefetch = [&](const SegA &sg) {
-            if (sg.e >= 0 && sg.e < g.E) cb_load<CB>(cb, a.cbs, sg.e, sg.m);
+            if (sg.e >= 0 && sg.e < g.E) cb_load<CB>(cb, a.cbs, a.cb_exp, sg.e, sg.m);
             const int col = sg.tile * kTileSlices * kVec + threadIdx.x;
             xv = (threadIdx.x < kTileSlices * kVec && col < g.d) ? a.x[(size_t)(sg.p / g.k) * g.d + col] : 0.f;
         };
@@ -1251,7 +1304,7 @@ __global__ __launch_bounds__(kBlock) void k_layer(LayerArgs a) {
                 const bool flush = pend_out && !extend;
                 __syncthreads();
                 if (flush) flush_pend();
-                build_lut<CB>(lut, vs, tile_exponent(red2));
+                build_lut<CB>(lut, vs, tile_exponent(red2), cb.ec);
                 if (flush) count(pend_p, pend_n);
                 if (pend_out && !y_signalled) publish();
                 __syncthreads();
@@ -1305,7 +1358,7 @@ __global__ __launch_bounds__(kBlock) void k_layer(LayerArgs a) {
         SegB cur{};
         if (u < u1) {
             cur = seg_b(u, u1, n_tf, n_cd, ord);
-            if (cur.e >= 0 && cur.e < g.E) cb_load<CB>(cb, a.cbs, cur.e, 2);
+            if (cur.e >= 0 && cur.e < g.E) cb_load<CB>(cb, a.cbs, a.cb_exp, cur.e, 2);
         }
         while (u < u1) {
             const int un = u + (cur.c1 - cur.c0);
@@ -1320,19 +1373,19 @@ __global__ __launch_bounds__(kBlock) void k_layer(LayerArgs a) {
                     load_chunk(base + (int64_t)(cur.c0 + wave) * kChunkBytes, lane, p[0], p[1], p[2], kNT);
                 // which gate/up partial slots of this pair hold sums (before the
                 // wait, whose barrier publishes it)
-                if (threadIdx.x < 128) {
-                    const int m = threadIdx.x >> 6, t = threadIdx.x & 63;
+                if (threadIdx.x < 2 * 64 * kMaskWords) {  // one wave per mask word
+                    const int m = threadIdx.x / (64 * kMaskWords), t = threadIdx.x % (64 * kMaskWords);
                     const int64_t u0 = (((int64_t)cur.p * 2 + m) * n_ti + t) * n_cf;
                     const bool has = t < n_ti && !(merge && merged_away(nA, G, u0, n_cf, t + 1 == n_ti));
                     const uint64_t bits = __ballot(has);
-                    if ((threadIdx.x & 63) == 0) vmask[m] = bits;
+                    if ((threadIdx.x & 63) == 0) vmask[m][t / 64] = bits;
                 }
                 wait_count(a.cntA + cur.p * kCntStride, needA, a.err);
                 finish_h(a, gate_src, cur.p, cur.ft, vs, red2, vmask);
                 __syncthreads();
-                build_lut<CB>(lut, vs, tile_exponent(red2));
+                build_lut<CB>(lut, vs, tile_exponent(red2), cb.ec);
                 __syncthreads();
-                if (un < u1 && nxt.e >= 0 && nxt.e < g.E) cb_load<CB>(cb, a.cbs, nxt.e, 2);
+                if (un < u1 && nxt.e >= 0 && nxt.e < g.E) cb_load<CB>(cb, a.cbs, a.cb_exp, nxt.e, 2);
                 if (!y_ready) {
                     wait_count(a.ycnt, G, a.err);
                     y_ready = true;
@@ -1348,7 +1401,7 @@ __global__ __launch_bounds__(kBlock) void k_layer(LayerArgs a) {
                 if (cur.ft == 0)
                     for (int r = cur.c0 * kChunkRows + threadIdx.x; r < min(g.d, cur.c1 * kChunkRows); r += kBlock)
                         unsafeAtomicAdd(a.y + (size_t)(cur.p / g.k) * g.d + r, __int_as_float(0x7fc00000));
-                if (un < u1 && nxt.e >= 0 && nxt.e < g.E) cb_load<CB>(cb, a.cbs, nxt.e, 2);
+                if (un < u1 && nxt.e >= 0 && nxt.e < g.E) cb_load<CB>(cb, a.cbs, a.cb_exp, nxt.e, 2);
             }
             __syncthreads();
             cur = nxt;
@@ -1383,18 +1436,15 @@ hipError_t launch_layer(const Geometry &g, Workspace &w, const uint8_t *codes, c
         const int par = w.fused_parity;
         rl_cur = w.fused_logits + (par ? cap : 0);
         rl_next = w.fused_logits + (par ? 0 : cap);
-        w.fused_parity ^= 1;
         T_reset = w.fused_prev_T;
-        w.fused_prev_T = T;
     }
     // counter sets rotate over launches (see kCntSets)
     const size_t set_ints = (size_t)w.cnt_per_set * kCntStride;
     int *cnt_cur = w.cnt + w.cnt_phase * set_ints;
     int *cnt_clear = w.cnt + ((w.cnt_phase + 1) % kCntSets) * set_ints;
-    w.cnt_phase = (w.cnt_phase + 1) % kCntSets;
     LayerArgs a{Wt, w.logits, w.sel, cnt_cur + (size_t)(w.cnt_per_set - 1) * kCntStride, cnt_clear, w.cnt_per_set,
-                rl_cur, rl_next, T_reset, list, codes, slot_tab, cbs, x, ids, gates, y, w.part_gu, cnt_cur,
-                w.err, g, T, pre, residual, eps};
+                rl_cur, rl_next, T_reset, list, codes, slot_tab, cbs, w.cb_exp, x, ids, gates, y, w.part_gu,
+                cnt_cur, w.err, g, T, pre, residual, eps};
     // A plain launch of exactly as many workgroups as can be resident at once
     // (sized at open from the occupancy query); the inter-workgroup waits are
     // bounded, so a launch that somehow did not get all of them resident ends
@@ -1402,7 +1452,16 @@ hipError_t launch_layer(const Geometry &g, Workspace &w, const uint8_t *codes, c
     const bool group = list || (T > 1 && T * g.k <= kOrderMax);  // the kernel takes the same decision
     hipLaunchKernelGGL(layer_kernel(g.cb_dtype, list ? kListed : route ? kRouted : kFromIds, !group), dim3(w.n_wg),
                        dim3(kBlock), 0, s, a);
-    return hipGetLastError();
+    const hipError_t e = hipGetLastError();
+    // the alternating buffers and counter sets advance only with a launch that
+    // was enqueued: a failed launch leaves them as the last launch left them
+    if (e != hipSuccess) return e;
+    if (route) {
+        w.fused_parity ^= 1;
+        w.fused_prev_T = T;
+    }
+    w.cnt_phase = (w.cnt_phase + 1) % kCntSets;
+    return hipSuccess;
 }
 
 hipError_t layer_blocks_per_cu(int cb_dtype, int *out) {

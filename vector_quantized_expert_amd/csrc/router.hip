@@ -488,9 +488,12 @@ hipError_t launch_route(const Geometry &g, Workspace &w, const float *x, const f
         double *lg[2] = {w.route_logits + w.route_cap, w.route_logits + w.route_cap + g.E};
         double *sl[2] = {w.route_logits + w.route_cap + 2 * g.E, w.route_logits + w.route_cap + 2 * g.E + kMaxTopK};
         const int p = w.route_parity;
-        w.route_parity ^= 1;
         hipLaunchKernelGGL(k_route_one, dim3(g.E), dim3(256), 0, s, x, Wt, g.d, g.E, g.k, pre, eps, lg[p], lg[p ^ 1],
                            sl[p], sl[p ^ 1], w.err, ids, gates);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;  // the buffers alternate only with an enqueued launch
+        w.route_parity ^= 1;
+        return hipSuccess;
     } else {
         // the logits area of the several-token path: plain values, handed from
         // the contraction to the selection across the launch boundary
