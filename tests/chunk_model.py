@@ -36,22 +36,27 @@ def matrices(record: np.ndarray, d: int, ffn: int):
     return g, u, dn
 
 
-def dense_weights(cb: np.ndarray, codes: np.ndarray) -> np.ndarray:
-    """bf16((c1 + c2) + c3) with the two sums in fp32, as a [rows][cols] float64 matrix."""
-    c = cb.astype(np.float32)
+def dense_weights(cb: np.ndarray, codes: np.ndarray, rounded: bool = True) -> np.ndarray:
+    """bf16((c1 + c2) + c3) with the two sums in fp32, as a [rows][cols] float64
+    matrix (rounded=False: the exact sum, in float64)."""
     rows, ns, _ = codes.shape
+    if not rounded:
+        c = cb.astype(np.float64)
+        return ((c[0][codes[:, :, 0]] + c[1][codes[:, :, 1]]) + c[2][codes[:, :, 2]]).reshape(rows, ns * 8)
+    c = cb.astype(np.float32)
     w = (c[0][codes[:, :, 0]] + c[1][codes[:, :, 1]]) + c[2][codes[:, :, 2]]
     return bf16(w.reshape(rows, ns * 8))
 
 
-def expert(cb: np.ndarray, record: np.ndarray, d: int, ffn: int, xb: np.ndarray):
-    """One expert on bf16 tokens xb: returns (y, Wd, H) with H = bf16(silu(a) b)."""
+def expert(cb: np.ndarray, record: np.ndarray, d: int, ffn: int, xb: np.ndarray, rounded: bool = True):
+    """One expert on tokens xb: returns (y, Wd, H) with H = bf16(silu(a) b)
+    (rounded=False: no rounding anywhere, for experts the table path evaluates)."""
     gc, uc, dc = matrices(record, d, ffn)
-    a = dense_weights(cb[0], gc) @ xb
-    b = dense_weights(cb[1], uc) @ xb
+    a = dense_weights(cb[0], gc, rounded) @ xb
+    b = dense_weights(cb[1], uc, rounded) @ xb
     h = a / (1.0 + np.exp(-a)) * b
-    H = bf16(h.astype(np.float32))
-    Wd = dense_weights(cb[2], dc)
+    H = bf16(h.astype(np.float32)) if rounded else h
+    Wd = dense_weights(cb[2], dc, rounded)
     return Wd @ H, Wd, H
 
 
@@ -66,16 +71,28 @@ def token_x(x: np.ndarray, pre_rmsnorm: bool, eps: float) -> np.ndarray:
     return bf16(x)
 
 
-def layer(x, ids, gates, get_codebook, get_record, d: int, ffn: int, pre_rmsnorm=False, eps=1e-6):
+def token_exact(x: np.ndarray, pre_rmsnorm: bool, eps: float) -> np.ndarray:
+    """The unrounded token (float64) the table path takes."""
+    x64 = np.asarray(x, dtype=np.float32).astype(np.float64)
+    return x64 / np.sqrt(np.dot(x64, x64) / x64.shape[0] + eps) if pre_rmsnorm else x64
+
+
+def layer(x, ids, gates, get_codebook, get_record, d: int, ffn: int, pre_rmsnorm=False, eps=1e-6,
+          table_experts=()):
     """MoE output (before any residual add) of one token under the chunk path's
     rounding, plus per-element error scales: for each output element q,
-    `peak` = sum_j g_j max_r |Wd_qr H_r| and `mass` = sum_j g_j sum_r |Wd_qr| |H_r|."""
+    `peak` = sum_j g_j max_r |Wd_qr H_r| and `mass` = sum_j g_j sum_r |Wd_qr| |H_r|.
+    Experts in table_experts (handed to the fp32 table path by adaptive
+    dispatch) are taken without any rounding."""
     xb = token_x(x, pre_rmsnorm, eps)
+    xe = token_exact(x, pre_rmsnorm, eps)
     y = np.zeros(d)
     peak = np.zeros(d)
     mass = np.zeros(d)
     for e, g in zip(ids, gates):
-        ye, Wd, H = expert(get_codebook(int(e)), get_record(int(e)), d, ffn, xb)
+        exact = int(e) in table_experts
+        ye, Wd, H = expert(get_codebook(int(e)), get_record(int(e)), d, ffn, xe if exact else xb,
+                           rounded=not exact)
         prod = np.abs(Wd) * np.abs(H)[None, :]
         y += float(g) * ye
         peak += float(g) * prod.max(axis=1)
