@@ -301,6 +301,29 @@ int rvq_moe_layer_forward(rvq_moe *h, const float *x, int32_t n_tokens, const in
                           const float *gates, float *y, void *stream);
 
 /*
+ * rvq_moe_layer_forward_noalloc -- rvq_moe_layer_forward's table path (per-token
+ * tables of partial dot products, fp32) with no memory of the handle's
+ * workspace and no allocation of any kind: for callers that cannot allocate
+ * while they run (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  The kernels' scratch -- gate/up partial
+ * sums and inter-workgroup completion counters -- lives in one static device
+ * array of 32 MiB per GPU (set up by the first rvq_moe_open on that GPU, held
+ * until the process ends); its counters are cleared by a small kernel (no
+ * memset) at the start of every call.  Every call on one GPU, from any
+ * handle, shares that array: calls that overlap in time on one GPU race.
+ * Same arguments, semantics and output as rvq_moe_layer_forward below its
+ * chunk threshold (always the table path here, whatever n_tokens).
+ *   Needs 2 * (n_tokens * top_k + 1) * 256 bytes of counters (rounded up to
+ *   256) plus n_tokens * top_k * 2 * ceil(d / 256) * ceil(ffn / 32) * 128
+ *   bytes of partial sums within the 32 MiB (d=7168, ffn=2048, top-16: up to
+ *   4 tokens per call).
+ * Errors: EINVAL (as layer_forward; or a call that needs more scratch than the
+ * array holds), ENOTSUP (streaming codes), EHIP.
+ */
+int rvq_moe_layer_forward_noalloc(rvq_moe *h, const float *x, int32_t n_tokens, const int32_t *ids,
+                                  const float *gates, float *y, void *stream);
+
+/*
  * rvq_moe_route_forward -- rvq_moe_route_topk and rvq_moe_layer_forward in one
  * launch: writes ids and gates (the same selection: top k of fp64 logits,
  * descending, ties to the lower id, softmax over the k) and y (the layer output

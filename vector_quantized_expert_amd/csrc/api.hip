@@ -175,6 +175,7 @@ static int open_impl(const rvq_moe_desc *desc, rvq_moe *h) {
     int per_cu = 0;
     HIP_TRY(layer_blocks_per_cu(D.codebook_dtype, &per_cu));
     if (n_cu < 1 || per_cu < 1) return fail(RVQ_MOE_EHIP, "occupancy query gave %d CUs x %d blocks", n_cu, per_cu);
+    HIP_TRY(static_scratch_setup(h->device));  // once per device: rvq_moe_layer_forward_noalloc's scratch
     HIP_TRY(init_route(h->ws, D.n_experts, D.top_k, T, n_cu, s));
     // a streaming handle's router may run on a side stream next to layer
     // kernels (router lookahead): it takes the kernels that need no co-resident grid
@@ -436,6 +437,48 @@ extern "C" int rvq_moe_layer_forward(rvq_moe *h, const float *x, int32_t T, cons
     h->stats.forward_calls++;
     h->stats.tokens_forwarded += (uint64_t)T;
     h->stats.expert_evals += (uint64_t)T * (uint64_t)h->g.k;
+    return RVQ_MOE_OK;
+}
+
+extern "C" int rvq_moe_layer_forward_noalloc(rvq_moe *h, const float *x, int32_t T, const int32_t *ids,
+                                             const float *gates, float *y, void *stream) {
+    int rc = check_call(h, x, T);
+    if (rc) return rc;
+    if (!ids || !gates || !y) return fail(RVQ_MOE_EINVAL, "ids/gates/y is NULL");
+    if ((const void *)y == (const void *)x) return fail(RVQ_MOE_EINVAL, "y aliases x");
+    if (h->streaming)
+        return fail(RVQ_MOE_ENOTSUP, "layer_forward_noalloc needs resident codes (streaming reads the ids on the host)");
+    // the static scratch: both completion counter sets, then the gate/up partial sums
+    const Geometry &g = h->g;
+    const int64_t P = (int64_t)T * g.k;
+    const size_t cnt_ints = (size_t)kCntSets * (size_t)(P + 1) * kCntStride;
+    const size_t part_off = (cnt_ints * sizeof(int) + 255) / 256 * 256;
+    const size_t need = part_off + sizeof(float) * (size_t)P * 2 * g.m[0].n_tiles * g.ffn_pad;
+    if (need > kStaticScratchBytes)
+        return fail(RVQ_MOE_EINVAL,
+                    "layer_forward_noalloc: %d tokens need %zu bytes of scratch, above the static %zu (fewer tokens "
+                    "per call)",
+                    T, need, kStaticScratchBytes);
+    char *base = static_scratch(h->device);
+    if (!base) return fail(RVQ_MOE_EHIP, "static scratch not set up on device %d", h->device);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    Workspace w = h->ws;  // the handle's own workspace is not touched
+    w.cnt = reinterpret_cast<int *>(base);
+    w.cnt_per_set = (int)(P + 1);
+    w.cnt_phase = 0;
+    w.part_gu = reinterpret_cast<float *>(base + part_off);
+    const bool prof = h->prof_every > 0 && (h->prof_calls++ % (uint64_t)h->prof_every) == 0;
+    {
+        ProfScope p(h, s, prof, 1);
+        // the counters start at zero in every call (the array keeps the last
+        // call's contents, possibly another handle's), by a kernel, not a memset
+        HIP_TRY(launch_zero_ints(w.cnt, (int)cnt_ints, s));
+        HIP_TRY(launch_layer(g, w, h->codes, nullptr, h->cbs, h->router_wt, x, ids, gates, y, T, h->pre_rmsnorm,
+                             h->residual, h->eps, false, s));
+    }
+    h->stats.forward_calls++;
+    h->stats.tokens_forwarded += (uint64_t)T;
+    h->stats.expert_evals += (uint64_t)T * (uint64_t)g.k;
     return RVQ_MOE_OK;
 }
 

@@ -211,6 +211,12 @@ hipError_t init_route(Workspace &w, int E, int k, int64_t max_tokens, int n_cu, 
 hipError_t launch_route(const Geometry &g, Workspace &w, const float *x, const float *Wt, int T, int pre,
                         double eps, int32_t *ids, float *gates, hipStream_t s);
 hipError_t layer_blocks_per_cu(int cb_dtype, int *out);
+// Static device scratch of rvq_moe_layer_forward_noalloc (noalloc.hip):
+// kStaticScratchBytes per device, its address looked up once per device.
+constexpr size_t kStaticScratchBytes = (size_t)32 << 20;
+hipError_t static_scratch_setup(int device);  // the device must be current
+char *static_scratch(int device);             // null before setup
+hipError_t launch_zero_ints(int *p, int n, hipStream_t s);
 // The table build's per-matrix scale exponents of fp32 codebooks (zeros for fp16).
 hipError_t launch_cb_exponents(const void *cbs, int cb_dtype, int n_experts, int *out, hipStream_t s);
 // Chunk path: prep + stage (grouping, bf16 tokens, y init), then the

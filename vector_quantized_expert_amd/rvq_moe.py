@@ -99,6 +99,7 @@ def lib():
         L.rvq_moe_route_topk.argtypes = [vp, vp, i32, vp, vp, vp]
         L.rvq_moe_layer_forward.argtypes = [vp, vp, i32, vp, vp, vp, vp]
         L.rvq_moe_route_forward.argtypes = [vp, vp, i32, vp, vp, vp, vp]
+        L.rvq_moe_layer_forward_noalloc.argtypes = [vp, vp, i32, vp, vp, vp, vp]
         L.rvq_moe_prefetch.argtypes = [vp, vp, i32, i32, vp]
         L.rvq_moe_bank_layout.argtypes = [ctypes.POINTER(Desc), ctypes.POINTER(ctypes.c_int64),
                                           ctypes.POINTER(ctypes.c_int64)]
@@ -113,6 +114,7 @@ def lib():
         L.rvq_moe_kernel_times.argtypes = [vp, ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(ctypes.c_uint64),
                                            ctypes.POINTER(ctypes.c_double), ctypes.c_int]
         for n in ("rvq_moe_open", "rvq_moe_route_topk", "rvq_moe_layer_forward", "rvq_moe_route_forward",
+                  "rvq_moe_layer_forward_noalloc",
                   "rvq_moe_prefetch", "rvq_moe_sync", "rvq_moe_bank_layout", "rvq_moe_write_bank",
                   "rvq_moe_close", "rvq_moe_abi_version", "rvq_moe_get_stats", "rvq_moe_set_profiling",
                   "rvq_moe_kernel_times"):
@@ -217,6 +219,10 @@ class RvqMoe:
     def layer_forward(self, x, n_tokens, ids, gates, y, stream=None):
         return _check(lib().rvq_moe_layer_forward(self.h, _ptr(x), n_tokens, _ptr(ids), _ptr(gates), _ptr(y),
                                                   _stream(stream)), "rvq_moe_layer_forward")
+
+    def layer_forward_noalloc(self, x, n_tokens, ids, gates, y, stream=None):
+        return _check(lib().rvq_moe_layer_forward_noalloc(self.h, _ptr(x), n_tokens, _ptr(ids), _ptr(gates),
+                                                          _ptr(y), _stream(stream)), "rvq_moe_layer_forward_noalloc")
 
     def route_forward(self, x, n_tokens, ids, gates, y, stream=None):
         return _check(lib().rvq_moe_route_forward(self.h, _ptr(x), n_tokens, _ptr(ids), _ptr(gates), _ptr(y),
