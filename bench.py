@@ -11,7 +11,19 @@ combine -- by default as one rvq_moe_route_forward call (the fastest way at
 batch 1; --path two-call times rvq_moe_route_topk then rvq_moe_layer_forward),
 every token distinct, all inputs resident in HBM before the timed region.
 
-Other workloads of the same layer shape:
+The default run also reports, in the same JSON line:
+  - five repetitions of the K timed steps (median and range of ms per step)
+    and per-call latency percentiles from events around every call;
+  - measured ceilings of this machine (HBM streaming read, the table path's
+    LDS gather rate, the fixed cost of a persistent-shaped launch, pinned
+    host-to-device copies of expert records);
+  - sub-records for the other workloads of the same layer shape: batched
+    decode (32 tokens per call), the prefill chunk (512 tokens per call,
+    resident) and the 16-layer depth chain;
+  - the oracle on the host cores (one thread and all threads) and a parity
+    sample of the timed tokens.
+
+Other workloads as the headline (flags):
   --batch B    B tokens per call (batched decode, pairs grouped by expert);
   --chunk      with --batch: every call takes the chunk path (prefill chunk:
                weights rebuilt as bf16 tiles feeding the matrix cores);
@@ -25,11 +37,6 @@ Other workloads of the same layer shape:
                the next layer's router runs on this layer's input and the
                first N of its predicted experts are prefetched into the next
                layer's slots (router lookahead).
-
-Prints one JSON line: tokens/s (value), effective compressed-weight GB/s and
-its fraction of the 8 TB/s HBM peak, the roofline record of the dominant
-kernel (the layer kernel, timed with HIP events on its launch stream), and the
-oracle timed on the host cores on a bounded sample (cpu_baseline).
 """
 from __future__ import annotations
 
@@ -38,6 +45,7 @@ import glob
 import hashlib
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -45,6 +53,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
 METRIC = "routed MoE-layer tokens/s + effective compressed-weight GB/s vs HBM peak"
 CB_BYTES = 3 * 3 * 256 * 8 * 2  # one expert's fp16 codebooks (3 matrices x 3 stages)
 
@@ -84,12 +93,257 @@ def recorded_traffic(fused: bool):
     return int(fields["traffic_bytes_per_launch"])
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def percentile(v, q):
+    s = sorted(v)
+    if not s:
+        return None
+    i = min(len(s) - 1, max(0, int(round(q / 100.0 * (len(s) - 1)))))
+    return s[i]
+
+
+def measure_ceilings(torch, shape):
+    """This machine's ceilings: HBM streaming read over 8 GiB, the table path's
+    LDS gather rate, the fixed cost of a persistent-shaped launch, and pinned
+    host-to-device copies of expert records (1 GiB in record-sized pieces)."""
+    from vector_quantized_expert_amd import ceilings as C
+    stream = torch.cuda.current_stream()
+    out = {}
+    buf = torch.empty(8 << 30, dtype=torch.uint8, device="cuda")
+    buf.fill_(1)
+    out["hbm_read_GBps"] = C.hbm_read_GBps(buf, 3, stream)
+    out["hbm_read_frac_of_peak"] = out["hbm_read_GBps"] / HBM_PEAK_GBPS
+    out["hbm_read_bytes"] = 3 * buf.numel()
+    del buf
+    torch.cuda.empty_cache()
+    lds = C.lds_gather_rate(2000, stream)
+    out["lds_gather_lookups_per_s"] = lds["lookups_per_s"]
+    out["lds_gather_code_GBps"] = lds["code_GBps"]
+    out["persistent_launch_us"] = C.launch_gap_us(500, stream)
+    rec_b = shape.record_bytes
+    n_rec = (1 << 30) // rec_b
+    src = torch.empty(n_rec * rec_b, dtype=torch.uint8, pin_memory=True)
+    dst = torch.empty(n_rec * rec_b, dtype=torch.uint8, device="cuda")
+    dst.copy_(src, non_blocking=True)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(3):
+        for i in range(n_rec):
+            dst[i * rec_b:(i + 1) * rec_b].copy_(src[i * rec_b:(i + 1) * rec_b], non_blocking=True)
+    e1.record()
+    torch.cuda.synchronize()
+    out["h2d_pinned_record_GBps"] = 3 * n_rec * rec_b / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del src, dst
+    torch.cuda.empty_cache()
+    return out
+
+
+def oracle_baseline(O, S, shape, tokens, w_r, cb_of, rec_of, pre, residual, layers_in=None):
+    """Time the oracle on the host: one thread on a few tokens, all threads on
+    more.  The code records it reads are fetched before each timed loop."""
+    def run(xs):
+        for x in xs:
+            O.layer(x, w_r, shape.top_k, cb_of, rec_of, shape.d, shape.ffn, pre_rmsnorm=pre, eps=1e-6,
+                    residual=residual)
+
+    # records of the experts each token routes to, fetched (untimed)
+    for x in tokens:
+        r = O.route(x, w_r, shape.top_k, pre_rmsnorm=pre, eps=1e-6)
+        for e in r.ids:
+            rec_of(int(e))
+    n_all = O.threads()
+    one = tokens[:4]
+    O.set_threads(1)
+    t0 = time.perf_counter()
+    run(one)
+    t_one = time.perf_counter() - t0
+    O.set_threads(n_all)
+    t0 = time.perf_counter()
+    run(tokens)
+    t_all = time.perf_counter() - t0
+    return {"one": len(one) / t_one, "all": len(tokens) / t_all, "n_one": len(one), "n_all": len(tokens),
+            "threads": n_all, "s_one": t_one, "s_all": t_all}
+
+
+class RecordCache:
+    """Host copies of expert records for the oracle: from a host copy of the
+    device bank when there is one, else regenerated from the seed."""
+
+    def __init__(self, S, seed, layer, rec_bytes, bank_host=None):
+        self.S, self.seed, self.layer, self.rb, self.bank = S, seed, layer, rec_bytes, bank_host
+        self.cache = {}
+
+    def __call__(self, e):
+        if self.bank is not None:
+            return self.bank[e]
+        if e not in self.cache:
+            self.cache[e] = self.S.expert_record(self.seed, self.layer, e, self.rb)
+        return self.cache[e]
+
+
+def sub_records(torch, np, G, S, O, RvqMoe, inp, args, bank_host):
+    """Batched decode (32 tokens per call), the resident prefill chunk (512
+    tokens per call) and the 16-layer depth chain, each timed briefly on the
+    same layer shape with a parity sample against the oracle."""
+    shape = S.K3
+    stream = torch.cuda.current_stream()
+    rec = shape.record_bytes
+    out = {}
+    rec_of = RecordCache(S, args.seed, 0, rec, bank_host)
+    handle = RvqMoe(d=shape.d, ffn=shape.ffn, n_experts=shape.n_experts, top_k=shape.top_k, codebook_dtype=1,
+                    router_w=inp.w_r_dev, codebooks=inp.cb_dev, codes=inp.codes_dev, max_tokens=512)
+    inp.free_codes()
+    torch.cuda.empty_cache()
+
+    def timed(B, calls, warm, t0):
+        x_host = S.tokens(args.seed, t0, (warm + calls) * B, shape.d)
+        x = G.to_device(x_host)
+        ids = torch.empty(((warm + calls) * B, shape.top_k), dtype=torch.int32, device="cuda")
+        g = torch.empty(((warm + calls) * B, shape.top_k), device="cuda")
+        y = torch.empty(((warm + calls) * B, shape.d), device="cuda")
+
+        def call(c):
+            r = slice(c * B, (c + 1) * B)
+            handle.route_topk(x[r], B, ids[r], g[r], stream)
+            handle.layer_forward(x[r], B, ids[r], g[r], y[r], stream)
+        for c in range(warm):
+            call(c)
+        handle.sync(stream)
+        handle.kernel_times()
+        handle.set_profiling(1)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for c in range(warm, warm + calls):
+            call(c)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        handle.set_profiling(0)
+        kt = handle.kernel_times()
+        handle.sync(stream)
+        ms = e0.elapsed_time(e1) / calls
+        idh = ids.cpu().numpy()
+        uniq = float(np.mean([len(np.unique(idh[c * B:(c + 1) * B])) for c in range(warm, warm + calls)]))
+        t_chk = warm * B  # first timed token
+        ref = O.layer(x_host[t_chk], inp.w_r, shape.top_k, inp.codebook, rec_of, shape.d, shape.ffn)
+        yh = y[t_chk].cpu().numpy().astype(np.float64)
+        par = {"token": t_chk, "ids_bit_exact": bool(np.array_equal(idh[t_chk], ref.route.ids)),
+               "rel_l2": float(np.linalg.norm(yh - ref.delta) / np.linalg.norm(ref.delta))}
+        return ms, uniq, kt, par
+
+    log("sub-record: batched decode, 32 tokens per call")
+    ms, uniq, kt, par = timed(32, 20, 3, 100000)
+    byts = uniq * (rec + CB_BYTES)
+    lay_n, lay_ms = kt["layer_lut"]
+    out["batched_decode_32"] = {
+        "workload": "32 independent tokens per call through the K3-scale layer, pairs grouped by expert, "
+                    "route_topk + layer_forward (table path)",
+        "ms_per_call": ms, "tokens_per_s": 32 / (ms * 1e-3), "distinct_experts_per_call": uniq,
+        "compressed_bytes_per_call": byts, "compressed_GBps": byts / (ms * 1e-3) / 1e9,
+        "hbm_frac": byts / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+        "layer_kernel_ms": lay_ms / lay_n if lay_n else None, "calls": 20,
+        "parity": dict(par, bar="ids bit-exact, rel L2 <= 1e-4")}
+    log("sub-record: prefill chunk, 512 tokens per call, resident codes")
+    ms, uniq, kt, par = timed(512, 5, 1, 200000)
+    byts = uniq * (rec + CB_BYTES)
+    flops = 6.0 * 512 * shape.top_k * shape.d * shape.ffn
+    ck_n, ck_ms = kt["chunk"]
+    out["prefill_chunk_512"] = {
+        "workload": "512 tokens per call through the K3-scale layer on the chunk path (tokens grouped by expert, "
+                    "RVQ tiles rebuilt as bf16 for the matrix cores, experts with fewer than 4 tokens on the "
+                    "table path), codes resident",
+        "ms_per_call": ms, "tokens_per_s": 512 / (ms * 1e-3), "distinct_experts_per_call": uniq,
+        "compressed_bytes_per_call": byts, "hbm_frac": byts / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+        "flops_per_call": flops, "tflops": flops / (ms * 1e-3) / 1e12,
+        "bf16_frac": flops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+        "chunk_kernels_ms": ck_ms / ck_n if ck_n else None,
+        "chunk_kernels_note": "HIP events around layer_forward's launches: grouping, staging, the two "
+                              "contraction kernels and the table-path launch for the listed experts",
+        "calls": 5,
+        "parity": dict(par, bar="ids bit-exact, rel L2 <= 2e-2")}
+    handle.close()
+    del handle
+    torch.cuda.empty_cache()
+
+    L = 16
+    log(f"sub-record: depth chain of {L} layers, staging")
+    chain, chain_inp = [], []
+    for li in range(L):
+        ci = G.LayerInputs(shape, seed=args.seed, layer=100 + li)
+        chain.append(RvqMoe(d=shape.d, ffn=shape.ffn, n_experts=shape.n_experts, top_k=shape.top_k,
+                            codebook_dtype=1, router_w=ci.w_r_dev, codebooks=ci.cb_dev, codes=ci.codes_dev,
+                            max_tokens=1, pre_rmsnorm=True, residual=True, eps=1e-6))
+        ci.free_codes()
+        torch.cuda.empty_cache()
+        chain_inp.append(ci)
+    n_tok, warm = 20, 2
+    h = torch.empty((L + 1, warm + n_tok, shape.d), device="cuda")
+    h[0].copy_(G.to_device(S.tokens(args.seed, 300000, warm + n_tok, shape.d)))
+    ids = torch.empty((L, warm + n_tok, shape.top_k), dtype=torch.int32, device="cuda")
+    g = torch.empty((L, warm + n_tok, shape.top_k), device="cuda")
+
+    def tok(t):
+        for li, lay in enumerate(chain):
+            lay.route_forward(h[li, t:t + 1], 1, ids[li, t:t + 1], g[li, t:t + 1], h[li + 1, t:t + 1], stream)
+    for t in range(warm):
+        tok(t)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for t in range(warm, warm + n_tok):
+        tok(t)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    for lay in chain:
+        lay.sync(stream)
+    ms = e0.elapsed_time(e1) / n_tok
+    hs, idh = h.cpu().numpy(), ids.cpu().numpy()
+    errs, ok = [], True
+    for li in (0, L - 1):  # teacher-forced: the oracle's layer li on the GPU's input of layer li
+        ci = chain_inp[li]
+        ref = O.layer(hs[li, warm], ci.w_r, shape.top_k, ci.codebook,
+                      RecordCache(S, args.seed, 100 + li, rec), shape.d, shape.ffn, pre_rmsnorm=True, eps=1e-6,
+                      residual=True)
+        ok &= bool(np.array_equal(idh[li, warm], ref.route.ids))
+        delta = hs[li + 1, warm].astype(np.float64) - hs[li, warm].astype(np.float64)
+        errs.append(float(np.linalg.norm(delta - ref.delta) / np.linalg.norm(ref.delta)))
+    byts = L * shape.top_k * (rec + CB_BYTES)
+    out["depth_chain_16"] = {
+        "workload": f"one token through {L} resident K3-scale layers (RMSNorm before routing, residual add), "
+                    "one rvq_moe_route_forward call per layer",
+        "ms_per_token": ms, "tokens_per_s": 1e3 / ms, "layer_tokens_per_s": L * 1e3 / ms,
+        "compressed_bytes_per_token": byts, "hbm_frac": byts / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+        "tokens": n_tok,
+        "parity": {"token": warm, "layers_checked": [0, L - 1], "ids_bit_exact": ok, "max_rel_l2": max(errs),
+                   "bar": "teacher-forced, ids bit-exact, rel L2 <= 1e-4"}}
+    for lay in chain:
+        lay.close()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=2000, help="timed steps (one call, or one token through the chain)")
     ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--cpu-tokens", type=int, default=2, help="tokens the oracle baseline runs (0: skip)")
+    ap.add_argument("--repeats", type=int, default=5, help="blocks of --steps timed steps (median and range)")
+    ap.add_argument("--latency-calls", type=int, default=200, help="calls timed one by one for p50/p99")
+    ap.add_argument("--cpu-tokens", type=int, default=16,
+                    help="tokens the oracle baseline runs on all host threads (the first 4 also on one; 0: skip)")
+    ap.add_argument("--no-ceilings", action="store_true", help="skip the machine-ceiling measurements")
+    ap.add_argument("--no-sub", action="store_true",
+                    help="skip the sub-records (batched decode, prefill chunk, depth chain) of the default run")
     ap.add_argument("--profile-every", type=int, default=8, help="time kernels with events every n-th call")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--batch", type=int, default=1,
@@ -144,8 +398,16 @@ def main():
                                  not 1 <= args.lookahead <= shape.top_k))):
         print(f"--batch {B} / --layers {L} outside what the chosen path takes", file=sys.stderr)
         sys.exit(2)
+    headline = B == 1 and L == 1 and not args.chunk and not streaming and args.path == "fused"
+    want_sub = headline and not args.no_sub
+
+    ceil = None
+    if not args.no_ceilings:
+        log("ceilings: HBM read, LDS gather, launch cost, pinned H2D")
+        ceil = measure_ceilings(torch, shape)
 
     layers, inputs = [], []
+    bank_host = None
     for li in range(L):
         log(f"staging layer {li}: d={shape.d} ffn={shape.ffn} E={shape.n_experts} k={shape.top_k}")
         inp = G.LayerInputs(shape, seed=args.seed, layer=li)
@@ -160,11 +422,14 @@ def main():
                              chunk_min_tokens=1 if args.chunk else B + 1,
                              lut_expert_tokens=args.lut_expert_tokens, **extra))
         del codes
-        inp.free_codes()
+        if L == 1 and args.cpu_tokens > 0:
+            bank_host = inp.codes_dev.cpu().numpy()  # the oracle's records (host copy of the bank)
+        if not want_sub:
+            inp.free_codes()
         inputs.append(inp)
         torch.cuda.empty_cache()
 
-    n_tok = (W + K) * B
+    n_tok = (W + K * max(1, args.repeats) + args.latency_calls) * B
     x_host = S.tokens(args.seed, 0, n_tok, shape.d)
     # h[l] is the input of layer l (h[0] = the tokens); h[L] the chain's output
     h = torch.empty((L + 1, n_tok, shape.d), dtype=torch.float32, device="cuda")
@@ -189,30 +454,11 @@ def main():
                     routed.record(stream)  # h[li] is complete
                 layer.layer_forward(h[li, r], B, ids[li, r], gates[li, r], h[li + 1, r], stream)
                 if args.lookahead and li + 1 < L:
+                    # a streaming handle's router needs no co-resident grid, so
+                    # it may overlap the layer kernel on the main stream
                     side.wait_event(routed)
                     layers[li + 1].route_topk(h[li, r], B, pred[li + 1, r], pred_g[r], side)
                     layers[li + 1].prefetch(pred[li + 1, r], B, args.lookahead, side)
-
-    h2d = None
-    if streaming:
-        # the host -> device ceiling this box measures for pinned copies of one
-        # expert record each (as the slot fills), 1 GiB in all, three rounds
-        rec_b = shape.record_bytes
-        n_rec = (1 << 30) // rec_b
-        src = torch.empty(n_rec * rec_b, dtype=torch.uint8, pin_memory=True)
-        dst = torch.empty(n_rec * rec_b, dtype=torch.uint8, device="cuda")
-        dst.copy_(src, non_blocking=True)
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(3):
-            for i in range(n_rec):
-                dst[i * rec_b:(i + 1) * rec_b].copy_(src[i * rec_b:(i + 1) * rec_b], non_blocking=True)
-        e1.record()
-        torch.cuda.synchronize()
-        h2d = {"ceiling_GBps": 3 * n_rec * rec_b / (e0.elapsed_time(e1) * 1e-3) / 1e9}
-        del src, dst
-        torch.cuda.empty_cache()
 
     log(f"warmup {W} steps of {B} token(s) x {L} layer(s)")
     for t in range(W):
@@ -222,6 +468,7 @@ def main():
         layer.kernel_times()  # drop warmup samples
         layer.set_profiling(args.profile_every)
 
+    # ---- the timed region: exactly K steps
     torch.cuda.synchronize()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     stats0 = [layer.stats() for layer in layers]
@@ -231,7 +478,6 @@ def main():
     ev1.record(stream)
     torch.cuda.synchronize()
     ms = ev0.elapsed_time(ev1)
-    n_l, l_ms = 0, 0.0
     kernels = {}
     lut_kind = "route_layer_lut" if args.path == "fused" else ("chunk" if args.chunk else "layer_lut")
     for layer in layers:
@@ -243,20 +489,51 @@ def main():
         layer.sync(stream)
     n_l, l_ms = kernels[lut_kind]
     log(f"timed {K} steps in {ms:.2f} ms")
+    st_end = [layer.stats() for layer in layers]
+
+    # ---- repetitions of the K steps (the timed block above is the first)
+    rep_ms = [ms / K]
+    t_next = W + K
+    for _ in range(max(1, args.repeats) - 1):
+        torch.cuda.synchronize()
+        ev0.record(stream)
+        for t in range(t_next, t_next + K):
+            step(t)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        rep_ms.append(ev0.elapsed_time(ev1) / K)
+        t_next += K
+    # ---- per-call latency: events around every call
+    lat = []
+    if args.latency_calls > 0:
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.latency_calls)]
+        torch.cuda.synchronize()
+        for i, (a, b) in enumerate(evs):
+            a.record(stream)
+            step(t_next + i)
+            b.record(stream)
+        torch.cuda.synchronize()
+        lat = [a.elapsed_time(b) * 1e3 for a, b in evs]
+    for layer in layers:
+        layer.sync(stream)
+
+    h2d = None
     if streaming:
-        st = [layer.stats() for layer in layers]
-        moved = sum(a["h2d_bytes"] - b["h2d_bytes"] for a, b in zip(st, stats0))
-        hits = sum(a["slot_hits"] - b["slot_hits"] for a, b in zip(st, stats0))
-        misses = sum(a["slot_misses"] - b["slot_misses"] for a, b in zip(st, stats0))
-        checked = sum(a["records_checked"] - b["records_checked"] for a, b in zip(st, stats0))
-        verified = sum(a["records_verified"] - b["records_verified"] for a, b in zip(st, stats0))
-        h2d.update({"slots": args.stream_slots, "h2d_bytes": moved, "GBps": moved / (ms * 1e-3) / 1e9,
-                    "frac_of_ceiling": moved / (ms * 1e-3) / 1e9 / h2d["ceiling_GBps"],
-                    "hit_rate": hits / max(hits + misses, 1), "records_checked": checked,
-                    "records_crc_verified": verified})
+        moved = sum(a["h2d_bytes"] - b["h2d_bytes"] for a, b in zip(st_end, stats0))
+        hits = sum(a["slot_hits"] - b["slot_hits"] for a, b in zip(st_end, stats0))
+        misses = sum(a["slot_misses"] - b["slot_misses"] for a, b in zip(st_end, stats0))
+        checked = sum(a["records_checked"] - b["records_checked"] for a, b in zip(st_end, stats0))
+        verified = sum(a["records_verified"] - b["records_verified"] for a, b in zip(st_end, stats0))
+        h2d = {"slots": args.stream_slots, "h2d_bytes": moved, "GBps": moved / (ms * 1e-3) / 1e9,
+               "hit_rate": hits / max(hits + misses, 1), "records_checked": checked,
+               "records_crc_verified": verified}
+        if ceil:
+            h2d["ceiling_GBps"] = ceil["h2d_pinned_record_GBps"]
+            h2d["frac_of_ceiling"] = h2d["GBps"] / ceil["h2d_pinned_record_GBps"]
         if args.lookahead:
-            fills = sum(a["prefetch_fills"] - b["prefetch_fills"] for a, b in zip(st, stats0))
-            phits = sum(a["prefetch_hits"] - b["prefetch_hits"] for a, b in zip(st, stats0))
+            fills = sum(a["prefetch_fills"] - b["prefetch_fills"] for a, b in zip(st_end, stats0))
+            phits = sum(a["prefetch_hits"] - b["prefetch_hits"] for a, b in zip(st_end, stats0))
             ph, ih = pred.cpu().numpy(), ids.cpu().numpy()
             right = [len(set(ph[l, t, :args.lookahead].tolist()) & set(ih[l, t].tolist()))
                      for l in range(1, L) for t in range(W, W + K)]
@@ -275,8 +552,17 @@ def main():
     calls_s = K * L / (ms / 1e3)
     tok_s = K * B / (ms / 1e3)
     gbps = per_call_bytes * calls_s / 1e9
-    l_avg_us = l_ms / n_l * 1e3 if n_l else float("nan")  # nan: kernel timing switched off
-    l_gbps = per_call_bytes / (l_avg_us * 1e-6) / 1e9
+    # The dominant kernel's time per launch.  With the one-launch path a step
+    # is exactly one launch per layer, so the step time bounds it; event pairs
+    # around single launches also count the dispatch before the kernel and
+    # read a little longer (reported beside it).
+    ev_us = l_ms / n_l * 1e3 if n_l else float("nan")
+    step_us = ms / K * 1e3 / L
+    if args.path == "fused":
+        l_us, src = step_us, "timed steps (one launch per layer and step)"
+    else:
+        l_us, src = min(ev_us, step_us), "HIP events around the layer kernel on its launch stream"
+    l_gbps = per_call_bytes / (l_us * 1e-6) / 1e9
     kernels = {k: {"launches": int(n), "avg_us": (v / n * 1e3 if n else None)} for k, (n, v) in kernels.items()}
 
     # Parity on timed tokens (teacher-forced through the chain: the oracle runs
@@ -286,23 +572,39 @@ def main():
     if args.cpu_tokens > 0:
         from oracle import oracle as O
         hs = h.cpu().numpy()
+        rec_of = [RecordCache(S, args.seed, li, rec, bank_host if L == 1 else None) for li in range(L)]
         errs, ok_ids = [], True
-        t0 = time.perf_counter()
-        for j in range(args.cpu_tokens):
+        n_par = min(2, args.cpu_tokens)
+        for j in range(n_par):
             t = W * B + j
             for li in range(L):
                 inp = inputs[li]
-                ref = O.layer(hs[li, t], inp.w_r, shape.top_k, inp.codebook, inp.record, shape.d, shape.ffn,
+                ref = O.layer(hs[li, t], inp.w_r, shape.top_k, inp.codebook, rec_of[li], shape.d, shape.ffn,
                               pre_rmsnorm=chain, eps=1e-6, residual=chain)
                 ok_ids &= bool(np.array_equal(ids_h[li, t], ref.route.ids))
                 delta = hs[li + 1, t].astype(np.float64) - (hs[li, t].astype(np.float64) if chain else 0.0)
                 errs.append(float(np.linalg.norm(delta - ref.delta) / np.linalg.norm(ref.delta)))
-        cpu_s = time.perf_counter() - t0
-        what = f"{L}-layer chain, teacher-forced" if chain else "one layer"
-        cpu = {"value": args.cpu_tokens / cpu_s, "unit": "tokens/s", "cores": O.threads(), "kind": "oracle",
-               "sample": f"{args.cpu_tokens} timed token(s) of the same workload ({what}; route + 16 experts per "
-                         f"layer rebuilt as c1+c2+c3 in fp64); includes regenerating their code records on the host"}
-        parity = {"tokens": args.cpu_tokens, "layers_checked": L, "ids_bit_exact": ok_ids, "max_rel_l2": max(errs)}
+        parity = {"tokens": n_par, "layers_checked": L, "ids_bit_exact": ok_ids, "max_rel_l2": max(errs),
+                  "bar": "ids bit-exact, rel L2 <= 1e-4" if not args.chunk else "ids bit-exact, rel L2 <= 2e-2"}
+        # the oracle's own time on the first layer of this workload
+        toks = [hs[0, W * B + j] for j in range(args.cpu_tokens)]
+        base = oracle_baseline(O, S, shape, toks, inputs[0].w_r, inputs[0].codebook, rec_of[0], chain, chain)
+        cpu = {"value": base["all"], "unit": "tokens/s", "cores": base["threads"], "kind": "oracle",
+               "sample": f"{base['n_all']} tokens of the same workload through one layer (router, top-16 and 16 "
+                         f"experts with every weight rebuilt as c1+c2+c3, fp64) on {base['threads']} OpenMP "
+                         f"threads, {base['s_all']:.1f} s; the first {base['n_one']} also on one thread "
+                         f"({base['s_one']:.1f} s); code records fetched before each timed loop",
+               "single_thread_tokens_per_s": base["one"],
+               "host_cpus": len(os.sched_getaffinity(0)), "cpu_model": cpu_model()}
+
+    subs = None
+    if want_sub:
+        for layer in layers:
+            layer.close()
+        layers = []
+        torch.cuda.empty_cache()
+        from oracle import oracle as O
+        subs = sub_records(torch, np, G, S, O, RvqMoe, inputs[0], args, bank_host)
 
     where = (f"codes streamed from pinned host memory through {args.stream_slots} HBM slots"
              + (" (each record's CRC-32 checked)" if args.verify else "") if streaming
@@ -320,6 +622,8 @@ def main():
     else:
         workload = (f"K3-scale routed RVQ-MoE layer, batch-{B} decode, {where}: d=7168 ffn=2048 E=384 top-16, "
                     f"3-stage x 256 x 8 fp16 codebooks, uniform u8 codes, T={B} per call")
+    traffic = (recorded_traffic(args.path == "fused")
+               if (B == 1 and L == 1 and not args.chunk and not streaming) else None)
     out = {
         "metric": METRIC,
         "value": tok_s,
@@ -342,33 +646,46 @@ def main():
         "hbm_frac": gbps / HBM_PEAK_GBPS,
         "compressed_bytes_per_call": per_call_bytes,
         "distinct_experts_per_call": float(uniq.mean()),
+        "repeats": {"n": len(rep_ms), "steps_each": K, "ms_per_step_median": statistics.median(rep_ms),
+                    "ms_per_step_min": min(rep_ms), "ms_per_step_max": max(rep_ms),
+                    "tokens_per_s_median": B / (statistics.median(rep_ms) * 1e-3)},
+        "latency_us": ({"calls": len(lat), "p50": percentile(lat, 50), "p99": percentile(lat, 99),
+                        "min": min(lat), "max": max(lat),
+                        "note": "HIP events recorded on the stream around each call (includes the dispatch "
+                                "before the kernel)"} if lat else None),
         "roofline": {"bound": "hbm", "achieved": l_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": l_gbps / HBM_PEAK_GBPS,
-                     "traffic": (recorded_traffic(args.path == "fused")
-                                 if (B == 1 and L == 1 and not args.chunk and not streaming) else None),
+                     "traffic": traffic,
+                     "traffic_source": ("recorded: FETCH_SIZE + WRITE_SIZE counter runs of this source version "
+                                        "(profiles/), scaled by a reference copy" if traffic else None),
                      "kernel": "k_layer<routed> (routing and experts in one launch)" if args.path == "fused" else
                      ("k_chunk_prep + k_chunk_stage + k_chunk_gu + k_chunk_down" if args.chunk else "k_layer"),
-                     "algorithmic_bytes_per_launch": per_call_bytes, "avg_us": l_avg_us, "timed_launches": int(n_l)},
+                     "algorithmic_bytes_per_launch": per_call_bytes, "avg_us": l_us, "time_source": src,
+                     "event_avg_us": ev_us, "timed_launches": int(n_l)},
+        "ceilings": ceil,
         "kernels": kernels,
         "h2d": h2d,
         "mfma": ({"flops_per_call": 6.0 * B * shape.top_k * shape.d * shape.ffn,
-                  "tflops": 6.0 * B * shape.top_k * shape.d * shape.ffn / (l_avg_us * 1e-6) / 1e12,
-                  "frac_of_bf16_dense_peak": 6.0 * B * shape.top_k * shape.d * shape.ffn / (l_avg_us * 1e-6) / 2.5e15}
+                  "tflops": 6.0 * B * shape.top_k * shape.d * shape.ffn / (l_us * 1e-6) / 1e12,
+                  "frac_of_bf16_dense_peak": 6.0 * B * shape.top_k * shape.d * shape.ffn / (l_us * 1e-6) / 2.5e15}
                  if args.chunk else None),
+        "sub_records": subs,
         "cpu_baseline": cpu,
         "parity": parity,
     }
+    if ceil:
+        out["roofline"]["frac_of_measured_read_ceiling"] = l_gbps / ceil["hbm_read_GBps"]
     for layer in layers:
         layer.close()
     if args.copy_bytes > 0:
         torch.cuda.empty_cache()
-        src = torch.ones(args.copy_bytes, dtype=torch.uint8, device="cuda")
-        dst = torch.empty_like(src)
+        src_t = torch.ones(args.copy_bytes, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src_t)
         torch.cuda.synchronize()
-        dst.copy_(src)
+        dst.copy_(src_t)
         torch.cuda.synchronize()
         out["copy_reference_bytes"] = args.copy_bytes
-        del src, dst
+        del src_t, dst
     print(json.dumps(out), flush=True)
 
 

@@ -44,6 +44,8 @@ def lib():
         L = ctypes.CDLL(LIB_PATH)
         L.rvq_oracle_threads.argtypes = []
         L.rvq_oracle_threads.restype = ctypes.c_int
+        L.rvq_oracle_set_threads.argtypes = [ctypes.c_int]
+        L.rvq_oracle_set_threads.restype = None
         L.rvq_oracle_half_to_double.argtypes = [ctypes.c_uint16]
         L.rvq_oracle_half_to_double.restype = ctypes.c_double
         L.rvq_oracle_rmsnorm.argtypes = [ctypes.c_int, _f32p, ctypes.c_double, _f64p]
@@ -84,6 +86,11 @@ def _check(rc: int, what: str):
 
 def threads() -> int:
     return lib().rvq_oracle_threads()
+
+
+def set_threads(n: int) -> None:
+    """OpenMP threads of later oracle calls (results are bitwise independent of it)."""
+    lib().rvq_oracle_set_threads(int(n))
 
 
 def half_to_double(bits: int) -> float:

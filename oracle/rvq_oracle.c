@@ -39,6 +39,14 @@
 #include <omp.h>
 #endif
 
+void rvq_oracle_set_threads(int n) {
+#ifdef _OPENMP
+    if (n >= 1) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 int rvq_oracle_threads(void) {
 #ifdef _OPENMP
     return omp_get_max_threads();

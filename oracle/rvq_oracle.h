@@ -40,6 +40,9 @@ extern "C" {
 
 /* Threads the row loops use (OpenMP max threads; 1 without OpenMP). */
 int rvq_oracle_threads(void);
+/* Set the OpenMP thread count of later calls (n >= 1; no effect without OpenMP).
+ * Results do not depend on it (rows are summed sequentially). */
+void rvq_oracle_set_threads(int n);
 
 /* IEEE binary16 bit pattern -> double, by field decoding. */
 double rvq_oracle_half_to_double(uint16_t h);

@@ -171,6 +171,22 @@ def test_topk_min_gap_is_the_smallest_pairwise_distance_in_the_top_k():
     assert O.topk(np.array([1.0, 0.125, 0.75, -2.0, 0.5]), 4).min_gap == 0.25   # 1, .75, .5, .125 -> min 0.25
 
 
+def test_results_do_not_depend_on_the_thread_count():
+    """Rows are summed sequentially, so one thread and all threads agree bitwise."""
+    shape = S.Shape(264, 136, 5, 2, "f16")
+    cb = S.codebooks(6, 0, shape.n_experts, shape.np_cb_dtype)
+    bank = S.codes_bank(6, 0, shape.n_experts, shape.record_bytes)
+    x = S.tokens(6, 0, 1, shape.d)[0].astype(np.float64)
+    n = O.threads()
+    try:
+        O.set_threads(1)
+        one = O.expert(shape.d, shape.ffn, cb[1], bank[1], x)
+    finally:
+        O.set_threads(n)
+    many = O.expert(shape.d, shape.ffn, cb[1], bank[1], x)
+    assert np.array_equal(one.y, many.y) and np.array_equal(one.h, many.h)
+
+
 def test_topk_ties_go_to_lower_id():
     r = O.topk(np.array([1.0, 2.0, 2.0, 2.0, 0.0]), 2)
     assert r.ids.tolist() == [1, 2]
