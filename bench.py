@@ -121,14 +121,14 @@ def measure_ceilings(torch, shape):
     out = {}
     buf = torch.empty(8 << 30, dtype=torch.uint8, device="cuda")
     buf.fill_(1)
-    out["hbm_read_GBps"] = C.hbm_read_GBps(buf, 3, stream)
-    out["hbm_read_frac_of_peak"] = out["hbm_read_GBps"] / HBM_PEAK_GBPS
+    rd = C.hbm_read_GBps(buf, 3, stream)
+    out["hbm_read_GBps"] = rd["best"]
+    out["hbm_read_frac_of_peak"] = rd["best"] / HBM_PEAK_GBPS
     out["hbm_read_bytes"] = 3 * buf.numel()
+    out["hbm_read_by_kernel_shape_GBps"] = {k: v for k, v in rd.items() if k != "best"}
     del buf
     torch.cuda.empty_cache()
-    lds = C.lds_gather_rate(2000, stream)
-    out["lds_gather_lookups_per_s"] = lds["lookups_per_s"]
-    out["lds_gather_code_GBps"] = lds["code_GBps"]
+    out["lds"] = C.lds_rates(stream)
     out["persistent_launch_us"] = C.launch_gap_us(500, stream)
     rec_b = shape.record_bytes
     n_rec = (1 << 30) // rec_b

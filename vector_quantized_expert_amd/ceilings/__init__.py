@@ -34,10 +34,11 @@ def lib():
             raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build()")
         L = ctypes.CDLL(LIB_PATH)
         vp, f32p = ctypes.c_void_p, ctypes.POINTER(ctypes.c_float)
-        L.vqe_ceiling_read.argtypes = [vp, ctypes.c_uint64, ctypes.c_int, vp, f32p]
-        L.vqe_ceiling_lds_gather.argtypes = [ctypes.c_int, vp, f32p, ctypes.POINTER(ctypes.c_int)]
-        L.vqe_ceiling_launch_gap.argtypes = [ctypes.c_int, vp, f32p]
-        for n in ("vqe_ceiling_read", "vqe_ceiling_lds_gather", "vqe_ceiling_launch_gap"):
+        i32 = ctypes.c_int
+        L.vqe_ceiling_read.argtypes = [vp, ctypes.c_uint64, i32, i32, i32, vp, f32p]
+        L.vqe_ceiling_lds.argtypes = [i32, i32, vp, f32p, ctypes.POINTER(ctypes.c_int)]
+        L.vqe_ceiling_launch_gap.argtypes = [i32, vp, f32p]
+        for n in ("vqe_ceiling_read", "vqe_ceiling_lds", "vqe_ceiling_launch_gap"):
             getattr(L, n).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -48,19 +49,35 @@ def _ok(rc, what):
         raise RuntimeError(f"{what} failed (hipError {rc})")
 
 
-def hbm_read_GBps(buf, reps: int, stream) -> float:
-    """Read rate of the whole device buffer `buf` (a torch uint8 tensor), GB/s."""
-    ms = ctypes.c_float()
-    _ok(lib().vqe_ceiling_read(buf.data_ptr(), buf.numel(), reps, stream.cuda_stream, ctypes.byref(ms)), "read")
-    return buf.numel() * reps / (ms.value * 1e-3) / 1e9
+def hbm_read_GBps(buf, reps: int, stream) -> dict:
+    """Read rate of the whole device buffer `buf` (a torch uint8 tensor), GB/s,
+    for each kernel shape tried; `best` is the ceiling."""
+    out = {}
+    for name, variant, per_cu in (("256x8_4inflight", 0, 0), ("1024x1_8inflight", 1, 1), ("1024x2_8inflight", 1, 2)):
+        ms = ctypes.c_float()
+        _ok(lib().vqe_ceiling_read(buf.data_ptr(), buf.numel(), reps, variant, per_cu, stream.cuda_stream,
+                                   ctypes.byref(ms)), "read")
+        out[name] = buf.numel() * reps / (ms.value * 1e-3) / 1e9
+    out["best"] = max(out.values())
+    return out
 
 
-def lds_gather_rate(iters: int, stream) -> dict:
-    """Table-path LDS lookups per second over every CU (one lookup per code byte)."""
+def lds_rates(stream) -> dict:
+    """LDS read rates over every CU: the table path's 4-byte lookups (per second;
+    one lookup per code byte) and 16-byte streaming reads (bytes per CU per clock
+    at 2.4 GHz as well as GB/s in all)."""
+    out = {}
     ms, blocks = ctypes.c_float(), ctypes.c_int()
-    _ok(lib().vqe_ceiling_lds_gather(iters, stream.cuda_stream, ctypes.byref(ms), ctypes.byref(blocks)), "lds")
+    iters = 4000
+    _ok(lib().vqe_ceiling_lds(0, iters, stream.cuda_stream, ctypes.byref(ms), ctypes.byref(blocks)), "lds b32")
     lookups = blocks.value * 1024 * 48 * iters
-    return {"lookups_per_s": lookups / (ms.value * 1e-3), "code_GBps": lookups / (ms.value * 1e-3) / 1e9}
+    out["table_lookups_per_s"] = lookups / (ms.value * 1e-3)
+    out["table_lookup_bytes_per_clk_per_cu"] = 4 * lookups / (ms.value * 1e-3) / blocks.value / 2.4e9
+    _ok(lib().vqe_ceiling_lds(1, iters, stream.cuda_stream, ctypes.byref(ms), ctypes.byref(blocks)), "lds b128")
+    byts = blocks.value * 1024 * 8 * 16 * iters
+    out["b128_GBps"] = byts / (ms.value * 1e-3) / 1e9
+    out["b128_bytes_per_clk_per_cu"] = byts / (ms.value * 1e-3) / blocks.value / 2.4e9
+    return out
 
 
 def launch_gap_us(launches: int, stream) -> float:

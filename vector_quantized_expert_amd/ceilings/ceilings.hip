@@ -5,10 +5,11 @@
 //    non-temporal loads, four in flight per thread, XOR-folded so that the
 //    loads cannot be dropped; the achievable read rate that the table path's
 //    code streaming is compared with.
-//  - LDS random gather: the table path's inner operation -- a 4-byte read from
-//    a 128 KB table at an address formed from a random code byte, lane l of
-//    each half-wave always in bank l -- issued back to back by 16 waves per
-//    CU; reported as lookups per second (one lookup per code byte).
+//  - LDS reads: the table path's inner operation -- 4-byte reads from a
+//    128 KB table, lane l of each half-wave always in bank l, at per-lane
+//    random rows -- issued back to back by 16 waves per CU (lookups per
+//    second, one lookup per code byte); and 16-byte streaming reads (bytes per
+//    second per CU), the chunk path's codebook and operand reads.
 //  - Kernel-to-kernel gap: a chain of launches on one stream of a grid shaped
 //    like the persistent layer kernel (one 1024-thread workgroup per CU with
 //    most of the LDS), each doing nothing; the time per launch is the fixed
@@ -36,30 +37,68 @@ __global__ __launch_bounds__(256) void k_read(const u32x4 *__restrict__ p, uint6
     if (acc == 0x9E3779B9u) out[blockIdx.x] = acc;  // practically never: keeps the loads live
 }
 
-// 1024 threads; the table is 32768 words of LDS.  Each iteration every lane
-// makes 48 lookups (one 32-row chunk's worth) at word c * 64 + 32 * (s == 1)
-// + 16384 * (s == 2) + l for pseudo-random codes c.
-__global__ __launch_bounds__(1024) void k_lds_gather(int iters, float *__restrict__ out) {
-    __shared__ float lut[32768];
-    for (int i = threadIdx.x; i < 32768; i += 1024) lut[i] = (float)(i & 255);
+// 1024 threads; the table is 32768 words of LDS, laid out like the table
+// path's (word c * 64 + l for lane l of a half-wave: every lane in its own
+// bank).  Each lane starts at a pseudo-random row and reads 48 rows of its
+// bank column per iteration (immediate offsets, so the address arithmetic
+// costs nothing inside the loop); the words are summed three at a time.
+__global__ __launch_bounds__(1024) void k_lds_gather(int iters, uint32_t *__restrict__ out) {
+    __shared__ uint32_t lut[32768];
+    for (int i = threadIdx.x; i < 32768; i += 1024) lut[i] = (uint32_t)i * 2654435761u;
     __syncthreads();
     const int l = threadIdx.x & 31;
-    uint32_t h = 0x9E3779B9u * (threadIdx.x + 1) + blockIdx.x;
-    float acc = 0.f;
+    const uint32_t row = ((threadIdx.x * 2654435761u) >> 8) % 400u;  // rows row .. row + 47 < 512
+    const uint32_t *base = lut + row * 64 + l;
+    uint32_t acc = 0;
     for (int it = 0; it < iters; it++) {
-        float t[48];
+        const uint32_t *b = base + ((it & 1) << 5);  // the other half of each row every other iteration
 #pragma unroll
-        for (int q = 0; q < 16; q++) {
-            h = h * 1664525u + 1013904223u;
-            const uint32_t c0 = h >> 24, c1 = (h >> 16) & 255, c2 = (h >> 8) & 255;
-            t[3 * q] = lut[c0 * 64 + l];
-            t[3 * q + 1] = lut[c1 * 64 + 32 + l];
-            t[3 * q + 2] = lut[16384 + c2 * 64 + l];
-        }
-#pragma unroll
-        for (int q = 0; q < 48; q++) acc += t[q];
+        for (int q = 0; q < 48; q += 2) acc = acc + b[q * 64] + b[(q + 1) * 64];
     }
-    if (acc == -1.f) out[blockIdx.x] = acc;
+    if (acc == 0x12345678u) out[blockIdx.x] = acc;
+}
+
+// LDS streaming read bandwidth with 16-byte reads: each wave reads 1 KB
+// contiguous per instruction, conflict free.
+typedef unsigned int u32x4b __attribute__((ext_vector_type(4)));
+__global__ __launch_bounds__(1024) void k_lds_b128(int iters, uint32_t *__restrict__ out) {
+    __shared__ u32x4b buf[8192];  // 128 KB
+    for (int i = threadIdx.x; i < 8192; i += 1024) buf[i] = u32x4b{(uint32_t)i, (uint32_t)i * 3u, 1u, 2u};
+    __syncthreads();
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    // entries wave * 64 + lane + 256 (it & 1) + q * 512 (q < 8): at most
+    // 1023 + 256 + 3584 < 8192, immediate offsets of at most 56 KB; the base
+    // moves with the data read so that no read can be hoisted
+    uint32_t acc = 0;
+    for (int it = 0; it < iters; it++) {
+        const u32x4b *b = buf + wave * 64 + lane + ((acc & 1) << 8);  // depends on the last reads
+#pragma unroll
+        for (int q = 0; q < 8; q++) {
+            const u32x4b v = b[q * 512];
+            acc = acc + v.x + v.y;
+            acc = acc + v.z + v.w;
+        }
+    }
+    if (acc == 0x12345678u) out[blockIdx.x] = acc;
+}
+
+// HBM read, 1024 threads per workgroup, eight 16-byte loads in flight per thread.
+__global__ __launch_bounds__(1024) void k_read8(const u32x4 *__restrict__ p, uint64_t n16, uint32_t *__restrict__ out) {
+    const uint64_t stride = (uint64_t)gridDim.x * 1024;
+    uint64_t i = (uint64_t)blockIdx.x * 1024 + threadIdx.x;
+    uint32_t acc = 0;
+    for (; i + 7 * stride < n16; i += 8 * stride) {
+        u32x4 v[8];
+#pragma unroll
+        for (int q = 0; q < 8; q++) v[q] = __builtin_nontemporal_load(p + i + q * stride);
+#pragma unroll
+        for (int q = 0; q < 8; q++) acc ^= v[q].x ^ v[q].y ^ v[q].z ^ v[q].w;
+    }
+    for (; i < n16; i += stride) {
+        const u32x4 a = __builtin_nontemporal_load(p + i);
+        acc ^= a.x ^ a.y ^ a.z ^ a.w;
+    }
+    if (acc == 0x9E3779B9u) out[blockIdx.x] = acc;
 }
 
 __global__ __launch_bounds__(1024) void k_empty(int *__restrict__ out) {
@@ -70,12 +109,14 @@ __global__ __launch_bounds__(1024) void k_empty(int *__restrict__ out) {
 extern "C" {
 
 // Each returns 0 or a hipError_t; *ms gets the elapsed time of the timed part.
-int vqe_ceiling_read(const void *buf, uint64_t bytes, int reps, void *stream, float *ms) {
+// variant 0: 256-thread workgroups, 8 per CU, 4 loads in flight per thread;
+// variant 1: 1024-thread workgroups, `per_cu` per CU, 8 loads in flight per thread.
+int vqe_ceiling_read(const void *buf, uint64_t bytes, int reps, int variant, int per_cu, void *stream, float *ms) {
     hipStream_t s = static_cast<hipStream_t>(stream);
     int n_cu = 0, dev = 0;
     hipGetDevice(&dev);
     hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
-    const int blocks = n_cu * 8;
+    const int blocks = variant == 0 ? n_cu * 8 : n_cu * per_cu;
     uint32_t *out = nullptr;
     hipError_t e = hipMalloc(&out, sizeof(uint32_t) * blocks);
     if (e != hipSuccess) return (int)e;
@@ -83,10 +124,16 @@ int vqe_ceiling_read(const void *buf, uint64_t bytes, int reps, void *stream, fl
     hipEventCreate(&a);
     hipEventCreate(&b);
     const uint64_t n16 = bytes / 16;
-    hipLaunchKernelGGL(k_read, dim3(blocks), dim3(256), 0, s, static_cast<const u32x4 *>(buf), n16, out);  // warm
+    const u32x4 *p = static_cast<const u32x4 *>(buf);
+    auto launch = [&]() {
+        if (variant == 0)
+            hipLaunchKernelGGL(k_read, dim3(blocks), dim3(256), 0, s, p, n16, out);
+        else
+            hipLaunchKernelGGL(k_read8, dim3(blocks), dim3(1024), 0, s, p, n16, out);
+    };
+    launch();  // warm
     hipEventRecord(a, s);
-    for (int r = 0; r < reps; r++)
-        hipLaunchKernelGGL(k_read, dim3(blocks), dim3(256), 0, s, static_cast<const u32x4 *>(buf), n16, out);
+    for (int r = 0; r < reps; r++) launch();
     hipEventRecord(b, s);
     e = hipEventSynchronize(b);
     if (e == hipSuccess) e = hipEventElapsedTime(ms, a, b);
@@ -96,20 +143,27 @@ int vqe_ceiling_read(const void *buf, uint64_t bytes, int reps, void *stream, fl
     return (int)e;
 }
 
-int vqe_ceiling_lds_gather(int iters, void *stream, float *ms, int *blocks_out) {
+// kind 0: the table path's 4-byte lookups; kind 1: 16-byte streaming reads.
+int vqe_ceiling_lds(int kind, int iters, void *stream, float *ms, int *blocks_out) {
     hipStream_t s = static_cast<hipStream_t>(stream);
     int n_cu = 0, dev = 0;
     hipGetDevice(&dev);
     hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
-    float *out = nullptr;
-    hipError_t e = hipMalloc(&out, sizeof(float) * n_cu);
+    uint32_t *out = nullptr;
+    hipError_t e = hipMalloc(&out, sizeof(uint32_t) * n_cu);
     if (e != hipSuccess) return (int)e;
     hipEvent_t a, b;
     hipEventCreate(&a);
     hipEventCreate(&b);
-    hipLaunchKernelGGL(k_lds_gather, dim3(n_cu), dim3(1024), 0, s, 8, out);
+    auto launch = [&](int it) {
+        if (kind == 0)
+            hipLaunchKernelGGL(k_lds_gather, dim3(n_cu), dim3(1024), 0, s, it, out);
+        else
+            hipLaunchKernelGGL(k_lds_b128, dim3(n_cu), dim3(1024), 0, s, it, out);
+    };
+    launch(8);
     hipEventRecord(a, s);
-    hipLaunchKernelGGL(k_lds_gather, dim3(n_cu), dim3(1024), 0, s, iters, out);
+    launch(iters);
     hipEventRecord(b, s);
     e = hipEventSynchronize(b);
     if (e == hipSuccess) e = hipEventElapsedTime(ms, a, b);

@@ -42,7 +42,6 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kCkThreads = 256;
-constexpr int kCkMt = 2;                      // 32-token tiles per pass
 constexpr int kXRow = kTileSlices * kVec + 8;  // bf16 per staged token row (padded: 264)
 
 // ---------------------------------------------------------------------------
@@ -258,42 +257,40 @@ __device__ inline bf16x8 ck_weights(const uint8_t *blk, const char *cb, int kk, 
     return w;
 }
 
-// Stage the token tiles of a pass: rows [p0, p0 + 32 * nmt) of the permuted
-// bf16 matrix src [P][ld], columns [c0, c0 + 256), into LDS rows of kXRow;
-// rows at or past p_end and columns at or past n_cols are zero.  Every
-// thread issues all its 16-byte loads before storing any, so the tile costs
-// one round trip.
-__device__ inline void ck_stage_rows(__bf16 *dst, const __bf16 *src, int ld, int p0, int p_end, int c0, int n_cols,
-                              int nmt) {
-    constexpr int kPer = 32 * kCkMt * 32 / kCkThreads;  // 16-byte pieces per thread (32 per row)
+// The token rows of a pass, one 256-wide input tile at a time: rows [p0, p0
+// + 32 * NT) of the permuted bf16 matrix src [P][ld], columns [c0, c0 + 256),
+// loaded into registers (all of a thread's 16-byte loads in flight together)
+// and later stored into LDS rows of kXRow; rows at or past p_end and columns
+// at or past n_cols are zero.  Split so that the next tile's rows are in
+// flight while the current tile is contracted.
+template <int NT>
+struct CkRows {
+    static constexpr int kPer = 32 * NT * 32 / kCkThreads;  // 16-byte pieces per thread (32 per row)
     typedef unsigned int w4 __attribute__((ext_vector_type(4)));
     w4 v[kPer];
+};
+
+template <int NT>
+__device__ inline void ck_load_rows(CkRows<NT> &r, const __bf16 *src, int ld, int p0, int p_end, int c0, int n_cols) {
+    using R = CkRows<NT>;
 #pragma unroll
-    for (int i = 0; i < kPer; i++) {
+    for (int i = 0; i < R::kPer; i++) {
         const int u = threadIdx.x + i * kCkThreads, row = u >> 5, piece = u & 31;
         const int p = p0 + row, col = c0 + piece * 8;
-        v[i] = w4{0u, 0u, 0u, 0u};
-        if (row < 32 * nmt && p < p_end && col + 8 <= n_cols)
-            v[i] = *global_view(reinterpret_cast<const w4 *>(src + (size_t)p * ld + col));
+        r.v[i] = typename R::w4{0u, 0u, 0u, 0u};
+        // d and ffn are multiples of 8, so a piece lies wholly inside or outside the row
+        if (p < p_end && col + 8 <= n_cols)
+            r.v[i] = *global_view(reinterpret_cast<const typename R::w4 *>(src + (size_t)p * ld + col));
     }
-    if (c0 + kTileSlices * kVec > n_cols) {  // ragged last tile: the piece that straddles n_cols
+}
+
+template <int NT>
+__device__ inline void ck_store_rows(__bf16 *dst, const CkRows<NT> &r) {
+    using R = CkRows<NT>;
 #pragma unroll
-        for (int i = 0; i < kPer; i++) {
-            const int u = threadIdx.x + i * kCkThreads, row = u >> 5, piece = u & 31;
-            const int p = p0 + row, col = c0 + piece * 8;
-            if (row < 32 * nmt && p < p_end && col < n_cols && col + 8 > n_cols) {
-                __bf16 tmp[8];
-                const __bf16 *s = src + (size_t)p * ld + col;
-#pragma unroll
-                for (int e = 0; e < 8; e++) tmp[e] = col + e < n_cols ? s[e] : (__bf16)0.f;
-                v[i] = *reinterpret_cast<const w4 *>(tmp);
-            }
-        }
-    }
-#pragma unroll
-    for (int i = 0; i < kPer; i++) {
+    for (int i = 0; i < R::kPer; i++) {
         const int u = threadIdx.x + i * kCkThreads, row = u >> 5, piece = u & 31;
-        if (row < 32 * nmt) *reinterpret_cast<w4 *>(dst + row * kXRow + piece * 8) = v[i];
+        *reinterpret_cast<typename R::w4 *>(dst + row * kXRow + piece * 8) = r.v[i];
     }
 }
 
@@ -331,82 +328,108 @@ struct ChunkArgs {
     Geometry g;
 };
 
+// One pass of a contraction kernel: NT token tiles (32 tokens each) against
+// this wave's 32-row chunk of one matrix, over all input tiles.  Per tile:
+// a barrier (the last tile's LDS reads are done), the tile's token rows and
+// this wave's code block go from registers into LDS, the next tile's rows and
+// codes are loaded into registers (in flight during the contraction), a
+// barrier, then 16 K-steps.  LDS: xs [32 * NT][kXRow], code_blk [3072].
+template <int CB, int NT>
+__device__ inline void ck_contract(f32x16c (&acc)[NT], const __bf16 *src, int ld, int n_cols, int p0, int g1,
+                                   const uint8_t *mat, const MatGeom &mg, int chunk, bool chunk_ok, const char *cb,
+                                   __bf16 *xs, uint8_t *code_blk, int lane) {
+#pragma unroll
+    for (int mt = 0; mt < NT; mt++)
+#pragma unroll
+        for (int v = 0; v < 16; v++) acc[mt][v] = 0.f;
+    ck_w4 cr[3];
+    CkRows<NT> xr;
+    ck_load_codes(cr, mat + (int64_t)chunk * kChunkBytes, chunk_ok, lane);
+    ck_load_rows<NT>(xr, src, ld, p0, g1, 0, n_cols);
+    for (int kt = 0; kt < mg.n_tiles; kt++) {
+        __syncthreads();  // the previous tile's LDS reads are done
+        ck_store_rows<NT>(xs, xr);
+        ck_store_codes(code_blk, cr, lane);
+        if (kt + 1 < mg.n_tiles) {
+            ck_load_codes(cr, mat + ((int64_t)(kt + 1) * mg.n_chunks + chunk) * kChunkBytes, chunk_ok, lane);
+            ck_load_rows<NT>(xr, src, ld, p0, g1, (kt + 1) * kTileSlices * kVec, n_cols);
+        }
+        __syncthreads();
+#pragma unroll 2
+        for (int kk = 0; kk < kTileSlices / 2; kk++) {
+            const bf16x8 w = ck_weights<CB>(code_blk, cb, kk, lane);
+#pragma unroll
+            for (int mt = 0; mt < NT; mt++)
+                acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ck_tokens(xs, mt, kk, lane), w, acc[mt], 0, 0, 0);
+        }
+    }
+}
+
+// Experts are split by tokens between two instances of each kernel: NMT = 1
+// (LDS for one 32-token tile: more workgroups resident per CU) takes experts
+// with at most 32 tokens in one pass, NMT = 2 takes the others in passes of
+// 64 (a last pass of at most 32 tokens contracts one tile).
+template <int NMT>
+__device__ inline bool ck_mine(int n_tok) {
+    return NMT == 1 ? n_tok <= 32 : n_tok > 32;
+}
+
 // ---------------------------------------------------------------------------
 // gate/up: grid (ceil(ffn / 64), E), 256 threads.  Workgroup (nb, a) takes
 // active expert act[a] and output rows nb * 64 .. + 64 of gate and of up:
 // wave w = (matrix w / 2, chunk 2 nb + w % 2).
-template <int CB>
+template <int CB, int NMT>
 __global__ __launch_bounds__(kCkThreads) void k_chunk_gu(ChunkArgs A) {
     const Geometry &g = A.g;
     const int a = A.a0 + blockIdx.y;
     if (a >= A.a1 || a >= A.act[g.E]) return;
     const int e = A.act[a];
     const int g0 = A.grp_off[e], g1 = A.grp_off[e + 1];
+    if (!ck_mine<NMT>(g1 - g0)) return;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int m = wave >> 1, chunk = 2 * blockIdx.x + (wave & 1);
     const MatGeom &mg = g.m[m];
     const bool chunk_ok = chunk < mg.n_chunks;
     __shared__ __align__(16) char cb_lds[2][CkCb<CB>::kBytes];
     __shared__ __align__(16) uint8_t code_lds[4][kChunkBytes];
-    __shared__ __align__(16) __bf16 xs[32 * kCkMt * kXRow];
+    __shared__ __align__(16) __bf16 xs[32 * NMT * kXRow];
     ck_stage_cb<CB>(cb_lds[0], A.cbs, e, 0);
     ck_stage_cb<CB>(cb_lds[1], A.cbs, e, 1);
     const uint8_t *mat = (A.slot_tab ? A.slot_tab[e] : A.codes + (int64_t)e * g.rec_int) + mg.off;
-    // one pass per 32 * kCkMt tokens of the group; a pass with at most 32 left
-    // runs the single-tile instance (no contraction of empty token rows)
-    auto pass = [&](int p0, auto nmt_c) {
-        constexpr int nmt = decltype(nmt_c)::value;
-        f32x16c acc[nmt];
-#pragma unroll
-        for (int mt = 0; mt < nmt; mt++)
-#pragma unroll
-            for (int v = 0; v < 16; v++) acc[mt][v] = 0.f;
-        ck_w4 cr[3];
-        ck_load_codes(cr, mat + (int64_t)chunk * kChunkBytes, chunk_ok, lane);
-        for (int kt = 0; kt < mg.n_tiles; kt++) {
-            __syncthreads();  // previous tile's LDS reads are done
-            ck_stage_rows(xs, A.X, g.d, p0, g1, kt * kTileSlices * kVec, g.d, nmt);
-            ck_store_codes(code_lds[wave], cr, lane);
-            if (kt + 1 < mg.n_tiles)
-                ck_load_codes(cr, mat + ((int64_t)(kt + 1) * mg.n_chunks + chunk) * kChunkBytes, chunk_ok, lane);
-            __syncthreads();
-#pragma unroll 2
-            for (int kk = 0; kk < kTileSlices / 2; kk++) {
-                const bf16x8 w = ck_weights<CB>(code_lds[wave], cb_lds[m], kk, lane);
-#pragma unroll
-                for (int mt = 0; mt < nmt; mt++)
-                    acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ck_tokens(xs, mt, kk, lane), w, acc[mt], 0, 0,
-                                                                      0);
-            }
-        }
+    auto pass = [&](int p0, auto nt_c) {
+        constexpr int NT = decltype(nt_c)::value;
+        f32x16c acc[NT];
+        ck_contract<CB, NT>(acc, A.X, g.d, g.d, p0, g1, mat, mg, chunk, chunk_ok, cb_lds[m], xs, code_lds[wave],
+                            lane);
         // h = silu(gate) * up: the up waves hand their tiles to the gate waves
         __syncthreads();
-        float *ex = reinterpret_cast<float *>(xs);  // [2 chunks][kCkMt][16][64]
+        float *ex = reinterpret_cast<float *>(xs);  // [2 chunks][NT][16][64]
+        static_assert(2 * NT * 16 * 64 * sizeof(float) <= sizeof(xs), "exchange fits the token tile");
         if (m == 1)
 #pragma unroll
-            for (int mt = 0; mt < nmt; mt++)
+            for (int mt = 0; mt < NT; mt++)
 #pragma unroll
-                for (int v = 0; v < 16; v++) ex[(((wave & 1) * kCkMt + mt) * 16 + v) * 64 + lane] = acc[mt][v];
+                for (int v = 0; v < 16; v++) ex[(((wave & 1) * NT + mt) * 16 + v) * 64 + lane] = acc[mt][v];
         __syncthreads();
         if (m == 0 && chunk_ok) {
             const int row = chunk * kChunkRows + (lane & 31);
 #pragma unroll
-            for (int mt = 0; mt < nmt; mt++) {
+            for (int mt = 0; mt < NT; mt++) {
 #pragma unroll
                 for (int v = 0; v < 16; v++) {
                     const int p = p0 + mt * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-                    const float ga = acc[mt][v], up = ex[(((wave & 1) * kCkMt + mt) * 16 + v) * 64 + lane];
+                    const float ga = acc[mt][v], up = ex[(((wave & 1) * NT + mt) * 16 + v) * 64 + lane];
                     const float h = ga / (1.f + expf(-ga)) * up;
                     if (p < g1 && row < g.ffn) A.H[(size_t)p * g.ffn + row] = (__bf16)h;
                 }
             }
         }
     };
-    for (int p0 = g0; p0 < g1; p0 += 32 * kCkMt) {
-        if (g1 - p0 <= 32)
+    for (int p0 = g0; p0 < g1; p0 += 32 * NMT) {
+        if (NMT == 1 || g1 - p0 <= 32)
             pass(p0, std::integral_constant<int, 1>{});
         else
-            pass(p0, std::integral_constant<int, kCkMt>{});
+            pass(p0, std::integral_constant<int, NMT>{});
     }
 }
 
@@ -414,52 +437,33 @@ __global__ __launch_bounds__(kCkThreads) void k_chunk_gu(ChunkArgs A) {
 // down: grid (ceil(d / 128), E), 256 threads.  Workgroup (nb, a) takes active
 // expert act[a] and output rows nb * 128 .. + 128 (wave w: chunk 4 nb + w);
 // y[t][row] += gate * (h W_d^T)[pos][row] with fp32 atomics.
-template <int CB>
+template <int CB, int NMT>
 __global__ __launch_bounds__(kCkThreads) void k_chunk_down(ChunkArgs A) {
     const Geometry &g = A.g;
     const int a = A.a0 + blockIdx.y;
     if (a >= A.a1 || a >= A.act[g.E]) return;
     const int e = A.act[a];
     const int g0 = A.grp_off[e], g1 = A.grp_off[e + 1];
+    if (!ck_mine<NMT>(g1 - g0)) return;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const MatGeom &mg = g.m[2];
     const int chunk = 4 * blockIdx.x + wave;
     const bool chunk_ok = chunk < mg.n_chunks;
     __shared__ __align__(16) char cb_lds[CkCb<CB>::kBytes];
     __shared__ __align__(16) uint8_t code_lds[4][kChunkBytes];
-    __shared__ __align__(16) __bf16 hs[32 * kCkMt * kXRow];
+    __shared__ __align__(16) __bf16 hs[32 * NMT * kXRow];
     ck_stage_cb<CB>(cb_lds, A.cbs, e, 2);
     const uint8_t *mat = (A.slot_tab ? A.slot_tab[e] : A.codes + (int64_t)e * g.rec_int) + mg.off;
     const int k = g.k;
-    auto pass = [&](int p0, auto nmt_c) {
-        constexpr int nmt = decltype(nmt_c)::value;
-        f32x16c acc[nmt];
-#pragma unroll
-        for (int mt = 0; mt < nmt; mt++)
-#pragma unroll
-            for (int v = 0; v < 16; v++) acc[mt][v] = 0.f;
-        ck_w4 cr[3];
-        ck_load_codes(cr, mat + (int64_t)chunk * kChunkBytes, chunk_ok, lane);
-        for (int kt = 0; kt < mg.n_tiles; kt++) {
-            __syncthreads();
-            ck_stage_rows(hs, A.H, g.ffn, p0, g1, kt * kTileSlices * kVec, g.ffn, nmt);
-            ck_store_codes(code_lds[wave], cr, lane);
-            if (kt + 1 < mg.n_tiles)
-                ck_load_codes(cr, mat + ((int64_t)(kt + 1) * mg.n_chunks + chunk) * kChunkBytes, chunk_ok, lane);
-            __syncthreads();
-#pragma unroll 2
-            for (int kk = 0; kk < kTileSlices / 2; kk++) {
-                const bf16x8 w = ck_weights<CB>(code_lds[wave], cb_lds, kk, lane);
-#pragma unroll
-                for (int mt = 0; mt < nmt; mt++)
-                    acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ck_tokens(hs, mt, kk, lane), w, acc[mt], 0, 0,
-                                                                      0);
-            }
-        }
+    auto pass = [&](int p0, auto nt_c) {
+        constexpr int NT = decltype(nt_c)::value;
+        f32x16c acc[NT];
+        ck_contract<CB, NT>(acc, A.H, g.ffn, g.ffn, p0, g1, mat, mg, chunk, chunk_ok, cb_lds, hs, code_lds[wave],
+                            lane);
         if (chunk_ok) {
             const int row = chunk * kChunkRows + (lane & 31);
 #pragma unroll
-            for (int mt = 0; mt < nmt; mt++) {
+            for (int mt = 0; mt < NT; mt++) {
 #pragma unroll
                 for (int v = 0; v < 16; v++) {
                     const int p = p0 + mt * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
@@ -471,11 +475,11 @@ __global__ __launch_bounds__(kCkThreads) void k_chunk_down(ChunkArgs A) {
             }
         }
     };
-    for (int p0 = g0; p0 < g1; p0 += 32 * kCkMt) {
-        if (g1 - p0 <= 32)
+    for (int p0 = g0; p0 < g1; p0 += 32 * NMT) {
+        if (NMT == 1 || g1 - p0 <= 32)
             pass(p0, std::integral_constant<int, 1>{});
         else
-            pass(p0, std::integral_constant<int, kCkMt>{});
+            pass(p0, std::integral_constant<int, NMT>{});
     }
 }
 
@@ -498,12 +502,17 @@ hipError_t launch_chunk_experts(const Geometry &g, const ChunkWork &cw, const ui
     if (a1 <= a0) return hipSuccess;
     ChunkArgs A{codes, slot_tab, a0, a1, cbs, cw.grp_off, cw.act, cw.perm, cw.X, cw.H, gates, y, g};
     const dim3 ggu((g.m[0].n_chunks + 1) / 2, a1 - a0), gdn((g.m[2].n_chunks + 3) / 4, a1 - a0);
+    // each kernel pair takes the experts of its token class and skips the others
     if (g.cb_dtype == 0) {
-        hipLaunchKernelGGL(k_chunk_gu<0>, ggu, dim3(kCkThreads), 0, s, A);
-        hipLaunchKernelGGL(k_chunk_down<0>, gdn, dim3(kCkThreads), 0, s, A);
+        hipLaunchKernelGGL((k_chunk_gu<0, 1>), ggu, dim3(kCkThreads), 0, s, A);
+        hipLaunchKernelGGL((k_chunk_gu<0, 2>), ggu, dim3(kCkThreads), 0, s, A);
+        hipLaunchKernelGGL((k_chunk_down<0, 1>), gdn, dim3(kCkThreads), 0, s, A);
+        hipLaunchKernelGGL((k_chunk_down<0, 2>), gdn, dim3(kCkThreads), 0, s, A);
     } else {
-        hipLaunchKernelGGL(k_chunk_gu<1>, ggu, dim3(kCkThreads), 0, s, A);
-        hipLaunchKernelGGL(k_chunk_down<1>, gdn, dim3(kCkThreads), 0, s, A);
+        hipLaunchKernelGGL((k_chunk_gu<1, 1>), ggu, dim3(kCkThreads), 0, s, A);
+        hipLaunchKernelGGL((k_chunk_gu<1, 2>), ggu, dim3(kCkThreads), 0, s, A);
+        hipLaunchKernelGGL((k_chunk_down<1, 1>), gdn, dim3(kCkThreads), 0, s, A);
+        hipLaunchKernelGGL((k_chunk_down<1, 2>), gdn, dim3(kCkThreads), 0, s, A);
     }
     return hipGetLastError();
 }
