@@ -64,7 +64,7 @@
 extern "C" {
 #endif
 
-#define RVQ_MOE_ABI_VERSION 5
+#define RVQ_MOE_ABI_VERSION 6
 
 typedef enum rvq_moe_status {
     RVQ_MOE_OK = 0,
@@ -196,7 +196,24 @@ typedef struct rvq_moe_record_trailer {
  *   verify_records  streaming handles: nonzero = also check the CRC-32 of
  *                every record copied into a slot (see rvq_moe_record_trailer);
  *                the trailer checks always run.  Ignored for DEVICE codes.
- *   reserved     must be 0.
+ *   deterministic  0 or 1.  1: every output is a fixed-order sum, so repeated
+ *                calls, streaming and resident codes, grouped and per-token
+ *                calls and prefetching on or off all give bitwise identical
+ *                y (the same tokens, ids and gates in, the same bits out).
+ *                [FR] "Lecture anticipée et prédiction du routeur": reading
+ *                ahead and overlapping leave the output exactly as it was.
+ *                Each (token, expert) pair's output rows (per down-projection
+ *                tile on the table path) go to a workspace buffer and a small
+ *                kernel adds them to y in the order (expert rank, tile), after
+ *                x when `residual`; gate/up partial sums are never merged
+ *                across tiles; adaptive dispatch is off (lut_expert_tokens is
+ *                taken as 1).  0 (the default): the layer kernels add into y
+ *                with fp32 atomics, whose order varies, so outputs agree to
+ *                ~1e-7 relative between runs; no extra launch and no buffer.
+ *                Cost of 1 on one MI355X at d=7168, ffn=2048, E=384, top-16:
+ *                +7 us per one-token routed call (+12 %), +4 % for 32-token
+ *                calls, +2 % for 512-token chunk-path calls; workspace
+ *                max_tokens * top_k * ceil(ffn / 256) * ceil(d / 32) * 128 bytes.
  *   stream       stream used for the upload and repack inside open.
  */
 typedef struct rvq_moe_desc {
@@ -217,7 +234,7 @@ typedef struct rvq_moe_desc {
     int32_t chunk_min_tokens;
     int32_t lut_expert_tokens;
     int32_t verify_records;
-    int32_t reserved;
+    int32_t deterministic;
     double eps;
     const float *router_w;
     const void *codebooks;
@@ -316,7 +333,9 @@ int rvq_moe_layer_forward(rvq_moe *h, const float *x, int32_t n_tokens, const in
  *   Needs 2 * (n_tokens * top_k + 1) * 256 bytes of counters (rounded up to
  *   256) plus n_tokens * top_k * 2 * ceil(d / 256) * ceil(ffn / 32) * 128
  *   bytes of partial sums within the 32 MiB (d=7168, ffn=2048, top-16: up to
- *   4 tokens per call).
+ *   4 tokens per call), and with `deterministic` also n_tokens * top_k *
+ *   ceil(ffn / 256) * ceil(d / 32) * 128 bytes of output rows (up to 2 tokens
+ *   per call at that shape).
  * Errors: EINVAL (as layer_forward; or a call that needs more scratch than the
  * array holds), ENOTSUP (streaming codes), EHIP.
  */

@@ -14,7 +14,7 @@ def test_library_exports_every_header_symbol():
     L = R.lib()
     for n in names:
         assert hasattr(L, n), n
-    assert L.rvq_moe_abi_version() == 5
+    assert L.rvq_moe_abi_version() == 6
 
 
 def _desc(**over):
@@ -45,7 +45,7 @@ def _desc(**over):
     (dict(codes_location=5), R.EINVAL),
     (dict(codes_location=2), R.EINVAL),  # a bank needs slots too
     (dict(codes_location=2, cache_slots=4), R.EINVAL),  # not pinned host memory
-    (dict(reserved=1), R.EINVAL),
+    (dict(deterministic=2), R.EINVAL),
     (dict(chunk_min_tokens=-1), R.EINVAL),
     (dict(eps=-1.0), R.EINVAL),
 ])

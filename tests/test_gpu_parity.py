@@ -49,6 +49,21 @@ def _run(torch, layer, shape, x, per_token=False):
     return ids.cpu().numpy(), gates.cpu().numpy(), y.cpu().numpy()
 
 
+def _forward(torch, layer, shape, x, ids, gates, per_token=False):
+    """layer_forward on given ids and gates (host arrays): one call, or one token per call."""
+    from synth import gpu as G
+    T = x.shape[0]
+    xd, idd, gd = G.to_device(x), G.to_device(ids), G.to_device(gates)
+    y = torch.empty((T, shape.d), dtype=torch.float32, device="cuda")
+    if per_token:
+        for t in range(T):
+            layer.layer_forward(xd[t:t + 1], 1, idd[t:t + 1], gd[t:t + 1], y[t:t + 1])
+    else:
+        layer.layer_forward(xd, T, idd, gd, y)
+    layer.sync()
+    return y.cpu().numpy()
+
+
 def _check(inp, shape, x, ids, gates, y, pre_rmsnorm=False, residual=False, tokens=None):
     worst = 0.0
     for t in (range(x.shape[0]) if tokens is None else tokens):
@@ -798,29 +813,41 @@ def _table_runs(ids, S):
     return runs
 
 
-def test_streaming_table_path_matches_resident_and_counts_lru(torch_mod, tiny):
+def _same_outputs(a, b, det):
+    """Deterministic handles: bitwise equal outputs.  Otherwise outputs agree
+    within the fp32 atomic summation order (1e-6 relative L2 per token)."""
+    if det:
+        assert np.array_equal(a, b), np.abs(a - b).max()
+    else:
+        err = np.linalg.norm(a - b, axis=1) / np.linalg.norm(b, axis=1)
+        assert err.max() <= 1e-6, err.max()
+
+
+@pytest.mark.parametrize("det", [False, True])
+def test_streaming_table_path_matches_resident_and_counts_lru(torch_mod, tiny, det):
     """Codes in pinned host memory through 5 HBM slots (k = 4): one-token calls
     that evict, and a 12-token call whose experts exceed the slots (run
     splitting), against a resident handle; hits/misses/bytes against the
-    policy's model."""
+    policy's model.  With the deterministic combine, streaming and resident,
+    and grouped and one-token calls, give bitwise identical outputs."""
     from synth import gpu as G
     shape = S.TINY
     bank = _pinned_bank(torch_mod, tiny)
     slots = 5
-    st = _layer(torch_mod, tiny, shape, 12, codes=bank, codes_location=1, cache_slots=slots)
-    rs = _layer(torch_mod, tiny, shape, 12)
+    st = _layer(torch_mod, tiny, shape, 12, codes=bank, codes_location=1, cache_slots=slots, deterministic=det)
+    rs = _layer(torch_mod, tiny, shape, 12, deterministic=det)
     x = S.tokens(0, 700, 20, shape.d)
     a = _run(torch_mod, st, shape, x, per_token=True)
     b = _run(torch_mod, rs, shape, x, per_token=True)
     assert np.array_equal(a[0], b[0])
-    err = np.linalg.norm(a[2] - b[2], axis=1) / np.linalg.norm(b[2], axis=1)
-    assert err.max() <= 1e-6, err.max()
+    _same_outputs(a[2], b[2], det)
     runs = [list(dict.fromkeys(row.tolist())) for row in a[0]]
     x2 = S.tokens(0, 800, 12, shape.d)
     a2 = _run(torch_mod, st, shape, x2)
     b2 = _run(torch_mod, rs, shape, x2)
-    err = np.linalg.norm(a2[2] - b2[2], axis=1) / np.linalg.norm(b2[2], axis=1)
-    assert err.max() <= 1e-6, err.max()
+    _same_outputs(a2[2], b2[2], det)
+    if det:  # grouped (one 12-token call) and one token per call, on the same ids and gates
+        assert np.array_equal(b2[2], _forward(torch_mod, rs, shape, x2, b2[0], b2[1], per_token=True))
     runs += _table_runs(a2[0], slots)
     hits, misses = _lru_model(slots, runs)
     stats = st.stats()
@@ -832,22 +859,24 @@ def test_streaming_table_path_matches_resident_and_counts_lru(torch_mod, tiny):
     rs.close()
 
 
-def test_streaming_chunk_path_matches_resident(torch_mod):
+@pytest.mark.parametrize("det", [False, True])
+def test_streaming_chunk_path_matches_resident(torch_mod, det):
     """The chunk path with 4 slots: experts in rounds of 2, copies overlapping
-    the previous round's kernels; same outputs as with resident codes."""
+    the previous round's kernels; same outputs as with resident codes (bitwise
+    with the deterministic combine)."""
     from synth import gpu as G
     shape = S.Shape(264, 136, 12, 3, "f16")
     inp = G.LayerInputs(shape, seed=23, layer=0, host_codes=True)
     bank = _pinned_bank(torch_mod, inp)
-    st = _layer(torch_mod, inp, shape, 48, codes=bank, codes_location=1, cache_slots=4, chunk_min_tokens=8)
-    rs = _layer(torch_mod, inp, shape, 48, chunk_min_tokens=8)
+    st = _layer(torch_mod, inp, shape, 48, codes=bank, codes_location=1, cache_slots=4, chunk_min_tokens=8,
+                deterministic=det)
+    rs = _layer(torch_mod, inp, shape, 48, chunk_min_tokens=8, deterministic=det)
     x = S.tokens(23, 0, 48, shape.d)
     for _ in range(2):
         a = _run(torch_mod, st, shape, x)
         b = _run(torch_mod, rs, shape, x)
         assert np.array_equal(a[0], b[0])
-        err = np.linalg.norm(a[2] - b[2], axis=1) / np.linalg.norm(b[2], axis=1)
-        assert err.max() <= 1e-6, err.max()
+        _same_outputs(a[2], b[2], det)
     _check_chunk(inp, shape, x, *a, tokens=[0, 47])
     n_exp = len(np.unique(a[0]))
     assert st.stats()["slot_misses"] + st.stats()["slot_hits"] == 2 * n_exp
@@ -922,18 +951,21 @@ def _lru_prefetch_model(S, events):
     return hits, misses, fills, phits
 
 
-def test_router_lookahead_prefetch_chain(torch_mod):
+@pytest.mark.parametrize("det", [False, True])
+def test_router_lookahead_prefetch_chain(torch_mod, det):
     """[FR] "Lecture anticipée et prédiction du routeur": a 3-layer streaming
     chain (RMS normalisation, residual), run with and without prefetching
     layer l+1's first 3 predicted experts (its router on layer l's input).
-    Ids are identical, outputs equal within the fp32 atomic-order bound, and
-    the slot counters match the cache policy's model, prefetches included."""
+    Ids are identical, outputs equal within the fp32 atomic-order bound
+    (bitwise with the deterministic combine: reading ahead leaves the output
+    exactly as it was), and the slot counters match the cache policy's model,
+    prefetches included."""
     from synth import gpu as G
     shape = S.Shape(512, 256, 32, 8, "f16")
     L, T, slots, ahead = 3, 6, 12, 3
     inps = [G.LayerInputs(shape, seed=31, layer=l, host_codes=True) for l in range(L)]
     banks = [_pinned_bank(torch_mod, inp) for inp in inps]
-    kw = dict(codes_location=1, cache_slots=slots, pre_rmsnorm=True, residual=True, eps=1e-6)
+    kw = dict(codes_location=1, cache_slots=slots, pre_rmsnorm=True, residual=True, eps=1e-6, deterministic=det)
     runs = {}
     for mode in ("plain", "ahead"):
         layers = [_layer(torch_mod, inps[l], shape, 1, codes=banks[l], **kw) for l in range(L)]
@@ -958,8 +990,7 @@ def test_router_lookahead_prefetch_chain(torch_mod):
     (ia, _, ha, sa), (ib, pb, hb, sb) = runs["plain"], runs["ahead"]
     assert np.array_equal(ia, ib)
     for l in range(1, L + 1):
-        err = np.linalg.norm(ha[l] - hb[l], axis=1) / np.linalg.norm(ha[l], axis=1)
-        assert err.max() <= 1e-6, (l, err.max())
+        _same_outputs(hb[l], ha[l], det)
     assert sum(st["prefetch_fills"] for st in sb) > 0
     assert all(st["prefetch_fills"] == 0 for st in sa)
     for l in range(L):
@@ -1007,24 +1038,25 @@ def test_prefetch_validation(torch_mod, tiny):
     st.close()
 
 
-def test_k3_streaming_batch1_matches_resident(torch_mod):
+@pytest.mark.parametrize("det", [False, True])
+def test_k3_streaming_batch1_matches_resident(torch_mod, det):
     """d=7168, ffn=2048, E=384, top-16 from a pinned host bank through 32 slots
     (every record's CRC-32 checked), one token per call; against a resident
-    handle and the oracle."""
+    handle (bitwise with the deterministic combine) and the oracle."""
     from synth import gpu as G
     shape = S.K3
     inp = G.LayerInputs(shape, seed=0, layer=6)
     bank = _pinned_bank(torch_mod, inp)
-    st = _layer(torch_mod, inp, shape, 1, codes=bank, codes_location=1, cache_slots=32, verify_records=True)
-    rs = _layer(torch_mod, inp, shape, 1)
+    st = _layer(torch_mod, inp, shape, 1, codes=bank, codes_location=1, cache_slots=32, verify_records=True,
+                deterministic=det)
+    rs = _layer(torch_mod, inp, shape, 1, deterministic=det)
     inp.free_codes()
     torch_mod.cuda.empty_cache()
     x = S.tokens(0, 4000, 4, shape.d)
     a = _run(torch_mod, st, shape, x, per_token=True)
     b = _run(torch_mod, rs, shape, x, per_token=True)
     assert np.array_equal(a[0], b[0])
-    err = np.linalg.norm(a[2] - b[2], axis=1) / np.linalg.norm(b[2], axis=1)
-    assert err.max() <= 1e-6, err.max()
+    _same_outputs(a[2], b[2], det)
     _check(inp, shape, x, *a, tokens=[0])
     assert st.stats()["slot_misses"] >= 16
     # every record copied in had its trailer and its 16.5 MB payload's CRC-32 checked
@@ -1033,6 +1065,60 @@ def test_k3_streaming_batch1_matches_resident(torch_mod):
     st.close()
     rs.close()
     del bank
+
+
+@pytest.mark.parametrize("shape_args", [(256, 128, 16, 4, "f32"), (1024, 520, 9, 3, "f16")])
+def test_deterministic_combine_repeats_bitwise_and_follows_the_oracle(torch_mod, shape_args):
+    """deterministic=1: repeated calls of every kind give the same bits
+    (one-token and grouped table path, the routed one-launch call, the chunk
+    path), the same bits as each other where the arithmetic is the same
+    (grouped vs one token per call), the fast handle's outputs within the fp32
+    atomic-order bound, and the oracle at the usual bars; an invalid id still
+    poisons only its token."""
+    from synth import gpu as G
+    from vector_quantized_expert_amd import RvqMoeError
+    shape = S.Shape(*shape_args)
+    inp = G.LayerInputs(shape, seed=61, layer=0, host_codes=True)
+    T = 6
+    det = _layer(torch_mod, inp, shape, T, deterministic=1, residual=True)
+    fast = _layer(torch_mod, inp, shape, T, residual=True)
+    chk = _layer(torch_mod, inp, shape, T, deterministic=1, chunk_min_tokens=4)
+    x = S.tokens(61, 0, T, shape.d)
+    a = _run(torch_mod, det, shape, x)
+    again = _run(torch_mod, det, shape, x)
+    assert np.array_equal(a[0], again[0]) and np.array_equal(a[1], again[1]) and np.array_equal(a[2], again[2])
+    assert np.array_equal(a[2], _forward(torch_mod, det, shape, x, a[0], a[1], per_token=True))
+    f = _run(torch_mod, fast, shape, x)
+    assert np.array_equal(a[0], f[0])
+    _same_outputs(a[2], f[2], False)
+    _check(inp, shape, x, *a, residual=True)
+    # the routed one-launch call, twice
+    xd = G.to_device(x[:1])
+    outs = []
+    for _ in range(2):
+        ids_d = torch_mod.empty((1, shape.top_k), dtype=torch_mod.int32, device="cuda")
+        g_d = torch_mod.empty((1, shape.top_k), device="cuda")
+        y_d = torch_mod.empty((1, shape.d), device="cuda")
+        det.route_forward(xd, 1, ids_d, g_d, y_d)
+        det.sync()
+        outs.append((ids_d.cpu().numpy(), g_d.cpu().numpy(), y_d.cpu().numpy()))
+    assert all(np.array_equal(u, v) for u, v in zip(*outs))
+    _check(inp, shape, x[:1], *outs[0], residual=True)
+    # the chunk path, twice
+    c1, c2 = _run(torch_mod, chk, shape, x), _run(torch_mod, chk, shape, x)
+    assert np.array_equal(c1[2], c2[2])
+    _check_chunk(inp, shape, x, *c1)
+    # an invalid id: its token's output is NaN, the others are finite
+    ids = torch_mod.tensor(a[0], device="cuda")
+    ids[1, 0] = shape.n_experts + 3
+    y = torch_mod.zeros((T, shape.d), device="cuda")
+    det.layer_forward(G.to_device(x), T, ids, G.to_device(a[1]), y)
+    with pytest.raises(RvqMoeError):
+        det.sync()
+    yh = y.cpu().numpy()
+    assert np.all(np.isnan(yh[1])) and np.all(np.isfinite(np.delete(yh, 1, axis=0)))
+    for h in (det, fast, chk):
+        h.close()
 
 
 def test_mixed_calls_on_one_handle_match_fresh_handles(torch_mod):

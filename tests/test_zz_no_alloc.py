@@ -94,3 +94,20 @@ def test_noalloc_k3_batch1_and_scratch_limit():
     assert ei.value.status == R.EINVAL
     assert torch.count_nonzero(y).item() == 0
     layer.close()
+
+
+def test_noalloc_deterministic_is_bitwise_layer_forward():
+    """With deterministic=1 the allocation-free call (output rows in the static
+    array too) gives the same bits as rvq_moe_layer_forward, twice in a row
+    (the second call smaller)."""
+    import torch
+    from synth import gpu as G
+    shape = S.Shape(264, 136, 5, 2, "f16")
+    inp = G.LayerInputs(shape, seed=2, layer=1, host_codes=True)
+    layer = _layer(inp, shape, 8, deterministic=1)
+    for T, t0 in ((7, 0), (3, 20)):
+        x = S.tokens(2, t0, T, shape.d)
+        ids, gates, y_ws, y_st = _both(torch, layer, shape, x)
+        assert np.array_equal(y_ws, y_st)
+        _compare(inp, shape, x, ids, gates, y_ws, y_st, tokens=[0])
+    layer.close()

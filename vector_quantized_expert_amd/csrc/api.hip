@@ -45,6 +45,7 @@ struct rvq_moe {
     int device;
     Geometry g;
     int pre_rmsnorm, residual, max_tokens;
+    bool det;            // deterministic combine (desc.deterministic)
     int chunk_min;       // layer_forward calls with T >= chunk_min take the chunk path
     int lut_tokens;      // in such a call, experts with fewer tokens take the table path
     ChunkWork cw;        // its workspace (all null when max_tokens < chunk_min)
@@ -110,6 +111,7 @@ static void free_handle(rvq_moe *h) {
     (void)hipFree(h->ws.cnt);
     (void)hipFree(h->ws.err);
     (void)hipFree(h->ws.cb_exp);
+    (void)hipFree(h->ws.part_y);
     (void)hipFree(h->cw.X);
     (void)hipFree(h->cw.H);
     (void)hipFree(h->cw.perm);
@@ -143,7 +145,8 @@ static int open_impl(const rvq_moe_desc *desc, rvq_moe *h) {
     h->max_tokens = D.max_tokens;
     h->chunk_min = D.chunk_min_tokens > 0 ? D.chunk_min_tokens : RVQ_MOE_CHUNK_MIN_TOKENS;
     h->lut_tokens = D.lut_expert_tokens > 0 ? D.lut_expert_tokens : RVQ_MOE_LUT_EXPERT_TOKENS;
-    if (D.codes_location != RVQ_MOE_CODES_DEVICE) h->lut_tokens = 1;
+    h->det = D.deterministic != 0;
+    if (D.codes_location != RVQ_MOE_CODES_DEVICE || h->det) h->lut_tokens = 1;
     const Geometry &g = h->g;
     const int64_t E = D.n_experts;
     h->streaming = D.codes_location != RVQ_MOE_CODES_DEVICE;
@@ -161,6 +164,11 @@ static int open_impl(const rvq_moe_desc *desc, rvq_moe *h) {
     HIP_TRY(hipMalloc(&h->ws.cnt, sizeof(int) * (size_t)kCntSets * (P + 1) * kCntStride));
     HIP_TRY(hipMalloc(&h->ws.err, sizeof(int)));
     HIP_TRY(hipMalloc(&h->ws.cb_exp, sizeof(int) * 3 * (size_t)E));
+    h->ws.det = h->cw.det = h->det;
+    if (h->det) {  // pair output rows per down tile (table path) or whole (chunk path: the first d_pad of each)
+        HIP_TRY(hipMalloc(&h->ws.part_y, sizeof(float) * (size_t)(P * g.m[2].n_tiles * g.d_pad)));
+        h->cw.part_y = h->ws.part_y;
+    }
     if (h->max_tokens >= h->chunk_min) {
         HIP_TRY(hipMalloc(&h->cw.X, 2 * (size_t)(P * D.d)));
         HIP_TRY(hipMalloc(&h->cw.H, 2 * (size_t)(P * D.ffn)));
@@ -256,7 +264,8 @@ extern "C" int rvq_moe_open(const rvq_moe_desc *desc, rvq_moe **out) {
     if (D.codes_location == RVQ_MOE_CODES_DEVICE && D.cache_slots != 0)
         return fail(RVQ_MOE_EINVAL, "cache_slots=%d: the slot cache streams PINNED_HOST or PINNED_BANK codes only",
                     D.cache_slots);
-    if (D.reserved != 0) return fail(RVQ_MOE_EINVAL, "reserved=%d must be 0", D.reserved);
+    if (D.deterministic != 0 && D.deterministic != 1)
+        return fail(RVQ_MOE_EINVAL, "deterministic=%d must be 0 or 1", D.deterministic);
     if (!D.router_w || !D.codebooks || !D.codes) return fail(RVQ_MOE_EINVAL, "null router_w/codebooks/codes");
     if (D.codes_location != RVQ_MOE_CODES_DEVICE) {
         if (D.cache_slots == 0) return fail(RVQ_MOE_EINVAL, "streamed codes need cache_slots >= top_k");
@@ -338,6 +347,15 @@ extern "C" int rvq_moe_route_topk(rvq_moe *h, const float *x, int32_t T, int32_t
     return RVQ_MOE_OK;
 }
 
+// The deterministic combine after the layer kernels of a call (tokens [0, T)
+// of x, ids, y): slots = the down projection's tiles on the table path, 1 on
+// the chunk path.
+static hipError_t combine(rvq_moe *h, const Workspace &w, int slots, const float *x, const int32_t *ids, float *y,
+                          int T, hipStream_t s) {
+    const Geometry &g = h->g;
+    return launch_combine(w.part_y, slots, x, ids, y, T, g.k, g.E, g.d, g.d_pad, h->residual, s);
+}
+
 // layer_forward with the codes streaming through the slot cache.  Reads the
 // call's ids back (the one host synchronisation), then enqueues everything:
 //  - table path: tokens in runs whose distinct experts fit the slots; per run,
@@ -372,6 +390,7 @@ static int stream_forward(rvq_moe *h, const float *x, int T, const int32_t *ids,
             HIP_TRY(launch_chunk_experts(g, h->cw, nullptr, c.tab_dev, h->cbs, gates, y, a0, a1, s));
             HIP_TRY(slots_release(c, h->call_used, s));
         }
+        if (h->det) HIP_TRY(combine(h, h->ws, 1, x, ids, y, T, s));
         return RVQ_MOE_OK;
     }
     int t0 = 0;
@@ -382,6 +401,9 @@ static int stream_forward(rvq_moe *h, const float *x, int T, const int32_t *ids,
                              ids + (size_t)t0 * k, gates + (size_t)t0 * k, y + (size_t)t0 * g.d, t1 - t0,
                              h->pre_rmsnorm, h->residual, h->eps, false, s));
         HIP_TRY(slots_release(c, h->call_used, s));
+        if (h->det)
+            HIP_TRY(combine(h, h->ws, g.m[2].n_tiles, x + (size_t)t0 * g.d, ids + (size_t)t0 * k,
+                            y + (size_t)t0 * g.d, t1 - t0, s));
         return RVQ_MOE_OK;
     };
     for (int t = 0; t < T; t++) {
@@ -429,10 +451,12 @@ extern "C" int rvq_moe_layer_forward(rvq_moe *h, const float *x, int32_t T, cons
         if (h->lut_tokens > 1)  // the experts with few tokens, listed by the chunk prep, on the table path
             HIP_TRY(launch_layer(h->g, h->ws, h->codes, nullptr, h->cbs, h->router_wt, x, ids, gates, y, T,
                                  h->pre_rmsnorm, h->residual, h->eps, false, s, h->cw.list));
+        if (h->det) HIP_TRY(combine(h, h->ws, 1, x, ids, y, T, s));
     } else {
         ProfScope p(h, s, prof, 1);
         HIP_TRY(launch_layer(h->g, h->ws, h->codes, nullptr, h->cbs, h->router_wt, x, ids, gates, y, T,
                              h->pre_rmsnorm, h->residual, h->eps, false, s));
+        if (h->det) HIP_TRY(combine(h, h->ws, h->g.m[2].n_tiles, x, ids, y, T, s));
     }
     h->stats.forward_calls++;
     h->stats.tokens_forwarded += (uint64_t)T;
@@ -453,7 +477,9 @@ extern "C" int rvq_moe_layer_forward_noalloc(rvq_moe *h, const float *x, int32_t
     const int64_t P = (int64_t)T * g.k;
     const size_t cnt_ints = (size_t)kCntSets * (size_t)(P + 1) * kCntStride;
     const size_t part_off = (cnt_ints * sizeof(int) + 255) / 256 * 256;
-    const size_t need = part_off + sizeof(float) * (size_t)P * 2 * g.m[0].n_tiles * g.ffn_pad;
+    const size_t party_off = (part_off + sizeof(float) * (size_t)P * 2 * g.m[0].n_tiles * g.ffn_pad + 255) / 256 * 256;
+    const size_t need = h->det ? party_off + sizeof(float) * (size_t)P * g.m[2].n_tiles * g.d_pad
+                               : part_off + sizeof(float) * (size_t)P * 2 * g.m[0].n_tiles * g.ffn_pad;
     if (need > kStaticScratchBytes)
         return fail(RVQ_MOE_EINVAL,
                     "layer_forward_noalloc: %d tokens need %zu bytes of scratch, above the static %zu (fewer tokens "
@@ -467,6 +493,7 @@ extern "C" int rvq_moe_layer_forward_noalloc(rvq_moe *h, const float *x, int32_t
     w.cnt_per_set = (int)(P + 1);
     w.cnt_phase = 0;
     w.part_gu = reinterpret_cast<float *>(base + part_off);
+    if (h->det) w.part_y = reinterpret_cast<float *>(base + party_off);
     const bool prof = h->prof_every > 0 && (h->prof_calls++ % (uint64_t)h->prof_every) == 0;
     {
         ProfScope p(h, s, prof, 1);
@@ -475,6 +502,7 @@ extern "C" int rvq_moe_layer_forward_noalloc(rvq_moe *h, const float *x, int32_t
         HIP_TRY(launch_zero_ints(w.cnt, (int)cnt_ints, s));
         HIP_TRY(launch_layer(g, w, h->codes, nullptr, h->cbs, h->router_wt, x, ids, gates, y, T, h->pre_rmsnorm,
                              h->residual, h->eps, false, s));
+        if (h->det) HIP_TRY(combine(h, w, g.m[2].n_tiles, x, ids, y, T, s));
     }
     h->stats.forward_calls++;
     h->stats.tokens_forwarded += (uint64_t)T;
@@ -501,6 +529,7 @@ extern "C" int rvq_moe_route_forward(rvq_moe *h, const float *x, int32_t T, int3
         ProfScope p(h, s, prof, 2);
         HIP_TRY(launch_layer(h->g, h->ws, h->codes, nullptr, h->cbs, h->router_wt, x, ids, gates, y, T,
                              h->pre_rmsnorm, h->residual, h->eps, true, s));
+        if (h->det) HIP_TRY(combine(h, h->ws, h->g.m[2].n_tiles, x, ids, y, T, s));
     }
     h->stats.route_calls++;
     h->stats.tokens_routed += (uint64_t)T;

@@ -156,7 +156,7 @@ __global__ __launch_bounds__(kCkThreads) void k_chunk_stage(const float *__restr
                                                             double eps, int residual, int E,
                                                             const int32_t *__restrict__ ids,
                                                             const int *__restrict__ pos_of, __bf16 *__restrict__ X,
-                                                            float *__restrict__ y) {
+                                                            float *__restrict__ y, int init_y) {
     const int t = blockIdx.x;
     const float *xt = x + (size_t)t * d;
     __shared__ double red[kCkThreads / 64];
@@ -178,7 +178,8 @@ __global__ __launch_bounds__(kCkThreads) void k_chunk_stage(const float *__restr
     __syncthreads();
     if (pre) r = sqrt((red[0] + red[1] + red[2] + red[3]) / (double)d + eps);
     const float poison = bad ? __int_as_float(0x7fc00000) : 0.f;
-    for (int i = threadIdx.x; i < d; i += kCkThreads) y[(size_t)t * d + i] = (residual ? xt[i] : 0.f) + poison;
+    if (init_y)  // (with the deterministic combine, y is written after the contractions)
+        for (int i = threadIdx.x; i < d; i += kCkThreads) y[(size_t)t * d + i] = (residual ? xt[i] : 0.f) + poison;
     for (int j = 0; j < k; j++) {
         __bf16 *dst = X + (size_t)pos_of[(size_t)t * k + j] * d;
         for (int i = threadIdx.x; i < d; i += kCkThreads) {
@@ -325,6 +326,7 @@ struct ChunkArgs {
     __bf16 *H;        // [P][ffn] permuted bf16 SwiGLU outputs
     const float *gates;
     float *y;
+    float *part_y;  // deterministic combine: [P][d_pad] output rows per pair (y untouched), else null
     Geometry g;
 };
 
@@ -469,7 +471,10 @@ __global__ __launch_bounds__(kCkThreads) void k_chunk_down(ChunkArgs A) {
                     const int p = p0 + mt * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
                     if (p < g1 && row < g.d) {
                         const int pair = A.perm[p];
-                        unsafeAtomicAdd(A.y + (size_t)(pair / k) * g.d + row, A.gates[pair] * acc[mt][v]);
+                        if (A.part_y)  // one writer per (pair, row): combined in a fixed order afterwards
+                            A.part_y[(size_t)pair * g.d_pad + row] = A.gates[pair] * acc[mt][v];
+                        else
+                            unsafeAtomicAdd(A.y + (size_t)(pair / k) * g.d + row, A.gates[pair] * acc[mt][v]);
                     }
                 }
             }
@@ -492,7 +497,7 @@ hipError_t launch_chunk_prep(const Geometry &g, const ChunkWork &cw, const float
     hipError_t rc = hipGetLastError();
     if (rc != hipSuccess) return rc;
     hipLaunchKernelGGL(k_chunk_stage, dim3(T), dim3(kCkThreads), 0, s, x, g.d, g.k, pre, eps, residual, g.E, ids,
-                       cw.pos_of, cw.X, y);
+                       cw.pos_of, cw.X, y, cw.det ? 0 : 1);
     return hipGetLastError();
 }
 
@@ -500,7 +505,8 @@ hipError_t launch_chunk_experts(const Geometry &g, const ChunkWork &cw, const ui
                                 const uint8_t *const *slot_tab, const void *cbs, const float *gates, float *y, int a0,
                                 int a1, hipStream_t s) {
     if (a1 <= a0) return hipSuccess;
-    ChunkArgs A{codes, slot_tab, a0, a1, cbs, cw.grp_off, cw.act, cw.perm, cw.X, cw.H, gates, y, g};
+    ChunkArgs A{codes, slot_tab, a0, a1, cbs, cw.grp_off, cw.act, cw.perm, cw.X, cw.H, gates, y,
+                cw.det ? cw.part_y : nullptr, g};
     const dim3 ggu((g.m[0].n_chunks + 1) / 2, a1 - a0), gdn((g.m[2].n_chunks + 3) / 4, a1 - a0);
     // each kernel pair takes the experts of its token class and skips the others
     if (g.cb_dtype == 0) {

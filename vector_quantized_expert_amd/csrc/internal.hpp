@@ -160,6 +160,8 @@ struct Workspace {
     int *err;           // device error flag: bit 0 bad id, bit 1 wait timeout
     int n_wg;           // persistent workgroups (all resident at once: blocks per CU x CUs)
     int *cb_exp;        // [E][3] scale exponents of fp32 codebook matrices (0 for fp16), set at open
+    bool det;           // deterministic combine: pair outputs go to part_y, combined by k_combine
+    float *part_y;      // det: [P][n_tiles of down][d_pad] output rows of each pair and down tile
 };
 
 // Chunk-path workspace (device), sized for max_tokens * k pairs.
@@ -171,6 +173,8 @@ struct ChunkWork {
     int *grp_off;  // [E + 2] group offsets (group E: invalid ids)
     int *act;      // [E + 1] experts on the matrix cores, then their count at [E]
     int *list;     // [kPairListInts] pairs handed to the table path (see below)
+    bool det;      // deterministic combine: pair outputs go to part_y [P][d_pad], combined by k_combine
+    float *part_y;
 };
 
 // The table path's order table holds up to kOrderMax (token, expert) pairs.
@@ -211,6 +215,11 @@ hipError_t init_route(Workspace &w, int E, int k, int64_t max_tokens, int n_cu, 
 hipError_t launch_route(const Geometry &g, Workspace &w, const float *x, const float *Wt, int T, int pre,
                         double eps, int32_t *ids, float *gates, hipStream_t s);
 hipError_t layer_blocks_per_cu(int cb_dtype, int *out);
+// Deterministic combine: y[t] = (x[t] when residual) + the k * slots rows
+// part[(t k + j) slots + s][0 .. d) added in the order (j, s); NaN for a
+// token with an id outside [0, E).  One launch after the layer's kernels.
+hipError_t launch_combine(const float *part, int slots, const float *x, const int32_t *ids, float *y, int T, int k,
+                          int E, int d, int d_pad, int residual, hipStream_t s);
 // Static device scratch of rvq_moe_layer_forward_noalloc (noalloc.hip):
 // kStaticScratchBytes per device, its address looked up once per device.
 constexpr size_t kStaticScratchBytes = (size_t)32 << 20;

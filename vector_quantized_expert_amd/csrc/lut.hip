@@ -564,6 +564,7 @@ struct LayerArgs {
     float *y;
     float *part_gu;  // [P][2][n_ti][ffn_pad]
     int *cntA;       // this launch's set: finished gate/up chunks of pair p at p * kCntStride
+    float *part_y;   // deterministic combine: [P][n_tf][d_pad] output rows per pair and down tile, else null
     int *err;
     Geometry g;
     int T;
@@ -1045,7 +1046,7 @@ __device__ void route_phase(const LayerArgs &a, double *scratch, float *gate_lds
     if (threadIdx.x < n_own)
         for (int t = 0; t < a.T_reset; t++)
             store_coherent(a.rl_next + (size_t)t * g.E + wg + threadIdx.x * G, unpub);
-    init_y(a);  // independent of the routing: done while the logits land
+    if (!a.part_y) init_y(a);  // independent of the routing: done while the logits land
     idle();
     // ---- R2
     const uint64_t t_start = wall_clock64();
@@ -1204,8 +1205,8 @@ __global__ __launch_bounds__(kBlock) void k_layer(LayerArgs a) {
     // ---------------- y starts as 0 (or x with the residual); the routed kernel
     // did this while routing, and with a handed-over pair list the chunk path
     // has set it already
-    if (!kList && !kRoute) init_y(a);
-    bool y_ready = false;
+    if (!kList && !kRoute && !a.part_y) init_y(a);
+    bool y_ready = a.part_y != nullptr;  // the deterministic combine writes y after the launch
     // Phase-A chunk counts are published per pair, once the workgroup moves on
     // to another pair or ends phase A (phase B waits for a pair's total), so
     // only those transitions wait for the stores to complete.  The y stores
@@ -1231,7 +1232,9 @@ __global__ __launch_bounds__(kBlock) void k_layer(LayerArgs a) {
     };
 
     // merged gate/up partial sums in the pair order (see merged_away)
-    const bool merge = !ord.tab && n_cf <= 64;
+    // (not with the deterministic combine: every order then sums each row's
+    // tiles one by one, in tile order)
+    const bool merge = !ord.tab && n_cf <= 64 && !a.part_y;
     const int64_t nA = (int64_t)P * 2 * n_ti * n_cf;
     __shared__ uint64_t vmask[2][kMaskWords];
     // ---------------- phase A: gate and up
@@ -1390,15 +1393,20 @@ __global__ __launch_bounds__(kBlock) void k_layer(LayerArgs a) {
                     wait_count(a.ycnt, G, a.err);
                     y_ready = true;
                 }
-                float *yt = a.y + (size_t)(cur.p / g.k) * g.d;
-                gather_segment<true, false>(lut, cb_area_stage(lut), base, cur.c0, cur.c1, yt, g.d, p, kNT);
+                if (a.part_y) {  // this pair's rows of down tile ft, combined after the launch
+                    float *pt = a.part_y + ((int64_t)cur.p * n_tf + cur.ft) * g.d_pad;
+                    gather_segment<false, false>(lut, cb_area_stage(lut), base, cur.c0, cur.c1, pt, g.d, p, kNT);
+                } else {
+                    float *yt = a.y + (size_t)(cur.p / g.k) * g.d;
+                    gather_segment<true, false>(lut, cb_area_stage(lut), base, cur.c0, cur.c1, yt, g.d, p, kNT);
+                }
             } else {
                 // an invalid id poisons its token's output (the error flag is already set)
                 if (!y_ready) {
                     wait_count(a.ycnt, G, a.err);
                     y_ready = true;
                 }
-                if (cur.ft == 0)
+                if (cur.ft == 0 && !a.part_y)  // (the deterministic combine poisons the token itself)
                     for (int r = cur.c0 * kChunkRows + threadIdx.x; r < min(g.d, cur.c1 * kChunkRows); r += kBlock)
                         unsafeAtomicAdd(a.y + (size_t)(cur.p / g.k) * g.d + r, __int_as_float(0x7fc00000));
                 if (un < u1 && nxt.e >= 0 && nxt.e < g.E) cb_load<CB>(cb, a.cbs, a.cb_exp, nxt.e, 2);
@@ -1411,6 +1419,61 @@ __global__ __launch_bounds__(kBlock) void k_layer(LayerArgs a) {
     // the other counter set starts the next launch at zero (see kCntSets)
     for (int i = range_lo(a.n_clear, wg, G) + threadIdx.x; i < range_lo(a.n_clear, wg + 1, G); i += kBlock)
         store_counter(a.cnt_clear + (size_t)i * kCntStride, 0);
+}
+
+// Deterministic combine (see launch_combine).  A workgroup takes 32 output
+// elements of one token; lane q (of kCombLanes) sums the token's partial rows
+// q, q + kCombLanes, ... in that order (all of its loads in flight together),
+// then the lanes' sums are added in lane order after x.  The order depends on
+// k, slots and the element only, never on timing or on how tokens were
+// grouped into calls.
+constexpr int kCombLanes = 8, kCombRows = 32, kCombInFlight = 16;
+__global__ __launch_bounds__(kCombLanes * kCombRows) void k_combine(const float *__restrict__ part, int slots,
+                                                                    const float *__restrict__ x,
+                                                                    const int32_t *__restrict__ ids,
+                                                                    float *__restrict__ y, int k, int E, int d,
+                                                                    int d_pad, int residual) {
+    const int t = blockIdx.y;
+    const int q = threadIdx.x / kCombRows, rr = threadIdx.x % kCombRows;
+    const int r = blockIdx.x * kCombRows + rr;
+    __shared__ float lane_sum[kCombLanes][kCombRows];
+    const int n = k * slots;
+    float acc = 0.f;
+    if (r < d) {
+        const float *p = part + (size_t)t * n * d_pad + r;
+        for (int i0 = q; i0 < n; i0 += kCombLanes * kCombInFlight) {
+            float v[kCombInFlight];
+#pragma unroll
+            for (int u = 0; u < kCombInFlight; u++) {
+                const int i = i0 + u * kCombLanes;
+                v[u] = i < n ? p[(size_t)i * d_pad] : 0.f;
+            }
+#pragma unroll
+            for (int u = 0; u < kCombInFlight; u++)
+                if (i0 + u * kCombLanes < n) acc += v[u];
+        }
+    }
+    lane_sum[q][rr] = acc;
+    __syncthreads();
+    if (q != 0 || r >= d) return;
+    bool bad = false;
+    for (int j = 0; j < k; j++) {
+        const int e = ids[(size_t)t * k + j];
+        bad |= e < 0 || e >= E;
+    }
+    float out = residual ? x[(size_t)t * d + r] : 0.f;
+    float sum = lane_sum[0][rr];
+#pragma unroll
+    for (int l = 1; l < kCombLanes; l++) sum += lane_sum[l][rr];
+    out += sum;
+    y[(size_t)t * d + r] = bad ? __int_as_float(0x7fc00000) : out;
+}
+
+hipError_t launch_combine(const float *part, int slots, const float *x, const int32_t *ids, float *y, int T, int k,
+                          int E, int d, int d_pad, int residual, hipStream_t s) {
+    hipLaunchKernelGGL(k_combine, dim3((d + kCombRows - 1) / kCombRows, T), dim3(kCombLanes * kCombRows), 0, s, part,
+                       slots, x, ids, y, k, E, d, d_pad, residual);
+    return hipGetLastError();
 }
 
 typedef void (*LayerKernel)(LayerArgs);
@@ -1444,7 +1507,7 @@ hipError_t launch_layer(const Geometry &g, Workspace &w, const uint8_t *codes, c
     int *cnt_clear = w.cnt + ((w.cnt_phase + 1) % kCntSets) * set_ints;
     LayerArgs a{Wt, w.logits, w.sel, cnt_cur + (size_t)(w.cnt_per_set - 1) * kCntStride, cnt_clear, w.cnt_per_set,
                 rl_cur, rl_next, T_reset, list, codes, slot_tab, cbs, w.cb_exp, x, ids, gates, y, w.part_gu,
-                cnt_cur, w.err, g, T, pre, residual, eps};
+                cnt_cur, w.det ? w.part_y : nullptr, w.err, g, T, pre, residual, eps};
     // A plain launch of exactly as many workgroups as can be resident at once
     // (sized at open from the occupancy query); the inter-workgroup waits are
     // bounded, so a launch that somehow did not get all of them resident ends

@@ -52,7 +52,7 @@ class Desc(ctypes.Structure):
         ("chunk_min_tokens", ctypes.c_int32),
         ("lut_expert_tokens", ctypes.c_int32),
         ("verify_records", ctypes.c_int32),
-        ("reserved", ctypes.c_int32),
+        ("deterministic", ctypes.c_int32),
         ("eps", ctypes.c_double),
         ("router_w", ctypes.c_void_p),
         ("codebooks", ctypes.c_void_p),
@@ -159,10 +159,11 @@ def _stream(stream) -> int:
 def make_desc(*, d, ffn, n_experts, top_k, codebook_dtype, router_w, codebooks, codes,
               codes_location=CODES_DEVICE, cache_slots=0, pre_rmsnorm=False, eps=1e-6, residual=False,
               max_tokens=1, chunk_min_tokens=0, lut_expert_tokens=0, verify_records=False, stream=None,
-              n_stages=3, n_codes=256, vec_dim=8, reserved=0) -> Desc:
+              n_stages=3, n_codes=256, vec_dim=8, deterministic=0) -> Desc:
     return Desc(ctypes.sizeof(Desc), d, ffn, n_experts, top_k, n_stages, n_codes, vec_dim, codebook_dtype,
                 codes_location, cache_slots, int(bool(pre_rmsnorm)), int(bool(residual)), max_tokens,
-                chunk_min_tokens, lut_expert_tokens, int(bool(verify_records)), reserved, eps, _ptr(router_w),
+                chunk_min_tokens, lut_expert_tokens, int(bool(verify_records)), int(deterministic), eps,
+                _ptr(router_w),
                 _ptr(codebooks), _ptr(codes), _stream(stream) if stream != 0 else 0)
 
 
