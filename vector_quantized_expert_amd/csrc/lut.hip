@@ -1102,7 +1102,10 @@ __device__ void route_gates(const LayerArgs &a, double *scratch, float *gate_lds
 // (rvq_moe_route_forward), or a pair list handed over by the chunk path.
 enum LayerMode { kFromIds = 0, kRouted = 1, kListed = 2 };
 
-template <int CB, int kMode, bool kNT>
+// kDet: the deterministic combine (output rows to a.part_y; see launch_combine).
+// A template parameter, not a runtime flag, so that the other instances keep
+// their register allocation.
+template <int CB, int kMode, bool kNT, bool kDet>
 __global__ __launch_bounds__(kBlock) void k_layer(LayerArgs a) {
     constexpr bool kRoute = kMode == kRouted, kList = kMode == kListed;
     __shared__ __align__(16) float lut[kLutWords];  // also 8-byte staging (logits, order masks)
@@ -1205,8 +1208,8 @@ __global__ __launch_bounds__(kBlock) void k_layer(LayerArgs a) {
     // ---------------- y starts as 0 (or x with the residual); the routed kernel
     // did this while routing, and with a handed-over pair list the chunk path
     // has set it already
-    if (!kList && !kRoute && !a.part_y) init_y(a);
-    bool y_ready = a.part_y != nullptr;  // the deterministic combine writes y after the launch
+    if (!kList && !kRoute && !kDet) init_y(a);
+    bool y_ready = kDet;  // the deterministic combine writes y after the launch
     // Phase-A chunk counts are published per pair, once the workgroup moves on
     // to another pair or ends phase A (phase B waits for a pair's total), so
     // only those transitions wait for the stores to complete.  The y stores
@@ -1234,7 +1237,7 @@ __global__ __launch_bounds__(kBlock) void k_layer(LayerArgs a) {
     // merged gate/up partial sums in the pair order (see merged_away)
     // (not with the deterministic combine: every order then sums each row's
     // tiles one by one, in tile order)
-    const bool merge = !ord.tab && n_cf <= 64 && !a.part_y;
+    const bool merge = !ord.tab && n_cf <= 64 && !kDet;
     const int64_t nA = (int64_t)P * 2 * n_ti * n_cf;
     __shared__ uint64_t vmask[2][kMaskWords];
     // ---------------- phase A: gate and up
@@ -1393,7 +1396,7 @@ __global__ __launch_bounds__(kBlock) void k_layer(LayerArgs a) {
                     wait_count(a.ycnt, G, a.err);
                     y_ready = true;
                 }
-                if (a.part_y) {  // this pair's rows of down tile ft, combined after the launch
+                if (kDet) {  // this pair's rows of down tile ft, combined after the launch
                     float *pt = a.part_y + ((int64_t)cur.p * n_tf + cur.ft) * g.d_pad;
                     gather_segment<false, false>(lut, cb_area_stage(lut), base, cur.c0, cur.c1, pt, g.d, p, kNT);
                 } else {
@@ -1406,7 +1409,7 @@ __global__ __launch_bounds__(kBlock) void k_layer(LayerArgs a) {
                     wait_count(a.ycnt, G, a.err);
                     y_ready = true;
                 }
-                if (cur.ft == 0 && !a.part_y)  // (the deterministic combine poisons the token itself)
+                if (cur.ft == 0 && !kDet)  // (the deterministic combine poisons the token itself)
                     for (int r = cur.c0 * kChunkRows + threadIdx.x; r < min(g.d, cur.c1 * kChunkRows); r += kBlock)
                         unsafeAtomicAdd(a.y + (size_t)(cur.p / g.k) * g.d + r, __int_as_float(0x7fc00000));
                 if (un < u1 && nxt.e >= 0 && nxt.e < g.E) cb_load<CB>(cb, a.cbs, a.cb_exp, nxt.e, 2);
@@ -1477,15 +1480,18 @@ hipError_t launch_combine(const float *part, int slots, const float *x, const in
 }
 
 typedef void (*LayerKernel)(LayerArgs);
-static LayerKernel layer_kernel(int cb_dtype, int mode, bool nt) {
-    if (cb_dtype == 0) {
-        if (mode == kListed) return k_layer<0, kListed, false>;
-        if (mode == kRouted) return nt ? k_layer<0, kRouted, true> : k_layer<0, kRouted, false>;
-        return nt ? k_layer<0, kFromIds, true> : k_layer<0, kFromIds, false>;
+template <int CB>
+static LayerKernel layer_kernel_cb(int mode, bool nt, bool det) {
+    if (mode == kListed) return k_layer<CB, kListed, false, false>;  // (never with the deterministic combine)
+    if (det) {
+        if (mode == kRouted) return nt ? k_layer<CB, kRouted, true, true> : k_layer<CB, kRouted, false, true>;
+        return nt ? k_layer<CB, kFromIds, true, true> : k_layer<CB, kFromIds, false, true>;
     }
-    if (mode == kListed) return k_layer<1, kListed, false>;
-    if (mode == kRouted) return nt ? k_layer<1, kRouted, true> : k_layer<1, kRouted, false>;
-    return nt ? k_layer<1, kFromIds, true> : k_layer<1, kFromIds, false>;
+    if (mode == kRouted) return nt ? k_layer<CB, kRouted, true, false> : k_layer<CB, kRouted, false, false>;
+    return nt ? k_layer<CB, kFromIds, true, false> : k_layer<CB, kFromIds, false, false>;
+}
+static LayerKernel layer_kernel(int cb_dtype, int mode, bool nt, bool det) {
+    return cb_dtype == 0 ? layer_kernel_cb<0>(mode, nt, det) : layer_kernel_cb<1>(mode, nt, det);
 }
 
 hipError_t launch_layer(const Geometry &g, Workspace &w, const uint8_t *codes, const uint8_t *const *slot_tab,
@@ -1513,8 +1519,8 @@ hipError_t launch_layer(const Geometry &g, Workspace &w, const uint8_t *codes, c
     // bounded, so a launch that somehow did not get all of them resident ends
     // with an error flag instead of hanging.
     const bool group = list || (T > 1 && T * g.k <= kOrderMax);  // the kernel takes the same decision
-    hipLaunchKernelGGL(layer_kernel(g.cb_dtype, list ? kListed : route ? kRouted : kFromIds, !group), dim3(w.n_wg),
-                       dim3(kBlock), 0, s, a);
+    hipLaunchKernelGGL(layer_kernel(g.cb_dtype, list ? kListed : route ? kRouted : kFromIds, !group, w.det && !list),
+                       dim3(w.n_wg), dim3(kBlock), 0, s, a);
     const hipError_t e = hipGetLastError();
     // the alternating buffers and counter sets advance only with a launch that
     // was enqueued: a failed launch leaves them as the last launch left them
@@ -1530,10 +1536,10 @@ hipError_t launch_layer(const Geometry &g, Workspace &w, const uint8_t *codes, c
 hipError_t layer_blocks_per_cu(int cb_dtype, int *out) {
     // the grid must be resident under every variant: take the smallest occupancy
     int best = 1 << 30;
-    for (int v = 0; v < 6; v++) {
+    for (int v = 0; v < 12; v++) {
         int n = 0;
-        const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, layer_kernel(cb_dtype, v >> 1, v & 1),
-                                                                          kBlock, 0);
+        const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &n, layer_kernel(cb_dtype, (v >> 1) % 3, v & 1, v >= 6), kBlock, 0);
         if (e != hipSuccess) return e;
         best = n < best ? n : best;
     }
