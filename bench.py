@@ -163,7 +163,7 @@ def oracle_baseline(O, S, shape, tokens, w_r, cb_of, rec_of, pre, residual, laye
         for e in r.ids:
             rec_of(int(e))
     n_all = O.threads()
-    one = tokens[:4]
+    one = tokens[:16]
     O.set_threads(1)
     t0 = time.perf_counter()
     run(one)
@@ -339,8 +339,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--repeats", type=int, default=5, help="blocks of --steps timed steps (median and range)")
     ap.add_argument("--latency-calls", type=int, default=200, help="calls timed one by one for p50/p99")
-    ap.add_argument("--cpu-tokens", type=int, default=16,
-                    help="tokens the oracle baseline runs on all host threads (the first 4 also on one; 0: skip)")
+    ap.add_argument("--cpu-tokens", type=int, default=160,
+                    help="tokens the oracle baseline runs on all host threads (the first 16 also on one; 0: skip)")
     ap.add_argument("--no-ceilings", action="store_true", help="skip the machine-ceiling measurements")
     ap.add_argument("--no-sub", action="store_true",
                     help="skip the sub-records (batched decode, prefill chunk, depth chain) of the default run")
@@ -356,6 +356,8 @@ def main():
                     help="stream the codes from a pinned host bank through this many HBM slots")
     ap.add_argument("--verify", action="store_true",
                     help="with --stream-slots: check the CRC-32 of every expert record copied into a slot")
+    ap.add_argument("--deterministic", action="store_true",
+                    help="fixed-order combine (bitwise reproducible outputs) instead of fp32 atomics")
     ap.add_argument("--lut-expert-tokens", type=int, default=0,
                     help="with --chunk: experts routed fewer tokens than this take the table path (0: the "
                          "library default, 1: every expert on the matrix cores)")
@@ -398,7 +400,8 @@ def main():
                                  not 1 <= args.lookahead <= shape.top_k))):
         print(f"--batch {B} / --layers {L} outside what the chosen path takes", file=sys.stderr)
         sys.exit(2)
-    headline = B == 1 and L == 1 and not args.chunk and not streaming and args.path == "fused"
+    headline = (B == 1 and L == 1 and not args.chunk and not streaming and args.path == "fused"
+                and not args.deterministic)
     want_sub = headline and not args.no_sub
 
     ceil = None
@@ -420,7 +423,8 @@ def main():
                              codebook_dtype=1, router_w=inp.w_r_dev, codebooks=inp.cb_dev, codes=codes,
                              max_tokens=B, pre_rmsnorm=chain, residual=chain, eps=1e-6,
                              chunk_min_tokens=1 if args.chunk else B + 1,
-                             lut_expert_tokens=args.lut_expert_tokens, **extra))
+                             lut_expert_tokens=args.lut_expert_tokens, deterministic=int(args.deterministic),
+                             **extra))
         del codes
         if L == 1 and args.cpu_tokens > 0:
             bank_host = inp.codes_dev.cpu().numpy()  # the oracle's records (host copy of the bank)
@@ -587,7 +591,7 @@ def main():
         parity = {"tokens": n_par, "layers_checked": L, "ids_bit_exact": ok_ids, "max_rel_l2": max(errs),
                   "bar": "ids bit-exact, rel L2 <= 1e-4" if not args.chunk else "ids bit-exact, rel L2 <= 2e-2"}
         # the oracle's own time on the first layer of this workload
-        toks = [hs[0, W * B + j] for j in range(args.cpu_tokens)]
+        toks = [hs[0, W * B + j] for j in range(min(args.cpu_tokens, hs.shape[1] - W * B))]
         base = oracle_baseline(O, S, shape, toks, inputs[0].w_r, inputs[0].codebook, rec_of[0], chain, chain)
         cpu = {"value": base["all"], "unit": "tokens/s", "cores": base["threads"], "kind": "oracle",
                "sample": f"{base['n_all']} tokens of the same workload through one layer (router, top-16 and 16 "
@@ -623,7 +627,7 @@ def main():
         workload = (f"K3-scale routed RVQ-MoE layer, batch-{B} decode, {where}: d=7168 ffn=2048 E=384 top-16, "
                     f"3-stage x 256 x 8 fp16 codebooks, uniform u8 codes, T={B} per call")
     traffic = (recorded_traffic(args.path == "fused")
-               if (B == 1 and L == 1 and not args.chunk and not streaming) else None)
+               if (B == 1 and L == 1 and not args.chunk and not streaming and not args.deterministic) else None)
     out = {
         "metric": METRIC,
         "value": tok_s,
@@ -640,7 +644,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": workload, "global_batch": B, "layers": L, "tokens": K * B,
                    "path": "rvq_moe_route_forward" if args.path == "fused"
-                   else "rvq_moe_route_topk + rvq_moe_layer_forward"},
+                   else "rvq_moe_route_topk + rvq_moe_layer_forward",
+                   "combine": "fixed order" if args.deterministic else "fp32 atomics"},
         "layer_calls_per_s": calls_s,
         "compressed_GBps": gbps,
         "hbm_frac": gbps / HBM_PEAK_GBPS,
