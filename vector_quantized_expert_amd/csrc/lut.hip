@@ -786,6 +786,44 @@ __device__ void build_order(const int32_t *ids, const int *lds_ids, int P, int E
 // First unit of range r when n units are split over G workgroups.
 __device__ inline int range_lo(int n, int r, int G) { return (int)((int64_t)n * r / G); }
 
+// How a phase's units reach the workgroups.  Contiguous: one range each (range
+// index rw, consecutive ranges on one XCD).  Strided, for the grouped orders:
+// the units form blocks -- all chunks of one (pair, matrix tile), one table
+// each -- and each XCD takes a contiguous eighth of the blocks and deals them
+// round-robin to its workgroups.  The blocks of an expert group's tokens are
+// consecutive, so those tokens stream the same code tile at the same time on
+// one XCD and the re-reads hit its L2 (with contiguous ranges each workgroup
+// re-reads a 192-672 KB tile after its XCD has streamed ~32 such tiles, more
+// than the L2 holds).  Taken when every workgroup gets at least 4 blocks.
+struct Deal {
+    bool strided = false;
+    int blk = 0, blk1 = 0, step = 1, n_c = 1;
+    // the first span [u, u1) of this workgroup
+    __device__ void start(bool grouped, int n_blocks, int n_chunks, int rw, int &u, int &u1) {
+        const int G = gridDim.x, wg = blockIdx.x;
+        strided = grouped && G % 8 == 0 && n_blocks >= 4 * G;
+        if (strided) {
+            n_c = n_chunks;
+            step = G / 8;
+            blk = range_lo(n_blocks, wg % 8, 8) + wg / 8;
+            blk1 = range_lo(n_blocks, wg % 8 + 1, 8);
+            u = blk * n_c;
+            u1 = blk < blk1 ? u + n_c : u;
+        } else {
+            const int n = n_blocks * n_chunks;
+            u = range_lo(n, rw, G);
+            u1 = range_lo(n, rw + 1, G);
+        }
+    }
+    // after the span ended: the next one (strided), or false
+    __device__ bool next(int &u, int &u1) {
+        if (!strided || (blk += step) >= blk1) return false;
+        u = blk * n_c;
+        u1 = u + n_c;
+        return true;
+    }
+};
+
 // Work units (one chunk of one pair's matrix tile) are numbered in 32 bits:
 // a call has fewer than 2^31 of them (checked when the handle is opened).
 __device__ inline SegA seg_a(int u, int u1, int n_ti, int n_cf, const Order &o) {
@@ -1140,13 +1178,13 @@ __global__ __launch_bounds__(kBlock) void k_layer(LayerArgs a) {
     // launch does while it waits for the logits.  The segment's expert is read
     // once the ids are known.
     const bool tab_order = kList || (a.T > 1 && P <= kOrderMax);
-    const int nA_units = (int)((int64_t)P * 2 * n_ti * n_cf);
     int uA = 0, uA1 = 0;
+    Deal dealA;
     SegA firstA{};
     bool firstA_placed = false;
     auto place_a = [&]() {
-        uA = range_lo(nA_units, rw, G);
-        uA1 = range_lo(nA_units, rw + 1, G);
+        // (the streaming-load instances serve the pair order only: no strided code there)
+        dealA.start(!kNT && tab_order, P * 2 * n_ti, n_cf, rw, uA, uA1);
         if (kRoute && !tab_order && uA < uA1) {
             Order pos_only{};  // no table; its expert lookups read the (not yet routed) LDS ids
             pos_only.tab = false;
@@ -1243,7 +1281,7 @@ __global__ __launch_bounds__(kBlock) void k_layer(LayerArgs a) {
     // ---------------- phase A: gate and up
     {
         int u = uA;
-        const int u1 = uA1;
+        int u1 = uA1;
         float xv = 0.f;  // this thread's raw input element of the segment's tile
         auto prefetch = [&](const SegA &sg) {
             if (sg.e >= 0 && sg.e < g.E) cb_load<CB>(cb, a.cbs, a.cb_exp, sg.e, sg.m);
@@ -1285,8 +1323,11 @@ __global__ __launch_bounds__(kBlock) void k_layer(LayerArgs a) {
         }
         while (u < u1) {
             const int un = u + (cur.c1 - cur.c0);
+            int nu = un, nu1 = u1;  // the next segment's span
+            if constexpr (!kNT)
+                if (un >= u1) dealA.next(nu, nu1);
             SegA nxt{};
-            if (un < u1) nxt = next_a(cur, un, u1, n_ti, n_cf, ord);
+            if (nu < nu1) nxt = nu == un ? next_a(cur, un, u1, n_ti, n_cf, ord) : seg_a(nu, nu1, n_ti, n_cf, ord);
             if (cur.e >= 0 && cur.e < g.E) {
                 const uint8_t *base = expert_record(a, cur.e) + g.m[cur.m].off +
                                       (int64_t)cur.tile * n_cf * kChunkBytes;
@@ -1314,7 +1355,7 @@ __global__ __launch_bounds__(kBlock) void k_layer(LayerArgs a) {
                 if (flush) count(pend_p, pend_n);
                 if (pend_out && !y_signalled) publish();
                 __syncthreads();
-                if (un < u1) prefetch(nxt);
+                if (nu < nu1) prefetch(nxt);
                 float *out = a.part_gu + (((int64_t)cur.p * 2 + cur.m) * n_ti + cur.tile) * g.ffn_pad;
                 Stage st = ast;
                 if (merge) st = Stage{hst + cur.c0 * kChunkRows, kChunkRows, ast.cap - cur.c0, true};
@@ -1342,10 +1383,11 @@ __global__ __launch_bounds__(kBlock) void k_layer(LayerArgs a) {
                     pend_out = nullptr;
                 }
                 count(cur.p, cur.c1 - cur.c0);
-                if (un < u1) prefetch(nxt);
+                if (nu < nu1) prefetch(nxt);
             }
             cur = nxt;
-            u = un;
+            u = nu;
+            u1 = nu1;
         }
         if (pend_out) {
             __syncthreads();
@@ -1357,9 +1399,9 @@ __global__ __launch_bounds__(kBlock) void k_layer(LayerArgs a) {
 
     // ---------------- phase B: SwiGLU finish, gate, down
     {
-        const int nB = P * n_tf * n_cd;
-        int u = range_lo(nB, rw, G);
-        const int u1 = range_lo(nB, rw + 1, G);
+        int u, u1;
+        Deal dealB;
+        dealB.start(!kNT && ord.tab, P * n_tf, n_cd, rw, u, u1);
         const int needA = 2 * n_ti * n_cf;
         SegB cur{};
         if (u < u1) {
@@ -1368,8 +1410,11 @@ __global__ __launch_bounds__(kBlock) void k_layer(LayerArgs a) {
         }
         while (u < u1) {
             const int un = u + (cur.c1 - cur.c0);
+            int nu = un, nu1 = u1;  // the next segment's span
+            if constexpr (!kNT)
+                if (un >= u1) dealB.next(nu, nu1);
             SegB nxt{};
-            if (un < u1) nxt = next_b(cur, un, u1, n_tf, n_cd, ord);
+            if (nu < nu1) nxt = nu == un ? next_b(cur, un, u1, n_tf, n_cd, ord) : seg_b(nu, nu1, n_tf, n_cd, ord);
             if (cur.e >= 0 && cur.e < g.E) {
                 const uint8_t *base = expert_record(a, cur.e) + g.m[2].off +
                                       (int64_t)cur.ft * n_cd * kChunkBytes;
@@ -1391,7 +1436,7 @@ __global__ __launch_bounds__(kBlock) void k_layer(LayerArgs a) {
                 __syncthreads();
                 build_lut<CB>(lut, vs, tile_exponent(red2), cb.ec);
                 __syncthreads();
-                if (un < u1 && nxt.e >= 0 && nxt.e < g.E) cb_load<CB>(cb, a.cbs, a.cb_exp, nxt.e, 2);
+                if (nu < nu1 && nxt.e >= 0 && nxt.e < g.E) cb_load<CB>(cb, a.cbs, a.cb_exp, nxt.e, 2);
                 if (!y_ready) {
                     wait_count(a.ycnt, G, a.err);
                     y_ready = true;
@@ -1412,11 +1457,12 @@ __global__ __launch_bounds__(kBlock) void k_layer(LayerArgs a) {
                 if (cur.ft == 0 && !kDet)  // (the deterministic combine poisons the token itself)
                     for (int r = cur.c0 * kChunkRows + threadIdx.x; r < min(g.d, cur.c1 * kChunkRows); r += kBlock)
                         unsafeAtomicAdd(a.y + (size_t)(cur.p / g.k) * g.d + r, __int_as_float(0x7fc00000));
-                if (un < u1 && nxt.e >= 0 && nxt.e < g.E) cb_load<CB>(cb, a.cbs, a.cb_exp, nxt.e, 2);
+                if (nu < nu1 && nxt.e >= 0 && nxt.e < g.E) cb_load<CB>(cb, a.cbs, a.cb_exp, nxt.e, 2);
             }
             __syncthreads();
             cur = nxt;
-            u = un;
+            u = nu;
+            u1 = nu1;
         }
     }
     // the other counter set starts the next launch at zero (see kCntSets)
