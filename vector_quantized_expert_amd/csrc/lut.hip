@@ -587,8 +587,7 @@ __device__ inline double token_r(const LayerArgs &a, int t, int &r_tok, double &
     const float *xt = a.x + (size_t)t * a.g.d;
     double ss = 0.0;
     for (int i = threadIdx.x; i < a.g.d; i += kBlock) ss = fma((double)xt[i], (double)xt[i], ss);
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
+    ss = wave_sum(ss);  // DPP and lane swaps: no LDS round trips
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
     __syncthreads();
     double tot = 0.0;
@@ -1003,8 +1002,11 @@ __device__ void select_top_local(const double *lg, int E, int k, double *sel_out
 //      each, summed in rank order); workgroup 0 writes ids and gates out.
 constexpr int kRouteExp = kRouteExperts;  // experts per workgroup (E <= 4 G)
 // `idle` runs once R1 is published, before the wait for the other logits.
+// With normalisation, r_tok / r_val receive the last token's RMS divisor (the
+// one its logits were divided by), so that the experts' token_r() reuses it.
 template <class Idle>
-__device__ void route_phase(const LayerArgs &a, double *scratch, float *gate_lds, int *pair_ids, Idle &&idle) {
+__device__ void route_phase(const LayerArgs &a, double *scratch, float *gate_lds, int *pair_ids, int &r_tok,
+                            double &r_val, Idle &&idle) {
     const Geometry &g = a.g;
     const int G = gridDim.x, wg = blockIdx.x;
     const int lane = threadIdx.x & 63, wave = wave_id();
@@ -1018,6 +1020,7 @@ __device__ void route_phase(const LayerArgs &a, double *scratch, float *gate_lds
     // ---- R1
     // own experts of this workgroup (wave-uniform): loads only for those
     const int n_own = min(kRouteExp, (g.E - wg + G - 1) / G);
+    __shared__ double r_share;  // the token's divisor, for the experts
     for (int t = 0; t < a.T; t++) {
         const float4 *x4 = reinterpret_cast<const float4 *>(a.x + (size_t)t * g.d);
         double acc[kRouteExp], ss = 0.0;
@@ -1075,7 +1078,16 @@ __device__ void route_phase(const LayerArgs &a, double *scratch, float *gate_lds
             const double r = a.pre ? sqrt(sq / (double)g.d + a.eps) : 1.0;
             store_coherent(a.rl_cur + (size_t)t * g.E + e, sa / r);
         }
+        if (a.pre && threadIdx.x == 0) {  // (also where this workgroup owns no expert)
+            double sq = 0.0;
+            for (int w = 0; w < kWaves; w++) sq += red[w * (kRouteExp + 1) + kRouteExp];
+            r_share = sqrt(sq / (double)g.d + a.eps);
+        }
         __syncthreads();
+        if (a.pre) {
+            r_tok = t;
+            r_val = r_share;
+        }
     }
     // The other buffer goes back to the marker for the next routed call: the
     // logit slots of this workgroup's experts that the previous routed call
@@ -1195,7 +1207,7 @@ __global__ __launch_bounds__(kBlock) void k_layer(LayerArgs a) {
     };
     if (kRoute) {
         // the routing scratch reuses the table area, which is idle until phase A
-        route_phase(a, reinterpret_cast<double *>(lut), gate_lds, pair_ids, place_a);
+        route_phase(a, reinterpret_cast<double *>(lut), gate_lds, pair_ids, r_tok, r_val, place_a);
         gate_src = gate_lds;
     } else {
         place_a();
