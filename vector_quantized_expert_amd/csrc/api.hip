@@ -115,7 +115,6 @@ static void free_handle(rvq_moe *h) {
     (void)hipFree(h->cw.X);
     (void)hipFree(h->cw.H);
     (void)hipFree(h->cw.perm);
-    (void)hipFree(h->cw.pos_of);
     (void)hipFree(h->cw.grp_off);
     (void)hipFree(h->cw.act);
     (void)hipFree(h->cw.list);
@@ -170,10 +169,9 @@ static int open_impl(const rvq_moe_desc *desc, rvq_moe *h) {
         h->cw.part_y = h->ws.part_y;
     }
     if (h->max_tokens >= h->chunk_min) {
-        HIP_TRY(hipMalloc(&h->cw.X, 2 * (size_t)(P * D.d)));
+        HIP_TRY(hipMalloc(&h->cw.X, 2 * (size_t)(T * D.d)));
         HIP_TRY(hipMalloc(&h->cw.H, 2 * (size_t)(P * D.ffn)));
         HIP_TRY(hipMalloc(&h->cw.perm, sizeof(int) * (size_t)P));
-        HIP_TRY(hipMalloc(&h->cw.pos_of, sizeof(int) * (size_t)P));
         HIP_TRY(hipMalloc(&h->cw.grp_off, sizeof(int) * (size_t)(E + 2)));
         HIP_TRY(hipMalloc(&h->cw.act, sizeof(int) * (size_t)(E + 1)));
         HIP_TRY(hipMalloc(&h->cw.list, sizeof(int) * (size_t)kPairListInts));

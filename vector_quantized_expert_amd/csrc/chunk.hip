@@ -8,15 +8,15 @@
 // rebuilt (fp32 sum of the three entries, rounded to bf16) and fed to
 // v_mfma_f32_32x32x16_bf16 with fp32 accumulation; tokens are rounded to bf16
 // (RNE) once, and so is the SwiGLU output h.  Pages "Lecture anticipée"
-// (a chunk of tokens touches most experts): the tokens are permuted so that
-// each expert's tokens are contiguous and every code tile is read once per
-// group of up to 64 tokens.
+// (a chunk of tokens touches most experts): the (token, expert) pairs are
+// ordered by expert, so that every code tile is read once per group of up to
+// 64 tokens.
 //
 // Steps (one launch each, all asynchronous on the caller's stream):
 //   prep   ids -> per-expert counts, offsets, the permutation and the list of
 //          experts for the matrix cores (one workgroup); experts with few
 //          tokens are listed for the table path instead (adaptive dispatch);
-//   stage  x -> bf16 rows in permuted order (RMS-normalised first when asked);
+//   stage  x -> one bf16 row per token (RMS-normalised first when asked);
 //          y <- x (residual) or 0, NaN for a token with an invalid id;
 //   gu     per (expert, 64 output rows): gate and up tiles -> h = silu(a) b in bf16;
 //   down   per (expert, 128 output rows): h W_d^T scaled by the gate, added into y.
@@ -55,8 +55,8 @@ constexpr int kXRow = kTileSlices * kVec + 8;  // bf16 per staged token row (pad
 // << 16, pair, expert.
 __global__ __launch_bounds__(1024) void k_chunk_prep(const int32_t *__restrict__ ids, int P, int E, int lut_tokens,
                                                      int *__restrict__ grp_off, int *__restrict__ perm,
-                                                     int *__restrict__ pos_of, int *__restrict__ act,
-                                                     int *__restrict__ list, int *__restrict__ err) {
+                                                     int *__restrict__ act, int *__restrict__ list,
+                                                     int *__restrict__ err) {
     __shared__ int cnt[kMaxExperts + 1];
     __shared__ int off[kMaxExperts + 2];
     __shared__ int aoff[kMaxExperts + 1];
@@ -138,7 +138,6 @@ __global__ __launch_bounds__(1024) void k_chunk_prep(const int32_t *__restrict__
         if (e < 0 || e >= E) e = E;
         const int pos = atomicAdd(&off[e], 1);
         perm[pos] = p;
-        pos_of[p] = pos;
         if (e < E && lpos[e] >= 0) {
             const int lp = lpos[e] + (pos - gstart[e]);
             list[1 + lp] = lpos[e] | (cnt[e] << 16);
@@ -149,16 +148,17 @@ __global__ __launch_bounds__(1024) void k_chunk_prep(const int32_t *__restrict__
 }
 
 // ---------------------------------------------------------------------------
-// stage: grid (T), 256 threads.  X[pos][i] = bf16(x_hat[t][i]) for the k
-// positions of token t; y[t] = x[t] (residual) or 0, or NaN if one of the
-// token's ids is invalid.
+// stage: grid (T), 256 threads.  X[t][i] = bf16(x_hat[t][i]), one row per
+// token (the gate/up kernel finds a position's row through its pair); y[t] =
+// x[t] (residual) or 0, or NaN if one of the token's ids is invalid.  Eight
+// elements per thread and step: 16-byte stores.
+typedef unsigned int ck_u4 __attribute__((ext_vector_type(4)));
 __global__ __launch_bounds__(kCkThreads) void k_chunk_stage(const float *__restrict__ x, int d, int k, int pre,
                                                             double eps, int residual, int E,
-                                                            const int32_t *__restrict__ ids,
-                                                            const int *__restrict__ pos_of, __bf16 *__restrict__ X,
+                                                            const int32_t *__restrict__ ids, __bf16 *__restrict__ X,
                                                             float *__restrict__ y, int init_y) {
     const int t = blockIdx.x;
-    const float *xt = x + (size_t)t * d;
+    const float4 *xt = reinterpret_cast<const float4 *>(x + (size_t)t * d);
     __shared__ double red[kCkThreads / 64];
     __shared__ int bad;
     double r = 1.0;
@@ -168,24 +168,41 @@ __global__ __launch_bounds__(kCkThreads) void k_chunk_stage(const float *__restr
         const int e = ids[(size_t)t * k + threadIdx.x];
         if (e < 0 || e >= E) bad = 1;
     }
+    const int n8 = d / kVec;  // d is a multiple of 8
     if (pre) {
         double ss = 0.0;
-        for (int i = threadIdx.x; i < d; i += kCkThreads) ss = fma((double)xt[i], (double)xt[i], ss);
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
+        for (int q = threadIdx.x; q < 2 * n8; q += kCkThreads) {
+            const float4 v = xt[q];
+            ss = fma((double)v.x, (double)v.x, ss);
+            ss = fma((double)v.y, (double)v.y, ss);
+            ss = fma((double)v.z, (double)v.z, ss);
+            ss = fma((double)v.w, (double)v.w, ss);
+        }
+        ss = wave_sum(ss);
         if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
     }
     __syncthreads();
     if (pre) r = sqrt((red[0] + red[1] + red[2] + red[3]) / (double)d + eps);
     const float poison = bad ? __int_as_float(0x7fc00000) : 0.f;
-    if (init_y)  // (with the deterministic combine, y is written after the contractions)
-        for (int i = threadIdx.x; i < d; i += kCkThreads) y[(size_t)t * d + i] = (residual ? xt[i] : 0.f) + poison;
-    for (int j = 0; j < k; j++) {
-        __bf16 *dst = X + (size_t)pos_of[(size_t)t * k + j] * d;
-        for (int i = threadIdx.x; i < d; i += kCkThreads) {
-            const float v = pre ? (float)((double)xt[i] / r) : xt[i];
-            dst[i] = (__bf16)v;
+    float4 *yt = reinterpret_cast<float4 *>(y + (size_t)t * d);
+    ck_u4 *Xt = reinterpret_cast<ck_u4 *>(X + (size_t)t * d);
+    for (int q = threadIdx.x; q < n8; q += kCkThreads) {
+        const float4 lo = xt[2 * q], hi = xt[2 * q + 1];
+        if (init_y) {  // (with the deterministic combine, y is written after the contractions)
+            yt[2 * q] = residual ? float4{lo.x + poison, lo.y + poison, lo.z + poison, lo.w + poison}
+                                 : float4{poison, poison, poison, poison};
+            yt[2 * q + 1] = residual ? float4{hi.x + poison, hi.y + poison, hi.z + poison, hi.w + poison}
+                                     : float4{poison, poison, poison, poison};
         }
+        const float v[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+        __bf16 b[8];
+#pragma unroll
+        for (int i = 0; i < 8; i++) b[i] = (__bf16)(pre ? (float)((double)v[i] / r) : v[i]);
+        ck_u4 w;
+#pragma unroll
+        for (int i = 0; i < 4; i++)
+            w[i] = (uint32_t)__builtin_bit_cast(uint16_t, b[2 * i]) | ((uint32_t)__builtin_bit_cast(uint16_t, b[2 * i + 1]) << 16);
+        Xt[q] = w;
     }
 }
 
@@ -259,7 +276,7 @@ __device__ inline bf16x8 ck_weights(const uint8_t *blk, const char *cb, int kk, 
 }
 
 // The token rows of a pass, one 256-wide input tile at a time: rows [p0, p0
-// + 32 * NT) of the permuted bf16 matrix src [P][ld], columns [c0, c0 + 256),
+// + 32 * NT) of a pass over the bf16 matrix src (see ck_row_offsets), columns [c0, c0 + 256),
 // loaded into registers (all of a thread's 16-byte loads in flight together)
 // and later stored into LDS rows of kXRow; rows at or past p_end and columns
 // at or past n_cols are zero.  Split so that the next tile's rows are in
@@ -271,17 +288,32 @@ struct CkRows {
     w4 v[kPer];
 };
 
+// Element offset in src of each row this thread stages (-1 past p_end): row
+// p of the pass, or with a row map the row of the token of the pair at
+// position p (map[p] / div).  The same for every input tile of a pass.
 template <int NT>
-__device__ inline void ck_load_rows(CkRows<NT> &r, const __bf16 *src, int ld, int p0, int p_end, int c0, int n_cols) {
+struct CkRowOff {
+    int64_t o[CkRows<NT>::kPer];
+};
+template <int NT>
+__device__ inline void ck_row_offsets(CkRowOff<NT> &ro, int ld, int p0, int p_end, const int *map, int div) {
+#pragma unroll
+    for (int i = 0; i < CkRows<NT>::kPer; i++) {
+        const int p = p0 + ((threadIdx.x + i * kCkThreads) >> 5);
+        ro.o[i] = p < p_end ? (int64_t)(map ? map[p] / div : p) * ld : -1;
+    }
+}
+
+template <int NT>
+__device__ inline void ck_load_rows(CkRows<NT> &r, const __bf16 *src, const CkRowOff<NT> &ro, int c0, int n_cols) {
     using R = CkRows<NT>;
 #pragma unroll
     for (int i = 0; i < R::kPer; i++) {
-        const int u = threadIdx.x + i * kCkThreads, row = u >> 5, piece = u & 31;
-        const int p = p0 + row, col = c0 + piece * 8;
+        const int col = c0 + ((threadIdx.x + i * kCkThreads) & 31) * 8;
         r.v[i] = typename R::w4{0u, 0u, 0u, 0u};
         // d and ffn are multiples of 8, so a piece lies wholly inside or outside the row
-        if (p < p_end && col + 8 <= n_cols)
-            r.v[i] = *global_view(reinterpret_cast<const typename R::w4 *>(src + (size_t)p * ld + col));
+        if (ro.o[i] >= 0 && col + 8 <= n_cols)
+            r.v[i] = *global_view(reinterpret_cast<const typename R::w4 *>(src + ro.o[i] + col));
     }
 }
 
@@ -322,7 +354,7 @@ struct ChunkArgs {
     int a0, a1;                      // active experts act[a0 .. a1)
     const void *cbs;
     const int *grp_off, *act, *perm;
-    const __bf16 *X;  // [P][d] permuted bf16 tokens
+    const __bf16 *X;  // [T][d] bf16 tokens (a position's row: X[perm[pos] / k])
     __bf16 *H;        // [P][ffn] permuted bf16 SwiGLU outputs
     const float *gates;
     float *y;
@@ -338,23 +370,25 @@ struct ChunkArgs {
 // barrier, then 16 K-steps.  LDS: xs [32 * NT][kXRow], code_blk [3072].
 template <int CB, int NT>
 __device__ inline void ck_contract(f32x16c (&acc)[NT], const __bf16 *src, int ld, int n_cols, int p0, int g1,
-                                   const uint8_t *mat, const MatGeom &mg, int chunk, bool chunk_ok, const char *cb,
-                                   __bf16 *xs, uint8_t *code_blk, int lane) {
+                                   const int *row_map, int row_div, const uint8_t *mat, const MatGeom &mg, int chunk,
+                                   bool chunk_ok, const char *cb, __bf16 *xs, uint8_t *code_blk, int lane) {
 #pragma unroll
     for (int mt = 0; mt < NT; mt++)
 #pragma unroll
         for (int v = 0; v < 16; v++) acc[mt][v] = 0.f;
     ck_w4 cr[3];
     CkRows<NT> xr;
+    CkRowOff<NT> ro;
+    ck_row_offsets<NT>(ro, ld, p0, g1, row_map, row_div);
     ck_load_codes(cr, mat + (int64_t)chunk * kChunkBytes, chunk_ok, lane);
-    ck_load_rows<NT>(xr, src, ld, p0, g1, 0, n_cols);
+    ck_load_rows<NT>(xr, src, ro, 0, n_cols);
     for (int kt = 0; kt < mg.n_tiles; kt++) {
         __syncthreads();  // the previous tile's LDS reads are done
         ck_store_rows<NT>(xs, xr);
         ck_store_codes(code_blk, cr, lane);
         if (kt + 1 < mg.n_tiles) {
             ck_load_codes(cr, mat + ((int64_t)(kt + 1) * mg.n_chunks + chunk) * kChunkBytes, chunk_ok, lane);
-            ck_load_rows<NT>(xr, src, ld, p0, g1, (kt + 1) * kTileSlices * kVec, n_cols);
+            ck_load_rows<NT>(xr, src, ro, (kt + 1) * kTileSlices * kVec, n_cols);
         }
         __syncthreads();
 #pragma unroll 2
@@ -401,8 +435,8 @@ __global__ __launch_bounds__(kCkThreads) void k_chunk_gu(ChunkArgs A) {
     auto pass = [&](int p0, auto nt_c) {
         constexpr int NT = decltype(nt_c)::value;
         f32x16c acc[NT];
-        ck_contract<CB, NT>(acc, A.X, g.d, g.d, p0, g1, mat, mg, chunk, chunk_ok, cb_lds[m], xs, code_lds[wave],
-                            lane);
+        ck_contract<CB, NT>(acc, A.X, g.d, g.d, p0, g1, A.perm, g.k, mat, mg, chunk, chunk_ok, cb_lds[m], xs,
+                            code_lds[wave], lane);
         // h = silu(gate) * up: the up waves hand their tiles to the gate waves
         __syncthreads();
         float *ex = reinterpret_cast<float *>(xs);  // [2 chunks][NT][16][64]
@@ -460,8 +494,8 @@ __global__ __launch_bounds__(kCkThreads) void k_chunk_down(ChunkArgs A) {
     auto pass = [&](int p0, auto nt_c) {
         constexpr int NT = decltype(nt_c)::value;
         f32x16c acc[NT];
-        ck_contract<CB, NT>(acc, A.H, g.ffn, g.ffn, p0, g1, mat, mg, chunk, chunk_ok, cb_lds, hs, code_lds[wave],
-                            lane);
+        ck_contract<CB, NT>(acc, A.H, g.ffn, g.ffn, p0, g1, nullptr, 1, mat, mg, chunk, chunk_ok, cb_lds, hs,
+                            code_lds[wave], lane);
         if (chunk_ok) {
             const int row = chunk * kChunkRows + (lane & 31);
 #pragma unroll
@@ -493,11 +527,11 @@ hipError_t launch_chunk_prep(const Geometry &g, const ChunkWork &cw, const float
                              int T, int pre, int residual, double eps, int lut_tokens, int *err, hipStream_t s) {
     const int P = T * g.k;
     hipLaunchKernelGGL(k_chunk_prep, dim3(1), dim3(1024), 0, s, ids, P, g.E, lut_tokens, cw.grp_off, cw.perm,
-                       cw.pos_of, cw.act, cw.list, err);
+                       cw.act, cw.list, err);
     hipError_t rc = hipGetLastError();
     if (rc != hipSuccess) return rc;
     hipLaunchKernelGGL(k_chunk_stage, dim3(T), dim3(kCkThreads), 0, s, x, g.d, g.k, pre, eps, residual, g.E, ids,
-                       cw.pos_of, cw.X, y, cw.det ? 0 : 1);
+                       cw.X, y, cw.det ? 0 : 1);
     return hipGetLastError();
 }
 

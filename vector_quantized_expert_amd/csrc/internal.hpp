@@ -166,10 +166,9 @@ struct Workspace {
 
 // Chunk-path workspace (device), sized for max_tokens * k pairs.
 struct ChunkWork {
-    __bf16 *X;     // [P][d] tokens in expert-grouped order, bf16
-    __bf16 *H;     // [P][ffn] SwiGLU outputs in the same order, bf16
+    __bf16 *X;     // [T][d] tokens (normalised), bf16
+    __bf16 *H;     // [P][ffn] SwiGLU outputs in expert-grouped order, bf16
     int *perm;     // [P] position -> pair
-    int *pos_of;   // [P] pair -> position
     int *grp_off;  // [E + 2] group offsets (group E: invalid ids)
     int *act;      // [E + 1] experts on the matrix cores, then their count at [E]
     int *list;     // [kPairListInts] pairs handed to the table path (see below)
