@@ -118,6 +118,9 @@ static void free_handle(rvq_moe *h) {
     (void)hipFree(h->cw.grp_off);
     (void)hipFree(h->cw.act);
     (void)hipFree(h->cw.list);
+    if (h->cw.fork) (void)hipEventDestroy(h->cw.fork);
+    if (h->cw.join) (void)hipEventDestroy(h->cw.join);
+    if (h->cw.side) (void)hipStreamDestroy(h->cw.side);
     for (hipEvent_t e : h->prof_pool) (void)hipEventDestroy(e);
     slots_close(h->cache);
     delete h;
@@ -175,6 +178,11 @@ static int open_impl(const rvq_moe_desc *desc, rvq_moe *h) {
         HIP_TRY(hipMalloc(&h->cw.grp_off, sizeof(int) * (size_t)(E + 2)));
         HIP_TRY(hipMalloc(&h->cw.act, sizeof(int) * (size_t)(E + 1)));
         HIP_TRY(hipMalloc(&h->cw.list, sizeof(int) * (size_t)kPairListInts));
+        if (!h->streaming) {  // (default priority, like every stream here)
+            HIP_TRY(hipStreamCreateWithFlags(&h->cw.side, hipStreamNonBlocking));
+            HIP_TRY(hipEventCreateWithFlags(&h->cw.fork, hipEventDisableTiming));
+            HIP_TRY(hipEventCreateWithFlags(&h->cw.join, hipEventDisableTiming));
+        }
     }
     int n_cu = 0;
     HIP_TRY(hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, h->device));

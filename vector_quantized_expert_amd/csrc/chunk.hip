@@ -542,19 +542,35 @@ hipError_t launch_chunk_experts(const Geometry &g, const ChunkWork &cw, const ui
     ChunkArgs A{codes, slot_tab, a0, a1, cbs, cw.grp_off, cw.act, cw.perm, cw.X, cw.H, gates, y,
                 cw.det ? cw.part_y : nullptr, g};
     const dim3 ggu((g.m[0].n_chunks + 1) / 2, a1 - a0), gdn((g.m[2].n_chunks + 3) / 4, a1 - a0);
-    // each kernel pair takes the experts of its token class and skips the others
-    if (g.cb_dtype == 0) {
-        hipLaunchKernelGGL((k_chunk_gu<0, 1>), ggu, dim3(kCkThreads), 0, s, A);
-        hipLaunchKernelGGL((k_chunk_gu<0, 2>), ggu, dim3(kCkThreads), 0, s, A);
-        hipLaunchKernelGGL((k_chunk_down<0, 1>), gdn, dim3(kCkThreads), 0, s, A);
-        hipLaunchKernelGGL((k_chunk_down<0, 2>), gdn, dim3(kCkThreads), 0, s, A);
-    } else {
-        hipLaunchKernelGGL((k_chunk_gu<1, 1>), ggu, dim3(kCkThreads), 0, s, A);
-        hipLaunchKernelGGL((k_chunk_gu<1, 2>), ggu, dim3(kCkThreads), 0, s, A);
-        hipLaunchKernelGGL((k_chunk_down<1, 1>), gdn, dim3(kCkThreads), 0, s, A);
-        hipLaunchKernelGGL((k_chunk_down<1, 2>), gdn, dim3(kCkThreads), 0, s, A);
+    // Each kernel pair takes the experts of its token class and skips the
+    // others.  The pair for experts with more than 32 tokens has few
+    // workgroups that each run long (a handful of experts at 512 uniform
+    // tokens): with a side stream it runs beside the other pair (forked after
+    // the staging, joined before anything later on s) instead of after it.
+    hipStream_t big = s;
+    if (cw.side && !slot_tab) {
+        hipError_t e = hipEventRecord(cw.fork, s);
+        if (e == hipSuccess) e = hipStreamWaitEvent(cw.side, cw.fork, 0);
+        if (e != hipSuccess) return e;
+        big = cw.side;
     }
-    return hipGetLastError();
+    if (g.cb_dtype == 0) {
+        hipLaunchKernelGGL((k_chunk_gu<0, 2>), ggu, dim3(kCkThreads), 0, big, A);
+        hipLaunchKernelGGL((k_chunk_down<0, 2>), gdn, dim3(kCkThreads), 0, big, A);
+        hipLaunchKernelGGL((k_chunk_gu<0, 1>), ggu, dim3(kCkThreads), 0, s, A);
+        hipLaunchKernelGGL((k_chunk_down<0, 1>), gdn, dim3(kCkThreads), 0, s, A);
+    } else {
+        hipLaunchKernelGGL((k_chunk_gu<1, 2>), ggu, dim3(kCkThreads), 0, big, A);
+        hipLaunchKernelGGL((k_chunk_down<1, 2>), gdn, dim3(kCkThreads), 0, big, A);
+        hipLaunchKernelGGL((k_chunk_gu<1, 1>), ggu, dim3(kCkThreads), 0, s, A);
+        hipLaunchKernelGGL((k_chunk_down<1, 1>), gdn, dim3(kCkThreads), 0, s, A);
+    }
+    hipError_t e = hipGetLastError();
+    if (e == hipSuccess && big != s) {
+        e = hipEventRecord(cw.join, big);
+        if (e == hipSuccess) e = hipStreamWaitEvent(s, cw.join, 0);
+    }
+    return e;
 }
 
 hipError_t launch_chunk(const Geometry &g, const ChunkWork &cw, const uint8_t *codes, const void *cbs, const float *x,

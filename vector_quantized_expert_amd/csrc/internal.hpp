@@ -174,6 +174,10 @@ struct ChunkWork {
     int *list;     // [kPairListInts] pairs handed to the table path (see below)
     bool det;      // deterministic combine: pair outputs go to part_y [P][d_pad], combined by k_combine
     float *part_y;
+    // resident codes: the kernels for experts with more than 32 tokens (few
+    // workgroups, long-running) run on this stream, beside the others
+    hipStream_t side;
+    hipEvent_t fork, join;
 };
 
 // The table path's order table holds up to kOrderMax (token, expert) pairs.
