@@ -144,9 +144,10 @@ struct Workspace {
     double *logits;     // [T][E] fp64 router logits
     double *sel;        // [T][k] fp64 logits of the selected experts, by rank
     double *route_logits;  // router logit slots (route_logit_slots()); unpublished slots hold a marker NaN:
-                           // [max_tokens][E] for several tokens, then [2][E] logits and [2][kMaxTopK]
-                           // selected logits for one token (alternating buffers)
-    int64_t route_cap;     // max_tokens * E
+                           // route_cap values for several tokens ([S][T][E] parts), then [2][E] logits
+                           // and [2][kMaxTopK] selected logits for one token (alternating buffers)
+    int64_t route_cap;     // max(max_tokens, 256) * E
+    int64_t fused_cap;     // max_tokens * E: one of the two fused_logits buffers
     int route_parity;      // buffer of the next one-token call
     double *fused_logits;  // in-launch routing slots, fused_route_slots() doubles (marker NaN when unpublished)
     int fused_parity;      // buffer of the next in-launch routing

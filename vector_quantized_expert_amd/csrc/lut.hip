@@ -1559,7 +1559,7 @@ hipError_t launch_layer(const Geometry &g, Workspace &w, const uint8_t *codes, c
     double *rl_cur = nullptr, *rl_next = nullptr;
     int T_reset = 0;
     if (route) {  // the slot buffers (see fused_route_slots) alternate between calls
-        const int64_t cap = w.route_cap;
+        const int64_t cap = w.fused_cap;  // fused_route_slots() = 2 buffers of this many
         const int par = w.fused_parity;
         rl_cur = w.fused_logits + (par ? cap : 0);
         rl_next = w.fused_logits + (par ? 0 : cap);

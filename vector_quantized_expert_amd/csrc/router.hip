@@ -311,9 +311,11 @@ __device__ void router_dot(const float *__restrict__ x, const float *__restrict_
 // Several tokens, step 1: the logits as a dense fp64 contraction on the
 // matrix cores, L[t][e] = sum_i x[t][i] Wt[e][i] with v_mfma_f64_16x16x4_f64
 // (fp32 inputs widened exactly, so every product is exact; fp64 sums).  Grid
-// (ceil(E / 16), ceil(T / 16)), 256 threads: wave w takes a quarter of the
-// 16-wide input blocks of one 16 token x 16 expert tile and the four partial
-// tiles are summed in wave order.  Operands: lane l = 16 q + r loads 4
+// (ceil(E / 16), ceil(T / 16), S), 256 threads: the input dimension is split
+// into S parts (so that few tokens still fill the GPU) and each part into four,
+// one per wave of one 16 token x 16 expert tile; the four partial tiles are
+// summed in wave order and written to part s of logits ([S][T][E]), which the
+// selection sums in part order.  Operands: lane l = 16 q + r loads 4
 // consecutive inputs 16 b + 4 q .. + 3 of token row r and of expert row r;
 // MFMA step j pairs the j-th of them (A[r][q] = x, B[q][r] = w), so the four
 // steps of a block cover its 16 inputs once.  The accumulator v of lane l is
@@ -326,7 +328,9 @@ __global__ __launch_bounds__(256) void k_route_mm(const float *__restrict__ x, c
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, r = lane & 15, q = lane >> 4;
     const float *xr = x + (size_t)min(t0 + r, T - 1) * d;
     const float *wr = Wt + (size_t)min(e0 + r, E - 1) * d;
-    const int nb = (d + 15) / 16, b0 = nb * wave / 4, b1 = nb * (wave + 1) / 4;
+    const int nq = 4 * gridDim.z, qi = 4 * blockIdx.z + wave;  // this wave's quarter of part blockIdx.z
+    const int nb = (d + 15) / 16, b0 = (int)((int64_t)nb * qi / nq), b1 = (int)((int64_t)nb * (qi + 1) / nq);
+    logits += (size_t)blockIdx.z * T * E;
     f64x4 acc = {0.0, 0.0, 0.0, 0.0};
     constexpr int kU = 4;  // blocks per pass, loads in flight together
     for (int b = b0; b < b1; b += kU) {
@@ -361,7 +365,7 @@ __global__ __launch_bounds__(256) void k_route_mm(const float *__restrict__ x, c
 // largest (ties to the lower id) and forms the softmax gates over them (one exp
 // per selected logit, summed in slot order).
 __global__ __launch_bounds__(256) void k_route_sel(const float *__restrict__ x, int d, int E, int k, int pre,
-                                                   double eps, const double *__restrict__ logits,
+                                                   double eps, const double *__restrict__ logits, int S, int T,
                                                    int32_t *__restrict__ ids, float *__restrict__ gates) {
     const int t = blockIdx.x;
     __shared__ SelectLds L;
@@ -383,7 +387,10 @@ __global__ __launch_bounds__(256) void k_route_sel(const float *__restrict__ x, 
 #pragma unroll
     for (int r = 0; r < kSelPer; r++) {
         const int i = threadIdx.x + 256 * r;
-        v[r] = rank_value(i < E ? logits[(size_t)t * E + i] / rdiv : -INFINITY);
+        double l = 0.0;  // the S parts, in part order
+        if (i < E)
+            for (int s = 0; s < S; s++) l += logits[((size_t)s * T + t) * E + i];
+        v[r] = rank_value(i < E ? l / rdiv : -INFINITY);
         key[r] = order_key(v[r]);
     }
     select_topk(key, v, E, k, L, ids + (size_t)t * k, sel);
@@ -497,19 +504,31 @@ hipError_t launch_route(const Geometry &g, Workspace &w, const float *x, const f
     } else {
         // the logits area of the several-token path: plain values, handed from
         // the contraction to the selection across the launch boundary
-        double *lg = w.route_logits;  // [T][E]
-        hipLaunchKernelGGL(k_route_mm, dim3((g.E + 15) / 16, (T + 15) / 16), dim3(256), 0, s, x, Wt, g.d, g.E, T, lg);
+        double *lg = w.route_logits;  // [S][T][E]
+        // parts of the input dimension: enough workgroups for the GPU (~768),
+        // at most 16, within the area (route_cap slots)
+        const int tiles = ((g.E + 15) / 16) * ((T + 15) / 16);
+        int S = 1;
+        while (S < 16 && tiles * 2 * S <= 768 && (int64_t)2 * S * T * g.E <= w.route_cap && 2 * S * 4 <= g.d / 16)
+            S *= 2;
+        hipLaunchKernelGGL(k_route_mm, dim3((g.E + 15) / 16, (T + 15) / 16, S), dim3(256), 0, s, x, Wt, g.d, g.E, T,
+                           lg);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL(k_route_sel, dim3(T), dim3(256), 0, s, x, g.d, g.E, g.k, pre, eps, lg, ids, gates);
+        hipLaunchKernelGGL(k_route_sel, dim3(T), dim3(256), 0, s, x, g.d, g.E, g.k, pre, eps, lg, S, T, ids, gates);
     }
     return hipGetLastError();
 }
 
-int64_t route_logit_slots(int64_t max_tokens, int E) { return max_tokens * E + 2 * E + 2 * kMaxTopK; }
+// The several-token area holds max(max_tokens, 256) x E values (parts of the
+// input dimension for calls of up to 128 tokens), then the one-token path's
+// alternating slots.
+static int64_t route_cap(int64_t max_tokens, int E) { return (max_tokens > 256 ? max_tokens : 256) * E; }
+int64_t route_logit_slots(int64_t max_tokens, int E) { return route_cap(max_tokens, E) + 2 * E + 2 * kMaxTopK; }
 
 hipError_t init_route(Workspace &w, int E, int k, int64_t max_tokens, int n_cu, hipStream_t s) {
-    w.route_cap = max_tokens * E;
+    w.route_cap = route_cap(max_tokens, E);
+    w.fused_cap = max_tokens * E;
     w.route_parity = 0;
     // the one-token kernel needs all E workgroups resident together
     int per_cu = 0;
