@@ -307,6 +307,11 @@ int rvq_moe_route_topk(rvq_moe *h, const float *x, int32_t n_tokens, int32_t *id
  * grouped by expert, the weights are rebuilt as bf16(c1 + c2 + c3) tile by
  * tile in registers, and x_hat and h are rounded to bf16 for bf16 x bf16 ->
  * fp32 matrix-core products: expect ~1e-3 relative error instead of ~1e-6.
+ * With resident codes the chunk path runs the kernels of experts with more
+ * than 32 tokens on a stream the handle owns, forked from `stream` after the
+ * call's earlier work and joined back by events before anything enqueued on
+ * `stream` later: the call is ordered as if all of it ran on `stream` (also
+ * under stream capture).
  *   x      [n_tokens][d] fp32.   ids [n_tokens][k] int32.   gates [n_tokens][k] fp32.
  *   y      [n_tokens][d] fp32 out (must not alias x).
  * Ids outside [0, E) are detected on the device: the affected outputs are
