@@ -332,23 +332,35 @@ __global__ __launch_bounds__(256) void k_route_mm(const float *__restrict__ x, c
     const int nb = (d + 15) / 16, b0 = (int)((int64_t)nb * qi / nq), b1 = (int)((int64_t)nb * (qi + 1) / nq);
     logits += (size_t)blockIdx.z * T * E;
     f64x4 acc = {0.0, 0.0, 0.0, 0.0};
-    constexpr int kU = 4;  // blocks per pass, loads in flight together
-    for (int b = b0; b < b1; b += kU) {
-        float4 xv[kU], wv[kU];
+    // kU blocks per pass with all their loads in flight together; the next
+    // pass's loads are issued before this pass's products (two register sets)
+    constexpr int kU = 4;
+    float4 xv[2][kU], wv[2][kU];
+    auto load = [&](int set, int b) {
 #pragma unroll
         for (int u = 0; u < kU; u++) {
             const int i = (b + u) * 16 + 4 * q;
             const bool ok = b + u < b1 && i < d;  // d % 8 == 0: a 4-aligned start below d has all 4 below d
-            xv[u] = ok ? *reinterpret_cast<const float4 *>(xr + i) : make_float4(0.f, 0.f, 0.f, 0.f);
-            wv[u] = ok ? *reinterpret_cast<const float4 *>(wr + i) : make_float4(0.f, 0.f, 0.f, 0.f);
+            xv[set][u] = ok ? *reinterpret_cast<const float4 *>(xr + i) : make_float4(0.f, 0.f, 0.f, 0.f);
+            wv[set][u] = ok ? *reinterpret_cast<const float4 *>(wr + i) : make_float4(0.f, 0.f, 0.f, 0.f);
         }
+    };
+    auto products = [&](int set) {
 #pragma unroll
         for (int u = 0; u < kU; u++) {
-            acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)xv[u].x, (double)wv[u].x, acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)xv[u].y, (double)wv[u].y, acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)xv[u].z, (double)wv[u].z, acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)xv[u].w, (double)wv[u].w, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)xv[set][u].x, (double)wv[set][u].x, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)xv[set][u].y, (double)wv[set][u].y, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)xv[set][u].z, (double)wv[set][u].z, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)xv[set][u].w, (double)wv[set][u].w, acc, 0, 0, 0);
         }
+    };
+    if (b0 < b1) load(0, b0);
+    for (int b = b0; b < b1; b += 2 * kU) {  // the sets alternate with no copies between them
+        if (b + kU < b1) load(1, b + kU);
+        products(0);
+        if (b + kU >= b1) break;
+        if (b + 2 * kU < b1) load(0, b + 2 * kU);
+        products(1);
     }
     __shared__ double part[4][16][17];  // [wave][token][expert], padded
 #pragma unroll
