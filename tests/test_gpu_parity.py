@@ -627,6 +627,38 @@ def test_chunk_path_follows_the_oracle(torch_mod, d, ffn, E, k, cb, T):
     layer.close()
 
 
+def test_chunk_group_sizes_at_the_kernel_boundaries(torch_mod):
+    """Explicit ids put exactly 32 tokens on one expert (the largest group one
+    32-token tile holds), one token on another and 33 on a third (the kernels
+    for larger groups), on a shape with ragged input tiles both ways and row
+    chunks that leave most waves of the last workgroup past the matrix.  Every
+    token is within the bf16 bar of the fp64 oracle on the same experts and,
+    element by element, within the precision model's tolerance."""
+    import chunk_model as M
+    from synth import gpu as G
+    shape = S.Shape(520, 264, 4, 2, "f16")
+    T = 33
+    inp = G.LayerInputs(shape, seed=29, layer=0, host_codes=True)
+    layer = _layer(torch_mod, inp, shape, T, chunk_min_tokens=1, lut_expert_tokens=1)
+    x = S.tokens(29, 0, T, shape.d)
+    ids = np.zeros((T, 2), np.int32)
+    ids[:, 0] = 2          # expert 2: all 33 tokens
+    ids[:32, 1] = 0        # expert 0: exactly 32
+    ids[32, 1] = 1         # expert 1: one token (expert 3: none)
+    g = np.random.default_rng(29).uniform(0.2, 0.8, (T, 1))
+    gates = np.concatenate([g, 1.0 - g], axis=1).astype(np.float32)
+    y = _forward(torch_mod, layer, shape, x, ids, gates)
+    for t in range(T):
+        ref = O.moe(shape.d, shape.ffn, gates[t], [inp.codebook(int(e)) for e in ids[t]],
+                    [inp.record(int(e)) for e in ids[t]], x[t])
+        err = np.linalg.norm(y[t] - ref) / np.linalg.norm(ref)
+        assert err <= TOL_Y_BF16, (t, err)
+        ym, peak, mass = M.layer(x[t], ids[t], gates[t], inp.codebook, inp.record, shape.d, shape.ffn)
+        bad = np.nonzero(np.abs(y[t] - ym) > M.element_tolerance(peak, mass))[0]
+        assert bad.size == 0, (t, bad[:8], y[t][bad[:8]], ym[bad[:8]])
+    layer.close()
+
+
 @pytest.mark.parametrize("cb", ["f32", "f16"])
 def test_chunk_path_closed_form_element_by_element(torch_mod, cb):
     """Stage codebooks that are one-hot vectors scaled by 1, 2, 4 (signs per

@@ -93,6 +93,8 @@ Geometry make_geometry(int d, int ffn, int E, int k, int cb_dtype) {
     g.cb_bytes = (int64_t)3 * kStages * kCodes * kVec * (cb_dtype == 0 ? 4 : 2);
     g.ffn_pad = g.m[0].n_chunks * kChunkRows;
     g.d_pad = g.m[2].n_chunks * kChunkRows;
+    g.d_tpad = g.m[0].n_tiles * kTileSlices * kVec;
+    g.ffn_tpad = g.m[2].n_tiles * kTileSlices * kVec;
     return g;
 }
 
@@ -172,8 +174,10 @@ static int open_impl(const rvq_moe_desc *desc, rvq_moe *h) {
         h->cw.part_y = h->ws.part_y;
     }
     if (h->max_tokens >= h->chunk_min) {
-        HIP_TRY(hipMalloc(&h->cw.X, 2 * (size_t)(T * D.d)));
-        HIP_TRY(hipMalloc(&h->cw.H, 2 * (size_t)(P * D.ffn)));
+        HIP_TRY(hipMalloc(&h->cw.X, 2 * (size_t)(T * g.d_tpad)));
+        HIP_TRY(hipMalloc(&h->cw.H, 2 * (size_t)(P * g.ffn_tpad)));
+        HIP_TRY(hipMemsetAsync(h->cw.X, 0, 2 * (size_t)(T * g.d_tpad), s));  // the pad columns stay zero
+        HIP_TRY(hipMemsetAsync(h->cw.H, 0, 2 * (size_t)(P * g.ffn_tpad), s));
         HIP_TRY(hipMalloc(&h->cw.perm, sizeof(int) * (size_t)P));
         HIP_TRY(hipMalloc(&h->cw.grp_off, sizeof(int) * (size_t)(E + 2)));
         HIP_TRY(hipMalloc(&h->cw.act, sizeof(int) * (size_t)(E + 1)));

@@ -18,16 +18,20 @@
 //          tokens are listed for the table path instead (adaptive dispatch);
 //   stage  x -> one bf16 row per token (RMS-normalised first when asked);
 //          y <- x (residual) or 0, NaN for a token with an invalid id;
-//   gu     per (expert, 64 output rows): gate and up tiles -> h = silu(a) b in bf16;
-//   down   per (expert, 128 output rows): h W_d^T scaled by the gate, added into y.
+//   gu     per (expert, output rows): gate and up tiles -> h = silu(a) b in bf16;
+//   down   per (expert, output rows): h W_d^T scaled by the gate, added into y.
 //
-// MI355X mapping.  A workgroup is 4 waves; each wave owns one 32-row chunk of a
-// matrix and one or two 32-token tiles (accumulators in registers).  Per
-// 256-wide input tile the token tile is staged in LDS (shared by the 4 waves)
-// and each wave stages its 3 KB code block in LDS; a lane then forms exactly
-// the B operand it needs (row l % 32, 8 consecutive inputs of one slice): three
-// code bytes, three codebook entries from LDS, fp32 sum, RNE to bf16.  The
-// dense weight tile never exists in LDS or HBM.
+// MI355X mapping.  Each wave owns one 32-row chunk of a matrix and one or two
+// 32-token tiles (accumulators in registers); per K-step a lane forms exactly
+// the B operand it needs (row l % 32, 8 consecutive inputs of one slice):
+// three code bytes, three codebook entries from LDS, fp32 sum, RNE to bf16.
+// The dense weight tile never exists in LDS or HBM.  Two kernel families:
+//   - experts with at most 32 tokens, fp16 codebooks (nearly all of them in a
+//     512-token chunk): the replicated-codebook kernels below, one 16-wave
+//     workgroup per CU with the matrix's codebooks copied so that the entry
+//     reads do not collide on LDS banks;
+//   - the others (more than 32 tokens, or fp32 codebooks): 4-wave workgroups
+//     that stage each tile's token rows and per-wave code blocks in LDS.
 #include <math.h>
 
 #include <type_traits>
@@ -148,15 +152,16 @@ __global__ __launch_bounds__(1024) void k_chunk_prep(const int32_t *__restrict__
 }
 
 // ---------------------------------------------------------------------------
-// stage: grid (T), 256 threads.  X[t][i] = bf16(x_hat[t][i]), one row per
-// token (the gate/up kernel finds a position's row through its pair); y[t] =
+// stage: grid (T), 256 threads.  X[t][i] = bf16(x_hat[t][i]), one row of
+// stride x_ld per token (the gate/up kernel finds a position's row through its
+// pair; columns d .. x_ld stay zero); y[t] =
 // x[t] (residual) or 0, or NaN if one of the token's ids is invalid.  Eight
 // elements per thread and step: 16-byte stores.
 typedef unsigned int ck_u4 __attribute__((ext_vector_type(4)));
 __global__ __launch_bounds__(kCkThreads) void k_chunk_stage(const float *__restrict__ x, int d, int k, int pre,
                                                             double eps, int residual, int E,
                                                             const int32_t *__restrict__ ids, __bf16 *__restrict__ X,
-                                                            float *__restrict__ y, int init_y) {
+                                                            int x_ld, float *__restrict__ y, int init_y) {
     const int t = blockIdx.x;
     const float4 *xt = reinterpret_cast<const float4 *>(x + (size_t)t * d);
     __shared__ double red[kCkThreads / 64];
@@ -185,7 +190,7 @@ __global__ __launch_bounds__(kCkThreads) void k_chunk_stage(const float *__restr
     if (pre) r = sqrt((red[0] + red[1] + red[2] + red[3]) / (double)d + eps);
     const float poison = bad ? __int_as_float(0x7fc00000) : 0.f;
     float4 *yt = reinterpret_cast<float4 *>(y + (size_t)t * d);
-    ck_u4 *Xt = reinterpret_cast<ck_u4 *>(X + (size_t)t * d);
+    ck_u4 *Xt = reinterpret_cast<ck_u4 *>(X + (size_t)t * x_ld);
     for (int q = threadIdx.x; q < n8; q += kCkThreads) {
         const float4 lo = xt[2 * q], hi = xt[2 * q + 1];
         if (init_y) {  // (with the deterministic combine, y is written after the contractions)
@@ -242,29 +247,38 @@ __device__ inline f32x8 ck_entry(const char *cb, int s, int c) {
 // B operand of K-step kk (slices 2kk, 2kk+1 of the tile) for lane l: row
 // l % 32 of the chunk, slice 2kk + l / 32, 8 weights = bf16(c1 + c2 + c3).
 // blk: the chunk's 3 KB code block in LDS ([stage][half][slice][16 rows]).
+typedef unsigned int ck_u32x4 __attribute__((ext_vector_type(4)));
+
+// bf16(a + b + c) of three 8-wide fp16 entries, summed in fp32 by
+// mixed-precision fmas (an fp16 source times 1 plus an fp32 or fp16 addend:
+// one instruction per add, no separate conversions), the same values as
+// converting and adding.
+__device__ inline bf16x8 ck_sum3_f16(const ck_u32x4 &a, const ck_u32x4 &b, const ck_u32x4 &c) {
+    bf16x8 w;
+#pragma unroll
+    for (int q = 0; q < 4; q++) {
+        float lo, hi;
+        asm("v_fma_mix_f32 %0, %1, 1.0, %2 op_sel_hi:[1,0,1]" : "=v"(lo) : "v"(a[q]), "v"(b[q]));
+        asm("v_fma_mix_f32 %0, %1, 1.0, %2 op_sel:[1,0,1] op_sel_hi:[1,0,1]" : "=v"(hi) : "v"(a[q]), "v"(b[q]));
+        asm("v_fma_mix_f32 %0, %1, 1.0, %2 op_sel_hi:[1,0,0]" : "=v"(lo) : "v"(c[q]), "v"(lo));
+        asm("v_fma_mix_f32 %0, %1, 1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(hi) : "v"(c[q]), "v"(hi));
+        w[2 * q] = (__bf16)lo;
+        w[2 * q + 1] = (__bf16)hi;
+    }
+    return w;
+}
+
 template <int CB>
 __device__ inline bf16x8 ck_weights(const uint8_t *blk, const char *cb, int kk, int lane) {
     const int n = lane & 31, j = 2 * kk + (lane >> 5);
     const int o = (n >> 4) * 512 + j * 16 + (n & 15);
     bf16x8 w;
     if (CB == 1) {
-        // fp16 entries, summed in fp32 by mixed-precision fmas (an fp16 source
-        // times 1 plus an fp32 or fp16 addend: one instruction per add, no
-        // separate conversions), the same values as converting and adding
-        typedef unsigned int u32x4c __attribute__((ext_vector_type(4)));
-        const u32x4c a = *reinterpret_cast<const u32x4c *>(cb + blk[o] * CkCb<CB>::kEntryBytes);
-        const u32x4c b = *reinterpret_cast<const u32x4c *>(cb + (kCodes + blk[1024 + o]) * CkCb<CB>::kEntryBytes);
-        const u32x4c c = *reinterpret_cast<const u32x4c *>(cb + (2 * kCodes + blk[2048 + o]) * CkCb<CB>::kEntryBytes);
-#pragma unroll
-        for (int q = 0; q < 4; q++) {
-            float lo, hi;
-            asm("v_fma_mix_f32 %0, %1, 1.0, %2 op_sel_hi:[1,0,1]" : "=v"(lo) : "v"(a[q]), "v"(b[q]));
-            asm("v_fma_mix_f32 %0, %1, 1.0, %2 op_sel:[1,0,1] op_sel_hi:[1,0,1]" : "=v"(hi) : "v"(a[q]), "v"(b[q]));
-            asm("v_fma_mix_f32 %0, %1, 1.0, %2 op_sel_hi:[1,0,0]" : "=v"(lo) : "v"(c[q]), "v"(lo));
-            asm("v_fma_mix_f32 %0, %1, 1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(hi) : "v"(c[q]), "v"(hi));
-            w[2 * q] = (__bf16)lo;
-            w[2 * q + 1] = (__bf16)hi;
-        }
+        const ck_u32x4 a = *reinterpret_cast<const ck_u32x4 *>(cb + blk[o] * CkCb<CB>::kEntryBytes);
+        const ck_u32x4 b = *reinterpret_cast<const ck_u32x4 *>(cb + (kCodes + blk[1024 + o]) * CkCb<CB>::kEntryBytes);
+        const ck_u32x4 c =
+            *reinterpret_cast<const ck_u32x4 *>(cb + (2 * kCodes + blk[2048 + o]) * CkCb<CB>::kEntryBytes);
+        w = ck_sum3_f16(a, b, c);
     } else {
         const f32x8 a = ck_entry<CB>(cb, 0, blk[o]);
         const f32x8 b = ck_entry<CB>(cb, 1, blk[1024 + o]);
@@ -354,13 +368,47 @@ struct ChunkArgs {
     int a0, a1;                      // active experts act[a0 .. a1)
     const void *cbs;
     const int *grp_off, *act, *perm;
-    const __bf16 *X;  // [T][d] bf16 tokens (a position's row: X[perm[pos] / k])
-    __bf16 *H;        // [P][ffn] permuted bf16 SwiGLU outputs
+    const __bf16 *X;  // [T][d_tpad] bf16 tokens (a position's row: X[perm[pos] / k])
+    __bf16 *H;        // [P][ffn_tpad] permuted bf16 SwiGLU outputs
     const float *gates;
     float *y;
     float *part_y;  // deterministic combine: [P][d_pad] output rows per pair (y untouched), else null
     Geometry g;
 };
+
+// SwiGLU output of one 32-token tile (pair positions p0 ..) for this lane's
+// row of the chunk: H[p][row] = bf16(silu(gate) * up), rows of stride h_ld;
+// up(v) is the up accumulator matching gate accumulator v.
+template <class Up>
+__device__ inline void ck_write_h(__bf16 *H, int h_ld, int ffn, int chunk, int p0, int g1, const f32x16c &ga, Up up,
+                                  int lane) {
+    const int row = chunk * kChunkRows + (lane & 31);
+#pragma unroll
+    for (int v = 0; v < 16; v++) {
+        const int p = p0 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+        const float h = ga[v] / (1.f + expf(-ga[v])) * up(v);
+        if (p < g1 && row < ffn) H[(size_t)p * h_ld + row] = (__bf16)h;
+    }
+}
+
+// Down-projection output of one 32-token tile for this lane's row: the
+// gate-weighted row of pair perm[p], into its own slot of part_y (combined in
+// a fixed order afterwards) or added into y with an fp32 atomic.
+__device__ inline void ck_write_down(const ChunkArgs &A, int chunk, int p0, int g1, const f32x16c &acc, int lane) {
+    const Geometry &g = A.g;
+    const int row = chunk * kChunkRows + (lane & 31);
+#pragma unroll
+    for (int v = 0; v < 16; v++) {
+        const int p = p0 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+        if (p < g1 && row < g.d) {
+            const int pair = A.perm[p];
+            if (A.part_y)
+                A.part_y[(size_t)pair * g.d_pad + row] = A.gates[pair] * acc[v];
+            else
+                unsafeAtomicAdd(A.y + (size_t)(pair / g.k) * g.d + row, A.gates[pair] * acc[v]);
+        }
+    }
+}
 
 // One pass of a contraction kernel: NT token tiles (32 tokens each) against
 // this wave's 32-row chunk of one matrix, over all input tiles.  Per tile:
@@ -403,7 +451,8 @@ __device__ inline void ck_contract(f32x16c (&acc)[NT], const __bf16 *src, int ld
 
 // Experts are split by tokens between two instances of each kernel: NMT = 1
 // (LDS for one 32-token tile: more workgroups resident per CU) takes experts
-// with at most 32 tokens in one pass, NMT = 2 takes the others in passes of
+// with at most 32 tokens in one pass (with fp16 codebooks the replicated-
+// codebook kernels take those instead), NMT = 2 takes the others in passes of
 // 64 (a last pass of at most 32 tokens contracts one tile).
 template <int NMT>
 __device__ inline bool ck_mine(int n_tok) {
@@ -435,7 +484,7 @@ __global__ __launch_bounds__(kCkThreads) void k_chunk_gu(ChunkArgs A) {
     auto pass = [&](int p0, auto nt_c) {
         constexpr int NT = decltype(nt_c)::value;
         f32x16c acc[NT];
-        ck_contract<CB, NT>(acc, A.X, g.d, g.d, p0, g1, A.perm, g.k, mat, mg, chunk, chunk_ok, cb_lds[m], xs,
+        ck_contract<CB, NT>(acc, A.X, g.d_tpad, g.d, p0, g1, A.perm, g.k, mat, mg, chunk, chunk_ok, cb_lds[m], xs,
                             code_lds[wave], lane);
         // h = silu(gate) * up: the up waves hand their tiles to the gate waves
         __syncthreads();
@@ -447,19 +496,11 @@ __global__ __launch_bounds__(kCkThreads) void k_chunk_gu(ChunkArgs A) {
 #pragma unroll
                 for (int v = 0; v < 16; v++) ex[(((wave & 1) * NT + mt) * 16 + v) * 64 + lane] = acc[mt][v];
         __syncthreads();
-        if (m == 0 && chunk_ok) {
-            const int row = chunk * kChunkRows + (lane & 31);
+        if (m == 0 && chunk_ok)
 #pragma unroll
-            for (int mt = 0; mt < NT; mt++) {
-#pragma unroll
-                for (int v = 0; v < 16; v++) {
-                    const int p = p0 + mt * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-                    const float ga = acc[mt][v], up = ex[(((wave & 1) * NT + mt) * 16 + v) * 64 + lane];
-                    const float h = ga / (1.f + expf(-ga)) * up;
-                    if (p < g1 && row < g.ffn) A.H[(size_t)p * g.ffn + row] = (__bf16)h;
-                }
-            }
-        }
+            for (int mt = 0; mt < NT; mt++)
+                ck_write_h(A.H, g.ffn_tpad, g.ffn, chunk, p0 + mt * 32, g1, acc[mt],
+                           [&](int v) { return ex[(((wave & 1) * NT + mt) * 16 + v) * 64 + lane]; }, lane);
     };
     for (int p0 = g0; p0 < g1; p0 += 32 * NMT) {
         if (NMT == 1 || g1 - p0 <= 32)
@@ -490,29 +531,14 @@ __global__ __launch_bounds__(kCkThreads) void k_chunk_down(ChunkArgs A) {
     __shared__ __align__(16) __bf16 hs[32 * NMT * kXRow];
     ck_stage_cb<CB>(cb_lds, A.cbs, e, 2);
     const uint8_t *mat = (A.slot_tab ? A.slot_tab[e] : A.codes + (int64_t)e * g.rec_int) + mg.off;
-    const int k = g.k;
     auto pass = [&](int p0, auto nt_c) {
         constexpr int NT = decltype(nt_c)::value;
         f32x16c acc[NT];
-        ck_contract<CB, NT>(acc, A.H, g.ffn, g.ffn, p0, g1, nullptr, 1, mat, mg, chunk, chunk_ok, cb_lds, hs,
+        ck_contract<CB, NT>(acc, A.H, g.ffn_tpad, g.ffn, p0, g1, nullptr, 1, mat, mg, chunk, chunk_ok, cb_lds, hs,
                             code_lds[wave], lane);
-        if (chunk_ok) {
-            const int row = chunk * kChunkRows + (lane & 31);
+        if (chunk_ok)
 #pragma unroll
-            for (int mt = 0; mt < NT; mt++) {
-#pragma unroll
-                for (int v = 0; v < 16; v++) {
-                    const int p = p0 + mt * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-                    if (p < g1 && row < g.d) {
-                        const int pair = A.perm[p];
-                        if (A.part_y)  // one writer per (pair, row): combined in a fixed order afterwards
-                            A.part_y[(size_t)pair * g.d_pad + row] = A.gates[pair] * acc[mt][v];
-                        else
-                            unsafeAtomicAdd(A.y + (size_t)(pair / k) * g.d + row, A.gates[pair] * acc[mt][v]);
-                    }
-                }
-            }
-        }
+            for (int mt = 0; mt < NT; mt++) ck_write_down(A, chunk, p0 + mt * 32, g1, acc[mt], lane);
     };
     for (int p0 = g0; p0 < g1; p0 += 32 * NMT) {
         if (NMT == 1 || g1 - p0 <= 32)
@@ -520,6 +546,209 @@ __global__ __launch_bounds__(kCkThreads) void k_chunk_down(ChunkArgs A) {
         else
             pass(p0, std::integral_constant<int, NMT>{});
     }
+}
+
+// ---------------------------------------------------------------------------
+// Replicated codebooks (fp16 codebooks, experts with at most 32 tokens).
+//
+// Rebuilding a weight vector reads one random 16-byte entry of each stage
+// codebook from LDS.  A 16-byte read is served 16 lanes at a time, one lane
+// per group of 4 banks, so random entries of one 4 KB table put several lanes
+// of a pass on one group and the pass repeats (about 2.7 times over, measured,
+// for random codes).  These kernels hold one matrix's codebooks in LDS as
+// interleaved copies that spread a pass over the groups: stage 0 in 16
+// copies (entry b of copy c in group c: lane l reads copy l % 16, never a
+// conflict), stages 1 and 2 in 8 copies (entry b of copy c in group c + 8 (b
+// & 1): lanes l and l + 8 of a pass meet only when their entries have the
+// same parity).  The values are the stored entries, so the results are those
+// of the kernels above.
+//
+// That is 128 KB; with the 32-token operand tile double-buffered beside it
+// (2 x 16 KB) a workgroup takes a whole CU, so it is 16 waves (4 per SIMD)
+// to hide the latency of each step's dependent reads.  What does not fit in
+// LDS is the per-wave code block: each lane loads its own code bytes (one
+// byte per stage and K-step, 16-byte runs of the record that two cache lines
+// hold) from global memory four steps ahead, and the next tile's block is
+// touched a tile ahead so that those loads find it in the caches.  The
+// operand tile is loaded once per workgroup and tile (all 16 waves share it),
+// one barrier per tile.
+constexpr int kRepThreads = 1024;
+constexpr int kRepWaves = kRepThreads / 64;
+constexpr int kRepS1 = 65536, kRepS2 = 98304, kRepBytes = 131072;  // stage 1, stage 2 offsets; size
+constexpr int kRepXRow = kTileSlices * kVec * 2;                   // bytes of one staged token row (512)
+constexpr int kRepXBytes = 32 * kRepXRow;                          // one 32-token tile
+constexpr int kRepAhead = 4;                                       // code bytes loaded this many steps ahead
+static_assert(kRepThreads == 4 * kCodes, "staging: four threads per entry");
+static_assert(kRepThreads == 32 * 32, "operand tile: one 16-byte piece per thread");
+static_assert(kRepBytes + 2 * kRepXBytes <= 160 * 1024, "LDS of one CU");
+
+// The fp16 codebooks of (expert e, matrix m) in the replicated layout.  Thread
+// t copies entry t % 256 into a quarter of its copies, rotated by the entry so
+// that 16 consecutive lanes write 16 different bank groups.
+__device__ inline void rep_stage_cb(char *rep, const void *cbs, int e, int m) {
+    const auto *src = global_view(reinterpret_cast<const ck_u32x4 *>(static_cast<const char *>(cbs) +
+                                                                     ((int64_t)e * 3 + m) * CkCb<1>::kBytes));
+    const int ent = threadIdx.x & (kCodes - 1), q = threadIdx.x >> 8;
+    const ck_u32x4 v0 = src[ent], v1 = src[kCodes + ent], v2 = src[2 * kCodes + ent];
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+        const int c = (4 * q + j + ent) & 15;
+        *reinterpret_cast<ck_u32x4 *>(rep + ent * 256 + c * 16) = v0;
+    }
+#pragma unroll
+    for (int j = 0; j < 2; j++) {
+        const int c = (2 * q + j + (ent >> 1)) & 7;
+        *reinterpret_cast<ck_u32x4 *>(rep + kRepS1 + ent * 128 + c * 16) = v1;
+        *reinterpret_cast<ck_u32x4 *>(rep + kRepS2 + ent * 128 + c * 16) = v2;
+    }
+}
+
+// The operand tile: token row r (of 32), 16-byte piece q (of 32) at r * 512 +
+// 16 (q ^ (r % 16)), so that the 16 rows a read pass covers (same piece) lie
+// in 16 different bank groups.  Thread t stages piece t % 32 of row t / 32:
+// xrow is its row (the expert's last token past its tokens: those rows feed
+// only output rows that are never written), already offset by its piece.
+__device__ inline ck_w4 rep_load_x(const __bf16 *xrow, int kt) {
+    return *global_view(reinterpret_cast<const ck_w4 *>(xrow + kt * kTileSlices * kVec));
+}
+__device__ inline void rep_store_x(char *xs, const ck_w4 &v) {
+    const int r = threadIdx.x >> 5, q = threadIdx.x & 31;
+    *reinterpret_cast<ck_w4 *>(xs + r * kRepXRow + ((q ^ (r & 15)) << 4)) = v;
+}
+
+// One matrix: each wave's 32-row chunk against the expert's (at most 32)
+// tokens over all input tiles; xrow as for rep_store_x.  Every wave takes
+// part in the staging and the barriers; a wave past the matrix's last chunk
+// computes the last chunk again (its rows are never written).
+//
+// Per step (K-step kk of tile kt) a lane: loads the code bytes of the step
+// kRepAhead later (global memory; ring of kRepAhead slots), reads the three
+// codebook entries of the next step (EA = 1; its bytes arrived a few steps
+// ago) or of this one (EA = 0: 12 registers fewer, for the gate/up kernel,
+// which holds a second accumulator), sums this step's entries into its 8
+// weights and issues the MFMA with its token operand from the tile.  The
+// scheduler is kept from merging the steps, which would make each step wait
+// for its own reads.
+template <int EA>
+__device__ inline void rep_contract(f32x16c &acc, const __bf16 *xrow, const uint8_t *mat, const MatGeom &mg, int chunk,
+                                    const char *rep, char *xs, int lane) {
+#pragma unroll
+    for (int v = 0; v < 16; v++) acc[v] = 0.f;
+    // (locals: read through the reference, the compiler reloads them with
+    // scalar loads whose wait would drain the loads in flight)
+    const int n_tiles = mg.n_tiles, n_chunks = mg.n_chunks;
+    const int ch = min(chunk, n_chunks - 1);
+    const int n = lane & 31, p = lane >> 5;
+    // this lane's code byte of (row n, slice 2 kk + p, stage s) in a tile's
+    // block: + s * 1024 + 32 kk
+    const uint8_t *cb0 = mat + (int64_t)ch * kChunkBytes + (n >> 4) * 512 + p * 16 + (n & 15);
+    const int64_t tstride = (int64_t)n_chunks * kChunkBytes;
+    auto tile_codes = [&](int t) { return cb0 + min(t, n_tiles - 1) * tstride; };
+    const char *r0 = rep + (lane & 15) * 16, *r1 = rep + kRepS1 + (lane & 7) * 16, *r2 = rep + kRepS2 + (lane & 7) * 16;
+    const int xa = n * kRepXRow, xm = n & 15;  // this lane's token row in the tile
+    uint32_t c[kRepAhead][3];  // code bytes, slot (step) % kRepAhead
+    ck_u32x4 en[EA + 1][3];    // entries of this step (and the next), slot step % (EA + 1)
+    uint32_t touch, sink = 0;  // the next tile's code block touched into the caches (a dword per 64 bytes)
+    auto load_codes = [&](uint32_t(&d)[3], const uint8_t *tp, int kk) {
+#pragma unroll
+        for (int st = 0; st < 3; st++) d[st] = *global_view(tp + st * 1024 + kk * 32);
+    };
+    auto read_entries = [&](ck_u32x4(&d)[3], const uint32_t(&k)[3]) {
+        d[0] = *reinterpret_cast<const ck_u32x4 *>(r0 + (k[0] << 8));
+        d[1] = *reinterpret_cast<const ck_u32x4 *>(r1 + (k[1] << 7));
+        d[2] = *reinterpret_cast<const ck_u32x4 *>(r2 + (k[2] << 7));
+    };
+    auto load_touch = [&](int t) {
+        touch = *global_view(reinterpret_cast<const uint32_t *>(
+            mat + ((int64_t)min(t, n_tiles - 1) * n_chunks + ch) * kChunkBytes + (lane % 48) * 64));
+    };
+    ck_w4 xv = rep_load_x(xrow, 0);
+    rep_store_x(xs, xv);
+    xv = rep_load_x(xrow, min(1, n_tiles - 1));
+    load_touch(1);
+#pragma unroll
+    for (int kk = 0; kk < kRepAhead; kk++) load_codes(c[kk], tile_codes(0), kk);
+    __syncthreads();  // the codebooks (staged by the caller) and the first operand tile
+    if (EA) read_entries(en[0], c[0]);
+    for (int kt = 0; kt < n_tiles; kt++) {
+        const uint8_t *tc = tile_codes(kt), *tn = tile_codes(kt + 1);
+        const char *xb = xs + (kt & 1) * kRepXBytes + xa;
+#pragma unroll
+        for (int kk = 0; kk < 16; kk++) {
+            // token operand, then entries (with EA = 0 from the slot refilled
+            // next), then the codes kRepAhead steps on: a wait for the
+            // operand leaves the next step's entries in flight
+            const ck_w4 a = *reinterpret_cast<const ck_w4 *>(xb + (((2 * kk + p) ^ xm) << 4));
+            read_entries(en[(kk + EA) % (EA + 1)], c[(kk + EA) % kRepAhead]);
+            const int ka = kk + kRepAhead;
+            load_codes(c[ka % kRepAhead], ka < 16 ? tc : tn, ka % 16);
+            __builtin_amdgcn_sched_barrier(0);
+            const ck_u32x4(&e)[3] = en[kk % (EA + 1)];
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), ck_sum3_f16(e[0], e[1], e[2]), acc,
+                                                          0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        // the next tile's operands into the other buffer (last read two tiles
+        // ago, before the previous barrier), the one after into registers
+        rep_store_x(xs + ((kt + 1) & 1) * kRepXBytes, xv);
+        xv = rep_load_x(xrow, min(kt + 2, n_tiles - 1));
+        sink ^= touch;
+        load_touch(kt + 2);
+        __syncthreads();
+    }
+    // keeps the touch loads (their values are never needed)
+    if (sink == 0x9e3779b9u && n_tiles < 0) acc[0] = __uint_as_float(sink);
+}
+
+// gate/up: grid (ceil(gate chunks / 16), E), 1024 threads.  Workgroup (nb,
+// a) takes active expert act[a] and output rows nb * 512 .. + 512 (wave w:
+// chunk 16 nb + w), first of gate, then (codebooks restaged) of up; h =
+// silu(gate) up.
+__global__ __launch_bounds__(kRepThreads) void k_chunk_gu_rep(ChunkArgs A) {
+    const Geometry &g = A.g;
+    const int a = A.a0 + blockIdx.y;
+    if (a >= A.a1 || a >= A.act[g.E]) return;
+    const int e = A.act[a];
+    const int g0 = A.grp_off[e], g1 = A.grp_off[e + 1];
+    if (!ck_mine<1>(g1 - g0)) return;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int chunk = kRepWaves * blockIdx.x + wave;  // gate and up have the same shape
+    __shared__ __align__(16) char rep[kRepBytes];
+    __shared__ __align__(16) char xs[2 * kRepXBytes];
+    const int xpos = min(g0 + (int)(threadIdx.x >> 5), g1 - 1);
+    const __bf16 *xrow = A.X + (int64_t)(A.perm[xpos] / g.k) * g.d_tpad + (threadIdx.x & 31) * 8;
+    const uint8_t *rec = A.slot_tab ? A.slot_tab[e] : A.codes + (int64_t)e * g.rec_int;
+    f32x16c acc, gate;
+    for (int m = 0; m < 2; m++) {
+        if (m) __syncthreads();  // every wave is done with the gate codebooks
+        rep_stage_cb(rep, A.cbs, e, m);
+        rep_contract<0>(acc, xrow, rec + g.m[m].off, g.m[m], chunk, rep, xs, lane);  // (its first barrier covers the staging)
+        if (m == 0) gate = acc;
+    }
+    if (chunk < g.m[0].n_chunks) ck_write_h(A.H, g.ffn_tpad, g.ffn, chunk, g0, g1, gate, [&](int v) { return acc[v]; }, lane);
+}
+
+// down: grid (ceil(down chunks / 16), E), 1024 threads.  Workgroup (nb, a)
+// takes active expert act[a] and output rows nb * 512 .. + 512.
+__global__ __launch_bounds__(kRepThreads) void k_chunk_down_rep(ChunkArgs A) {
+    const Geometry &g = A.g;
+    const int a = A.a0 + blockIdx.y;
+    if (a >= A.a1 || a >= A.act[g.E]) return;
+    const int e = A.act[a];
+    const int g0 = A.grp_off[e], g1 = A.grp_off[e + 1];
+    if (!ck_mine<1>(g1 - g0)) return;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const MatGeom &mg = g.m[2];
+    const int chunk = kRepWaves * blockIdx.x + wave;
+    __shared__ __align__(16) char rep[kRepBytes];
+    __shared__ __align__(16) char xs[2 * kRepXBytes];
+    rep_stage_cb(rep, A.cbs, e, 2);
+    const int xpos = min(g0 + (int)(threadIdx.x >> 5), g1 - 1);
+    const __bf16 *xrow = A.H + (int64_t)xpos * g.ffn_tpad + (threadIdx.x & 31) * 8;
+    const uint8_t *mat = (A.slot_tab ? A.slot_tab[e] : A.codes + (int64_t)e * g.rec_int) + mg.off;
+    f32x16c acc;
+    rep_contract<1>(acc, xrow, mat, mg, chunk, rep, xs, lane);
+    if (chunk < mg.n_chunks) ck_write_down(A, chunk, g0, g1, acc, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -531,7 +760,7 @@ hipError_t launch_chunk_prep(const Geometry &g, const ChunkWork &cw, const float
     hipError_t rc = hipGetLastError();
     if (rc != hipSuccess) return rc;
     hipLaunchKernelGGL(k_chunk_stage, dim3(T), dim3(kCkThreads), 0, s, x, g.d, g.k, pre, eps, residual, g.E, ids,
-                       cw.X, y, cw.det ? 0 : 1);
+                       cw.X, g.d_tpad, y, cw.det ? 0 : 1);
     return hipGetLastError();
 }
 
@@ -554,6 +783,8 @@ hipError_t launch_chunk_experts(const Geometry &g, const ChunkWork &cw, const ui
         if (e != hipSuccess) return e;
         big = cw.side;
     }
+    const dim3 rgu((g.m[0].n_chunks + kRepWaves - 1) / kRepWaves, a1 - a0),
+        rdn((g.m[2].n_chunks + kRepWaves - 1) / kRepWaves, a1 - a0);
     if (g.cb_dtype == 0) {
         hipLaunchKernelGGL((k_chunk_gu<0, 2>), ggu, dim3(kCkThreads), 0, big, A);
         hipLaunchKernelGGL((k_chunk_down<0, 2>), gdn, dim3(kCkThreads), 0, big, A);
@@ -562,8 +793,8 @@ hipError_t launch_chunk_experts(const Geometry &g, const ChunkWork &cw, const ui
     } else {
         hipLaunchKernelGGL((k_chunk_gu<1, 2>), ggu, dim3(kCkThreads), 0, big, A);
         hipLaunchKernelGGL((k_chunk_down<1, 2>), gdn, dim3(kCkThreads), 0, big, A);
-        hipLaunchKernelGGL((k_chunk_gu<1, 1>), ggu, dim3(kCkThreads), 0, s, A);
-        hipLaunchKernelGGL((k_chunk_down<1, 1>), gdn, dim3(kCkThreads), 0, s, A);
+        hipLaunchKernelGGL(k_chunk_gu_rep, rgu, dim3(kRepThreads), 0, s, A);
+        hipLaunchKernelGGL(k_chunk_down_rep, rdn, dim3(kRepThreads), 0, s, A);
     }
     hipError_t e = hipGetLastError();
     if (e == hipSuccess && big != s) {

@@ -45,6 +45,8 @@ struct Geometry {
     int64_t cb_bytes;      // one expert's codebooks: 3 * 3 * 256 * 8 * elem
     int ffn_pad;           // gate chunks * 32
     int d_pad;             // down chunks * 32
+    int d_tpad, ffn_tpad;  // d, ffn rounded up to whole input tiles (256): row strides of the chunk
+                           // path's bf16 X and H, whose pad columns are zero (cleared once, never written)
 };
 
 Geometry make_geometry(int d, int ffn, int E, int k, int cb_dtype);
@@ -167,8 +169,8 @@ struct Workspace {
 
 // Chunk-path workspace (device), sized for max_tokens * k pairs.
 struct ChunkWork {
-    __bf16 *X;     // [T][d] tokens (normalised), bf16
-    __bf16 *H;     // [P][ffn] SwiGLU outputs in expert-grouped order, bf16
+    __bf16 *X;     // [T][d_tpad] tokens (normalised), bf16
+    __bf16 *H;     // [P][ffn_tpad] SwiGLU outputs in expert-grouped order, bf16
     int *perm;     // [P] position -> pair
     int *grp_off;  // [E + 2] group offsets (group E: invalid ids)
     int *act;      // [E + 1] experts on the matrix cores, then their count at [E]
