@@ -397,7 +397,7 @@ static int stream_forward(rvq_moe *h, const float *x, int T, const int32_t *ids,
         for (int a0 = 0; a0 < (int)U.size(); a0 += R) {
             const int a1 = a0 + R < (int)U.size() ? a0 + R : (int)U.size();
             HIP_TRY(slots_acquire(c, U.data() + a0, a1 - a0, s, h->call_used));
-            HIP_TRY(launch_chunk_experts(g, h->cw, nullptr, c.tab_dev, h->cbs, gates, y, a0, a1, s));
+            HIP_TRY(launch_chunk_experts(g, h->cw, nullptr, c.tab_dev, h->cbs, gates, y, a0, a1, T * k, s));
             HIP_TRY(slots_release(c, h->call_used, s));
         }
         if (h->det) HIP_TRY(combine(h, h->ws, 1, x, ids, y, T, s));

@@ -26,12 +26,13 @@
 // the B operand it needs (row l % 32, 8 consecutive inputs of one slice):
 // three code bytes, three codebook entries from LDS, fp32 sum, RNE to bf16.
 // The dense weight tile never exists in LDS or HBM.  Two kernel families:
-//   - experts with at most 32 tokens, fp16 codebooks (nearly all of them in a
-//     512-token chunk): the replicated-codebook kernels below, one 16-wave
-//     workgroup per CU with the matrix's codebooks copied so that the entry
-//     reads do not collide on LDS banks;
-//   - the others (more than 32 tokens, or fp32 codebooks): 4-wave workgroups
-//     that stage each tile's token rows and per-wave code blocks in LDS.
+//   - experts with at most 32 tokens, fp16 codebooks, in calls with enough
+//     (token, expert) pairs to fill the GPU (nearly all experts of a 512-token
+//     chunk): the replicated-codebook kernels below, one 16-wave workgroup per
+//     CU with the matrix's codebooks copied so that the entry reads do not
+//     collide on LDS banks;
+//   - the others: 4-wave workgroups that stage each tile's token rows and
+//     per-wave code blocks in LDS, several per CU.
 #include <math.h>
 
 #include <type_traits>
@@ -451,8 +452,8 @@ __device__ inline void ck_contract(f32x16c (&acc)[NT], const __bf16 *src, int ld
 
 // Experts are split by tokens between two instances of each kernel: NMT = 1
 // (LDS for one 32-token tile: more workgroups resident per CU) takes experts
-// with at most 32 tokens in one pass (with fp16 codebooks the replicated-
-// codebook kernels take those instead), NMT = 2 takes the others in passes of
+// with at most 32 tokens in one pass (in large fp16-codebook calls the
+// replicated-codebook kernels take those instead), NMT = 2 takes the others in passes of
 // 64 (a last pass of at most 32 tokens contracts one tile).
 template <int NMT>
 __device__ inline bool ck_mine(int n_tok) {
@@ -766,7 +767,7 @@ hipError_t launch_chunk_prep(const Geometry &g, const ChunkWork &cw, const float
 
 hipError_t launch_chunk_experts(const Geometry &g, const ChunkWork &cw, const uint8_t *codes,
                                 const uint8_t *const *slot_tab, const void *cbs, const float *gates, float *y, int a0,
-                                int a1, hipStream_t s) {
+                                int a1, int pairs, hipStream_t s) {
     if (a1 <= a0) return hipSuccess;
     ChunkArgs A{codes, slot_tab, a0, a1, cbs, cw.grp_off, cw.act, cw.perm, cw.X, cw.H, gates, y,
                 cw.det ? cw.part_y : nullptr, g};
@@ -785,6 +786,14 @@ hipError_t launch_chunk_experts(const Geometry &g, const ChunkWork &cw, const ui
     }
     const dim3 rgu((g.m[0].n_chunks + kRepWaves - 1) / kRepWaves, a1 - a0),
         rdn((g.m[2].n_chunks + kRepWaves - 1) / kRepWaves, a1 - a0);
+    // The replicated-codebook kernels give a whole CU to 512 rows of one
+    // expert: they pay off when many experts have several tokens (measured at
+    // the K3 shape: 32 tokens per call 1.48 against 1.36 ms, 40 tokens equal,
+    // 64 tokens 2.20 against 2.32 ms, 512 tokens 3.31 against 3.56 ms), so
+    // they take calls with 2 or more pairs per expert on average; a
+    // slot-cache round (a few dozen experts) keeps the one-copy kernels unless
+    // it covers 64 experts or more.
+    const bool rep = g.cb_dtype == 1 && (int64_t)pairs >= 2 * (int64_t)g.E && (!slot_tab || a1 - a0 >= 64);
     if (g.cb_dtype == 0) {
         hipLaunchKernelGGL((k_chunk_gu<0, 2>), ggu, dim3(kCkThreads), 0, big, A);
         hipLaunchKernelGGL((k_chunk_down<0, 2>), gdn, dim3(kCkThreads), 0, big, A);
@@ -793,8 +802,13 @@ hipError_t launch_chunk_experts(const Geometry &g, const ChunkWork &cw, const ui
     } else {
         hipLaunchKernelGGL((k_chunk_gu<1, 2>), ggu, dim3(kCkThreads), 0, big, A);
         hipLaunchKernelGGL((k_chunk_down<1, 2>), gdn, dim3(kCkThreads), 0, big, A);
-        hipLaunchKernelGGL(k_chunk_gu_rep, rgu, dim3(kRepThreads), 0, s, A);
-        hipLaunchKernelGGL(k_chunk_down_rep, rdn, dim3(kRepThreads), 0, s, A);
+        if (rep) {
+            hipLaunchKernelGGL(k_chunk_gu_rep, rgu, dim3(kRepThreads), 0, s, A);
+            hipLaunchKernelGGL(k_chunk_down_rep, rdn, dim3(kRepThreads), 0, s, A);
+        } else {
+            hipLaunchKernelGGL((k_chunk_gu<1, 1>), ggu, dim3(kCkThreads), 0, s, A);
+            hipLaunchKernelGGL((k_chunk_down<1, 1>), gdn, dim3(kCkThreads), 0, s, A);
+        }
     }
     hipError_t e = hipGetLastError();
     if (e == hipSuccess && big != s) {
@@ -809,7 +823,7 @@ hipError_t launch_chunk(const Geometry &g, const ChunkWork &cw, const uint8_t *c
                         int lut_tokens, int *err, hipStream_t s) {
     const hipError_t rc = launch_chunk_prep(g, cw, x, ids, y, T, pre, residual, eps, lut_tokens, err, s);
     if (rc != hipSuccess) return rc;
-    return launch_chunk_experts(g, cw, codes, nullptr, cbs, gates, y, 0, g.E, s);
+    return launch_chunk_experts(g, cw, codes, nullptr, cbs, gates, y, 0, g.E, T * g.k, s);
 }
 
 }  // namespace rvq

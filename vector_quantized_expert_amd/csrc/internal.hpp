@@ -241,9 +241,10 @@ hipError_t launch_cb_exponents(const void *cbs, int cb_dtype, int n_experts, int
 // left out of the matrix-core kernels and listed for the table path (1: none).
 hipError_t launch_chunk_prep(const Geometry &g, const ChunkWork &cw, const float *x, const int32_t *ids, float *y,
                              int T, int pre, int residual, double eps, int lut_tokens, int *err, hipStream_t s);
+// pairs: the call's (token, expert) pairs (chooses between the kernel families)
 hipError_t launch_chunk_experts(const Geometry &g, const ChunkWork &cw, const uint8_t *codes,
                                 const uint8_t *const *slot_tab, const void *cbs, const float *gates, float *y, int a0,
-                                int a1, hipStream_t s);
+                                int a1, int pairs, hipStream_t s);
 hipError_t launch_chunk(const Geometry &g, const ChunkWork &cw, const uint8_t *codes, const void *cbs, const float *x,
                         const int32_t *ids, const float *gates, float *y, int T, int pre, int residual, double eps,
                         int lut_tokens, int *err, hipStream_t s);
