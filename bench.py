@@ -255,7 +255,7 @@ def sub_records(torch, np, G, S, O, RvqMoe, inp, args, bank_host):
         "layer_kernel_ms": lay_ms / lay_n if lay_n else None, "calls": 20,
         "parity": dict(par, bar="ids bit-exact, rel L2 <= 1e-4")}
     log("sub-record: prefill chunk, 512 tokens per call, resident codes")
-    ms, uniq, kt, par = timed(512, 5, 1, 200000)
+    ms, uniq, kt, par = timed(512, 12, 2, 200000)
     byts = uniq * (rec + CB_BYTES)
     flops = 6.0 * 512 * shape.top_k * shape.d * shape.ffn
     ck_n, ck_ms = kt["chunk"]
@@ -270,7 +270,7 @@ def sub_records(torch, np, G, S, O, RvqMoe, inp, args, bank_host):
         "chunk_kernels_ms": ck_ms / ck_n if ck_n else None,
         "chunk_kernels_note": "HIP events around layer_forward's launches: grouping, staging, the two "
                               "contraction kernels and the table-path launch for the listed experts",
-        "calls": 5,
+        "calls": 12,
         "parity": dict(par, bar="ids bit-exact, rel L2 <= 2e-2")}
     handle.close()
     del handle
