@@ -916,6 +916,30 @@ def test_streaming_table_path_matches_resident_and_counts_lru(torch_mod, tiny, d
     rs.close()
 
 
+def test_streaming_rounds_of_64_experts_on_the_replicated_kernels(torch_mod):
+    """128 slots: experts in rounds of 64, enough for the replicated-codebook
+    kernels to take a slot-cache round (they read each expert's record through
+    the slot table).  Same outputs as with resident codes, bitwise with the
+    deterministic combine, and the oracle at the bf16 bar."""
+    from synth import gpu as G
+    shape = S.Shape(256, 128, 128, 4, "f16")
+    T = 96  # 384 pairs: 3 per expert on average
+    inp = G.LayerInputs(shape, seed=31, layer=0, host_codes=True)
+    bank = _pinned_bank(torch_mod, inp)
+    st = _layer(torch_mod, inp, shape, T, codes=bank, codes_location=1, cache_slots=128, chunk_min_tokens=8,
+                lut_expert_tokens=1, deterministic=True)
+    rs = _layer(torch_mod, inp, shape, T, chunk_min_tokens=8, lut_expert_tokens=1, deterministic=True)
+    x = S.tokens(31, 0, T, shape.d)
+    a = _run(torch_mod, st, shape, x)
+    b = _run(torch_mod, rs, shape, x)
+    assert np.array_equal(a[0], b[0])
+    assert np.array_equal(a[2], b[2])
+    assert len(np.unique(a[0])) > 64  # at least two rounds
+    _check_chunk(inp, shape, x, *a, tokens=[0, 50, 95])
+    st.close()
+    rs.close()
+
+
 @pytest.mark.parametrize("det", [False, True])
 def test_streaming_chunk_path_matches_resident(torch_mod, det):
     """The chunk path with 4 slots: experts in rounds of 2, copies overlapping
