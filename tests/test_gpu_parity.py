@@ -659,6 +659,26 @@ def test_chunk_group_sizes_at_the_kernel_boundaries(torch_mod):
     layer.close()
 
 
+def test_chunk_kernel_families_agree_bitwise(torch_mod):
+    """The chunk path's two kernel families compute the same sums in the same
+    order: 24 tokens in one call (96 pairs, 6 per expert: the replicated-
+    codebook kernels) and the same tokens one per call (4 pairs: the one-copy
+    kernels) give bitwise equal outputs with the deterministic combine, on
+    ragged tiles both ways; and the oracle at the bf16 bar."""
+    from synth import gpu as G
+    shape = S.Shape(1032, 264, 16, 4, "f16")
+    T = 24
+    inp = G.LayerInputs(shape, seed=37, layer=0, host_codes=True)
+    layer = _layer(torch_mod, inp, shape, T, chunk_min_tokens=1, lut_expert_tokens=1, deterministic=True)
+    x = S.tokens(37, 0, T, shape.d)
+    grp = _run(torch_mod, layer, shape, x)
+    one = _run(torch_mod, layer, shape, x, per_token=True)
+    assert np.array_equal(grp[0], one[0])
+    assert np.array_equal(grp[2], one[2]), np.abs(grp[2] - one[2]).max()
+    _check_chunk(inp, shape, x, *grp, tokens=[0, 11, 23])
+    layer.close()
+
+
 @pytest.mark.parametrize("cb", ["f32", "f16"])
 def test_chunk_path_closed_form_element_by_element(torch_mod, cb):
     """Stage codebooks that are one-hot vectors scaled by 1, 2, 4 (signs per
